@@ -1,0 +1,246 @@
+"""CPU oracle for the top-2 sparse MoE feed-forward layer.
+
+TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this package.  The library's product
+path never calls it, and it shares no code with the HIP library: the
+arithmetic lives in ``moe_oracle.c`` (plain C, fp64), built by ``build()``
+with gcc, and the integer bookkeeping below is plain Python.
+
+Functions, each following "Mixtral 8x7B -- The Evolving Transformer",
+section 05 (MOE ROUTER + MOE), and section 04 (SWIGLU):
+
+* ``route``        router logits, top-2 with lowest-index ties, softmax over
+                   the two selected logits (MoERouter; formula of section 05)
+* ``dispatch``     stable grouping of (token, slot) assignments by expert:
+                   the per-expert token batches that section 05 says
+                   production stacks form instead of looping with masks
+* ``expert_rows``  one SwiGLU expert applied to given rows (section 04)
+* ``combine``      y[t] = w[t,0] o[t,0] + w[t,1] o[t,1] (formula of section 05)
+* ``forward``      the whole layer, token by token
+
+Parity status: every function is pinned by tests/test_oracle.py against
+closed forms, brute force, library routines (numpy fp64) and invariants.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
+_lib = None
+
+ORC_F32, ORC_BF16 = 0, 1
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the oracle with gcc: IEEE semantics (no fast-math, no FMA
+    contraction), so each sum is evaluated in the order the source states."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+           "-ffp-contract=off", "-fno-fast-math", _SRC, "-lm", "-o", _LIB_PATH + ".tmp"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    return _LIB_PATH
+
+
+def _bind(path: str):
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    lib.oracle_route.argtypes = [I, I, I, P, P, I, P, P, P, I]
+    lib.oracle_route.restype = I
+    lib.oracle_expert_rows.argtypes = [I, I, I, I, P, P, P, P, P, I, P, I]
+    lib.oracle_expert_rows.restype = I
+    lib.oracle_forward.argtypes = [I, I, I, I, P, P, P, P, P, I, P, P, P, P, I]
+    lib.oracle_forward.restype = I
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build()
+    _lib = _bind(_LIB_PATH)
+    return _lib
+
+
+def use_library(lib):
+    """Swap the loaded oracle library for another build (a path or a handle
+    returned earlier).  Returns the previous handle.  The pin tests use this
+    to run the same checks against copies with planted mistakes."""
+    global _lib
+    prev = _load()
+    _lib = _bind(lib) if isinstance(lib, str) else lib
+    return prev
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+# ---------------------------------------------------------------------------
+# Array marshalling.  Inputs are numpy fp32 arrays, or bf16 values carried as
+# their uint16 bit patterns, or torch CPU tensors of either dtype.
+
+def _as_host(a) -> Tuple[np.ndarray, int]:
+    """Return (contiguous numpy array, dtype code) without changing values."""
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            a = a.detach().cpu().contiguous()
+            if a.dtype == torch.bfloat16:
+                return a.view(torch.int16).numpy().view(np.uint16), ORC_BF16
+            if a.dtype == torch.float32:
+                return a.numpy(), ORC_F32
+            raise TypeError(f"oracle takes fp32 or bf16 tensors, got {a.dtype}")
+    except ImportError:  # pragma: no cover
+        pass
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float32:
+        return a, ORC_F32
+    if a.dtype == np.uint16:
+        return a, ORC_BF16
+    raise TypeError(f"oracle takes float32 or bf16-bit (uint16) arrays, got {a.dtype}")
+
+
+def _same_dtype(*codes):
+    if len(set(codes)) != 1:
+        raise TypeError("all inputs of one oracle call must share a dtype")
+    return codes[0]
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+# ---------------------------------------------------------------------------
+
+def route(x, w_gate, threads: Optional[int] = None, return_logits: bool = False):
+    """Router for every token: returns idx int32 [T,2] (slot 0 = larger
+    logit), w float64 [T,2], and optionally logits float64 [T,E]."""
+    xa, dx = _as_host(x)
+    ga, dg = _as_host(w_gate)
+    dt = _same_dtype(dx, dg)
+    T, d = xa.shape
+    d2, E = ga.shape
+    assert d == d2
+    idx = np.zeros((T, 2), np.int32)
+    w = np.zeros((T, 2), np.float64)
+    logits = np.zeros((T, E), np.float64)
+    rc = _load().oracle_route(T, d, E, _ptr(xa), _ptr(ga), dt, _ptr(idx), _ptr(w),
+                              _ptr(logits), threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_route rejected its sizes")
+    return (idx, w, logits) if return_logits else (idx, w)
+
+
+def dispatch(idx: np.ndarray, n_experts: int):
+    """Group the 2T (token, slot) assignments by expert, keeping token order
+    and then slot order inside each expert.
+
+    Returns counts int32 [E], offsets int32 [E+1] (exclusive prefix sum of
+    counts), pos int32 [T,2] (row of assignment (t, s) in the grouped order)
+    and src int32 [2T] (the flat assignment t*2+s held by each grouped row).
+    """
+    idx = np.asarray(idx)
+    T = idx.shape[0]
+    counts = np.zeros(n_experts, np.int32)
+    for t in range(T):
+        for s in range(2):
+            counts[int(idx[t, s])] += 1
+    offsets = np.zeros(n_experts + 1, np.int32)
+    for e in range(n_experts):
+        offsets[e + 1] = offsets[e] + counts[e]
+    fill = offsets[:-1].copy()
+    pos = np.zeros((T, 2), np.int32)
+    src = np.zeros(2 * T, np.int32)
+    for t in range(T):
+        for s in range(2):
+            e = int(idx[t, s])
+            pos[t, s] = fill[e]
+            src[fill[e]] = 2 * t + s
+            fill[e] += 1
+    return counts, offsets, pos, src
+
+
+def expert_rows(rows, expert: np.ndarray, w1, w3, w2, threads: Optional[int] = None):
+    """out[r] = SwiGLU expert ``expert[r]`` applied to rows[r]; float64 [n, d]."""
+    ra, dr = _as_host(rows)
+    a1, d1 = _as_host(w1)
+    a3, d3 = _as_host(w3)
+    a2, d2 = _as_host(w2)
+    dt = _same_dtype(dr, d1, d3, d2)
+    n, d = ra.shape
+    E, d_, f = a1.shape
+    assert d_ == d and a3.shape == a1.shape and a2.shape == (E, f, d)
+    ex = np.ascontiguousarray(expert, dtype=np.int32)
+    assert ex.shape == (n,)
+    out = np.zeros((n, d), np.float64)
+    rc = _load().oracle_expert_rows(n, d, f, E, _ptr(ra), _ptr(ex), _ptr(a1), _ptr(a3),
+                                    _ptr(a2), dt, _ptr(out), threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_expert_rows rejected its sizes or expert ids")
+    return out
+
+
+def combine(o_slot: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """y[t] = w[t,0] * o_slot[t,0] + w[t,1] * o_slot[t,1], fp64; o_slot is
+    [T, 2, d] (the two expert outputs of each token, slot order)."""
+    o = np.asarray(o_slot, np.float64)
+    w = np.asarray(w, np.float64)
+    return w[:, 0:1] * o[:, 0, :] + w[:, 1:2] * o[:, 1, :]
+
+
+def forward(x, w_gate, w1, w3, w2, threads: Optional[int] = None, return_logits=False):
+    """The whole layer: returns y float64 [T,d], idx int32 [T,2], w float64
+    [T,2] (and logits float64 [T,E] when asked)."""
+    xa, dx = _as_host(x)
+    ga, dg = _as_host(w_gate)
+    a1, d1 = _as_host(w1)
+    a3, d3 = _as_host(w3)
+    a2, d2 = _as_host(w2)
+    dt = _same_dtype(dx, dg, d1, d3, d2)
+    T, d = xa.shape
+    E, d_, f = a1.shape
+    assert d_ == d and ga.shape == (d, E) and a3.shape == a1.shape and a2.shape == (E, f, d)
+    y = np.zeros((T, d), np.float64)
+    idx = np.zeros((T, 2), np.int32)
+    w = np.zeros((T, 2), np.float64)
+    logits = np.zeros((T, E), np.float64)
+    rc = _load().oracle_forward(T, d, f, E, _ptr(xa), _ptr(ga), _ptr(a1), _ptr(a3),
+                                _ptr(a2), dt, _ptr(y), _ptr(idx), _ptr(w), _ptr(logits),
+                                threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_forward rejected its sizes")
+    return (y, idx, w, logits) if return_logits else (y, idx, w)
+
+
+# ---------------------------------------------------------------------------
+# Near-tie screening, used to keep the routing decision unambiguous in parity
+# inputs: a token whose 1st/2nd or 2nd/3rd largest logits lie within ``gap``
+# of each other could be routed differently by any change of summation order.
+
+NEAR_TIE_GAP = 1e-3
+
+
+def near_tie_tokens(x, w_gate, gap: float = NEAR_TIE_GAP, threads: Optional[int] = None):
+    """Bool [T]: tokens whose fp64 logits have a 1st/2nd or 2nd/3rd gap < gap."""
+    import torch
+    _, _, logits = route(x, w_gate, threads=threads, return_logits=True)
+    srt = -np.sort(-logits, axis=1)
+    bad = (srt[:, 0] - srt[:, 1] < gap)
+    if logits.shape[1] >= 3:
+        bad |= (srt[:, 1] - srt[:, 2] < gap)
+    return torch.from_numpy(bad)

@@ -1,0 +1,254 @@
+/*
+ * CPU oracle for the top-2 sparse mixture-of-experts feed-forward layer.
+ *
+ * TEST INFRASTRUCTURE.  This file is the slow, plain reference that the HIP
+ * library is checked against.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg load it.  It shares no code, header, table or
+ * helper with the GPU library, and the GPU library never calls it.
+ *
+ * What it computes, per token t and independently of every other token
+ * ("Mixtral 8x7B -- The Evolving Transformer", section 05 MOE ROUTER + MOE,
+ * its formula y = sum_k w_k E_{i_k}(x) and the MoERouter / MoE modules;
+ * section 04 SWIGLU for the expert body):
+ *
+ *   1. router logits   l[e] = sum_j x[t,j] * Wg[j,e]          (bias-free Linear)
+ *   2. top-2           i0 = argmax_e l[e], i1 = argmax_{e != i0} l[e],
+ *                      exact ties resolved toward the lower expert index
+ *   3. weights         softmax over the two selected logits:
+ *                      q = exp(l[i1] - l[i0]);  w0 = 1/(1+q),  w1 = q/(1+q)
+ *                      (equal to softmax over all experts, keep the top two,
+ *                      divide by their sum -- the page's order of steps)
+ *   4. experts         for s in {0,1}, e = i_s:
+ *                      g = x W1[e], u = x W3[e]           (gate, up)
+ *                      a = silu(g) * u,  silu(v) = v / (1 + exp(-v))
+ *                      o_s = a W2[e]                      (down)
+ *   5. combine         y[t] = w0 * o_0 + w1 * o_1
+ *
+ * Matrix names follow the layer's C interface: W1 = gate, W3 = up,
+ * W2 = down.  (The page's SwiGLU listing calls the same three matrices
+ * w1 = gate, w2 = up, w3 = down.)  Layouts are dense row-major with no
+ * transposes: x [T,d], Wg [d,E], W1/W3 [E,d,f], W2 [E,f,d], y [T,d].
+ *
+ * Precision.  Inputs arrive as fp32 or as bf16 bit patterns; both are
+ * widened exactly to double.  Every sum, product and exp is fp64, sums run
+ * in ascending index order, and nothing is rounded except where stated:
+ * the top-2 decision is taken on the logits rounded to fp32, the precision
+ * in which the GPU library takes it, so that both sides decide the same
+ * integer the same way.  The weights use the unrounded fp64 logits.
+ *
+ * Threads split the tokens; each token's arithmetic is the same sequential
+ * loop whichever thread runs it.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORC_F32 = 0, ORC_BF16 = 1 };
+
+/* Widen element i of an fp32 or bf16 array to double (exact in both cases:
+ * a bf16 value is the upper half of an fp32 bit pattern). */
+static double load_elem(const void *p, int dtype, size_t i) {
+    float v;
+    if (dtype == ORC_F32) {
+        v = ((const float *)p)[i];
+    } else {
+        uint32_t bits = (uint32_t)((const uint16_t *)p)[i] << 16;
+        memcpy(&v, &bits, sizeof v);
+    }
+    return (double)v;
+}
+
+/* Step 1: l[e] = sum_j x[j] * Wg[j, e], j ascending. */
+static void router_logits(int d, int E, const void *x, size_t x_off,
+                          const void *wg, int dtype, double *l) {
+    for (int e = 0; e < E; ++e) l[e] = 0.0;
+    for (int j = 0; j < d; ++j) {
+        double xj = load_elem(x, dtype, x_off + (size_t)j);
+        for (int e = 0; e < E; ++e)
+            l[e] += xj * load_elem(wg, dtype, (size_t)j * E + e);
+    }
+}
+
+/* Steps 2-3 on one token's logits.  Strict '>' keeps the first (lowest)
+ * index among equal values. */
+static void top2_softmax(int E, const double *l, int32_t *idx, double *w) {
+    int i0 = 0;
+    for (int e = 1; e < E; ++e)
+        if ((float)l[e] > (float)l[i0]) i0 = e;
+    int i1 = -1;
+    for (int e = 0; e < E; ++e) {
+        if (e == i0) continue;
+        if (i1 < 0 || (float)l[e] > (float)l[i1]) i1 = e;
+    }
+    double q = exp(l[i1] - l[i0]);
+    idx[0] = i0;
+    idx[1] = i1;
+    w[0] = 1.0 / (1.0 + q);
+    w[1] = q / (1.0 + q);
+}
+
+/* Step 4 for one input row xr[d] and expert e.  g, u are scratch [f];
+ * the result goes to o[d]. */
+static void swiglu_expert(int d, int f, const double *xr, int e,
+                          const void *w1, const void *w3, const void *w2,
+                          int dtype, double *g, double *u, double *o) {
+    size_t in_base = (size_t)e * d * f;   /* W1[e], W3[e] : [d, f] */
+    size_t out_base = (size_t)e * f * d;  /* W2[e]        : [f, d] */
+    for (int n = 0; n < f; ++n) { g[n] = 0.0; u[n] = 0.0; }
+    for (int j = 0; j < d; ++j) {
+        double xj = xr[j];
+        size_t row = in_base + (size_t)j * f;
+        for (int n = 0; n < f; ++n) {
+            g[n] += xj * load_elem(w1, dtype, row + n);
+            u[n] += xj * load_elem(w3, dtype, row + n);
+        }
+    }
+    for (int n = 0; n < f; ++n)
+        g[n] = g[n] / (1.0 + exp(-g[n])) * u[n];   /* a = silu(g) * u */
+    for (int m = 0; m < d; ++m) o[m] = 0.0;
+    for (int n = 0; n < f; ++n) {
+        double an = g[n];
+        size_t row = out_base + (size_t)n * d;
+        for (int m = 0; m < d; ++m) o[m] += an * load_elem(w2, dtype, row + m);
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Threading: split [0, n) into contiguous chunks, one per thread.     */
+
+typedef void (*range_fn)(void *ctx, int lo, int hi);
+typedef struct { range_fn fn; void *ctx; int lo, hi; } chunk_t;
+
+static void *run_chunk(void *p) {
+    chunk_t *c = (chunk_t *)p;
+    c->fn(c->ctx, c->lo, c->hi);
+    return NULL;
+}
+
+static void parallel_for(int n, int threads, range_fn fn, void *ctx) {
+    if (threads < 1) threads = 1;
+    if (threads > n) threads = n > 0 ? n : 1;
+    pthread_t tid[256];
+    chunk_t ch[256];
+    if (threads > 256) threads = 256;
+    int done = 0;
+    for (int i = 0; i < threads; ++i) {
+        int lo = (int)((long long)n * i / threads);
+        int hi = (int)((long long)n * (i + 1) / threads);
+        ch[i] = (chunk_t){fn, ctx, lo, hi};
+        if (i == threads - 1 || pthread_create(&tid[i], NULL, run_chunk, &ch[i]) != 0) {
+            run_chunk(&ch[i]);
+            tid[i] = 0;
+        }
+        done = i + 1;
+    }
+    for (int i = 0; i < done; ++i)
+        if (tid[i]) pthread_join(tid[i], NULL);
+}
+
+/* ------------------------------------------------------------------ */
+/* Entry points (called through ctypes by the Python side).            */
+
+typedef struct {
+    int T, d, f, E, dtype;
+    const void *x, *wg, *w1, *w3, *w2;
+    int32_t *idx;
+    double *w, *logits, *y;
+} layer_ctx;
+
+static void route_range(void *p, int lo, int hi) {
+    layer_ctx *c = (layer_ctx *)p;
+    double l[256];
+    for (int t = lo; t < hi; ++t) {
+        router_logits(c->d, c->E, c->x, (size_t)t * c->d, c->wg, c->dtype, l);
+        if (c->logits)
+            for (int e = 0; e < c->E; ++e) c->logits[(size_t)t * c->E + e] = l[e];
+        top2_softmax(c->E, l, c->idx + 2 * (size_t)t, c->w + 2 * (size_t)t);
+    }
+}
+
+/* Router for T tokens: idx [T,2] int32 (slot 0 = larger logit), w [T,2]
+ * fp64, logits [T,E] fp64 (may be NULL).  Returns 0, or -1 on bad sizes. */
+int oracle_route(int T, int d, int E, const void *x, const void *wg, int dtype,
+                 int32_t *idx, double *w, double *logits, int threads) {
+    if (T < 0 || d < 1 || E < 2 || E > 256) return -1;
+    layer_ctx c = {T, d, 0, E, dtype, x, wg, NULL, NULL, NULL, idx, w, logits, NULL};
+    parallel_for(T, threads, route_range, &c);
+    return 0;
+}
+
+typedef struct {
+    int n, d, f, dtype;
+    const void *rows;          /* [n, d] */
+    const int32_t *expert;     /* [n]    */
+    const void *w1, *w3, *w2;
+    double *out;               /* [n, d] */
+} rows_ctx;
+
+static void expert_rows_range(void *p, int lo, int hi) {
+    rows_ctx *c = (rows_ctx *)p;
+    double *xr = malloc(sizeof(double) * c->d);
+    double *g = malloc(sizeof(double) * c->f);
+    double *u = malloc(sizeof(double) * c->f);
+    if (!xr || !g || !u) { free(xr); free(g); free(u); return; }
+    for (int r = lo; r < hi; ++r) {
+        for (int j = 0; j < c->d; ++j)
+            xr[j] = load_elem(c->rows, c->dtype, (size_t)r * c->d + j);
+        swiglu_expert(c->d, c->f, xr, c->expert[r], c->w1, c->w3, c->w2,
+                      c->dtype, g, u, c->out + (size_t)r * c->d);
+    }
+    free(xr); free(g); free(u);
+}
+
+/* Step 4 alone: out[r] = expert(expert[r]) applied to rows[r], fp64.
+ * Returns 0, or -1 on bad sizes / expert ids out of [0, E). */
+int oracle_expert_rows(int n, int d, int f, int E, const void *rows,
+                       const int32_t *expert, const void *w1, const void *w3,
+                       const void *w2, int dtype, double *out, int threads) {
+    if (n < 0 || d < 1 || f < 1) return -1;
+    for (int r = 0; r < n; ++r)
+        if (expert[r] < 0 || expert[r] >= E) return -1;
+    rows_ctx c = {n, d, f, dtype, rows, expert, w1, w3, w2, out};
+    parallel_for(n, threads, expert_rows_range, &c);
+    return 0;
+}
+
+static void forward_range(void *p, int lo, int hi) {
+    layer_ctx *c = (layer_ctx *)p;
+    double l[256];
+    double *xr = malloc(sizeof(double) * c->d);
+    double *o0 = malloc(sizeof(double) * c->d);
+    double *o1 = malloc(sizeof(double) * c->d);
+    double *g = malloc(sizeof(double) * c->f);
+    double *u = malloc(sizeof(double) * c->f);
+    if (!xr || !o0 || !o1 || !g || !u) goto out;
+    for (int t = lo; t < hi; ++t) {
+        size_t xo = (size_t)t * c->d;
+        int32_t *it = c->idx + 2 * (size_t)t;
+        double *wt = c->w + 2 * (size_t)t;
+        router_logits(c->d, c->E, c->x, xo, c->wg, c->dtype, l);
+        if (c->logits)
+            for (int e = 0; e < c->E; ++e) c->logits[(size_t)t * c->E + e] = l[e];
+        top2_softmax(c->E, l, it, wt);
+        for (int j = 0; j < c->d; ++j) xr[j] = load_elem(c->x, c->dtype, xo + j);
+        swiglu_expert(c->d, c->f, xr, it[0], c->w1, c->w3, c->w2, c->dtype, g, u, o0);
+        swiglu_expert(c->d, c->f, xr, it[1], c->w1, c->w3, c->w2, c->dtype, g, u, o1);
+        for (int m = 0; m < c->d; ++m)                       /* step 5 */
+            c->y[xo + m] = wt[0] * o0[m] + wt[1] * o1[m];
+    }
+out:
+    free(xr); free(o0); free(o1); free(g); free(u);
+}
+
+/* The whole layer for T tokens: y [T,d] fp64, idx [T,2], w [T,2] fp64,
+ * logits [T,E] fp64 (may be NULL).  Returns 0, or -1 on bad sizes. */
+int oracle_forward(int T, int d, int f, int E, const void *x, const void *wg,
+                   const void *w1, const void *w3, const void *w2, int dtype,
+                   double *y, int32_t *idx, double *w, double *logits, int threads) {
+    if (T < 0 || d < 1 || f < 1 || E < 2 || E > 256) return -1;
+    layer_ctx c = {T, d, f, E, dtype, x, wg, w1, w3, w2, idx, w, logits, y};
+    parallel_for(T, threads, forward_range, &c);
+    return 0;
+}

@@ -1,0 +1,332 @@
+"""Pins for the CPU oracle, checked against facts that do not come from the
+oracle itself: hand-derived worked examples, brute force, numpy fp64
+library routines, and invariants of the layer's definition
+("Mixtral 8x7B -- The Evolving Transformer", sections 04 and 05).
+
+The mutation tests at the end plant plausible mistakes in a copy of the
+oracle's C source and check that these pins catch every one of them.
+"""
+import itertools
+import json
+import math
+import os
+import re
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_mixture_experts_top2_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
+
+
+def _s(v):
+    return 1.0 / (1.0 + math.exp(-v))
+
+
+def _silu(v):
+    return v * _s(v)
+
+
+def _closed_form(expr: str) -> float:
+    if not re.fullmatch(r"[0-9a-z_.+\-*/() ]+", expr):
+        raise ValueError(expr)
+    return float(eval(expr, {"__builtins__": {}}, {"s": _s, "silu": _silu, "math": math}))
+
+
+def _golden_examples():
+    with open(GOLDEN) as fh:
+        data = json.load(fh)
+    out = []
+    for ex in data["examples"]:
+        x = np.array(ex["x"], np.float32)
+        wg = np.array(ex["w_gate"], np.float32)
+        if "scaled_experts" in ex:
+            se = ex["scaled_experts"]
+            E, d = wg.shape[1], wg.shape[0]
+            gc, uc, dr = (np.array(se[k], np.float32) for k in ("gate_col", "up_col", "down_row"))
+            w1 = np.stack([(e + 1) * gc[:, None] for e in range(E)]).astype(np.float32)
+            w3 = np.stack([(e + 1) * uc[:, None] for e in range(E)]).astype(np.float32)
+            w2 = np.stack([(e + 1) * dr[None, :] for e in range(E)]).astype(np.float32)
+        else:
+            w1 = np.array(ex["w1"], np.float32)
+            w3 = np.array(ex["w3"], np.float32)
+            w2 = np.array(ex["w2"], np.float32)
+        out.append((ex["name"], x, wg, w1, w3, w2, np.array(ex["idx"], np.int32),
+                    np.array([[_closed_form(v) for v in row] for row in ex["w"]]),
+                    np.array([[_closed_form(v) for v in row] for row in ex["y"]])))
+    return out
+
+
+def _bf16_bits(a: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16)
+    assert torch.equal(t.float(), torch.from_numpy(np.ascontiguousarray(a, np.float32))), \
+        "worked example values must be exact in bf16"
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def _rand_layer(T=24, d=16, f=12, E=8, seed=0, dtype=W.F32):
+    wl = W.small_workload(T, d, f, E=E, dtype=dtype, seed=seed)
+    return W.make_inputs(wl)
+
+
+def _f64(t):
+    return t.float().numpy().astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Pins.  Each takes no arguments and uses whatever oracle library is loaded,
+# so the mutation tests can run the same checks against a planted mistake.
+
+def pin_worked_examples():
+    for name, x, wg, w1, w3, w2, idx_e, w_e, y_e in _golden_examples():
+        for conv in (lambda a: a, _bf16_bits):
+            y, idx, w = oracle.forward(conv(x), conv(wg), conv(w1), conv(w3), conv(w2), threads=1)
+            np.testing.assert_array_equal(idx, idx_e, err_msg=name)
+            np.testing.assert_allclose(w, w_e, rtol=1e-15, atol=1e-16, err_msg=name)
+            np.testing.assert_allclose(y, y_e, rtol=1e-13, atol=1e-15, err_msg=name)
+
+
+def pin_logits_match_numpy():
+    for seed, dtype in ((1, W.F32), (2, W.BF16)):
+        inp = _rand_layer(T=40, d=64, E=8, seed=seed, dtype=dtype)
+        _, _, logits = oracle.route(inp.x, inp.w_gate, return_logits=True)
+        ref = _f64(inp.x) @ _f64(inp.w_gate)
+        np.testing.assert_allclose(logits, ref, rtol=1e-12, atol=1e-12)
+
+
+def _brute_force_top2(l32: np.ndarray):
+    """The unique ordered pair (a, b) such that a beats b and b beats every
+    other expert, where u beats v iff l[u] > l[v] or (l[u] == l[v] and u < v)."""
+    E = l32.shape[0]
+
+    def beats(u, v):
+        return l32[u] > l32[v] or (l32[u] == l32[v] and u < v)
+
+    hits = [(a, b) for a, b in itertools.permutations(range(E), 2)
+            if beats(a, b) and all(beats(b, c) for c in range(E) if c not in (a, b))]
+    assert len(hits) == 1
+    return hits[0]
+
+
+def pin_top2_brute_force():
+    rng = np.random.default_rng(5)
+    # random logits, plus coarse-grid logits that tie often
+    for trial in range(3):
+        T, d, E = 60, 8, (8, 5, 3)[trial]
+        x = rng.standard_normal((T, d)).astype(np.float32)
+        wg = rng.standard_normal((d, E)).astype(np.float32)
+        if trial > 0:
+            x = np.round(x * 2) / 2
+            wg = np.round(wg * 2) / 2
+            wg[:, E - 1] = wg[:, 0]      # an exact duplicate column: guaranteed ties
+        idx, _, logits = oracle.route(x, wg, return_logits=True)
+        for t in range(T):
+            assert tuple(idx[t]) == _brute_force_top2(logits[t].astype(np.float32)), (trial, t)
+
+
+def pin_weights_closed_form_and_page_form():
+    inp = _rand_layer(T=50, d=32, E=8, seed=3)
+    idx, w, logits = oracle.route(inp.x, inp.w_gate, return_logits=True)
+    rows = np.arange(idx.shape[0])
+    l0, l1 = logits[rows, idx[:, 0]], logits[rows, idx[:, 1]]
+    # closed form: w0 is the logistic function of the logit gap
+    np.testing.assert_allclose(w[:, 0], 1.0 / (1.0 + np.exp(l1 - l0)), rtol=1e-14)
+    # the page's order: softmax over all experts, keep the two, renormalise
+    p = np.exp(logits - logits.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    sel = np.stack([p[rows, idx[:, 0]], p[rows, idx[:, 1]]], axis=1)
+    np.testing.assert_allclose(w, sel / sel.sum(axis=1, keepdims=True), rtol=1e-12)
+    # invariants
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+    assert np.all(w[:, 0] >= 0.5) and np.all(w[:, 1] <= 0.5)
+
+
+def _numpy_dense_by_expert(inp):
+    """Every expert on every token with numpy fp64 matmuls, then select."""
+    x, wg = _f64(inp.x), _f64(inp.w_gate)
+    w1, w3, w2 = _f64(inp.w1), _f64(inp.w3), _f64(inp.w2)
+    logits = x @ wg
+    outs = []
+    for e in range(w1.shape[0]):
+        g = x @ w1[e]
+        u = x @ w3[e]
+        outs.append((g / (1.0 + np.exp(-g)) * u) @ w2[e])
+    outs = np.stack(outs, axis=1)                      # [T, E, d]
+    return logits, outs
+
+
+def pin_forward_matches_numpy_dense():
+    for seed, dtype in ((11, W.F32), (12, W.BF16)):
+        inp = _rand_layer(T=48, d=32, f=24, E=8, seed=seed, dtype=dtype)
+        y, idx, w = oracle.forward(inp.x, inp.w_gate, inp.w1, inp.w3, inp.w2)
+        logits, outs = _numpy_dense_by_expert(inp)
+        # routing by sorting fp32-rounded logits (ties: lower index first)
+        order = np.lexsort((np.tile(np.arange(logits.shape[1]), (logits.shape[0], 1)),
+                            -logits.astype(np.float32)), axis=1)
+        np.testing.assert_array_equal(idx, order[:, :2].astype(np.int32))
+        rows = np.arange(y.shape[0])
+        g = logits[rows, idx[:, 1]] - logits[rows, idx[:, 0]]
+        w0 = 1.0 / (1.0 + np.exp(g))
+        ref = w0[:, None] * outs[rows, idx[:, 0]] + (1 - w0)[:, None] * outs[rows, idx[:, 1]]
+        np.testing.assert_allclose(y, ref, rtol=1e-11, atol=1e-12)
+
+
+def pin_expert_rows_match_numpy():
+    inp = _rand_layer(T=30, d=16, f=40, E=4, seed=21, dtype=W.BF16)
+    ex = np.arange(30, dtype=np.int32) % 4
+    out = oracle.expert_rows(inp.x, ex, inp.w1, inp.w3, inp.w2)
+    x, w1, w3, w2 = _f64(inp.x), _f64(inp.w1), _f64(inp.w3), _f64(inp.w2)
+    for r in range(30):
+        e = ex[r]
+        g, u = x[r] @ w1[e], x[r] @ w3[e]
+        np.testing.assert_allclose(out[r], (g / (1 + np.exp(-g)) * u) @ w2[e], rtol=1e-12, atol=1e-13)
+
+
+def pin_identical_experts_equal_dense_swiglu():
+    """All experts equal => the layer is one dense SwiGLU block (the page's
+    dense Mistral FFN), because the two routing weights sum to one."""
+    inp = _rand_layer(T=32, d=24, f=20, E=8, seed=31)
+    for t in (inp.w1, inp.w3, inp.w2):
+        t[:] = t[0:1].clone()
+    y, _, _ = oracle.forward(inp.x, inp.w_gate, inp.w1, inp.w3, inp.w2)
+    x = _f64(inp.x)
+    g, u = x @ _f64(inp.w1[0]), x @ _f64(inp.w3[0])
+    dense = (g / (1 + np.exp(-g)) * u) @ _f64(inp.w2[0])
+    np.testing.assert_allclose(y, dense, rtol=1e-12, atol=1e-13)
+
+
+def pin_forced_one_hot_router():
+    """A constant input column with a huge router weight on expert a makes
+    w = (1, 0) exactly in fp64, so y must equal expert a's output exactly."""
+    for a in (0, 5):
+        inp = _rand_layer(T=20, d=16, f=16, E=8, seed=40 + a)
+        inp.x[:, -1] = 1.0
+        inp.w_gate[-1, :] = 0.0
+        inp.w_gate[-1, a] = 1000.0
+        y, idx, w = oracle.forward(inp.x, inp.w_gate, inp.w1, inp.w3, inp.w2)
+        assert np.all(idx[:, 0] == a)
+        assert np.all(w[:, 0] == 1.0) and np.all(w[:, 1] == 0.0)
+        single = oracle.expert_rows(inp.x, np.full(20, a, np.int32), inp.w1, inp.w3, inp.w2)
+        np.testing.assert_array_equal(y, single)
+
+
+def pin_power_of_two_scaling():
+    inp = _rand_layer(T=16, d=16, f=16, seed=50)
+    y, _, _ = oracle.forward(inp.x, inp.w_gate, inp.w1, inp.w3, inp.w2)
+    y2, _, _ = oracle.forward(inp.x, inp.w_gate, inp.w1, inp.w3, inp.w2 * 2)
+    np.testing.assert_array_equal(y2, 2 * y)
+
+
+def pin_expert_relabelling_and_token_permutation():
+    inp = _rand_layer(T=24, d=16, f=16, seed=60)
+    y, idx, w = oracle.forward(inp.x, inp.w_gate, inp.w1, inp.w3, inp.w2)
+    perm = torch.tensor([3, 7, 0, 5, 1, 6, 2, 4])
+    inv = torch.argsort(perm)
+    y2, idx2, w2 = oracle.forward(inp.x, inp.w_gate[:, perm].contiguous(), inp.w1[perm].contiguous(),
+                                  inp.w3[perm].contiguous(), inp.w2[perm].contiguous())
+    np.testing.assert_array_equal(y2, y)
+    np.testing.assert_array_equal(perm.numpy()[idx2], idx)
+    tp = torch.randperm(24, generator=torch.Generator().manual_seed(1))
+    y3, idx3, _ = oracle.forward(inp.x[tp].contiguous(), inp.w_gate, inp.w1, inp.w3, inp.w2)
+    np.testing.assert_array_equal(y3, y[tp.numpy()])
+    np.testing.assert_array_equal(idx3, idx[tp.numpy()])
+    _ = inv
+
+
+def pin_dispatch_is_stable_grouping():
+    rng = np.random.default_rng(8)
+    for T, E in ((1, 8), (37, 8), (300, 5), (64, 8)):
+        idx = np.stack([rng.integers(0, E, T), rng.integers(0, E, T)], axis=1).astype(np.int32)
+        if T == 64:
+            idx[:, 0] = 2                    # one expert takes every slot-0 assignment
+        counts, offsets, pos, src = oracle.dispatch(idx, E)
+        flat = idx.reshape(-1)
+        np.testing.assert_array_equal(counts, np.bincount(flat, minlength=E))
+        np.testing.assert_array_equal(offsets, np.concatenate([[0], np.cumsum(counts)]))
+        order = np.argsort(flat, kind="stable")
+        np.testing.assert_array_equal(src, order)
+        np.testing.assert_array_equal(pos.reshape(-1)[order], np.arange(2 * T))
+
+
+PINS = [pin_worked_examples, pin_logits_match_numpy, pin_top2_brute_force,
+        pin_weights_closed_form_and_page_form, pin_forward_matches_numpy_dense,
+        pin_expert_rows_match_numpy, pin_identical_experts_equal_dense_swiglu,
+        pin_forced_one_hot_router, pin_power_of_two_scaling,
+        pin_expert_relabelling_and_token_permutation, pin_dispatch_is_stable_grouping]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
+def test_pin(pin):
+    pin()
+
+
+def test_combine_definition():
+    o = np.array([[[1.0, 2.0], [10.0, -20.0]]])
+    w = np.array([[0.75, 0.25]])
+    np.testing.assert_array_equal(oracle.combine(o, w), [[3.25, -3.5]])
+
+
+def test_threads_do_not_change_results():
+    inp = _rand_layer(T=33, d=16, f=16, seed=70, dtype=W.BF16)
+    a = oracle.forward(inp.x, inp.w_gate, inp.w1, inp.w3, inp.w2, threads=1)
+    b = oracle.forward(inp.x, inp.w_gate, inp.w1, inp.w3, inp.w2, threads=7)
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
+
+
+# ---------------------------------------------------------------------------
+# Mutation tests: plant one plausible mistake in a copy of the oracle's C
+# source, build it, and require that at least one pin fails.
+
+MUTANTS = {
+    "gate_up_swapped": ("g[n] = g[n] / (1.0 + exp(-g[n])) * u[n];",
+                        "g[n] = u[n] / (1.0 + exp(-u[n])) * g[n];"),
+    "silu_sign": ("g[n] / (1.0 + exp(-g[n]))", "g[n] / (1.0 + exp(g[n]))"),
+    "tie_to_higher_index": ("if ((float)l[e] > (float)l[i0]) i0 = e;",
+                            "if ((float)l[e] >= (float)l[i0]) i0 = e;"),
+    "slot_weights_swapped": ("w[0] = 1.0 / (1.0 + q);\n    w[1] = q / (1.0 + q);",
+                             "w[1] = 1.0 / (1.0 + q);\n    w[0] = q / (1.0 + q);"),
+    "down_transposed": ("o[m] += an * load_elem(w2, dtype, row + m);",
+                        "o[m] += an * load_elem(w2, dtype, out_base + (size_t)m * f + n);"),
+    "dropped_first_term": ("for (int j = 0; j < d; ++j) {\n        double xj = xr[j];",
+                           "for (int j = 1; j < d; ++j) {\n        double xj = xr[j];"),
+    "router_column_index": ("l[e] += xj * load_elem(wg, dtype, (size_t)j * E + e);",
+                            "l[e] += xj * load_elem(wg, dtype, (size_t)e * d + j);"),
+    "combine_second_slot_dropped": ("c->y[xo + m] = wt[0] * o0[m] + wt[1] * o1[m];",
+                                    "c->y[xo + m] = wt[0] * o0[m] + wt[1] * o0[m];"),
+}
+
+
+def _build_mutant(name, tmpdir):
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "moe_oracle.c")).read()
+    old, new = MUTANTS[name]
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    path_c = os.path.join(tmpdir, f"{name}.c")
+    path_so = os.path.join(tmpdir, f"{name}.so")
+    with open(path_c, "w") as fh:
+        fh.write(src.replace(old, new))
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+                    "-ffp-contract=off", path_c, "-lm", "-o", path_so], check=True)
+    return path_so
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name):
+    with tempfile.TemporaryDirectory() as tmp:
+        so = _build_mutant(name, tmp)
+        prev = oracle.use_library(so)
+        try:
+            caught = []
+            for pin in PINS:
+                try:
+                    pin()
+                except AssertionError:
+                    caught.append(pin.__name__)
+            assert caught, f"no pin catches the planted mistake {name}"
+        finally:
+            oracle.use_library(prev)
