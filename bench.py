@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Throughput of the top-2 sparse MoE layer (Mixtral 8x7B shape) on one MI355X.
+
+One step = one ``moe_forward`` call (route, dispatch, gate/up, down,
+combine) over one batch of synthetic tokens whose inputs are already in HBM.
+The headline workload is the 8x7B decode step (T = 32 tokens); the 8x7B
+prefill (T = 4096) is measured in the same run and reported under
+``secondary``.  Prints ONE JSON line.
+
+Roofline entries: the dominant kernel of each workload (the gate/up grouped
+GEMM: two thirds of the layer's bytes and FLOPs) is timed on its own with
+HIP events on the stream it runs on; its algorithmic bytes (decode, HBM
+bound: the selected experts' w1/w3 plus xp read and h written) or FLOPs
+(prefill, MFMA bound: 2 * 2T * d * 2f) per launch are divided by that time.
+
+The CPU baseline is the plain oracle (fp64, all host threads up to 16) run
+on the decode tokens for a bounded time.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s (8x7B shape, T=32 & T=4096); % of HBM / MFMA peak"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default per workload)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default per workload)")
+    ap.add_argument("--workload", default="decode_8x7b")
+    ap.add_argument("--secondary", default="prefill_8x7b", help="'' to skip")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall time budget of the CPU oracle baseline (0 to skip)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this size (for counter scaling)")
+    return ap.parse_args()
+
+
+def time_region(fn, steps, stream):
+    """Mean ms per call of fn() over `steps` calls, with HIP events on `stream`."""
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def measure(wl_name, steps, warmup):
+    import torch
+    import sparse_mixture_experts_top2_amd as moe
+    from sparse_mixture_experts_top2_amd import workloads as W
+
+    wl = W.WORKLOADS[wl_name]
+    dev = torch.device("cuda:0")
+    log(f"{wl_name}: drawing inputs on the GPU (T={wl.T}, d={wl.d}, f={wl.f}, E={wl.E})")
+    inp = W.make_inputs(wl, device="cuda")
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ws = moe.alloc_workspace(wl.T, wl.d, wl.f, wl.E, inp.x.dtype, dev)
+    y = torch.empty(wl.T, wl.d, dtype=inp.x.dtype, device=dev)
+
+    def step():
+        moe.forward(inp.x, inp.w_gate, inp.w1, inp.w3, inp.w2, workspace=ws, out=y)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ms_events = time_region(step, steps, stream)
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    ms = ms_events
+
+    # The dominant kernel alone: gate/up over the same routed rows.
+    idx, w = moe.route(inp.x, inp.w_gate)
+    counts, offsets, pos, xp = moe.dispatch(inp.x, idx, wl.E)
+    h = torch.empty(2 * wl.T, wl.f, dtype=inp.x.dtype, device=dev)
+
+    def gateup():
+        moe.expert_gateup(xp, counts, offsets, inp.w1, inp.w3, out=h)
+
+    for _ in range(max(2, warmup)):
+        gateup()
+    k_ms = time_region(gateup, steps, stream)
+    c = counts.cpu().tolist()
+    active = sum(1 for v in c if v > 0)
+    eb = 2 if wl.dtype == W.BF16 else 4
+    weight_bytes_gu = active * 2 * wl.d * wl.f * eb
+    gu_bytes = weight_bytes_gu + 2 * wl.T * wl.d * eb + 2 * wl.T * wl.f * eb
+    gu_flops = 2.0 * (2 * wl.T) * wl.d * (2 * wl.f)
+    layer_flops = wl.T * (2.0 * 2 * 3 * wl.d * wl.f + 2.0 * wl.d * wl.E)
+    layer_bytes = active * 3 * wl.d * wl.f * eb + 2 * wl.T * wl.d * eb + wl.d * wl.E * eb
+    hbm_bound = wl.T <= 32
+    if hbm_bound:
+        ach = gu_bytes / (k_ms * 1e-3) / 1e9
+        roof = {"kernel": "expert gate/up (weight-streaming MFMA)", "bound": "hbm",
+                "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_ms": round(k_ms, 5)}
+        lay = layer_bytes / (ms * 1e-3) / 1e9
+        layer = {"bound": "hbm", "achieved": round(lay, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                 "frac": round(lay / PEAK_HBM_GBS, 4), "algorithmic_bytes_per_step": layer_bytes}
+    else:
+        ach = gu_flops / (k_ms * 1e-3) / 1e12
+        roof = {"kernel": "expert gate/up (LDS-tiled MFMA grouped GEMM)", "bound": "mfma",
+                "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "algorithmic_flops_per_launch": gu_flops, "avg_launch_ms": round(k_ms, 5)}
+        lay = layer_flops / (ms * 1e-3) / 1e12
+        layer = {"bound": "mfma", "achieved": round(lay, 1), "peak": PEAK_BF16_TFLOPS,
+                 "unit": "TFLOP/s", "frac": round(lay / PEAK_BF16_TFLOPS, 4),
+                 "algorithmic_flops_per_step": layer_flops}
+    log(f"{wl_name}: {ms:.4f} ms/step ({wl.T / ms * 1e3:.0f} tokens/s); gate/up {k_ms:.4f} ms; "
+        f"counts {c}")
+    return dict(wl=wl, inp=inp, ms=ms, ms_events=ms_events, wall_ms=wall_ms,
+                tokens_per_s=wl.T / (ms * 1e-3), roofline=roof, layer_roofline=layer,
+                counts=c, active_experts=active)
+
+
+def cpu_baseline(res, budget_s):
+    """The oracle as it stands, on the decode tokens, for about budget_s."""
+    import oracle
+    threads = min(16, oracle.default_threads())
+    inp = res["inp"]
+    log(f"cpu baseline: copying inputs to host, oracle on {threads} threads")
+    host = [t.cpu() for t in (inp.x, inp.w_gate, inp.w1, inp.w3, inp.w2)]
+    T = inp.wl.T
+    chunk = min(T, 16)
+    done, t0 = 0, time.perf_counter()
+    while True:
+        lo = done % T
+        rows = slice(lo, min(T, lo + chunk))
+        oracle.forward(host[0][rows], *host[1:], threads=threads)
+        done += rows.stop - rows.start
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(done / el, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} token-evaluations of {inp.wl.name} (its {T} tokens in chunks of "
+                      f"{chunk}, repeated) in {el:.1f} s; fp64 per-token loop"}
+
+
+def copy_calibration(mib, steps):
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    ms = time_region(lambda: torch.mul(src, 1.0, out=dst), steps, torch.cuda.current_stream())
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4,
+                      "ms": round(ms, 5), "GBps_rw": round(2 * n * 4 / ms / 1e6, 1)}), flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the layer has no "
+              "multi-GPU path in this library.", flush=True)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU: the layer runs only in HIP kernels", flush=True)
+        sys.exit(1)
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib, args.steps or 20)
+        return
+
+    def defaults(name):
+        if name.startswith("decode"):
+            return (args.steps or 200, args.warmup if args.warmup is not None else 20)
+        return (args.steps or 30, args.warmup if args.warmup is not None else 5)
+
+    steps, warmup = defaults(args.workload)
+    main_res = measure(args.workload, steps, warmup)
+    sec = None
+    if args.secondary:
+        s_steps, s_warm = defaults(args.secondary)
+        r = measure(args.secondary, s_steps, s_warm)
+        sec = {"workload": r["wl"].name, "value": round(r["tokens_per_s"], 1), "unit": "tokens/s",
+               "ms_per_step": round(r["ms"], 5), "steps": s_steps, "warmup": s_warm,
+               "config": {"T": r["wl"].T, "d_model": r["wl"].d, "d_ff": r["wl"].f,
+                          "n_experts": r["wl"].E, "top_k": 2},
+               "roofline": r["roofline"], "layer_roofline": r["layer_roofline"],
+               "expert_counts": r["counts"]}
+        del r
+        torch.cuda.empty_cache()
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(main_res, args.cpu_seconds)
+    wl = main_res["wl"]
+    out = {
+        "metric": METRIC,
+        "value": round(main_res["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(main_res["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded torch draws on the GPU: x ~ N(0,1), experts ~ N(0, 1/fan_in), "
+                "router std 0.02)",
+        "config": {"workload": wl.name, "T": wl.T, "d_model": wl.d, "d_ff": wl.f,
+                   "n_experts": wl.E, "top_k": 2},
+        "roofline": main_res["roofline"],
+        "layer_roofline": main_res["layer_roofline"],
+        "expert_counts": main_res["counts"],
+        "cpu_baseline": cpu,
+        "secondary": sec,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,157 @@
+/*
+ * moe.h -- C interface of the MI355X (gfx950) top-2 sparse mixture-of-experts
+ * feed-forward layer.
+ *
+ * The layer ("Mixtral 8x7B -- The Evolving Transformer", section 05 MOE ROUTER
+ * + MOE, formula y = sum_k w_k E_{i_k}(x); section 04 SWIGLU for the expert):
+ * a bias-free linear router scores E experts per token, the two largest
+ * scores are kept, a softmax over those two gives their weights, the token
+ * runs through both SwiGLU experts  down(silu(x W1) * (x W3))  and the two
+ * expert outputs are summed with those weights.  The KerasFormers Mixtral
+ * page (API table: num_experts, num_experts_per_tok) names the same two
+ * parameters; every expert stays resident in device memory.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Shapes   T tokens, d = d_model, f = d_ff, E = n_experts, top_k = 2.
+ *          The caller flattens (batch, seq) into T rows.
+ * Layout   dense row-major, no transposes, y = x W:
+ *            x [T, d]      w_gate [d, E]
+ *            w1 [E, d, f]  (gate)     w3 [E, d, f]  (up)     w2 [E, f, d]  (down)
+ *            y [T, d]
+ *          (The page's SwiGLU listing calls gate / up / down w1 / w2 / w3;
+ *          this interface calls them w1 / w3 / w2.)
+ * Dtypes   x, w_gate, w1, w3, w2, y, xp all have shape->dtype (MOE_F32 or
+ *          MOE_BF16).  Routing indices are int32, routing weights fp32 and
+ *          expert outputs o fp32, in both modes.  Arithmetic is fp32
+ *          throughout; with MOE_BF16 the SwiGLU activation between the gate/up
+ *          and down products and the output y are rounded to bf16
+ *          (round-to-nearest-even).  Router logits are never rounded.
+ * Memory   every array argument is a device pointer owned by the caller,
+ *          16-byte aligned.  The library allocates and frees nothing; the
+ *          scratch it needs comes from the caller's workspace.
+ * Streams  `stream` is a hipStream_t (NULL = the null stream).  Calls only
+ *          enqueue work on it and return; results are valid once the
+ *          stream has been synchronised.  There is no host/device
+ *          synchronisation and no device-to-host copy inside any call.
+ * Errors   arguments are checked before anything is enqueued; a failed
+ *          check returns a non-zero moe_status_t and enqueues nothing.
+ *          MOE_ERR_HIP reports a launch failure (hipGetLastError); faults
+ *          inside kernels surface at the caller's next synchronisation.
+ *          No call prints, throws or exits.
+ * Determinism  no float atomics; every reduction has a fixed order, so two
+ *          calls on the same inputs give bit-identical outputs.
+ * Concurrency  calls are re-entrant; calls that share a workspace must be
+ *          ordered on one stream.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_NULL = 1,        /* a required pointer is NULL                       */
+    MOE_ERR_SHAPE = 2,       /* T < 0, d or f not a positive multiple of 8, ...   */
+    MOE_ERR_DTYPE = 3,       /* dtype is neither MOE_F32 nor MOE_BF16              */
+    MOE_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                  */
+    MOE_ERR_ALIAS = 5,       /* an output overlaps an input                       */
+    MOE_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than moe_workspace_bytes */
+    MOE_ERR_UNSUPPORTED = 7, /* top_k != 2, or E outside [2, 32]                   */
+    MOE_ERR_HIP = 8          /* a HIP launch failed                               */
+} moe_status_t;
+
+typedef struct {
+    int32_t T;          /* tokens (rows of x); T = 0 returns MOE_OK at once */
+    int32_t d_model;    /* d: multiple of 8, >= 8                            */
+    int32_t d_ff;       /* f: multiple of 8, >= 8                            */
+    int32_t n_experts;  /* E: 2 .. 32                                        */
+    int32_t top_k;      /* must be 2                                         */
+    int32_t dtype;      /* moe_dtype_t                                       */
+} moe_shape_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *moe_status_str(int status);
+
+/* Bytes of device workspace that moe_forward and moe_experts need for this
+ * shape (0 for an invalid shape).  The size depends on every field. */
+size_t moe_workspace_bytes(const moe_shape_t *shape);
+
+/* Router: section 05's MoERouter (bias-free Linear d -> E, softmax, top-2,
+ * renormalise over the two kept experts), in the equivalent form
+ *   l[t,e] = sum_j x[t,j] w_gate[j,e]                 (fp32, never rounded)
+ *   topk_idx[t,0] = argmax_e l,  topk_idx[t,1] = argmax_{e != idx0} l,
+ *                   equal logits resolved toward the lower expert index
+ *   topk_w[t,0] = 1 / (1 + q),  topk_w[t,1] = q / (1 + q),
+ *                   q = exp(l[idx1] - l[idx0])       (softmax of the two logits)
+ * Outputs topk_idx int32 [T, 2] and topk_w fp32 [T, 2], slot 0 holding the
+ * larger logit. */
+int moe_route(const moe_shape_t *shape, const void *x, const void *w_gate,
+              int32_t *topk_idx, float *topk_w, void *stream);
+
+/* Dispatch: the per-expert batching of tokens that section 05 names as the
+ * production form of its mask loop.  The 2T (token, slot) assignments in
+ * topk_idx are grouped by expert, keeping token order and then slot order
+ * within each expert (a stable counting sort):
+ *   counts[e]    number of assignments to expert e               int32 [E]
+ *   offsets[e]   sum of counts[0..e-1]; offsets[E] = 2T           int32 [E+1]
+ *   pos[t,s]     row of assignment (t,s) in the grouped order     int32 [T, 2]
+ *   xp[pos[t,s], :] = x[t, :]                                      [2T, d]
+ * topk_idx entries must lie in [0, E); out-of-range entries are not
+ * detected on the device and give undefined results.  xp must have room
+ * for 2T rows. */
+int moe_dispatch(const moe_shape_t *shape, const void *x, const int32_t *topk_idx,
+                 int32_t *counts, int32_t *offsets, int32_t *pos, void *xp,
+                 void *stream);
+
+/* Expert gate/up: the first half of section 04's SwiGLU block, for every
+ * expert e over its rows r in [offsets[e], offsets[e+1]) of xp:
+ *   h[r, :] = silu(xp[r] w1[e]) * (xp[r] w3[e]),  silu(v) = v / (1 + exp(-v))
+ * fp32 accumulation; h [2T, f] has the layer dtype (rounded to bf16 for
+ * MOE_BF16).  counts / offsets are moe_dispatch's outputs, left in device
+ * memory (never read back to the host).  h must not overlap xp. */
+int moe_expert_gateup(const moe_shape_t *shape, const void *xp, const int32_t *counts,
+                      const int32_t *offsets, const void *w1, const void *w3, void *h,
+                      void *stream);
+
+/* Expert down: the second half of section 04's SwiGLU block,
+ *   o[r, :] = h[r] w2[e]   for r in [offsets[e], offsets[e+1]),
+ * fp32 accumulation, o fp32 [2T, d].  o must not overlap h. */
+int moe_expert_down(const moe_shape_t *shape, const void *h, const int32_t *counts,
+                    const int32_t *offsets, const void *w2, float *o, void *stream);
+
+/* Experts: moe_expert_gateup then moe_expert_down, with h kept in the
+ * workspace:  o[r] = (silu(xp[r] w1[e]) * (xp[r] w3[e])) w2[e].
+ * o is fp32 [2T, d].  ws / ws_bytes: workspace of at least
+ * moe_workspace_bytes(shape). */
+int moe_experts(const moe_shape_t *shape, const void *xp, const int32_t *counts,
+                const int32_t *offsets, const void *w1, const void *w3,
+                const void *w2, float *o, void *ws, size_t ws_bytes, void *stream);
+
+/* Combine: section 05's weighted sum, slot 0 then slot 1, fp32 math:
+ *   y[t, :] = topk_w[t,0] * o[pos[t,0], :] + topk_w[t,1] * o[pos[t,1], :]
+ * rounded to y's dtype.  Every row of y is written. */
+int moe_combine(const moe_shape_t *shape, const float *o, const int32_t *pos,
+                const float *topk_w, void *y, void *stream);
+
+/* The whole layer: route, dispatch, experts, combine, enqueued back to back
+ * on `stream`.  topk_idx_opt / topk_w_opt (int32 [T,2], fp32 [T,2]) receive
+ * the routing when non-NULL.  y must not overlap x.
+ * ws / ws_bytes: workspace of at least moe_workspace_bytes(shape). */
+int moe_forward(const moe_shape_t *shape, const void *x, const void *w_gate,
+                const void *w1, const void *w3, const void *w2, void *y,
+                int32_t *topk_idx_opt, float *topk_w_opt,
+                void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -14,7 +14,9 @@ section 05 (MOE ROUTER + MOE), and section 04 (SWIGLU):
 * ``dispatch``     stable grouping of (token, slot) assignments by expert:
                    the per-expert token batches that section 05 says
                    production stacks form instead of looping with masks
-* ``expert_rows``  one SwiGLU expert applied to given rows (section 04)
+* ``expert_rows``  one SwiGLU expert applied to given rows (section 04),
+                   and its two halves ``expert_hidden`` (silu(x W1) * (x W3))
+                   and ``expert_down`` (h W2)
 * ``combine``      y[t] = w[t,0] o[t,0] + w[t,1] o[t,1] (formula of section 05)
 * ``forward``      the whole layer, token by token
 
@@ -60,6 +62,10 @@ def _bind(path: str):
     lib.oracle_expert_rows.restype = I
     lib.oracle_forward.argtypes = [I, I, I, I, P, P, P, P, P, I, P, P, P, P, I]
     lib.oracle_forward.restype = I
+    lib.oracle_expert_hidden.argtypes = [I, I, I, I, P, P, P, P, I, P, I]
+    lib.oracle_expert_hidden.restype = I
+    lib.oracle_expert_down.argtypes = [I, I, I, I, P, P, P, I, P, I]
+    lib.oracle_expert_down.restype = I
     return lib
 
 
@@ -192,6 +198,44 @@ def expert_rows(rows, expert: np.ndarray, w1, w3, w2, threads: Optional[int] = N
                                     _ptr(a2), dt, _ptr(out), threads or default_threads())
     if rc != 0:
         raise ValueError("oracle_expert_rows rejected its sizes or expert ids")
+    return out
+
+
+def expert_hidden(rows, expert: np.ndarray, w1, w3, threads: Optional[int] = None):
+    """SwiGLU hidden activation silu(rows[r] W1[e]) * (rows[r] W3[e]),
+    e = expert[r]; float64 [n, f]."""
+    ra, dr = _as_host(rows)
+    a1, d1 = _as_host(w1)
+    a3, d3 = _as_host(w3)
+    dt = _same_dtype(dr, d1, d3)
+    n, d = ra.shape
+    E, d_, f = a1.shape
+    assert d_ == d and a3.shape == a1.shape
+    ex = np.ascontiguousarray(expert, dtype=np.int32)
+    assert ex.shape == (n,)
+    out = np.zeros((n, f), np.float64)
+    rc = _load().oracle_expert_hidden(n, d, f, E, _ptr(ra), _ptr(ex), _ptr(a1), _ptr(a3), dt,
+                                      _ptr(out), threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_expert_hidden rejected its sizes or expert ids")
+    return out
+
+
+def expert_down(hid, expert: np.ndarray, w2, threads: Optional[int] = None):
+    """Down projection hid[r] W2[e], e = expert[r]; float64 [n, d]."""
+    ha, dh = _as_host(hid)
+    a2, d2 = _as_host(w2)
+    dt = _same_dtype(dh, d2)
+    n, f = ha.shape
+    E, f_, d = a2.shape
+    assert f_ == f
+    ex = np.ascontiguousarray(expert, dtype=np.int32)
+    assert ex.shape == (n,)
+    out = np.zeros((n, d), np.float64)
+    rc = _load().oracle_expert_down(n, d, f, E, _ptr(ha), _ptr(ex), _ptr(a2), dt, _ptr(out),
+                                    threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_expert_down rejected its sizes or expert ids")
     return out
 
 

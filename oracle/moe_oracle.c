@@ -89,13 +89,11 @@ static void top2_softmax(int E, const double *l, int32_t *idx, double *w) {
     w[1] = q / (1.0 + q);
 }
 
-/* Step 4 for one input row xr[d] and expert e.  g, u are scratch [f];
- * the result goes to o[d]. */
-static void swiglu_expert(int d, int f, const double *xr, int e,
-                          const void *w1, const void *w3, const void *w2,
-                          int dtype, double *g, double *u, double *o) {
+/* Step 4a for one input row xr[d] and expert e: the SwiGLU hidden
+ * activation a = silu(x W1[e]) * (x W3[e]) into g[f]; u is scratch [f]. */
+static void swiglu_hidden(int d, int f, const double *xr, int e, const void *w1,
+                          const void *w3, int dtype, double *g, double *u) {
     size_t in_base = (size_t)e * d * f;   /* W1[e], W3[e] : [d, f] */
-    size_t out_base = (size_t)e * f * d;  /* W2[e]        : [f, d] */
     for (int n = 0; n < f; ++n) { g[n] = 0.0; u[n] = 0.0; }
     for (int j = 0; j < d; ++j) {
         double xj = xr[j];
@@ -107,12 +105,27 @@ static void swiglu_expert(int d, int f, const double *xr, int e,
     }
     for (int n = 0; n < f; ++n)
         g[n] = g[n] / (1.0 + exp(-g[n])) * u[n];   /* a = silu(g) * u */
+}
+
+/* Step 4b: o[d] = a[f] W2[e]. */
+static void swiglu_down(int d, int f, const double *a, int e, const void *w2, int dtype,
+                        double *o) {
+    size_t out_base = (size_t)e * f * d;  /* W2[e] : [f, d] */
     for (int m = 0; m < d; ++m) o[m] = 0.0;
     for (int n = 0; n < f; ++n) {
-        double an = g[n];
+        double an = a[n];
         size_t row = out_base + (size_t)n * d;
         for (int m = 0; m < d; ++m) o[m] += an * load_elem(w2, dtype, row + m);
     }
+}
+
+/* Step 4 for one input row xr[d] and expert e.  g, u are scratch [f];
+ * the result goes to o[d]. */
+static void swiglu_expert(int d, int f, const double *xr, int e,
+                          const void *w1, const void *w3, const void *w2,
+                          int dtype, double *g, double *u, double *o) {
+    swiglu_hidden(d, f, xr, e, w1, w3, dtype, g, u);
+    swiglu_down(d, f, g, e, w2, dtype, o);
 }
 
 /* ------------------------------------------------------------------ */
@@ -212,6 +225,60 @@ int oracle_expert_rows(int n, int d, int f, int E, const void *rows,
         if (expert[r] < 0 || expert[r] >= E) return -1;
     rows_ctx c = {n, d, f, dtype, rows, expert, w1, w3, w2, out};
     parallel_for(n, threads, expert_rows_range, &c);
+    return 0;
+}
+
+typedef struct {
+    int n, d, f, dtype, mode;  /* mode 0: hidden a [n,f] from rows [n,d];
+                                  mode 1: down o [n,d] from rows [n,f] */
+    const void *rows;
+    const int32_t *expert;
+    const void *w1, *w3, *w2;
+    double *out;
+} stage_ctx;
+
+static void stage_range(void *p, int lo, int hi) {
+    stage_ctx *c = (stage_ctx *)p;
+    int in_w = c->mode == 0 ? c->d : c->f;
+    double *xr = malloc(sizeof(double) * in_w);
+    double *u = malloc(sizeof(double) * c->f);
+    if (!xr || !u) { free(xr); free(u); return; }
+    for (int r = lo; r < hi; ++r) {
+        for (int j = 0; j < in_w; ++j)
+            xr[j] = load_elem(c->rows, c->dtype, (size_t)r * in_w + j);
+        if (c->mode == 0)
+            swiglu_hidden(c->d, c->f, xr, c->expert[r], c->w1, c->w3, c->dtype,
+                          c->out + (size_t)r * c->f, u);
+        else
+            swiglu_down(c->d, c->f, xr, c->expert[r], c->w2, c->dtype,
+                        c->out + (size_t)r * c->d);
+    }
+    free(xr); free(u);
+}
+
+/* Step 4a alone: out[r] (fp64 [n,f]) = silu(rows[r] W1[e]) * (rows[r] W3[e]),
+ * e = expert[r].  Returns 0, or -1 on bad sizes / expert ids. */
+int oracle_expert_hidden(int n, int d, int f, int E, const void *rows,
+                         const int32_t *expert, const void *w1, const void *w3,
+                         int dtype, double *out, int threads) {
+    if (n < 0 || d < 1 || f < 1) return -1;
+    for (int r = 0; r < n; ++r)
+        if (expert[r] < 0 || expert[r] >= E) return -1;
+    stage_ctx c = {n, d, f, dtype, 0, rows, expert, w1, w3, NULL, out};
+    parallel_for(n, threads, stage_range, &c);
+    return 0;
+}
+
+/* Step 4b alone: out[r] (fp64 [n,d]) = hid[r] W2[e], hid [n,f] in the
+ * input dtype, e = expert[r].  Returns 0, or -1 on bad sizes / expert ids. */
+int oracle_expert_down(int n, int d, int f, int E, const void *hid,
+                       const int32_t *expert, const void *w2, int dtype,
+                       double *out, int threads) {
+    if (n < 0 || d < 1 || f < 1) return -1;
+    for (int r = 0; r < n; ++r)
+        if (expert[r] < 0 || expert[r] >= E) return -1;
+    stage_ctx c = {n, d, f, dtype, 1, hid, expert, NULL, NULL, w2, out};
+    parallel_for(n, threads, stage_range, &c);
     return 0;
 }
 

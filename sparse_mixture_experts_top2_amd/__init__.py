@@ -1,0 +1,296 @@
+"""Top-2 sparse mixture-of-experts feed-forward layer for AMD Instinct MI355X.
+
+Thin Python binding over ``libmoe.so`` (the C interface declared in
+``include/moe.h``).  This module only checks tensors, allocates outputs and
+workspace with torch, and passes device pointers and the current HIP stream
+to the library; every step of the layer runs in the library's HIP kernels.
+There is no CPU or PyTorch fallback: if the library is missing, calls raise.
+
+Functions mirror the C entry points: ``route``, ``dispatch``,
+``expert_gateup``, ``expert_down``, ``experts``, ``combine``, ``forward`` and
+``workspace_bytes``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+MOE_OK = 0
+STATUS_NAMES = ["MOE_OK", "MOE_ERR_NULL", "MOE_ERR_SHAPE", "MOE_ERR_DTYPE", "MOE_ERR_ALIGN",
+                "MOE_ERR_ALIAS", "MOE_ERR_WORKSPACE", "MOE_ERR_UNSUPPORTED", "MOE_ERR_HIP"]
+EXPORTED = ["moe_status_str", "moe_workspace_bytes", "moe_route", "moe_dispatch",
+            "moe_expert_gateup", "moe_expert_down", "moe_experts", "moe_combine",
+            "moe_forward"]
+
+
+class MoeShape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None):
+    """Load libmoe.so (raises if it is missing: there is no fallback)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"libmoe.so not found at {p}; build it with "
+                           "`python -m sparse_mixture_experts_top2_amd.build`")
+    lib = ctypes.CDLL(p)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    S = ctypes.POINTER(MoeShape)
+    lib.moe_status_str.argtypes = [I]
+    lib.moe_status_str.restype = ctypes.c_char_p
+    lib.moe_workspace_bytes.argtypes = [S]
+    lib.moe_workspace_bytes.restype = Z
+    lib.moe_route.argtypes = [S, P, P, P, P, P]
+    lib.moe_route.restype = I
+    lib.moe_dispatch.argtypes = [S, P, P, P, P, P, P, P]
+    lib.moe_dispatch.restype = I
+    lib.moe_expert_gateup.argtypes = [S, P, P, P, P, P, P, P]
+    lib.moe_expert_gateup.restype = I
+    lib.moe_expert_down.argtypes = [S, P, P, P, P, P, P]
+    lib.moe_expert_down.restype = I
+    lib.moe_experts.argtypes = [S, P, P, P, P, P, P, P, P, Z, P]
+    lib.moe_experts.restype = I
+    lib.moe_combine.argtypes = [S, P, P, P, P, P]
+    lib.moe_combine.restype = I
+    lib.moe_forward.argtypes = [S, P, P, P, P, P, P, P, P, P, Z, P]
+    lib.moe_forward.restype = I
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load_library().moe_status_str(status).decode()
+
+
+class MoeArgumentError(ValueError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def _check(status: int, what: str):
+    """Argument errors raise MoeArgumentError (a ValueError); a failed HIP
+    launch raises MoeError (a RuntimeError)."""
+    if status == MOE_OK:
+        return
+    msg = f"{what}: {status_str(status)}"
+    if status == 8:
+        raise MoeError(status, msg)
+    raise MoeArgumentError(status, msg)
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return MOE_BF16
+    if t == torch.float32:
+        return MOE_F32
+    raise TypeError(f"unsupported dtype {t}; the layer takes float32 or bfloat16")
+
+
+def make_shape(T: int, d: int, f: int, E: int, dtype, top_k: int = 2) -> MoeShape:
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return MoeShape(T, d, f, E, top_k, code)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, device=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (the layer runs only in HIP kernels)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (dense row-major)")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def workspace_bytes(T: int, d: int, f: int, E: int, dtype) -> int:
+    return int(load_library().moe_workspace_bytes(ctypes.byref(make_shape(T, d, f, E, dtype))))
+
+
+def alloc_workspace(T: int, d: int, f: int, E: int, dtype, device) -> torch.Tensor:
+    n = workspace_bytes(T, d, f, E, dtype)
+    if n == 0:
+        raise ValueError("invalid layer shape")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def route(x: torch.Tensor, w_gate: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Router: returns (topk_idx int32 [T,2], topk_w fp32 [T,2])."""
+    _need(x, "x")
+    T, d = x.shape
+    _need(w_gate, "w_gate", x.dtype, x.device)
+    E = w_gate.shape[1]
+    _need(w_gate, "w_gate", shape=(d, E))
+    idx = torch.empty(T, 2, dtype=torch.int32, device=x.device)
+    w = torch.empty(T, 2, dtype=torch.float32, device=x.device)
+    shape = make_shape(T, d, 8, E, x.dtype)
+    st = load_library().moe_route(ctypes.byref(shape), _ptr(x), _ptr(w_gate), _ptr(idx), _ptr(w),
+                                  _stream(x.device))
+    _check(st, "moe_route")
+    return idx, w
+
+
+def dispatch(x: torch.Tensor, topk_idx: torch.Tensor, n_experts: int):
+    """Stable grouping by expert: returns (counts [E], offsets [E+1],
+    pos [T,2], xp [2T,d])."""
+    _need(x, "x")
+    T, d = x.shape
+    _need(topk_idx, "topk_idx", torch.int32, x.device, (T, 2))
+    dev = x.device
+    counts = torch.empty(n_experts, dtype=torch.int32, device=dev)
+    offsets = torch.empty(n_experts + 1, dtype=torch.int32, device=dev)
+    pos = torch.empty(T, 2, dtype=torch.int32, device=dev)
+    xp = torch.empty(2 * T, d, dtype=x.dtype, device=dev)
+    shape = make_shape(T, d, 8, n_experts, x.dtype)
+    st = load_library().moe_dispatch(ctypes.byref(shape), _ptr(x), _ptr(topk_idx), _ptr(counts),
+                                     _ptr(offsets), _ptr(pos), _ptr(xp), _stream(dev))
+    _check(st, "moe_dispatch")
+    return counts, offsets, pos, xp
+
+
+def _expert_args(xp, counts, offsets, w, w_name):
+    _need(xp, "xp")
+    R, k_in = xp.shape
+    if R % 2:
+        raise ValueError("xp / h must have 2T rows")
+    _need(w, w_name, xp.dtype, xp.device)
+    E = w.shape[0]
+    _need(counts, "counts", torch.int32, xp.device, (E,))
+    _need(offsets, "offsets", torch.int32, xp.device, (E + 1,))
+    return R // 2, k_in, E
+
+
+def expert_gateup(xp: torch.Tensor, counts: torch.Tensor, offsets: torch.Tensor,
+                  w1: torch.Tensor, w3: torch.Tensor, out: Optional[torch.Tensor] = None):
+    """h = silu(xp w1[e]) * (xp w3[e]) per expert row group; [2T, f]."""
+    T, d, E = _expert_args(xp, counts, offsets, w1, "w1")
+    f = w1.shape[2]
+    _need(w1, "w1", shape=(E, d, f))
+    _need(w3, "w3", xp.dtype, xp.device, (E, d, f))
+    h = out if out is not None else torch.empty(2 * T, f, dtype=xp.dtype, device=xp.device)
+    _need(h, "h", xp.dtype, xp.device, (2 * T, f))
+    shape = make_shape(T, d, f, E, xp.dtype)
+    st = load_library().moe_expert_gateup(ctypes.byref(shape), _ptr(xp), _ptr(counts),
+                                          _ptr(offsets), _ptr(w1), _ptr(w3), _ptr(h),
+                                          _stream(xp.device))
+    _check(st, "moe_expert_gateup")
+    return h
+
+
+def expert_down(h: torch.Tensor, counts: torch.Tensor, offsets: torch.Tensor, w2: torch.Tensor,
+                out: Optional[torch.Tensor] = None):
+    """o = h w2[e] per expert row group; fp32 [2T, d]."""
+    T, f, E = _expert_args(h, counts, offsets, w2, "w2")
+    d = w2.shape[2]
+    _need(w2, "w2", shape=(E, f, d))
+    o = out if out is not None else torch.empty(2 * T, d, dtype=torch.float32, device=h.device)
+    _need(o, "o", torch.float32, h.device, (2 * T, d))
+    shape = make_shape(T, d, f, E, h.dtype)
+    st = load_library().moe_expert_down(ctypes.byref(shape), _ptr(h), _ptr(counts), _ptr(offsets),
+                                        _ptr(w2), _ptr(o), _stream(h.device))
+    _check(st, "moe_expert_down")
+    return o
+
+
+def experts(xp: torch.Tensor, counts: torch.Tensor, offsets: torch.Tensor, w1: torch.Tensor,
+            w3: torch.Tensor, w2: torch.Tensor, workspace: Optional[torch.Tensor] = None):
+    """Grouped SwiGLU over expert-sorted rows: returns o fp32 [2T, d]."""
+    _need(xp, "xp")
+    R, d = xp.shape
+    if R % 2:
+        raise ValueError("xp must have 2T rows")
+    T = R // 2
+    _need(w1, "w1", xp.dtype, xp.device)
+    E, _, f = w1.shape
+    _need(w1, "w1", shape=(E, d, f))
+    _need(w3, "w3", xp.dtype, xp.device, (E, d, f))
+    _need(w2, "w2", xp.dtype, xp.device, (E, f, d))
+    _need(counts, "counts", torch.int32, xp.device, (E,))
+    _need(offsets, "offsets", torch.int32, xp.device, (E + 1,))
+    ws = workspace if workspace is not None else alloc_workspace(T, d, f, E, xp.dtype, xp.device)
+    o = torch.empty(R, d, dtype=torch.float32, device=xp.device)
+    shape = make_shape(T, d, f, E, xp.dtype)
+    st = load_library().moe_experts(ctypes.byref(shape), _ptr(xp), _ptr(counts), _ptr(offsets),
+                                    _ptr(w1), _ptr(w3), _ptr(w2), _ptr(o), _ptr(ws),
+                                    ws.numel(), _stream(xp.device))
+    _check(st, "moe_experts")
+    return o
+
+
+def combine(o: torch.Tensor, pos: torch.Tensor, topk_w: torch.Tensor, dtype) -> torch.Tensor:
+    """y[t] = w[t,0] o[pos[t,0]] + w[t,1] o[pos[t,1]], as ``dtype``."""
+    _need(o, "o", torch.float32)
+    R, d = o.shape
+    T = R // 2
+    _need(pos, "pos", torch.int32, o.device, (T, 2))
+    _need(topk_w, "topk_w", torch.float32, o.device, (T, 2))
+    y = torch.empty(T, d, dtype=dtype, device=o.device)
+    shape = make_shape(T, d, 8, 2, dtype)
+    st = load_library().moe_combine(ctypes.byref(shape), _ptr(o), _ptr(pos), _ptr(topk_w), _ptr(y),
+                                    _stream(o.device))
+    _check(st, "moe_combine")
+    return y
+
+
+def forward(x: torch.Tensor, w_gate: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor,
+            w2: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+            return_routing: bool = False, out: Optional[torch.Tensor] = None):
+    """The whole layer.  Returns y [T, d] (and (topk_idx, topk_w) when
+    ``return_routing``)."""
+    _need(x, "x")
+    T, d = x.shape
+    _need(w_gate, "w_gate", x.dtype, x.device)
+    E = w_gate.shape[1]
+    _need(w_gate, "w_gate", shape=(d, E))
+    _need(w1, "w1", x.dtype, x.device)
+    f = w1.shape[2]
+    _need(w1, "w1", shape=(E, d, f))
+    _need(w3, "w3", x.dtype, x.device, (E, d, f))
+    _need(w2, "w2", x.dtype, x.device, (E, f, d))
+    ws = workspace if workspace is not None else alloc_workspace(T, d, f, E, x.dtype, x.device)
+    y = out if out is not None else torch.empty(T, d, dtype=x.dtype, device=x.device)
+    _need(y, "out", x.dtype, x.device, (T, d))
+    idx = w = None
+    if return_routing:
+        idx = torch.empty(T, 2, dtype=torch.int32, device=x.device)
+        w = torch.empty(T, 2, dtype=torch.float32, device=x.device)
+    shape = make_shape(T, d, f, E, x.dtype)
+    st = load_library().moe_forward(ctypes.byref(shape), _ptr(x), _ptr(w_gate), _ptr(w1), _ptr(w3),
+                                    _ptr(w2), _ptr(y), _ptr(idx), _ptr(w), _ptr(ws), ws.numel(),
+                                    _stream(x.device))
+    _check(st, "moe_forward")
+    return (y, idx, w) if return_routing else y

@@ -1,0 +1,237 @@
+// C interface of libmoe: argument checks, workspace planning and the launch
+// sequence of the layer (route -> dispatch -> experts -> combine), all
+// enqueued on the caller's stream with no host synchronisation.  The
+// contract of every entry point is stated in include/moe.h.
+#include <string.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+Layout plan_workspace(const moe_shape_t &s) {
+    Layout L{};
+    const size_t T = (size_t)s.T, d = (size_t)s.d_model, f = (size_t)s.d_ff;
+    const size_t E = (size_t)s.n_experts, eb = elem_bytes(s.dtype);
+    const size_t rows = 2 * T;
+    size_t off = 0;
+    L.idx = off;     off += align256(T * 2 * sizeof(int32_t));
+    L.w = off;       off += align256(T * 2 * sizeof(float));
+    L.counts = off;  off += align256(E * sizeof(int32_t));
+    L.offsets = off; off += align256((E + 1) * sizeof(int32_t));
+    L.pos = off;     off += align256(T * 2 * sizeof(int32_t));
+    L.xp = off;      off += align256(rows * d * eb);
+    L.h = off;       off += align256(rows * f * eb);
+    L.o = off;       off += align256(2 * T * d * sizeof(float));
+    L.total = off;
+    return L;
+}
+
+hipError_t launch_gateup(const moe_shape_t &s, const void *xp, const int32_t *counts,
+                         const int32_t *offsets, const void *w1, const void *w3, void *h,
+                         hipStream_t stream) {
+    if (s.T == 0) return hipSuccess;
+    if (s.dtype == MOE_F32)
+        return launch_gateup_f32(s, static_cast<const float *>(xp), counts, offsets,
+                                 static_cast<const float *>(w1), static_cast<const float *>(w3),
+                                 static_cast<float *>(h), stream);
+    return launch_gateup_bf16(s, static_cast<const uint16_t *>(xp), counts, offsets,
+                              static_cast<const uint16_t *>(w1),
+                              static_cast<const uint16_t *>(w3), static_cast<uint16_t *>(h),
+                              stream);
+}
+
+hipError_t launch_down(const moe_shape_t &s, const void *h, const int32_t *counts,
+                       const int32_t *offsets, const void *w2, float *o, hipStream_t stream) {
+    if (s.T == 0) return hipSuccess;
+    if (s.dtype == MOE_F32)
+        return launch_down_f32(s, static_cast<const float *>(h), counts, offsets,
+                               static_cast<const float *>(w2), o, stream);
+    return launch_down_bf16(s, static_cast<const uint16_t *>(h), counts, offsets,
+                            static_cast<const uint16_t *>(w2), o, stream);
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+namespace {
+
+int check_shape(const moe_shape_t *s) {
+    if (!s) return MOE_ERR_NULL;
+    if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_ERR_DTYPE;
+    if (s->top_k != 2) return MOE_ERR_UNSUPPORTED;
+    if (s->n_experts < 2 || s->n_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+    if (s->T < 0 || s->d_model < 8 || s->d_ff < 8) return MOE_ERR_SHAPE;
+    if (s->d_model % 8 != 0 || s->d_ff % 8 != 0) return MOE_ERR_SHAPE;
+    // Keep every element index of the largest array inside 2^31 * 16 bytes
+    // of address arithmetic done in size_t, and row counts inside int32.
+    if ((int64_t)s->T > (1 << 29)) return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+bool misaligned(const void *p) { return ((uintptr_t)p & 15u) != 0; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_str(int status) {
+    switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_NULL: return "MOE_ERR_NULL: a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE: T < 0, or d_model / d_ff not a positive multiple of 8";
+    case MOE_ERR_DTYPE: return "MOE_ERR_DTYPE: dtype must be MOE_F32 or MOE_BF16";
+    case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN: device pointers must be 16-byte aligned";
+    case MOE_ERR_ALIAS: return "MOE_ERR_ALIAS: an output overlaps an input";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or smaller than moe_workspace_bytes";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: top_k must be 2 and n_experts in [2, 32]";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP kernel launch failed";
+    default: return "unknown moe status";
+    }
+}
+
+size_t moe_workspace_bytes(const moe_shape_t *s) {
+    if (check_shape(s) != MOE_OK) return 0;
+    return plan_workspace(*s).total;
+}
+
+int moe_route(const moe_shape_t *s, const void *x, const void *w_gate, int32_t *topk_idx,
+              float *topk_w, void *stream) {
+    int st = check_shape(s);
+    if (st) return st;
+    if (s->T == 0) return MOE_OK;  // nothing to read or write
+    if (!x || !w_gate || !topk_idx || !topk_w) return MOE_ERR_NULL;
+    if (misaligned(x) || misaligned(w_gate) || misaligned(topk_idx) || misaligned(topk_w))
+        return MOE_ERR_ALIGN;
+    return hip_status(launch_route(*s, x, w_gate, topk_idx, topk_w, (hipStream_t)stream));
+}
+
+int moe_dispatch(const moe_shape_t *s, const void *x, const int32_t *topk_idx, int32_t *counts,
+                 int32_t *offsets, int32_t *pos, void *xp, void *stream) {
+    int st = check_shape(s);
+    if (st) return st;
+    if (s->T == 0) return MOE_OK;  // nothing to read or write
+    if (!x || !topk_idx || !counts || !offsets || !pos || !xp) return MOE_ERR_NULL;
+    if (misaligned(x) || misaligned(topk_idx) || misaligned(counts) || misaligned(offsets) ||
+        misaligned(pos) || misaligned(xp))
+        return MOE_ERR_ALIGN;
+    const size_t row = (size_t)s->d_model * elem_bytes(s->dtype);
+    if (overlap(xp, 2 * (size_t)s->T * row, x, (size_t)s->T * row)) return MOE_ERR_ALIAS;
+    return hip_status(
+        launch_dispatch(*s, x, topk_idx, counts, offsets, pos, xp, (hipStream_t)stream));
+}
+
+int moe_expert_gateup(const moe_shape_t *s, const void *xp, const int32_t *counts,
+                      const int32_t *offsets, const void *w1, const void *w3, void *h,
+                      void *stream) {
+    int st = check_shape(s);
+    if (st) return st;
+    if (s->T == 0) return MOE_OK;  // nothing to read or write
+    if (!xp || !counts || !offsets || !w1 || !w3 || !h) return MOE_ERR_NULL;
+    if (misaligned(xp) || misaligned(counts) || misaligned(offsets) || misaligned(w1) ||
+        misaligned(w3) || misaligned(h))
+        return MOE_ERR_ALIGN;
+    const size_t eb = elem_bytes(s->dtype);
+    if (overlap(h, 2 * (size_t)s->T * s->d_ff * eb, xp, 2 * (size_t)s->T * s->d_model * eb))
+        return MOE_ERR_ALIAS;
+    return hip_status(launch_gateup(*s, xp, counts, offsets, w1, w3, h, (hipStream_t)stream));
+}
+
+int moe_expert_down(const moe_shape_t *s, const void *h, const int32_t *counts,
+                    const int32_t *offsets, const void *w2, float *o, void *stream) {
+    int st = check_shape(s);
+    if (st) return st;
+    if (s->T == 0) return MOE_OK;  // nothing to read or write
+    if (!h || !counts || !offsets || !w2 || !o) return MOE_ERR_NULL;
+    if (misaligned(h) || misaligned(counts) || misaligned(offsets) || misaligned(w2) ||
+        misaligned(o))
+        return MOE_ERR_ALIGN;
+    const size_t eb = elem_bytes(s->dtype);
+    if (overlap(o, 2 * (size_t)s->T * s->d_model * sizeof(float), h,
+                2 * (size_t)s->T * s->d_ff * eb))
+        return MOE_ERR_ALIAS;
+    return hip_status(launch_down(*s, h, counts, offsets, w2, o, (hipStream_t)stream));
+}
+
+int moe_experts(const moe_shape_t *s, const void *xp, const int32_t *counts,
+                const int32_t *offsets, const void *w1, const void *w3, const void *w2, float *o,
+                void *ws, size_t ws_bytes, void *stream) {
+    int st = check_shape(s);
+    if (st) return st;
+    if (s->T == 0) return MOE_OK;  // nothing to read or write
+    if (!xp || !counts || !offsets || !w1 || !w3 || !w2 || !o) return MOE_ERR_NULL;
+    if (misaligned(xp) || misaligned(counts) || misaligned(offsets) || misaligned(w1) ||
+        misaligned(w3) || misaligned(w2) || misaligned(o))
+        return MOE_ERR_ALIGN;
+    const Layout L = plan_workspace(*s);
+    if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    if (misaligned(ws)) return MOE_ERR_ALIGN;
+    const size_t o_bytes = 2 * (size_t)s->T * s->d_model * sizeof(float);
+    if (overlap(o, o_bytes, xp, 2 * (size_t)s->T * s->d_model * elem_bytes(s->dtype)))
+        return MOE_ERR_ALIAS;
+    void *h = static_cast<char *>(ws) + L.h;
+    hipStream_t str = (hipStream_t)stream;
+    hipError_t e = launch_gateup(*s, xp, counts, offsets, w1, w3, h, str);
+    if (e == hipSuccess) e = launch_down(*s, h, counts, offsets, w2, o, str);
+    return hip_status(e);
+}
+
+int moe_combine(const moe_shape_t *s, const float *o, const int32_t *pos, const float *topk_w,
+                void *y, void *stream) {
+    int st = check_shape(s);
+    if (st) return st;
+    if (s->T == 0) return MOE_OK;  // nothing to read or write
+    if (!o || !pos || !topk_w || !y) return MOE_ERR_NULL;
+    if (misaligned(o) || misaligned(pos) || misaligned(topk_w) || misaligned(y))
+        return MOE_ERR_ALIGN;
+    const size_t y_bytes = (size_t)s->T * s->d_model * elem_bytes(s->dtype);
+    if (overlap(y, y_bytes, o, 2 * (size_t)s->T * s->d_model * sizeof(float)))
+        return MOE_ERR_ALIAS;
+    return hip_status(launch_combine(*s, o, pos, topk_w, y, (hipStream_t)stream));
+}
+
+int moe_forward(const moe_shape_t *s, const void *x, const void *w_gate, const void *w1,
+                const void *w3, const void *w2, void *y, int32_t *topk_idx_opt,
+                float *topk_w_opt, void *ws, size_t ws_bytes, void *stream) {
+    int st = check_shape(s);
+    if (st) return st;
+    if (s->T == 0) return MOE_OK;  // nothing to read or write
+    if (!x || !w_gate || !w1 || !w3 || !w2 || !y) return MOE_ERR_NULL;
+    if (misaligned(x) || misaligned(w_gate) || misaligned(w1) || misaligned(w3) ||
+        misaligned(w2) || misaligned(y) || misaligned(topk_idx_opt) || misaligned(topk_w_opt))
+        return MOE_ERR_ALIGN;
+    const Layout L = plan_workspace(*s);
+    if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    if (misaligned(ws)) return MOE_ERR_ALIGN;
+    const size_t act = (size_t)s->T * s->d_model * elem_bytes(s->dtype);
+    if (overlap(y, act, x, act)) return MOE_ERR_ALIAS;
+
+    hipStream_t str = (hipStream_t)stream;
+    char *base = static_cast<char *>(ws);
+    int32_t *idx = topk_idx_opt ? topk_idx_opt : reinterpret_cast<int32_t *>(base + L.idx);
+    float *w = topk_w_opt ? topk_w_opt : reinterpret_cast<float *>(base + L.w);
+    int32_t *counts = reinterpret_cast<int32_t *>(base + L.counts);
+    int32_t *offsets = reinterpret_cast<int32_t *>(base + L.offsets);
+    int32_t *pos = reinterpret_cast<int32_t *>(base + L.pos);
+    void *xp = base + L.xp;
+    void *h = base + L.h;
+    float *o = reinterpret_cast<float *>(base + L.o);
+
+    hipError_t e = launch_route(*s, x, w_gate, idx, w, str);
+    if (e == hipSuccess) e = launch_dispatch(*s, x, idx, counts, offsets, pos, xp, str);
+    if (e == hipSuccess) e = launch_gateup(*s, xp, counts, offsets, w1, w3, h, str);
+    if (e == hipSuccess) e = launch_down(*s, h, counts, offsets, w2, o, str);
+    if (e == hipSuccess) e = launch_combine(*s, o, pos, w, y, str);
+    return hip_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// Combine: y[t] = w[t,0] * o[pos[t,0]] + w[t,1] * o[pos[t,1]], slot 0 then
+// slot 1, fp32 math, rounded once to y's dtype.  "Mixtral 8x7B -- The
+// Evolving Transformer", section 05: the formula y = sum_k w_k E_{i_k}(x),
+// and the MoE module's accumulation of each slot's weighted expert output
+// into a zeroed output.  Here every row of y is written exactly once by a
+// gather, so no zero fill and no atomics are needed and the result does not
+// depend on scheduling.  One wavefront per token, 16-byte fp32 loads; bound
+// by HBM (2*T*d*4 bytes read, T*d*elem written).
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+template <bool BF16_OUT>
+__global__ __launch_bounds__(256) void combine_kernel(const float4 *__restrict__ o,
+                                                      const int32_t *__restrict__ pos,
+                                                      const float *__restrict__ w, int n_tok,
+                                                      int d4, void *__restrict__ y) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= n_tok) return;
+    const float4 *r0 = o + (size_t)pos[2 * t] * d4;
+    const float4 *r1 = o + (size_t)pos[2 * t + 1] * d4;
+    const float w0 = w[2 * t], w1 = w[2 * t + 1];
+    for (int j = lane; j < d4; j += 64) {
+        const float4 a = r0[j], b = r1[j];
+        float4 v;
+        v.x = w0 * a.x + w1 * b.x;
+        v.y = w0 * a.y + w1 * b.y;
+        v.z = w0 * a.z + w1 * b.z;
+        v.w = w0 * a.w + w1 * b.w;
+        if (BF16_OUT) {
+            uint2 p;
+            p.x = f32_to_bf16(v.x) | (f32_to_bf16(v.y) << 16);
+            p.y = f32_to_bf16(v.z) | (f32_to_bf16(v.w) << 16);
+            reinterpret_cast<uint2 *>(y)[(size_t)t * d4 + j] = p;
+        } else {
+            reinterpret_cast<float4 *>(y)[(size_t)t * d4 + j] = v;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const moe_shape_t &s, const float *o, const int32_t *pos,
+                          const float *w, void *y, hipStream_t stream) {
+    if (s.T == 0) return hipSuccess;
+    const int d4 = s.d_model / 4;
+    const dim3 grid((s.T + 3) / 4), block(256);
+    if (s.dtype == MOE_BF16)
+        hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, stream,
+                           reinterpret_cast<const float4 *>(o), pos, w, s.T, d4, y);
+    else
+        hipLaunchKernelGGL(combine_kernel<false>, grid, block, 0, stream,
+                           reinterpret_cast<const float4 *>(o), pos, w, s.T, d4, y);
+    return hipGetLastError();
+}
+
+}  // namespace moe

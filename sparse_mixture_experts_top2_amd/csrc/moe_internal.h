@@ -1,0 +1,108 @@
+// Internal declarations shared by the HIP translation units of libmoe:
+// workspace planning, device helpers and the kernel launchers that the
+// C interface (abi.hip) sequences.  Not installed; include/moe.h is the
+// public surface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kMaxExperts = 32;
+// Token counts up to this use the weight-streaming (decode) expert kernels;
+// an expert then has at most 32 rows (a token never picks one expert twice).
+constexpr int kDecodeMaxT = 32;
+
+struct Layout {
+    size_t idx, w, counts, offsets, pos, xp, h, o, total;
+};
+
+// Byte offsets of every workspace region for this shape (256-byte aligned).
+Layout plan_workspace(const moe_shape_t &s);
+
+inline size_t elem_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
+
+// ---------------------------------------------------------------------------
+// Kernel launchers.  Each enqueues on `stream` and returns hipGetLastError().
+
+hipError_t launch_route(const moe_shape_t &s, const void *x, const void *w_gate,
+                        int32_t *idx, float *w, hipStream_t stream);
+
+hipError_t launch_dispatch(const moe_shape_t &s, const void *x, const int32_t *idx,
+                           int32_t *counts, int32_t *offsets, int32_t *pos, void *xp,
+                           hipStream_t stream);
+
+// Grouped SwiGLU over expert-sorted rows, in two launches:
+//   gate/up: h = silu(xp w1[e]) * (xp w3[e])    (h in the layer dtype)
+//   down:    o = h w2[e]                          (o fp32)
+hipError_t launch_gateup(const moe_shape_t &s, const void *xp, const int32_t *counts,
+                         const int32_t *offsets, const void *w1, const void *w3, void *h,
+                         hipStream_t stream);
+hipError_t launch_down(const moe_shape_t &s, const void *h, const int32_t *counts,
+                       const int32_t *offsets, const void *w2, float *o, hipStream_t stream);
+
+hipError_t launch_combine(const moe_shape_t &s, const float *o, const int32_t *pos,
+                          const float *w, void *y, hipStream_t stream);
+
+// Per-dtype expert launchers (experts_f32.hip, experts_bf16.hip).  The bf16
+// ones pick the weight-streaming kernels for T <= kDecodeMaxT.
+hipError_t launch_gateup_f32(const moe_shape_t &s, const float *xp, const int32_t *counts,
+                             const int32_t *offsets, const float *w1, const float *w3,
+                             float *h, hipStream_t stream);
+hipError_t launch_down_f32(const moe_shape_t &s, const float *h, const int32_t *counts,
+                           const int32_t *offsets, const float *w2, float *o,
+                           hipStream_t stream);
+hipError_t launch_gateup_bf16(const moe_shape_t &s, const uint16_t *xp, const int32_t *counts,
+                              const int32_t *offsets, const uint16_t *w1, const uint16_t *w3,
+                              uint16_t *h, hipStream_t stream);
+hipError_t launch_down_bf16(const moe_shape_t &s, const uint16_t *h, const int32_t *counts,
+                            const int32_t *offsets, const uint16_t *w2, float *o,
+                            hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Device helpers.
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16 with round-to-nearest-even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float v) {
+    uint32_t u = __float_as_uint(v);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+
+// Row-group lookup for grouped GEMMs.  Expert e owns ceil(counts[e]/bm)
+// row tiles, laid out expert after expert.  Maps the flat tile number `mt`
+// to (expert, first row, end row); returns false past the last tile.
+__device__ __forceinline__ bool find_row_tile(const int32_t *counts, const int32_t *offsets,
+                                              int E, int bm, int mt, int &e_out,
+                                              int &row0, int &row_end) {
+    int acc = 0;
+    for (int e = 0; e < E; ++e) {
+        int c = counts[e];
+        int nt = (c + bm - 1) / bm;
+        if (mt < acc + nt) {
+            e_out = e;
+            row0 = offsets[e] + (mt - acc) * bm;
+            row_end = offsets[e] + c;
+            return true;
+        }
+        acc += nt;
+    }
+    return false;
+}
+
+}  // namespace moe

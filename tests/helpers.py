@@ -1,0 +1,39 @@
+"""Shared test helpers: seeded inputs with near-tie screening (the screen
+uses the oracle's router), error metrics and tolerances."""
+import numpy as np
+import torch
+
+import oracle
+from sparse_mixture_experts_top2_amd import workloads as W
+
+# Output tolerance, row-max-normalised: max_t max_m |y - ref| / max_m |ref|.
+# bf16 I/O with fp32 accumulation: 2e-2; fp32 layers: 1e-5.
+Y_TOL = {W.F32: 1e-5, W.BF16: 2e-2}
+# Routing weight tolerance (absolute).
+RW_TOL = {W.F32: 1e-5, W.BF16: 1e-4}
+
+
+def checked_inputs(wl, seed=None, device="cpu"):
+    """Seeded inputs whose routing decisions have a clear margin (every
+    token's 1st/2nd and 2nd/3rd logits differ by at least 1e-3)."""
+    return W.make_inputs(wl, seed, gap_fn=oracle.near_tie_tokens, device=device)
+
+
+def to_f64(t) -> np.ndarray:
+    if isinstance(t, torch.Tensor):
+        return t.detach().float().cpu().numpy().astype(np.float64)
+    return np.asarray(t, np.float64)
+
+
+def row_max_rel_err(y, ref) -> float:
+    y = to_f64(y)
+    ref = to_f64(ref)
+    if y.size == 0:
+        return 0.0
+    num = np.abs(y - ref).max(axis=1)
+    den = np.abs(ref).max(axis=1)
+    return float((num / np.maximum(den, 1e-30)).max())
+
+
+def bf16_bits(t: torch.Tensor) -> torch.Tensor:
+    return t.contiguous().view(torch.int16)

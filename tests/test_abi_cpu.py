@@ -1,0 +1,111 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point that
+include/moe.h declares, and rejects bad arguments before touching any
+device memory (every call here returns from its argument checks)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import sparse_mixture_experts_top2_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+P16 = ctypes.c_void_p(0x10000)   # aligned fake pointers: never dereferenced here
+P16B = ctypes.c_void_p(0x90000000)
+P17 = ctypes.c_void_p(0x10001)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(moe.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (moe_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(moe.load_library(), name)
+
+
+def shape(T=64, d=128, f=256, E=8, k=2, dtype=moe.MOE_BF16):
+    return moe.MoeShape(T, d, f, E, k, dtype)
+
+
+def call_forward(s, ws_bytes=1 << 40, x=P16, y=P16B, ws=P16):
+    lib = moe.load_library()
+    return lib.moe_forward(ctypes.byref(s) if s is not None else None, x, P16, P16, P16, P16, y,
+                           None, None, ws, ws_bytes, None)
+
+
+def test_status_strings():
+    for code, name in enumerate(moe.STATUS_NAMES):
+        assert moe.status_str(code).startswith(name)
+    assert moe.status_str(99) == "unknown moe status"
+
+
+@pytest.mark.parametrize("bad,expect", [
+    (dict(k=1), "MOE_ERR_UNSUPPORTED"), (dict(k=3), "MOE_ERR_UNSUPPORTED"),
+    (dict(E=1), "MOE_ERR_UNSUPPORTED"), (dict(E=33), "MOE_ERR_UNSUPPORTED"),
+    (dict(T=-1), "MOE_ERR_SHAPE"), (dict(d=100), "MOE_ERR_SHAPE"), (dict(f=12), "MOE_ERR_SHAPE"),
+    (dict(d=0), "MOE_ERR_SHAPE"), (dict(dtype=7), "MOE_ERR_DTYPE"),
+])
+def test_shape_checks(bad, expect):
+    s = shape(**bad)
+    st = call_forward(s)
+    assert moe.STATUS_NAMES[st] == expect
+    assert moe.load_library().moe_workspace_bytes(ctypes.byref(s)) == 0
+
+
+def test_null_alignment_alias_workspace_checks():
+    lib = moe.load_library()
+    s = shape()
+    need = lib.moe_workspace_bytes(ctypes.byref(s))
+    assert need > 0
+    assert moe.STATUS_NAMES[call_forward(None)] == "MOE_ERR_NULL"
+    assert moe.STATUS_NAMES[call_forward(s, x=None)] == "MOE_ERR_NULL"
+    assert moe.STATUS_NAMES[call_forward(s, x=P17)] == "MOE_ERR_ALIGN"
+    assert moe.STATUS_NAMES[call_forward(s, y=P16)] == "MOE_ERR_ALIAS"
+    assert moe.STATUS_NAMES[call_forward(s, ws_bytes=need - 1)] == "MOE_ERR_WORKSPACE"
+    assert moe.STATUS_NAMES[call_forward(s, ws=None)] == "MOE_ERR_WORKSPACE"
+    st = lib.moe_route(ctypes.byref(s), P16, P16, P17, P16, None)
+    assert moe.STATUS_NAMES[st] == "MOE_ERR_ALIGN"
+    st = lib.moe_dispatch(ctypes.byref(s), P16, P16, P16, P16, P16, P16, None)
+    assert moe.STATUS_NAMES[st] == "MOE_ERR_ALIAS"
+    st = lib.moe_combine(ctypes.byref(s), P16, P16, P16, None, None)
+    assert moe.STATUS_NAMES[st] == "MOE_ERR_NULL"
+    st = lib.moe_experts(ctypes.byref(s), P16, P16, P16, P16, P16, P16, P16B, P16, 16, None)
+    assert moe.STATUS_NAMES[st] == "MOE_ERR_WORKSPACE"
+
+
+def test_zero_tokens_is_a_valid_no_op():
+    # T = 0 passes every check and returns before any HIP call.
+    s = shape(T=0)
+    assert moe.load_library().moe_workspace_bytes(ctypes.byref(s)) > 0
+    assert call_forward(s) == moe.MOE_OK
+
+
+def test_workspace_grows_with_every_dimension():
+    lib = moe.load_library()
+    base = lib.moe_workspace_bytes(ctypes.byref(shape()))
+    for kw in (dict(T=65), dict(d=136), dict(f=264), dict(dtype=moe.MOE_F32)):
+        assert lib.moe_workspace_bytes(ctypes.byref(shape(**kw))) > base, kw
+    # decode shape: xp 64 x 4096 bf16, h 64 x 14336 bf16, o 64 x 4096 fp32 and small tables
+    s = shape(T=32, d=4096, f=14336)
+    assert lib.moe_workspace_bytes(ctypes.byref(s)) >= 64 * (4096 * 2 + 14336 * 2 + 4096 * 4)
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        moe.route(x, torch.zeros(16, 8, dtype=torch.bfloat16))

@@ -1,0 +1,231 @@
+"""GPU parity: the HIP library (through its C interface) against the CPU
+oracle on the same seeded inputs.
+
+Bars: routing indices and every integer output bit-exact; routing weights
+within 1e-5 (fp32) / 1e-4 (bf16) absolute; layer outputs within a
+row-max-normalised error of 1e-5 (fp32) / 2e-2 (bf16 I/O, fp32 accumulation).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_mixture_experts_top2_amd as moe
+from sparse_mixture_experts_top2_amd import workloads as W
+
+from helpers import RW_TOL, Y_TOL, checked_inputs, row_max_rel_err, to_f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def announce(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+
+
+def check_routing(inp, idx_g, w_g, dtype):
+    idx_o, w_o = oracle.route(inp.x, inp.w_gate)
+    np.testing.assert_array_equal(idx_g.cpu().numpy(), idx_o)
+    np.testing.assert_allclose(w_g.cpu().numpy(), w_o, rtol=0, atol=RW_TOL[dtype])
+    return idx_o, w_o
+
+
+def run_forward_parity(inp, sample=None):
+    wl = inp.wl
+    g = inp.to(DEV)
+    y, idx, w = moe.forward(g.x, g.w_gate, g.w1, g.w3, g.w2, return_routing=True)
+    torch.cuda.synchronize()
+    idx_o, _ = check_routing(inp, idx, w, wl.dtype)
+    rows = np.arange(wl.T) if sample is None else np.asarray(sample)
+    y_o, idx_s, _ = oracle.forward(inp.x[rows], inp.w_gate, inp.w1, inp.w3, inp.w2)
+    np.testing.assert_array_equal(idx_s, idx_o[rows])
+    err = row_max_rel_err(y[torch.as_tensor(rows, device=DEV)], y_o)
+    announce(f"{wl.name} T={wl.T} rows={len(rows)} row-max-rel err {err:.3e}")
+    assert err <= Y_TOL[wl.dtype], err
+    return y, idx_o
+
+
+SMALL = [
+    W.WORKLOADS["tiny_fp32"],
+    W.small_workload(50, 72, 40, dtype=W.F32, seed=3),
+    W.small_workload(1, 128, 256, seed=4),
+    W.small_workload(7, 128, 256, seed=5),
+    W.small_workload(16, 256, 512, seed=6),
+    W.small_workload(32, 256, 512, seed=7),
+    W.small_workload(20, 200, 328, seed=8),
+    W.small_workload(33, 256, 512, seed=9),
+    W.small_workload(77, 192, 264, seed=10),
+    W.small_workload(300, 256, 512, seed=11),
+    W.small_workload(700, 256, 384, seed=12),
+    W.small_workload(100, 200, 328, seed=13),
+    W.small_workload(200, 128, 256, E=2, seed=14),
+    W.small_workload(200, 128, 256, E=4, seed=15),
+    W.small_workload(150, 128, 256, E=16, seed=16),
+    W.small_workload(150, 128, 256, E=32, seed=17),
+    W.small_workload(24, 128, 256, E=32, seed=18),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: w.name)
+def test_forward_small(wl):
+    announce(f"forward {wl.name}")
+    run_forward_parity(checked_inputs(wl))
+
+
+STEP_CASES = [SMALL[0], SMALL[1], SMALL[5], SMALL[6], SMALL[9], SMALL[11], SMALL[15]]
+
+
+@pytest.mark.parametrize("wl", STEP_CASES, ids=lambda w: w.name)
+def test_each_step(wl):
+    """route -> dispatch -> gate/up -> down -> combine, each step on its own
+    against the oracle.  Every step's inputs come from the generator or from
+    the oracle's previous step, never from a GPU output."""
+    announce(f"steps {wl.name}")
+    inp = checked_inputs(wl)
+    g = inp.to(DEV)
+    tdt = g.x.dtype
+    # route
+    idx, w = moe.route(g.x, g.w_gate)
+    idx_o, w_o = check_routing(inp, idx, w, wl.dtype)
+    # dispatch
+    counts, offsets, pos, xp = moe.dispatch(g.x, torch.as_tensor(idx_o, device=DEV), wl.E)
+    c_o, off_o, pos_o, src_o = oracle.dispatch(idx_o, wl.E)
+    np.testing.assert_array_equal(counts.cpu().numpy(), c_o)
+    np.testing.assert_array_equal(offsets.cpu().numpy(), off_o)
+    np.testing.assert_array_equal(pos.cpu().numpy(), pos_o)
+    xp_o = inp.x[torch.as_tensor(src_o // 2)].contiguous()
+    assert torch.equal(xp.cpu().view(torch.int16) if tdt == torch.bfloat16 else xp.cpu(),
+                       xp_o.view(torch.int16) if tdt == torch.bfloat16 else xp_o)
+    expert_of_row = np.repeat(np.arange(wl.E, dtype=np.int32), c_o)
+    c_d = torch.as_tensor(c_o, device=DEV)
+    off_d = torch.as_tensor(off_o, device=DEV)
+    # gate/up + SwiGLU epilogue
+    h = moe.expert_gateup(xp_o.to(DEV), c_d, off_d, g.w1, g.w3)
+    h_ref = oracle.expert_hidden(xp_o, expert_of_row, inp.w1, inp.w3)
+    err = row_max_rel_err(h, h_ref)
+    announce(f"  gate/up row-max-rel err {err:.3e}")
+    assert err <= (1e-5 if wl.dtype == W.F32 else 1e-2), err
+    # down, fed the oracle's hidden activation rounded to the layer dtype
+    h_in = torch.from_numpy(h_ref).to(tdt)
+    o = moe.expert_down(h_in.to(DEV), c_d, off_d, g.w2)
+    o_ref = oracle.expert_down(h_in, expert_of_row, inp.w2)
+    err = row_max_rel_err(o, o_ref)
+    announce(f"  down row-max-rel err {err:.3e}")
+    assert err <= (1e-5 if wl.dtype == W.F32 else 1e-4), err
+    # the two halves together
+    o2 = moe.experts(xp_o.to(DEV), c_d, off_d, g.w1, g.w3, g.w2)
+    o2_ref = oracle.expert_rows(xp_o, expert_of_row, inp.w1, inp.w3, inp.w2)
+    assert row_max_rel_err(o2, o2_ref) <= Y_TOL[wl.dtype]
+    # combine, fed the oracle's expert outputs as fp32 and its weights
+    o_in = torch.from_numpy(o2_ref).float()
+    w_in = torch.from_numpy(w_o).float()
+    y = moe.combine(o_in.to(DEV), torch.as_tensor(pos_o, device=DEV), w_in.to(DEV), tdt)
+    o64 = o_in.double().numpy()
+    ref = oracle.combine(np.stack([o64[pos_o[:, 0]], o64[pos_o[:, 1]]], axis=1),
+                         w_in.double().numpy())
+    err = row_max_rel_err(y, ref)
+    assert err <= (2 ** -8 if wl.dtype == W.BF16 else 1e-6), err
+
+
+def _biased(wl, bias_col, screen=True):
+    inp = checked_inputs(wl) if screen else W.make_inputs(wl)
+    inp.x[:, -1] = 1.0
+    inp.w_gate[-1, :] = 0.0
+    for e, b in bias_col.items():
+        inp.w_gate[-1, e] = b
+    return inp
+
+
+@pytest.mark.parametrize("T", [1, 32, 300])
+def test_expert_with_no_tokens(T):
+    wl = W.small_workload(T, 128, 256, seed=20 + T)
+    inp = _biased(wl, {3: -1000.0, 6: -1000.0})
+    assert not oracle.near_tie_tokens(inp.x, inp.w_gate).any()
+    y, idx_o = run_forward_parity(inp)
+    assert not np.isin(idx_o, [3, 6]).any()
+
+
+@pytest.mark.parametrize("T", [16, 32, 257])
+def test_every_token_on_the_same_two_experts(T):
+    wl = W.small_workload(T, 128, 256, seed=30 + T)
+    inp = _biased(wl, {4: 60.0, 1: 50.0}, screen=False)
+    y, idx_o = run_forward_parity(inp)
+    assert np.all(idx_o[:, 0] == 4) and np.all(idx_o[:, 1] == 1)
+
+
+@pytest.mark.parametrize("dtype", [W.F32, W.BF16])
+def test_exact_tie_takes_the_lower_index(dtype):
+    """Duplicate router columns give bit-identical logits on both sides;
+    the lower expert index must take slot 0 and the weights are 1/2."""
+    wl = W.small_workload(40, 128, 256, dtype=dtype, seed=41)
+    inp = _biased(wl, {2: 50.0, 5: 50.0}, screen=False)
+    inp.w_gate[:, 5] = inp.w_gate[:, 2]
+    g = inp.to(DEV)
+    idx, w = moe.route(g.x, g.w_gate)
+    assert torch.all(idx[:, 0] == 2) and torch.all(idx[:, 1] == 5)
+    assert torch.all(w == 0.5)
+    run_forward_parity(inp)
+
+
+def test_zero_tokens():
+    wl = W.small_workload(4, 128, 256)
+    g = W.make_inputs(wl).to(DEV)
+    y = moe.forward(g.x[:0], g.w_gate, g.w1, g.w3, g.w2)
+    assert y.shape == (0, 128)
+
+
+def test_bit_identical_reruns_and_token_permutation():
+    wl = W.small_workload(300, 256, 512, seed=50)
+    inp = checked_inputs(wl)
+    g = inp.to(DEV)
+    y1 = moe.forward(g.x, g.w_gate, g.w1, g.w3, g.w2)
+    y2 = moe.forward(g.x, g.w_gate, g.w1, g.w3, g.w2)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    # Each row's value does not depend on which other tokens share the call
+    # except through the grouped order, so a permutation keeps rows close.
+    perm = torch.randperm(wl.T, generator=torch.Generator().manual_seed(0)).to(DEV)
+    y3 = moe.forward(g.x[perm].contiguous(), g.w_gate, g.w1, g.w3, g.w2)
+    assert row_max_rel_err(y3, y1[perm]) <= Y_TOL[wl.dtype]
+
+
+def test_power_of_two_scaling_is_exact():
+    wl = W.small_workload(64, 128, 256, dtype=W.F32, seed=60)
+    g = checked_inputs(wl).to(DEV)
+    y1 = moe.forward(g.x, g.w_gate, g.w1, g.w3, g.w2)
+    y2 = moe.forward(g.x, g.w_gate, g.w1, g.w3, (2 * g.w2).contiguous())
+    assert torch.equal(y2, 2 * y1)
+
+
+# ---------------------------------------------------------------------------
+# The full layer shapes, in the launch configuration the benchmark times.
+# The oracle runs on a sample of tokens (each token is independent); routing
+# is checked for every token.
+
+FULL = [("decode_8x7b", None), ("prefill_8x7b", 24), ("skewed_8x7b", 24),
+        ("larger_expert", 12)]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,n_sample", FULL, ids=[f[0] for f in FULL])
+def test_full_size(name, n_sample):
+    wl = W.WORKLOADS[name]
+    announce(f"full {name}: drawing inputs")
+    inp = checked_inputs(wl)
+    announce(f"full {name}: {inp.redrawn_rows} rows redrawn; running")
+    sample = None
+    if n_sample is not None:
+        rng = np.random.default_rng(0)
+        sample = np.sort(rng.choice(wl.T, size=n_sample, replace=False))
+        sample[0], sample[-1] = 0, wl.T - 1
+    y, idx_o = run_forward_parity(inp, sample)
+    # dispatch integers over every token
+    g_idx = torch.as_tensor(idx_o, device=DEV)
+    counts, offsets, pos, _ = moe.dispatch(inp.x.to(DEV), g_idx, wl.E)
+    c_o, off_o, pos_o, _ = oracle.dispatch(idx_o, wl.E)
+    np.testing.assert_array_equal(counts.cpu().numpy(), c_o)
+    np.testing.assert_array_equal(pos.cpu().numpy(), pos_o)
+    announce(f"full {name}: counts {c_o.tolist()}")
+    # the same call again is bit-identical
+    g = inp.to(DEV)
+    y2 = moe.forward(g.x, g.w_gate, g.w1, g.w3, g.w2)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
