@@ -11,8 +11,9 @@
 // giving 8 vectors of 8 consecutive K values, one per column.
 //
 // Two variants:
-//  * prefill (many rows per expert): 128 x 256 output tiles staged through
-//    LDS, v_mfma_f32_32x32x16_bf16, four wavefronts in a 2 x 2 arrangement.
+//  * prefill (many rows per expert): 256 x 256 output tiles staged through
+//    double-buffered LDS, v_mfma_f32_32x32x16_bf16, tiles ordered so that
+//    the workgroups resident on one XCD share weight tiles in its L2.
 //    MFMA-bound when an expert has more rows than the ridge point.
 //  * decode (at most 32 rows in total per expert): each workgroup streams
 //    one 128-column slab of an expert's weights over the whole K range
@@ -55,124 +56,182 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
 // Prefill: LDS-tiled grouped GEMM.
 //   NMAT = 2: C = bf16(silu(A B0[e]) * (A B1[e]))   (gate/up, C = h)
 //   NMAT = 1: C = fp32(A B0[e])                     (down,    C = o)
+//
+// Workgroup tile 256 rows x 256 columns (for gate/up: 128 gate + the same
+// 128 up columns, so the epilogue pairs them in registers), K step 64.
+// WM x WN wavefronts; each owns a (256/WM) x (256/WN) sub-tile of 32x32
+// MFMA blocks.  Both operands are staged in LDS, double-buffered: the
+// global loads of step k+1 are in flight while step k computes, and one
+// barrier per step separates the two buffers.  The weight operand is
+// transposed in registers on its way into LDS (K contiguous per column).
 
-constexpr int PBM = 128, PBN = 256, PBK = 64;
-constexpr int PLD = PBK + 8;  // LDS row pitch in bf16: 144 bytes keeps 8-lane groups of
-                              // 16-byte reads on distinct banks
+constexpr int PBM = 256, PBN = 256, PBK = 64;
+constexpr int PLD = PBK + 8;  // LDS row pitch in bf16 (144 bytes): consecutive rows start
+                              // 16 bytes apart modulo 128, so 8-lane groups of 16-byte
+                              // reads and writes fall on distinct banks
+constexpr int PGM = 4;        // row tiles per scheduling group (see prefill_tile)
+#ifndef MOE_PREFILL_WN
+#define MOE_PREFILL_WN 4
+#endif
+constexpr int PWM = 2, PWN = MOE_PREFILL_WN;
+
+// Work decomposition shared by the prefill kernels.  Row tiles of PBM rows
+// are numbered expert after expert; the flat tile list orders them in
+// groups of PGM row tiles, with all column tiles of a group before the
+// next group (row tile fastest inside a group).  Workgroup b runs on XCD
+// b % 8 (round-robin dispatch); each XCD takes a contiguous eighth of the
+// flat list, so the ~32 workgroups resident on one XCD share the same few
+// weight column tiles and activation row tiles through that XCD's L2.
+__device__ __forceinline__ bool prefill_tile(const int32_t *counts, const int32_t *offsets,
+                                             int E, int n_tiles, int &e, int &row0,
+                                             int &row_end, int &nt) {
+    int mt_total = 0;
+    for (int i = 0; i < E; ++i) mt_total += (counts[i] + PBM - 1) / PBM;
+    const int total = mt_total * n_tiles;
+    const int per_xcd = (total + 7) >> 3;
+    const int li = blockIdx.x >> 3;
+    if (li >= per_xcd) return false;
+    const int L = (blockIdx.x & 7) * per_xcd + li;
+    if (L >= total) return false;
+    const int group = L / (PGM * n_tiles);
+    const int first = group * PGM;
+    const int gm = min(PGM, mt_total - first);
+    const int within = L - group * PGM * n_tiles;
+    const int mt = first + within % gm;
+    nt = within / gm;
+    return find_row_tile(counts, offsets, E, PBM, mt, e, row0, row_end);
+}
 
 template <int NMAT>
-__global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
+__global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_gemm_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B0,
     const uint16_t *__restrict__ B1, void *__restrict__ C, const int32_t *__restrict__ counts,
     const int32_t *__restrict__ offsets, int E, int K, int N, int a_rows) {
-    constexpr int BNM = PBN / NMAT;  // columns of each weight matrix in this tile
-    int e, row0, row_end;
-    if (!find_row_tile(counts, offsets, E, PBM, blockIdx.y, e, row0, row_end)) return;
-    const int n0 = blockIdx.x * BNM;
+    constexpr int NT = PWM * PWN * 64;            // threads
+    constexpr int TM = PBM / PWM, TN = PBN / PWN;  // wave sub-tile
+    constexpr int MB = TM / 32, NB = TN / 32;      // 32x32 blocks per wave
+    constexpr int BNM = PBN / NMAT;                // columns of each matrix per tile
+    constexpr int AV = PBM * PBK / 8 / NT;         // 16-byte A vectors per thread
+    static_assert(NMAT == 1 || NB % 2 == 0, "gate/up blocks come in pairs");
 
-    __shared__ __attribute__((aligned(16))) uint16_t As[PBM * PLD];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[PBN * PLD];
+    const int n_tiles = (N + BNM - 1) / BNM;
+    int e, row0, row_end, nt;
+    if (!prefill_tile(counts, offsets, E, n_tiles, e, row0, row_end, nt)) return;
+    const int n0 = nt * BNM;
+
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2][(PBM + PBN) * PLD];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / PWN, wn = wave % PWN;
 
-    // Global -> register assignment.  A: four 16-byte vectors per thread.
-    // B: one 8 x 8 block per thread (kb = K block, nb = N block).
-    const int kb = tid & 7;
-    const int mat = NMAT == 2 ? (tid >> 7) : 0;
-    const int nb = NMAT == 2 ? ((tid & 127) >> 3) : (tid >> 3);
-    const int bcol = n0 + nb * 8;
+    // A: vector v = tid + NT*i covers row v/8, K chunk v%8.  Rows past the
+    // end of A are clamped onto its last row (never stored).
+    const uint16_t *Arow[AV];
+#pragma unroll
+    for (int i = 0; i < AV; ++i)
+        Arow[i] = A + (size_t)min(row0 + ((tid + NT * i) >> 3), a_rows - 1) * K;
+    // B: 256 blocks of 8 K-rows x 8 columns, one per thread of the first 256
+    // threads.  kb (K block) is the fastest index so that the 8 lanes that
+    // write one LDS row after the transpose hit 8 consecutive 16-byte chunks.
+    const bool do_b = tid < 256;
+    const int kb = tid & 7, nb = (tid & 255) >> 3;          // nb: 0..31
+    const int mat = NMAT == 2 ? nb >> 4 : 0;
+    const int bcol = n0 + (NMAT == 2 ? (nb & 15) : nb) * 8;
     const bool bcol_ok = bcol < N;
     const uint16_t *Bp = (mat ? B1 : B0) + (size_t)e * K * N + (bcol_ok ? bcol : 0);
-    // Rows past the last expert-sorted row are clamped onto it: a row tile
-    // may run past the end of A, and those rows are never stored.
-    const uint16_t *Arow[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        Arow[i] = A + (size_t)min(row0 + ((tid + 256 * i) >> 3), a_rows - 1) * K;
 
-    uint4 ra[4], rb[8];
+    uint4 ra[AV], rb[8];
     auto gload = [&](int k0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int k = k0 + ((tid + 256 * i) & 7) * 8;
+        for (int i = 0; i < AV; ++i) {
+            const int k = k0 + ((tid + NT * i) & 7) * 8;
             ra[i] = k < K ? *reinterpret_cast<const uint4 *>(Arow[i] + k) : zero4();
         }
+        if (do_b)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int k = k0 + kb * 8 + i;
-            rb[i] = (k < K && bcol_ok) ? *reinterpret_cast<const uint4 *>(Bp + (size_t)k * N)
-                                       : zero4();
-        }
+            for (int i = 0; i < 8; ++i) {
+                const int k = k0 + kb * 8 + i;
+                rb[i] = (k < K && bcol_ok) ? *reinterpret_cast<const uint4 *>(Bp + (size_t)k * N)
+                                           : zero4();
+            }
     };
-    auto lstore = [&]() {
+    auto lstore = [&](int st) {
+        uint16_t *As = smem[st], *Bs = smem[st] + PBM * PLD;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int v = tid + 256 * i;
+        for (int i = 0; i < AV; ++i) {
+            const int v = tid + NT * i;
             *reinterpret_cast<uint4 *>(&As[(v >> 3) * PLD + (v & 7) * 8]) = ra[i];
         }
-        uint4 tb[8];
-        transpose8x8(rb, tb);
+        if (do_b) {
+            uint4 tb[8];
+            transpose8x8(rb, tb);
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
-            *reinterpret_cast<uint4 *>(&Bs[(mat * BNM + nb * 8 + c) * PLD + kb * 8]) = tb[c];
+            for (int c = 0; c < 8; ++c)
+                *reinterpret_cast<uint4 *>(&Bs[(nb * 8 + c) * PLD + kb * 8]) = tb[c];
+        }
     };
-    // LDS row (within Bs) of this wave's N block j (0..3).
-    auto bcol_lds = [&](int j) {
-        if (NMAT == 2) return (j >> 1) * 128 + wn * 64 + (j & 1) * 32;
-        return wn * 128 + j * 32;
+    // LDS row of this wave's column block j: gate/up waves take TN/2 gate
+    // columns (LDS rows 0..127) and the same TN/2 up columns (rows 128..255).
+    auto brow = [&](int j) {
+        if (NMAT == 2) return (j / (NB / 2)) * 128 + wn * (TN / 2) + (j % (NB / 2)) * 32;
+        return wn * TN + j * 32;
     };
 
-    f32x16_t acc[2][4];
+    f32x16_t acc[MB][NB];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NB; ++j)
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
     const int nk = (K + PBK - 1) / PBK;
     gload(0);
+    lstore(0);
+    __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
-        __syncthreads();
-        lstore();
-        __syncthreads();
+        const int cur = kt & 1;
         if (kt + 1 < nk) gload((kt + 1) * PBK);
+        const uint16_t *As = smem[cur], *Bs = smem[cur] + PBM * PLD;
 #pragma unroll
         for (int kk = 0; kk < PBK; kk += 16) {
             const int koff = kk + (lane >> 5) * 8;
-            bf16x8_t af[2], bfr[4];
+            bf16x8_t af[MB], bfr[NB];
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < MB; ++i)
                 af[i] = as_bf16x8(*reinterpret_cast<const uint4 *>(
-                    &As[(wm * 64 + i * 32 + (lane & 31)) * PLD + koff]));
+                    &As[(wm * TM + i * 32 + (lane & 31)) * PLD + koff]));
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < NB; ++j)
                 bfr[j] = as_bf16x8(*reinterpret_cast<const uint4 *>(
-                    &Bs[(bcol_lds(j) + (lane & 31)) * PLD + koff]));
+                    &Bs[(brow(j) + (lane & 31)) * PLD + koff]));
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < MB; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < NB; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j],
                                                                          acc[i][j], 0, 0, 0);
         }
+        if (kt + 1 < nk) lstore(cur ^ 1);
+        __syncthreads();
     }
 
     // Epilogue.  32x32 accumulator layout: value q of lane l is row
     // 8*(q/4) + 4*(l/32) + q%4, column l%32 of the block.
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < MB; ++i) {
 #pragma unroll
-        for (int j = 0; j < (NMAT == 2 ? 2 : 4); ++j) {
-            const int col = n0 + (NMAT == 2 ? wn * 64 + j * 32 : wn * 128 + j * 32) + (lane & 31);
+        for (int j = 0; j < (NMAT == 2 ? NB / 2 : NB); ++j) {
+            const int col = n0 + (NMAT == 2 ? wn * (TN / 2) + j * 32 : wn * TN + j * 32) +
+                            (lane & 31);
             if (col >= N) continue;
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
-                const int row = row0 + wm * 64 + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                const int row =
+                    row0 + wm * TM + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
                 if (row >= row_end) continue;
                 if (NMAT == 2) {
-                    const float h = silu_f32(acc[i][j][q]) * acc[i][j + 2][q];
+                    const float h = silu_f32(acc[i][j][q]) * acc[i][j + NB / 2][q];
                     static_cast<uint16_t *>(C)[(size_t)row * N + col] = (uint16_t)f32_to_bf16(h);
                 } else {
                     static_cast<float *>(C)[(size_t)row * N + col] = acc[i][j][q];
@@ -180,6 +239,248 @@ __global__ __launch_bounds__(256, 2) void prefill_gemm_kernel(
             }
         }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Prefill, deep-pipelined variant (K % 32 == 0 and N a multiple of the tile's
+// columns per matrix, which every Mixtral shape satisfies).  Same tiles and
+// schedule as prefill_gemm_kernel, but operands go from global memory
+// straight into a 4-stage LDS ring (global_load_lds_dwordx4: no registers,
+// no VALU work), so three K steps of loads are in flight while one computes.
+//
+// LDS layouts (16-byte chunks are XOR-swizzled by row so that MFMA operand
+// reads from consecutive rows fall on distinct banks):
+//   A stage: 256 rows x 32 bf16 (64 B = 4 chunks); chunk c of row r holds
+//            K chunk c ^ aswz(r).
+//   B stage: 32 K rows x 256 columns (512 B = 32 chunks), the weights'
+//            own row-major layout (for gate/up: 128 gate then 128 up
+//            columns); chunk c of row r holds column chunk c ^ bswz(r).
+// A fragments are plain 16-byte reads.  B fragments use the CDNA4 LDS
+// transpose read ds_read_b64_tr_b16: within each 16-lane group, lane 4i+q
+// points at 4 consecutive columns of K row i and lane j receives column j
+// of those 4 rows, i.e. 4 consecutive K values of one column.  Two such
+// reads give the 8 K values a 32x32x16 operand lane holds.
+
+#ifndef MOE_DMA_BK
+#define MOE_DMA_BK 64
+#endif
+constexpr int DBK = MOE_DMA_BK;               // K per stage: 64 makes every A row
+constexpr int DSTAGES = DBK == 64 ? 2 : 4;    // segment a full 128-byte line
+constexpr int DA_BYTES = PBM * DBK * 2;
+constexpr int DB_BYTES = DBK * PBN * 2;
+constexpr int DSTAGE_BYTES = DA_BYTES + DB_BYTES;
+constexpr int DACH = DBK / 8;                 // 16-byte chunks per A row
+
+// A swizzle: any 8 (and 16) consecutive rows reading the same K chunk land
+// on distinct 16-byte bank groups.
+__device__ __forceinline__ int aswz(int r) {
+    if (DACH == 8) return ((r >> 1) & 7) ^ ((r & 1) << 2);
+    return ((r >> 1) & 3) ^ ((r >> 3) & 1);
+}
+__device__ __forceinline__ int bswz(int r) { return (r & 7) << 2; }
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Barrier of the LDS ring.  Each wavefront first waits until at most N of
+// its own LDS-DMA loads are outstanding (so its part of the stage about to
+// be read has landed) and until its LDS reads have returned (so the stage
+// about to be refilled is no longer being read), then all wavefronts meet.
+// __syncthreads() is not used here: its release fence waits for every
+// outstanding load, which would collapse the ring to one stage in flight.
+// The empty asm statements keep the compiler from moving memory accesses
+// across the barrier.  gfx9 s_waitcnt encoding: vmcnt bits 3:0 and 15:14,
+// expcnt 6:4 (left at its maximum), lgkmcnt 11:8 (zero).
+template <int N>
+__device__ __forceinline__ void ring_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int NMAT>
+__global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_dma_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B0,
+    const uint16_t *__restrict__ B1, void *__restrict__ C, const int32_t *__restrict__ counts,
+    const int32_t *__restrict__ offsets, int E, int K, int N, int a_rows) {
+    constexpr int NW = PWM * PWN;
+    constexpr int TM = PBM / PWM, TN = PBN / PWN;
+    constexpr int MB = TM / 32, NB = TN / 32;
+    constexpr int BNM = PBN / NMAT;
+    constexpr int AI = DA_BYTES / 1024 / NW;   // A load instructions per wave per stage
+    constexpr int BI = DB_BYTES / 1024 / NW;   // B load instructions per wave per stage
+    constexpr int LPS = AI + BI;               // loads per lane per stage
+    static_assert(NMAT == 1 || NB % 2 == 0, "gate/up blocks come in pairs");
+
+    const int n_tiles = N / BNM;
+    int e, row0, row_end, nt;
+    if (!prefill_tile(counts, offsets, E, n_tiles, e, row0, row_end, nt)) return;
+    const int n0 = nt * BNM;
+
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[DSTAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t st1[DSTAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t st2[DSTAGES > 2 ? DSTAGE_BYTES : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t st3[DSTAGES > 2 ? DSTAGE_BYTES : 16];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / PWN, wn = wave % PWN;
+
+    // Global sources of this wave's load instructions.  A instruction g
+    // covers 64/DACH rows (DACH lanes x 16 B per row); B instruction g
+    // covers 2 K rows (32 lanes x 16 B each).  Addresses are recomputed at
+    // each issue from a few per-lane values, which keeps register use low.
+    constexpr int AROWS = 64 / DACH;           // A rows per load instruction
+    const int a_r0 = wave * AI * AROWS + lane / DACH;  // row of instruction 0
+    int a_kc[2];                               // K chunk for even / odd instructions
+#pragma unroll
+    for (int p = 0; p < 2; ++p) a_kc[p] = (lane % DACH) ^ aswz(a_r0 + p * AROWS);
+    // B: row parity pattern repeats every 4 instructions (bswz uses r & 7).
+    size_t b_base[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int r = (wave * BI + p) * 2 + (lane >> 5);
+        const int cc = (lane & 31) ^ bswz(r);
+        const uint16_t *base;
+        int col;
+        if (NMAT == 2) {
+            base = cc < 16 ? B0 : B1;
+            col = n0 + (cc & 15) * 8;
+        } else {
+            base = B0;
+            col = n0 + cc * 8;
+        }
+        b_base[p] = (size_t)(base - B0) + (size_t)e * K * N + (size_t)r * N + col;
+    }
+
+    auto issue = [&](uint8_t *stage, int k0) {
+#pragma unroll
+        for (int j = 0; j < AI; ++j) {
+            const int r = min(row0 + a_r0 + j * AROWS, a_rows - 1);
+            const uint16_t *src = A + (size_t)r * K + k0 + a_kc[j & 1] * 8;
+            __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(stage + (wave * AI + j) * 1024),
+                                             16, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < BI; ++j) {
+            const uint16_t *src = B0 + b_base[j & 3] + (size_t)(k0 + (j & ~3) * 2) * N;
+            __builtin_amdgcn_global_load_lds(src,
+                                             (lds_void_t *)(stage + DA_BYTES + (wave * BI + j) * 1024),
+                                             16, 0, 0);
+        }
+    };
+
+    // Operand read offsets inside a stage.  The A swizzle depends only on
+    // the row modulo 16, i.e. on the lane, so M blocks and K steps become
+    // immediate offsets; the B swizzle depends only on the K row modulo 8.
+    constexpr int KS = DBK / 16;                   // 32x32x16 steps per stage
+    const int a_row = wm * TM + (lane & 31);
+    int a_off[KS];
+#pragma unroll
+    for (int h = 0; h < KS; ++h)
+        a_off[h] = a_row * (DBK * 2) + (((h * 2 + (lane >> 5)) ^ aswz(a_row)) << 4);
+    const int G = lane >> 4, jq = (lane & 15) >> 2, q = lane & 3;
+    int b_off[NB][2];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        int nb;
+        if (NMAT == 2) nb = (j / (NB / 2)) * 128 + wn * (TN / 2) + (j % (NB / 2)) * 32;
+        else nb = wn * TN + j * 32;
+        const int n = nb + 16 * (G & 1) + 4 * q;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int r = 8 * (G >> 1) + 4 * u + jq;     // + 16 * step (immediate)
+            b_off[j][u] = DA_BYTES + r * 512 + ((((n >> 3) ^ bswz(r))) << 4) + (n & 7) * 2;
+        }
+    }
+
+    f32x16_t acc[MB][NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int qq = 0; qq < 16; ++qq) acc[i][j][qq] = 0.0f;
+
+    auto compute = [&](const uint8_t *stage) {
+#pragma unroll
+        for (int h = 0; h < KS; ++h) {
+            bf16x8_t af[MB], bfr[NB];
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+                af[i] = as_bf16x8(*reinterpret_cast<const uint4 *>(
+                    stage + a_off[h] + i * 32 * (DBK * 2)));
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4_t *)(stage + b_off[j][0] + h * 8192));
+                s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4_t *)(stage + b_off[j][1] + h * 8192));
+                bfr[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3,
+                                                                                4, 5, 6, 7));
+            }
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j],
+                                                                         acc[i][j], 0, 0, 0);
+        }
+    };
+
+    uint8_t *const stages[4] = {st0, st1, st2, st3};
+    const int nk = K / DBK;
+    // Prologue: stages 0..2 in flight.
+#pragma unroll
+    for (int s = 0; s < DSTAGES - 1; ++s)
+        if (s < nk) issue(stages[s], s * DBK);
+    // Main loop, unrolled by the ring size so every stage index is static.
+    for (int kb = 0; kb < nk; kb += DSTAGES) {
+#pragma unroll
+        for (int s = 0; s < DSTAGES; ++s) {
+            const int kt = kb + s;
+            if (kt < nk) {
+                // Stage kt's loads are done once at most the loads of the
+                // stages issued after it are still outstanding.
+                const int later = min(DSTAGES - 2, nk - 1 - kt);
+                if (later >= 2) ring_barrier<2 * LPS>();
+                else if (later == 1) ring_barrier<LPS>();
+                else ring_barrier<0>();
+                if (kt + DSTAGES - 1 < nk)
+                    issue(stages[(s + DSTAGES - 1) % DSTAGES], (kt + DSTAGES - 1) * DBK);
+                compute(stages[s]);
+            }
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+#pragma unroll
+        for (int j = 0; j < (NMAT == 2 ? NB / 2 : NB); ++j) {
+            const int col = n0 + (NMAT == 2 ? wn * (TN / 2) + j * 32 : wn * TN + j * 32) +
+                            (lane & 31);
+#pragma unroll
+            for (int qq = 0; qq < 16; ++qq) {
+                const int row =
+                    row0 + wm * TM + i * 32 + 8 * (qq >> 2) + 4 * (lane >> 5) + (qq & 3);
+                if (row >= row_end) continue;
+                if (NMAT == 2) {
+                    const float hv = silu_f32(acc[i][j][qq]) * acc[i][j + NB / 2][qq];
+                    static_cast<uint16_t *>(C)[(size_t)row * N + col] = (uint16_t)f32_to_bf16(hv);
+                } else {
+                    static_cast<float *>(C)[(size_t)row * N + col] = acc[i][j][qq];
+                }
+            }
+        }
+    }
+}
+
+// Grid for the prefill kernels: worst-case tile count (every expert may
+// end with a partial row tile), rounded up to a multiple of the 8 XCDs.
+inline int prefill_grid(int rows, int E, int n_tiles) {
+    const long tiles = (long)((rows + PBM - 1) / PBM + E) * n_tiles;
+    return (int)((tiles + 7) / 8 * 8);
 }
 
 // ---------------------------------------------------------------------------
@@ -318,9 +619,13 @@ hipError_t launch_gateup_bf16(const moe_shape_t &s, const uint16_t *xp, const in
                            dim3(DWAVES * 64), 0, stream, xp, w1, w3, h, counts, offsets, d, f,
                            rows);
     } else {
-        const int m_tiles = (rows + PBM - 1) / PBM + E;
-        hipLaunchKernelGGL(prefill_gemm_kernel<2>, dim3((f + PBN / 2 - 1) / (PBN / 2), m_tiles),
-                           dim3(256), 0, stream, xp, w1, w3, h, counts, offsets, E, d, f, rows);
+        const int grid = prefill_grid(rows, E, (f + PBN / 2 - 1) / (PBN / 2));
+        if (d % DBK == 0 && f % (PBN / 2) == 0)
+            hipLaunchKernelGGL(prefill_dma_kernel<2>, dim3(grid), dim3(PWM * PWN * 64), 0,
+                               stream, xp, w1, w3, h, counts, offsets, E, d, f, rows);
+        else
+            hipLaunchKernelGGL(prefill_gemm_kernel<2>, dim3(grid), dim3(PWM * PWN * 64), 0,
+                               stream, xp, w1, w3, h, counts, offsets, E, d, f, rows);
     }
     return hipGetLastError();
 }
@@ -338,10 +643,13 @@ hipError_t launch_down_bf16(const moe_shape_t &s, const uint16_t *h, const int32
                            dim3(DWAVES * 64), 0, stream, h, w2, nullptr, o, counts, offsets, f,
                            d, rows);
     } else {
-        const int m_tiles = (rows + PBM - 1) / PBM + E;
-        hipLaunchKernelGGL(prefill_gemm_kernel<1>, dim3((d + PBN - 1) / PBN, m_tiles),
-                           dim3(256), 0, stream, h, w2, nullptr, o, counts, offsets, E, f, d,
-                           rows);
+        const int grid = prefill_grid(rows, E, (d + PBN - 1) / PBN);
+        if (f % DBK == 0 && d % PBN == 0)
+            hipLaunchKernelGGL(prefill_dma_kernel<1>, dim3(grid), dim3(PWM * PWN * 64), 0,
+                               stream, h, w2, nullptr, o, counts, offsets, E, f, d, rows);
+        else
+            hipLaunchKernelGGL(prefill_gemm_kernel<1>, dim3(grid), dim3(PWM * PWN * 64), 0,
+                               stream, h, w2, nullptr, o, counts, offsets, E, f, d, rows);
     }
     return hipGetLastError();
 }

@@ -2,11 +2,8 @@
 // over the two kept logits.  "Mixtral 8x7B -- The Evolving Transformer",
 // section 05 (MoERouter and the formula y = sum_k w_k E_{i_k}(x)).
 //
-// One wavefront owns TPW tokens.  Lane l walks d in 8-element chunks
-// l, l+64, l+128, ... and keeps per-expert partial sums for its tokens;
-// a butterfly across the 64 lanes then completes every logit in every lane.
 // The router matrix (d x E, 64 KiB at the 8x7B shape) is read once per
-// wavefront from L2 and reused for its TPW tokens.  The kernel is bound by
+// workgroup from L2 and reused for its tokens; the kernel is bound by
 // reading x once (T*d*elem bytes).
 #include "moe_internal.h"
 
@@ -42,78 +39,110 @@ __device__ __forceinline__ float load1<float>(const float *p) { return *p; }
 template <>
 __device__ __forceinline__ float load1<uint16_t>(const uint16_t *p) { return bf16_to_f32(*p); }
 
-template <typename T, int EMAX, int TPW>
+// Router row j (E values) widened to fp32.  When E == EMAX the row is
+// contiguous and 16-byte aligned (w_gate is 16-byte aligned and
+// EMAX * sizeof(T) is a multiple of 16), so it is read with vector loads.
+template <typename T, int EMAX>
+__device__ __forceinline__ void load_router_row(const T *row, int E, float (&wr)[EMAX]) {
+    if (E == EMAX) {
+        constexpr int per16 = 16 / (int)sizeof(T);
+#pragma unroll
+        for (int v = 0; v < EMAX / per16; ++v) {
+            float t[8];
+            if constexpr (sizeof(T) == 2) {
+                load8<T>(row + v * 8, t);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) wr[v * 8 + i] = t[i];
+            } else {
+                float4 q = reinterpret_cast<const float4 *>(row)[v];
+                wr[v * 4 + 0] = q.x; wr[v * 4 + 1] = q.y; wr[v * 4 + 2] = q.z; wr[v * 4 + 3] = q.w;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < EMAX; ++e) wr[e] = e < E ? load1<T>(row + e) : 0.0f;
+    }
+}
+
+// One workgroup (4 wavefronts) owns TPB consecutive tokens.  Thread i walks
+// d in 8-element chunks i, i+256, ...; per-thread partial logits are summed
+// across each wavefront with a butterfly and then across the four
+// wavefronts in LDS, in a fixed order.
+template <typename T, int EMAX, int TPB>
 __global__ __launch_bounds__(256) void route_kernel(const T *__restrict__ x,
                                                     const T *__restrict__ wg, int n_tok,
                                                     int d, int E, int32_t *__restrict__ idx,
                                                     float *__restrict__ wout) {
-    const int lane = threadIdx.x & 63;
-    const int t0 = (blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * TPW;
-    if (t0 >= n_tok) return;
+    __shared__ float part[4][TPB][EMAX];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t0 = blockIdx.x * TPB;
 
-    float acc[TPW][EMAX];
+    float acc[TPB][EMAX];
 #pragma unroll
-    for (int tt = 0; tt < TPW; ++tt)
+    for (int tt = 0; tt < TPB; ++tt)
 #pragma unroll
         for (int e = 0; e < EMAX; ++e) acc[tt][e] = 0.0f;
 
     const int nchunk = d >> 3;
-    for (int c = lane; c < nchunk; c += 64) {
-        float xv[TPW][8];
+    for (int c = tid; c < nchunk; c += 256) {
+        float xv[TPB][8];
 #pragma unroll
-        for (int tt = 0; tt < TPW; ++tt) {
-            int t = t0 + tt < n_tok ? t0 + tt : n_tok - 1;
+        for (int tt = 0; tt < TPB; ++tt) {
+            const int t = min(t0 + tt, n_tok - 1);
             load8<T>(x + (size_t)t * d + c * 8, xv[tt]);
         }
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            const T *wrow = wg + (size_t)(c * 8 + r) * E;
             float wr[EMAX];
+            load_router_row<T, EMAX>(wg + (size_t)(c * 8 + r) * E, E, wr);
 #pragma unroll
-            for (int e = 0; e < EMAX; ++e) wr[e] = e < E ? load1<T>(wrow + e) : 0.0f;
-#pragma unroll
-            for (int tt = 0; tt < TPW; ++tt)
+            for (int tt = 0; tt < TPB; ++tt)
 #pragma unroll
                 for (int e = 0; e < EMAX; ++e) acc[tt][e] += xv[tt][r] * wr[e];
         }
     }
-    // Butterfly over the wavefront: fixed pairing, so the result is the same
-    // on every call (and identical in every lane).
+    // Butterfly over the wavefront (fixed pairing: same result every call).
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1)
 #pragma unroll
-        for (int tt = 0; tt < TPW; ++tt)
+        for (int tt = 0; tt < TPB; ++tt)
 #pragma unroll
             for (int e = 0; e < EMAX; ++e) acc[tt][e] += __shfl_xor(acc[tt][e], off, 64);
-
+    if (lane == 0)
 #pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) {
-        const int t = t0 + tt;
-        if (lane != tt || t >= n_tok) continue;
-        int i0 = 0;
-        float l0 = acc[tt][0];
+        for (int tt = 0; tt < TPB; ++tt)
 #pragma unroll
-        for (int e = 1; e < EMAX; ++e)
-            if (e < E && acc[tt][e] > l0) { i0 = e; l0 = acc[tt][e]; }
-        int i1 = -1;
-        float l1 = 0.0f;
+            for (int e = 0; e < EMAX; ++e) part[wave][tt][e] = acc[tt][e];
+    __syncthreads();
+    if (tid >= TPB) return;
+    const int t = t0 + tid;
+    if (t >= n_tok) return;
+    float l[EMAX];
 #pragma unroll
-        for (int e = 0; e < EMAX; ++e)
-            if (e < E && e != i0 && (i1 < 0 || acc[tt][e] > l1)) { i1 = e; l1 = acc[tt][e]; }
-        const float q = expf(l1 - l0);
-        idx[2 * t] = i0;
-        idx[2 * t + 1] = i1;
-        wout[2 * t] = 1.0f / (1.0f + q);
-        wout[2 * t + 1] = q / (1.0f + q);
-    }
+    for (int e = 0; e < EMAX; ++e)
+        l[e] = ((part[0][tid][e] + part[1][tid][e]) + part[2][tid][e]) + part[3][tid][e];
+    int i0 = 0;
+    float l0 = l[0];
+#pragma unroll
+    for (int e = 1; e < EMAX; ++e)
+        if (e < E && l[e] > l0) { i0 = e; l0 = l[e]; }
+    int i1 = -1;
+    float l1 = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e)
+        if (e < E && e != i0 && (i1 < 0 || l[e] > l1)) { i1 = e; l1 = l[e]; }
+    const float q = expf(l1 - l0);
+    idx[2 * t] = i0;
+    idx[2 * t + 1] = i1;
+    wout[2 * t] = 1.0f / (1.0f + q);
+    wout[2 * t + 1] = q / (1.0f + q);
 }
 
-template <typename T, int EMAX, int TPW>
+template <typename T, int EMAX, int TPB>
 hipError_t launch_route_t(const moe_shape_t &s, const void *x, const void *wg, int32_t *idx,
                           float *w, hipStream_t stream) {
-    const int waves = (s.T + TPW - 1) / TPW;
-    const int blocks = (waves + 3) / 4;
-    hipLaunchKernelGGL((route_kernel<T, EMAX, TPW>), dim3(blocks), dim3(256), 0, stream,
+    const int blocks = (s.T + TPB - 1) / TPB;
+    hipLaunchKernelGGL((route_kernel<T, EMAX, TPB>), dim3(blocks), dim3(256), 0, stream,
                        static_cast<const T *>(x), static_cast<const T *>(wg), s.T, s.d_model,
                        s.n_experts, idx, w);
     return hipGetLastError();
@@ -122,9 +151,9 @@ hipError_t launch_route_t(const moe_shape_t &s, const void *x, const void *wg, i
 template <typename T>
 hipError_t launch_route_dtype(const moe_shape_t &s, const void *x, const void *wg,
                               int32_t *idx, float *w, hipStream_t stream) {
-    if (s.n_experts <= 8) return launch_route_t<T, 8, 4>(s, x, wg, idx, w, stream);
-    if (s.n_experts <= 16) return launch_route_t<T, 16, 2>(s, x, wg, idx, w, stream);
-    return launch_route_t<T, 32, 1>(s, x, wg, idx, w, stream);
+    if (s.n_experts <= 8) return launch_route_t<T, 8, 8>(s, x, wg, idx, w, stream);
+    if (s.n_experts <= 16) return launch_route_t<T, 16, 4>(s, x, wg, idx, w, stream);
+    return launch_route_t<T, 32, 2>(s, x, wg, idx, w, stream);
 }
 
 }  // namespace

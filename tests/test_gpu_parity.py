@@ -128,12 +128,13 @@ def test_each_step(wl):
 
 
 def _biased(wl, bias_col, screen=True):
-    inp = checked_inputs(wl) if screen else W.make_inputs(wl)
-    inp.x[:, -1] = 1.0
-    inp.w_gate[-1, :] = 0.0
+    """A constant input column with router weights `bias_col` on it (folded
+    in by the generator, before any near-tie screening)."""
+    bias = [0.0] * wl.E
     for e, b in bias_col.items():
-        inp.w_gate[-1, e] = b
-    return inp
+        bias[e] = b
+    wl = wl.with_(bias=tuple(bias))
+    return checked_inputs(wl) if screen else W.make_inputs(wl)
 
 
 @pytest.mark.parametrize("T", [1, 32, 300])
