@@ -52,6 +52,15 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
+// 16-byte load with the non-temporal hint, for data read exactly once (the
+// decode path's weights): it streams past the caches instead of evicting
+// the activations that every workgroup re-reads.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream16(const uint16_t *p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // ---------------------------------------------------------------------------
 // Prefill: LDS-tiled grouped GEMM.
 //   NMAT = 2: C = bf16(silu(A B0[e]) * (A B1[e]))   (gate/up, C = h)
@@ -531,9 +540,8 @@ __global__ __launch_bounds__(DWAVES * 64) void decode_gemm_kernel(
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                rb[m][i] = (k + i < K && col_ok)
-                               ? *reinterpret_cast<const uint4 *>(Bp[m] + (size_t)(k + i) * N)
-                               : zero4();
+                rb[m][i] = (k + i < K && col_ok) ? load_stream16(Bp[m] + (size_t)(k + i) * N)
+                                                 : zero4();
         bf16x8_t af[MB];
 #pragma unroll
         for (int i = 0; i < MB; ++i)

@@ -101,18 +101,41 @@ __global__ __launch_bounds__(256) void route_kernel(const T *__restrict__ x,
                 for (int e = 0; e < EMAX; ++e) acc[tt][e] += xv[tt][r] * wr[e];
         }
     }
-    // Butterfly over the wavefront (fixed pairing: same result every call).
+    // Reduce-scatter butterfly over the wavefront: at each step a lane keeps
+    // half of its remaining values and adds its partner's copy of that half,
+    // so after log2(64) steps lane l holds the wavefront sum of value l
+    // (63 exchanges instead of 6 per value).  The pairing is fixed, so the
+    // result is the same on every call.
+    constexpr int NV = TPB * EMAX;   // values per lane (8 .. 64)
+    constexpr int RS = NV >= 64 ? 6 : NV >= 32 ? 5 : NV >= 16 ? 4 : 3;  // log2(NV)
+    static_assert((1 << RS) == NV, "values per lane must be a power of two");
+    float v[NV];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
+    for (int tt = 0; tt < TPB; ++tt)
 #pragma unroll
-        for (int tt = 0; tt < TPB; ++tt)
+        for (int e = 0; e < EMAX; ++e) v[tt * EMAX + e] = acc[tt][e];
+    // Steps with partner distance 32, 16, ... (RS of them): lanes with that
+    // bit clear keep the lower half of the remaining values, the others the
+    // upper half.  Afterwards lane l holds value l >> (6 - RS), summed over
+    // the lanes that differ from it in the top RS bits; a plain butterfly
+    // over the remaining low bits completes the sum.
 #pragma unroll
-            for (int e = 0; e < EMAX; ++e) acc[tt][e] += __shfl_xor(acc[tt][e], off, 64);
-    if (lane == 0)
+    for (int st = 0, n = NV; st < RS; ++st, n >>= 1) {
+        const int off = 32 >> st;
+        const bool upper = (lane & off) != 0;
 #pragma unroll
-        for (int tt = 0; tt < TPB; ++tt)
+        for (int i = 0; i < n / 2; ++i) {
+            const float send = upper ? v[i] : v[i + n / 2];
+            const float keep = upper ? v[i + n / 2] : v[i];
+            v[i] = keep + __shfl_xor(send, off, 64);
+        }
+    }
 #pragma unroll
-            for (int e = 0; e < EMAX; ++e) part[wave][tt][e] = acc[tt][e];
+    for (int off = 32 >> RS; off >= 1; off >>= 1) v[0] += __shfl_xor(v[0], off, 64);
+    if ((lane & ((64 >> RS) - 1)) == 0) {
+        const int vi = lane >> (6 - RS);
+        part[wave][vi / EMAX][vi % EMAX] = v[0];
+    }
     __syncthreads();
     if (tid >= TPB) return;
     const int t = t0 + tid;
@@ -148,12 +171,21 @@ hipError_t launch_route_t(const moe_shape_t &s, const void *x, const void *wg, i
     return hipGetLastError();
 }
 
+// Few tokens: one token per workgroup, so that enough workgroups share the
+// reduction over d.  Many tokens: eight per workgroup, reusing each router
+// row read for all of them.
 template <typename T>
 hipError_t launch_route_dtype(const moe_shape_t &s, const void *x, const void *wg,
                               int32_t *idx, float *w, hipStream_t stream) {
-    if (s.n_experts <= 8) return launch_route_t<T, 8, 8>(s, x, wg, idx, w, stream);
-    if (s.n_experts <= 16) return launch_route_t<T, 16, 4>(s, x, wg, idx, w, stream);
-    return launch_route_t<T, 32, 2>(s, x, wg, idx, w, stream);
+    const bool few = s.T <= 256;
+    if (s.n_experts <= 8)
+        return few ? launch_route_t<T, 8, 1>(s, x, wg, idx, w, stream)
+                   : launch_route_t<T, 8, 8>(s, x, wg, idx, w, stream);
+    if (s.n_experts <= 16)
+        return few ? launch_route_t<T, 16, 1>(s, x, wg, idx, w, stream)
+                   : launch_route_t<T, 16, 4>(s, x, wg, idx, w, stream);
+    return few ? launch_route_t<T, 32, 1>(s, x, wg, idx, w, stream)
+               : launch_route_t<T, 32, 2>(s, x, wg, idx, w, stream);
 }
 
 }  // namespace
