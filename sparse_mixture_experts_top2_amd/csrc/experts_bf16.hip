@@ -61,6 +61,13 @@ __device__ __forceinline__ uint4 load_stream16(const uint16_t *p) {
     return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// 16-byte store with the non-temporal hint: output written once and not
+// re-read by this kernel, kept from displacing the operand tiles that the
+// workgroups on this XCD share through L2.
+__device__ __forceinline__ void store_stream16(uint16_t *p, uint4 v) {
+    __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t *>(p));
+}
+
 // ---------------------------------------------------------------------------
 // Prefill: LDS-tiled grouped GEMM.
 //   NMAT = 2: C = bf16(silu(A B0[e]) * (A B1[e]))   (gate/up, C = h)
@@ -412,29 +419,47 @@ __global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_dma_kernel(
 #pragma unroll
             for (int qq = 0; qq < 16; ++qq) acc[i][j][qq] = 0.0f;
 
+    // Operand fragments of one 32x32x16 step: A for MB row blocks, B for NB
+    // column blocks (two transpose reads each).
+    auto read_frags = [&](const uint8_t *stage, int h, bf16x8_t (&af)[MB], bf16x8_t (&bfr)[NB]) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+            af[i] = as_bf16x8(*reinterpret_cast<const uint4 *>(
+                stage + a_off[h] + i * 32 * (DBK * 2)));
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4_t *)(stage + b_off[j][0] + h * 8192));
+            s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4_t *)(stage + b_off[j][1] + h * 8192));
+            bfr[j] = __builtin_bit_cast(bf16x8_t,
+                                        __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+    };
+    // Software-pipelined over the stage's KS steps: the fragments of step
+    // h+1 are read while the MFMAs of step h run, so LDS latency hides
+    // behind matrix work instead of stalling every step.
     auto compute = [&](const uint8_t *stage) {
+        bf16x8_t af[2][MB], bfr[2][NB];
+        read_frags(stage, 0, af[0], bfr[0]);
 #pragma unroll
         for (int h = 0; h < KS; ++h) {
-            bf16x8_t af[MB], bfr[NB];
-#pragma unroll
-            for (int i = 0; i < MB; ++i)
-                af[i] = as_bf16x8(*reinterpret_cast<const uint4 *>(
-                    stage + a_off[h] + i * 32 * (DBK * 2)));
-#pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4_t *)(stage + b_off[j][0] + h * 8192));
-                s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4_t *)(stage + b_off[j][1] + h * 8192));
-                bfr[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3,
-                                                                                4, 5, 6, 7));
-            }
+            const int cur = h & 1;
+            if (h + 1 < KS) read_frags(stage, h + 1, af[cur ^ 1], bfr[cur ^ 1]);
 #pragma unroll
             for (int i = 0; i < MB; ++i)
 #pragma unroll
                 for (int j = 0; j < NB; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j],
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j],
                                                                          acc[i][j], 0, 0, 0);
+            if (h + 1 < KS) {
+                // Interleave: one operand read between consecutive MFMAs.
+#pragma unroll
+                for (int g = 0; g < MB * NB; ++g) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+                }
+            }
         }
     };
 
@@ -463,25 +488,58 @@ __global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_dma_kernel(
         }
     }
 
+    if constexpr (NMAT == 2) {
+        // h = silu(g) * u for the tile's 256 rows x 128 columns, staged
+        // through LDS (the ring is free now) as row-major bf16, then written
+        // out as full 16-byte row segments.  Storing 2-byte elements straight
+        // from the MFMA layout (one column per lane) cost a quarter of the
+        // kernel's time.
+        constexpr int HP = BNM + 8;                      // LDS row pitch (bf16)
+        constexpr int HALF = PBM / 2;                    // rows per stage buffer
+        static_assert(HALF * HP * 2 <= DSTAGE_BYTES, "half the h tile fits in one stage");
+        static_assert(TM == HALF, "each wavefront's rows lie in one half");
+        uint16_t *const hw = reinterpret_cast<uint16_t *>(wm == 0 ? st0 : st1);
+        __syncthreads();
 #pragma unroll
-    for (int i = 0; i < MB; ++i) {
+        for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int j = 0; j < (NMAT == 2 ? NB / 2 : NB); ++j) {
-            const int col = n0 + (NMAT == 2 ? wn * (TN / 2) + j * 32 : wn * TN + j * 32) +
-                            (lane & 31);
+            for (int j = 0; j < NB / 2; ++j)
 #pragma unroll
-            for (int qq = 0; qq < 16; ++qq) {
-                const int row =
-                    row0 + wm * TM + i * 32 + 8 * (qq >> 2) + 4 * (lane >> 5) + (qq & 3);
-                if (row >= row_end) continue;
-                if (NMAT == 2) {
+                for (int qq = 0; qq < 16; ++qq) {
+                    const int r = i * 32 + 8 * (qq >> 2) + 4 * (lane >> 5) + (qq & 3);
+                    const int cl = wn * (TN / 2) + j * 32 + (lane & 31);
                     const float hv = silu_f32(acc[i][j][qq]) * acc[i][j + NB / 2][qq];
-                    static_cast<uint16_t *>(C)[(size_t)row * N + col] = (uint16_t)f32_to_bf16(hv);
-                } else {
-                    static_cast<float *>(C)[(size_t)row * N + col] = acc[i][j][qq];
+                    hw[r * HP + cl] = (uint16_t)f32_to_bf16(hv);
                 }
+        __syncthreads();
+        constexpr int CH = BNM / 8;                      // 16-byte chunks per row
+        uint16_t *H = static_cast<uint16_t *>(C);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const uint16_t *hh = reinterpret_cast<const uint16_t *>(hf == 0 ? st0 : st1);
+            for (int v = tid; v < HALF * CH; v += NW * 64) {
+                const int r = v / CH, c8 = (v % CH) * 8;
+                if (row0 + hf * HALF + r < row_end)
+                    store_stream16(H + (size_t)(row0 + hf * HALF + r) * N + n0 + c8,
+                                   *reinterpret_cast<const uint4 *>(hh + r * HP + c8));
             }
         }
+    } else {
+        // 32x32 accumulator layout: value q of lane l is row
+        // 8*(q/4) + 4*(l/32) + q%4, column l%32 of the block.
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const int col = n0 + wn * TN + j * 32 + (lane & 31);
+#pragma unroll
+                for (int qq = 0; qq < 16; ++qq) {
+                    const int row =
+                        row0 + wm * TM + i * 32 + 8 * (qq >> 2) + 4 * (lane >> 5) + (qq & 3);
+                    if (row < row_end)
+                        static_cast<float *>(C)[(size_t)row * N + col] = acc[i][j][qq];
+                }
+            }
     }
 }
 
