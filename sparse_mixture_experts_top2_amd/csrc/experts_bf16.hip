@@ -85,7 +85,10 @@ constexpr int PBM = 256, PBN = 256, PBK = 64;
 constexpr int PLD = PBK + 8;  // LDS row pitch in bf16 (144 bytes): consecutive rows start
                               // 16 bytes apart modulo 128, so 8-lane groups of 16-byte
                               // reads and writes fall on distinct banks
-constexpr int PGM = 4;        // row tiles per scheduling group (see prefill_tile)
+#ifndef MOE_PREFILL_PGM
+#define MOE_PREFILL_PGM 4
+#endif
+constexpr int PGM = MOE_PREFILL_PGM;   // row tiles per scheduling group (see prefill_tile)
 #ifndef MOE_PREFILL_WN
 #define MOE_PREFILL_WN 4
 #endif
@@ -258,17 +261,20 @@ __global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_gemm_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Prefill, deep-pipelined variant (K % 32 == 0 and N a multiple of the tile's
+// Prefill, direct-to-LDS variant (K % 64 == 0 and N a multiple of the tile's
 // columns per matrix, which every Mixtral shape satisfies).  Same tiles and
 // schedule as prefill_gemm_kernel, but operands go from global memory
-// straight into a 4-stage LDS ring (global_load_lds_dwordx4: no registers,
-// no VALU work), so three K steps of loads are in flight while one computes.
+// straight into LDS rings (global_load_lds_dwordx4: no registers, no VALU
+// work).  The activation operand A has a 2-deep ring; the weight operand B,
+// whose tiles mostly come from HBM rather than L2, has a 3-deep ring, so its
+// loads are issued two K steps ahead.  Both rings together fill the 160 KiB
+// of LDS.
 //
 // LDS layouts (16-byte chunks are XOR-swizzled by row so that MFMA operand
 // reads from consecutive rows fall on distinct banks):
-//   A stage: 256 rows x 32 bf16 (64 B = 4 chunks); chunk c of row r holds
+//   A stage: 256 rows x 64 bf16 (128 B = 8 chunks); chunk c of row r holds
 //            K chunk c ^ aswz(r).
-//   B stage: 32 K rows x 256 columns (512 B = 32 chunks), the weights'
+//   B stage: 64 K rows x 256 columns (512 B = 32 chunks), the weights'
 //            own row-major layout (for gate/up: 128 gate then 128 up
 //            columns); chunk c of row r holds column chunk c ^ bswz(r).
 // A fragments are plain 16-byte reads.  B fragments use the CDNA4 LDS
@@ -277,36 +283,34 @@ __global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_gemm_kernel(
 // of those 4 rows, i.e. 4 consecutive K values of one column.  Two such
 // reads give the 8 K values a 32x32x16 operand lane holds.
 
-#ifndef MOE_DMA_BK
-#define MOE_DMA_BK 64
+constexpr int DBK = 64;                       // K per stage: every A row segment is
+                                              // one full 128-byte line
+#ifndef MOE_DMA_BSTAGES
+#define MOE_DMA_BSTAGES 3
 #endif
-constexpr int DBK = MOE_DMA_BK;               // K per stage: 64 makes every A row
-constexpr int DSTAGES = DBK == 64 ? 2 : 4;    // segment a full 128-byte line
-constexpr int DA_BYTES = PBM * DBK * 2;
-constexpr int DB_BYTES = DBK * PBN * 2;
-constexpr int DSTAGE_BYTES = DA_BYTES + DB_BYTES;
+constexpr int DBS = MOE_DMA_BSTAGES;          // B ring depth (A ring depth is 2)
+static_assert(DBS == 2 || DBS == 3, "B ring depth");
+constexpr int DA_BYTES = PBM * DBK * 2;       // 32 KiB
+constexpr int DB_BYTES = DBK * PBN * 2;       // 32 KiB
 constexpr int DACH = DBK / 8;                 // 16-byte chunks per A row
 
 // A swizzle: any 8 (and 16) consecutive rows reading the same K chunk land
 // on distinct 16-byte bank groups.
-__device__ __forceinline__ int aswz(int r) {
-    if (DACH == 8) return ((r >> 1) & 7) ^ ((r & 1) << 2);
-    return ((r >> 1) & 3) ^ ((r >> 3) & 1);
-}
+__device__ __forceinline__ int aswz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
 __device__ __forceinline__ int bswz(int r) { return (r & 7) << 2; }
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// Barrier of the LDS ring.  Each wavefront first waits until at most N of
+// Barrier of the LDS rings.  Each wavefront first waits until at most N of
 // its own LDS-DMA loads are outstanding (so its part of the stage about to
 // be read has landed) and until its LDS reads have returned (so the stage
 // about to be refilled is no longer being read), then all wavefronts meet.
 // __syncthreads() is not used here: its release fence waits for every
-// outstanding load, which would collapse the ring to one stage in flight.
-// The empty asm statements keep the compiler from moving memory accesses
-// across the barrier.  gfx9 s_waitcnt encoding: vmcnt bits 3:0 and 15:14,
-// expcnt 6:4 (left at its maximum), lgkmcnt 11:8 (zero).
+// outstanding load, which would drain the rings.  The empty asm statements
+// keep the compiler from moving memory accesses across the barrier.  gfx9
+// s_waitcnt encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4 (left at its
+// maximum), lgkmcnt 11:8 (zero).
 template <int N>
 __device__ __forceinline__ void ring_barrier() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -315,6 +319,18 @@ __device__ __forceinline__ void ring_barrier() {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
+
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1, so that i is a
+// constant inside f.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for_from(F &&f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for_from<I + 1, N>(f);
+    }
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) { static_for_from<0, N>(f); }
 
 template <int NMAT>
 __global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_dma_kernel(
@@ -327,7 +343,6 @@ __global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_dma_kernel(
     constexpr int BNM = PBN / NMAT;
     constexpr int AI = DA_BYTES / 1024 / NW;   // A load instructions per wave per stage
     constexpr int BI = DB_BYTES / 1024 / NW;   // B load instructions per wave per stage
-    constexpr int LPS = AI + BI;               // loads per lane per stage
     static_assert(NMAT == 1 || NB % 2 == 0, "gate/up blocks come in pairs");
 
     const int n_tiles = N / BNM;
@@ -335,24 +350,29 @@ __global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_dma_kernel(
     if (!prefill_tile(counts, offsets, E, n_tiles, e, row0, row_end, nt)) return;
     const int n0 = nt * BNM;
 
-    __shared__ __attribute__((aligned(1024))) uint8_t st0[DSTAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t st1[DSTAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) uint8_t st2[DSTAGES > 2 ? DSTAGE_BYTES : 16];
-    __shared__ __attribute__((aligned(1024))) uint8_t st3[DSTAGES > 2 ? DSTAGE_BYTES : 16];
+    // One array per ring slot: the compiler then knows that the LDS-DMA
+    // writes into one slot never alias the fragment reads from another and
+    // keeps them overlapped (with a single array it waits for every
+    // outstanding load before each read, about 15% slower).
+    __shared__ __attribute__((aligned(1024))) uint8_t sa0[DA_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t sa1[DA_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t sb0[DB_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t sb1[DB_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t sb2[DBS > 2 ? DB_BYTES : 16];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / PWN, wn = wave % PWN;
 
     // Global sources of this wave's load instructions.  A instruction g
-    // covers 64/DACH rows (DACH lanes x 16 B per row); B instruction g
-    // covers 2 K rows (32 lanes x 16 B each).  Addresses are recomputed at
-    // each issue from a few per-lane values, which keeps register use low.
+    // covers 8 rows (8 lanes x 16 B per row); B instruction g covers 2 K rows
+    // (32 lanes x 16 B each).  Addresses are recomputed at each issue from a
+    // few per-lane values, which keeps register use low.
     constexpr int AROWS = 64 / DACH;           // A rows per load instruction
     const int a_r0 = wave * AI * AROWS + lane / DACH;  // row of instruction 0
     int a_kc[2];                               // K chunk for even / odd instructions
 #pragma unroll
     for (int p = 0; p < 2; ++p) a_kc[p] = (lane % DACH) ^ aswz(a_r0 + p * AROWS);
-    // B: row parity pattern repeats every 4 instructions (bswz uses r & 7).
+    // B: the swizzle pattern repeats every 4 instructions (bswz uses r & 7).
     size_t b_base[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -370,19 +390,20 @@ __global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_dma_kernel(
         b_base[p] = (size_t)(base - B0) + (size_t)e * K * N + (size_t)r * N + col;
     }
 
-    auto issue = [&](uint8_t *stage, int k0) {
+    auto issue_a = [&](uint8_t *sa, int k0) {
 #pragma unroll
         for (int j = 0; j < AI; ++j) {
             const int r = min(row0 + a_r0 + j * AROWS, a_rows - 1);
             const uint16_t *src = A + (size_t)r * K + k0 + a_kc[j & 1] * 8;
-            __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(stage + (wave * AI + j) * 1024),
+            __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(sa + (wave * AI + j) * 1024),
                                              16, 0, 0);
         }
+    };
+    auto issue_b = [&](uint8_t *sb, int k0) {
 #pragma unroll
         for (int j = 0; j < BI; ++j) {
             const uint16_t *src = B0 + b_base[j & 3] + (size_t)(k0 + (j & ~3) * 2) * N;
-            __builtin_amdgcn_global_load_lds(src,
-                                             (lds_void_t *)(stage + DA_BYTES + (wave * BI + j) * 1024),
+            __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(sb + (wave * BI + j) * 1024),
                                              16, 0, 0);
         }
     };
@@ -407,7 +428,7 @@ __global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_dma_kernel(
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int r = 8 * (G >> 1) + 4 * u + jq;     // + 16 * step (immediate)
-            b_off[j][u] = DA_BYTES + r * 512 + ((((n >> 3) ^ bswz(r))) << 4) + (n & 7) * 2;
+            b_off[j][u] = r * 512 + ((((n >> 3) ^ bswz(r))) << 4) + (n & 7) * 2;
         }
     }
 
@@ -419,110 +440,123 @@ __global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_dma_kernel(
 #pragma unroll
             for (int qq = 0; qq < 16; ++qq) acc[i][j][qq] = 0.0f;
 
-    // Operand fragments of one 32x32x16 step: A for MB row blocks, B for NB
-    // column blocks (two transpose reads each).
-    auto read_frags = [&](const uint8_t *stage, int h, bf16x8_t (&af)[MB], bf16x8_t (&bfr)[NB]) {
+    // One stage, in halves of KH steps: the operand fragments of a half are
+    // read first (in step order, so the waits before each step's MFMAs are
+    // partial), and the scheduler interleaves the reads of one half with
+    // the MFMAs of the other (iglp strategy 0).
+#ifndef MOE_DMA_KH
+#define MOE_DMA_KH 1
+#endif
+    constexpr int KH = MOE_DMA_KH;
+    static_assert(KS % KH == 0, "whole halves");
+    auto compute = [&](const uint8_t *sa, const uint8_t *sb) {
+        __builtin_amdgcn_iglp_opt(0);
 #pragma unroll
-        for (int i = 0; i < MB; ++i)
-            af[i] = as_bf16x8(*reinterpret_cast<const uint4 *>(
-                stage + a_off[h] + i * 32 * (DBK * 2)));
+        for (int h0 = 0; h0 < KS; h0 += KH) {
+            bf16x8_t af[KH][MB], bfr[KH][NB];
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4_t *)(stage + b_off[j][0] + h * 8192));
-            s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4_t *)(stage + b_off[j][1] + h * 8192));
-            bfr[j] = __builtin_bit_cast(bf16x8_t,
-                                        __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        }
-    };
-    // Software-pipelined over the stage's KS steps: the fragments of step
-    // h+1 are read while the MFMAs of step h run, so LDS latency hides
-    // behind matrix work instead of stalling every step.
-    auto compute = [&](const uint8_t *stage) {
-        bf16x8_t af[2][MB], bfr[2][NB];
-        read_frags(stage, 0, af[0], bfr[0]);
+            for (int hh = 0; hh < KH; ++hh) {
+                const int h = h0 + hh;
 #pragma unroll
-        for (int h = 0; h < KS; ++h) {
-            const int cur = h & 1;
-            if (h + 1 < KS) read_frags(stage, h + 1, af[cur ^ 1], bfr[cur ^ 1]);
+                for (int i = 0; i < MB; ++i)
+                    af[hh][i] = as_bf16x8(*reinterpret_cast<const uint4 *>(
+                        sa + a_off[h] + i * 32 * (DBK * 2)));
 #pragma unroll
-            for (int i = 0; i < MB; ++i)
-#pragma unroll
-                for (int j = 0; j < NB; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j],
-                                                                         acc[i][j], 0, 0, 0);
-            if (h + 1 < KS) {
-                // Interleave: one operand read between consecutive MFMAs.
-#pragma unroll
-                for (int g = 0; g < MB * NB; ++g) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+                for (int j = 0; j < NB; ++j) {
+                    s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4_t *)(sb + b_off[j][0] + h * 8192));
+                    s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4_t *)(sb + b_off[j][1] + h * 8192));
+                    bfr[hh][j] = __builtin_bit_cast(
+                        bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 }
             }
+#pragma unroll
+            for (int hh = 0; hh < KH; ++hh)
+#pragma unroll
+                for (int i = 0; i < MB; ++i)
+#pragma unroll
+                    for (int j = 0; j < NB; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            af[hh][i], bfr[hh][j], acc[i][j], 0, 0, 0);
         }
     };
 
-    uint8_t *const stages[4] = {st0, st1, st2, st3};
+    // Issue order: B_0, A_0, B_1 (prologue), then at step kt A_{kt+1} and
+    // B_{kt+DBS-1}.  Stage kt has landed once at most the loads issued after
+    // A_kt are outstanding: B_{kt+1} when the B ring is 3 deep, else none.
+    // Loads are issued unconditionally, past the last stage with K clamped
+    // to it (harmless re-reads into free slots), so the steady-state loop has
+    // no branches and every wait count is a constant; the rings are drained
+    // before the epilogue reuses them.
     const int nk = K / DBK;
-    // Prologue: stages 0..2 in flight.
-#pragma unroll
-    for (int s = 0; s < DSTAGES - 1; ++s)
-        if (s < nk) issue(stages[s], s * DBK);
-    // Main loop, unrolled by the ring size so every stage index is static.
-    for (int kb = 0; kb < nk; kb += DSTAGES) {
-#pragma unroll
-        for (int s = 0; s < DSTAGES; ++s) {
-            const int kt = kb + s;
-            if (kt < nk) {
-                // Stage kt's loads are done once at most the loads of the
-                // stages issued after it are still outstanding.
-                const int later = min(DSTAGES - 2, nk - 1 - kt);
-                if (later >= 2) ring_barrier<2 * LPS>();
-                else if (later == 1) ring_barrier<LPS>();
-                else ring_barrier<0>();
-                if (kt + DSTAGES - 1 < nk)
-                    issue(stages[(s + DSTAGES - 1) % DSTAGES], (kt + DSTAGES - 1) * DBK);
-                compute(stages[s]);
-            }
-        }
-    }
+    auto kclamp = [&](int kt) { return min(kt, nk - 1) * DBK; };
+    issue_b(sb0, 0);
+    issue_a(sa0, 0);
+    if (DBS > 2) issue_b(sb1, kclamp(1));
+    constexpr int U = DBS == 3 ? 6 : 2;            // unroll: every ring slot is static
+    auto step = [&](auto s_c, int kt) {
+        constexpr int s = decltype(s_c)::value;
+        ring_barrier<(DBS > 2 ? BI : 0)>();
+        uint8_t *const sa_cur = s % 2 == 0 ? sa0 : sa1;
+        uint8_t *const sa_nxt = s % 2 == 0 ? sa1 : sa0;
+        uint8_t *const sb_cur = s % DBS == 0 ? sb0 : s % DBS == 1 ? sb1 : sb2;
+        uint8_t *const sb_nxt = (s + DBS - 1) % DBS == 0   ? sb0
+                                : (s + DBS - 1) % DBS == 1 ? sb1
+                                                           : sb2;
+        issue_a(sa_nxt, kclamp(kt + 1));
+        issue_b(sb_nxt, kclamp(kt + DBS - 1));
+        compute(sa_cur, sb_cur);
+    };
+    int kt = 0;
+    for (; kt + U <= nk; kt += U)
+        static_for<U>([&](auto s_c) { step(s_c, kt + decltype(s_c)::value); });
+    static_for<U - 1>([&](auto s_c) {
+        if (kt + decltype(s_c)::value < nk) step(s_c, kt + decltype(s_c)::value);
+    });
+    ring_barrier<0>();
 
     if constexpr (NMAT == 2) {
         // h = silu(g) * u for the tile's 256 rows x 128 columns, staged
-        // through LDS (the ring is free now) as row-major bf16, then written
-        // out as full 16-byte row segments.  Storing 2-byte elements straight
-        // from the MFMA layout (one column per lane) cost a quarter of the
-        // kernel's time.
+        // through LDS (the rings are free now) as row-major bf16, then
+        // written out as full 16-byte row segments.  Storing 2-byte elements
+        // straight from the MFMA layout (one column per lane) cost a quarter
+        // of the kernel's time.  Rows are split into four pieces of 64, piece
+        // p held by ring slot p.
         constexpr int HP = BNM + 8;                      // LDS row pitch (bf16)
-        constexpr int HALF = PBM / 2;                    // rows per stage buffer
-        static_assert(HALF * HP * 2 <= DSTAGE_BYTES, "half the h tile fits in one stage");
-        static_assert(TM == HALF, "each wavefront's rows lie in one half");
-        uint16_t *const hw = reinterpret_cast<uint16_t *>(wm == 0 ? st0 : st1);
+        constexpr int RQ = 64;
+        static_assert(RQ * HP * 2 <= DA_BYTES && RQ * HP * 2 <= DB_BYTES, "piece fits a slot");
+        static_assert(PBM / RQ == 4 && TM % RQ == 0, "four pieces, 32-row blocks inside one");
+        auto piece = [&](int pc) {
+            uint8_t *pp = sa0;
+            if (pc == 1) pp = sa1;
+            if (pc == 2) pp = sb0;
+            if (pc == 3) pp = sb1;
+            return reinterpret_cast<uint16_t *>(pp);
+        };
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < MB; ++i)
+        for (int i = 0; i < MB; ++i) {
+            const int rb = wm * TM + i * 32;             // first row of this block
+            uint16_t *const hw = piece(rb / RQ) + (rb % RQ) * HP;
 #pragma unroll
             for (int j = 0; j < NB / 2; ++j)
 #pragma unroll
                 for (int qq = 0; qq < 16; ++qq) {
-                    const int r = i * 32 + 8 * (qq >> 2) + 4 * (lane >> 5) + (qq & 3);
+                    const int r = 8 * (qq >> 2) + 4 * (lane >> 5) + (qq & 3);
                     const int cl = wn * (TN / 2) + j * 32 + (lane & 31);
                     const float hv = silu_f32(acc[i][j][qq]) * acc[i][j + NB / 2][qq];
                     hw[r * HP + cl] = (uint16_t)f32_to_bf16(hv);
                 }
+        }
         __syncthreads();
         constexpr int CH = BNM / 8;                      // 16-byte chunks per row
         uint16_t *H = static_cast<uint16_t *>(C);
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-            const uint16_t *hh = reinterpret_cast<const uint16_t *>(hf == 0 ? st0 : st1);
-            for (int v = tid; v < HALF * CH; v += NW * 64) {
-                const int r = v / CH, c8 = (v % CH) * 8;
-                if (row0 + hf * HALF + r < row_end)
-                    store_stream16(H + (size_t)(row0 + hf * HALF + r) * N + n0 + c8,
-                                   *reinterpret_cast<const uint4 *>(hh + r * HP + c8));
-            }
+        for (int v = tid; v < PBM * CH; v += NW * 64) {
+            const int r = v / CH, c8 = (v % CH) * 8;
+            if (row0 + r < row_end)
+                store_stream16(H + (size_t)(row0 + r) * N + n0 + c8,
+                               *reinterpret_cast<const uint4 *>(piece(r / RQ) + (r % RQ) * HP + c8));
         }
     } else {
         // 32x32 accumulator layout: value q of lane l is row

@@ -189,6 +189,41 @@ def test_bit_identical_reruns_and_token_permutation():
     assert row_max_rel_err(y3, y1[perm]) <= Y_TOL[wl.dtype]
 
 
+# Many-token shapes whose tile counts fall on either side of the CU count:
+#   40 tokens, f=2048: far fewer 256x256 tiles than CUs;
+#   1500 tokens, f=3968: between one and two tiles per CU (f not a multiple
+#       of 256, so gate/up's column tiles straddle the split of 2 x 128);
+#   3000 tokens: about three tiles per CU, ragged row tiles per expert.
+MANY_TOKENS = [
+    W.small_workload(40, 1024, 2048, seed=60),
+    W.small_workload(1500, 1024, 3968, seed=61),
+    W.small_workload(3000, 1024, 3968, seed=62),
+]
+
+
+@pytest.mark.parametrize("wl", MANY_TOKENS, ids=lambda w: w.name)
+def test_many_tokens_shared_workspace(wl):
+    """Parity, and bit-identical results over three calls that share one
+    workspace (nothing a call leaves in the workspace may leak into the
+    next)."""
+    announce(f"many tokens {wl.name}")
+    inp = checked_inputs(wl)
+    g = inp.to(DEV)
+    ws = moe.alloc_workspace(wl.T, wl.d, wl.f, wl.E, g.x.dtype, DEV)
+    ys = [moe.forward(g.x, g.w_gate, g.w1, g.w3, g.w2, workspace=ws) for _ in range(3)]
+    torch.cuda.synchronize()
+    for y in ys[1:]:
+        assert torch.equal(y.view(torch.int16), ys[0].view(torch.int16))
+    rng = np.random.default_rng(wl.seed)
+    rows = np.arange(wl.T) if wl.T <= 256 else np.sort(rng.choice(wl.T, 192, replace=False))
+    idx_o, _ = oracle.route(inp.x, inp.w_gate)
+    y_o, idx_s, _ = oracle.forward(inp.x[rows], inp.w_gate, inp.w1, inp.w3, inp.w2)
+    np.testing.assert_array_equal(idx_s, idx_o[rows])
+    err = row_max_rel_err(ys[0][torch.as_tensor(rows, device=DEV)], y_o)
+    announce(f"{wl.name} rows={len(rows)} row-max-rel err {err:.3e}")
+    assert err <= Y_TOL[wl.dtype], err
+
+
 def test_power_of_two_scaling_is_exact():
     wl = W.small_workload(64, 128, 256, dtype=W.F32, seed=60)
     g = checked_inputs(wl).to(DEV)
