@@ -12,6 +12,9 @@ GEMM: two thirds of the layer's bytes and FLOPs) is timed on its own with
 HIP events on the stream it runs on; its algorithmic bytes (decode, HBM
 bound: the selected experts' w1/w3 plus xp read and h written) or FLOPs
 (prefill, MFMA bound: 2 * 2T * d * 2f) per launch are divided by that time.
+``traffic`` is the measured HBM bytes per launch from the committed
+rocprofv3 counter summary under profiles/ (null once the kernels' source no
+longer matches the one the counters were taken on).
 
 The CPU baseline is the plain oracle (fp64, all host threads up to 16) run
 on the decode tokens for a bounded time.
@@ -114,7 +117,7 @@ def measure(wl_name, steps, warmup):
         ach = gu_bytes / (k_ms * 1e-3) / 1e9
         roof = {"kernel": "expert gate/up (weight-streaming MFMA)", "bound": "hbm",
                 "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": counter_traffic(wl_name),
                 "algorithmic_bytes_per_launch": gu_bytes, "avg_launch_ms": round(k_ms, 5)}
         lay = layer_bytes / (ms * 1e-3) / 1e9
         layer = {"bound": "hbm", "achieved": round(lay, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -123,7 +126,7 @@ def measure(wl_name, steps, warmup):
         ach = gu_flops / (k_ms * 1e-3) / 1e12
         roof = {"kernel": "expert gate/up (LDS-tiled MFMA grouped GEMM)", "bound": "mfma",
                 "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": counter_traffic(wl_name),
                 "algorithmic_flops_per_launch": gu_flops, "avg_launch_ms": round(k_ms, 5)}
         lay = layer_flops / (ms * 1e-3) / 1e12
         layer = {"bound": "mfma", "achieved": round(lay, 1), "peak": PEAK_BF16_TFLOPS,
@@ -134,6 +137,36 @@ def measure(wl_name, steps, warmup):
     return dict(wl=wl, inp=inp, ms=ms, ms_events=ms_events, wall_ms=wall_ms,
                 tokens_per_s=wl.T / (ms * 1e-3), roofline=roof, layer_roofline=layer,
                 counts=c, active_experts=active)
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_gateup_8x7b.md")
+
+
+def counter_traffic(wl_name):
+    """HBM bytes per gate/up launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, each scaled by a copy kernel of known
+    size), or None when there is no entry for this workload or the kernels'
+    source has changed since the counters were taken."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    block = text.rsplit("```", 2)[-2] if text.count("```") >= 2 else ""
+    kv = {}
+    for line in block.splitlines():
+        if ":" in line:
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    try:
+        src = os.path.join(ROOT, kv["source_file"])
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv["source_sha256"]:
+            return None
+        fields = dict(f.split("=") for f in kv[wl_name].split())
+        return int(round((float(fields["fetch_kib"]) * float(kv["fetch_scale"]) +
+                          float(fields["write_kib"]) * float(kv["write_scale"])) * 1024))
+    except (KeyError, ValueError, OSError):
+        return None
 
 
 def cpu_baseline(res, budget_s):
