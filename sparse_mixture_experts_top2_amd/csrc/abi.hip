@@ -21,6 +21,7 @@ Layout plan_workspace(const moe_shape_t &s) {
     L.counts = off;  off += align256(E * sizeof(int32_t));
     L.offsets = off; off += align256((E + 1) * sizeof(int32_t));
     L.pos = off;     off += align256(T * 2 * sizeof(int32_t));
+    L.src = off;     off += align256(T * 2 * sizeof(int32_t));
     L.xp = off;      off += align256(rows * d * eb);
     L.h = off;       off += align256(rows * f * eb);
     L.o = off;       off += align256(2 * T * d * sizeof(float));
@@ -227,8 +228,20 @@ int moe_forward(const moe_shape_t *s, const void *x, const void *w_gate, const v
     float *o = reinterpret_cast<float *>(base + L.o);
 
     hipError_t e = launch_route(*s, x, w_gate, idx, w, str);
-    if (e == hipSuccess) e = launch_dispatch(*s, x, idx, counts, offsets, pos, xp, str);
-    if (e == hipSuccess) e = launch_gateup(*s, xp, counts, offsets, w1, w3, h, str);
+    if (s->dtype == MOE_BF16 && s->T <= kDecodeMaxT) {
+        // Few tokens: the gate/up kernel gathers its rows straight from x
+        // through the row -> token table, so no xp copy is made.
+        int32_t *src = reinterpret_cast<int32_t *>(base + L.src);
+        if (e == hipSuccess) e = launch_rank(*s, idx, counts, offsets, pos, src, str);
+        if (e == hipSuccess)
+            e = launch_gateup_bf16(*s, static_cast<const uint16_t *>(x), counts, offsets,
+                                   static_cast<const uint16_t *>(w1),
+                                   static_cast<const uint16_t *>(w3),
+                                   static_cast<uint16_t *>(h), str, src);
+    } else {
+        if (e == hipSuccess) e = launch_dispatch(*s, x, idx, counts, offsets, pos, xp, str);
+        if (e == hipSuccess) e = launch_gateup(*s, xp, counts, offsets, w1, w3, h, str);
+    }
     if (e == hipSuccess) e = launch_down(*s, h, counts, offsets, w2, o, str);
     if (e == hipSuccess) e = launch_combine(*s, o, pos, w, y, str);
     return hip_status(e);

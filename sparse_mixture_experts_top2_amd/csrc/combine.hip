@@ -4,8 +4,12 @@
 // and the MoE module's accumulation of each slot's weighted expert output
 // into a zeroed output.  Here every row of y is written exactly once by a
 // gather, so no zero fill and no atomics are needed and the result does not
-// depend on scheduling.  One wavefront per token, 16-byte fp32 loads; bound
-// by HBM (2*T*d*4 bytes read, T*d*elem written).
+// depend on scheduling.  One wavefront per (token, column chunk), 16-byte
+// fp32 loads; with few tokens each row is cut into chunks so that the reads
+// spread over many CUs.  Bound by HBM (2*T*d*4 bytes read, T*d*elem
+// written).
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -15,14 +19,16 @@ template <bool BF16_OUT>
 __global__ __launch_bounds__(256) void combine_kernel(const float4 *__restrict__ o,
                                                       const int32_t *__restrict__ pos,
                                                       const float *__restrict__ w, int n_tok,
-                                                      int d4, void *__restrict__ y) {
+                                                      int d4, int chunk4,
+                                                      void *__restrict__ y) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= n_tok) return;
     const float4 *r0 = o + (size_t)pos[2 * t] * d4;
     const float4 *r1 = o + (size_t)pos[2 * t + 1] * d4;
     const float w0 = w[2 * t], w1 = w[2 * t + 1];
-    for (int j = lane; j < d4; j += 64) {
+    const int j1 = min(d4, (int)(blockIdx.y + 1) * chunk4);
+    for (int j = blockIdx.y * chunk4 + lane; j < j1; j += 64) {
         const float4 a = r0[j], b = r1[j];
         float4 v;
         v.x = w0 * a.x + w1 * b.x;
@@ -46,13 +52,18 @@ hipError_t launch_combine(const moe_shape_t &s, const float *o, const int32_t *p
                           const float *w, void *y, hipStream_t stream) {
     if (s.T == 0) return hipSuccess;
     const int d4 = s.d_model / 4;
-    const dim3 grid((s.T + 3) / 4), block(256);
+    // Column chunks of whole 64-vector passes, enough for ~512 workgroups.
+    const int tok_groups = (s.T + 3) / 4;
+    const int passes = (d4 + 63) / 64;
+    const int nch = std::max(1, std::min(passes, 512 / tok_groups));
+    const int chunk4 = (passes + nch - 1) / nch * 64;
+    const dim3 grid(tok_groups, (d4 + chunk4 - 1) / chunk4), block(256);
     if (s.dtype == MOE_BF16)
         hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, stream,
-                           reinterpret_cast<const float4 *>(o), pos, w, s.T, d4, y);
+                           reinterpret_cast<const float4 *>(o), pos, w, s.T, d4, chunk4, y);
     else
         hipLaunchKernelGGL(combine_kernel<false>, grid, block, 0, stream,
-                           reinterpret_cast<const float4 *>(o), pos, w, s.T, d4, y);
+                           reinterpret_cast<const float4 *>(o), pos, w, s.T, d4, chunk4, y);
     return hipGetLastError();
 }
 

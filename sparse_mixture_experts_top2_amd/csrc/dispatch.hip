@@ -5,11 +5,15 @@
 // loop; the order within an expert (token, then slot) is the order in which
 // that loop visits the tokens.
 //
-// Kernel 1 (one workgroup of 256 threads): thread i owns a contiguous run
-// of assignments.  Its per-expert counts go to LDS, one block-wide exclusive
-// scan per expert turns them into the thread's first rank inside each
-// expert, and a second pass over the run writes pos.  Thread order equals
-// assignment order, so the grouping is stable and the integers are exact.
+// Kernel 1 (one workgroup of 16 wavefronts): wavefront w owns a contiguous
+// run of assignments and walks it 64 at a time.  For each expert, a ballot
+// of the lanes holding that expert gives the number of such assignments in
+// the batch (popcount) and each lane's rank among them (popcount of the
+// lower lanes).  Pass 1 counts per wavefront and expert; a scan over
+// wavefronts and experts (in LDS) gives every wavefront's first rank in each
+// expert and the offsets; pass 2 writes pos.  Lane order and wavefront order
+// equal assignment order, so the grouping is stable and the integers are
+// exact.  Two barriers in all, whatever E is.
 // Kernel 2 (many workgroups): one wavefront per token copies the row with
 // 16-byte loads and stores; it is bound by HBM (T*d*elem read, 2*T*d*elem
 // written).
@@ -18,74 +22,108 @@
 namespace moe {
 namespace {
 
-constexpr int kScanThreads = 256;
-
-__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        int u = __shfl_up(v, off, 64);
-        if (lane >= off) v += u;
-    }
-    return v;
-}
+constexpr int kRankWaves = 16;
 
 __device__ __forceinline__ int clamp_expert(int e, int E) {
     return (int)min((unsigned)e, (unsigned)(E - 1));
 }
 
-__global__ __launch_bounds__(kScanThreads) void dispatch_rank_kernel(
+__global__ __launch_bounds__(kRankWaves * 64) void dispatch_rank_kernel(
     const int32_t *__restrict__ idx, int n_assign, int E, int32_t *__restrict__ counts,
-    int32_t *__restrict__ offsets, int32_t *__restrict__ pos) {
-    extern __shared__ int32_t lds[];
-    int32_t *hist = lds;                                // [E][kScanThreads]
-    int32_t *wave_tot = lds + E * kScanThreads;        // [kScanThreads / 64]
-    int32_t *off_sh = wave_tot + kScanThreads / 64;     // [E + 1]
+    int32_t *__restrict__ offsets, int32_t *__restrict__ pos, int32_t *__restrict__ src) {
+    __shared__ int32_t wbase[kRankWaves][kMaxExperts];   // per-wavefront counts, then bases
+    __shared__ int32_t ebase[kMaxExperts + 1];           // expert offsets
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint64_t lower = (1ull << lane) - 1ull;        // lanes below this one
+    // Contiguous runs of whole 64-assignment batches, in wavefront order.
+    const int batches = (n_assign + 63) / 64;
+    const int per = (batches + kRankWaves - 1) / kRankWaves;
+    const int a0 = min(n_assign, wave * per * 64), a1 = min(n_assign, a0 + per * 64);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int chunk = (n_assign + kScanThreads - 1) / kScanThreads;
-    const int a0 = min(n_assign, tid * chunk), a1 = min(n_assign, a0 + chunk);
-
-    for (int e = 0; e < E; ++e) hist[e * kScanThreads + tid] = 0;
-    // Expert ids are clamped into [0, E) so that a corrupt id can never send
-    // a row outside xp; valid ids are unaffected.
-    for (int a = a0; a < a1; ++a) hist[clamp_expert(idx[a], E) * kScanThreads + tid] += 1;
-    __syncthreads();
-
-    // Exclusive scan over threads, one expert at a time.
-    for (int e = 0; e < E; ++e) {
-        const int v = hist[e * kScanThreads + tid];
-        const int inc = wave_inclusive_scan(v, lane);
-        if (lane == 63) wave_tot[wave] = inc;
-        __syncthreads();
-        if (wave == 0) {
-            constexpr int nw = kScanThreads / 64;
-            int wt = lane < nw ? wave_tot[lane] : 0;
-            int winc = wave_inclusive_scan(wt, lane);
-            if (lane < nw) wave_tot[lane] = winc - wt;   // exclusive wave bases
-            if (lane == nw - 1) off_sh[e] = winc;        // this expert's total
+    // The run is read kLoadBatches batches at a time, all loads issued
+    // before any is used, so a pass costs one memory round trip per group
+    // rather than one per batch.  Expert ids are clamped into [0, E) so that
+    // a corrupt id can never send a row outside xp; valid ids are
+    // unaffected; -1 marks lanes past the run.
+    constexpr int kLoadBatches = 8;
+    auto load_group = [&](int g0, int (&ev)[kLoadBatches]) {
+#pragma unroll
+        for (int b = 0; b < kLoadBatches; ++b) {
+            const int a = g0 + b * 64 + lane;
+            ev[b] = a < a1 ? clamp_expert(idx[a], E) : -1;
         }
-        __syncthreads();
-        hist[e * kScanThreads + tid] = wave_tot[wave] + inc - v;
-        __syncthreads();
-    }
-    if (tid == 0) {
-        int run = 0;
-        for (int e = 0; e < E; ++e) {
-            int c = off_sh[e];
-            counts[e] = c;
-            offsets[e] = run;
-            off_sh[e] = run;
-            run += c;
+    };
+    // Pass 1: this wavefront's count per expert (lane e holds expert e).
+    int my_count = 0;
+    for (int g0 = a0; g0 < a1; g0 += kLoadBatches * 64) {
+        int ev[kLoadBatches];
+        load_group(g0, ev);
+#pragma unroll
+        for (int b = 0; b < kLoadBatches; ++b) {
+            if (g0 + b * 64 >= a1) break;
+            for (int x = 0; x < E; ++x) {
+                const int c = __popcll(__ballot(ev[b] == x));
+                if (lane == x) my_count += c;
+            }
         }
-        offsets[E] = run;
-        off_sh[E] = run;
+    }
+    if (lane < E) wbase[wave][lane] = my_count;
+    __syncthreads();
+    // Scan: for each expert, exclusive prefix over wavefronts; then the
+    // exclusive prefix of the expert totals (wave 0, lane e = expert e).
+    if (wave == 0) {
+        int tot = 0;
+        if (lane < E)
+            for (int w = 0; w < kRankWaves; ++w) {
+                const int c = wbase[w][lane];
+                wbase[w][lane] = tot;
+                tot += c;
+            }
+        int inc = tot;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int u = __shfl_up(inc, off, 64);
+            if (lane >= off) inc += u;
+        }
+        if (lane < E) {
+            counts[lane] = tot;
+            offsets[lane] = inc - tot;
+            ebase[lane] = inc - tot;
+        }
+        if (lane == E - 1) {
+            offsets[E] = inc;
+            ebase[E] = inc;
+        }
     }
     __syncthreads();
-    for (int a = a0; a < a1; ++a) {
-        const int e = clamp_expert(idx[a], E);
-        int32_t &r = hist[e * kScanThreads + tid];
-        pos[a] = off_sh[e] + r;
-        r += 1;
+    // Pass 2: rank of each assignment = expert offset + wavefront base +
+    // assignments of the same expert earlier in this wavefront's run.
+    // next[e] (this wavefront's row of LDS) is the next grouped row of
+    // expert e; each batch reads it once per lane and lane e advances it.
+    int32_t *next = wbase[wave];
+    if (lane < E) next[lane] += ebase[lane];
+    for (int g0 = a0; g0 < a1; g0 += kLoadBatches * 64) {
+        int ev[kLoadBatches];
+        load_group(g0, ev);
+#pragma unroll
+        for (int b = 0; b < kLoadBatches; ++b) {
+            const int a = g0 + b * 64;
+            if (a >= a1) break;
+            uint64_t mine = 0;   // lanes holding this lane's expert
+            int added = 0;       // lane e: assignments of expert e in the batch
+            for (int x = 0; x < E; ++x) {
+                const uint64_t m = __ballot(ev[b] == x);
+                if (ev[b] == x) mine = m;
+                if (lane == x) added = __popcll(m);
+            }
+            const int first = ev[b] >= 0 ? next[ev[b]] : 0;
+            if (ev[b] >= 0) {
+                const int p = first + __popcll(mine & lower);
+                pos[a + lane] = p;
+                if (src) src[p] = (a + lane) >> 1;   // token of grouped row p
+            }
+            if (lane < E) next[lane] += added;   // after every lane has read
+        }
     }
 }
 
@@ -108,14 +146,17 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const uint4 *__restri
 
 }  // namespace
 
+hipError_t launch_rank(const moe_shape_t &s, const int32_t *idx, int32_t *counts,
+                       int32_t *offsets, int32_t *pos, int32_t *src, hipStream_t stream) {
+    hipLaunchKernelGGL(dispatch_rank_kernel, dim3(1), dim3(kRankWaves * 64), 0, stream, idx,
+                       2 * s.T, s.n_experts, counts, offsets, pos, src);
+    return hipGetLastError();
+}
+
 hipError_t launch_dispatch(const moe_shape_t &s, const void *x, const int32_t *idx,
                            int32_t *counts, int32_t *offsets, int32_t *pos, void *xp,
                            hipStream_t stream) {
-    const int E = s.n_experts;
-    const size_t lds = sizeof(int32_t) * ((size_t)E * kScanThreads + kScanThreads / 64 + E + 1);
-    hipLaunchKernelGGL(dispatch_rank_kernel, dim3(1), dim3(kScanThreads), lds, stream, idx,
-                       2 * s.T, E, counts, offsets, pos);
-    hipError_t err = hipGetLastError();
+    hipError_t err = launch_rank(s, idx, counts, offsets, pos, nullptr, stream);
     if (err != hipSuccess || s.T == 0) return err;
     const int row_vecs = (int)((size_t)s.d_model * elem_bytes(s.dtype) / 16);
     hipLaunchKernelGGL(scatter_rows_kernel, dim3((s.T + 3) / 4), dim3(256), 0, stream,

@@ -285,11 +285,15 @@ __global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_gemm_kernel(
 
 constexpr int DBK = 64;                       // K per stage: every A row segment is
                                               // one full 128-byte line
+#ifndef MOE_DMA_ASTAGES
+#define MOE_DMA_ASTAGES 2
+#endif
 #ifndef MOE_DMA_BSTAGES
 #define MOE_DMA_BSTAGES 3
 #endif
-constexpr int DBS = MOE_DMA_BSTAGES;          // B ring depth (A ring depth is 2)
-static_assert(DBS == 2 || DBS == 3, "B ring depth");
+constexpr int DAS = MOE_DMA_ASTAGES;          // A ring depth
+constexpr int DBS = MOE_DMA_BSTAGES;          // B ring depth
+static_assert(DAS >= 2 && DBS >= 2 && DAS + DBS <= 5, "five 32 KiB slots fit in LDS");
 constexpr int DA_BYTES = PBM * DBK * 2;       // 32 KiB
 constexpr int DB_BYTES = DBK * PBN * 2;       // 32 KiB
 constexpr int DACH = DBK / 8;                 // 16-byte chunks per A row
@@ -319,6 +323,11 @@ __device__ __forceinline__ void ring_barrier() {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
+
+// The stage loop is built from lambdas; each must be inlined, or ring slots
+// would become run-time pointers (and every LDS read would wait for every
+// outstanding load).
+#define MOE_INLINE __attribute__((always_inline))
 
 // Calls f(std::integral_constant<int, i>) for i = 0 .. N-1, so that i is a
 // constant inside f.
@@ -356,9 +365,19 @@ __global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_dma_kernel(
     // outstanding load before each read, about 15% slower).
     __shared__ __attribute__((aligned(1024))) uint8_t sa0[DA_BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t sa1[DA_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t sa2[DAS > 2 ? DA_BYTES : 16];
     __shared__ __attribute__((aligned(1024))) uint8_t sb0[DB_BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t sb1[DB_BYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t sb2[DBS > 2 ? DB_BYTES : 16];
+    // Slot of stage i in each ring (i a compile-time constant at every use).
+    auto slot_a = [&](auto i_c) MOE_INLINE {
+        constexpr int i = decltype(i_c)::value % DAS;
+        return i == 0 ? sa0 : i == 1 ? sa1 : sa2;
+    };
+    auto slot_b = [&](auto i_c) MOE_INLINE {
+        constexpr int i = decltype(i_c)::value % DBS;
+        return i == 0 ? sb0 : i == 1 ? sb1 : sb2;
+    };
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / PWN, wn = wave % PWN;
@@ -390,7 +409,7 @@ __global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_dma_kernel(
         b_base[p] = (size_t)(base - B0) + (size_t)e * K * N + (size_t)r * N + col;
     }
 
-    auto issue_a = [&](uint8_t *sa, int k0) {
+    auto issue_a = [&](uint8_t *sa, int k0) MOE_INLINE {
 #pragma unroll
         for (int j = 0; j < AI; ++j) {
             const int r = min(row0 + a_r0 + j * AROWS, a_rows - 1);
@@ -399,7 +418,7 @@ __global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_dma_kernel(
                                              16, 0, 0);
         }
     };
-    auto issue_b = [&](uint8_t *sb, int k0) {
+    auto issue_b = [&](uint8_t *sb, int k0) MOE_INLINE {
 #pragma unroll
         for (int j = 0; j < BI; ++j) {
             const uint16_t *src = B0 + b_base[j & 3] + (size_t)(k0 + (j & ~3) * 2) * N;
@@ -449,7 +468,7 @@ __global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_dma_kernel(
 #endif
     constexpr int KH = MOE_DMA_KH;
     static_assert(KS % KH == 0, "whole halves");
-    auto compute = [&](const uint8_t *sa, const uint8_t *sb) {
+    auto compute = [&](const uint8_t *sa, const uint8_t *sb) MOE_INLINE {
         __builtin_amdgcn_iglp_opt(0);
 #pragma unroll
         for (int h0 = 0; h0 < KS; h0 += KH) {
@@ -482,36 +501,43 @@ __global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_dma_kernel(
         }
     };
 
-    // Issue order: B_0, A_0, B_1 (prologue), then at step kt A_{kt+1} and
-    // B_{kt+DBS-1}.  Stage kt has landed once at most the loads issued after
-    // A_kt are outstanding: B_{kt+1} when the B ring is 3 deep, else none.
+    // Issue order: at step kt, A_{kt+DAS-1} and B_{kt+DBS-1}, the operand
+    // with the shorter lookahead first; the prologue issues what steps -2
+    // and -1 would have.  Stage kt has landed once at most the loads issued
+    // after its later operand are outstanding: those of the deeper ring's
+    // operand issued in the same step (none when both rings are 2 deep).
     // Loads are issued unconditionally, past the last stage with K clamped
     // to it (harmless re-reads into free slots), so the steady-state loop has
     // no branches and every wait count is a constant; the rings are drained
     // before the epilogue reuses them.
     const int nk = K / DBK;
     auto kclamp = [&](int kt) { return min(kt, nk - 1) * DBK; };
-    issue_b(sb0, 0);
-    issue_a(sa0, 0);
-    if (DBS > 2) issue_b(sb1, kclamp(1));
-    constexpr int U = DBS == 3 ? 6 : 2;            // unroll: every ring slot is static
-    auto step = [&](auto s_c, int kt) {
+    constexpr int LA = DAS - 1, LB = DBS - 1;      // lookahead of each ring
+    constexpr int WAIT = DAS > DBS ? AI : DBS > DAS ? BI : 0;
+    auto issue_step = [&](auto s_c, int kt) MOE_INLINE {   // loads of step kt (slot s)
         constexpr int s = decltype(s_c)::value;
-        ring_barrier<(DBS > 2 ? BI : 0)>();
-        uint8_t *const sa_cur = s % 2 == 0 ? sa0 : sa1;
-        uint8_t *const sa_nxt = s % 2 == 0 ? sa1 : sa0;
-        uint8_t *const sb_cur = s % DBS == 0 ? sb0 : s % DBS == 1 ? sb1 : sb2;
-        uint8_t *const sb_nxt = (s + DBS - 1) % DBS == 0   ? sb0
-                                : (s + DBS - 1) % DBS == 1 ? sb1
-                                                           : sb2;
-        issue_a(sa_nxt, kclamp(kt + 1));
-        issue_b(sb_nxt, kclamp(kt + DBS - 1));
-        compute(sa_cur, sb_cur);
+        auto a = [&]() MOE_INLINE {
+            if (kt + LA >= 0)
+                issue_a(slot_a(std::integral_constant<int, s + LA>{}), kclamp(kt + LA));
+        };
+        auto b = [&]() MOE_INLINE {
+            if (kt + LB >= 0)
+                issue_b(slot_b(std::integral_constant<int, s + LB>{}), kclamp(kt + LB));
+        };
+        if (LA <= LB) { a(); b(); } else { b(); a(); }
+    };
+    constexpr int U = DAS == 3 || DBS == 3 ? 6 : 2;   // unroll: every ring slot is static
+    issue_step(std::integral_constant<int, U - 2>{}, -2);
+    issue_step(std::integral_constant<int, U - 1>{}, -1);
+    auto step = [&](auto s_c, int kt) MOE_INLINE {
+        ring_barrier<WAIT>();
+        issue_step(s_c, kt);
+        compute(slot_a(s_c), slot_b(s_c));
     };
     int kt = 0;
     for (; kt + U <= nk; kt += U)
-        static_for<U>([&](auto s_c) { step(s_c, kt + decltype(s_c)::value); });
-    static_for<U - 1>([&](auto s_c) {
+        static_for<U>([&](auto s_c) MOE_INLINE { step(s_c, kt + decltype(s_c)::value); });
+    static_for<U - 1>([&](auto s_c) MOE_INLINE {
         if (kt + decltype(s_c)::value < nk) step(s_c, kt + decltype(s_c)::value);
     });
     ring_barrier<0>();
@@ -594,7 +620,8 @@ template <int MB, int NMAT>
 __global__ __launch_bounds__(DWAVES * 64) void decode_gemm_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B0,
     const uint16_t *__restrict__ B1, void *__restrict__ C, const int32_t *__restrict__ counts,
-    const int32_t *__restrict__ offsets, int K, int N, int a_rows) {
+    const int32_t *__restrict__ offsets, int K, int N, int a_rows,
+    const int32_t *__restrict__ src) {
     const int e = blockIdx.y;
     const int Me = counts[e];
     if (Me == 0) return;  // an expert no token chose: its weights are never read
@@ -609,11 +636,14 @@ __global__ __launch_bounds__(DWAVES * 64) void decode_gemm_kernel(
     Bp[0] = B0 + (size_t)e * K * N + (col_ok ? col : 0);
     if (NMAT == 2) Bp[NMAT - 1] = B1 + (size_t)e * K * N + (col_ok ? col : 0);
     // Row i*16 + lane%16 of this expert; rows past the end of A are clamped
-    // onto its last row (their results are never stored).
+    // onto its last row (their results are never stored).  With src, grouped
+    // row r is row src[r] of A (A is then x itself: a gather, no copy).
     const uint16_t *Arow[MB];
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
-        Arow[i] = A + (size_t)min(r0 + i * 16 + (lane & 15), a_rows - 1) * K;
+    for (int i = 0; i < MB; ++i) {
+        const int r = min(r0 + i * 16 + (lane & 15), a_rows - 1);
+        Arow[i] = A + (size_t)(src ? src[r] : r) * K;
+    }
 
     f32x4_t acc[NMAT][MB][8];
 #pragma unroll
@@ -708,16 +738,18 @@ __global__ __launch_bounds__(DWAVES * 64) void decode_gemm_kernel(
 
 hipError_t launch_gateup_bf16(const moe_shape_t &s, const uint16_t *xp, const int32_t *counts,
                               const int32_t *offsets, const uint16_t *w1, const uint16_t *w3,
-                              uint16_t *h, hipStream_t stream) {
+                              uint16_t *h, hipStream_t stream, const int32_t *src) {
     const int d = s.d_model, f = s.d_ff, E = s.n_experts, rows = 2 * s.T;
     if (s.T <= 16) {
         hipLaunchKernelGGL((decode_gemm_kernel<1, 2>), dim3((f + DCOLS - 1) / DCOLS, E),
                            dim3(DWAVES * 64), 0, stream, xp, w1, w3, h, counts, offsets, d, f,
-                           rows);
+                           rows, src);
     } else if (s.T <= kDecodeMaxT) {
         hipLaunchKernelGGL((decode_gemm_kernel<2, 2>), dim3((f + DCOLS - 1) / DCOLS, E),
                            dim3(DWAVES * 64), 0, stream, xp, w1, w3, h, counts, offsets, d, f,
-                           rows);
+                           rows, src);
+    } else if (src) {
+        return hipErrorInvalidValue;   // the gather is only built into the decode kernels
     } else {
         const int grid = prefill_grid(rows, E, (f + PBN / 2 - 1) / (PBN / 2));
         if (d % DBK == 0 && f % (PBN / 2) == 0)
@@ -737,11 +769,11 @@ hipError_t launch_down_bf16(const moe_shape_t &s, const uint16_t *h, const int32
     if (s.T <= 16) {
         hipLaunchKernelGGL((decode_gemm_kernel<1, 1>), dim3((d + DCOLS - 1) / DCOLS, E),
                            dim3(DWAVES * 64), 0, stream, h, w2, nullptr, o, counts, offsets, f,
-                           d, rows);
+                           d, rows, nullptr);
     } else if (s.T <= kDecodeMaxT) {
         hipLaunchKernelGGL((decode_gemm_kernel<2, 1>), dim3((d + DCOLS - 1) / DCOLS, E),
                            dim3(DWAVES * 64), 0, stream, h, w2, nullptr, o, counts, offsets, f,
-                           d, rows);
+                           d, rows, nullptr);
     } else {
         const int grid = prefill_grid(rows, E, (d + PBN - 1) / PBN);
         if (f % DBK == 0 && d % PBN == 0)

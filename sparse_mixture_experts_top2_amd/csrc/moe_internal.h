@@ -18,7 +18,7 @@ constexpr int kMaxExperts = 32;
 constexpr int kDecodeMaxT = 32;
 
 struct Layout {
-    size_t idx, w, counts, offsets, pos, xp, h, o, total;
+    size_t idx, w, counts, offsets, pos, src, xp, h, o, total;
 };
 
 // Byte offsets of every workspace region for this shape (256-byte aligned).
@@ -35,6 +35,11 @@ hipError_t launch_route(const moe_shape_t &s, const void *x, const void *w_gate,
 hipError_t launch_dispatch(const moe_shape_t &s, const void *x, const int32_t *idx,
                            int32_t *counts, int32_t *offsets, int32_t *pos, void *xp,
                            hipStream_t stream);
+// The ranking half of the dispatch alone (counts, offsets, pos), plus, when
+// src is not NULL, src[r] = the token of grouped row r, for kernels that
+// gather their rows from x instead of reading xp.
+hipError_t launch_rank(const moe_shape_t &s, const int32_t *idx, int32_t *counts,
+                       int32_t *offsets, int32_t *pos, int32_t *src, hipStream_t stream);
 
 // Grouped SwiGLU over expert-sorted rows, in two launches:
 //   gate/up: h = silu(xp w1[e]) * (xp w3[e])    (h in the layer dtype)
@@ -56,9 +61,11 @@ hipError_t launch_gateup_f32(const moe_shape_t &s, const float *xp, const int32_
 hipError_t launch_down_f32(const moe_shape_t &s, const float *h, const int32_t *counts,
                            const int32_t *offsets, const float *w2, float *o,
                            hipStream_t stream);
+// With src not NULL (only for T <= kDecodeMaxT), row r of the activations
+// is read from xp + src[r] * d_model, i.e. xp is x itself.
 hipError_t launch_gateup_bf16(const moe_shape_t &s, const uint16_t *xp, const int32_t *counts,
                               const int32_t *offsets, const uint16_t *w1, const uint16_t *w3,
-                              uint16_t *h, hipStream_t stream);
+                              uint16_t *h, hipStream_t stream, const int32_t *src = nullptr);
 hipError_t launch_down_bf16(const moe_shape_t &s, const uint16_t *h, const int32_t *counts,
                             const int32_t *offsets, const uint16_t *w2, float *o,
                             hipStream_t stream);
