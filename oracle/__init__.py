@@ -66,6 +66,8 @@ def _bind(path: str):
     lib.oracle_expert_hidden.restype = I
     lib.oracle_expert_down.argtypes = [I, I, I, I, P, P, P, I, P, I]
     lib.oracle_expert_down.restype = I
+    lib.oracle_rmsnorm.argtypes = [I, I, P, P, ctypes.c_double, I, P, P, I]
+    lib.oracle_rmsnorm.restype = I
     return lib
 
 
@@ -269,6 +271,51 @@ def forward(x, w_gate, w1, w3, w2, threads: Optional[int] = None, return_logits=
     if rc != 0:
         raise ValueError("oracle_forward rejected its sizes")
     return (y, idx, w, logits) if return_logits else (y, idx, w)
+
+
+# ---------------------------------------------------------------------------
+# Block boundary ("Mixtral 8x7B -- The Evolving Transformer", section 03
+# MISTRAL BLOCK): the layer runs on rms_2 of the residual stream h and its
+# output is added back onto the stream.
+
+def rmsnorm(h, g, eps: float, threads: Optional[int] = None):
+    """xn = h * rstd * g, rounded once to h's dtype (RNE), with
+    rstd[t] = 1/sqrt(mean_j h[t,j]^2 + eps) in fp64.  Returns (xn as a torch
+    CPU tensor of h's dtype, rstd float64 [T])."""
+    import torch
+    ha, dh = _as_host(h)
+    ga, dg = _as_host(g)
+    dt = _same_dtype(dh, dg)
+    T, d = ha.shape
+    assert ga.shape == (d,)
+    xn = np.zeros_like(ha)
+    rstd = np.zeros(T, np.float64)
+    rc = _load().oracle_rmsnorm(T, d, _ptr(ha), _ptr(ga), ctypes.c_double(eps), dt, _ptr(xn),
+                                _ptr(rstd), threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_rmsnorm rejected its sizes or eps")
+    out = torch.from_numpy(xn.view(np.int16)).view(torch.bfloat16) if dt == ORC_BF16 \
+        else torch.from_numpy(xn)
+    return out, rstd
+
+
+def block_forward(h, g, eps: float, w_gate, w1, w3, w2, residual=None,
+                  threads: Optional[int] = None):
+    """out = residual + layer(rmsnorm(h)) in fp64 (residual None: no add).
+    Returns (out float64 [T,d], idx, w, xn)."""
+    xn, _ = rmsnorm(h, g, eps, threads=threads)
+    y, idx, w = forward(xn, w_gate, w1, w3, w2, threads=threads)
+    if residual is not None:
+        ra, code = _as_host(residual)
+        y = y + _to_f64(ra, code)
+    return y, idx, w, xn
+
+
+def _to_f64(a: np.ndarray, code: int) -> np.ndarray:
+    """Exact widening of an fp32 array or bf16 bit patterns to float64."""
+    if code == ORC_F32:
+        return a.astype(np.float64)
+    return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
 # ---------------------------------------------------------------------------

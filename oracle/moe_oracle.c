@@ -38,6 +38,16 @@
  *
  * Threads split the tokens; each token's arithmetic is the same sequential
  * loop whichever thread runs it.
+ *
+ * Block boundary (the same page, section 03 MISTRAL BLOCK and the Block
+ * module: the layer's input is rms_2 of the residual stream, and the
+ * layer's output is added back onto it):
+ *
+ *   r[t]    = 1 / sqrt( (1/d) sum_j h[t,j]^2 + eps )
+ *   xn[t,j] = h[t,j] * r[t] * g[j], rounded once to the layer dtype
+ *             (round to nearest, ties to even), the precision in which the
+ *             layer consumes its input
+ *   out[t]  = res[t] + y[t],  y = the layer applied to xn
  */
 #include <math.h>
 #include <pthread.h>
@@ -319,3 +329,63 @@ int oracle_forward(int T, int d, int f, int E, const void *x, const void *wg,
     parallel_for(T, threads, forward_range, &c);
     return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * Block boundary: RMSNorm before the layer.  */
+
+/* v rounded to the nearest bf16 value (8 significant bits), ties to even,
+ * taken directly from the double (no intermediate rounding to fp32). */
+static double round_bf16(double v) {
+    if (v == 0.0 || !isfinite(v)) return v;
+    int ex;
+    const double m = frexp(v, &ex);            /* |m| in [0.5, 1) */
+    const double r = nearbyint(ldexp(m, 8));   /* 8 significant bits, RNE */
+    return ldexp(r, ex - 8);
+}
+
+static void store_elem(void *p, int dtype, size_t i, double v) {
+    if (dtype == ORC_F32) {
+        ((float *)p)[i] = (float)v;            /* C conversion: round to nearest even */
+    } else {
+        const float f = (float)round_bf16(v);  /* exact: 8 significant bits */
+        uint32_t bits;
+        memcpy(&bits, &f, sizeof bits);
+        ((uint16_t *)p)[i] = (uint16_t)(bits >> 16);
+    }
+}
+
+struct norm_ctx {
+    int d, dtype;
+    const void *h, *g;
+    double eps;
+    void *xn;
+    double *rstd;
+};
+
+static void norm_range(void *p, int lo, int hi) {
+    const struct norm_ctx *c = (const struct norm_ctx *)p;
+    for (int t = lo; t < hi; ++t) {
+        const size_t row = (size_t)t * c->d;
+        double ss = 0.0;
+        for (int j = 0; j < c->d; ++j) {
+            const double v = load_elem(c->h, c->dtype, row + j);
+            ss += v * v;
+        }
+        const double r = 1.0 / sqrt(ss / (double)c->d + c->eps);
+        c->rstd[t] = r;
+        for (int j = 0; j < c->d; ++j)
+            store_elem(c->xn, c->dtype, row + j,
+                       load_elem(c->h, c->dtype, row + j) * r * load_elem(c->g, c->dtype, j));
+    }
+}
+
+/* xn [T,d] in the layer dtype and rstd [T] (fp64) from h [T,d] and the
+ * norm's per-channel weight g [d]. */
+int oracle_rmsnorm(int T, int d, const void *h, const void *g, double eps, int dtype,
+                   void *xn, double *rstd, int threads) {
+    if (T < 0 || d <= 0 || !(eps >= 0.0)) return 1;
+    struct norm_ctx c = {d, dtype, h, g, eps, xn, rstd};
+    parallel_for(T, threads, norm_range, &c);
+    return 0;
+}
+

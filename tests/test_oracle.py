@@ -253,11 +253,79 @@ def pin_dispatch_is_stable_grouping():
         np.testing.assert_array_equal(pos.reshape(-1)[order], np.arange(2 * T))
 
 
+def _bf16(vals):
+    return torch.tensor(vals, dtype=torch.float32).to(torch.bfloat16)
+
+
+def pin_rmsnorm_closed_forms():
+    """Hand-derived rows ("Mixtral 8x7B -- The Evolving Transformer",
+    section 03: rms_2 before the MoE).  A row of 3s with eps = 7 has mean
+    square 9, so rstd = 1/sqrt(16) = 1/4 and xn = 0.75 * g, exact in bf16.
+    The row (3, 4, 0, 0) has mean square 25/4, so with eps = 0 rstd = 2/5
+    and xn = (1.2, 1.6, 0, 0) * g, rounded once to bf16.  A zero row gives
+    xn = 0 and rstd = 1/sqrt(eps)."""
+    g = _bf16([1.0, 2.0, -0.5, 0.0])
+    xn, r = oracle.rmsnorm(_bf16([[3.0] * 4, [3.0, 4.0, 0.0, 0.0], [0.0] * 4]), g, 7.0)
+    np.testing.assert_array_equal(r[0], 0.25)
+    np.testing.assert_array_equal(xn[0].float().numpy(), [0.75, 1.5, -0.375, 0.0])
+    np.testing.assert_array_equal(r[2], 1.0 / np.sqrt(7.0))
+    np.testing.assert_array_equal(xn[2].float().numpy(), [0.0] * 4)
+    xn, r = oracle.rmsnorm(_bf16([[3.0, 4.0, 0.0, 0.0]]), g, 0.0)
+    np.testing.assert_array_equal(r[0], 0.4)
+    want = _bf16([1.2, 1.6 * 2.0, 0.0, 0.0]).float().numpy()   # RNE of the exact values
+    np.testing.assert_array_equal(xn[0].float().numpy(), want)
+    # fp32 layers: the same rows, rounded to fp32 instead
+    xn32, _ = oracle.rmsnorm(torch.tensor([[3.0, 4.0, 0.0, 0.0]]),
+                             torch.tensor([1.0, 2.0, -0.5, 0.0]), 0.0)
+    np.testing.assert_array_equal(xn32[0].numpy(), np.float32([1.2, 3.2, 0.0, 0.0]))
+
+
+def pin_rmsnorm_invariants():
+    """With eps = 0 the norm ignores the row's scale: a power-of-two
+    scaling of h leaves xn bit-identical.  Doubling g doubles xn exactly,
+    and a zero in g zeroes that channel."""
+    h = torch.randn(9, 64, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    g = torch.randn(64, generator=torch.Generator().manual_seed(4)).to(torch.bfloat16)
+    a, ra = oracle.rmsnorm(h, g, 0.0)
+    b, rb = oracle.rmsnorm((h.float() * 4.0).to(torch.bfloat16), g, 0.0)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    np.testing.assert_array_equal(ra, 4.0 * rb)
+    c, _ = oracle.rmsnorm(h, (g.float() * 2.0).to(torch.bfloat16), 0.0)
+    assert torch.equal(c.float(), a.float() * 2.0)
+    g0 = g.clone()
+    g0[5] = 0.0
+    z, _ = oracle.rmsnorm(h, g0, 0.0)
+    assert torch.all(z[:, 5].float() == 0.0)
+    # the mean square is over d: a row of ones has rstd 1 whatever d is
+    for d in (8, 200):
+        _, r1 = oracle.rmsnorm(torch.ones(1, d, dtype=torch.bfloat16),
+                               torch.ones(d, dtype=torch.bfloat16), 0.0)
+        np.testing.assert_array_equal(r1, [1.0])
+
+
+def pin_block_identities():
+    """out = res + layer(rmsnorm(h)): with W2 = 0 the layer adds nothing and
+    out is the residual exactly; otherwise out - res is the layer's output on
+    the normalised rows."""
+    inp = _rand_layer(T=12, d=16, f=24, seed=91, dtype=W.BF16)
+    g = torch.randn(16, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16)
+    out, idx, w, xn = oracle.block_forward(inp.x, g, 1e-5, inp.w_gate, inp.w1, inp.w3,
+                                           torch.zeros_like(inp.w2), residual=inp.x)
+    np.testing.assert_array_equal(out, inp.x.double().numpy())
+    out, idx, w, xn = oracle.block_forward(inp.x, g, 1e-5, inp.w_gate, inp.w1, inp.w3,
+                                           inp.w2, residual=inp.x)
+    y, idx2, _ = oracle.forward(xn, inp.w_gate, inp.w1, inp.w3, inp.w2)
+    np.testing.assert_array_equal(idx, idx2)
+    # fp64 rounding of the sum is the only difference
+    np.testing.assert_allclose(out - inp.x.double().numpy(), y, rtol=0, atol=1e-13)
+
+
 PINS = [pin_worked_examples, pin_logits_match_numpy, pin_top2_brute_force,
         pin_weights_closed_form_and_page_form, pin_forward_matches_numpy_dense,
         pin_expert_rows_match_numpy, pin_identical_experts_equal_dense_swiglu,
         pin_forced_one_hot_router, pin_power_of_two_scaling,
-        pin_expert_relabelling_and_token_permutation, pin_dispatch_is_stable_grouping]
+        pin_expert_relabelling_and_token_permutation, pin_dispatch_is_stable_grouping,
+        pin_rmsnorm_closed_forms, pin_rmsnorm_invariants, pin_block_identities]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -299,6 +367,13 @@ MUTANTS = {
                             "l[e] += xj * load_elem(wg, dtype, (size_t)e * d + j);"),
     "combine_second_slot_dropped": ("c->y[xo + m] = wt[0] * o0[m] + wt[1] * o1[m];",
                                     "c->y[xo + m] = wt[0] * o0[m] + wt[1] * o0[m];"),
+    "norm_sum_not_mean": ("sqrt(ss / (double)c->d + c->eps)", "sqrt(ss + c->eps)"),
+    "norm_no_sqrt": ("sqrt(ss / (double)c->d + c->eps)", "(ss / (double)c->d + c->eps)"),
+    "norm_eps_outside": ("1.0 / sqrt(ss / (double)c->d + c->eps)",
+                         "1.0 / (sqrt(ss / (double)c->d) + c->eps)"),
+    "norm_weight_dropped": ("load_elem(c->h, c->dtype, row + j) * r * load_elem(c->g, c->dtype, j)",
+                            "load_elem(c->h, c->dtype, row + j) * r"),
+    "norm_rounds_toward_zero": ("nearbyint(ldexp(m, 8))", "trunc(ldexp(m, 8))"),
 }
 
 
