@@ -19,6 +19,10 @@ longer matches the one the counters were taken on).
 The CPU baseline is the plain oracle (fp64, all host threads up to 16) run
 on the decode tokens for a bounded time.
 
+``block_boundary``: the same workloads through moe_block_forward (RMSNorm
+fused into the router, residual add into the combine), with the time the
+fused steps add over the plain layer.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 import argparse
@@ -49,6 +53,8 @@ def parse():
     ap.add_argument("--secondary", default="prefill_8x7b", help="'' to skip")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall time budget of the CPU oracle baseline (0 to skip)")
+    ap.add_argument("--no-block", dest="block", action="store_false",
+                    help="skip the block-boundary (RMSNorm + residual) measurement")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this size (for counter scaling)")
     return ap.parse_args()
@@ -139,6 +145,36 @@ def measure(wl_name, steps, warmup):
                 counts=c, active_experts=active)
 
 
+def measure_block(wl_name, steps, warmup, plain_ms):
+    """The block boundary on the same workload: out = x + layer(RMSNorm(x))
+    in one moe_block_forward call (norm fused into the router, residual into
+    the combine), timed like the plain layer.  Reports its step time and
+    the cost of the fused norm and residual over the plain layer."""
+    import torch
+    import sparse_mixture_experts_top2_amd as moe
+    from sparse_mixture_experts_top2_amd import workloads as W
+
+    wl = W.WORKLOADS[wl_name]
+    dev = torch.device("cuda:0")
+    inp = W.make_inputs(wl, device="cuda")
+    g = W.make_norm_weight(wl.d, wl.seed + 500, wl.dtype, device="cuda")
+    stream = torch.cuda.current_stream(dev)
+    ws = moe.alloc_workspace(wl.T, wl.d, wl.f, wl.E, inp.x.dtype, dev)
+    out = torch.empty_like(inp.x)
+
+    def step():
+        moe.block_forward(inp.x, g, 1e-5, inp.w_gate, inp.w1, inp.w3, inp.w2, residual=inp.x,
+                          workspace=ws, out=out)
+
+    for _ in range(warmup):
+        step()
+    ms = time_region(step, steps, stream)
+    log(f"{wl_name} block: {ms:.4f} ms/step ({wl.T / ms * 1e3:.0f} tokens/s)")
+    return {"workload": wl_name, "value": round(wl.T / (ms * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_step": round(ms, 5), "steps": steps, "warmup": warmup,
+            "fused_norm_residual_ms": round(ms - plain_ms, 5)}
+
+
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_gateup_8x7b.md")
 
 
@@ -226,10 +262,15 @@ def main():
 
     steps, warmup = defaults(args.workload)
     main_res = measure(args.workload, steps, warmup)
+    blocks = []
+    if args.block:
+        blocks.append(measure_block(args.workload, steps, warmup, main_res["ms"]))
     sec = None
     if args.secondary:
         s_steps, s_warm = defaults(args.secondary)
         r = measure(args.secondary, s_steps, s_warm)
+        if args.block:
+            blocks.append(measure_block(args.secondary, s_steps, s_warm, r["ms"]))
         sec = {"workload": r["wl"].name, "value": round(r["tokens_per_s"], 1), "unit": "tokens/s",
                "ms_per_step": round(r["ms"], 5), "steps": s_steps, "warmup": s_warm,
                "config": {"T": r["wl"].T, "d_model": r["wl"].d, "d_ff": r["wl"].f,
@@ -263,6 +304,7 @@ def main():
         "expert_counts": main_res["counts"],
         "cpu_baseline": cpu,
         "secondary": sec,
+        "block_boundary": blocks or None,
     }
     print(json.dumps(out), flush=True)
 

@@ -150,6 +150,34 @@ int moe_forward(const moe_shape_t *shape, const void *x, const void *w_gate,
                 int32_t *topk_idx_opt, float *topk_w_opt,
                 void *ws, size_t ws_bytes, void *stream);
 
+/* ---- Block boundary ----------------------------------------------------
+ * The Mistral block of "Mixtral 8x7B -- The Evolving Transformer", section
+ * 03 MISTRAL BLOCK, runs the layer on rms_2 of the residual stream and adds
+ * its output back onto the stream.  These calls fuse both into the layer:
+ *   rstd[t]  = 1 / sqrt( (1/d) sum_j h[t,j]^2 + eps )        (fp32)
+ *   xn[t,j]  = h[t,j] * rstd[t] * rms_weight[j], rounded to the layer dtype
+ *   out[t]   = residual[t] + layer(xn)[t], rounded once to the layer dtype
+ * rms_weight is [d] in the layer dtype; eps must be finite and >= 0
+ * (MOE_ERR_SHAPE otherwise). */
+
+/* Router on the normalised rows: writes xn [T, d] (layer dtype) and the
+ * routing as moe_route does, routing on xn as rounded.  xn must not overlap
+ * h. */
+int moe_rmsnorm_route(const moe_shape_t *shape, const void *h, const void *rms_weight,
+                      float eps, const void *w_gate, void *xn, int32_t *topk_idx,
+                      float *topk_w, void *stream);
+
+/* The whole block boundary: out = residual + layer(RMSNorm(h)).  residual
+ * may be NULL (out = layer(RMSNorm(h))) and is usually h itself.  out may
+ * be exactly h or exactly residual (an in-place update of the stream); any
+ * other overlap with them is MOE_ERR_ALIAS.  topk_idx_opt / topk_w_opt as
+ * in moe_forward.  ws / ws_bytes: workspace of at least
+ * moe_workspace_bytes(shape) (it holds xn). */
+int moe_block_forward(const moe_shape_t *shape, const void *h, const void *rms_weight,
+                      float eps, const void *residual, const void *w_gate, const void *w1,
+                      const void *w3, const void *w2, void *out, int32_t *topk_idx_opt,
+                      float *topk_w_opt, void *ws, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

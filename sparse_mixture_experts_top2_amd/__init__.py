@@ -27,7 +27,7 @@ STATUS_NAMES = ["MOE_OK", "MOE_ERR_NULL", "MOE_ERR_SHAPE", "MOE_ERR_DTYPE", "MOE
                 "MOE_ERR_ALIAS", "MOE_ERR_WORKSPACE", "MOE_ERR_UNSUPPORTED", "MOE_ERR_HIP"]
 EXPORTED = ["moe_status_str", "moe_workspace_bytes", "moe_route", "moe_dispatch",
             "moe_expert_gateup", "moe_expert_down", "moe_experts", "moe_combine",
-            "moe_forward"]
+            "moe_forward", "moe_rmsnorm_route", "moe_block_forward"]
 
 
 class MoeShape(ctypes.Structure):
@@ -75,6 +75,11 @@ def load_library(path: Optional[str] = None):
     lib.moe_combine.restype = I
     lib.moe_forward.argtypes = [S, P, P, P, P, P, P, P, P, P, Z, P]
     lib.moe_forward.restype = I
+    F = ctypes.c_float
+    lib.moe_rmsnorm_route.argtypes = [S, P, P, F, P, P, P, P, P]
+    lib.moe_rmsnorm_route.restype = I
+    lib.moe_block_forward.argtypes = [S, P, P, F, P, P, P, P, P, P, P, P, P, Z, P]
+    lib.moe_block_forward.restype = I
     if path is None:
         _lib = lib
     return lib
@@ -294,3 +299,62 @@ def forward(x: torch.Tensor, w_gate: torch.Tensor, w1: torch.Tensor, w3: torch.T
                                     _stream(x.device))
     _check(st, "moe_forward")
     return (y, idx, w) if return_routing else y
+
+
+def rmsnorm_route(h: torch.Tensor, rms_weight: torch.Tensor, eps: float, w_gate: torch.Tensor,
+                  xn: Optional[torch.Tensor] = None):
+    """Router on RMSNorm(h).  Returns (xn [T, d], topk_idx int32 [T, 2],
+    topk_w fp32 [T, 2])."""
+    _need(h, "h")
+    T, d = h.shape
+    _need(rms_weight, "rms_weight", h.dtype, h.device, (d,))
+    _need(w_gate, "w_gate", h.dtype, h.device)
+    E = w_gate.shape[1]
+    _need(w_gate, "w_gate", shape=(d, E))
+    xn = xn if xn is not None else torch.empty_like(h)
+    _need(xn, "xn", h.dtype, h.device, (T, d))
+    idx = torch.empty(T, 2, dtype=torch.int32, device=h.device)
+    w = torch.empty(T, 2, dtype=torch.float32, device=h.device)
+    shape = make_shape(T, d, 8, E, h.dtype)
+    st = load_library().moe_rmsnorm_route(ctypes.byref(shape), _ptr(h), _ptr(rms_weight),
+                                          float(eps), _ptr(w_gate), _ptr(xn), _ptr(idx), _ptr(w),
+                                          _stream(h.device))
+    _check(st, "moe_rmsnorm_route")
+    return xn, idx, w
+
+
+def block_forward(h: torch.Tensor, rms_weight: torch.Tensor, eps: float, w_gate: torch.Tensor,
+                  w1: torch.Tensor, w3: torch.Tensor, w2: torch.Tensor,
+                  residual: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, return_routing: bool = False,
+                  out: Optional[torch.Tensor] = None):
+    """out = residual + layer(RMSNorm(h)) (no add when residual is None).
+    Returns out [T, d] (and (topk_idx, topk_w) when ``return_routing``)."""
+    _need(h, "h")
+    T, d = h.shape
+    _need(rms_weight, "rms_weight", h.dtype, h.device, (d,))
+    _need(w_gate, "w_gate", h.dtype, h.device)
+    E = w_gate.shape[1]
+    _need(w_gate, "w_gate", shape=(d, E))
+    _need(w1, "w1", h.dtype, h.device)
+    f = w1.shape[2]
+    _need(w1, "w1", shape=(E, d, f))
+    _need(w3, "w3", h.dtype, h.device, (E, d, f))
+    _need(w2, "w2", h.dtype, h.device, (E, f, d))
+    if residual is not None:
+        _need(residual, "residual", h.dtype, h.device, (T, d))
+    ws = workspace if workspace is not None else alloc_workspace(T, d, f, E, h.dtype, h.device)
+    y = out if out is not None else torch.empty(T, d, dtype=h.dtype, device=h.device)
+    _need(y, "out", h.dtype, h.device, (T, d))
+    idx = w = None
+    if return_routing:
+        idx = torch.empty(T, 2, dtype=torch.int32, device=h.device)
+        w = torch.empty(T, 2, dtype=torch.float32, device=h.device)
+    shape = make_shape(T, d, f, E, h.dtype)
+    st = load_library().moe_block_forward(ctypes.byref(shape), _ptr(h), _ptr(rms_weight),
+                                          float(eps), _ptr(residual), _ptr(w_gate), _ptr(w1),
+                                          _ptr(w3), _ptr(w2), _ptr(y), _ptr(idx), _ptr(w), _ptr(ws),
+                                          ws.numel(), _stream(h.device))
+    _check(st, "moe_block_forward")
+    return (y, idx, w) if return_routing else y
+

@@ -2,6 +2,7 @@
 // sequence of the layer (route -> dispatch -> experts -> combine), all
 // enqueued on the caller's stream with no host synchronisation.  The
 // contract of every entry point is stated in include/moe.h.
+#include <math.h>
 #include <string.h>
 
 #include "moe_internal.h"
@@ -22,6 +23,7 @@ Layout plan_workspace(const moe_shape_t &s) {
     L.offsets = off; off += align256((E + 1) * sizeof(int32_t));
     L.pos = off;     off += align256(T * 2 * sizeof(int32_t));
     L.src = off;     off += align256(T * 2 * sizeof(int32_t));
+    L.xn = off;      off += align256(T * d * eb);
     L.xp = off;      off += align256(rows * d * eb);
     L.h = off;       off += align256(rows * f * eb);
     L.o = off;       off += align256(2 * T * d * sizeof(float));
@@ -80,6 +82,52 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Overlap that is not an exact alias (same start, same size).
+bool partial_overlap(const void *a, const void *b, size_t n) {
+    return a != b && overlap(a, n, b, n);
+}
+
+// The layer's launch sequence.  With g (RMSNorm weight) the router first
+// normalises x into the workspace and every later step reads the normalised
+// rows; with res the combine adds the residual.
+hipError_t run_layer(const moe_shape_t &s, const void *x, const void *g, float eps,
+                     const void *w_gate, const void *w1, const void *w3, const void *w2,
+                     void *y, const void *res, int32_t *idx, float *w, const Layout &L,
+                     char *base, hipStream_t str) {
+    int32_t *counts = reinterpret_cast<int32_t *>(base + L.counts);
+    int32_t *offsets = reinterpret_cast<int32_t *>(base + L.offsets);
+    int32_t *pos = reinterpret_cast<int32_t *>(base + L.pos);
+    void *xp = base + L.xp;
+    void *h = base + L.h;
+    float *o = reinterpret_cast<float *>(base + L.o);
+
+    hipError_t e;
+    const void *xin = x;
+    if (g) {
+        xin = base + L.xn;
+        e = launch_route_norm(s, x, g, eps, w_gate, base + L.xn, idx, w, str);
+    } else {
+        e = launch_route(s, x, w_gate, idx, w, str);
+    }
+    if (s.dtype == MOE_BF16 && s.T <= kDecodeMaxT) {
+        // Few tokens: the gate/up kernel gathers its rows straight from the
+        // layer input through the row -> token table, so no xp copy is made.
+        int32_t *src = reinterpret_cast<int32_t *>(base + L.src);
+        if (e == hipSuccess) e = launch_rank(s, idx, counts, offsets, pos, src, str);
+        if (e == hipSuccess)
+            e = launch_gateup_bf16(s, static_cast<const uint16_t *>(xin), counts, offsets,
+                                   static_cast<const uint16_t *>(w1),
+                                   static_cast<const uint16_t *>(w3),
+                                   static_cast<uint16_t *>(h), str, src);
+    } else {
+        if (e == hipSuccess) e = launch_dispatch(s, xin, idx, counts, offsets, pos, xp, str);
+        if (e == hipSuccess) e = launch_gateup(s, xp, counts, offsets, w1, w3, h, str);
+    }
+    if (e == hipSuccess) e = launch_down(s, h, counts, offsets, w2, o, str);
+    if (e == hipSuccess) e = launch_combine(s, o, pos, w, y, str, res);
+    return e;
+}
 
 }  // namespace
 
@@ -216,35 +264,58 @@ int moe_forward(const moe_shape_t *s, const void *x, const void *w_gate, const v
     const size_t act = (size_t)s->T * s->d_model * elem_bytes(s->dtype);
     if (overlap(y, act, x, act)) return MOE_ERR_ALIAS;
 
-    hipStream_t str = (hipStream_t)stream;
     char *base = static_cast<char *>(ws);
     int32_t *idx = topk_idx_opt ? topk_idx_opt : reinterpret_cast<int32_t *>(base + L.idx);
     float *w = topk_w_opt ? topk_w_opt : reinterpret_cast<float *>(base + L.w);
-    int32_t *counts = reinterpret_cast<int32_t *>(base + L.counts);
-    int32_t *offsets = reinterpret_cast<int32_t *>(base + L.offsets);
-    int32_t *pos = reinterpret_cast<int32_t *>(base + L.pos);
-    void *xp = base + L.xp;
-    void *h = base + L.h;
-    float *o = reinterpret_cast<float *>(base + L.o);
+    return hip_status(run_layer(*s, x, nullptr, 0.0f, w_gate, w1, w3, w2, y, nullptr, idx, w, L,
+                                base, (hipStream_t)stream));
+}
 
-    hipError_t e = launch_route(*s, x, w_gate, idx, w, str);
-    if (s->dtype == MOE_BF16 && s->T <= kDecodeMaxT) {
-        // Few tokens: the gate/up kernel gathers its rows straight from x
-        // through the row -> token table, so no xp copy is made.
-        int32_t *src = reinterpret_cast<int32_t *>(base + L.src);
-        if (e == hipSuccess) e = launch_rank(*s, idx, counts, offsets, pos, src, str);
-        if (e == hipSuccess)
-            e = launch_gateup_bf16(*s, static_cast<const uint16_t *>(x), counts, offsets,
-                                   static_cast<const uint16_t *>(w1),
-                                   static_cast<const uint16_t *>(w3),
-                                   static_cast<uint16_t *>(h), str, src);
-    } else {
-        if (e == hipSuccess) e = launch_dispatch(*s, x, idx, counts, offsets, pos, xp, str);
-        if (e == hipSuccess) e = launch_gateup(*s, xp, counts, offsets, w1, w3, h, str);
-    }
-    if (e == hipSuccess) e = launch_down(*s, h, counts, offsets, w2, o, str);
-    if (e == hipSuccess) e = launch_combine(*s, o, pos, w, y, str);
-    return hip_status(e);
+int moe_rmsnorm_route(const moe_shape_t *s, const void *h, const void *rms_weight, float eps,
+                      const void *w_gate, void *xn, int32_t *topk_idx, float *topk_w,
+                      void *stream) {
+    int st = check_shape(s);
+    if (st) return st;
+    if (!(eps >= 0.0f) || eps == INFINITY) return MOE_ERR_SHAPE;
+    if (s->T == 0) return MOE_OK;  // nothing to read or write
+    if (!h || !rms_weight || !w_gate || !xn || !topk_idx || !topk_w) return MOE_ERR_NULL;
+    if (misaligned(h) || misaligned(rms_weight) || misaligned(w_gate) || misaligned(xn) ||
+        misaligned(topk_idx) || misaligned(topk_w))
+        return MOE_ERR_ALIGN;
+    const size_t act = (size_t)s->T * s->d_model * elem_bytes(s->dtype);
+    if (overlap(xn, act, h, act)) return MOE_ERR_ALIAS;
+    return hip_status(launch_route_norm(*s, h, rms_weight, eps, w_gate, xn, topk_idx, topk_w,
+                                        (hipStream_t)stream));
+}
+
+int moe_block_forward(const moe_shape_t *s, const void *h, const void *rms_weight, float eps,
+                      const void *residual, const void *w_gate, const void *w1, const void *w3,
+                      const void *w2, void *out, int32_t *topk_idx_opt, float *topk_w_opt,
+                      void *ws, size_t ws_bytes, void *stream) {
+    int st = check_shape(s);
+    if (st) return st;
+    if (!(eps >= 0.0f) || eps == INFINITY) return MOE_ERR_SHAPE;
+    if (s->T == 0) return MOE_OK;  // nothing to read or write
+    if (!h || !rms_weight || !w_gate || !w1 || !w3 || !w2 || !out) return MOE_ERR_NULL;
+    if (misaligned(h) || misaligned(rms_weight) || misaligned(residual) || misaligned(w_gate) ||
+        misaligned(w1) || misaligned(w3) || misaligned(w2) || misaligned(out) ||
+        misaligned(topk_idx_opt) || misaligned(topk_w_opt))
+        return MOE_ERR_ALIGN;
+    const Layout L = plan_workspace(*s);
+    if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    if (misaligned(ws)) return MOE_ERR_ALIGN;
+    // out may be h or the residual itself (an in-place block update): h is
+    // read only by the first kernel, and the combine reads each residual
+    // element before writing it.  Partial overlaps are refused.
+    const size_t act = (size_t)s->T * s->d_model * elem_bytes(s->dtype);
+    if (partial_overlap(out, h, act) || (residual && partial_overlap(out, residual, act)))
+        return MOE_ERR_ALIAS;
+
+    char *base = static_cast<char *>(ws);
+    int32_t *idx = topk_idx_opt ? topk_idx_opt : reinterpret_cast<int32_t *>(base + L.idx);
+    float *w = topk_w_opt ? topk_w_opt : reinterpret_cast<float *>(base + L.w);
+    return hip_status(run_layer(*s, h, rms_weight, eps, w_gate, w1, w3, w2, out, residual, idx,
+                                w, L, base, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -15,12 +15,16 @@
 namespace moe {
 namespace {
 
+// With res (the residual stream, same dtype as y), y = res + combine: the
+// block's residual add ("Mixtral 8x7B -- The Evolving Transformer", section
+// 03 MISTRAL BLOCK), still rounded once.  y may be res itself: each element
+// is read before the same thread writes it.
 template <bool BF16_OUT>
 __global__ __launch_bounds__(256) void combine_kernel(const float4 *__restrict__ o,
                                                       const int32_t *__restrict__ pos,
                                                       const float *__restrict__ w, int n_tok,
-                                                      int d4, int chunk4,
-                                                      void *__restrict__ y) {
+                                                      int d4, int chunk4, const void *res,
+                                                      void *y) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= n_tok) return;
@@ -35,6 +39,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const float4 *__restrict__
         v.y = w0 * a.y + w1 * b.y;
         v.z = w0 * a.z + w1 * b.z;
         v.w = w0 * a.w + w1 * b.w;
+        if (res) {
+            float4 r;
+            if (BF16_OUT) {
+                const uint2 p = reinterpret_cast<const uint2 *>(res)[(size_t)t * d4 + j];
+                r = make_float4(bf16_to_f32(p.x & 0xffffu), bf16_to_f32(p.x >> 16),
+                                bf16_to_f32(p.y & 0xffffu), bf16_to_f32(p.y >> 16));
+            } else {
+                r = reinterpret_cast<const float4 *>(res)[(size_t)t * d4 + j];
+            }
+            v.x += r.x;
+            v.y += r.y;
+            v.z += r.z;
+            v.w += r.w;
+        }
         if (BF16_OUT) {
             uint2 p;
             p.x = f32_to_bf16(v.x) | (f32_to_bf16(v.y) << 16);
@@ -49,7 +67,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float4 *__restrict__
 }  // namespace
 
 hipError_t launch_combine(const moe_shape_t &s, const float *o, const int32_t *pos,
-                          const float *w, void *y, hipStream_t stream) {
+                          const float *w, void *y, hipStream_t stream, const void *res) {
     if (s.T == 0) return hipSuccess;
     const int d4 = s.d_model / 4;
     // Column chunks of whole 64-vector passes, enough for ~512 workgroups.
@@ -60,10 +78,12 @@ hipError_t launch_combine(const moe_shape_t &s, const float *o, const int32_t *p
     const dim3 grid(tok_groups, (d4 + chunk4 - 1) / chunk4), block(256);
     if (s.dtype == MOE_BF16)
         hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, stream,
-                           reinterpret_cast<const float4 *>(o), pos, w, s.T, d4, chunk4, y);
+                           reinterpret_cast<const float4 *>(o), pos, w, s.T, d4, chunk4, res,
+                           y);
     else
         hipLaunchKernelGGL(combine_kernel<false>, grid, block, 0, stream,
-                           reinterpret_cast<const float4 *>(o), pos, w, s.T, d4, chunk4, y);
+                           reinterpret_cast<const float4 *>(o), pos, w, s.T, d4, chunk4, res,
+                           y);
     return hipGetLastError();
 }
 

@@ -18,7 +18,7 @@ constexpr int kMaxExperts = 32;
 constexpr int kDecodeMaxT = 32;
 
 struct Layout {
-    size_t idx, w, counts, offsets, pos, src, xp, h, o, total;
+    size_t idx, w, counts, offsets, pos, src, xn, xp, h, o, total;
 };
 
 // Byte offsets of every workspace region for this shape (256-byte aligned).
@@ -31,6 +31,11 @@ inline size_t elem_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
 
 hipError_t launch_route(const moe_shape_t &s, const void *x, const void *w_gate,
                         int32_t *idx, float *w, hipStream_t stream);
+// Router on the RMSNorm of x (weight g, eps); writes the normalised rows to
+// xn (layer dtype).  g == NULL: plain launch_route.
+hipError_t launch_route_norm(const moe_shape_t &s, const void *x, const void *g, float eps,
+                             const void *w_gate, void *xn, int32_t *idx, float *w,
+                             hipStream_t stream);
 
 hipError_t launch_dispatch(const moe_shape_t &s, const void *x, const int32_t *idx,
                            int32_t *counts, int32_t *offsets, int32_t *pos, void *xp,
@@ -50,8 +55,10 @@ hipError_t launch_gateup(const moe_shape_t &s, const void *xp, const int32_t *co
 hipError_t launch_down(const moe_shape_t &s, const void *h, const int32_t *counts,
                        const int32_t *offsets, const void *w2, float *o, hipStream_t stream);
 
+// y = w0 o[pos0] + w1 o[pos1] (+ res when res is not NULL), rounded once.
 hipError_t launch_combine(const moe_shape_t &s, const float *o, const int32_t *pos,
-                          const float *w, void *y, hipStream_t stream);
+                          const float *w, void *y, hipStream_t stream,
+                          const void *res = nullptr);
 
 // Per-dtype expert launchers (experts_f32.hip, experts_bf16.hip).  The bf16
 // ones pick the weight-streaming kernels for T <= kDecodeMaxT.

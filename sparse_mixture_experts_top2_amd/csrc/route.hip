@@ -32,6 +32,34 @@ __device__ __forceinline__ void load8<uint16_t>(const uint16_t *p, float (&v)[8]
     }
 }
 
+// Eight fp32 values rounded to the element type and stored (16 or 32 B).
+template <typename T>
+__device__ __forceinline__ void store8(T *p, const float (&v)[8]);
+
+template <>
+__device__ __forceinline__ void store8<float>(float *p, const float (&v)[8]) {
+    *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4 *>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+template <>
+__device__ __forceinline__ void store8<uint16_t>(uint16_t *p, const float (&v)[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = f32_to_bf16(v[2 * i]) | (f32_to_bf16(v[2 * i + 1]) << 16);
+    *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// fp32 value rounded to the element type and widened back.
+template <typename T>
+__device__ __forceinline__ float round_to(float v);
+template <>
+__device__ __forceinline__ float round_to<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ float round_to<uint16_t>(float v) {
+    return bf16_to_f32(f32_to_bf16(v));
+}
+
 template <typename T>
 __device__ __forceinline__ float load1(const T *p);
 template <>
@@ -68,14 +96,52 @@ __device__ __forceinline__ void load_router_row(const T *row, int E, float (&wr)
 // d in 8-element chunks i, i+256, ...; per-thread partial logits are summed
 // across each wavefront with a butterfly and then across the four
 // wavefronts in LDS, in a fixed order.
-template <typename T, int EMAX, int TPB>
+//
+// NORM: the router input is the RMSNorm of the rows ("Mixtral 8x7B -- The
+// Evolving Transformer", section 03 MISTRAL BLOCK: rms_2 before the MoE).
+// A first pass sums each row's squares (fixed-order reduction as above),
+// rstd = 1/sqrt(sum/d + eps); the second pass re-reads the row (from L2),
+// forms xn = round(x * rstd * g) in the element type, writes it to xn_out
+// for the experts, and feeds the rounded values to the router.
+template <typename T, int EMAX, int TPB, bool NORM>
 __global__ __launch_bounds__(256) void route_kernel(const T *__restrict__ x,
                                                     const T *__restrict__ wg, int n_tok,
                                                     int d, int E, int32_t *__restrict__ idx,
-                                                    float *__restrict__ wout) {
+                                                    float *__restrict__ wout,
+                                                    const T *__restrict__ g, float eps,
+                                                    T *__restrict__ xn_out) {
     __shared__ float part[4][TPB][EMAX];
+    __shared__ float ssq[4][TPB];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int t0 = blockIdx.x * TPB;
+    const int nchunk = d >> 3;
+
+    float rstd[TPB];
+    if constexpr (NORM) {
+        float sq[TPB];
+#pragma unroll
+        for (int tt = 0; tt < TPB; ++tt) sq[tt] = 0.0f;
+        for (int c = tid; c < nchunk; c += 256) {
+#pragma unroll
+            for (int tt = 0; tt < TPB; ++tt) {
+                float v[8];
+                load8<T>(x + (size_t)min(t0 + tt, n_tok - 1) * d + c * 8, v);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) sq[tt] += v[i] * v[i];
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < TPB; ++tt) {
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) sq[tt] += __shfl_xor(sq[tt], off, 64);
+            if (lane == 0) ssq[wave][tt] = sq[tt];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int tt = 0; tt < TPB; ++tt)
+            rstd[tt] = 1.0f / sqrtf(((ssq[0][tt] + ssq[1][tt]) + (ssq[2][tt] + ssq[3][tt])) /
+                                        (float)d + eps);
+    }
 
     float acc[TPB][EMAX];
 #pragma unroll
@@ -83,13 +149,25 @@ __global__ __launch_bounds__(256) void route_kernel(const T *__restrict__ x,
 #pragma unroll
         for (int e = 0; e < EMAX; ++e) acc[tt][e] = 0.0f;
 
-    const int nchunk = d >> 3;
     for (int c = tid; c < nchunk; c += 256) {
         float xv[TPB][8];
 #pragma unroll
         for (int tt = 0; tt < TPB; ++tt) {
             const int t = min(t0 + tt, n_tok - 1);
             load8<T>(x + (size_t)t * d + c * 8, xv[tt]);
+        }
+        if constexpr (NORM) {
+            float gv[8];
+            load8<T>(g + c * 8, gv);
+#pragma unroll
+            for (int tt = 0; tt < TPB; ++tt) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) xv[tt][i] = xv[tt][i] * rstd[tt] * gv[i];
+                store8<T>(xn_out + (size_t)min(t0 + tt, n_tok - 1) * d + c * 8, xv[tt]);
+                // the router sees the rounded values the experts will see
+#pragma unroll
+                for (int i = 0; i < 8; ++i) xv[tt][i] = round_to<T>(xv[tt][i]);
+            }
         }
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
@@ -163,11 +241,17 @@ __global__ __launch_bounds__(256) void route_kernel(const T *__restrict__ x,
 
 template <typename T, int EMAX, int TPB>
 hipError_t launch_route_t(const moe_shape_t &s, const void *x, const void *wg, int32_t *idx,
-                          float *w, hipStream_t stream) {
+                          float *w, const void *g, float eps, void *xn, hipStream_t stream) {
     const int blocks = (s.T + TPB - 1) / TPB;
-    hipLaunchKernelGGL((route_kernel<T, EMAX, TPB>), dim3(blocks), dim3(256), 0, stream,
-                       static_cast<const T *>(x), static_cast<const T *>(wg), s.T, s.d_model,
-                       s.n_experts, idx, w);
+    if (g)
+        hipLaunchKernelGGL((route_kernel<T, EMAX, TPB, true>), dim3(blocks), dim3(256), 0,
+                           stream, static_cast<const T *>(x), static_cast<const T *>(wg), s.T,
+                           s.d_model, s.n_experts, idx, w, static_cast<const T *>(g), eps,
+                           static_cast<T *>(xn));
+    else
+        hipLaunchKernelGGL((route_kernel<T, EMAX, TPB, false>), dim3(blocks), dim3(256), 0,
+                           stream, static_cast<const T *>(x), static_cast<const T *>(wg), s.T,
+                           s.d_model, s.n_experts, idx, w, nullptr, 0.0f, nullptr);
     return hipGetLastError();
 }
 
@@ -176,26 +260,33 @@ hipError_t launch_route_t(const moe_shape_t &s, const void *x, const void *wg, i
 // row read for all of them.
 template <typename T>
 hipError_t launch_route_dtype(const moe_shape_t &s, const void *x, const void *wg,
-                              int32_t *idx, float *w, hipStream_t stream) {
+                              int32_t *idx, float *w, const void *g, float eps, void *xn,
+                              hipStream_t stream) {
     const bool few = s.T <= 256;
     if (s.n_experts <= 8)
-        return few ? launch_route_t<T, 8, 1>(s, x, wg, idx, w, stream)
-                   : launch_route_t<T, 8, 8>(s, x, wg, idx, w, stream);
+        return few ? launch_route_t<T, 8, 1>(s, x, wg, idx, w, g, eps, xn, stream)
+                   : launch_route_t<T, 8, 8>(s, x, wg, idx, w, g, eps, xn, stream);
     if (s.n_experts <= 16)
-        return few ? launch_route_t<T, 16, 1>(s, x, wg, idx, w, stream)
-                   : launch_route_t<T, 16, 4>(s, x, wg, idx, w, stream);
-    return few ? launch_route_t<T, 32, 1>(s, x, wg, idx, w, stream)
-               : launch_route_t<T, 32, 2>(s, x, wg, idx, w, stream);
+        return few ? launch_route_t<T, 16, 1>(s, x, wg, idx, w, g, eps, xn, stream)
+                   : launch_route_t<T, 16, 4>(s, x, wg, idx, w, g, eps, xn, stream);
+    return few ? launch_route_t<T, 32, 1>(s, x, wg, idx, w, g, eps, xn, stream)
+               : launch_route_t<T, 32, 2>(s, x, wg, idx, w, g, eps, xn, stream);
 }
 
 }  // namespace
 
 hipError_t launch_route(const moe_shape_t &s, const void *x, const void *w_gate, int32_t *idx,
                         float *w, hipStream_t stream) {
+    return launch_route_norm(s, x, nullptr, 0.0f, w_gate, nullptr, idx, w, stream);
+}
+
+hipError_t launch_route_norm(const moe_shape_t &s, const void *x, const void *g, float eps,
+                             const void *w_gate, void *xn, int32_t *idx, float *w,
+                             hipStream_t stream) {
     if (s.T == 0) return hipSuccess;
     if (s.dtype == MOE_BF16)
-        return launch_route_dtype<uint16_t>(s, x, w_gate, idx, w, stream);
-    return launch_route_dtype<float>(s, x, w_gate, idx, w, stream);
+        return launch_route_dtype<uint16_t>(s, x, w_gate, idx, w, g, eps, xn, stream);
+    return launch_route_dtype<float>(s, x, w_gate, idx, w, g, eps, xn, stream);
 }
 
 }  // namespace moe

@@ -180,3 +180,13 @@ def small_workload(T: int, d: int, f: int, E: int = 8, dtype: str = BF16,
     rs = router_std if router_std is not None else 1.0 / math.sqrt(d)
     return Workload(f"small_T{T}_d{d}_f{f}_E{E}_{dtype}", T=T, d=d, f=f, E=E,
                     dtype=dtype, router_std=rs, bias=bias, seed=seed)
+
+
+def make_norm_weight(d: int, seed: int, dtype: str, device: str = "cpu") -> torch.Tensor:
+    """Channel weights of the RMSNorm in front of the layer: 1 + 0.1 * N(0, 1)
+    from ``torch.Generator(device).manual_seed(seed)``, rounded to ``dtype``
+    (synthetic stand-ins for trained rms_2 weights, which sit near 1)."""
+    gen = torch.Generator(device=device).manual_seed(seed)
+    g = 1.0 + 0.1 * torch.randn(d, generator=gen, device=device)
+    return _cast(g, dtype)
+

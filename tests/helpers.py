@@ -19,6 +19,16 @@ def checked_inputs(wl, seed=None, device="cpu"):
     return W.make_inputs(wl, seed, gap_fn=oracle.near_tie_tokens, device=device)
 
 
+def checked_block_inputs(wl, g, eps, seed=None, device="cpu"):
+    """Seeded inputs for the block boundary (the layer runs on RMSNorm(x)):
+    the near-tie screen looks at the logits of the normalised rows, which
+    is where the routing is decided."""
+    def gap(x, w_gate):
+        xn, _ = oracle.rmsnorm(x, g, eps)
+        return oracle.near_tie_tokens(xn, w_gate)
+    return W.make_inputs(wl, seed, gap_fn=gap, device=device)
+
+
 def to_f64(t) -> np.ndarray:
     if isinstance(t, torch.Tensor):
         return t.detach().float().cpu().numpy().astype(np.float64)

@@ -87,6 +87,37 @@ def test_null_alignment_alias_workspace_checks():
     assert moe.STATUS_NAMES[st] == "MOE_ERR_WORKSPACE"
 
 
+def call_block(s, h=P16, g=P16, eps=1e-5, res=None, out=P16B, ws=P16, ws_bytes=1 << 40):
+    lib = moe.load_library()
+    return lib.moe_block_forward(ctypes.byref(s), h, g, eps, res, P16, P16, P16, P16, out, None,
+                                 None, ws, ws_bytes, None)
+
+
+def test_block_boundary_checks():
+    lib = moe.load_library()
+    s = shape()
+    name = lambda st: moe.STATUS_NAMES[st]
+    assert name(call_block(s, g=None)) == "MOE_ERR_NULL"
+    assert name(call_block(s, h=None)) == "MOE_ERR_NULL"
+    assert name(call_block(s, eps=-1.0)) == "MOE_ERR_SHAPE"
+    assert name(call_block(s, eps=float("nan"))) == "MOE_ERR_SHAPE"
+    assert name(call_block(s, eps=float("inf"))) == "MOE_ERR_SHAPE"
+    assert name(call_block(s, g=P17)) == "MOE_ERR_ALIGN"
+    assert name(call_block(s, res=P17)) == "MOE_ERR_ALIGN"
+    assert name(call_block(s, ws_bytes=16)) == "MOE_ERR_WORKSPACE"
+    # out may be exactly h or exactly the residual, never a shifted view of them
+    row = 128 * 2
+    shifted = ctypes.c_void_p(0x10000 + row)
+    assert name(call_block(s, out=shifted)) == "MOE_ERR_ALIAS"
+    assert name(call_block(s, res=P16B, out=ctypes.c_void_p(0x90000000 + row))) == \
+        "MOE_ERR_ALIAS"
+    assert call_block(shape(T=0), out=P16) == moe.MOE_OK
+    st = lib.moe_rmsnorm_route(ctypes.byref(s), P16, P16, 1e-5, P16, P16, P16B, P16B, None)
+    assert name(st) == "MOE_ERR_ALIAS"          # xn written over h
+    st = lib.moe_rmsnorm_route(ctypes.byref(s), P16, None, 1e-5, P16, P16B, P16, P16, None)
+    assert name(st) == "MOE_ERR_NULL"
+
+
 def test_zero_tokens_is_a_valid_no_op():
     # T = 0 passes every check and returns before any HIP call.
     s = shape(T=0)

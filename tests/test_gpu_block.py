@@ -1,0 +1,140 @@
+"""GPU parity of the block boundary (RMSNorm before the layer, residual add
+after it) against the CPU oracle on the same seeded inputs.
+
+Bars: routing indices bit-exact; routing weights as for the plain layer;
+the normalised rows within one unit in the last place of the layer dtype
+(the GPU forms rstd in fp32 with its own summation order, the oracle in
+fp64, so a value lying next to a rounding boundary may round the other
+way; nothing else may differ); outputs within the plain layer's
+row-max-normalised tolerance.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_mixture_experts_top2_amd as moe
+from sparse_mixture_experts_top2_amd import workloads as W
+
+from helpers import RW_TOL, Y_TOL, checked_block_inputs, row_max_rel_err, to_f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+EPS = 1e-5
+# one unit in the last place, relative: bf16 keeps 8 significant bits, fp32 24
+ULP_REL = {W.BF16: 2.0 ** -7, W.F32: 2.0 ** -22}
+
+
+def announce(msg):
+    print(f"[gpu-block] {msg}", flush=True)
+
+
+def _inputs(wl, seed_g=77):
+    g = W.make_norm_weight(wl.d, seed_g, wl.dtype)
+    return checked_block_inputs(wl, g, EPS), g
+
+
+def _check_xn(xn_gpu, xn_ref, dtype):
+    a, b = to_f64(xn_gpu), to_f64(xn_ref)
+    bound = ULP_REL[dtype] * np.maximum(np.abs(a), np.abs(b))
+    bad = np.abs(a - b) > bound
+    assert not bad.any(), f"{int(bad.sum())} normalised values differ by more than one ulp"
+    return int((a != b).sum())
+
+
+CASES = [
+    W.WORKLOADS["tiny_fp32"],
+    W.small_workload(1, 128, 256, seed=31),
+    W.small_workload(32, 256, 512, seed=32),
+    W.small_workload(77, 192, 264, seed=33),
+    W.small_workload(300, 256, 512, seed=34),
+    W.small_workload(100, 200, 328, dtype=W.F32, seed=35),
+]
+
+
+@pytest.mark.parametrize("wl", CASES, ids=lambda w: w.name)
+def test_rmsnorm_route_step(wl):
+    announce(f"rmsnorm_route {wl.name}")
+    inp, g = _inputs(wl)
+    xn, idx, w = moe.rmsnorm_route(inp.x.to(DEV), g.to(DEV), EPS, inp.w_gate.to(DEV))
+    torch.cuda.synchronize()
+    xn_o, _ = oracle.rmsnorm(inp.x, g, EPS)
+    diff = _check_xn(xn, xn_o, wl.dtype)
+    idx_o, w_o = oracle.route(xn_o, inp.w_gate)
+    np.testing.assert_array_equal(idx.cpu().numpy(), idx_o)
+    np.testing.assert_allclose(w.cpu().numpy(), w_o, rtol=0, atol=RW_TOL[wl.dtype])
+    announce(f"{wl.name}: {diff} of {xn.numel()} normalised values one ulp apart")
+
+
+@pytest.mark.parametrize("wl", CASES, ids=lambda w: w.name)
+@pytest.mark.parametrize("with_residual", [True, False], ids=["residual", "no_residual"])
+def test_block_forward(wl, with_residual):
+    announce(f"block_forward {wl.name} residual={with_residual}")
+    inp, g = _inputs(wl)
+    d = inp.to(DEV)
+    gd = g.to(DEV)
+    res = d.x if with_residual else None
+    out, idx, w = moe.block_forward(d.x, gd, EPS, d.w_gate, d.w1, d.w3, d.w2, residual=res,
+                                    return_routing=True)
+    torch.cuda.synchronize()
+    out_o, idx_o, w_o, _ = oracle.block_forward(inp.x, g, EPS, inp.w_gate, inp.w1, inp.w3,
+                                                inp.w2, residual=inp.x if with_residual else None)
+    np.testing.assert_array_equal(idx.cpu().numpy(), idx_o)
+    np.testing.assert_allclose(w.cpu().numpy(), w_o, rtol=0, atol=RW_TOL[wl.dtype])
+    err = row_max_rel_err(out, out_o)
+    announce(f"{wl.name}: row-max-rel err {err:.3e}")
+    assert err <= Y_TOL[wl.dtype], err
+
+
+def test_block_in_place_and_zero_experts():
+    """out written over h (the residual stream updated in place) equals the
+    out-of-place result bit for bit; with W2 = 0 the block returns the
+    residual exactly."""
+    wl = W.small_workload(40, 256, 512, seed=36)
+    inp, g = _inputs(wl)
+    d = inp.to(DEV)
+    gd = g.to(DEV)
+    ref = moe.block_forward(d.x, gd, EPS, d.w_gate, d.w1, d.w3, d.w2, residual=d.x)
+    h = d.x.clone()
+    moe.block_forward(h, gd, EPS, d.w_gate, d.w1, d.w3, d.w2, residual=h, out=h)
+    torch.cuda.synchronize()
+    assert torch.equal(h.view(torch.int16), ref.view(torch.int16))
+    z = moe.block_forward(d.x, gd, EPS, d.w_gate, d.w1, d.w3, torch.zeros_like(d.w2),
+                          residual=d.x)
+    torch.cuda.synchronize()
+    assert torch.equal(z.view(torch.int16), d.x.view(torch.int16))
+
+
+def test_block_zero_tokens():
+    wl = W.small_workload(0, 128, 256, seed=37)
+    x = torch.empty(0, 128, dtype=torch.bfloat16, device=DEV)
+    g = torch.ones(128, dtype=torch.bfloat16, device=DEV)
+    wg = torch.zeros(128, 8, dtype=torch.bfloat16, device=DEV)
+    w1 = torch.zeros(8, 128, 256, dtype=torch.bfloat16, device=DEV)
+    w2 = torch.zeros(8, 256, 128, dtype=torch.bfloat16, device=DEV)
+    out = moe.block_forward(x, g, EPS, wg, w1, w1, w2, residual=x)
+    assert out.shape == (0, 128)
+    _ = wl
+
+
+@pytest.mark.parametrize("name,n_sample", [("decode_8x7b", 32), ("prefill_8x7b", 24)])
+def test_block_full_size(name, n_sample):
+    """The 8x7B shapes in the launch configuration the benchmark times
+    (decode: rows gathered from the normalised input; prefill: the 256x256
+    tile kernels), checked on sampled tokens."""
+    wl = W.WORKLOADS[name]
+    announce(f"block full size {name}")
+    inp, g = _inputs(wl)
+    d = inp.to(DEV)
+    gd = g.to(DEV)
+    out, idx, _ = moe.block_forward(d.x, gd, EPS, d.w_gate, d.w1, d.w3, d.w2, residual=d.x,
+                                    return_routing=True)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(wl.seed).choice(wl.T, min(n_sample, wl.T),
+                                                         replace=False))
+    out_o, idx_o, _, _ = oracle.block_forward(inp.x[rows], g, EPS, inp.w_gate, inp.w1, inp.w3,
+                                              inp.w2, residual=inp.x[rows])
+    np.testing.assert_array_equal(idx.cpu().numpy()[rows], idx_o)
+    err = row_max_rel_err(out[torch.as_tensor(rows, device=DEV)], out_o)
+    announce(f"{name}: rows={len(rows)} row-max-rel err {err:.3e}")
+    assert err <= Y_TOL[wl.dtype], err
