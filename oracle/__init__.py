@@ -56,11 +56,11 @@ def _bind(path: str):
     lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     I = ctypes.c_int
-    lib.oracle_route.argtypes = [I, I, I, P, P, I, P, P, P, I]
+    lib.oracle_route.argtypes = [I, I, I, I, P, P, I, P, P, P, I]
     lib.oracle_route.restype = I
     lib.oracle_expert_rows.argtypes = [I, I, I, I, P, P, P, P, P, I, P, I]
     lib.oracle_expert_rows.restype = I
-    lib.oracle_forward.argtypes = [I, I, I, I, P, P, P, P, P, I, P, P, P, P, I]
+    lib.oracle_forward.argtypes = [I, I, I, I, I, P, P, P, P, P, I, P, P, P, P, I]
     lib.oracle_forward.restype = I
     lib.oracle_expert_hidden.argtypes = [I, I, I, I, P, P, P, P, I, P, I]
     lib.oracle_expert_hidden.restype = I
@@ -135,19 +135,20 @@ def _ptr(a: np.ndarray):
 
 # ---------------------------------------------------------------------------
 
-def route(x, w_gate, threads: Optional[int] = None, return_logits: bool = False):
-    """Router for every token: returns idx int32 [T,2] (slot 0 = larger
-    logit), w float64 [T,2], and optionally logits float64 [T,E]."""
+def route(x, w_gate, threads: Optional[int] = None, return_logits: bool = False,
+          top_k: int = 2):
+    """Router for every token: returns idx int32 [T,k] (slots in decreasing
+    logit order), w float64 [T,k], and optionally logits float64 [T,E]."""
     xa, dx = _as_host(x)
     ga, dg = _as_host(w_gate)
     dt = _same_dtype(dx, dg)
     T, d = xa.shape
     d2, E = ga.shape
     assert d == d2
-    idx = np.zeros((T, 2), np.int32)
-    w = np.zeros((T, 2), np.float64)
+    idx = np.zeros((T, top_k), np.int32)
+    w = np.zeros((T, top_k), np.float64)
     logits = np.zeros((T, E), np.float64)
-    rc = _load().oracle_route(T, d, E, _ptr(xa), _ptr(ga), dt, _ptr(idx), _ptr(w),
+    rc = _load().oracle_route(T, d, E, top_k, _ptr(xa), _ptr(ga), dt, _ptr(idx), _ptr(w),
                               _ptr(logits), threads or default_threads())
     if rc != 0:
         raise ValueError("oracle_route rejected its sizes")
@@ -155,30 +156,30 @@ def route(x, w_gate, threads: Optional[int] = None, return_logits: bool = False)
 
 
 def dispatch(idx: np.ndarray, n_experts: int):
-    """Group the 2T (token, slot) assignments by expert, keeping token order
+    """Group the kT (token, slot) assignments by expert, keeping token order
     and then slot order inside each expert.
 
     Returns counts int32 [E], offsets int32 [E+1] (exclusive prefix sum of
-    counts), pos int32 [T,2] (row of assignment (t, s) in the grouped order)
-    and src int32 [2T] (the flat assignment t*2+s held by each grouped row).
+    counts), pos int32 [T,k] (row of assignment (t, s) in the grouped order)
+    and src int32 [kT] (the flat assignment t*k+s held by each grouped row).
     """
     idx = np.asarray(idx)
-    T = idx.shape[0]
+    T, k = idx.shape
     counts = np.zeros(n_experts, np.int32)
     for t in range(T):
-        for s in range(2):
+        for s in range(k):
             counts[int(idx[t, s])] += 1
     offsets = np.zeros(n_experts + 1, np.int32)
     for e in range(n_experts):
         offsets[e + 1] = offsets[e] + counts[e]
     fill = offsets[:-1].copy()
-    pos = np.zeros((T, 2), np.int32)
-    src = np.zeros(2 * T, np.int32)
+    pos = np.zeros((T, k), np.int32)
+    src = np.zeros(k * T, np.int32)
     for t in range(T):
-        for s in range(2):
+        for s in range(k):
             e = int(idx[t, s])
             pos[t, s] = fill[e]
-            src[fill[e]] = 2 * t + s
+            src[fill[e]] = k * t + s
             fill[e] += 1
     return counts, offsets, pos, src
 
@@ -242,16 +243,20 @@ def expert_down(hid, expert: np.ndarray, w2, threads: Optional[int] = None):
 
 
 def combine(o_slot: np.ndarray, w: np.ndarray) -> np.ndarray:
-    """y[t] = w[t,0] * o_slot[t,0] + w[t,1] * o_slot[t,1], fp64; o_slot is
-    [T, 2, d] (the two expert outputs of each token, slot order)."""
+    """y[t] = w[t,0] * o_slot[t,0] + w[t,1] * o_slot[t,1] + ..., fp64, in
+    slot order; o_slot is [T, k, d] (each token's expert outputs)."""
     o = np.asarray(o_slot, np.float64)
     w = np.asarray(w, np.float64)
-    return w[:, 0:1] * o[:, 0, :] + w[:, 1:2] * o[:, 1, :]
+    y = np.zeros((o.shape[0], o.shape[2]), np.float64)
+    for s in range(o.shape[1]):
+        y = y + w[:, s:s + 1] * o[:, s, :]
+    return y
 
 
-def forward(x, w_gate, w1, w3, w2, threads: Optional[int] = None, return_logits=False):
-    """The whole layer: returns y float64 [T,d], idx int32 [T,2], w float64
-    [T,2] (and logits float64 [T,E] when asked)."""
+def forward(x, w_gate, w1, w3, w2, threads: Optional[int] = None, return_logits=False,
+            top_k: int = 2):
+    """The whole layer: returns y float64 [T,d], idx int32 [T,k], w float64
+    [T,k] (and logits float64 [T,E] when asked)."""
     xa, dx = _as_host(x)
     ga, dg = _as_host(w_gate)
     a1, d1 = _as_host(w1)
@@ -262,10 +267,10 @@ def forward(x, w_gate, w1, w3, w2, threads: Optional[int] = None, return_logits=
     E, d_, f = a1.shape
     assert d_ == d and ga.shape == (d, E) and a3.shape == a1.shape and a2.shape == (E, f, d)
     y = np.zeros((T, d), np.float64)
-    idx = np.zeros((T, 2), np.int32)
-    w = np.zeros((T, 2), np.float64)
+    idx = np.zeros((T, top_k), np.int32)
+    w = np.zeros((T, top_k), np.float64)
     logits = np.zeros((T, E), np.float64)
-    rc = _load().oracle_forward(T, d, f, E, _ptr(xa), _ptr(ga), _ptr(a1), _ptr(a3),
+    rc = _load().oracle_forward(T, d, f, E, top_k, _ptr(xa), _ptr(ga), _ptr(a1), _ptr(a3),
                                 _ptr(a2), dt, _ptr(y), _ptr(idx), _ptr(w), _ptr(logits),
                                 threads or default_threads())
     if rc != 0:
@@ -300,11 +305,11 @@ def rmsnorm(h, g, eps: float, threads: Optional[int] = None):
 
 
 def block_forward(h, g, eps: float, w_gate, w1, w3, w2, residual=None,
-                  threads: Optional[int] = None):
+                  threads: Optional[int] = None, top_k: int = 2):
     """out = residual + layer(rmsnorm(h)) in fp64 (residual None: no add).
     Returns (out float64 [T,d], idx, w, xn)."""
     xn, _ = rmsnorm(h, g, eps, threads=threads)
-    y, idx, w = forward(xn, w_gate, w1, w3, w2, threads=threads)
+    y, idx, w = forward(xn, w_gate, w1, w3, w2, threads=threads, top_k=top_k)
     if residual is not None:
         ra, code = _as_host(residual)
         y = y + _to_f64(ra, code)
@@ -326,12 +331,15 @@ def _to_f64(a: np.ndarray, code: int) -> np.ndarray:
 NEAR_TIE_GAP = 1e-3
 
 
-def near_tie_tokens(x, w_gate, gap: float = NEAR_TIE_GAP, threads: Optional[int] = None):
-    """Bool [T]: tokens whose fp64 logits have a 1st/2nd or 2nd/3rd gap < gap."""
+def near_tie_tokens(x, w_gate, gap: float = NEAR_TIE_GAP, threads: Optional[int] = None,
+                    top_k: int = 2):
+    """Bool [T]: tokens whose fp64 logits have a gap < gap between the
+    s-th and (s+1)-th largest for some s <= top_k (1st/2nd and 2nd/3rd for
+    top-2): the picks and their order must be clear."""
     import torch
-    _, _, logits = route(x, w_gate, threads=threads, return_logits=True)
+    _, _, logits = route(x, w_gate, threads=threads, return_logits=True, top_k=1)
     srt = -np.sort(-logits, axis=1)
-    bad = (srt[:, 0] - srt[:, 1] < gap)
-    if logits.shape[1] >= 3:
-        bad |= (srt[:, 1] - srt[:, 2] < gap)
+    bad = np.zeros(logits.shape[0], bool)
+    for s in range(min(top_k, logits.shape[1] - 1)):
+        bad |= (srt[:, s] - srt[:, s + 1] < gap)
     return torch.from_numpy(bad)

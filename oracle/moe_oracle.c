@@ -12,17 +12,18 @@
  * section 04 SWIGLU for the expert body):
  *
  *   1. router logits   l[e] = sum_j x[t,j] * Wg[j,e]          (bias-free Linear)
- *   2. top-2           i0 = argmax_e l[e], i1 = argmax_{e != i0} l[e],
- *                      exact ties resolved toward the lower expert index
- *   3. weights         softmax over the two selected logits:
+ *   2. top-k           i0 = argmax_e l[e], i1 = argmax_{e != i0} l[e], ...
+ *                      (k = 2 for Mixtral; 1 <= k <= 4 here), exact ties
+ *                      resolved toward the lower expert index
+ *   3. weights         softmax over the k selected logits; for k = 2:
  *                      q = exp(l[i1] - l[i0]);  w0 = 1/(1+q),  w1 = q/(1+q)
- *                      (equal to softmax over all experts, keep the top two,
+ *                      (equal to softmax over all experts, keep the top k,
  *                      divide by their sum -- the page's order of steps)
- *   4. experts         for s in {0,1}, e = i_s:
+ *   4. experts         for each slot s, e = i_s:
  *                      g = x W1[e], u = x W3[e]           (gate, up)
  *                      a = silu(g) * u,  silu(v) = v / (1 + exp(-v))
  *                      o_s = a W2[e]                      (down)
- *   5. combine         y[t] = w0 * o_0 + w1 * o_1
+ *   5. combine         y[t] = w0 * o_0 + w1 * o_1 + ...   (slot order)
  *
  * Matrix names follow the layer's C interface: W1 = gate, W3 = up,
  * W2 = down.  (The page's SwiGLU listing calls the same three matrices
@@ -81,22 +82,32 @@ static void router_logits(int d, int E, const void *x, size_t x_off,
     }
 }
 
-/* Steps 2-3 on one token's logits.  Strict '>' keeps the first (lowest)
- * index among equal values. */
-static void top2_softmax(int E, const double *l, int32_t *idx, double *w) {
-    int i0 = 0;
-    for (int e = 1; e < E; ++e)
-        if ((float)l[e] > (float)l[i0]) i0 = e;
-    int i1 = -1;
-    for (int e = 0; e < E; ++e) {
-        if (e == i0) continue;
-        if (i1 < 0 || (float)l[e] > (float)l[i1]) i1 = e;
+/* Steps 2-3 on one token's logits, for top-k (1 <= k <= 4; the page's
+ * MoERouter takes k as a parameter, Mixtral uses 2).  The k experts are
+ * picked greedily: each pick is the largest fp32-rounded logit among the
+ * experts not yet picked, and strict '>' keeps the first (lowest) index
+ * among equal values.  The weights are the softmax over the picked logits,
+ * taken relative to the first: e_0 = 1, e_s = exp(l[i_s] - l[i_0]),
+ * w_s = e_s / (e_0 + ... + e_{k-1}).  For k = 2 this is w_0 = 1/(1+q),
+ * w_1 = q/(1+q) with q = exp(l[i_1] - l[i_0]). */
+enum { ORC_MAX_K = 4 };
+static void topk_softmax(int E, int k, const double *l, int32_t *idx, double *w) {
+    for (int s = 0; s < k; ++s) {
+        int best = -1;
+        for (int e = 0; e < E; ++e) {
+            int taken = 0;
+            for (int r = 0; r < s; ++r) taken |= idx[r] == e;
+            if (taken) continue;
+            if (best < 0 || (float)l[e] > (float)l[best]) best = e;
+        }
+        idx[s] = best;
     }
-    double q = exp(l[i1] - l[i0]);
-    idx[0] = i0;
-    idx[1] = i1;
-    w[0] = 1.0 / (1.0 + q);
-    w[1] = q / (1.0 + q);
+    double ex[ORC_MAX_K], sum = 0.0;
+    for (int s = 0; s < k; ++s) {
+        ex[s] = s == 0 ? 1.0 : exp(l[idx[s]] - l[idx[0]]);
+        sum += ex[s];
+    }
+    for (int s = 0; s < k; ++s) w[s] = ex[s] / sum;
 }
 
 /* Step 4a for one input row xr[d] and expert e: the SwiGLU hidden
@@ -175,7 +186,7 @@ static void parallel_for(int n, int threads, range_fn fn, void *ctx) {
 /* Entry points (called through ctypes by the Python side).            */
 
 typedef struct {
-    int T, d, f, E, dtype;
+    int T, d, f, E, k, dtype;
     const void *x, *wg, *w1, *w3, *w2;
     int32_t *idx;
     double *w, *logits, *y;
@@ -188,16 +199,16 @@ static void route_range(void *p, int lo, int hi) {
         router_logits(c->d, c->E, c->x, (size_t)t * c->d, c->wg, c->dtype, l);
         if (c->logits)
             for (int e = 0; e < c->E; ++e) c->logits[(size_t)t * c->E + e] = l[e];
-        top2_softmax(c->E, l, c->idx + 2 * (size_t)t, c->w + 2 * (size_t)t);
+        topk_softmax(c->E, c->k, l, c->idx + (size_t)c->k * t, c->w + (size_t)c->k * t);
     }
 }
 
 /* Router for T tokens: idx [T,2] int32 (slot 0 = larger logit), w [T,2]
  * fp64, logits [T,E] fp64 (may be NULL).  Returns 0, or -1 on bad sizes. */
-int oracle_route(int T, int d, int E, const void *x, const void *wg, int dtype,
+int oracle_route(int T, int d, int E, int k, const void *x, const void *wg, int dtype,
                  int32_t *idx, double *w, double *logits, int threads) {
-    if (T < 0 || d < 1 || E < 2 || E > 256) return -1;
-    layer_ctx c = {T, d, 0, E, dtype, x, wg, NULL, NULL, NULL, idx, w, logits, NULL};
+    if (T < 0 || d < 1 || E < 1 || E > 256 || k < 1 || k > ORC_MAX_K || k > E) return -1;
+    layer_ctx c = {T, d, 0, E, k, dtype, x, wg, NULL, NULL, NULL, idx, w, logits, NULL};
     parallel_for(T, threads, route_range, &c);
     return 0;
 }
@@ -296,36 +307,37 @@ static void forward_range(void *p, int lo, int hi) {
     layer_ctx *c = (layer_ctx *)p;
     double l[256];
     double *xr = malloc(sizeof(double) * c->d);
-    double *o0 = malloc(sizeof(double) * c->d);
-    double *o1 = malloc(sizeof(double) * c->d);
+    double *os = malloc(sizeof(double) * c->d * ORC_MAX_K);
     double *g = malloc(sizeof(double) * c->f);
     double *u = malloc(sizeof(double) * c->f);
-    if (!xr || !o0 || !o1 || !g || !u) goto out;
+    if (!xr || !os || !g || !u) goto out;
     for (int t = lo; t < hi; ++t) {
         size_t xo = (size_t)t * c->d;
-        int32_t *it = c->idx + 2 * (size_t)t;
-        double *wt = c->w + 2 * (size_t)t;
+        int32_t *it = c->idx + (size_t)c->k * t;
+        double *wt = c->w + (size_t)c->k * t;
         router_logits(c->d, c->E, c->x, xo, c->wg, c->dtype, l);
         if (c->logits)
             for (int e = 0; e < c->E; ++e) c->logits[(size_t)t * c->E + e] = l[e];
-        top2_softmax(c->E, l, it, wt);
+        topk_softmax(c->E, c->k, l, it, wt);
         for (int j = 0; j < c->d; ++j) xr[j] = load_elem(c->x, c->dtype, xo + j);
-        swiglu_expert(c->d, c->f, xr, it[0], c->w1, c->w3, c->w2, c->dtype, g, u, o0);
-        swiglu_expert(c->d, c->f, xr, it[1], c->w1, c->w3, c->w2, c->dtype, g, u, o1);
-        for (int m = 0; m < c->d; ++m)                       /* step 5 */
-            c->y[xo + m] = wt[0] * o0[m] + wt[1] * o1[m];
+        for (int s = 0; s < c->k; ++s)
+            swiglu_expert(c->d, c->f, xr, it[s], c->w1, c->w3, c->w2, c->dtype, g, u,
+                          os + (size_t)s * c->d);
+        for (int m = 0; m < c->d; ++m) {                     /* step 5, slot order */
+            double acc = 0.0;
+            for (int s = 0; s < c->k; ++s) acc += wt[s] * os[(size_t)s * c->d + m];
+            c->y[xo + m] = acc;
+        }
     }
 out:
-    free(xr); free(o0); free(o1); free(g); free(u);
+    free(xr); free(os); free(g); free(u);
 }
-
-/* The whole layer for T tokens: y [T,d] fp64, idx [T,2], w [T,2] fp64,
- * logits [T,E] fp64 (may be NULL).  Returns 0, or -1 on bad sizes. */
-int oracle_forward(int T, int d, int f, int E, const void *x, const void *wg,
+int oracle_forward(int T, int d, int f, int E, int k, const void *x, const void *wg,
                    const void *w1, const void *w3, const void *w2, int dtype,
                    double *y, int32_t *idx, double *w, double *logits, int threads) {
-    if (T < 0 || d < 1 || f < 1 || E < 2 || E > 256) return -1;
-    layer_ctx c = {T, d, f, E, dtype, x, wg, w1, w3, w2, idx, w, logits, y};
+    if (T < 0 || d < 1 || f < 1 || E < 1 || E > 256 || k < 1 || k > ORC_MAX_K || k > E)
+        return -1;
+    layer_ctx c = {T, d, f, E, k, dtype, x, wg, w1, w3, w2, idx, w, logits, y};
     parallel_for(T, threads, forward_range, &c);
     return 0;
 }

@@ -320,12 +320,76 @@ def pin_block_identities():
     np.testing.assert_allclose(out - inp.x.double().numpy(), y, rtol=0, atol=1e-13)
 
 
+def pin_topk_brute_force_and_special_weights():
+    """Top-k for k = 1, 3, 4 ("Mixtral 8x7B -- The Evolving Transformer",
+    section 05: the MoERouter's top_k is a parameter).  The picks are the k
+    largest fp32-rounded logits in decreasing order, equal values toward the
+    lower index: a plain sort of (-logit, index) gives them.  Weights: equal
+    picked logits give exactly 1/k each; k = E is the page's softmax over
+    all experts (no renormalisation left to do); the weights sum to 1."""
+    rng = np.random.default_rng(21)
+    for E in (4, 5, 8, 16):
+        for k in (1, 3, 4):
+            if k > E:
+                continue
+            x = torch.tensor(rng.standard_normal((40, 6)), dtype=torch.float32)
+            wg = torch.tensor(rng.standard_normal((6, E)), dtype=torch.float32)
+            wg[:, 1] = wg[:, 0]                      # exact ties between experts 0 and 1
+            if E > 4:
+                wg[:, E - 1] = wg[:, 2]
+            idx, w, logits = oracle.route(x, wg, return_logits=True, top_k=k)
+            for t in range(40):
+                key = sorted(range(E), key=lambda e: (-float(np.float32(logits[t, e])), e))
+                assert list(idx[t]) == key[:k], (E, k, t)
+            np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+            if k == 1:
+                np.testing.assert_array_equal(w, 1.0)
+    # all picked logits equal -> weights exactly 1/k
+    x = torch.ones(3, 4)
+    wg = torch.zeros(4, 8)
+    for k in (1, 2, 3, 4):
+        idx, w = oracle.route(x, wg, top_k=k)
+        np.testing.assert_array_equal(idx, np.tile(np.arange(k), (3, 1)))
+        np.testing.assert_array_equal(w, np.full((3, k), 1.0 / k))
+    # k = E: the softmax over all experts, in decreasing-logit order
+    x = torch.tensor(rng.standard_normal((10, 5)), dtype=torch.float32)
+    wg = torch.tensor(rng.standard_normal((5, 4)), dtype=torch.float32)
+    idx, w, logits = oracle.route(x, wg, return_logits=True, top_k=4)
+    full = np.exp(logits - logits.max(axis=1, keepdims=True))
+    full /= full.sum(axis=1, keepdims=True)
+    np.testing.assert_allclose(w, np.take_along_axis(full, idx, axis=1), rtol=1e-14)
+
+
+def pin_topk_layer_special_cases():
+    """k = 1: y is exactly the picked expert's output.  Identical experts:
+    y is the dense SwiGLU for every k (the weights sum to one).  Dispatch
+    groups kT assignments stably for k = 3, 4."""
+    inp = _rand_layer(T=10, d=16, f=24, seed=92, dtype=W.F32)
+    y, idx, w = oracle.forward(inp.x, inp.w_gate, inp.w1, inp.w3, inp.w2, top_k=1)
+    rows = oracle.expert_rows(inp.x, idx[:, 0], inp.w1, inp.w3, inp.w2)
+    np.testing.assert_array_equal(y, rows)
+    same = lambda m: m[:1].expand_as(m).contiguous()
+    dense = oracle.expert_rows(inp.x, np.zeros(10, np.int32), inp.w1, inp.w3, inp.w2)
+    for k in (1, 3, 4):
+        y, _, _ = oracle.forward(inp.x, inp.w_gate, same(inp.w1), same(inp.w3), same(inp.w2),
+                                 top_k=k)
+        np.testing.assert_allclose(y, dense, rtol=0, atol=1e-12 * np.abs(dense).max())
+    rng = np.random.default_rng(9)
+    for k in (3, 4):
+        idx = np.stack([rng.permutation(8)[:k] for _ in range(50)]).astype(np.int32)
+        counts, offsets, pos, src = oracle.dispatch(idx, 8)
+        order = np.argsort(idx.reshape(-1), kind="stable")
+        np.testing.assert_array_equal(src, order)
+        np.testing.assert_array_equal(pos.reshape(-1)[order], np.arange(k * 50))
+
+
 PINS = [pin_worked_examples, pin_logits_match_numpy, pin_top2_brute_force,
         pin_weights_closed_form_and_page_form, pin_forward_matches_numpy_dense,
         pin_expert_rows_match_numpy, pin_identical_experts_equal_dense_swiglu,
         pin_forced_one_hot_router, pin_power_of_two_scaling,
         pin_expert_relabelling_and_token_permutation, pin_dispatch_is_stable_grouping,
-        pin_rmsnorm_closed_forms, pin_rmsnorm_invariants, pin_block_identities]
+        pin_rmsnorm_closed_forms, pin_rmsnorm_invariants, pin_block_identities,
+        pin_topk_brute_force_and_special_weights, pin_topk_layer_special_cases]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -355,18 +419,22 @@ MUTANTS = {
     "gate_up_swapped": ("g[n] = g[n] / (1.0 + exp(-g[n])) * u[n];",
                         "g[n] = u[n] / (1.0 + exp(-u[n])) * g[n];"),
     "silu_sign": ("g[n] / (1.0 + exp(-g[n]))", "g[n] / (1.0 + exp(g[n]))"),
-    "tie_to_higher_index": ("if ((float)l[e] > (float)l[i0]) i0 = e;",
-                            "if ((float)l[e] >= (float)l[i0]) i0 = e;"),
-    "slot_weights_swapped": ("w[0] = 1.0 / (1.0 + q);\n    w[1] = q / (1.0 + q);",
-                             "w[1] = 1.0 / (1.0 + q);\n    w[0] = q / (1.0 + q);"),
+    "tie_to_higher_index": ("if (best < 0 || (float)l[e] > (float)l[best]) best = e;",
+                            "if (best < 0 || (float)l[e] >= (float)l[best]) best = e;"),
+    "slot_weights_swapped": ("for (int s = 0; s < k; ++s) w[s] = ex[s] / sum;",
+                             "for (int s = 0; s < k; ++s) w[s] = ex[k - 1 - s] / sum;"),
     "down_transposed": ("o[m] += an * load_elem(w2, dtype, row + m);",
                         "o[m] += an * load_elem(w2, dtype, out_base + (size_t)m * f + n);"),
     "dropped_first_term": ("for (int j = 0; j < d; ++j) {\n        double xj = xr[j];",
                            "for (int j = 1; j < d; ++j) {\n        double xj = xr[j];"),
     "router_column_index": ("l[e] += xj * load_elem(wg, dtype, (size_t)j * E + e);",
                             "l[e] += xj * load_elem(wg, dtype, (size_t)e * d + j);"),
-    "combine_second_slot_dropped": ("c->y[xo + m] = wt[0] * o0[m] + wt[1] * o1[m];",
-                                    "c->y[xo + m] = wt[0] * o0[m] + wt[1] * o0[m];"),
+    "combine_second_slot_dropped": ("for (int s = 0; s < c->k; ++s) acc += wt[s]",
+                                    "for (int s = 0; s < 1; ++s) acc += wt[s]"),
+    "softmax_not_relative_to_first": ("ex[s] = s == 0 ? 1.0 : exp(l[idx[s]] - l[idx[0]]);",
+                                      "ex[s] = s == 0 ? 1.0 : exp(l[idx[0]] - l[idx[s]]);"),
+    "second_pick_may_repeat": ("for (int r = 0; r < s; ++r) taken |= idx[r] == e;",
+                               "for (int r = 0; r < s - 1; ++r) taken |= idx[r] == e;"),
     "norm_sum_not_mean": ("sqrt(ss / (double)c->d + c->eps)", "sqrt(ss + c->eps)"),
     "norm_no_sqrt": ("sqrt(ss / (double)c->d + c->eps)", "(ss / (double)c->d + c->eps)"),
     "norm_eps_outside": ("1.0 / sqrt(ss / (double)c->d + c->eps)",
