@@ -1,20 +1,23 @@
 /*
- * moe.h -- C interface of the MI355X (gfx950) top-2 sparse mixture-of-experts
- * feed-forward layer.
+ * moe.h -- C interface of the MI355X (gfx950) top-k sparse mixture-of-experts
+ * feed-forward layer (Mixtral: 8 experts, top-2).
  *
  * The layer ("Mixtral 8x7B -- The Evolving Transformer", section 05 MOE ROUTER
  * + MOE, formula y = sum_k w_k E_{i_k}(x); section 04 SWIGLU for the expert):
- * a bias-free linear router scores E experts per token, the two largest
- * scores are kept, a softmax over those two gives their weights, the token
- * runs through both SwiGLU experts  down(silu(x W1) * (x W3))  and the two
- * expert outputs are summed with those weights.  The KerasFormers Mixtral
- * page (API table: num_experts, num_experts_per_tok) names the same two
- * parameters; every expert stays resident in device memory.
+ * a bias-free linear router scores E experts per token, the top_k largest
+ * scores are kept (Mixtral: 2 of 8), a softmax over the kept scores gives
+ * their weights, the token runs through each kept SwiGLU expert
+ * down(silu(x W1) * (x W3)) and the expert outputs are summed with those
+ * weights.  Section 05's MoERouter takes k as a parameter, and the
+ * KerasFormers Mixtral page (API table: num_experts, num_experts_per_tok)
+ * names the same two parameters; every expert stays resident in device
+ * memory.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- * Shapes   T tokens, d = d_model, f = d_ff, E = n_experts, top_k = 2.
- *          The caller flattens (batch, seq) into T rows.
+ * Shapes   T tokens, d = d_model, f = d_ff, E = n_experts, k = top_k.
+ *          The caller flattens (batch, seq) into T rows; the layer routes
+ *          R = k T (token, slot) assignments.
  * Layout   dense row-major, no transposes, y = x W:
  *            x [T, d]      w_gate [d, E]
  *            w1 [E, d, f]  (gate)     w3 [E, d, f]  (up)     w2 [E, f, d]  (down)
@@ -64,7 +67,7 @@ typedef enum {
     MOE_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                  */
     MOE_ERR_ALIAS = 5,       /* an output overlaps an input                       */
     MOE_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than moe_workspace_bytes */
-    MOE_ERR_UNSUPPORTED = 7, /* top_k != 2, or E outside [2, 32]                   */
+    MOE_ERR_UNSUPPORTED = 7, /* E outside [2, 64], or top_k outside [1, min(4, E)] */
     MOE_ERR_HIP = 8          /* a HIP launch failed                               */
 } moe_status_t;
 
@@ -72,8 +75,8 @@ typedef struct {
     int32_t T;          /* tokens (rows of x); T = 0 returns MOE_OK at once */
     int32_t d_model;    /* d: multiple of 8, >= 8                            */
     int32_t d_ff;       /* f: multiple of 8, >= 8                            */
-    int32_t n_experts;  /* E: 2 .. 32                                        */
-    int32_t top_k;      /* must be 2                                         */
+    int32_t n_experts;  /* E: 2 .. 64                                        */
+    int32_t top_k;      /* k: 1 .. min(4, E); k T <= 2^29                    */
     int32_t dtype;      /* moe_dtype_t                                       */
 } moe_shape_t;
 
@@ -84,29 +87,30 @@ const char *moe_status_str(int status);
  * shape (0 for an invalid shape).  The size depends on every field. */
 size_t moe_workspace_bytes(const moe_shape_t *shape);
 
-/* Router: section 05's MoERouter (bias-free Linear d -> E, softmax, top-2,
- * renormalise over the two kept experts), in the equivalent form
+/* Router: section 05's MoERouter (bias-free Linear d -> E, softmax, top-k,
+ * renormalise over the kept experts), in the equivalent form
  *   l[t,e] = sum_j x[t,j] w_gate[j,e]                 (fp32, never rounded)
- *   topk_idx[t,0] = argmax_e l,  topk_idx[t,1] = argmax_{e != idx0} l,
+ *   topk_idx[t,s] = argmax of l over the experts not in topk_idx[t,0..s-1],
  *                   equal logits resolved toward the lower expert index
- *   topk_w[t,0] = 1 / (1 + q),  topk_w[t,1] = q / (1 + q),
- *                   q = exp(l[idx1] - l[idx0])       (softmax of the two logits)
- * Outputs topk_idx int32 [T, 2] and topk_w fp32 [T, 2], slot 0 holding the
- * larger logit. */
+ *   topk_w[t,s] = e_s / (e_0 + ... + e_{k-1}),  e_s = exp(l[idx_s] - l[idx_0])
+ *                   (the softmax of the kept logits; for k = 2 this is
+ *                   1/(1+q), q/(1+q) with q = exp(l[idx1] - l[idx0]))
+ * Outputs topk_idx int32 [T, k] and topk_w fp32 [T, k], slots in decreasing
+ * logit order. */
 int moe_route(const moe_shape_t *shape, const void *x, const void *w_gate,
               int32_t *topk_idx, float *topk_w, void *stream);
 
 /* Dispatch: the per-expert batching of tokens that section 05 names as the
- * production form of its mask loop.  The 2T (token, slot) assignments in
- * topk_idx are grouped by expert, keeping token order and then slot order
- * within each expert (a stable counting sort):
+ * production form of its mask loop.  The R = k T (token, slot) assignments
+ * in topk_idx [T, k] are grouped by expert, keeping token order and then
+ * slot order within each expert (a stable counting sort):
  *   counts[e]    number of assignments to expert e               int32 [E]
- *   offsets[e]   sum of counts[0..e-1]; offsets[E] = 2T           int32 [E+1]
- *   pos[t,s]     row of assignment (t,s) in the grouped order     int32 [T, 2]
- *   xp[pos[t,s], :] = x[t, :]                                      [2T, d]
- * topk_idx entries must lie in [0, E); out-of-range entries are not
- * detected on the device and give undefined results.  xp must have room
- * for 2T rows. */
+ *   offsets[e]   sum of counts[0..e-1]; offsets[E] = R            int32 [E+1]
+ *   pos[t,s]     row of assignment (t,s) in the grouped order     int32 [T, k]
+ *   xp[pos[t,s], :] = x[t, :]                                      [R, d]
+ * topk_idx entries must lie in [0, E) and a token's k entries must differ
+ * (the router's output always does); other entries are not detected on the
+ * device and give undefined results.  xp must have room for R rows. */
 int moe_dispatch(const moe_shape_t *shape, const void *x, const int32_t *topk_idx,
                  int32_t *counts, int32_t *offsets, int32_t *pos, void *xp,
                  void *stream);
@@ -114,7 +118,7 @@ int moe_dispatch(const moe_shape_t *shape, const void *x, const int32_t *topk_id
 /* Expert gate/up: the first half of section 04's SwiGLU block, for every
  * expert e over its rows r in [offsets[e], offsets[e+1]) of xp:
  *   h[r, :] = silu(xp[r] w1[e]) * (xp[r] w3[e]),  silu(v) = v / (1 + exp(-v))
- * fp32 accumulation; h [2T, f] has the layer dtype (rounded to bf16 for
+ * fp32 accumulation; h [R, f] has the layer dtype (rounded to bf16 for
  * MOE_BF16).  counts / offsets are moe_dispatch's outputs, left in device
  * memory (never read back to the host).  h must not overlap xp. */
 int moe_expert_gateup(const moe_shape_t *shape, const void *xp, const int32_t *counts,
@@ -123,26 +127,28 @@ int moe_expert_gateup(const moe_shape_t *shape, const void *xp, const int32_t *c
 
 /* Expert down: the second half of section 04's SwiGLU block,
  *   o[r, :] = h[r] w2[e]   for r in [offsets[e], offsets[e+1]),
- * fp32 accumulation, o fp32 [2T, d].  o must not overlap h. */
+ * fp32 accumulation, o fp32 [R, d].  o must not overlap h. */
 int moe_expert_down(const moe_shape_t *shape, const void *h, const int32_t *counts,
                     const int32_t *offsets, const void *w2, float *o, void *stream);
 
 /* Experts: moe_expert_gateup then moe_expert_down, with h kept in the
  * workspace:  o[r] = (silu(xp[r] w1[e]) * (xp[r] w3[e])) w2[e].
- * o is fp32 [2T, d].  ws / ws_bytes: workspace of at least
+ * o is fp32 [R, d].  ws / ws_bytes: workspace of at least
  * moe_workspace_bytes(shape). */
 int moe_experts(const moe_shape_t *shape, const void *xp, const int32_t *counts,
                 const int32_t *offsets, const void *w1, const void *w3,
                 const void *w2, float *o, void *ws, size_t ws_bytes, void *stream);
 
-/* Combine: section 05's weighted sum, slot 0 then slot 1, fp32 math:
- *   y[t, :] = topk_w[t,0] * o[pos[t,0], :] + topk_w[t,1] * o[pos[t,1], :]
- * rounded to y's dtype.  Every row of y is written. */
+/* Combine: section 05's weighted sum over the k slots in slot order, fp32
+ * math:
+ *   y[t, :] = topk_w[t,0] * o[pos[t,0], :] + ... + topk_w[t,k-1] * o[pos[t,k-1], :]
+ * rounded to y's dtype.  o is [R, d], pos and topk_w [T, k].  Every row of
+ * y is written. */
 int moe_combine(const moe_shape_t *shape, const float *o, const int32_t *pos,
                 const float *topk_w, void *y, void *stream);
 
 /* The whole layer: route, dispatch, experts, combine, enqueued back to back
- * on `stream`.  topk_idx_opt / topk_w_opt (int32 [T,2], fp32 [T,2]) receive
+ * on `stream`.  topk_idx_opt / topk_w_opt (int32 [T,k], fp32 [T,k]) receive
  * the routing when non-NULL.  y must not overlap x.
  * ws / ws_bytes: workspace of at least moe_workspace_bytes(shape). */
 int moe_forward(const moe_shape_t *shape, const void *x, const void *w_gate,

@@ -142,27 +142,40 @@ def _need(t: torch.Tensor, name: str, dtype=None, device=None, shape=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
-def workspace_bytes(T: int, d: int, f: int, E: int, dtype) -> int:
-    return int(load_library().moe_workspace_bytes(ctypes.byref(make_shape(T, d, f, E, dtype))))
+def workspace_bytes(T: int, d: int, f: int, E: int, dtype, top_k: int = 2) -> int:
+    shape = make_shape(T, d, f, E, dtype, top_k)
+    return int(load_library().moe_workspace_bytes(ctypes.byref(shape)))
 
 
-def alloc_workspace(T: int, d: int, f: int, E: int, dtype, device) -> torch.Tensor:
-    n = workspace_bytes(T, d, f, E, dtype)
+def alloc_workspace(T: int, d: int, f: int, E: int, dtype, device,
+                    top_k: int = 2) -> torch.Tensor:
+    n = workspace_bytes(T, d, f, E, dtype, top_k)
     if n == 0:
         raise ValueError("invalid layer shape")
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def route(x: torch.Tensor, w_gate: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Router: returns (topk_idx int32 [T,2], topk_w fp32 [T,2])."""
+def _routing_out(T: int, k: int, device):
+    return (torch.empty(T, k, dtype=torch.int32, device=device),
+            torch.empty(T, k, dtype=torch.float32, device=device))
+
+
+def _routed_tokens(rows: int, top_k: int, what: str) -> int:
+    if top_k < 1 or rows % top_k:
+        raise ValueError(f"{what} must have top_k * T rows (top_k = {top_k}, {rows} rows)")
+    return rows // top_k
+
+
+def route(x: torch.Tensor, w_gate: torch.Tensor,
+          top_k: int = 2) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Router: returns (topk_idx int32 [T,k], topk_w fp32 [T,k])."""
     _need(x, "x")
     T, d = x.shape
     _need(w_gate, "w_gate", x.dtype, x.device)
     E = w_gate.shape[1]
     _need(w_gate, "w_gate", shape=(d, E))
-    idx = torch.empty(T, 2, dtype=torch.int32, device=x.device)
-    w = torch.empty(T, 2, dtype=torch.float32, device=x.device)
-    shape = make_shape(T, d, 8, E, x.dtype)
+    idx, w = _routing_out(T, top_k, x.device)
+    shape = make_shape(T, d, 8, E, x.dtype, top_k)
     st = load_library().moe_route(ctypes.byref(shape), _ptr(x), _ptr(w_gate), _ptr(idx), _ptr(w),
                                   _stream(x.device))
     _check(st, "moe_route")
@@ -171,44 +184,48 @@ def route(x: torch.Tensor, w_gate: torch.Tensor) -> Tuple[torch.Tensor, torch.Te
 
 def dispatch(x: torch.Tensor, topk_idx: torch.Tensor, n_experts: int):
     """Stable grouping by expert: returns (counts [E], offsets [E+1],
-    pos [T,2], xp [2T,d])."""
+    pos [T,k], xp [kT,d]); k is topk_idx's second dimension."""
     _need(x, "x")
     T, d = x.shape
-    _need(topk_idx, "topk_idx", torch.int32, x.device, (T, 2))
+    _need(topk_idx, "topk_idx", torch.int32, x.device)
+    if topk_idx.dim() != 2 or topk_idx.shape[0] != T:
+        raise ValueError(f"topk_idx must be [T, k] with T = {T}, got {tuple(topk_idx.shape)}")
+    k = topk_idx.shape[1]
     dev = x.device
     counts = torch.empty(n_experts, dtype=torch.int32, device=dev)
     offsets = torch.empty(n_experts + 1, dtype=torch.int32, device=dev)
-    pos = torch.empty(T, 2, dtype=torch.int32, device=dev)
-    xp = torch.empty(2 * T, d, dtype=x.dtype, device=dev)
-    shape = make_shape(T, d, 8, n_experts, x.dtype)
+    pos = torch.empty(T, k, dtype=torch.int32, device=dev)
+    xp = torch.empty(k * T, d, dtype=x.dtype, device=dev)
+    shape = make_shape(T, d, 8, n_experts, x.dtype, k)
     st = load_library().moe_dispatch(ctypes.byref(shape), _ptr(x), _ptr(topk_idx), _ptr(counts),
                                      _ptr(offsets), _ptr(pos), _ptr(xp), _stream(dev))
     _check(st, "moe_dispatch")
     return counts, offsets, pos, xp
 
 
-def _expert_args(xp, counts, offsets, w, w_name):
+def _expert_args(xp, counts, offsets, w, w_name, top_k):
     _need(xp, "xp")
     R, k_in = xp.shape
-    if R % 2:
-        raise ValueError("xp / h must have 2T rows")
+    T = _routed_tokens(R, top_k, "xp / h")
     _need(w, w_name, xp.dtype, xp.device)
     E = w.shape[0]
     _need(counts, "counts", torch.int32, xp.device, (E,))
     _need(offsets, "offsets", torch.int32, xp.device, (E + 1,))
-    return R // 2, k_in, E
+    return T, k_in, E
 
 
 def expert_gateup(xp: torch.Tensor, counts: torch.Tensor, offsets: torch.Tensor,
-                  w1: torch.Tensor, w3: torch.Tensor, out: Optional[torch.Tensor] = None):
-    """h = silu(xp w1[e]) * (xp w3[e]) per expert row group; [2T, f]."""
-    T, d, E = _expert_args(xp, counts, offsets, w1, "w1")
+                  w1: torch.Tensor, w3: torch.Tensor, out: Optional[torch.Tensor] = None,
+                  top_k: int = 2):
+    """h = silu(xp w1[e]) * (xp w3[e]) per expert row group; [kT, f]."""
+    T, d, E = _expert_args(xp, counts, offsets, w1, "w1", top_k)
+    R = xp.shape[0]
     f = w1.shape[2]
     _need(w1, "w1", shape=(E, d, f))
     _need(w3, "w3", xp.dtype, xp.device, (E, d, f))
-    h = out if out is not None else torch.empty(2 * T, f, dtype=xp.dtype, device=xp.device)
-    _need(h, "h", xp.dtype, xp.device, (2 * T, f))
-    shape = make_shape(T, d, f, E, xp.dtype)
+    h = out if out is not None else torch.empty(R, f, dtype=xp.dtype, device=xp.device)
+    _need(h, "h", xp.dtype, xp.device, (R, f))
+    shape = make_shape(T, d, f, E, xp.dtype, top_k)
     st = load_library().moe_expert_gateup(ctypes.byref(shape), _ptr(xp), _ptr(counts),
                                           _ptr(offsets), _ptr(w1), _ptr(w3), _ptr(h),
                                           _stream(xp.device))
@@ -217,14 +234,15 @@ def expert_gateup(xp: torch.Tensor, counts: torch.Tensor, offsets: torch.Tensor,
 
 
 def expert_down(h: torch.Tensor, counts: torch.Tensor, offsets: torch.Tensor, w2: torch.Tensor,
-                out: Optional[torch.Tensor] = None):
-    """o = h w2[e] per expert row group; fp32 [2T, d]."""
-    T, f, E = _expert_args(h, counts, offsets, w2, "w2")
+                out: Optional[torch.Tensor] = None, top_k: int = 2):
+    """o = h w2[e] per expert row group; fp32 [kT, d]."""
+    T, f, E = _expert_args(h, counts, offsets, w2, "w2", top_k)
+    R = h.shape[0]
     d = w2.shape[2]
     _need(w2, "w2", shape=(E, f, d))
-    o = out if out is not None else torch.empty(2 * T, d, dtype=torch.float32, device=h.device)
-    _need(o, "o", torch.float32, h.device, (2 * T, d))
-    shape = make_shape(T, d, f, E, h.dtype)
+    o = out if out is not None else torch.empty(R, d, dtype=torch.float32, device=h.device)
+    _need(o, "o", torch.float32, h.device, (R, d))
+    shape = make_shape(T, d, f, E, h.dtype, top_k)
     st = load_library().moe_expert_down(ctypes.byref(shape), _ptr(h), _ptr(counts), _ptr(offsets),
                                         _ptr(w2), _ptr(o), _stream(h.device))
     _check(st, "moe_expert_down")
@@ -232,13 +250,12 @@ def expert_down(h: torch.Tensor, counts: torch.Tensor, offsets: torch.Tensor, w2
 
 
 def experts(xp: torch.Tensor, counts: torch.Tensor, offsets: torch.Tensor, w1: torch.Tensor,
-            w3: torch.Tensor, w2: torch.Tensor, workspace: Optional[torch.Tensor] = None):
-    """Grouped SwiGLU over expert-sorted rows: returns o fp32 [2T, d]."""
+            w3: torch.Tensor, w2: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+            top_k: int = 2):
+    """Grouped SwiGLU over expert-sorted rows: returns o fp32 [kT, d]."""
     _need(xp, "xp")
     R, d = xp.shape
-    if R % 2:
-        raise ValueError("xp must have 2T rows")
-    T = R // 2
+    T = _routed_tokens(R, top_k, "xp")
     _need(w1, "w1", xp.dtype, xp.device)
     E, _, f = w1.shape
     _need(w1, "w1", shape=(E, d, f))
@@ -246,9 +263,10 @@ def experts(xp: torch.Tensor, counts: torch.Tensor, offsets: torch.Tensor, w1: t
     _need(w2, "w2", xp.dtype, xp.device, (E, f, d))
     _need(counts, "counts", torch.int32, xp.device, (E,))
     _need(offsets, "offsets", torch.int32, xp.device, (E + 1,))
-    ws = workspace if workspace is not None else alloc_workspace(T, d, f, E, xp.dtype, xp.device)
+    ws = workspace if workspace is not None else alloc_workspace(T, d, f, E, xp.dtype, xp.device,
+                                                                 top_k)
     o = torch.empty(R, d, dtype=torch.float32, device=xp.device)
-    shape = make_shape(T, d, f, E, xp.dtype)
+    shape = make_shape(T, d, f, E, xp.dtype, top_k)
     st = load_library().moe_experts(ctypes.byref(shape), _ptr(xp), _ptr(counts), _ptr(offsets),
                                     _ptr(w1), _ptr(w3), _ptr(w2), _ptr(o), _ptr(ws),
                                     ws.numel(), _stream(xp.device))
@@ -257,14 +275,19 @@ def experts(xp: torch.Tensor, counts: torch.Tensor, offsets: torch.Tensor, w1: t
 
 
 def combine(o: torch.Tensor, pos: torch.Tensor, topk_w: torch.Tensor, dtype) -> torch.Tensor:
-    """y[t] = w[t,0] o[pos[t,0]] + w[t,1] o[pos[t,1]], as ``dtype``."""
+    """y[t] = sum_s w[t,s] o[pos[t,s]] over the k slots, as ``dtype``; k is
+    pos's second dimension."""
     _need(o, "o", torch.float32)
     R, d = o.shape
-    T = R // 2
-    _need(pos, "pos", torch.int32, o.device, (T, 2))
-    _need(topk_w, "topk_w", torch.float32, o.device, (T, 2))
+    _need(pos, "pos", torch.int32, o.device)
+    if pos.dim() != 2:
+        raise ValueError(f"pos must be [T, k], got {tuple(pos.shape)}")
+    T, k = pos.shape
+    if R != k * T:
+        raise ValueError(f"o must have k * T = {k * T} rows, got {R}")
+    _need(topk_w, "topk_w", torch.float32, o.device, (T, k))
     y = torch.empty(T, d, dtype=dtype, device=o.device)
-    shape = make_shape(T, d, 8, 2, dtype)
+    shape = make_shape(T, d, 8, max(2, k), dtype, k)
     st = load_library().moe_combine(ctypes.byref(shape), _ptr(o), _ptr(pos), _ptr(topk_w), _ptr(y),
                                     _stream(o.device))
     _check(st, "moe_combine")
@@ -273,9 +296,10 @@ def combine(o: torch.Tensor, pos: torch.Tensor, topk_w: torch.Tensor, dtype) -> 
 
 def forward(x: torch.Tensor, w_gate: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor,
             w2: torch.Tensor, workspace: Optional[torch.Tensor] = None,
-            return_routing: bool = False, out: Optional[torch.Tensor] = None):
-    """The whole layer.  Returns y [T, d] (and (topk_idx, topk_w) when
-    ``return_routing``)."""
+            return_routing: bool = False, out: Optional[torch.Tensor] = None,
+            top_k: int = 2):
+    """The whole layer.  Returns y [T, d] (and (topk_idx, topk_w), each
+    [T, top_k], when ``return_routing``)."""
     _need(x, "x")
     T, d = x.shape
     _need(w_gate, "w_gate", x.dtype, x.device)
@@ -286,14 +310,14 @@ def forward(x: torch.Tensor, w_gate: torch.Tensor, w1: torch.Tensor, w3: torch.T
     _need(w1, "w1", shape=(E, d, f))
     _need(w3, "w3", x.dtype, x.device, (E, d, f))
     _need(w2, "w2", x.dtype, x.device, (E, f, d))
-    ws = workspace if workspace is not None else alloc_workspace(T, d, f, E, x.dtype, x.device)
+    ws = workspace if workspace is not None else alloc_workspace(T, d, f, E, x.dtype, x.device,
+                                                                 top_k)
     y = out if out is not None else torch.empty(T, d, dtype=x.dtype, device=x.device)
     _need(y, "out", x.dtype, x.device, (T, d))
     idx = w = None
     if return_routing:
-        idx = torch.empty(T, 2, dtype=torch.int32, device=x.device)
-        w = torch.empty(T, 2, dtype=torch.float32, device=x.device)
-    shape = make_shape(T, d, f, E, x.dtype)
+        idx, w = _routing_out(T, top_k, x.device)
+    shape = make_shape(T, d, f, E, x.dtype, top_k)
     st = load_library().moe_forward(ctypes.byref(shape), _ptr(x), _ptr(w_gate), _ptr(w1), _ptr(w3),
                                     _ptr(w2), _ptr(y), _ptr(idx), _ptr(w), _ptr(ws), ws.numel(),
                                     _stream(x.device))
@@ -302,9 +326,9 @@ def forward(x: torch.Tensor, w_gate: torch.Tensor, w1: torch.Tensor, w3: torch.T
 
 
 def rmsnorm_route(h: torch.Tensor, rms_weight: torch.Tensor, eps: float, w_gate: torch.Tensor,
-                  xn: Optional[torch.Tensor] = None):
-    """Router on RMSNorm(h).  Returns (xn [T, d], topk_idx int32 [T, 2],
-    topk_w fp32 [T, 2])."""
+                  xn: Optional[torch.Tensor] = None, top_k: int = 2):
+    """Router on RMSNorm(h).  Returns (xn [T, d], topk_idx int32 [T, k],
+    topk_w fp32 [T, k])."""
     _need(h, "h")
     T, d = h.shape
     _need(rms_weight, "rms_weight", h.dtype, h.device, (d,))
@@ -313,9 +337,8 @@ def rmsnorm_route(h: torch.Tensor, rms_weight: torch.Tensor, eps: float, w_gate:
     _need(w_gate, "w_gate", shape=(d, E))
     xn = xn if xn is not None else torch.empty_like(h)
     _need(xn, "xn", h.dtype, h.device, (T, d))
-    idx = torch.empty(T, 2, dtype=torch.int32, device=h.device)
-    w = torch.empty(T, 2, dtype=torch.float32, device=h.device)
-    shape = make_shape(T, d, 8, E, h.dtype)
+    idx, w = _routing_out(T, top_k, h.device)
+    shape = make_shape(T, d, 8, E, h.dtype, top_k)
     st = load_library().moe_rmsnorm_route(ctypes.byref(shape), _ptr(h), _ptr(rms_weight),
                                           float(eps), _ptr(w_gate), _ptr(xn), _ptr(idx), _ptr(w),
                                           _stream(h.device))
@@ -327,7 +350,7 @@ def block_forward(h: torch.Tensor, rms_weight: torch.Tensor, eps: float, w_gate:
                   w1: torch.Tensor, w3: torch.Tensor, w2: torch.Tensor,
                   residual: Optional[torch.Tensor] = None,
                   workspace: Optional[torch.Tensor] = None, return_routing: bool = False,
-                  out: Optional[torch.Tensor] = None):
+                  out: Optional[torch.Tensor] = None, top_k: int = 2):
     """out = residual + layer(RMSNorm(h)) (no add when residual is None).
     Returns out [T, d] (and (topk_idx, topk_w) when ``return_routing``)."""
     _need(h, "h")
@@ -343,14 +366,14 @@ def block_forward(h: torch.Tensor, rms_weight: torch.Tensor, eps: float, w_gate:
     _need(w2, "w2", h.dtype, h.device, (E, f, d))
     if residual is not None:
         _need(residual, "residual", h.dtype, h.device, (T, d))
-    ws = workspace if workspace is not None else alloc_workspace(T, d, f, E, h.dtype, h.device)
+    ws = workspace if workspace is not None else alloc_workspace(T, d, f, E, h.dtype, h.device,
+                                                                 top_k)
     y = out if out is not None else torch.empty(T, d, dtype=h.dtype, device=h.device)
     _need(y, "out", h.dtype, h.device, (T, d))
     idx = w = None
     if return_routing:
-        idx = torch.empty(T, 2, dtype=torch.int32, device=h.device)
-        w = torch.empty(T, 2, dtype=torch.float32, device=h.device)
-    shape = make_shape(T, d, f, E, h.dtype)
+        idx, w = _routing_out(T, top_k, h.device)
+    shape = make_shape(T, d, f, E, h.dtype, top_k)
     st = load_library().moe_block_forward(ctypes.byref(shape), _ptr(h), _ptr(rms_weight),
                                           float(eps), _ptr(residual), _ptr(w_gate), _ptr(w1),
                                           _ptr(w3), _ptr(w2), _ptr(y), _ptr(idx), _ptr(w), _ptr(ws),

@@ -15,18 +15,18 @@ Layout plan_workspace(const moe_shape_t &s) {
     Layout L{};
     const size_t T = (size_t)s.T, d = (size_t)s.d_model, f = (size_t)s.d_ff;
     const size_t E = (size_t)s.n_experts, eb = elem_bytes(s.dtype);
-    const size_t rows = 2 * T;
+    const size_t rows = (size_t)s.top_k * T;      // routed rows
     size_t off = 0;
-    L.idx = off;     off += align256(T * 2 * sizeof(int32_t));
-    L.w = off;       off += align256(T * 2 * sizeof(float));
+    L.idx = off;     off += align256(rows * sizeof(int32_t));
+    L.w = off;       off += align256(rows * sizeof(float));
     L.counts = off;  off += align256(E * sizeof(int32_t));
     L.offsets = off; off += align256((E + 1) * sizeof(int32_t));
-    L.pos = off;     off += align256(T * 2 * sizeof(int32_t));
-    L.src = off;     off += align256(T * 2 * sizeof(int32_t));
+    L.pos = off;     off += align256(rows * sizeof(int32_t));
+    L.src = off;     off += align256(rows * sizeof(int32_t));
     L.xn = off;      off += align256(T * d * eb);
     L.xp = off;      off += align256(rows * d * eb);
     L.h = off;       off += align256(rows * f * eb);
-    L.o = off;       off += align256(2 * T * d * sizeof(float));
+    L.o = off;       off += align256(rows * d * sizeof(float));
     L.total = off;
     return L;
 }
@@ -64,13 +64,14 @@ namespace {
 int check_shape(const moe_shape_t *s) {
     if (!s) return MOE_ERR_NULL;
     if (s->dtype != MOE_F32 && s->dtype != MOE_BF16) return MOE_ERR_DTYPE;
-    if (s->top_k != 2) return MOE_ERR_UNSUPPORTED;
     if (s->n_experts < 2 || s->n_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+    if (s->top_k < 1 || s->top_k > kMaxTopK || s->top_k > s->n_experts)
+        return MOE_ERR_UNSUPPORTED;
     if (s->T < 0 || s->d_model < 8 || s->d_ff < 8) return MOE_ERR_SHAPE;
     if (s->d_model % 8 != 0 || s->d_ff % 8 != 0) return MOE_ERR_SHAPE;
     // Keep every element index of the largest array inside 2^31 * 16 bytes
     // of address arithmetic done in size_t, and row counts inside int32.
-    if ((int64_t)s->T > (1 << 29)) return MOE_ERR_SHAPE;
+    if ((int64_t)s->T * s->top_k > (1 << 29)) return MOE_ERR_SHAPE;
     return MOE_OK;
 }
 
@@ -142,7 +143,7 @@ const char *moe_status_str(int status) {
     case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN: device pointers must be 16-byte aligned";
     case MOE_ERR_ALIAS: return "MOE_ERR_ALIAS: an output overlaps an input";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or smaller than moe_workspace_bytes";
-    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: top_k must be 2 and n_experts in [2, 32]";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: n_experts must be in [2, 64] and top_k in [1, min(4, n_experts)]";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP kernel launch failed";
     default: return "unknown moe status";
     }
@@ -174,7 +175,7 @@ int moe_dispatch(const moe_shape_t *s, const void *x, const int32_t *topk_idx, i
         misaligned(pos) || misaligned(xp))
         return MOE_ERR_ALIGN;
     const size_t row = (size_t)s->d_model * elem_bytes(s->dtype);
-    if (overlap(xp, 2 * (size_t)s->T * row, x, (size_t)s->T * row)) return MOE_ERR_ALIAS;
+    if (overlap(xp, (size_t)routed_rows(*s) * row, x, (size_t)s->T * row)) return MOE_ERR_ALIAS;
     return hip_status(
         launch_dispatch(*s, x, topk_idx, counts, offsets, pos, xp, (hipStream_t)stream));
 }
@@ -190,7 +191,8 @@ int moe_expert_gateup(const moe_shape_t *s, const void *xp, const int32_t *count
         misaligned(w3) || misaligned(h))
         return MOE_ERR_ALIGN;
     const size_t eb = elem_bytes(s->dtype);
-    if (overlap(h, 2 * (size_t)s->T * s->d_ff * eb, xp, 2 * (size_t)s->T * s->d_model * eb))
+    const size_t R = (size_t)routed_rows(*s);
+    if (overlap(h, R * s->d_ff * eb, xp, R * s->d_model * eb))
         return MOE_ERR_ALIAS;
     return hip_status(launch_gateup(*s, xp, counts, offsets, w1, w3, h, (hipStream_t)stream));
 }
@@ -205,8 +207,8 @@ int moe_expert_down(const moe_shape_t *s, const void *h, const int32_t *counts,
         misaligned(o))
         return MOE_ERR_ALIGN;
     const size_t eb = elem_bytes(s->dtype);
-    if (overlap(o, 2 * (size_t)s->T * s->d_model * sizeof(float), h,
-                2 * (size_t)s->T * s->d_ff * eb))
+    const size_t R = (size_t)routed_rows(*s);
+    if (overlap(o, R * s->d_model * sizeof(float), h, R * s->d_ff * eb))
         return MOE_ERR_ALIAS;
     return hip_status(launch_down(*s, h, counts, offsets, w2, o, (hipStream_t)stream));
 }
@@ -224,8 +226,9 @@ int moe_experts(const moe_shape_t *s, const void *xp, const int32_t *counts,
     const Layout L = plan_workspace(*s);
     if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
     if (misaligned(ws)) return MOE_ERR_ALIGN;
-    const size_t o_bytes = 2 * (size_t)s->T * s->d_model * sizeof(float);
-    if (overlap(o, o_bytes, xp, 2 * (size_t)s->T * s->d_model * elem_bytes(s->dtype)))
+    const size_t R = (size_t)routed_rows(*s);
+    const size_t o_bytes = R * s->d_model * sizeof(float);
+    if (overlap(o, o_bytes, xp, R * s->d_model * elem_bytes(s->dtype)))
         return MOE_ERR_ALIAS;
     void *h = static_cast<char *>(ws) + L.h;
     hipStream_t str = (hipStream_t)stream;
@@ -243,7 +246,7 @@ int moe_combine(const moe_shape_t *s, const float *o, const int32_t *pos, const 
     if (misaligned(o) || misaligned(pos) || misaligned(topk_w) || misaligned(y))
         return MOE_ERR_ALIGN;
     const size_t y_bytes = (size_t)s->T * s->d_model * elem_bytes(s->dtype);
-    if (overlap(y, y_bytes, o, 2 * (size_t)s->T * s->d_model * sizeof(float)))
+    if (overlap(y, y_bytes, o, (size_t)routed_rows(*s) * s->d_model * sizeof(float)))
         return MOE_ERR_ALIAS;
     return hip_status(launch_combine(*s, o, pos, topk_w, y, (hipStream_t)stream));
 }

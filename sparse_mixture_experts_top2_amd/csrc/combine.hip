@@ -1,12 +1,12 @@
-// Combine: y[t] = w[t,0] * o[pos[t,0]] + w[t,1] * o[pos[t,1]], slot 0 then
-// slot 1, fp32 math, rounded once to y's dtype.  "Mixtral 8x7B -- The
+// Combine: y[t] = w[t,0] * o[pos[t,0]] + w[t,1] * o[pos[t,1]] + ..., in slot
+// order, fp32 math, rounded once to y's dtype.  "Mixtral 8x7B -- The
 // Evolving Transformer", section 05: the formula y = sum_k w_k E_{i_k}(x),
 // and the MoE module's accumulation of each slot's weighted expert output
 // into a zeroed output.  Here every row of y is written exactly once by a
 // gather, so no zero fill and no atomics are needed and the result does not
 // depend on scheduling.  One wavefront per (token, column chunk), 16-byte
 // fp32 loads; with few tokens each row is cut into chunks so that the reads
-// spread over many CUs.  Bound by HBM (2*T*d*4 bytes read, T*d*elem
+// spread over many CUs.  Bound by HBM (k*T*d*4 bytes read, T*d*elem
 // written).
 #include <algorithm>
 
@@ -23,22 +23,32 @@ template <bool BF16_OUT>
 __global__ __launch_bounds__(256) void combine_kernel(const float4 *__restrict__ o,
                                                       const int32_t *__restrict__ pos,
                                                       const float *__restrict__ w, int n_tok,
-                                                      int d4, int chunk4, const void *res,
-                                                      void *y) {
+                                                      int k, int d4, int chunk4,
+                                                      const void *res, void *y) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= n_tok) return;
-    const float4 *r0 = o + (size_t)pos[2 * t] * d4;
-    const float4 *r1 = o + (size_t)pos[2 * t + 1] * d4;
-    const float w0 = w[2 * t], w1 = w[2 * t + 1];
+    const float4 *r[kMaxTopK];
+    float ws[kMaxTopK];
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) {
+        r[s] = s < k ? o + (size_t)pos[k * t + s] * d4 : o;
+        ws[s] = s < k ? w[k * t + s] : 0.0f;
+    }
     const int j1 = min(d4, (int)(blockIdx.y + 1) * chunk4);
     for (int j = blockIdx.y * chunk4 + lane; j < j1; j += 64) {
-        const float4 a = r0[j], b = r1[j];
-        float4 v;
-        v.x = w0 * a.x + w1 * b.x;
-        v.y = w0 * a.y + w1 * b.y;
-        v.z = w0 * a.z + w1 * b.z;
-        v.w = w0 * a.w + w1 * b.w;
+        // slot order: ((w0 o0 + w1 o1) + w2 o2) + w3 o3
+        const float4 a = r[0][j];
+        float4 v = make_float4(ws[0] * a.x, ws[0] * a.y, ws[0] * a.z, ws[0] * a.w);
+#pragma unroll
+        for (int s = 1; s < kMaxTopK; ++s) {
+            if (s >= k) break;
+            const float4 b = r[s][j];
+            v.x = v.x + ws[s] * b.x;
+            v.y = v.y + ws[s] * b.y;
+            v.z = v.z + ws[s] * b.z;
+            v.w = v.w + ws[s] * b.w;
+        }
         if (res) {
             float4 r;
             if (BF16_OUT) {
@@ -78,11 +88,11 @@ hipError_t launch_combine(const moe_shape_t &s, const float *o, const int32_t *p
     const dim3 grid(tok_groups, (d4 + chunk4 - 1) / chunk4), block(256);
     if (s.dtype == MOE_BF16)
         hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, stream,
-                           reinterpret_cast<const float4 *>(o), pos, w, s.T, d4, chunk4, res,
+                           reinterpret_cast<const float4 *>(o), pos, w, s.T, s.top_k, d4, chunk4, res,
                            y);
     else
         hipLaunchKernelGGL(combine_kernel<false>, grid, block, 0, stream,
-                           reinterpret_cast<const float4 *>(o), pos, w, s.T, d4, chunk4, res,
+                           reinterpret_cast<const float4 *>(o), pos, w, s.T, s.top_k, d4, chunk4, res,
                            y);
     return hipGetLastError();
 }

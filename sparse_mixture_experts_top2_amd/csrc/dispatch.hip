@@ -1,5 +1,5 @@
-// Dispatch: group the 2T (token, slot) assignments by expert, stably, and
-// copy each token's row of x to its two grouped rows of xp.  This is the
+// Dispatch: group the kT (token, slot) assignments by expert, stably, and
+// copy each token's row of x to its k grouped rows of xp.  This is the
 // per-expert token batching that "Mixtral 8x7B -- The Evolving Transformer",
 // section 05, says production stacks use in place of its per-expert mask
 // loop; the order within an expert (token, then slot) is the order in which
@@ -29,7 +29,7 @@ __device__ __forceinline__ int clamp_expert(int e, int E) {
 }
 
 __global__ __launch_bounds__(kRankWaves * 64) void dispatch_rank_kernel(
-    const int32_t *__restrict__ idx, int n_assign, int E, int32_t *__restrict__ counts,
+    const int32_t *__restrict__ idx, int n_assign, int E, int k, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ pos, int32_t *__restrict__ src) {
     __shared__ int32_t wbase[kRankWaves][kMaxExperts];   // per-wavefront counts, then bases
     __shared__ int32_t ebase[kMaxExperts + 1];           // expert offsets
@@ -120,7 +120,7 @@ __global__ __launch_bounds__(kRankWaves * 64) void dispatch_rank_kernel(
             if (ev[b] >= 0) {
                 const int p = first + __popcll(mine & lower);
                 pos[a + lane] = p;
-                if (src) src[p] = (a + lane) >> 1;   // token of grouped row p
+                if (src) src[p] = (a + lane) / k;   // token of grouped row p
             }
             if (lane < E) next[lane] += added;   // after every lane has read
         }
@@ -129,18 +129,21 @@ __global__ __launch_bounds__(kRankWaves * 64) void dispatch_rank_kernel(
 
 __global__ __launch_bounds__(256) void scatter_rows_kernel(const uint4 *__restrict__ x,
                                                            const int32_t *__restrict__ pos,
-                                                           int n_tok, int row_vecs,
+                                                           int n_tok, int k, int row_vecs,
                                                            uint4 *__restrict__ xp) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= n_tok) return;
     const uint4 *src = x + (size_t)t * row_vecs;
-    uint4 *d0 = xp + (size_t)pos[2 * t] * row_vecs;
-    uint4 *d1 = xp + (size_t)pos[2 * t + 1] * row_vecs;
+    uint4 *dst[kMaxTopK];
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s)
+        dst[s] = s < k ? xp + (size_t)pos[k * t + s] * row_vecs : nullptr;
     for (int j = lane; j < row_vecs; j += 64) {
-        uint4 v = src[j];
-        d0[j] = v;
-        d1[j] = v;
+        const uint4 v = src[j];
+#pragma unroll
+        for (int s = 0; s < kMaxTopK; ++s)
+            if (s < k) dst[s][j] = v;
     }
 }
 
@@ -149,7 +152,7 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const uint4 *__restri
 hipError_t launch_rank(const moe_shape_t &s, const int32_t *idx, int32_t *counts,
                        int32_t *offsets, int32_t *pos, int32_t *src, hipStream_t stream) {
     hipLaunchKernelGGL(dispatch_rank_kernel, dim3(1), dim3(kRankWaves * 64), 0, stream, idx,
-                       2 * s.T, s.n_experts, counts, offsets, pos, src);
+                       routed_rows(s), s.n_experts, s.top_k, counts, offsets, pos, src);
     return hipGetLastError();
 }
 
@@ -160,7 +163,7 @@ hipError_t launch_dispatch(const moe_shape_t &s, const void *x, const int32_t *i
     if (err != hipSuccess || s.T == 0) return err;
     const int row_vecs = (int)((size_t)s.d_model * elem_bytes(s.dtype) / 16);
     hipLaunchKernelGGL(scatter_rows_kernel, dim3((s.T + 3) / 4), dim3(256), 0, stream,
-                       static_cast<const uint4 *>(x), pos, s.T, row_vecs,
+                       static_cast<const uint4 *>(x), pos, s.T, s.top_k, row_vecs,
                        static_cast<uint4 *>(xp));
     return hipGetLastError();
 }

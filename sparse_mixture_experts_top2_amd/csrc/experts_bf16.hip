@@ -739,7 +739,7 @@ __global__ __launch_bounds__(DWAVES * 64) void decode_gemm_kernel(
 hipError_t launch_gateup_bf16(const moe_shape_t &s, const uint16_t *xp, const int32_t *counts,
                               const int32_t *offsets, const uint16_t *w1, const uint16_t *w3,
                               uint16_t *h, hipStream_t stream, const int32_t *src) {
-    const int d = s.d_model, f = s.d_ff, E = s.n_experts, rows = 2 * s.T;
+    const int d = s.d_model, f = s.d_ff, E = s.n_experts, rows = routed_rows(s);
     if (s.T <= 16) {
         hipLaunchKernelGGL((decode_gemm_kernel<1, 2>), dim3((f + DCOLS - 1) / DCOLS, E),
                            dim3(DWAVES * 64), 0, stream, xp, w1, w3, h, counts, offsets, d, f,
@@ -765,7 +765,7 @@ hipError_t launch_gateup_bf16(const moe_shape_t &s, const uint16_t *xp, const in
 hipError_t launch_down_bf16(const moe_shape_t &s, const uint16_t *h, const int32_t *counts,
                             const int32_t *offsets, const uint16_t *w2, float *o,
                             hipStream_t stream) {
-    const int d = s.d_model, f = s.d_ff, E = s.n_experts, rows = 2 * s.T;
+    const int d = s.d_model, f = s.d_ff, E = s.n_experts, rows = routed_rows(s);
     if (s.T <= 16) {
         hipLaunchKernelGGL((decode_gemm_kernel<1, 1>), dim3((d + DCOLS - 1) / DCOLS, E),
                            dim3(DWAVES * 64), 0, stream, h, w2, nullptr, o, counts, offsets, f,

@@ -88,9 +88,9 @@ hipError_t launch_gateup_f32(const moe_shape_t &s, const float *xp, const int32_
                              const int32_t *offsets, const float *w1, const float *w3,
                              float *h, hipStream_t stream) {
     const int d = s.d_model, f = s.d_ff, E = s.n_experts;
-    const int m_tiles = (2 * s.T + BM - 1) / BM + E;
+    const int m_tiles = (routed_rows(s) + BM - 1) / BM + E;
     hipLaunchKernelGGL(gemm_f32_kernel<2>, dim3((f + BN - 1) / BN, m_tiles), dim3(256), 0,
-                       stream, xp, w1, w3, h, counts, offsets, E, d, f, 2 * s.T);
+                       stream, xp, w1, w3, h, counts, offsets, E, d, f, routed_rows(s));
     return hipGetLastError();
 }
 
@@ -98,9 +98,9 @@ hipError_t launch_down_f32(const moe_shape_t &s, const float *h, const int32_t *
                            const int32_t *offsets, const float *w2, float *o,
                            hipStream_t stream) {
     const int d = s.d_model, f = s.d_ff, E = s.n_experts;
-    const int m_tiles = (2 * s.T + BM - 1) / BM + E;
+    const int m_tiles = (routed_rows(s) + BM - 1) / BM + E;
     hipLaunchKernelGGL(gemm_f32_kernel<1>, dim3((d + BN - 1) / BN, m_tiles), dim3(256), 0,
-                       stream, h, w2, nullptr, o, counts, offsets, E, f, d, 2 * s.T);
+                       stream, h, w2, nullptr, o, counts, offsets, E, f, d, routed_rows(s));
     return hipGetLastError();
 }
 

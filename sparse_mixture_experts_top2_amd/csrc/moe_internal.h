@@ -12,9 +12,11 @@
 
 namespace moe {
 
-constexpr int kMaxExperts = 32;
+constexpr int kMaxExperts = 64;
+constexpr int kMaxTopK = 4;     // experts per token
 // Token counts up to this use the weight-streaming (decode) expert kernels;
-// an expert then has at most 32 rows (a token never picks one expert twice).
+// an expert then has at most 32 rows (a token never picks one expert twice,
+// whatever top_k is).
 constexpr int kDecodeMaxT = 32;
 
 struct Layout {
@@ -25,6 +27,8 @@ struct Layout {
 Layout plan_workspace(const moe_shape_t &s);
 
 inline size_t elem_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
+// Routed rows: top_k per token.
+inline int routed_rows(const moe_shape_t &s) { return s.top_k * s.T; }
 
 // ---------------------------------------------------------------------------
 // Kernel launchers.  Each enqueues on `stream` and returns hipGetLastError().

@@ -1,5 +1,5 @@
-// Router: logits = x w_gate (fp32), top-2 with lowest-index ties, softmax
-// over the two kept logits.  "Mixtral 8x7B -- The Evolving Transformer",
+// Router: logits = x w_gate (fp32), top-k (k <= 4; Mixtral uses 2) with
+// lowest-index ties, softmax over the k kept logits.  "Mixtral 8x7B -- The Evolving Transformer",
 // section 05 (MoERouter and the formula y = sum_k w_k E_{i_k}(x)).
 //
 // The router matrix (d x E, 64 KiB at the 8x7B shape) is read once per
@@ -106,7 +106,8 @@ __device__ __forceinline__ void load_router_row(const T *row, int E, float (&wr)
 template <typename T, int EMAX, int TPB, bool NORM>
 __global__ __launch_bounds__(256) void route_kernel(const T *__restrict__ x,
                                                     const T *__restrict__ wg, int n_tok,
-                                                    int d, int E, int32_t *__restrict__ idx,
+                                                    int d, int E, int k,
+                                                    int32_t *__restrict__ idx,
                                                     float *__restrict__ wout,
                                                     const T *__restrict__ g, float eps,
                                                     T *__restrict__ xn_out) {
@@ -169,7 +170,11 @@ __global__ __launch_bounds__(256) void route_kernel(const T *__restrict__ x,
                 for (int i = 0; i < 8; ++i) xv[tt][i] = round_to<T>(xv[tt][i]);
             }
         }
-#pragma unroll
+        // Router rows are read 8 at a time when few values are accumulated;
+        // wider rows (32+ experts per token) go one or two at a time so that
+        // the accumulators and the row stay in registers.
+        constexpr int RU = EMAX >= 64 ? 1 : EMAX >= 32 ? 2 : 8;
+#pragma unroll RU
         for (int r = 0; r < 8; ++r) {
             float wr[EMAX];
             load_router_row<T, EMAX>(wg + (size_t)(c * 8 + r) * E, E, wr);
@@ -218,25 +223,45 @@ __global__ __launch_bounds__(256) void route_kernel(const T *__restrict__ x,
     if (tid >= TPB) return;
     const int t = t0 + tid;
     if (t >= n_tok) return;
-    float l[EMAX];
-#pragma unroll
-    for (int e = 0; e < EMAX; ++e)
+    // The token's logits, summed over the four wavefronts in a fixed order,
+    // stay in this thread's row of LDS (no other thread touches it).
+    float *l = part[0][tid];
+#pragma unroll 1
+    for (int e = 0; e < E; ++e)
         l[e] = ((part[0][tid][e] + part[1][tid][e]) + part[2][tid][e]) + part[3][tid][e];
-    int i0 = 0;
-    float l0 = l[0];
+    // Top-k, picked greedily: each pick is the largest logit among the
+    // experts not yet picked; strict '>' keeps the lowest index among equal
+    // values.  Weights: softmax over the picked logits relative to the first,
+    // e_0 = 1, e_s = exp(l_s - l_0), w_s = e_s / sum (for k = 2:
+    // w_0 = 1/(1+q), w_1 = q/(1+q)).
+    int sel[kMaxTopK];
+    float ls[kMaxTopK];
 #pragma unroll
-    for (int e = 1; e < EMAX; ++e)
-        if (e < E && l[e] > l0) { i0 = e; l0 = l[e]; }
-    int i1 = -1;
-    float l1 = 0.0f;
+    for (int s = 0; s < kMaxTopK; ++s) {
+        sel[s] = -1;
+        ls[s] = 0.0f;
+        if (s >= k) continue;
+#pragma unroll 1
+        for (int e = 0; e < E; ++e) {
+            bool taken = false;
 #pragma unroll
-    for (int e = 0; e < EMAX; ++e)
-        if (e < E && e != i0 && (i1 < 0 || l[e] > l1)) { i1 = e; l1 = l[e]; }
-    const float q = expf(l1 - l0);
-    idx[2 * t] = i0;
-    idx[2 * t + 1] = i1;
-    wout[2 * t] = 1.0f / (1.0f + q);
-    wout[2 * t + 1] = q / (1.0f + q);
+            for (int r = 0; r < s; ++r) taken |= sel[r] == e;
+            const float le = l[e];
+            if (!taken && (sel[s] < 0 || le > ls[s])) { sel[s] = e; ls[s] = le; }
+        }
+    }
+    float ex[kMaxTopK], sum = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) {
+        ex[s] = s == 0 ? 1.0f : expf(ls[s] - ls[0]);
+        if (s < k) sum += ex[s];
+    }
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) {
+        if (s >= k) break;
+        idx[k * t + s] = sel[s];
+        wout[k * t + s] = ex[s] / sum;
+    }
 }
 
 template <typename T, int EMAX, int TPB>
@@ -246,12 +271,12 @@ hipError_t launch_route_t(const moe_shape_t &s, const void *x, const void *wg, i
     if (g)
         hipLaunchKernelGGL((route_kernel<T, EMAX, TPB, true>), dim3(blocks), dim3(256), 0,
                            stream, static_cast<const T *>(x), static_cast<const T *>(wg), s.T,
-                           s.d_model, s.n_experts, idx, w, static_cast<const T *>(g), eps,
-                           static_cast<T *>(xn));
+                           s.d_model, s.n_experts, s.top_k, idx, w, static_cast<const T *>(g),
+                           eps, static_cast<T *>(xn));
     else
         hipLaunchKernelGGL((route_kernel<T, EMAX, TPB, false>), dim3(blocks), dim3(256), 0,
                            stream, static_cast<const T *>(x), static_cast<const T *>(wg), s.T,
-                           s.d_model, s.n_experts, idx, w, nullptr, 0.0f, nullptr);
+                           s.d_model, s.n_experts, s.top_k, idx, w, nullptr, 0.0f, nullptr);
     return hipGetLastError();
 }
 
@@ -269,8 +294,11 @@ hipError_t launch_route_dtype(const moe_shape_t &s, const void *x, const void *w
     if (s.n_experts <= 16)
         return few ? launch_route_t<T, 16, 1>(s, x, wg, idx, w, g, eps, xn, stream)
                    : launch_route_t<T, 16, 4>(s, x, wg, idx, w, g, eps, xn, stream);
-    return few ? launch_route_t<T, 32, 1>(s, x, wg, idx, w, g, eps, xn, stream)
-               : launch_route_t<T, 32, 2>(s, x, wg, idx, w, g, eps, xn, stream);
+    if (s.n_experts <= 32)
+        return few ? launch_route_t<T, 32, 1>(s, x, wg, idx, w, g, eps, xn, stream)
+                   : launch_route_t<T, 32, 2>(s, x, wg, idx, w, g, eps, xn, stream);
+    // 64 logits per token already fill the reduce-scatter's 64 lanes
+    return launch_route_t<T, 64, 1>(s, x, wg, idx, w, g, eps, xn, stream);
 }
 
 }  // namespace

@@ -173,13 +173,15 @@ def make_inputs(wl: Workload, seed: Optional[int] = None, *,
 
 
 def small_workload(T: int, d: int, f: int, E: int = 8, dtype: str = BF16,
-                   seed: int = 7, bias=None, router_std: Optional[float] = None) -> Workload:
+                   seed: int = 7, bias=None, router_std: Optional[float] = None,
+                   top_k: int = 2) -> Workload:
     """A parity-sized workload with the same value distributions as the
     8x7B decode/prefill recipe (router std 1/sqrt(d) unless given, so that
     logits stay O(1) at small d)."""
     rs = router_std if router_std is not None else 1.0 / math.sqrt(d)
-    return Workload(f"small_T{T}_d{d}_f{f}_E{E}_{dtype}", T=T, d=d, f=f, E=E,
-                    dtype=dtype, router_std=rs, bias=bias, seed=seed)
+    kname = "" if top_k == 2 else f"_k{top_k}"
+    return Workload(f"small_T{T}_d{d}_f{f}_E{E}{kname}_{dtype}", T=T, d=d, f=f, E=E,
+                    top_k=top_k, dtype=dtype, router_std=rs, bias=bias, seed=seed)
 
 
 def make_norm_weight(d: int, seed: int, dtype: str, device: str = "cpu") -> torch.Tensor:

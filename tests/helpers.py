@@ -14,9 +14,12 @@ RW_TOL = {W.F32: 1e-5, W.BF16: 1e-4}
 
 
 def checked_inputs(wl, seed=None, device="cpu"):
-    """Seeded inputs whose routing decisions have a clear margin (every
-    token's 1st/2nd and 2nd/3rd logits differ by at least 1e-3)."""
-    return W.make_inputs(wl, seed, gap_fn=oracle.near_tie_tokens, device=device)
+    """Seeded inputs whose routing decisions have a clear margin (for top-k,
+    every token's s-th and (s+1)-th largest logits differ by at least 1e-3
+    for s = 1 .. k)."""
+    def gap(x, w_gate):
+        return oracle.near_tie_tokens(x, w_gate, top_k=wl.top_k)
+    return W.make_inputs(wl, seed, gap_fn=gap, device=device)
 
 
 def checked_block_inputs(wl, g, eps, seed=None, device="cpu"):
@@ -25,7 +28,7 @@ def checked_block_inputs(wl, g, eps, seed=None, device="cpu"):
     is where the routing is decided."""
     def gap(x, w_gate):
         xn, _ = oracle.rmsnorm(x, g, eps)
-        return oracle.near_tie_tokens(xn, w_gate)
+        return oracle.near_tie_tokens(xn, w_gate, top_k=wl.top_k)
     return W.make_inputs(wl, seed, gap_fn=gap, device=device)
 
 

@@ -54,8 +54,10 @@ def test_status_strings():
 
 
 @pytest.mark.parametrize("bad,expect", [
-    (dict(k=1), "MOE_ERR_UNSUPPORTED"), (dict(k=3), "MOE_ERR_UNSUPPORTED"),
-    (dict(E=1), "MOE_ERR_UNSUPPORTED"), (dict(E=33), "MOE_ERR_UNSUPPORTED"),
+    (dict(k=0), "MOE_ERR_UNSUPPORTED"), (dict(k=5, E=8), "MOE_ERR_UNSUPPORTED"),
+    (dict(k=3, E=2), "MOE_ERR_UNSUPPORTED"), (dict(k=-1), "MOE_ERR_UNSUPPORTED"),
+    (dict(E=1, k=1), "MOE_ERR_UNSUPPORTED"), (dict(E=65), "MOE_ERR_UNSUPPORTED"),
+    (dict(T=(1 << 27) + 1, k=4), "MOE_ERR_SHAPE"),
     (dict(T=-1), "MOE_ERR_SHAPE"), (dict(d=100), "MOE_ERR_SHAPE"), (dict(f=12), "MOE_ERR_SHAPE"),
     (dict(d=0), "MOE_ERR_SHAPE"), (dict(dtype=7), "MOE_ERR_DTYPE"),
 ])
@@ -64,6 +66,23 @@ def test_shape_checks(bad, expect):
     st = call_forward(s)
     assert moe.STATUS_NAMES[st] == expect
     assert moe.load_library().moe_workspace_bytes(ctypes.byref(s)) == 0
+
+
+@pytest.mark.parametrize("E,k", [(2, 1), (2, 2), (8, 1), (8, 3), (8, 4), (16, 4), (33, 2),
+                                 (64, 1), (64, 4), (4, 4)])
+def test_supported_routings(E, k):
+    # every E in [2, 64] with k in [1, min(4, E)] passes the shape check
+    s = shape(E=E, k=k)
+    assert call_forward(shape(T=0, E=E, k=k)) == moe.MOE_OK
+    assert moe.load_library().moe_workspace_bytes(ctypes.byref(s)) > 0
+
+
+def test_workspace_scales_with_top_k():
+    lib = moe.load_library()
+    sizes = [lib.moe_workspace_bytes(ctypes.byref(shape(T=256, E=8, k=k))) for k in (1, 2, 3, 4)]
+    assert sizes == sorted(sizes) and len(set(sizes)) == 4
+    # the routed rows (xp, h, o: bf16 d + bf16 f + fp32 d per row) grow by T per extra slot
+    assert sizes[3] - sizes[2] >= 256 * (128 * 2 + 256 * 2 + 128 * 4)
 
 
 def test_null_alignment_alias_workspace_checks():
