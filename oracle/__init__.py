@@ -9,8 +9,11 @@ with gcc, and the integer bookkeeping below is plain Python.
 Functions, each following "Mixtral 8x7B -- The Evolving Transformer",
 section 05 (MOE ROUTER + MOE), and section 04 (SWIGLU):
 
-* ``route``        router logits, top-2 with lowest-index ties, softmax over
-                   the two selected logits (MoERouter; formula of section 05)
+* ``route``        router logits, top-k (Mixtral: top-2) with lowest-index
+                   ties, softmax over the selected logits (MoERouter; formula
+                   of section 05)
+* ``route_probs``  the same router in the page's order of steps: softmax
+                   over all experts, top-k of the probabilities, renormalise
 * ``dispatch``     stable grouping of (token, slot) assignments by expert:
                    the per-expert token batches that section 05 says
                    production stacks form instead of looping with masks
@@ -66,6 +69,8 @@ def _bind(path: str):
     lib.oracle_expert_hidden.restype = I
     lib.oracle_expert_down.argtypes = [I, I, I, I, P, P, P, I, P, I]
     lib.oracle_expert_down.restype = I
+    lib.oracle_route_probs.argtypes = [I, I, I, I, P, P, I, P, P, P, I]
+    lib.oracle_route_probs.restype = I
     lib.oracle_rmsnorm.argtypes = [I, I, P, P, ctypes.c_double, I, P, P, I]
     lib.oracle_rmsnorm.restype = I
     return lib
@@ -153,6 +158,26 @@ def route(x, w_gate, threads: Optional[int] = None, return_logits: bool = False,
     if rc != 0:
         raise ValueError("oracle_route rejected its sizes")
     return (idx, w, logits) if return_logits else (idx, w)
+
+
+def route_probs(x, w_gate, top_k: int = 2, threads: Optional[int] = None):
+    """The router in the page's order of steps: softmax over all E logits,
+    top-k of the probabilities, kept probabilities divided by their sum.
+    Returns probs float64 [T,E], idx int32 [T,k], w float64 [T,k]."""
+    xa, dx = _as_host(x)
+    ga, dg = _as_host(w_gate)
+    dt = _same_dtype(dx, dg)
+    T, d = xa.shape
+    d2, E = ga.shape
+    assert d == d2
+    probs = np.zeros((T, E), np.float64)
+    idx = np.zeros((T, top_k), np.int32)
+    w = np.zeros((T, top_k), np.float64)
+    rc = _load().oracle_route_probs(T, d, E, top_k, _ptr(xa), _ptr(ga), dt, _ptr(probs),
+                                    _ptr(idx), _ptr(w), threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_route_probs rejected its sizes")
+    return probs, idx, w
 
 
 def dispatch(idx: np.ndarray, n_experts: int):

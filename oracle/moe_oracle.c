@@ -213,6 +213,64 @@ int oracle_route(int T, int d, int E, int k, const void *x, const void *wg, int 
     return 0;
 }
 
+/* The router in the page's own order of steps (section 05, MoERouter:
+ * softmax over all E logits, top-k of the probabilities, divide the kept
+ * probabilities by their sum), for one token:
+ *   p[e]  = exp(l[e] - m) / sum_e' exp(l[e'] - m),  m = max_e l[e]
+ *           (subtracting m changes nothing mathematically and keeps exp finite)
+ *   picks = greedy largest p among the experts not yet picked, decided on p
+ *           rounded to fp32 (the GPU's precision), ties to the lower index
+ *   w_s   = p[i_s] / (p[i_0] + ... + p[i_{k-1}])
+ * Mathematically the picks and weights equal topk_softmax's; only rounding
+ * differs. */
+static void softmax_topk(int E, int k, const double *l, double *p, int32_t *idx, double *w) {
+    double m = l[0];
+    for (int e = 1; e < E; ++e) if (l[e] > m) m = l[e];
+    double z = 0.0;
+    for (int e = 0; e < E; ++e) { p[e] = exp(l[e] - m); z += p[e]; }
+    for (int e = 0; e < E; ++e) p[e] /= z;
+    for (int s = 0; s < k; ++s) {
+        int pick = -1;
+        for (int e = 0; e < E; ++e) {
+            int used = 0;
+            for (int r = 0; r < s; ++r) used |= idx[r] == e;
+            if (!used && (pick < 0 || (float)p[e] > (float)p[pick])) pick = e;
+        }
+        idx[s] = pick;
+    }
+    double kept = 0.0;
+    for (int s = 0; s < k; ++s) kept += p[idx[s]];
+    for (int s = 0; s < k; ++s) w[s] = p[idx[s]] / kept;
+}
+
+typedef struct {
+    int T, d, E, k, dtype;
+    const void *x, *wg;
+    double *probs;
+    int32_t *idx;
+    double *w;
+} probs_ctx;
+
+static void route_probs_range(void *p, int lo, int hi) {
+    probs_ctx *c = (probs_ctx *)p;
+    double l[256];
+    for (int t = lo; t < hi; ++t) {
+        router_logits(c->d, c->E, c->x, (size_t)t * c->d, c->wg, c->dtype, l);
+        softmax_topk(c->E, c->k, l, c->probs + (size_t)t * c->E, c->idx + (size_t)c->k * t,
+                     c->w + (size_t)c->k * t);
+    }
+}
+
+/* Page-form router for T tokens: probs [T,E], idx [T,k], w [T,k] (fp64 but
+ * idx).  Returns 0, or -1 on bad sizes. */
+int oracle_route_probs(int T, int d, int E, int k, const void *x, const void *wg, int dtype,
+                       double *probs, int32_t *idx, double *w, int threads) {
+    if (T < 0 || d < 1 || E < 1 || E > 256 || k < 1 || k > ORC_MAX_K || k > E) return -1;
+    probs_ctx c = {T, d, E, k, dtype, x, wg, probs, idx, w};
+    parallel_for(T, threads, route_probs_range, &c);
+    return 0;
+}
+
 typedef struct {
     int n, d, f, dtype;
     const void *rows;          /* [n, d] */

@@ -383,13 +383,55 @@ def pin_topk_layer_special_cases():
         np.testing.assert_array_equal(pos.reshape(-1)[order], np.arange(k * 50))
 
 
+def pin_route_probs_page_form():
+    """The router in the page's order of steps ("Mixtral 8x7B -- The Evolving
+    Transformer", section 05, MoERouter: softmax over all experts, top-k,
+    divide by the kept sum).  Probabilities: scipy's softmax of numpy fp64
+    logits, and a hand-derived case.  Picks: a plain sort of (-fp32 p,
+    index).  Weights: equal to the softmax over the picked logits (the two
+    orders of steps agree mathematically).  A common shift of every logit by
+    800 changes nothing (exp of the unshifted values would overflow)."""
+    from scipy.special import softmax
+    probs, idx, w = oracle.route_probs(np.ones((1, 1), np.float32),
+                                       np.array([[2.0, 1.0, 0.0]], np.float32), top_k=2)
+    p0 = 1.0 / (1.0 + math.exp(-1.0) + math.exp(-2.0))
+    np.testing.assert_allclose(probs[0], [p0, p0 * math.exp(-1.0), p0 * math.exp(-2.0)],
+                               rtol=1e-15)
+    np.testing.assert_array_equal(idx, [[0, 1]])
+    np.testing.assert_allclose(w[0], [_s(1.0), 1.0 - _s(1.0)], rtol=1e-15)
+    rng = np.random.default_rng(33)
+    for E, k in ((8, 2), (8, 1), (16, 4), (5, 3), (4, 4), (64, 4)):
+        x = rng.standard_normal((30, 12)).astype(np.float32)
+        wg = rng.standard_normal((12, E)).astype(np.float32)
+        wg[:, E - 1] = wg[:, 0]                  # exact ties between experts 0 and E-1
+        probs, idx, w = oracle.route_probs(x, wg, top_k=k)
+        ref = softmax(x.astype(np.float64) @ wg.astype(np.float64), axis=1)
+        np.testing.assert_allclose(probs, ref, rtol=1e-12, atol=0)
+        for t in range(30):
+            key = sorted(range(E), key=lambda e: (-float(np.float32(probs[t, e])), e))
+            assert list(idx[t]) == key[:k], (E, k, t)
+        idx_l, w_l = oracle.route(x, wg, top_k=k)
+        np.testing.assert_array_equal(idx, idx_l)
+        np.testing.assert_allclose(w, w_l, rtol=1e-13, atol=0)
+        np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+        if k == E:
+            np.testing.assert_allclose(w, np.take_along_axis(probs, idx, axis=1), rtol=1e-14)
+        xs = np.concatenate([x, np.ones((30, 1), np.float32)], axis=1)
+        ws = np.concatenate([wg, np.full((1, E), 800.0, np.float32)], axis=0)
+        probs_s, idx_s, w_s = oracle.route_probs(xs, ws, top_k=k)
+        np.testing.assert_array_equal(idx_s, idx)
+        np.testing.assert_allclose(probs_s, probs, rtol=1e-9, atol=1e-300)
+        np.testing.assert_allclose(w_s, w, rtol=1e-9)
+
+
 PINS = [pin_worked_examples, pin_logits_match_numpy, pin_top2_brute_force,
         pin_weights_closed_form_and_page_form, pin_forward_matches_numpy_dense,
         pin_expert_rows_match_numpy, pin_identical_experts_equal_dense_swiglu,
         pin_forced_one_hot_router, pin_power_of_two_scaling,
         pin_expert_relabelling_and_token_permutation, pin_dispatch_is_stable_grouping,
         pin_rmsnorm_closed_forms, pin_rmsnorm_invariants, pin_block_identities,
-        pin_topk_brute_force_and_special_weights, pin_topk_layer_special_cases]
+        pin_topk_brute_force_and_special_weights, pin_topk_layer_special_cases,
+        pin_route_probs_page_form]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -435,6 +477,11 @@ MUTANTS = {
                                       "ex[s] = s == 0 ? 1.0 : exp(l[idx[0]] - l[idx[s]]);"),
     "second_pick_may_repeat": ("for (int r = 0; r < s; ++r) taken |= idx[r] == e;",
                                "for (int r = 0; r < s - 1; ++r) taken |= idx[r] == e;"),
+    "probs_not_renormalised": ("for (int s = 0; s < k; ++s) w[s] = p[idx[s]] / kept;",
+                               "for (int s = 0; s < k; ++s) w[s] = p[idx[s]];"),
+    "probs_ties_to_higher_index": ("(pick < 0 || (float)p[e] > (float)p[pick])",
+                                   "(pick < 0 || (float)p[e] >= (float)p[pick])"),
+    "probs_without_max_shift": ("p[e] = exp(l[e] - m);", "p[e] = exp(l[e]);"),
     "norm_sum_not_mean": ("sqrt(ss / (double)c->d + c->eps)", "sqrt(ss + c->eps)"),
     "norm_no_sqrt": ("sqrt(ss / (double)c->d + c->eps)", "(ss / (double)c->d + c->eps)"),
     "norm_eps_outside": ("1.0 / sqrt(ss / (double)c->d + c->eps)",
