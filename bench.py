@@ -23,6 +23,11 @@ on the decode tokens for a bounded time.
 fused into the router, residual add into the combine), with the time the
 fused steps add over the plain layer.
 
+``top_k``: the same workloads routed to 1 and to 4 experts per token
+(Mixtral uses 2), each with its layer roofline: bytes of the experts that
+received tokens for the decode step, 2 k T (3 d f) + 2 T d E FLOPs for the
+prefill.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 import argparse
@@ -55,6 +60,8 @@ def parse():
                     help="wall time budget of the CPU oracle baseline (0 to skip)")
     ap.add_argument("--no-block", dest="block", action="store_false",
                     help="skip the block-boundary (RMSNorm + residual) measurement")
+    ap.add_argument("--no-topk", dest="topk", action="store_false",
+                    help="skip the top-1 / top-4 measurement")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this size (for counter scaling)")
     return ap.parse_args()
@@ -175,6 +182,49 @@ def measure_block(wl_name, steps, warmup, plain_ms):
             "fused_norm_residual_ms": round(ms - plain_ms, 5)}
 
 
+def measure_topk(wl_name, k, steps, warmup):
+    """The layer on the same workload shape with top_k = k: step time and
+    the layer's roofline fraction (decode: HBM bytes of the experts that
+    received tokens plus x and y; prefill: 2 k T (3 d f) + 2 T d E FLOPs)."""
+    import torch
+    import sparse_mixture_experts_top2_amd as moe
+    from sparse_mixture_experts_top2_amd import workloads as W
+
+    wl = W.WORKLOADS[wl_name].with_(top_k=k)
+    dev = torch.device("cuda:0")
+    inp = W.make_inputs(wl, device="cuda")
+    stream = torch.cuda.current_stream(dev)
+    ws = moe.alloc_workspace(wl.T, wl.d, wl.f, wl.E, inp.x.dtype, dev, top_k=k)
+    y = torch.empty_like(inp.x)
+
+    def step():
+        moe.forward(inp.x, inp.w_gate, inp.w1, inp.w3, inp.w2, workspace=ws, out=y, top_k=k)
+
+    for _ in range(warmup):
+        step()
+    ms = time_region(step, steps, stream)
+    idx, _ = moe.route(inp.x, inp.w_gate, top_k=k)
+    c = torch.bincount(idx.flatten().long(), minlength=wl.E).cpu().tolist()
+    active = sum(1 for v in c if v > 0)
+    eb = 2 if wl.dtype == W.BF16 else 4
+    if wl.T <= 32:
+        nbytes = active * 3 * wl.d * wl.f * eb + 2 * wl.T * wl.d * eb + wl.d * wl.E * eb
+        ach = nbytes / (ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "algorithmic_bytes_per_step": nbytes}
+    else:
+        flops = wl.T * (2.0 * k * 3 * wl.d * wl.f + 2.0 * wl.d * wl.E)
+        ach = flops / (ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "algorithmic_flops_per_step": flops}
+    log(f"{wl_name} top-{k}: {ms:.4f} ms/step ({wl.T / ms * 1e3:.0f} tokens/s); "
+        f"layer {roof['frac'] * 100:.1f}% of {roof['bound']} peak; counts {c}")
+    return {"workload": wl_name, "top_k": k, "value": round(wl.T / (ms * 1e-3), 1),
+            "unit": "tokens/s", "ms_per_step": round(ms, 5), "steps": steps, "warmup": warmup,
+            "layer_roofline": roof, "expert_counts": c}
+
+
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_gateup_8x7b.md")
 
 
@@ -265,12 +315,19 @@ def main():
     blocks = []
     if args.block:
         blocks.append(measure_block(args.workload, steps, warmup, main_res["ms"]))
+    topk = []
+    if args.topk:
+        for k in (1, 4):
+            topk.append(measure_topk(args.workload, k, max(20, steps // 2), warmup))
     sec = None
     if args.secondary:
         s_steps, s_warm = defaults(args.secondary)
         r = measure(args.secondary, s_steps, s_warm)
         if args.block:
             blocks.append(measure_block(args.secondary, s_steps, s_warm, r["ms"]))
+        if args.topk:
+            for k in (1, 4):
+                topk.append(measure_topk(args.secondary, k, s_steps // 2 or 1, s_warm))
         sec = {"workload": r["wl"].name, "value": round(r["tokens_per_s"], 1), "unit": "tokens/s",
                "ms_per_step": round(r["ms"], 5), "steps": s_steps, "warmup": s_warm,
                "config": {"T": r["wl"].T, "d_model": r["wl"].d, "d_ff": r["wl"].f,
@@ -305,6 +362,7 @@ def main():
         "cpu_baseline": cpu,
         "secondary": sec,
         "block_boundary": blocks or None,
+        "top_k": topk or None,
     }
     print(json.dumps(out), flush=True)
 

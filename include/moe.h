@@ -100,6 +100,24 @@ size_t moe_workspace_bytes(const moe_shape_t *shape);
 int moe_route(const moe_shape_t *shape, const void *x, const void *w_gate,
               int32_t *topk_idx, float *topk_w, void *stream);
 
+/* Router in the page's own order of steps: section 05's MoERouter applies
+ * a softmax over all E logits, keeps the top_k probabilities and divides
+ * them by their sum:
+ *   l[t,e]     = sum_j x[t,j] w_gate[j,e]                        (fp32)
+ *   probs[t,e] = exp(l[t,e] - m_t) / sum_e' exp(l[t,e'] - m_t),  m_t = max_e l[t,e]
+ *                (the sum runs in expert order)
+ *   topk_idx[t,s] = argmax of probs over the experts not yet picked, equal
+ *                   probabilities resolved toward the lower expert index
+ *   topk_w[t,s]   = probs[t,idx_s] / (probs[t,idx_0] + ... + probs[t,idx_{k-1}])
+ * The picks and weights equal moe_route's mathematically (exp is increasing
+ * and the common factor cancels); only fp32 rounding differs, by a few
+ * ulps in the weights, and two logits within an exp rounding of each other
+ * may tie here where moe_route orders them.  probs_opt (fp32 [T, E], may be
+ * NULL) receives the probabilities.  Outputs must not overlap one another,
+ * x or w_gate (MOE_ERR_ALIAS). */
+int moe_route_probs(const moe_shape_t *shape, const void *x, const void *w_gate,
+                    float *probs_opt, int32_t *topk_idx, float *topk_w, void *stream);
+
 /* Dispatch: the per-expert batching of tokens that section 05 names as the
  * production form of its mask loop.  The R = k T (token, slot) assignments
  * in topk_idx [T, k] are grouped by expert, keeping token order and then

@@ -25,7 +25,8 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_OK = 0
 STATUS_NAMES = ["MOE_OK", "MOE_ERR_NULL", "MOE_ERR_SHAPE", "MOE_ERR_DTYPE", "MOE_ERR_ALIGN",
                 "MOE_ERR_ALIAS", "MOE_ERR_WORKSPACE", "MOE_ERR_UNSUPPORTED", "MOE_ERR_HIP"]
-EXPORTED = ["moe_status_str", "moe_workspace_bytes", "moe_route", "moe_dispatch",
+EXPORTED = ["moe_status_str", "moe_workspace_bytes", "moe_route", "moe_route_probs",
+            "moe_dispatch",
             "moe_expert_gateup", "moe_expert_down", "moe_experts", "moe_combine",
             "moe_forward", "moe_rmsnorm_route", "moe_block_forward"]
 
@@ -63,6 +64,8 @@ def load_library(path: Optional[str] = None):
     lib.moe_workspace_bytes.restype = Z
     lib.moe_route.argtypes = [S, P, P, P, P, P]
     lib.moe_route.restype = I
+    lib.moe_route_probs.argtypes = [S, P, P, P, P, P, P]
+    lib.moe_route_probs.restype = I
     lib.moe_dispatch.argtypes = [S, P, P, P, P, P, P, P]
     lib.moe_dispatch.restype = I
     lib.moe_expert_gateup.argtypes = [S, P, P, P, P, P, P, P]
@@ -180,6 +183,25 @@ def route(x: torch.Tensor, w_gate: torch.Tensor,
                                   _stream(x.device))
     _check(st, "moe_route")
     return idx, w
+
+
+def route_probs(x: torch.Tensor, w_gate: torch.Tensor, top_k: int = 2,
+                return_probs: bool = True):
+    """Router in the page's order of steps (softmax over all experts, top-k
+    of the probabilities, renormalised).  Returns (probs fp32 [T,E] or None,
+    topk_idx int32 [T,k], topk_w fp32 [T,k])."""
+    _need(x, "x")
+    T, d = x.shape
+    _need(w_gate, "w_gate", x.dtype, x.device)
+    E = w_gate.shape[1]
+    _need(w_gate, "w_gate", shape=(d, E))
+    idx, w = _routing_out(T, top_k, x.device)
+    probs = torch.empty(T, E, dtype=torch.float32, device=x.device) if return_probs else None
+    shape = make_shape(T, d, 8, E, x.dtype, top_k)
+    st = load_library().moe_route_probs(ctypes.byref(shape), _ptr(x), _ptr(w_gate), _ptr(probs),
+                                        _ptr(idx), _ptr(w), _stream(x.device))
+    _check(st, "moe_route_probs")
+    return probs, idx, w
 
 
 def dispatch(x: torch.Tensor, topk_idx: torch.Tensor, n_experts: int):

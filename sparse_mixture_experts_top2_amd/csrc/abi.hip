@@ -165,6 +165,30 @@ int moe_route(const moe_shape_t *s, const void *x, const void *w_gate, int32_t *
     return hip_status(launch_route(*s, x, w_gate, topk_idx, topk_w, (hipStream_t)stream));
 }
 
+int moe_route_probs(const moe_shape_t *s, const void *x, const void *w_gate, float *probs_opt,
+                    int32_t *topk_idx, float *topk_w, void *stream) {
+    int st = check_shape(s);
+    if (st) return st;
+    if (s->T == 0) return MOE_OK;  // nothing to read or write
+    if (!x || !w_gate || !topk_idx || !topk_w) return MOE_ERR_NULL;
+    if (misaligned(x) || misaligned(w_gate) || misaligned(topk_idx) || misaligned(topk_w) ||
+        misaligned(probs_opt))
+        return MOE_ERR_ALIGN;
+    const size_t eb = elem_bytes(s->dtype), T = (size_t)s->T, E = (size_t)s->n_experts;
+    const size_t kb = T * s->top_k * 4, pb = probs_opt ? T * E * 4 : 0;
+    const size_t xb = T * s->d_model * eb, gb = (size_t)s->d_model * E * eb;
+    const void *outs[3] = {probs_opt, topk_idx, topk_w};
+    const size_t ob[3] = {pb, kb, kb};
+    for (int i = 0; i < 3; ++i) {
+        if (overlap(outs[i], ob[i], x, xb) || overlap(outs[i], ob[i], w_gate, gb))
+            return MOE_ERR_ALIAS;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlap(outs[i], ob[i], outs[j], ob[j])) return MOE_ERR_ALIAS;
+    }
+    return hip_status(
+        launch_route_probs(*s, x, w_gate, probs_opt, topk_idx, topk_w, (hipStream_t)stream));
+}
+
 int moe_dispatch(const moe_shape_t *s, const void *x, const int32_t *topk_idx, int32_t *counts,
                  int32_t *offsets, int32_t *pos, void *xp, void *stream) {
     int st = check_shape(s);

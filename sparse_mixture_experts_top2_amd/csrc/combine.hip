@@ -18,22 +18,23 @@ namespace {
 // With res (the residual stream, same dtype as y), y = res + combine: the
 // block's residual add ("Mixtral 8x7B -- The Evolving Transformer", section
 // 03 MISTRAL BLOCK), still rounded once.  y may be res itself: each element
-// is read before the same thread writes it.
-template <bool BF16_OUT>
+// is read before the same thread writes it.  K (slots per token) is a
+// template parameter so that the slot loops are straight-line code.
+template <bool BF16_OUT, int K>
 __global__ __launch_bounds__(256) void combine_kernel(const float4 *__restrict__ o,
                                                       const int32_t *__restrict__ pos,
                                                       const float *__restrict__ w, int n_tok,
-                                                      int k, int d4, int chunk4,
-                                                      const void *res, void *y) {
+                                                      int d4, int chunk4, const void *res,
+                                                      void *y) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= n_tok) return;
-    const float4 *r[kMaxTopK];
-    float ws[kMaxTopK];
+    const float4 *r[K];
+    float ws[K];
 #pragma unroll
-    for (int s = 0; s < kMaxTopK; ++s) {
-        r[s] = s < k ? o + (size_t)pos[k * t + s] * d4 : o;
-        ws[s] = s < k ? w[k * t + s] : 0.0f;
+    for (int s = 0; s < K; ++s) {
+        r[s] = o + (size_t)pos[K * t + s] * d4;
+        ws[s] = w[K * t + s];
     }
     const int j1 = min(d4, (int)(blockIdx.y + 1) * chunk4);
     for (int j = blockIdx.y * chunk4 + lane; j < j1; j += 64) {
@@ -41,8 +42,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float4 *__restrict__
         const float4 a = r[0][j];
         float4 v = make_float4(ws[0] * a.x, ws[0] * a.y, ws[0] * a.z, ws[0] * a.w);
 #pragma unroll
-        for (int s = 1; s < kMaxTopK; ++s) {
-            if (s >= k) break;
+        for (int s = 1; s < K; ++s) {
             const float4 b = r[s][j];
             v.x = v.x + ws[s] * b.x;
             v.y = v.y + ws[s] * b.y;
@@ -74,6 +74,34 @@ __global__ __launch_bounds__(256) void combine_kernel(const float4 *__restrict__
     }
 }
 
+template <bool BF16_OUT>
+hipError_t launch_combine_t(const moe_shape_t &s, dim3 grid, const float4 *o, const int32_t *pos,
+                            const float *w, int d4, int chunk4, const void *res, void *y,
+                            hipStream_t stream) {
+    const dim3 block(256);
+    switch (s.top_k) {
+    case 1:
+        hipLaunchKernelGGL((combine_kernel<BF16_OUT, 1>), grid, block, 0, stream, o, pos, w, s.T,
+                           d4, chunk4, res, y);
+        break;
+    case 2:
+        hipLaunchKernelGGL((combine_kernel<BF16_OUT, 2>), grid, block, 0, stream, o, pos, w, s.T,
+                           d4, chunk4, res, y);
+        break;
+    case 3:
+        hipLaunchKernelGGL((combine_kernel<BF16_OUT, 3>), grid, block, 0, stream, o, pos, w, s.T,
+                           d4, chunk4, res, y);
+        break;
+    case 4:
+        hipLaunchKernelGGL((combine_kernel<BF16_OUT, 4>), grid, block, 0, stream, o, pos, w, s.T,
+                           d4, chunk4, res, y);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_combine(const moe_shape_t &s, const float *o, const int32_t *pos,
@@ -85,16 +113,11 @@ hipError_t launch_combine(const moe_shape_t &s, const float *o, const int32_t *p
     const int passes = (d4 + 63) / 64;
     const int nch = std::max(1, std::min(passes, 512 / tok_groups));
     const int chunk4 = (passes + nch - 1) / nch * 64;
-    const dim3 grid(tok_groups, (d4 + chunk4 - 1) / chunk4), block(256);
+    const dim3 grid(tok_groups, (d4 + chunk4 - 1) / chunk4);
+    const float4 *o4 = reinterpret_cast<const float4 *>(o);
     if (s.dtype == MOE_BF16)
-        hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, stream,
-                           reinterpret_cast<const float4 *>(o), pos, w, s.T, s.top_k, d4, chunk4, res,
-                           y);
-    else
-        hipLaunchKernelGGL(combine_kernel<false>, grid, block, 0, stream,
-                           reinterpret_cast<const float4 *>(o), pos, w, s.T, s.top_k, d4, chunk4, res,
-                           y);
-    return hipGetLastError();
+        return launch_combine_t<true>(s, grid, o4, pos, w, d4, chunk4, res, y, stream);
+    return launch_combine_t<false>(s, grid, o4, pos, w, d4, chunk4, res, y, stream);
 }
 
 }  // namespace moe

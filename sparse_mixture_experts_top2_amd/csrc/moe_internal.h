@@ -41,6 +41,12 @@ hipError_t launch_route_norm(const moe_shape_t &s, const void *x, const void *g,
                              const void *w_gate, void *xn, int32_t *idx, float *w,
                              hipStream_t stream);
 
+// Router in the page's order of steps: softmax over all E logits, top-k
+// of the probabilities, kept probabilities renormalised; probs [T, E] is
+// written when not NULL.
+hipError_t launch_route_probs(const moe_shape_t &s, const void *x, const void *w_gate,
+                              float *probs, int32_t *idx, float *w, hipStream_t stream);
+
 hipError_t launch_dispatch(const moe_shape_t &s, const void *x, const int32_t *idx,
                            int32_t *counts, int32_t *offsets, int32_t *pos, void *xp,
                            hipStream_t stream);

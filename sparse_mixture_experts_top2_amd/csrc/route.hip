@@ -1,6 +1,9 @@
 // Router: logits = x w_gate (fp32), top-k (k <= 4; Mixtral uses 2) with
 // lowest-index ties, softmax over the k kept logits.  "Mixtral 8x7B -- The Evolving Transformer",
 // section 05 (MoERouter and the formula y = sum_k w_k E_{i_k}(x)).
+// Page form (the MoERouter's own order of steps): softmax over all E
+// logits, top-k of the probabilities, kept probabilities renormalised; the
+// probabilities can be written out.
 //
 // The router matrix (d x E, 64 KiB at the 8x7B shape) is read once per
 // workgroup from L2 and reused for its tokens; the kernel is bound by
@@ -67,28 +70,107 @@ __device__ __forceinline__ float load1<float>(const float *p) { return *p; }
 template <>
 __device__ __forceinline__ float load1<uint16_t>(const uint16_t *p) { return bf16_to_f32(*p); }
 
-// Router row j (E values) widened to fp32.  When E == EMAX the row is
-// contiguous and 16-byte aligned (w_gate is 16-byte aligned and
-// EMAX * sizeof(T) is a multiple of 16), so it is read with vector loads.
+// Router row j (E values) widened to fp32.  When E is a multiple of the
+// values per 16 bytes, every row is 16-byte aligned (w_gate is 16-byte
+// aligned), so it is read with vector loads, one condition per 16 bytes,
+// and slots e >= E hold 0.  Otherwise element by element, slots e >= E
+// repeating column E-1 (their sums are never read).  The clamp bound sits
+// in a vector register so that the compiler does not hoist EMAX uniform
+// compares or offsets out of the loop into scalar registers.
 template <typename T, int EMAX>
 __device__ __forceinline__ void load_router_row(const T *row, int E, float (&wr)[EMAX]) {
-    if (E == EMAX) {
-        constexpr int per16 = 16 / (int)sizeof(T);
+    constexpr int per16 = 16 / (int)sizeof(T);
+    if (E % per16 == 0) {
 #pragma unroll
         for (int v = 0; v < EMAX / per16; ++v) {
             float t[8];
-            if constexpr (sizeof(T) == 2) {
-                load8<T>(row + v * 8, t);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) wr[v * 8 + i] = t[i];
+            if (v * per16 < E) {
+                if constexpr (sizeof(T) == 2) {
+                    load8<T>(row + v * 8, t);
+                } else {
+                    float4 q = reinterpret_cast<const float4 *>(row)[v];
+                    t[0] = q.x; t[1] = q.y; t[2] = q.z; t[3] = q.w;
+                }
             } else {
-                float4 q = reinterpret_cast<const float4 *>(row)[v];
-                wr[v * 4 + 0] = q.x; wr[v * 4 + 1] = q.y; wr[v * 4 + 2] = q.z; wr[v * 4 + 3] = q.w;
+#pragma unroll
+                for (int i = 0; i < per16; ++i) t[i] = 0.0f;
             }
+#pragma unroll
+            for (int i = 0; i < per16; ++i) wr[v * per16 + i] = t[i];
         }
     } else {
+        int last;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(last) : "s"(E - 1));
 #pragma unroll
-        for (int e = 0; e < EMAX; ++e) wr[e] = e < E ? load1<T>(row + e) : 0.0f;
+        for (int e = 0; e < EMAX; ++e) wr[e] = load1<T>(row + min(e, last));
+    }
+}
+
+// One token's routing from its E logits l[0..E) (a register array, with
+// U = EMAX to unroll every loop over experts, or a row of LDS with U = 1).
+//
+// Page form: the logits become their softmax over all E experts (max
+// subtracted, sum in expert order), written to probs when it is not NULL,
+// and the picks and weights are taken on those probabilities.
+// Top-k, picked greedily: each pick is the largest value among the experts
+// not yet picked; strict '>' keeps the lowest index among equal values.
+// Weights: softmax over the picked logits relative to the first, e_0 = 1,
+// e_s = exp(l_s - l_0), w_s = e_s / sum (for k = 2: w_0 = 1/(1+q),
+// w_1 = q/(1+q)); page form: w_s = p_s / (sum of the kept p).
+template <int EMAX, int U, typename Row>
+__device__ __forceinline__ void finish_token(Row &l, int E, int k, int page, float *probs,
+                                             int t, int32_t *__restrict__ idx,
+                                             float *__restrict__ wout) {
+    if (page) {
+        float m = l[0];
+#pragma unroll U
+        for (int e = 1; e < EMAX; ++e) {
+            if (e >= E) break;
+            m = fmaxf(m, l[e]);
+        }
+        float z = 0.0f;
+#pragma unroll U
+        for (int e = 0; e < EMAX; ++e) {
+            if (e >= E) break;
+            const float pe = expf(l[e] - m);
+            l[e] = pe;
+            z += pe;
+        }
+#pragma unroll U
+        for (int e = 0; e < EMAX; ++e) {
+            if (e >= E) break;
+            l[e] = l[e] / z;
+            if (probs) probs[(size_t)t * E + e] = l[e];
+        }
+    }
+    int sel[kMaxTopK];
+    float ls[kMaxTopK];
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) {
+        sel[s] = -1;
+        ls[s] = 0.0f;
+        if (s >= k) continue;
+#pragma unroll U
+        for (int e = 0; e < EMAX; ++e) {
+            if (e >= E) break;
+            bool taken = false;
+#pragma unroll
+            for (int r = 0; r < s; ++r) taken |= sel[r] == e;
+            const float le = l[e];
+            if (!taken && (sel[s] < 0 || le > ls[s])) { sel[s] = e; ls[s] = le; }
+        }
+    }
+    float ex[kMaxTopK], sum = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) {
+        ex[s] = page ? ls[s] : s == 0 ? 1.0f : expf(ls[s] - ls[0]);
+        if (s < k) sum += ex[s];
+    }
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) {
+        if (s >= k) break;
+        idx[k * t + s] = sel[s];
+        wout[k * t + s] = ex[s] / sum;
     }
 }
 
@@ -110,7 +192,8 @@ __global__ __launch_bounds__(256) void route_kernel(const T *__restrict__ x,
                                                     int32_t *__restrict__ idx,
                                                     float *__restrict__ wout,
                                                     const T *__restrict__ g, float eps,
-                                                    T *__restrict__ xn_out) {
+                                                    T *__restrict__ xn_out, int page,
+                                                    float *__restrict__ probs) {
     __shared__ float part[4][TPB][EMAX];
     __shared__ float ssq[4][TPB];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -223,60 +306,49 @@ __global__ __launch_bounds__(256) void route_kernel(const T *__restrict__ x,
     if (tid >= TPB) return;
     const int t = t0 + tid;
     if (t >= n_tok) return;
-    // The token's logits, summed over the four wavefronts in a fixed order,
-    // stay in this thread's row of LDS (no other thread touches it).
-    float *l = part[0][tid];
+    // The token's logits, summed over the four wavefronts in a fixed order.
+    // Up to 16 experts they sit in registers and every loop over experts is
+    // unrolled; wider rows stay in this thread's row of LDS (no other
+    // thread touches it) and the loops stay rolled.
+    if constexpr (EMAX <= 16) {
+        float l[EMAX];
+#pragma unroll
+        for (int e = 0; e < EMAX; ++e)
+            l[e] = ((part[0][tid][e] + part[1][tid][e]) + part[2][tid][e]) + part[3][tid][e];
+        finish_token<EMAX, EMAX>(l, E, k, page, probs, t, idx, wout);
+    } else {
+        float *l = part[0][tid];
 #pragma unroll 1
-    for (int e = 0; e < E; ++e)
-        l[e] = ((part[0][tid][e] + part[1][tid][e]) + part[2][tid][e]) + part[3][tid][e];
-    // Top-k, picked greedily: each pick is the largest logit among the
-    // experts not yet picked; strict '>' keeps the lowest index among equal
-    // values.  Weights: softmax over the picked logits relative to the first,
-    // e_0 = 1, e_s = exp(l_s - l_0), w_s = e_s / sum (for k = 2:
-    // w_0 = 1/(1+q), w_1 = q/(1+q)).
-    int sel[kMaxTopK];
-    float ls[kMaxTopK];
-#pragma unroll
-    for (int s = 0; s < kMaxTopK; ++s) {
-        sel[s] = -1;
-        ls[s] = 0.0f;
-        if (s >= k) continue;
-#pragma unroll 1
-        for (int e = 0; e < E; ++e) {
-            bool taken = false;
-#pragma unroll
-            for (int r = 0; r < s; ++r) taken |= sel[r] == e;
-            const float le = l[e];
-            if (!taken && (sel[s] < 0 || le > ls[s])) { sel[s] = e; ls[s] = le; }
-        }
-    }
-    float ex[kMaxTopK], sum = 0.0f;
-#pragma unroll
-    for (int s = 0; s < kMaxTopK; ++s) {
-        ex[s] = s == 0 ? 1.0f : expf(ls[s] - ls[0]);
-        if (s < k) sum += ex[s];
-    }
-#pragma unroll
-    for (int s = 0; s < kMaxTopK; ++s) {
-        if (s >= k) break;
-        idx[k * t + s] = sel[s];
-        wout[k * t + s] = ex[s] / sum;
+        for (int e = 0; e < E; ++e)
+            l[e] = ((part[0][tid][e] + part[1][tid][e]) + part[2][tid][e]) + part[3][tid][e];
+        finish_token<EMAX, 1>(l, E, k, page, probs, t, idx, wout);
     }
 }
 
+// Router options: RMSNorm in front (g, eps, xn) and the page form (page,
+// probs).
+struct RouteOpts {
+    const void *g = nullptr;
+    float eps = 0.0f;
+    void *xn = nullptr;
+    int page = 0;
+    float *probs = nullptr;
+};
+
 template <typename T, int EMAX, int TPB>
 hipError_t launch_route_t(const moe_shape_t &s, const void *x, const void *wg, int32_t *idx,
-                          float *w, const void *g, float eps, void *xn, hipStream_t stream) {
+                          float *w, const RouteOpts &o, hipStream_t stream) {
     const int blocks = (s.T + TPB - 1) / TPB;
-    if (g)
+    if (o.g)
         hipLaunchKernelGGL((route_kernel<T, EMAX, TPB, true>), dim3(blocks), dim3(256), 0,
                            stream, static_cast<const T *>(x), static_cast<const T *>(wg), s.T,
-                           s.d_model, s.n_experts, s.top_k, idx, w, static_cast<const T *>(g),
-                           eps, static_cast<T *>(xn));
+                           s.d_model, s.n_experts, s.top_k, idx, w, static_cast<const T *>(o.g),
+                           o.eps, static_cast<T *>(o.xn), o.page, o.probs);
     else
         hipLaunchKernelGGL((route_kernel<T, EMAX, TPB, false>), dim3(blocks), dim3(256), 0,
                            stream, static_cast<const T *>(x), static_cast<const T *>(wg), s.T,
-                           s.d_model, s.n_experts, s.top_k, idx, w, nullptr, 0.0f, nullptr);
+                           s.d_model, s.n_experts, s.top_k, idx, w, nullptr, 0.0f, nullptr,
+                           o.page, o.probs);
     return hipGetLastError();
 }
 
@@ -285,20 +357,19 @@ hipError_t launch_route_t(const moe_shape_t &s, const void *x, const void *wg, i
 // row read for all of them.
 template <typename T>
 hipError_t launch_route_dtype(const moe_shape_t &s, const void *x, const void *wg,
-                              int32_t *idx, float *w, const void *g, float eps, void *xn,
-                              hipStream_t stream) {
+                              int32_t *idx, float *w, const RouteOpts &o, hipStream_t stream) {
     const bool few = s.T <= 256;
     if (s.n_experts <= 8)
-        return few ? launch_route_t<T, 8, 1>(s, x, wg, idx, w, g, eps, xn, stream)
-                   : launch_route_t<T, 8, 8>(s, x, wg, idx, w, g, eps, xn, stream);
+        return few ? launch_route_t<T, 8, 1>(s, x, wg, idx, w, o, stream)
+                   : launch_route_t<T, 8, 8>(s, x, wg, idx, w, o, stream);
     if (s.n_experts <= 16)
-        return few ? launch_route_t<T, 16, 1>(s, x, wg, idx, w, g, eps, xn, stream)
-                   : launch_route_t<T, 16, 4>(s, x, wg, idx, w, g, eps, xn, stream);
+        return few ? launch_route_t<T, 16, 1>(s, x, wg, idx, w, o, stream)
+                   : launch_route_t<T, 16, 4>(s, x, wg, idx, w, o, stream);
     if (s.n_experts <= 32)
-        return few ? launch_route_t<T, 32, 1>(s, x, wg, idx, w, g, eps, xn, stream)
-                   : launch_route_t<T, 32, 2>(s, x, wg, idx, w, g, eps, xn, stream);
+        return few ? launch_route_t<T, 32, 1>(s, x, wg, idx, w, o, stream)
+                   : launch_route_t<T, 32, 2>(s, x, wg, idx, w, o, stream);
     // 64 logits per token already fill the reduce-scatter's 64 lanes
-    return launch_route_t<T, 64, 1>(s, x, wg, idx, w, g, eps, xn, stream);
+    return launch_route_t<T, 64, 1>(s, x, wg, idx, w, o, stream);
 }
 
 }  // namespace
@@ -308,13 +379,31 @@ hipError_t launch_route(const moe_shape_t &s, const void *x, const void *w_gate,
     return launch_route_norm(s, x, nullptr, 0.0f, w_gate, nullptr, idx, w, stream);
 }
 
+namespace {
+hipError_t launch_route_opts(const moe_shape_t &s, const void *x, const void *w_gate,
+                             int32_t *idx, float *w, const RouteOpts &o, hipStream_t stream) {
+    if (s.T == 0) return hipSuccess;
+    if (s.dtype == MOE_BF16) return launch_route_dtype<uint16_t>(s, x, w_gate, idx, w, o, stream);
+    return launch_route_dtype<float>(s, x, w_gate, idx, w, o, stream);
+}
+}  // namespace
+
 hipError_t launch_route_norm(const moe_shape_t &s, const void *x, const void *g, float eps,
                              const void *w_gate, void *xn, int32_t *idx, float *w,
                              hipStream_t stream) {
-    if (s.T == 0) return hipSuccess;
-    if (s.dtype == MOE_BF16)
-        return launch_route_dtype<uint16_t>(s, x, w_gate, idx, w, g, eps, xn, stream);
-    return launch_route_dtype<float>(s, x, w_gate, idx, w, g, eps, xn, stream);
+    RouteOpts o;
+    o.g = g;
+    o.eps = eps;
+    o.xn = xn;
+    return launch_route_opts(s, x, w_gate, idx, w, o, stream);
+}
+
+hipError_t launch_route_probs(const moe_shape_t &s, const void *x, const void *w_gate,
+                              float *probs, int32_t *idx, float *w, hipStream_t stream) {
+    RouteOpts o;
+    o.page = 1;
+    o.probs = probs;
+    return launch_route_opts(s, x, w_gate, idx, w, o, stream);
 }
 
 }  // namespace moe

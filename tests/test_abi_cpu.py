@@ -100,6 +100,19 @@ def test_null_alignment_alias_workspace_checks():
     assert moe.STATUS_NAMES[st] == "MOE_ERR_ALIGN"
     st = lib.moe_dispatch(ctypes.byref(s), P16, P16, P16, P16, P16, P16, None)
     assert moe.STATUS_NAMES[st] == "MOE_ERR_ALIAS"
+    # page-form router: null, alignment and every output-overlap case
+    rp = lambda x, g, p, i, w: moe.STATUS_NAMES[lib.moe_route_probs(ctypes.byref(s), x, g, p,
+                                                                     i, w, None)]
+    A, B, C, D, G = (ctypes.c_void_p(0x10000000 * n) for n in (1, 2, 3, 4, 5))
+    assert rp(A, G, None, C, None) == "MOE_ERR_NULL"
+    assert rp(None, G, B, C, D) == "MOE_ERR_NULL"
+    assert rp(A, G, P17, C, D) == "MOE_ERR_ALIGN"
+    assert rp(A, G, B, C, P17) == "MOE_ERR_ALIGN"
+    assert rp(A, G, A, C, D) == "MOE_ERR_ALIAS"       # probs over x
+    assert rp(A, G, B, G, D) == "MOE_ERR_ALIAS"       # idx over w_gate
+    assert rp(A, G, B, B, D) == "MOE_ERR_ALIAS"       # idx over probs
+    assert rp(A, G, None, C, C) == "MOE_ERR_ALIAS"    # w over idx
+    assert rp(A, G, B, C, ctypes.c_void_p(0x30000000 + 64 * 2 * 4 - 16)) == "MOE_ERR_ALIAS"
     st = lib.moe_combine(ctypes.byref(s), P16, P16, P16, None, None)
     assert moe.STATUS_NAMES[st] == "MOE_ERR_NULL"
     st = lib.moe_experts(ctypes.byref(s), P16, P16, P16, P16, P16, P16, P16B, P16, 16, None)

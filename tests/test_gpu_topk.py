@@ -78,6 +78,9 @@ CASES = [
     sw(40, 128, 256, E=4, top_k=4, seed=118),
     sw(300, 128, 256, E=3, dtype=W.F32, top_k=3, seed=119),
     sw(20, 128, 256, E=2, top_k=1, seed=120),
+    # expert counts whose router rows are not a multiple of 16 bytes
+    sw(70, 128, 256, E=33, top_k=4, seed=121),
+    sw(500, 128, 256, E=20, top_k=2, seed=122),
 ]
 
 
@@ -235,3 +238,39 @@ def test_binding_checks_k_against_shapes():
         moe.experts(xp, counts, offsets, g.w1, g.w3, g.w2, top_k=4)
     with pytest.raises(moe.MoeArgumentError):
         moe.route(g.x, g.w_gate, top_k=5)
+
+
+PROBS_CASES = [
+    sw(40, 128, 256, seed=190),
+    sw(300, 256, 512, top_k=4, seed=191),
+    sw(100, 128, 256, E=64, top_k=3, seed=192),
+    sw(600, 128, 256, E=12, dtype=W.F32, top_k=1, seed=193),
+    sw(70, 128, 256, E=33, top_k=4, seed=194),
+    sw(500, 128, 256, E=20, top_k=2, seed=195),
+    sw(500, 128, 256, E=20, dtype=W.F32, top_k=3, seed=196),
+    sw(30, 64, 128, E=4, top_k=4, seed=197),
+]
+
+
+@pytest.mark.parametrize("wl", PROBS_CASES, ids=lambda w: w.name)
+def test_route_probs_page_form(wl):
+    """The page's order of steps (softmax over all experts, top-k of the
+    probabilities, renormalised) against the oracle's; the picks also equal
+    the default router's and the weights agree with it to fp32 rounding."""
+    announce(f"route_probs {wl.name}")
+    k = wl.top_k
+    inp = checked_inputs(wl)
+    g = inp.to(DEV)
+    probs, idx, w = moe.route_probs(g.x, g.w_gate, top_k=k)
+    torch.cuda.synchronize()
+    p_o, idx_o, w_o = oracle.route_probs(inp.x, inp.w_gate, top_k=k)
+    np.testing.assert_array_equal(idx.cpu().numpy(), idx_o)
+    np.testing.assert_allclose(w.cpu().numpy(), w_o, rtol=0, atol=RW_TOL[wl.dtype])
+    np.testing.assert_allclose(probs.cpu().numpy(), p_o, rtol=0, atol=RW_TOL[wl.dtype])
+    err = float(np.abs(probs.cpu().numpy() - p_o).max())
+    announce(f"  probs max abs err {err:.3e}")
+    idx_d, w_d = moe.route(g.x, g.w_gate, top_k=k)
+    assert torch.equal(idx_d, idx)
+    assert float((w_d - w).abs().max()) <= 2e-6
+    _, idx2, w2 = moe.route_probs(g.x, g.w_gate, top_k=k, return_probs=False)
+    assert torch.equal(idx2, idx) and torch.equal(w2, w)
