@@ -22,6 +22,8 @@ section 05 (MOE ROUTER + MOE), and section 04 (SWIGLU):
                    and ``expert_down`` (h W2)
 * ``combine``      y[t] = w[t,0] o[t,0] + w[t,1] o[t,1] (formula of section 05)
 * ``forward``      the whole layer, token by token
+* ``quantize_int8``, ``forward_w8``  weight-only int8 expert weights (one
+                   scale per output channel) and the layer on them
 
 Parity status: every function is pinned by tests/test_oracle.py against
 closed forms, brute force, library routines (numpy fp64) and invariants.
@@ -71,6 +73,10 @@ def _bind(path: str):
     lib.oracle_expert_down.restype = I
     lib.oracle_route_probs.argtypes = [I, I, I, I, P, P, I, P, P, P, I]
     lib.oracle_route_probs.restype = I
+    lib.oracle_quantize_int8.argtypes = [I, I, I, P, I, P, P, I]
+    lib.oracle_quantize_int8.restype = I
+    lib.oracle_forward_w8.argtypes = [I, I, I, I, I, P, P, I, P, P, P, P, P, P, P, P, P, I]
+    lib.oracle_forward_w8.restype = I
     lib.oracle_rmsnorm.argtypes = [I, I, P, P, ctypes.c_double, I, P, P, I]
     lib.oracle_rmsnorm.restype = I
     return lib
@@ -368,3 +374,48 @@ def near_tie_tokens(x, w_gate, gap: float = NEAR_TIE_GAP, threads: Optional[int]
     for s in range(min(top_k, logits.shape[1] - 1)):
         bad |= (srt[:, s] - srt[:, s + 1] < gap)
     return torch.from_numpy(bad)
+
+
+# ---------------------------------------------------------------------------
+# Weight-only int8 expert weights (one fp32 scale per output channel).
+
+def quantize_int8(w, threads: Optional[int] = None):
+    """W [E, K, N] (fp32 or bf16) -> (q int8 [E, K, N], scale float32 [E, N]):
+    s[n] = max_j |W[j,n]| / 127 and q = rint(W / s) clamped to [-127, 127],
+    both in fp32; a zero column gets s = 0 and q = 0."""
+    wa, dw = _as_host(w)
+    E, K, N = wa.shape
+    q = np.zeros((E, K, N), np.int8)
+    scale = np.zeros((E, N), np.float32)
+    rc = _load().oracle_quantize_int8(E, K, N, _ptr(wa), dw, _ptr(q), _ptr(scale),
+                                      threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_quantize_int8 rejected its sizes")
+    return q, scale
+
+
+def forward_w8(x, w_gate, q1, s1, q3, s3, q2, s2, top_k: int = 2,
+               threads: Optional[int] = None):
+    """The layer with int8 expert weights W~ = s * q (router and x in their
+    own dtype): returns y float64 [T,d], idx int32 [T,k], w float64 [T,k]."""
+    xa, dx = _as_host(x)
+    ga, dg = _as_host(w_gate)
+    dt = _same_dtype(dx, dg)
+    T, d = xa.shape
+    E = ga.shape[1]
+    f = q1.shape[2]
+    arrs = [np.ascontiguousarray(a) for a in (q1, s1, q3, s3, q2, s2)]
+    for a, dtype, shape in zip(arrs, (np.int8, np.float32) * 3,
+                               ((E, d, f), (E, f), (E, d, f), (E, f), (E, f, d), (E, d))):
+        if a.dtype != dtype or a.shape != shape:
+            raise ValueError(f"int8 weights: expected {dtype.__name__} {shape}, got "
+                             f"{a.dtype} {a.shape}")
+    y = np.zeros((T, d), np.float64)
+    idx = np.zeros((T, top_k), np.int32)
+    w = np.zeros((T, top_k), np.float64)
+    rc = _load().oracle_forward_w8(T, d, f, E, top_k, _ptr(xa), _ptr(ga), dt,
+                                   *[_ptr(a) for a in arrs], _ptr(y), _ptr(idx), _ptr(w),
+                                   threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_forward_w8 rejected its sizes")
+    return y, idx, w

@@ -401,6 +401,156 @@ int oracle_forward(int T, int d, int f, int E, int k, const void *x, const void 
 }
 
 /* ------------------------------------------------------------------------
+ * Weight-only int8 expert weights.
+ *
+ * The pages name weight-only int8 loading for this model (the KerasFormers
+ * Mixtral page's quantization option; the Hugging Face page's low-memory
+ * loading) but give no scheme.  The plainest one is used: symmetric, one
+ * scale per output channel of each expert matrix.  For a matrix W [K, N]
+ * (K = input, N = output channel) and each column n:
+ *
+ *   a[n]    = max_j |W[j,n]|
+ *   s[n]    = a[n] / 127            (fp32 division; s = 0 for a zero column)
+ *   q[j,n]  = rint(W[j,n] / s[n])   (fp32 division, round half to even,
+ *                                    clamped to [-127, 127]; q = 0 when s = 0)
+ *
+ * The division and the rounding are the decision that produces an integer,
+ * so they are taken in fp32, the precision the GPU library takes them in.
+ * The layer then uses W~[j,n] = s[n] * q[j,n] in place of W: with the scale
+ * taken out of each sum, g[n] = s1[n] * sum_j x[j] q1[j,n] and likewise for
+ * u and the down projection, all in fp64.  */
+
+static void quantize_column(int K, int N, const void *w, int dtype, size_t base, int n,
+                            int8_t *q, float *scale) {
+    float a = 0.0f;
+    for (int j = 0; j < K; ++j) {
+        const float v = fabsf((float)load_elem(w, dtype, base + (size_t)j * N + n));
+        if (v > a) a = v;
+    }
+    const float sc = a / 127.0f;
+    *scale = sc;
+    for (int j = 0; j < K; ++j) {
+        int8_t code = 0;
+        if (sc > 0.0f) {
+            float r = rintf((float)load_elem(w, dtype, base + (size_t)j * N + n) / sc);
+            if (r > 127.0f) r = 127.0f;
+            if (r < -127.0f) r = -127.0f;
+            code = (int8_t)r;
+        }
+        q[base + (size_t)j * N + n] = code;
+    }
+}
+
+typedef struct {
+    int K, N, dtype;
+    const void *w;
+    int8_t *q;
+    float *scale;
+} quant_ctx;
+
+static void quantize_range(void *p, int lo, int hi) {
+    quant_ctx *c = (quant_ctx *)p;
+    for (int col = lo; col < hi; ++col) {        /* col = e * N + n */
+        const int e = col / c->N, n = col % c->N;
+        quantize_column(c->K, c->N, c->w, c->dtype, (size_t)e * c->K * c->N, n, c->q,
+                        c->scale + col);
+    }
+}
+
+/* E matrices W [E, K, N] -> q int8 [E, K, N], scale fp32 [E, N]. */
+int oracle_quantize_int8(int E, int K, int N, const void *w, int dtype, int8_t *q,
+                         float *scale, int threads) {
+    if (E < 1 || K < 1 || N < 1) return -1;
+    quant_ctx c = {K, N, dtype, w, q, scale};
+    parallel_for(E * N, threads, quantize_range, &c);
+    return 0;
+}
+
+typedef struct {
+    int T, d, f, E, k, dtype;
+    const void *x, *wg;
+    const int8_t *q1, *q3, *q2;
+    const float *s1, *s3, *s2;
+    int32_t *idx;
+    double *w, *y;
+} w8_ctx;
+
+/* a = silu(x W~1[e]) * (x W~3[e]) into g[f]; u is scratch [f]. */
+static void w8_hidden(const w8_ctx *c, const double *xr, int e, double *g, double *u) {
+    const int d = c->d, f = c->f;
+    const size_t base = (size_t)e * d * f;
+    for (int n = 0; n < f; ++n) { g[n] = 0.0; u[n] = 0.0; }
+    for (int j = 0; j < d; ++j) {
+        const double xj = xr[j];
+        const size_t row = base + (size_t)j * f;
+        for (int n = 0; n < f; ++n) {
+            g[n] += xj * (double)c->q1[row + n];
+            u[n] += xj * (double)c->q3[row + n];
+        }
+    }
+    for (int n = 0; n < f; ++n) {
+        const double gn = (double)c->s1[(size_t)e * f + n] * g[n];
+        const double un = (double)c->s3[(size_t)e * f + n] * u[n];
+        g[n] = gn / (1.0 + exp(-gn)) * un;
+    }
+}
+
+/* o[d] = a[f] W~2[e]. */
+static void w8_down(const w8_ctx *c, const double *a, int e, double *o) {
+    const int d = c->d, f = c->f;
+    const size_t base = (size_t)e * f * d;
+    for (int m = 0; m < d; ++m) o[m] = 0.0;
+    for (int n = 0; n < f; ++n) {
+        const double an = a[n];
+        const size_t row = base + (size_t)n * d;
+        for (int m = 0; m < d; ++m) o[m] += an * (double)c->q2[row + m];
+    }
+    for (int m = 0; m < d; ++m) o[m] *= (double)c->s2[(size_t)e * d + m];
+}
+
+static void w8_forward_range(void *p, int lo, int hi) {
+    w8_ctx *c = (w8_ctx *)p;
+    double l[256];
+    double *xr = malloc(sizeof(double) * c->d);
+    double *os = malloc(sizeof(double) * c->d * ORC_MAX_K);
+    double *g = malloc(sizeof(double) * c->f);
+    double *u = malloc(sizeof(double) * c->f);
+    if (!xr || !os || !g || !u) goto out;
+    for (int t = lo; t < hi; ++t) {
+        const size_t xo = (size_t)t * c->d;
+        int32_t *it = c->idx + (size_t)c->k * t;
+        double *wt = c->w + (size_t)c->k * t;
+        router_logits(c->d, c->E, c->x, xo, c->wg, c->dtype, l);
+        topk_softmax(c->E, c->k, l, it, wt);
+        for (int j = 0; j < c->d; ++j) xr[j] = load_elem(c->x, c->dtype, xo + j);
+        for (int s = 0; s < c->k; ++s) {
+            w8_hidden(c, xr, it[s], g, u);
+            w8_down(c, g, it[s], os + (size_t)s * c->d);
+        }
+        for (int m = 0; m < c->d; ++m) {                     /* slot order */
+            double acc = 0.0;
+            for (int s = 0; s < c->k; ++s) acc += os[(size_t)s * c->d + m] * wt[s];
+            c->y[xo + m] = acc;
+        }
+    }
+out:
+    free(xr); free(os); free(g); free(u);
+}
+
+/* The layer with int8 expert weights (router and x in `dtype`): y [T,d]
+ * fp64, idx [T,k], w [T,k]. */
+int oracle_forward_w8(int T, int d, int f, int E, int k, const void *x, const void *wg,
+                      int dtype, const int8_t *q1, const float *s1, const int8_t *q3,
+                      const float *s3, const int8_t *q2, const float *s2, double *y,
+                      int32_t *idx, double *w, int threads) {
+    if (T < 0 || d < 1 || f < 1 || E < 1 || E > 256 || k < 1 || k > ORC_MAX_K || k > E)
+        return -1;
+    w8_ctx c = {T, d, f, E, k, dtype, x, wg, q1, q3, q2, s1, s3, s2, idx, w, y};
+    parallel_for(T, threads, w8_forward_range, &c);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------
  * Block boundary: RMSNorm before the layer.  */
 
 /* v rounded to the nearest bf16 value (8 significant bits), ties to even,

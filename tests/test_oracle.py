@@ -424,6 +424,71 @@ def pin_route_probs_page_form():
         np.testing.assert_allclose(w_s, w, rtol=1e-9)
 
 
+def pin_quantize_int8():
+    """Per-output-channel symmetric int8: s = max|W| / 127, q = rint(W / s),
+    in fp32.  Hand-derived codes (63.5 and 31.75 rounding), round half to
+    even on exact halves, a zero column (s = 0, q = 0), the bound
+    |W - s q| <= s/2 with +-127 at each column's largest entry, and exact
+    recovery of W = 2^-7 * integers whose column maxima are 127."""
+    w = np.array([[[1.0, 0.0, -3.0], [0.5, 0.0, 3.0], [-2.0, 0.0, 1.5]]], np.float32)
+    q, sc = oracle.quantize_int8(w)
+    np.testing.assert_array_equal(q[0], [[64, 0, -127], [32, 0, 127], [-127, 0, 64]])
+    np.testing.assert_array_equal(sc[0], np.array([2, 0, 3], np.float32) / np.float32(127))
+    # a = 127 gives s = 1 exactly; halves round to even
+    col = np.array([127.0, 0.5, 1.5, 2.5, -0.5, -2.5, 3.5, -126.5], np.float32)
+    q, sc = oracle.quantize_int8(col.reshape(1, 8, 1))
+    assert sc[0, 0] == 1.0
+    np.testing.assert_array_equal(q[0, :, 0], [127, 0, 2, 2, 0, -2, 4, -126])
+    rng = np.random.default_rng(44)
+    w = (rng.standard_normal((3, 40, 24)) * rng.uniform(0.01, 3, (3, 1, 24))).astype(np.float32)
+    for conv in (lambda a: a, lambda a: torch.from_numpy(a).to(torch.bfloat16)):
+        wi = conv(w)
+        wf = wi.float().numpy() if isinstance(wi, torch.Tensor) else wi
+        q, sc = oracle.quantize_int8(wi)
+        amax = np.abs(wf).max(axis=1)
+        np.testing.assert_array_equal(sc, (amax / np.float32(127)).astype(np.float32))
+        err = np.abs(wf.astype(np.float64) - sc[:, None, :].astype(np.float64) * q)
+        assert np.all(err <= sc[:, None, :] * (0.5 + 1e-6))
+        top = np.take_along_axis(q, np.abs(wf).argmax(axis=1)[:, None, :], axis=1)
+        np.testing.assert_array_equal(np.abs(top), 127)
+        assert np.all(np.sign(q) == np.sign(np.round(wf / sc[:, None, :])))
+    ints = rng.integers(-127, 128, (2, 16, 10)).astype(np.float32)
+    ints[:, 3, :] = 127.0
+    q, sc = oracle.quantize_int8(ints * np.float32(2.0 ** -7))
+    np.testing.assert_array_equal(q, ints)
+    np.testing.assert_array_equal(sc, np.float32(2.0 ** -7))
+
+
+def pin_forward_w8_power_of_two_scales():
+    """With power-of-two scales, s * q is exact in fp32, and scaling by a
+    power of two is exact in fp64.  So the int8 layer equals the plain
+    layer on W = s * q, bit for bit.  Every column gets its own scale,
+    different for w1, w3 and w2.  Quantising that W again gives back q when
+    each column reaches 127."""
+    rng = np.random.default_rng(45)
+    T, d, f, E = 12, 16, 24, 4
+    x = torch.tensor(rng.standard_normal((T, d)), dtype=torch.float32)
+    wg = torch.tensor(rng.standard_normal((d, E)) * 0.5, dtype=torch.float32)
+    def mat(K, N):
+        qi = rng.integers(-127, 128, (E, K, N)).astype(np.int8)
+        qi[:, 0, :] = 127
+        sc = (2.0 ** rng.integers(-9, -4, (E, N))).astype(np.float32)
+        return qi, sc, torch.from_numpy(qi.astype(np.float32) * sc[:, None, :])
+    q1, s1, w1 = mat(d, f)
+    q3, s3, w3 = mat(d, f)
+    q2, s2, w2 = mat(f, d)
+    for k in (1, 2, 3):
+        y8, idx8, w8 = oracle.forward_w8(x, wg, q1, s1, q3, s3, q2, s2, top_k=k)
+        y, idx, w = oracle.forward(x, wg, w1, w3, w2, top_k=k)
+        np.testing.assert_array_equal(idx8, idx)
+        np.testing.assert_array_equal(w8, w)
+        np.testing.assert_array_equal(y8, y)
+    for qq, ss, ww in ((q1, s1, w1), (q2, s2, w2)):
+        qb, sb = oracle.quantize_int8(ww)
+        np.testing.assert_array_equal(qb, qq)
+        np.testing.assert_array_equal(sb, ss)
+
+
 PINS = [pin_worked_examples, pin_logits_match_numpy, pin_top2_brute_force,
         pin_weights_closed_form_and_page_form, pin_forward_matches_numpy_dense,
         pin_expert_rows_match_numpy, pin_identical_experts_equal_dense_swiglu,
@@ -431,7 +496,7 @@ PINS = [pin_worked_examples, pin_logits_match_numpy, pin_top2_brute_force,
         pin_expert_relabelling_and_token_permutation, pin_dispatch_is_stable_grouping,
         pin_rmsnorm_closed_forms, pin_rmsnorm_invariants, pin_block_identities,
         pin_topk_brute_force_and_special_weights, pin_topk_layer_special_cases,
-        pin_route_probs_page_form]
+        pin_route_probs_page_form, pin_quantize_int8, pin_forward_w8_power_of_two_scales]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -482,6 +547,12 @@ MUTANTS = {
     "probs_ties_to_higher_index": ("(pick < 0 || (float)p[e] > (float)p[pick])",
                                    "(pick < 0 || (float)p[e] >= (float)p[pick])"),
     "probs_without_max_shift": ("p[e] = exp(l[e] - m);", "p[e] = exp(l[e]);"),
+    "quant_round_half_away": ("float r = rintf(", "float r = roundf("),
+    "quant_scale_over_255": ("const float sc = a / 127.0f;", "const float sc = a / 255.0f;"),
+    "w8_down_scale_dropped": ("for (int m = 0; m < d; ++m) o[m] *= (double)c->s2[(size_t)e * d + m];",
+                              "for (int m = 0; m < d; ++m) o[m] *= 1.0;"),
+    "w8_gate_takes_up_scale": ("const double gn = (double)c->s1[(size_t)e * f + n] * g[n];",
+                               "const double gn = (double)c->s3[(size_t)e * f + n] * g[n];"),
     "norm_sum_not_mean": ("sqrt(ss / (double)c->d + c->eps)", "sqrt(ss + c->eps)"),
     "norm_no_sqrt": ("sqrt(ss / (double)c->d + c->eps)", "(ss / (double)c->d + c->eps)"),
     "norm_eps_outside": ("1.0 / sqrt(ss / (double)c->d + c->eps)",
