@@ -23,6 +23,11 @@ on the decode tokens for a bounded time.
 fused into the router, residual add into the combine), with the time the
 fused steps add over the plain layer.
 
+``w8``: the decode workload with weight-only int8 expert weights (one
+fp32 scale per output column, quantized once before timing): step time,
+the layer's bytes (codes and scales of the experts that received tokens,
+x, y, router) over HBM peak, and the int8 gate/up kernel alone.
+
 ``top_k``: the same workloads routed to 1 and to 4 experts per token
 (Mixtral uses 2), each with its layer roofline: bytes of the experts that
 received tokens for the decode step, 2 k T (3 d f) + 2 T d E FLOPs for the
@@ -62,6 +67,8 @@ def parse():
                     help="skip the block-boundary (RMSNorm + residual) measurement")
     ap.add_argument("--no-topk", dest="topk", action="store_false",
                     help="skip the top-1 / top-4 measurement")
+    ap.add_argument("--no-w8", dest="w8", action="store_false",
+                    help="skip the int8-weight decode measurement")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this size (for counter scaling)")
     return ap.parse_args()
@@ -225,6 +232,63 @@ def measure_topk(wl_name, k, steps, warmup):
             "layer_roofline": roof, "expert_counts": c}
 
 
+def measure_w8(wl_name, steps, warmup):
+    """The decode layer on int8 expert weights (moe_forward_w8)."""
+    import torch
+    import sparse_mixture_experts_top2_amd as moe
+    from sparse_mixture_experts_top2_amd import workloads as W
+
+    wl = W.WORKLOADS[wl_name]
+    dev = torch.device("cuda:0")
+    inp = W.make_inputs(wl, device="cuda")
+    q1, s1 = moe.quantize_int8(inp.w1)
+    q3, s3 = moe.quantize_int8(inp.w3)
+    q2, s2 = moe.quantize_int8(inp.w2)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ws = moe.alloc_workspace(wl.T, wl.d, wl.f, wl.E, inp.x.dtype, dev)
+    y = torch.empty_like(inp.x)
+
+    def step():
+        moe.forward_w8(inp.x, inp.w_gate, q1, s1, q3, s3, q2, s2, workspace=ws, out=y)
+
+    for _ in range(warmup):
+        step()
+    ms = time_region(step, steps, stream)
+    idx, _ = moe.route(inp.x, inp.w_gate)
+    counts, offsets, pos, xp = moe.dispatch(inp.x, idx, wl.E)
+    h = torch.empty(2 * wl.T, wl.f, dtype=inp.x.dtype, device=dev)
+
+    def gateup():
+        moe.expert_gateup_w8(xp, counts, offsets, q1, s1, q3, s3, out=h)
+
+    for _ in range(max(2, warmup)):
+        gateup()
+    k_ms = time_region(gateup, steps, stream)
+    c = counts.cpu().tolist()
+    active = sum(1 for v in c if v > 0)
+    gu_bytes = (active * (2 * wl.d * wl.f + 2 * wl.f * 4) + 2 * wl.T * wl.d * 2 +
+                2 * wl.T * wl.f * 2)
+    layer_bytes = (active * (3 * wl.d * wl.f + (2 * wl.f + wl.d) * 4) + 2 * wl.T * wl.d * 2 +
+                   wl.d * wl.E * 2)
+    ach = gu_bytes / (k_ms * 1e-3) / 1e9
+    lay = layer_bytes / (ms * 1e-3) / 1e9
+    log(f"{wl_name} int8 weights: {ms:.4f} ms/step ({wl.T / ms * 1e3:.0f} tokens/s); "
+        f"gate/up {k_ms:.4f} ms ({ach:.0f} GB/s); layer {lay:.0f} GB/s")
+    return {"workload": wl_name, "weights": "int8, one fp32 scale per output column",
+            "value": round(wl.T / (ms * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_step": round(ms, 5), "steps": steps, "warmup": warmup,
+            "roofline": {"kernel": "expert gate/up on int8 codes (weight-streaming MFMA)",
+                         "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                         "algorithmic_bytes_per_launch": gu_bytes,
+                         "avg_launch_ms": round(k_ms, 5)},
+            "layer_roofline": {"bound": "hbm", "achieved": round(lay, 1), "peak": PEAK_HBM_GBS,
+                               "unit": "GB/s", "frac": round(lay / PEAK_HBM_GBS, 4),
+                               "algorithmic_bytes_per_step": layer_bytes},
+            "expert_counts": c}
+
+
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_gateup_8x7b.md")
 
 
@@ -315,6 +379,10 @@ def main():
     blocks = []
     if args.block:
         blocks.append(measure_block(args.workload, steps, warmup, main_res["ms"]))
+    w8 = None
+    if args.w8 and main_res["wl"].T <= 32 and main_res["wl"].dtype == "bf16":
+        w8 = measure_w8(args.workload, steps, warmup)
+        torch.cuda.empty_cache()
     topk = []
     if args.topk:
         for k in (1, 4):
@@ -363,6 +431,7 @@ def main():
         "secondary": sec,
         "block_boundary": blocks or None,
         "top_k": topk or None,
+        "w8": w8,
     }
     print(json.dumps(out), flush=True)
 

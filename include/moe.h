@@ -67,7 +67,8 @@ typedef enum {
     MOE_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                  */
     MOE_ERR_ALIAS = 5,       /* an output overlaps an input                       */
     MOE_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than moe_workspace_bytes */
-    MOE_ERR_UNSUPPORTED = 7, /* E outside [2, 64], or top_k outside [1, min(4, E)] */
+    MOE_ERR_UNSUPPORTED = 7, /* E outside [2, 64], top_k outside [1, min(4, E)],
+                                 or an int8-weight call off bf16 / T <= 32          */
     MOE_ERR_HIP = 8          /* a HIP launch failed                               */
 } moe_status_t;
 
@@ -201,6 +202,56 @@ int moe_block_forward(const moe_shape_t *shape, const void *h, const void *rms_w
                       float eps, const void *residual, const void *w_gate, const void *w1,
                       const void *w3, const void *w2, void *out, int32_t *topk_idx_opt,
                       float *topk_w_opt, void *ws, size_t ws_bytes, void *stream);
+
+/* ---- Weight-only int8 expert weights (decode) ----------------------------
+ * The KerasFormers Mixtral page offers int8 weight quantization for this
+ * model, and the Hugging Face page offers low-memory loading. Neither gives
+ * a scheme. These calls use symmetric int8 with one fp32 scale per output
+ * channel of each expert matrix: W[j,n] ~ s[n] q[j,n]. Decode streams the
+ * selected experts' weights, so the codes halve the bytes of the step.
+ * Activations, router and outputs keep the layer dtype, which must be
+ * MOE_BF16. The layer calls take T <= 32 (decode sizes); other shapes
+ * return MOE_ERR_UNSUPPORTED. Codes become bf16 exactly, and each product
+ * accumulates in fp32 on the bf16 matrix cores. The scale multiplies the
+ * finished sum of each output column.
+ *
+ * Codes have the weights' layout: q1, q3 int8 [E, d, f] and q2 int8
+ * [E, f, d]. Scales are s1, s3 fp32 [E, f] and s2 fp32 [E, d]. */
+
+/* Quantize n_mat matrices W [n_mat, K, N] (dtype MOE_F32 or MOE_BF16)
+ * into codes q int8 [n_mat, K, N] and scales fp32 [n_mat, N]. Per column
+ * n of each matrix:
+ *   s[n]   = max_j |W[j,n]| / 127                       (fp32 division)
+ *   q[j,n] = rint(W[j,n] / s[n]) clamped to [-127, 127] (fp32 division,
+ *            round half to even)
+ * A zero column gets s = 0 and q = 0. N must be a positive multiple of 8
+ * and n_mat at most 65535. Outputs must not overlap W or each other. The
+ * call is a one-time preparation and runs on `stream` like every other
+ * call. */
+int moe_quantize_int8(int n_mat, int K, int N, int dtype, const void *w, int8_t *q,
+                      float *scale, void *stream);
+
+/* moe_expert_gateup on int8 codes:
+ *   h[r, :] = silu(s1[e] * (xp[r] q1[e])) * (s3[e] * (xp[r] q3[e])), bf16 [R, f]. */
+int moe_expert_gateup_w8(const moe_shape_t *shape, const void *xp, const int32_t *counts,
+                         const int32_t *offsets, const int8_t *q1, const float *s1,
+                         const int8_t *q3, const float *s3, void *h, void *stream);
+
+/* moe_expert_down on int8 codes:
+ *   o[r, :] = s2[e] * (h[r] q2[e]), fp32 [R, d]. */
+int moe_expert_down_w8(const moe_shape_t *shape, const void *h, const int32_t *counts,
+                       const int32_t *offsets, const int8_t *q2, const float *s2, float *o,
+                       void *stream);
+
+/* The whole layer with int8 expert weights: route and dispatch as in
+ * moe_forward. Gate/up reads its rows straight from x. Down runs in four K
+ * slices, and the combine adds the slices in order before it weights the
+ * slots. y [T, d] bf16. ws / ws_bytes: at least moe_workspace_bytes(shape).
+ * y must not overlap x. */
+int moe_forward_w8(const moe_shape_t *shape, const void *x, const void *w_gate,
+                   const int8_t *q1, const float *s1, const int8_t *q3, const float *s3,
+                   const int8_t *q2, const float *s2, void *y, int32_t *topk_idx_opt,
+                   float *topk_w_opt, void *ws, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

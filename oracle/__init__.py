@@ -77,6 +77,8 @@ def _bind(path: str):
     lib.oracle_quantize_int8.restype = I
     lib.oracle_forward_w8.argtypes = [I, I, I, I, I, P, P, I, P, P, P, P, P, P, P, P, P, I]
     lib.oracle_forward_w8.restype = I
+    lib.oracle_expert_stage_w8.argtypes = [I, I, I, I, I, P, P, I, P, P, P, P, P, P, P, I]
+    lib.oracle_expert_stage_w8.restype = I
     lib.oracle_rmsnorm.argtypes = [I, I, P, P, ctypes.c_double, I, P, P, I]
     lib.oracle_rmsnorm.restype = I
     return lib
@@ -419,3 +421,32 @@ def forward_w8(x, w_gate, q1, s1, q3, s3, q2, s2, top_k: int = 2,
     if rc != 0:
         raise ValueError("oracle_forward_w8 rejected its sizes")
     return y, idx, w
+
+
+def _w8_stage(mode, rows, expert, d, f, E, mats, threads):
+    ra, dr = _as_host(rows)
+    n = ra.shape[0]
+    ex = np.ascontiguousarray(expert, np.int32)
+    z8, z32 = np.zeros(1, np.int8), np.zeros(1, np.float32)
+    arrs = [np.ascontiguousarray(a) if a is not None else z for a, z in
+            zip(mats, (z8, z32) * 3)]
+    out = np.zeros((n, f if mode == 0 else d), np.float64)
+    rc = _load().oracle_expert_stage_w8(mode, n, d, f, E, _ptr(ra), _ptr(ex), dr,
+                                        *[_ptr(a) for a in arrs], _ptr(out),
+                                        threads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_expert_stage_w8 rejected its sizes")
+    return out
+
+
+def expert_hidden_w8(rows, expert: np.ndarray, q1, s1, q3, s3, threads: Optional[int] = None):
+    """silu(s1 * (rows[r] q1[e])) * (s3 * (rows[r] q3[e])), e = expert[r];
+    float64 [n, f]."""
+    E, d, f = q1.shape
+    return _w8_stage(0, rows, expert, d, f, E, (q1, s1, q3, s3, None, None), threads)
+
+
+def expert_down_w8(hid, expert: np.ndarray, q2, s2, threads: Optional[int] = None):
+    """s2 * (hid[r] q2[e]), e = expert[r]; float64 [n, d]."""
+    E, f, d = q2.shape
+    return _w8_stage(1, hid, expert, d, f, E, (None, None, None, None, q2, s2), threads)

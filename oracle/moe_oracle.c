@@ -537,6 +537,48 @@ out:
     free(xr); free(os); free(g); free(u);
 }
 
+typedef struct {
+    const w8_ctx *c;
+    int mode;                  /* 0: hidden a [n,f] from rows [n,d]; 1: down o [n,d] from [n,f] */
+    const void *rows;          /* layer dtype */
+    const int32_t *expert;
+    double *out;
+} w8_stage_ctx;
+
+static void w8_stage_range(void *p, int lo, int hi) {
+    const w8_stage_ctx *sc = (const w8_stage_ctx *)p;
+    const w8_ctx *c = sc->c;
+    const int in_w = sc->mode == 0 ? c->d : c->f;
+    double *xr = malloc(sizeof(double) * in_w);
+    double *u = malloc(sizeof(double) * c->f);
+    if (!xr || !u) { free(xr); free(u); return; }
+    for (int r = lo; r < hi; ++r) {
+        for (int j = 0; j < in_w; ++j)
+            xr[j] = load_elem(sc->rows, c->dtype, (size_t)r * in_w + j);
+        if (sc->mode == 0)
+            w8_hidden(c, xr, sc->expert[r], sc->out + (size_t)r * c->f, u);
+        else
+            w8_down(c, xr, sc->expert[r], sc->out + (size_t)r * c->d);
+    }
+    free(xr); free(u);
+}
+
+/* The int8 gate/up stage alone: out [n,f] = silu(s1 (rows q1[e])) * (s3 (rows q3[e])),
+ * e = expert[r] (mode 0); or the down stage: out [n,d] = s2 (rows q2[e]) (mode 1).
+ * rows are in `dtype`.  Returns 0, or -1 on bad sizes / expert ids. */
+int oracle_expert_stage_w8(int mode, int n, int d, int f, int E, const void *rows,
+                           const int32_t *expert, int dtype, const int8_t *q1, const float *s1,
+                           const int8_t *q3, const float *s3, const int8_t *q2,
+                           const float *s2, double *out, int threads) {
+    if (n < 0 || d < 1 || f < 1 || (mode != 0 && mode != 1)) return -1;
+    for (int r = 0; r < n; ++r)
+        if (expert[r] < 0 || expert[r] >= E) return -1;
+    w8_ctx c = {0, d, f, E, 1, dtype, NULL, NULL, q1, q3, q2, s1, s3, s2, NULL, NULL, NULL};
+    w8_stage_ctx sc = {&c, mode, rows, expert, out};
+    parallel_for(n, threads, w8_stage_range, &sc);
+    return 0;
+}
+
 /* The layer with int8 expert weights (router and x in `dtype`): y [T,d]
  * fp64, idx [T,k], w [T,k]. */
 int oracle_forward_w8(int T, int d, int f, int E, int k, const void *x, const void *wg,

@@ -28,7 +28,8 @@ STATUS_NAMES = ["MOE_OK", "MOE_ERR_NULL", "MOE_ERR_SHAPE", "MOE_ERR_DTYPE", "MOE
 EXPORTED = ["moe_status_str", "moe_workspace_bytes", "moe_route", "moe_route_probs",
             "moe_dispatch",
             "moe_expert_gateup", "moe_expert_down", "moe_experts", "moe_combine",
-            "moe_forward", "moe_rmsnorm_route", "moe_block_forward"]
+            "moe_forward", "moe_rmsnorm_route", "moe_block_forward", "moe_quantize_int8",
+            "moe_expert_gateup_w8", "moe_expert_down_w8", "moe_forward_w8"]
 
 
 class MoeShape(ctypes.Structure):
@@ -83,6 +84,14 @@ def load_library(path: Optional[str] = None):
     lib.moe_rmsnorm_route.restype = I
     lib.moe_block_forward.argtypes = [S, P, P, F, P, P, P, P, P, P, P, P, P, Z, P]
     lib.moe_block_forward.restype = I
+    lib.moe_quantize_int8.argtypes = [I, I, I, I, P, P, P, P]
+    lib.moe_quantize_int8.restype = I
+    lib.moe_expert_gateup_w8.argtypes = [S, P, P, P, P, P, P, P, P, P]
+    lib.moe_expert_gateup_w8.restype = I
+    lib.moe_expert_down_w8.argtypes = [S, P, P, P, P, P, P, P]
+    lib.moe_expert_down_w8.restype = I
+    lib.moe_forward_w8.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
+    lib.moe_forward_w8.restype = I
     if path is None:
         _lib = lib
     return lib
@@ -403,3 +412,101 @@ def block_forward(h: torch.Tensor, rms_weight: torch.Tensor, eps: float, w_gate:
     _check(st, "moe_block_forward")
     return (y, idx, w) if return_routing else y
 
+
+
+# ---------------------------------------------------------------------------
+# Weight-only int8 expert weights (decode sizes: bf16 layers, T <= 32).
+
+def quantize_int8(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """W [n, K, N] (bf16 or fp32) -> (codes int8 [n, K, N], scales fp32
+    [n, N]): one symmetric scale per output column, s = max|W| / 127,
+    q = rint(W / s) clamped to [-127, 127]."""
+    _need(w, "w")
+    if w.dim() != 3:
+        raise ValueError(f"w must be [n, K, N], got {tuple(w.shape)}")
+    n, K, N = w.shape
+    q = torch.empty(n, K, N, dtype=torch.int8, device=w.device)
+    sc = torch.empty(n, N, dtype=torch.float32, device=w.device)
+    st = load_library().moe_quantize_int8(n, K, N, _dtype_code(w.dtype), _ptr(w), _ptr(q),
+                                          _ptr(sc), _stream(w.device))
+    _check(st, "moe_quantize_int8")
+    return q, sc
+
+
+def _need_w8(q, sc, name, device, E, K, N):
+    _need(q, f"q{name}", torch.int8, device, (E, K, N))
+    _need(sc, f"s{name}", torch.float32, device, (E, N))
+
+
+def expert_gateup_w8(xp: torch.Tensor, counts: torch.Tensor, offsets: torch.Tensor,
+                     q1: torch.Tensor, s1: torch.Tensor, q3: torch.Tensor, s3: torch.Tensor,
+                     top_k: int = 2, out: Optional[torch.Tensor] = None):
+    """h = silu(s1 * (xp q1[e])) * (s3 * (xp q3[e])) per expert row group."""
+    _need(xp, "xp", torch.bfloat16)
+    R, d = xp.shape
+    T = _routed_tokens(R, top_k, "xp")
+    E, _, f = q1.shape
+    _need_w8(q1, s1, "1", xp.device, E, d, f)
+    _need_w8(q3, s3, "3", xp.device, E, d, f)
+    _need(counts, "counts", torch.int32, xp.device, (E,))
+    _need(offsets, "offsets", torch.int32, xp.device, (E + 1,))
+    h = out if out is not None else torch.empty(R, f, dtype=torch.bfloat16, device=xp.device)
+    _need(h, "h", torch.bfloat16, xp.device, (R, f))
+    shape = make_shape(T, d, f, E, torch.bfloat16, top_k)
+    st = load_library().moe_expert_gateup_w8(ctypes.byref(shape), _ptr(xp), _ptr(counts),
+                                             _ptr(offsets), _ptr(q1), _ptr(s1), _ptr(q3),
+                                             _ptr(s3), _ptr(h), _stream(xp.device))
+    _check(st, "moe_expert_gateup_w8")
+    return h
+
+
+def expert_down_w8(h: torch.Tensor, counts: torch.Tensor, offsets: torch.Tensor,
+                   q2: torch.Tensor, s2: torch.Tensor, top_k: int = 2,
+                   out: Optional[torch.Tensor] = None):
+    """o = s2 * (h q2[e]) per expert row group; fp32 [kT, d]."""
+    _need(h, "h", torch.bfloat16)
+    R, f = h.shape
+    T = _routed_tokens(R, top_k, "h")
+    E, _, d = q2.shape
+    _need_w8(q2, s2, "2", h.device, E, f, d)
+    _need(counts, "counts", torch.int32, h.device, (E,))
+    _need(offsets, "offsets", torch.int32, h.device, (E + 1,))
+    o = out if out is not None else torch.empty(R, d, dtype=torch.float32, device=h.device)
+    _need(o, "o", torch.float32, h.device, (R, d))
+    shape = make_shape(T, d, f, E, torch.bfloat16, top_k)
+    st = load_library().moe_expert_down_w8(ctypes.byref(shape), _ptr(h), _ptr(counts),
+                                           _ptr(offsets), _ptr(q2), _ptr(s2), _ptr(o),
+                                           _stream(h.device))
+    _check(st, "moe_expert_down_w8")
+    return o
+
+
+def forward_w8(x: torch.Tensor, w_gate: torch.Tensor, q1: torch.Tensor, s1: torch.Tensor,
+               q3: torch.Tensor, s3: torch.Tensor, q2: torch.Tensor, s2: torch.Tensor,
+               workspace: Optional[torch.Tensor] = None, return_routing: bool = False,
+               out: Optional[torch.Tensor] = None, top_k: int = 2):
+    """The layer with int8 expert weights (bf16 x, T <= 32).  Returns y
+    [T, d] (and (topk_idx, topk_w) when ``return_routing``)."""
+    _need(x, "x", torch.bfloat16)
+    T, d = x.shape
+    _need(w_gate, "w_gate", x.dtype, x.device)
+    E = w_gate.shape[1]
+    _need(w_gate, "w_gate", shape=(d, E))
+    f = q1.shape[2]
+    _need_w8(q1, s1, "1", x.device, E, d, f)
+    _need_w8(q3, s3, "3", x.device, E, d, f)
+    _need_w8(q2, s2, "2", x.device, E, f, d)
+    ws = workspace if workspace is not None else alloc_workspace(T, d, f, E, x.dtype, x.device,
+                                                                 top_k)
+    y = out if out is not None else torch.empty(T, d, dtype=x.dtype, device=x.device)
+    _need(y, "out", x.dtype, x.device, (T, d))
+    idx = w = None
+    if return_routing:
+        idx, w = _routing_out(T, top_k, x.device)
+    shape = make_shape(T, d, f, E, x.dtype, top_k)
+    st = load_library().moe_forward_w8(ctypes.byref(shape), _ptr(x), _ptr(w_gate), _ptr(q1),
+                                       _ptr(s1), _ptr(q3), _ptr(s3), _ptr(q2), _ptr(s2), _ptr(y),
+                                       _ptr(idx), _ptr(w), _ptr(ws), ws.numel(),
+                                       _stream(x.device))
+    _check(st, "moe_forward_w8")
+    return (y, idx, w) if return_routing else y

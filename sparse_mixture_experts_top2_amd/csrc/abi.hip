@@ -26,7 +26,9 @@ Layout plan_workspace(const moe_shape_t &s) {
     L.xn = off;      off += align256(T * d * eb);
     L.xp = off;      off += align256(rows * d * eb);
     L.h = off;       off += align256(rows * f * eb);
-    L.o = off;       off += align256(rows * d * sizeof(float));
+    // o: at decode sizes room for the int8 path's K-slice partial sums
+    const size_t o_parts = T <= (size_t)kDecodeMaxT ? (size_t)kDownParts : 1;
+    L.o = off;       off += align256(o_parts * rows * d * sizeof(float));
     L.total = off;
     return L;
 }
@@ -130,6 +132,14 @@ hipError_t run_layer(const moe_shape_t &s, const void *x, const void *g, float e
     return e;
 }
 
+// The int8-weight expert calls: bf16 activations, decode sizes only.
+int check_w8(const moe_shape_t *s) {
+    int st = check_shape(s);
+    if (st) return st;
+    if (s->dtype != MOE_BF16 || s->T > kDecodeMaxT) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -143,7 +153,7 @@ const char *moe_status_str(int status) {
     case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN: device pointers must be 16-byte aligned";
     case MOE_ERR_ALIAS: return "MOE_ERR_ALIAS: an output overlaps an input";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or smaller than moe_workspace_bytes";
-    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: n_experts must be in [2, 64] and top_k in [1, min(4, n_experts)]";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: n_experts must be in [2, 64] and top_k in [1, min(4, n_experts)]; the int8-weight calls take bf16 layers with T <= 32";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP kernel launch failed";
     default: return "unknown moe status";
     }
@@ -343,6 +353,94 @@ int moe_block_forward(const moe_shape_t *s, const void *h, const void *rms_weigh
     float *w = topk_w_opt ? topk_w_opt : reinterpret_cast<float *>(base + L.w);
     return hip_status(run_layer(*s, h, rms_weight, eps, w_gate, w1, w3, w2, out, residual, idx,
                                 w, L, base, (hipStream_t)stream));
+}
+
+// ---- Weight-only int8 expert weights -------------------------------------
+
+int moe_quantize_int8(int n_mat, int K, int N, int dtype, const void *w, int8_t *q,
+                      float *scale, void *stream) {
+    if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_DTYPE;
+    if (n_mat < 1 || n_mat > 65535 || K < 1 || N < 8 || N % 8 != 0) return MOE_ERR_SHAPE;
+    if (!w || !q || !scale) return MOE_ERR_NULL;
+    if (misaligned(w) || misaligned(q) || misaligned(scale)) return MOE_ERR_ALIGN;
+    const size_t n = (size_t)n_mat * K * N;
+    const size_t wb = n * elem_bytes(dtype), sb = (size_t)n_mat * N * sizeof(float);
+    if (overlap(q, n, w, wb) || overlap(scale, sb, w, wb) || overlap(q, n, scale, sb))
+        return MOE_ERR_ALIAS;
+    return hip_status(launch_quantize_int8(n_mat, K, N, dtype, w, q, scale, (hipStream_t)stream));
+}
+
+int moe_expert_gateup_w8(const moe_shape_t *s, const void *xp, const int32_t *counts,
+                         const int32_t *offsets, const int8_t *q1, const float *s1,
+                         const int8_t *q3, const float *s3, void *h, void *stream) {
+    int st = check_w8(s);
+    if (st) return st;
+    if (s->T == 0) return MOE_OK;  // nothing to read or write
+    if (!xp || !counts || !offsets || !q1 || !s1 || !q3 || !s3 || !h) return MOE_ERR_NULL;
+    if (misaligned(xp) || misaligned(counts) || misaligned(offsets) || misaligned(q1) ||
+        misaligned(s1) || misaligned(q3) || misaligned(s3) || misaligned(h))
+        return MOE_ERR_ALIGN;
+    const size_t R = (size_t)routed_rows(*s);
+    if (overlap(h, R * s->d_ff * 2, xp, R * s->d_model * 2)) return MOE_ERR_ALIAS;
+    return hip_status(launch_gateup_w8(*s, static_cast<const uint16_t *>(xp), counts, offsets,
+                                       q1, s1, q3, s3, static_cast<uint16_t *>(h),
+                                       (hipStream_t)stream));
+}
+
+int moe_expert_down_w8(const moe_shape_t *s, const void *h, const int32_t *counts,
+                       const int32_t *offsets, const int8_t *q2, const float *s2, float *o,
+                       void *stream) {
+    int st = check_w8(s);
+    if (st) return st;
+    if (s->T == 0) return MOE_OK;  // nothing to read or write
+    if (!h || !counts || !offsets || !q2 || !s2 || !o) return MOE_ERR_NULL;
+    if (misaligned(h) || misaligned(counts) || misaligned(offsets) || misaligned(q2) ||
+        misaligned(s2) || misaligned(o))
+        return MOE_ERR_ALIGN;
+    const size_t R = (size_t)routed_rows(*s);
+    if (overlap(o, R * s->d_model * sizeof(float), h, R * s->d_ff * 2)) return MOE_ERR_ALIAS;
+    return hip_status(launch_down_w8(*s, static_cast<const uint16_t *>(h), counts, offsets, q2,
+                                     s2, o, 1, (hipStream_t)stream));
+}
+
+int moe_forward_w8(const moe_shape_t *s, const void *x, const void *w_gate, const int8_t *q1,
+                   const float *s1, const int8_t *q3, const float *s3, const int8_t *q2,
+                   const float *s2, void *y, int32_t *topk_idx_opt, float *topk_w_opt, void *ws,
+                   size_t ws_bytes, void *stream) {
+    int st = check_w8(s);
+    if (st) return st;
+    if (s->T == 0) return MOE_OK;  // nothing to read or write
+    if (!x || !w_gate || !q1 || !s1 || !q3 || !s3 || !q2 || !s2 || !y) return MOE_ERR_NULL;
+    if (misaligned(x) || misaligned(w_gate) || misaligned(q1) || misaligned(s1) ||
+        misaligned(q3) || misaligned(s3) || misaligned(q2) || misaligned(s2) || misaligned(y) ||
+        misaligned(topk_idx_opt) || misaligned(topk_w_opt))
+        return MOE_ERR_ALIGN;
+    const Layout L = plan_workspace(*s);
+    if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    if (misaligned(ws)) return MOE_ERR_ALIGN;
+    const size_t act = (size_t)s->T * s->d_model * 2;
+    if (overlap(y, act, x, act)) return MOE_ERR_ALIAS;
+
+    char *base = static_cast<char *>(ws);
+    int32_t *idx = topk_idx_opt ? topk_idx_opt : reinterpret_cast<int32_t *>(base + L.idx);
+    float *w = topk_w_opt ? topk_w_opt : reinterpret_cast<float *>(base + L.w);
+    int32_t *counts = reinterpret_cast<int32_t *>(base + L.counts);
+    int32_t *offsets = reinterpret_cast<int32_t *>(base + L.offsets);
+    int32_t *pos = reinterpret_cast<int32_t *>(base + L.pos);
+    int32_t *src = reinterpret_cast<int32_t *>(base + L.src);
+    uint16_t *h = reinterpret_cast<uint16_t *>(base + L.h);
+    float *o = reinterpret_cast<float *>(base + L.o);
+    const hipStream_t str = (hipStream_t)stream;
+    // Route, rank with the row -> token table, gate/up gathering its rows
+    // from x, down in kDownParts K slices, combine adding the slices.
+    hipError_t e = launch_route(*s, x, w_gate, idx, w, str);
+    if (e == hipSuccess) e = launch_rank(*s, idx, counts, offsets, pos, src, str);
+    if (e == hipSuccess)
+        e = launch_gateup_w8(*s, static_cast<const uint16_t *>(x), counts, offsets, q1, s1, q3,
+                             s3, h, str, src);
+    if (e == hipSuccess) e = launch_down_w8(*s, h, counts, offsets, q2, s2, o, kDownParts, str);
+    if (e == hipSuccess) e = launch_combine(*s, o, pos, w, y, str, nullptr, kDownParts);
+    return hip_status(e);
 }
 
 }  // extern "C"

@@ -20,12 +20,16 @@ namespace {
 // 03 MISTRAL BLOCK), still rounded once.  y may be res itself: each element
 // is read before the same thread writes it.  K (slots per token) is a
 // template parameter so that the slot loops are straight-line code.
+// With parts > 1, o holds that many partial sums (K slices of the down
+// projection), part_stride4 float4s apart; each expert row is their sum,
+// slice 0 first, before it is weighted.
 template <bool BF16_OUT, int K>
 __global__ __launch_bounds__(256) void combine_kernel(const float4 *__restrict__ o,
                                                       const int32_t *__restrict__ pos,
                                                       const float *__restrict__ w, int n_tok,
                                                       int d4, int chunk4, const void *res,
-                                                      void *y) {
+                                                      void *y, int parts,
+                                                      size_t part_stride4) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= n_tok) return;
@@ -37,13 +41,21 @@ __global__ __launch_bounds__(256) void combine_kernel(const float4 *__restrict__
         ws[s] = w[K * t + s];
     }
     const int j1 = min(d4, (int)(blockIdx.y + 1) * chunk4);
+    auto expert_row = [&](int s, int j) {
+        float4 a = r[s][j];
+        for (int p = 1; p < parts; ++p) {
+            const float4 b = r[s][j + p * part_stride4];
+            a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+        }
+        return a;
+    };
     for (int j = blockIdx.y * chunk4 + lane; j < j1; j += 64) {
         // slot order: ((w0 o0 + w1 o1) + w2 o2) + w3 o3
-        const float4 a = r[0][j];
+        const float4 a = expert_row(0, j);
         float4 v = make_float4(ws[0] * a.x, ws[0] * a.y, ws[0] * a.z, ws[0] * a.w);
 #pragma unroll
         for (int s = 1; s < K; ++s) {
-            const float4 b = r[s][j];
+            const float4 b = expert_row(s, j);
             v.x = v.x + ws[s] * b.x;
             v.y = v.y + ws[s] * b.y;
             v.z = v.z + ws[s] * b.z;
@@ -77,24 +89,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const float4 *__restrict__
 template <bool BF16_OUT>
 hipError_t launch_combine_t(const moe_shape_t &s, dim3 grid, const float4 *o, const int32_t *pos,
                             const float *w, int d4, int chunk4, const void *res, void *y,
-                            hipStream_t stream) {
+                            int parts, size_t ps4, hipStream_t stream) {
     const dim3 block(256);
     switch (s.top_k) {
     case 1:
         hipLaunchKernelGGL((combine_kernel<BF16_OUT, 1>), grid, block, 0, stream, o, pos, w, s.T,
-                           d4, chunk4, res, y);
+                           d4, chunk4, res, y, parts, ps4);
         break;
     case 2:
         hipLaunchKernelGGL((combine_kernel<BF16_OUT, 2>), grid, block, 0, stream, o, pos, w, s.T,
-                           d4, chunk4, res, y);
+                           d4, chunk4, res, y, parts, ps4);
         break;
     case 3:
         hipLaunchKernelGGL((combine_kernel<BF16_OUT, 3>), grid, block, 0, stream, o, pos, w, s.T,
-                           d4, chunk4, res, y);
+                           d4, chunk4, res, y, parts, ps4);
         break;
     case 4:
         hipLaunchKernelGGL((combine_kernel<BF16_OUT, 4>), grid, block, 0, stream, o, pos, w, s.T,
-                           d4, chunk4, res, y);
+                           d4, chunk4, res, y, parts, ps4);
         break;
     default:
         return hipErrorInvalidValue;
@@ -105,7 +117,8 @@ hipError_t launch_combine_t(const moe_shape_t &s, dim3 grid, const float4 *o, co
 }  // namespace
 
 hipError_t launch_combine(const moe_shape_t &s, const float *o, const int32_t *pos,
-                          const float *w, void *y, hipStream_t stream, const void *res) {
+                          const float *w, void *y, hipStream_t stream, const void *res,
+                          int parts) {
     if (s.T == 0) return hipSuccess;
     const int d4 = s.d_model / 4;
     // Column chunks of whole 64-vector passes, enough for ~512 workgroups.
@@ -115,9 +128,11 @@ hipError_t launch_combine(const moe_shape_t &s, const float *o, const int32_t *p
     const int chunk4 = (passes + nch - 1) / nch * 64;
     const dim3 grid(tok_groups, (d4 + chunk4 - 1) / chunk4);
     const float4 *o4 = reinterpret_cast<const float4 *>(o);
+    const size_t ps4 = (size_t)routed_rows(s) * d4;
     if (s.dtype == MOE_BF16)
-        return launch_combine_t<true>(s, grid, o4, pos, w, d4, chunk4, res, y, stream);
-    return launch_combine_t<false>(s, grid, o4, pos, w, d4, chunk4, res, y, stream);
+        return launch_combine_t<true>(s, grid, o4, pos, w, d4, chunk4, res, y, parts, ps4,
+                                      stream);
+    return launch_combine_t<false>(s, grid, o4, pos, w, d4, chunk4, res, y, parts, ps4, stream);
 }
 
 }  // namespace moe

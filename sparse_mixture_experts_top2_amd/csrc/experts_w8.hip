@@ -1,0 +1,363 @@
+// Weight-only int8 expert weights for the decode path.  The KerasFormers
+// Mixtral page offers int8 weight quantization for this model, and the
+// Hugging Face page low-memory loading; neither gives a scheme, so the
+// plainest is used: symmetric int8 with one fp32 scale per output channel
+// of each expert matrix, W[j, n] ~ s[n] * q[j, n].
+//
+// Decode is bound by streaming the selected experts' weights (section 05 of
+// "Mixtral 8x7B -- The Evolving Transformer": only the chosen experts run),
+// so int8 codes halve the bytes of the step.  The activations stay bf16:
+// each lane turns its codes into bf16 (exact, |q| <= 127) and the product
+// runs on the bf16 matrix cores with fp32 accumulation; the scale of each
+// output column multiplies the finished sum.
+//
+//  * quantize_int8_kernel: s[n] = max_j |W[j, n]| / 127 and
+//    q = rint(W / s) clamped to [-127, 127], in fp32 (s = 0, q = 0 for a
+//    zero column).  One pass for the maxima, one for the codes.
+//  * decode_w8_kernel: a workgroup streams a 256-column slab of one
+//    expert's codes (256-byte row segments, read once, non-temporal) over
+//    its K range.  Eight wavefronts: two column halves of 128 times four K
+//    parts, whose partial sums meet in a fixed LDS tree.  Gate/up fuses
+//    the scales and silu(g) * u and writes h in bf16; down writes fp32
+//    partial sums of one K slice each (the combine adds the slices in
+//    order before it weights the slots).
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int W8_WAVES = 8;                     // 2 column halves x 4 K parts
+constexpr int W8_HALF = 128;                    // columns per wavefront
+constexpr int W8_HALVES = 2;                    // column halves per workgroup
+constexpr int W8_COLS = W8_HALVES * W8_HALF;    // weight columns per workgroup
+constexpr int W8_KPARTS = W8_WAVES / W8_HALVES; // wavefronts along K per column half
+
+// Code `c` (0..7) of an 8-code row segment, as an fp32 value.
+__device__ __forceinline__ float code_f32(uint2 r, int c) {
+    const uint32_t w = c < 4 ? r.x : r.y;
+    return (float)(int)(int8_t)(w >> (8 * (c & 3)));
+}
+
+// Two fp32 values that bf16 holds exactly, packed as bf16 (lo in the low
+// half); gfx950 converts the pair in one instruction.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_exact_bf16(float lo, float hi) {
+    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// r[i] holds row i of an 8 x 8 block of codes (8 columns, one byte each).
+// Returns column c as the MFMA B operand: 8 bf16 along K, row 0 lowest.
+__device__ __forceinline__ bf16x8_t column_operand(const uint2 (&r)[8], int c) {
+    uint4 v;
+    v.x = pack_exact_bf16(code_f32(r[0], c), code_f32(r[1], c));
+    v.y = pack_exact_bf16(code_f32(r[2], c), code_f32(r[3], c));
+    v.z = pack_exact_bf16(code_f32(r[4], c), code_f32(r[5], c));
+    v.w = pack_exact_bf16(code_f32(r[6], c), code_f32(r[7], c));
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// 8-byte load with the non-temporal hint: each code is read exactly once.
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 load_stream8(const int8_t *p) {
+    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
+    return make_uint2(v[0], v[1]);
+}
+
+template <typename T>
+__device__ __forceinline__ void load4(const T *p, float (&v)[4]);
+template <>
+__device__ __forceinline__ void load4<float>(const float *p, float (&v)[4]) {
+    const float4 a = *reinterpret_cast<const float4 *>(p);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+}
+template <>
+__device__ __forceinline__ void load4<uint16_t>(const uint16_t *p, float (&v)[4]) {
+    const uint2 a = *reinterpret_cast<const uint2 *>(p);
+    v[0] = bf16_to_f32(a.x & 0xffffu); v[1] = bf16_to_f32(a.x >> 16);
+    v[2] = bf16_to_f32(a.y & 0xffffu); v[3] = bf16_to_f32(a.y >> 16);
+}
+
+// grid (ceil(N / 256), n_mat), 256 threads: thread (kp, lane) owns columns
+// 4*lane .. 4*lane+3 of the workgroup's 256 and the K quarter kp.  The
+// column maxima of the four quarters meet in LDS (a maximum is exact in
+// any order).
+template <typename T>
+__global__ __launch_bounds__(256) void quantize_int8_kernel(const T *__restrict__ W, int K,
+                                                            int N, int8_t *__restrict__ Q,
+                                                            float *__restrict__ S) {
+    __shared__ float amax[4][256];
+    const int lane = threadIdx.x & 63, kp = threadIdx.x >> 6;
+    const int e = blockIdx.y;
+    const int col = blockIdx.x * 256 + lane * 4;
+    const bool ok = col < N;   // N % 4 == 0: the four columns are all in or all out
+    const size_t base = (size_t)e * K * N + (ok ? col : 0);
+    const int j0 = (int)((int64_t)K * kp / 4), j1 = (int)((int64_t)K * (kp + 1) / 4);
+    float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (ok)
+        for (int j = j0; j < j1; ++j) {
+            float v[4];
+            load4<T>(W + base + (size_t)j * N, v);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) a[c] = fmaxf(a[c], fabsf(v[c]));
+        }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) amax[kp][lane * 4 + c] = a[c];
+    __syncthreads();
+    float s[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int i = lane * 4 + c;
+        s[c] = fmaxf(fmaxf(amax[0][i], amax[1][i]), fmaxf(amax[2][i], amax[3][i])) / 127.0f;
+    }
+    if (!ok) return;
+    if (kp == 0)
+        *reinterpret_cast<float4 *>(S + (size_t)e * N + col) = make_float4(s[0], s[1], s[2], s[3]);
+    for (int j = j0; j < j1; ++j) {
+        float v[4];
+        load4<T>(W + base + (size_t)j * N, v);
+        uint32_t packed = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            int code = 0;
+            if (s[c] > 0.0f) code = (int)fminf(fmaxf(rintf(v[c] / s[c]), -127.0f), 127.0f);
+            packed |= (uint32_t)(code & 0xff) << (8 * c);
+        }
+        *reinterpret_cast<uint32_t *>(Q + base + (size_t)j * N) = packed;
+    }
+}
+
+// C[r, n] for the rows r of expert e = blockIdx.y (at most 16 * MB of
+// them), columns n of slab blockIdx.x, K slice blockIdx.z of gridDim.z:
+//   NMAT = 2: C = bf16(silu(S0 * (A Q0[e])) * (S1 * (A Q1[e])))   (h)
+//   NMAT = 1: C + z * part_stride = fp32(S0 * (A Q0[e]) over slice z) (o)
+// With src not NULL, grouped row r is row src[r] of A.
+//
+// Wavefront w covers column half w % 2 (128 columns) and K part w / 2.
+// Lane l loads 8 columns (8 * (l % 16) ..) of 8 rows (8 * (l / 16) ..) of
+// each 32-row step; the two halves of a workgroup read each 256-byte row
+// segment together.  A lane's 8 columns give 8 MFMA B operands; block c of
+// the accumulators holds weight columns 8 * (l % 16) + c.  (Measured: one
+// wavefront per SIMD streaming whole 256-byte segments hides less latency,
+// and 128-column workgroups reading 128-byte segments stream slower.)
+template <int MB, int NMAT>
+__global__ __launch_bounds__(W8_WAVES * 64) void decode_w8_kernel(
+    const uint16_t *__restrict__ A, const int8_t *__restrict__ Q0, const float *__restrict__ S0,
+    const int8_t *__restrict__ Q1, const float *__restrict__ S1, void *__restrict__ C,
+    const int32_t *__restrict__ counts, const int32_t *__restrict__ offsets, int K, int N,
+    int a_rows, const int32_t *__restrict__ src, size_t part_stride) {
+    const int e = blockIdx.y;
+    const int Me = counts[e];
+    if (Me == 0) return;  // an expert no token chose: its codes are never read
+    const int r0 = offsets[e];
+    const int nmb = min(MB, (Me + 15) >> 4);
+    // The wavefront index is uniform: read it into a scalar so that the K
+    // loop bounds are scalar and the loop is not taken for a divergent one.
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int half = wave % W8_HALVES, kp = wave / W8_HALVES;
+    const int kg = lane >> 4, nb = lane & 15;
+    const int col = blockIdx.x * W8_COLS + half * W8_HALF + nb * 8;
+    const bool col_ok = col < N;   // N % 8 == 0: the 8 columns are all in or all out
+
+    // Codes are addressed as a uniform base (this expert's matrix) plus a
+    // 32-bit lane offset (an expert matrix is far below 4 GiB).
+    const int8_t *Qb[NMAT];
+    Qb[0] = Q0 + (size_t)e * K * N;
+    if (NMAT == 2) Qb[NMAT - 1] = Q1 + (size_t)e * K * N;
+    const uint32_t lane_col = (uint32_t)(col_ok ? col : 0);
+    const uint16_t *Arow[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+        const int r = min(r0 + i * 16 + (lane & 15), a_rows - 1);
+        Arow[i] = A + (size_t)(src ? src[r] : r) * K;
+    }
+
+    f32x4_t acc[NMAT][MB][8];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[m][i][c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // 32-row K steps: this workgroup's slice, then this wavefront's quarter.
+    const int nks = (K + 31) >> 5;
+    const int z0 = (int)((int64_t)nks * blockIdx.z / gridDim.z);
+    const int z1 = (int)((int64_t)nks * (blockIdx.z + 1) / gridDim.z);
+    const int ks0 = z0 + (z1 - z0) * kp / W8_KPARTS;
+    const int ks1 = z0 + (z1 - z0) * (kp + 1) / W8_KPARTS;
+    if (ks0 < ks1) {
+        // Two register buffers: the loads of step ks + 1 are in flight while
+        // step ks computes.  Loads are unconditional, from clamped
+        // addresses, so they issue back to back and the wait counts stay
+        // exact: rows past K (K % 8 == 0, so a lane's 8 rows are all in or
+        // all out) meet activations set to zero; lanes past N are not
+        // stored.
+        uint2 rb[2][NMAT][8];
+        uint4 ar[2][MB];
+        uint32_t keep[2];   // all ones, or zero for rows past K (applied at use)
+        auto load_step = [&](int b, int ks) __attribute__((always_inline)) {
+            const int k = ks * 32 + kg * 8;
+            const int kr = min(k, K - 8);
+            const uint32_t off = (uint32_t)kr * (uint32_t)N + lane_col;
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    rb[b][m][i] = load_stream8(Qb[m] + off + (uint32_t)i * (uint32_t)N);
+#pragma unroll
+            for (int i = 0; i < MB; ++i) ar[b][i] = *reinterpret_cast<const uint4 *>(Arow[i] + kr);
+            keep[b] = k < K ? 0xffffffffu : 0u;
+        };
+        auto compute_step = [&](int b) __attribute__((always_inline)) {
+            bf16x8_t aop[MB];
+#pragma unroll
+            for (int i = 0; i < MB; ++i) {
+                const uint4 a = ar[b][i];
+                aop[i] = __builtin_bit_cast(bf16x8_t, make_uint4(a.x & keep[b], a.y & keep[b],
+                                                                 a.z & keep[b], a.w & keep[b]));
+            }
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const bf16x8_t bop = column_operand(rb[b][m], c);
+#pragma unroll
+                    for (int i = 0; i < MB; ++i) {
+                        if (i >= nmb) continue;
+                        acc[m][i][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[i], bop,
+                                                                               acc[m][i][c], 0, 0, 0);
+                    }
+                }
+        };
+        load_step(0, ks0);
+        int ks = ks0;
+        while (ks + 1 < ks1) {
+            load_step(1, ks + 1);
+            compute_step(0);
+            if (ks + 2 < ks1) load_step(0, ks + 2);
+            compute_step(1);
+            ks += 2;
+        }
+        if (ks < ks1) compute_step(0);   // an odd step count: the last step
+    }
+
+    // Fixed-order tree over the four K parts of each column half:
+    // (k0 + k2) + (k1 + k3).
+    constexpr int SLOTS = W8_KPARTS / 2;
+    __shared__ f32x4_t red[W8_HALVES * SLOTS][NMAT * 8][64];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+        if (i >= nmb) break;
+#pragma unroll
+        for (int hs = SLOTS; hs >= 1; hs >>= 1) {
+            if (kp >= hs && kp < 2 * hs)
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                    for (int c = 0; c < 8; ++c)
+                        red[half * SLOTS + kp - hs][m * 8 + c][lane] = acc[m][i][c];
+            __syncthreads();
+            if (kp < hs)
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) acc[m][i][c] += red[half * SLOTS + kp][m * 8 + c][lane];
+            __syncthreads();
+        }
+        if (kp != 0 || !col_ok) continue;
+        float sc[NMAT][8];
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+            const float4 *sp =
+                reinterpret_cast<const float4 *>((m == 0 ? S0 : S1) + (size_t)e * N + col);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const float4 v = sp[q];
+                sc[m][4 * q] = v.x; sc[m][4 * q + 1] = v.y;
+                sc[m][4 * q + 2] = v.z; sc[m][4 * q + 3] = v.w;
+            }
+        }
+        // 16x16 accumulator layout: value j of lane l is row 4*(l/16) + j,
+        // column l%16 of the block; block c holds weight columns 8*(l%16) + c.
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = i * 16 + 4 * kg + j;
+            if (row >= Me) continue;
+            if (NMAT == 2) {
+                uint32_t p[4];
+#pragma unroll
+                for (int c = 0; c < 8; c += 2) {
+                    const float g0 = sc[0][c] * acc[0][i][c][j];
+                    const float g1 = sc[0][c + 1] * acc[0][i][c + 1][j];
+                    const float u0 = sc[NMAT - 1][c] * acc[NMAT - 1][i][c][j];
+                    const float u1 = sc[NMAT - 1][c + 1] * acc[NMAT - 1][i][c + 1][j];
+                    p[c >> 1] = f32_to_bf16(silu_f32(g0) * u0) |
+                                (f32_to_bf16(silu_f32(g1) * u1) << 16);
+                }
+                *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(C) + (size_t)(r0 + row) * N +
+                                           col) = make_uint4(p[0], p[1], p[2], p[3]);
+            } else {
+                float4 *dst = reinterpret_cast<float4 *>(static_cast<float *>(C) +
+                                                         blockIdx.z * part_stride +
+                                                         (size_t)(r0 + row) * N + col);
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+                    dst[q] = make_float4(sc[0][4 * q] * acc[0][i][4 * q][j],
+                                         sc[0][4 * q + 1] * acc[0][i][4 * q + 1][j],
+                                         sc[0][4 * q + 2] * acc[0][i][4 * q + 2][j],
+                                         sc[0][4 * q + 3] * acc[0][i][4 * q + 3][j]);
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_int8(int n_mat, int K, int N, int dtype, const void *w, int8_t *q,
+                                float *scale, hipStream_t stream) {
+    const dim3 grid((N + 255) / 256, n_mat);
+    if (dtype == MOE_BF16)
+        hipLaunchKernelGGL(quantize_int8_kernel<uint16_t>, grid, dim3(256), 0, stream,
+                           static_cast<const uint16_t *>(w), K, N, q, scale);
+    else
+        hipLaunchKernelGGL(quantize_int8_kernel<float>, grid, dim3(256), 0, stream,
+                           static_cast<const float *>(w), K, N, q, scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_gateup_w8(const moe_shape_t &s, const uint16_t *xp, const int32_t *counts,
+                            const int32_t *offsets, const int8_t *q1, const float *s1,
+                            const int8_t *q3, const float *s3, uint16_t *h, hipStream_t stream,
+                            const int32_t *src) {
+    const int d = s.d_model, f = s.d_ff, E = s.n_experts, rows = routed_rows(s);
+    const dim3 grid((f + W8_COLS - 1) / W8_COLS, E, 1), block(W8_WAVES * 64);
+    if (s.T <= 16)
+        hipLaunchKernelGGL((decode_w8_kernel<1, 2>), grid, block, 0, stream, xp, q1, s1, q3, s3,
+                           h, counts, offsets, d, f, rows, src, (size_t)0);
+    else if (s.T <= kDecodeMaxT)
+        hipLaunchKernelGGL((decode_w8_kernel<2, 2>), grid, block, 0, stream, xp, q1, s1, q3, s3,
+                           h, counts, offsets, d, f, rows, src, (size_t)0);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_down_w8(const moe_shape_t &s, const uint16_t *h, const int32_t *counts,
+                          const int32_t *offsets, const int8_t *q2, const float *s2, float *o,
+                          int parts, hipStream_t stream) {
+    const int d = s.d_model, f = s.d_ff, E = s.n_experts, rows = routed_rows(s);
+    const size_t part_stride = (size_t)rows * d;
+    const dim3 grid((d + W8_COLS - 1) / W8_COLS, E, parts), block(W8_WAVES * 64);
+    if (s.T <= 16)
+        hipLaunchKernelGGL((decode_w8_kernel<1, 1>), grid, block, 0, stream, h, q2, s2, nullptr,
+                           nullptr, o, counts, offsets, f, d, rows, nullptr, part_stride);
+    else if (s.T <= kDecodeMaxT)
+        hipLaunchKernelGGL((decode_w8_kernel<2, 1>), grid, block, 0, stream, h, q2, s2, nullptr,
+                           nullptr, o, counts, offsets, f, d, rows, nullptr, part_stride);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -18,6 +18,13 @@ constexpr int kMaxTopK = 4;     // experts per token
 // an expert then has at most 32 rows (a token never picks one expert twice,
 // whatever top_k is).
 constexpr int kDecodeMaxT = 32;
+// K slices of the int8-weight down projection at decode sizes; the combine
+// adds the slices in order.  The workspace's o region holds this many
+// copies of o when T <= kDecodeMaxT.
+#ifndef MOE_DOWN_PARTS
+#define MOE_DOWN_PARTS 4
+#endif
+constexpr int kDownParts = MOE_DOWN_PARTS;
 
 struct Layout {
     size_t idx, w, counts, offsets, pos, src, xn, xp, h, o, total;
@@ -65,10 +72,26 @@ hipError_t launch_gateup(const moe_shape_t &s, const void *xp, const int32_t *co
 hipError_t launch_down(const moe_shape_t &s, const void *h, const int32_t *counts,
                        const int32_t *offsets, const void *w2, float *o, hipStream_t stream);
 
-// y = w0 o[pos0] + w1 o[pos1] (+ res when res is not NULL), rounded once.
+// y = w0 o[pos0] + w1 o[pos1] + ... (+ res when res is not NULL), rounded
+// once.  With parts > 1, o holds that many partial sums, each kT x d, one
+// after the other; every row is their sum in order before it is weighted.
 hipError_t launch_combine(const moe_shape_t &s, const float *o, const int32_t *pos,
                           const float *w, void *y, hipStream_t stream,
-                          const void *res = nullptr);
+                          const void *res = nullptr, int parts = 1);
+
+// Weight-only int8 (experts_w8.hip).  W [n_mat, K, N] (dtype) -> codes
+// q [n_mat, K, N] and per-column scales [n_mat, N].
+hipError_t launch_quantize_int8(int n_mat, int K, int N, int dtype, const void *w, int8_t *q,
+                                float *scale, hipStream_t stream);
+// Gate/up and down on int8 codes, T <= kDecodeMaxT only (bf16 activations).
+// Down writes `parts` K-slice partial sums, each kT x d, one after another.
+hipError_t launch_gateup_w8(const moe_shape_t &s, const uint16_t *xp, const int32_t *counts,
+                            const int32_t *offsets, const int8_t *q1, const float *s1,
+                            const int8_t *q3, const float *s3, uint16_t *h, hipStream_t stream,
+                            const int32_t *src = nullptr);
+hipError_t launch_down_w8(const moe_shape_t &s, const uint16_t *h, const int32_t *counts,
+                          const int32_t *offsets, const int8_t *q2, const float *s2, float *o,
+                          int parts, hipStream_t stream);
 
 // Per-dtype expert launchers (experts_f32.hip, experts_bf16.hip).  The bf16
 // ones pick the weight-streaming kernels for T <= kDecodeMaxT.

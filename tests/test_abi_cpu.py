@@ -21,7 +21,7 @@ P17 = ctypes.c_void_p(0x10001)
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_entry_points():
@@ -172,3 +172,50 @@ def test_python_binding_refuses_cpu_tensors():
     x = torch.zeros(4, 16, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU tensor"):
         moe.route(x, torch.zeros(16, 8, dtype=torch.bfloat16))
+
+
+def test_int8_weight_checks():
+    lib = moe.load_library()
+    name = lambda st: moe.STATUS_NAMES[st]
+    Q = lambda *a: name(lib.moe_quantize_int8(*a))
+    A, B, C = (ctypes.c_void_p(0x10000000 * n) for n in (1, 2, 3))
+    assert Q(2, 64, 256, 7, A, B, C, None) == "MOE_ERR_DTYPE"
+    assert Q(0, 64, 256, moe.MOE_BF16, A, B, C, None) == "MOE_ERR_SHAPE"
+    assert Q(2, 64, 12, moe.MOE_BF16, A, B, C, None) == "MOE_ERR_SHAPE"
+    assert Q(2, 0, 256, moe.MOE_BF16, A, B, C, None) == "MOE_ERR_SHAPE"
+    assert Q(70000, 8, 8, moe.MOE_BF16, A, B, C, None) == "MOE_ERR_SHAPE"
+    assert Q(2, 64, 256, moe.MOE_BF16, None, B, C, None) == "MOE_ERR_NULL"
+    assert Q(2, 64, 256, moe.MOE_BF16, A, P17, C, None) == "MOE_ERR_ALIGN"
+    assert Q(2, 64, 256, moe.MOE_BF16, A, ctypes.c_void_p(0x10000000 + 4096), C, None) == \
+        "MOE_ERR_ALIAS"                                   # codes over the weights
+    assert Q(2, 64, 256, moe.MOE_BF16, A, B, ctypes.c_void_p(0x20000000 + 256), None) == \
+        "MOE_ERR_ALIAS"                                   # scales over the codes
+    # the layer calls: bf16 at decode sizes only
+    F = lambda s: name(lib.moe_forward_w8(ctypes.byref(s), P16, P16, P16, P16, P16, P16, P16,
+                                          P16, P16B, None, None, P16, 1 << 40, None))
+    assert F(shape(T=33)) == "MOE_ERR_UNSUPPORTED"
+    assert F(shape(T=16, dtype=moe.MOE_F32)) == "MOE_ERR_UNSUPPORTED"
+    assert F(shape(T=16, k=5)) == "MOE_ERR_UNSUPPORTED"
+    assert F(shape(T=0)) == "MOE_OK"
+    s = shape(T=16)
+    assert name(lib.moe_forward_w8(ctypes.byref(s), P16, P16, None, P16, P16, P16, P16, P16,
+                                   P16B, None, None, P16, 1 << 40, None)) == "MOE_ERR_NULL"
+    assert name(lib.moe_forward_w8(ctypes.byref(s), P16, P16, P16, P17, P16, P16, P16, P16,
+                                   P16B, None, None, P16, 1 << 40, None)) == "MOE_ERR_ALIGN"
+    assert name(lib.moe_forward_w8(ctypes.byref(s), P16, P16, P16, P16, P16, P16, P16, P16,
+                                   P16, None, None, P16B, 1 << 40, None)) == "MOE_ERR_ALIAS"
+    assert name(lib.moe_forward_w8(ctypes.byref(s), P16, P16, P16, P16, P16, P16, P16, P16,
+                                   P16B, None, None, P16, 16, None)) == "MOE_ERR_WORKSPACE"
+    G = lambda s: name(lib.moe_expert_gateup_w8(ctypes.byref(s), P16, P16, P16, P16, P16, P16,
+                                                P16, P16, None))
+    D = lambda s: name(lib.moe_expert_down_w8(ctypes.byref(s), P16, P16, P16, P16, P16, P16,
+                                              None))
+    assert G(shape(T=40)) == "MOE_ERR_UNSUPPORTED" and D(shape(T=40)) == "MOE_ERR_UNSUPPORTED"
+    assert G(shape(T=8)) == "MOE_ERR_ALIAS" and D(shape(T=8)) == "MOE_ERR_ALIAS"
+
+
+def test_decode_workspace_holds_the_down_slices():
+    # T <= 32: o holds four K-slice partial sums of kT x d fp32
+    lib = moe.load_library()
+    s = shape(T=32, d=4096, f=14336, k=2)
+    assert lib.moe_workspace_bytes(ctypes.byref(s)) >= 4 * 64 * 4096 * 4 + 64 * 14336 * 2

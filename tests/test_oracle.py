@@ -487,6 +487,13 @@ def pin_forward_w8_power_of_two_scales():
         qb, sb = oracle.quantize_int8(ww)
         np.testing.assert_array_equal(qb, qq)
         np.testing.assert_array_equal(sb, ss)
+    # the two stages alone equal the plain layer's stages on W = s * q
+    ex = rng.integers(0, E, T).astype(np.int32)
+    np.testing.assert_array_equal(oracle.expert_hidden_w8(x, ex, q1, s1, q3, s3),
+                                  oracle.expert_hidden(x, ex, w1, w3))
+    hid = torch.tensor(rng.standard_normal((T, f)), dtype=torch.float32)
+    np.testing.assert_array_equal(oracle.expert_down_w8(hid, ex, q2, s2),
+                                  oracle.expert_down(hid, ex, w2))
 
 
 PINS = [pin_worked_examples, pin_logits_match_numpy, pin_top2_brute_force,
