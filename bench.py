@@ -281,6 +281,7 @@ def measure_w8(wl_name, steps, warmup):
             "roofline": {"kernel": "expert gate/up on int8 codes (weight-streaming MFMA)",
                          "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                         "traffic": counter_traffic(wl_name, TRAFFIC_PROFILE_W8),
                          "algorithmic_bytes_per_launch": gu_bytes,
                          "avg_launch_ms": round(k_ms, 5)},
             "layer_roofline": {"bound": "hbm", "achieved": round(lay, 1), "peak": PEAK_HBM_GBS,
@@ -290,16 +291,17 @@ def measure_w8(wl_name, steps, warmup):
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_gateup_8x7b.md")
+TRAFFIC_PROFILE_W8 = os.path.join(ROOT, "profiles", "hbm_traffic_gateup_w8_decode_8x7b.md")
 
 
-def counter_traffic(wl_name):
+def counter_traffic(wl_name, profile=None):
     """HBM bytes per gate/up launch from the committed rocprofv3 counter
     summary (FETCH_SIZE and WRITE_SIZE, each scaled by a copy kernel of known
     size), or None when there is no entry for this workload or the kernels'
     source has changed since the counters were taken."""
     import hashlib
     try:
-        text = open(TRAFFIC_PROFILE).read()
+        text = open(profile or TRAFFIC_PROFILE).read()
     except OSError:
         return None
     block = text.rsplit("```", 2)[-2] if text.count("```") >= 2 else ""
