@@ -24,6 +24,8 @@ section 05 (MOE ROUTER + MOE), and section 04 (SWIGLU):
 * ``forward``      the whole layer, token by token
 * ``quantize_int8``, ``forward_w8``  weight-only int8 expert weights (one
                    scale per output channel) and the layer on them
+* ``backward``     gradients of sum(dy * y) for x, the router and the three
+                   expert matrices (top-k picks held fixed)
 
 Parity status: every function is pinned by tests/test_oracle.py against
 closed forms, brute force, library routines (numpy fp64) and invariants.
@@ -79,6 +81,8 @@ def _bind(path: str):
     lib.oracle_forward_w8.restype = I
     lib.oracle_expert_stage_w8.argtypes = [I, I, I, I, I, P, P, I, P, P, P, P, P, P, P, I]
     lib.oracle_expert_stage_w8.restype = I
+    lib.oracle_backward.argtypes = [I, I, I, I, I, P, P, P, P, P, I, P, P, P, P, P, P, P, P, I]
+    lib.oracle_backward.restype = I
     lib.oracle_rmsnorm.argtypes = [I, I, P, P, ctypes.c_double, I, P, P, I]
     lib.oracle_rmsnorm.restype = I
     return lib
@@ -450,3 +454,40 @@ def expert_down_w8(hid, expert: np.ndarray, q2, s2, threads: Optional[int] = Non
     """s2 * (hid[r] q2[e]), e = expert[r]; float64 [n, d]."""
     E, f, d = q2.shape
     return _w8_stage(1, hid, expert, d, f, E, (None, None, None, None, q2, s2), threads)
+
+
+# ---------------------------------------------------------------------------
+# Backward.
+
+def backward(x, w_gate, w1, w3, w2, dy, top_k: int = 2, threads: Optional[int] = None):
+    """Gradients of L = sum(dy * y) with y = forward(x, ...): returns a dict
+    with dx [T,d], dw_gate [d,E], dw1, dw3 [E,d,f], dw2 [E,f,d] (float64),
+    and the routing idx [T,k], w [T,k].  dy is any float array [T,d]; it is
+    used in float64 as given."""
+    xa, dx_ = _as_host(x)
+    ga, dg_ = _as_host(w_gate)
+    a1, d1 = _as_host(w1)
+    a3, d3 = _as_host(w3)
+    a2, d2 = _as_host(w2)
+    dt = _same_dtype(dx_, dg_, d1, d3, d2)
+    try:
+        import torch
+        if isinstance(dy, torch.Tensor):
+            dy = dy.detach().cpu().double().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    dya = np.ascontiguousarray(dy, np.float64)
+    T, d = xa.shape
+    E = ga.shape[1]
+    f = a1.shape[2]
+    assert dya.shape == (T, d)
+    out = {"dx": np.zeros((T, d)), "dw_gate": np.zeros((d, E)), "dw1": np.zeros((E, d, f)),
+           "dw3": np.zeros((E, d, f)), "dw2": np.zeros((E, f, d)),
+           "idx": np.zeros((T, top_k), np.int32), "w": np.zeros((T, top_k))}
+    rc = _load().oracle_backward(T, d, f, E, top_k, _ptr(xa), _ptr(ga), _ptr(a1), _ptr(a3),
+                                 _ptr(a2), dt, _ptr(dya), _ptr(out["dx"]), _ptr(out["dw_gate"]),
+                                 _ptr(out["dw1"]), _ptr(out["dw3"]), _ptr(out["dw2"]),
+                                 _ptr(out["idx"]), _ptr(out["w"]), threads or default_threads())
+    if rc != 0:
+        raise ValueError(f"oracle_backward failed ({rc})")
+    return out

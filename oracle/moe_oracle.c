@@ -401,6 +401,200 @@ int oracle_forward(int T, int d, int f, int E, int k, const void *x, const void 
 }
 
 /* ------------------------------------------------------------------------
+ * Backward.  The pages train the router and the experts together and name
+ * no loss, capacity or auxiliary term, so the backward is the gradient of
+ * the forward above as written, for a given upstream gradient dy [T,d]
+ * (L = sum_t dy[t] . y[t]).  The top-k picks are a discrete choice: they
+ * stay fixed, and the gradient reaches the router only through the softmax
+ * over the picked logits.  Per token t and slot s (e = i_s):
+ *
+ *   dw_s   = dy . o_s                             (o_s the expert's output)
+ *   dl_e   = w_s (dw_s - sum_r w_r dw_r)          (softmax Jacobian; 0 for
+ *                                                  experts not picked)
+ *   do_s   = w_s dy
+ *   da     = do_s W2[e]^T,   da_n = sum_m do_m W2[e][n][m]
+ *   dg     = da * u * silu'(g),  silu'(g) = sig(g) (1 + g (1 - sig(g)))
+ *   du     = da * silu(g)
+ *   dx    += dg W1[e]^T + du W3[e]^T             (slots in order)
+ *   dW1[e] += x^T dg,  dW3[e] += x^T du,  dW2[e] += a^T do_s
+ *   dx    += dl Wg^T,    dWg += x^T dl
+ *
+ * Weight gradients sum over tokens in token order (then slot order).  */
+
+typedef struct {
+    int T, d, f, E, k, dtype;
+    const void *x, *wg, *w1, *w3, *w2;
+    const double *dy;                 /* [T, d] */
+    int32_t *idx;                     /* [T, k] */
+    double *w;                        /* [T, k] */
+    double *dx;                       /* [T, d] */
+    double *dl;                       /* [T, E] */
+    double *a, *dg, *du, *dov;        /* per assignment: [R, f] x3, [R, d] */
+} bwd_ctx;
+
+static void bwd_token_range(void *p, int lo, int hi) {
+    bwd_ctx *c = (bwd_ctx *)p;
+    const int d = c->d, f = c->f, E = c->E, k = c->k;
+    double l[256], dws[ORC_MAX_K];
+    double *xr = malloc(sizeof(double) * d);
+    double *g = malloc(sizeof(double) * f);
+    double *u = malloc(sizeof(double) * f);
+    double *o = malloc(sizeof(double) * d);
+    double *da = malloc(sizeof(double) * f);
+    if (!xr || !g || !u || !o || !da) goto out;
+    for (int t = lo; t < hi; ++t) {
+        const size_t xo = (size_t)t * d;
+        int32_t *it = c->idx + (size_t)k * t;
+        double *wt = c->w + (size_t)k * t;
+        const double *dyt = c->dy + xo;
+        double *dxt = c->dx + xo;
+        router_logits(d, E, c->x, xo, c->wg, c->dtype, l);
+        topk_softmax(E, k, l, it, wt);
+        for (int j = 0; j < d; ++j) { xr[j] = load_elem(c->x, c->dtype, xo + j); dxt[j] = 0.0; }
+        for (int s = 0; s < k; ++s) {
+            const int e = it[s];
+            const size_t r = (size_t)k * t + s;
+            double *ar = c->a + r * f, *dgr = c->dg + r * f, *dur = c->du + r * f;
+            double *dor = c->dov + r * d;
+            /* forward pieces: g, u, a, o */
+            const size_t in_base = (size_t)e * d * f;
+            for (int n = 0; n < f; ++n) { g[n] = 0.0; u[n] = 0.0; }
+            for (int j = 0; j < d; ++j) {
+                const size_t row = in_base + (size_t)j * f;
+                for (int n = 0; n < f; ++n) {
+                    g[n] += xr[j] * load_elem(c->w1, c->dtype, row + n);
+                    u[n] += xr[j] * load_elem(c->w3, c->dtype, row + n);
+                }
+            }
+            for (int n = 0; n < f; ++n) ar[n] = u[n] * g[n] * (1.0 / (1.0 + exp(-g[n])));
+            const size_t out_base = (size_t)e * f * d;
+            for (int m = 0; m < d; ++m) o[m] = 0.0;
+            for (int n = 0; n < f; ++n) {
+                const size_t row = out_base + (size_t)n * d;
+                for (int m = 0; m < d; ++m) o[m] += ar[n] * load_elem(c->w2, c->dtype, row + m);
+            }
+            /* dw_s, do_s */
+            double acc = 0.0;
+            for (int m = 0; m < d; ++m) acc += dyt[m] * o[m];
+            dws[s] = acc;
+            for (int m = 0; m < d; ++m) dor[m] = wt[s] * dyt[m];
+            /* da = do W2[e]^T */
+            for (int n = 0; n < f; ++n) {
+                const size_t row = out_base + (size_t)n * d;
+                double v = 0.0;
+                for (int m = 0; m < d; ++m) v += dor[m] * load_elem(c->w2, c->dtype, row + m);
+                da[n] = v;
+            }
+            /* dg, du */
+            for (int n = 0; n < f; ++n) {
+                const double sg = 1.0 / (1.0 + exp(-g[n]));
+                dgr[n] = da[n] * u[n] * sg * (1.0 + g[n] * (1.0 - sg));
+                dur[n] = da[n] * g[n] * sg;
+            }
+            /* dx += dg W1[e]^T + du W3[e]^T */
+            for (int j = 0; j < d; ++j) {
+                const size_t row = in_base + (size_t)j * f;
+                double v = 0.0;
+                for (int n = 0; n < f; ++n)
+                    v += dgr[n] * load_elem(c->w1, c->dtype, row + n) +
+                         dur[n] * load_elem(c->w3, c->dtype, row + n);
+                dxt[j] += v;
+            }
+        }
+        /* router: softmax Jacobian over the picked logits */
+        double mean = 0.0;
+        for (int s = 0; s < k; ++s) mean += wt[s] * dws[s];
+        double *dlt = c->dl + (size_t)t * E;
+        for (int e = 0; e < E; ++e) dlt[e] = 0.0;
+        for (int s = 0; s < k; ++s) dlt[it[s]] = wt[s] * (dws[s] - mean);
+        for (int j = 0; j < d; ++j) {
+            double v = 0.0;
+            for (int e = 0; e < E; ++e) v += dlt[e] * load_elem(c->wg, c->dtype, (size_t)j * E + e);
+            dxt[j] += v;
+        }
+    }
+out:
+    free(xr); free(g); free(u); free(o); free(da);
+}
+
+typedef struct {
+    const bwd_ctx *c;
+    double *dwg, *dw1, *dw3, *dw2;
+} bwd_w_ctx;
+
+/* Weight gradients, one (expert, input row) of each matrix per item:
+ * items [0, E*d) are rows j of dW1[e] / dW3[e], items [E*d, E*d + E*f) rows
+ * n of dW2[e], items past that rows j of dWg.  Each sums over tokens in
+ * order, then slots. */
+static void bwd_weight_range(void *p, int lo, int hi) {
+    const bwd_w_ctx *wc = (const bwd_w_ctx *)p;
+    const bwd_ctx *c = wc->c;
+    const int d = c->d, f = c->f, E = c->E, k = c->k, T = c->T;
+    for (int item = lo; item < hi; ++item) {
+        if (item < E * d) {
+            const int e = item / d, j = item % d;
+            double *r1 = wc->dw1 + ((size_t)e * d + j) * f, *r3 = wc->dw3 + ((size_t)e * d + j) * f;
+            for (int n = 0; n < f; ++n) { r1[n] = 0.0; r3[n] = 0.0; }
+            for (int t = 0; t < T; ++t)
+                for (int s = 0; s < k; ++s) {
+                    if (c->idx[(size_t)k * t + s] != e) continue;
+                    const double xj = load_elem(c->x, c->dtype, (size_t)t * d + j);
+                    const size_t r = (size_t)k * t + s;
+                    for (int n = 0; n < f; ++n) {
+                        r1[n] += xj * c->dg[r * f + n];
+                        r3[n] += xj * c->du[r * f + n];
+                    }
+                }
+        } else if (item < E * d + E * f) {
+            const int it2 = item - E * d, e = it2 / f, n = it2 % f;
+            double *r2 = wc->dw2 + ((size_t)e * f + n) * d;
+            for (int m = 0; m < d; ++m) r2[m] = 0.0;
+            for (int t = 0; t < T; ++t)
+                for (int s = 0; s < k; ++s) {
+                    if (c->idx[(size_t)k * t + s] != e) continue;
+                    const size_t r = (size_t)k * t + s;
+                    const double an = c->a[r * f + n];
+                    for (int m = 0; m < d; ++m) r2[m] += an * c->dov[r * d + m];
+                }
+        } else {
+            const int j = item - E * d - E * f;
+            double *rg = wc->dwg + (size_t)j * E;
+            for (int e = 0; e < E; ++e) rg[e] = 0.0;
+            for (int t = 0; t < T; ++t) {
+                const double xj = load_elem(c->x, c->dtype, (size_t)t * d + j);
+                for (int e = 0; e < E; ++e) rg[e] += xj * c->dl[(size_t)t * E + e];
+            }
+        }
+    }
+}
+
+/* Gradients of L = sum(dy * y) for the layer: dx [T,d], dwg [d,E], dw1 and
+ * dw3 [E,d,f], dw2 [E,f,d] (all fp64), plus the routing (idx, w).  Returns
+ * 0, -1 on bad sizes, -2 when out of memory. */
+int oracle_backward(int T, int d, int f, int E, int k, const void *x, const void *wg,
+                    const void *w1, const void *w3, const void *w2, int dtype, const double *dy,
+                    double *dx, double *dwg, double *dw1, double *dw3, double *dw2,
+                    int32_t *idx, double *w, int threads) {
+    if (T < 0 || d < 1 || f < 1 || E < 1 || E > 256 || k < 1 || k > ORC_MAX_K || k > E)
+        return -1;
+    const size_t R = (size_t)T * k;
+    double *dl = calloc((size_t)T * E + 1, sizeof(double));
+    double *a = malloc(sizeof(double) * (R * f + 1));
+    double *dg = malloc(sizeof(double) * (R * f + 1));
+    double *du = malloc(sizeof(double) * (R * f + 1));
+    double *dov = malloc(sizeof(double) * (R * d + 1));
+    int rc = 0;
+    if (!dl || !a || !dg || !du || !dov) { rc = -2; goto out; }
+    bwd_ctx c = {T, d, f, E, k, dtype, x, wg, w1, w3, w2, dy, idx, w, dx, dl, a, dg, du, dov};
+    parallel_for(T, threads, bwd_token_range, &c);
+    bwd_w_ctx wc = {&c, dwg, dw1, dw3, dw2};
+    parallel_for(E * d + E * f + d, threads, bwd_weight_range, &wc);
+out:
+    free(dl); free(a); free(dg); free(du); free(dov);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------
  * Weight-only int8 expert weights.
  *
  * The pages name weight-only int8 loading for this model (the KerasFormers

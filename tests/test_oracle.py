@@ -496,6 +496,70 @@ def pin_forward_w8_power_of_two_scales():
                                   oracle.expert_down(hid, ex, w2))
 
 
+def _loss(inp_tensors, dy, k):
+    x, wg, w1, w3, w2 = inp_tensors
+    y, idx, _ = oracle.forward(x, wg, w1, w3, w2, top_k=k, threads=1)
+    return float((y * dy).sum()), idx
+
+
+def pin_backward_finite_differences():
+    """Every gradient against central differences of the oracle's forward:
+    L = sum(y * dy), perturbation h = 2^-14 (exact in fp32 for these
+    values), elements whose perturbation changes the top-k picks skipped.
+    The finite differences share no arithmetic with the backward's
+    formulas."""
+    rng = np.random.default_rng(61)
+    h = 2.0 ** -14
+    names = ("dx", "dw_gate", "dw1", "dw3", "dw2")
+    for k, E in ((2, 4), (1, 4), (3, 5)):
+        wl = W.small_workload(6, 16, 12, E=E, dtype=W.F32, seed=60 + k)
+        inp = W.make_inputs(wl)
+        ts = [inp.x.clone(), inp.w_gate.clone(), inp.w1.clone(), inp.w3.clone(), inp.w2.clone()]
+        dy = rng.standard_normal((6, 16))
+        grads = oracle.backward(*ts, dy, top_k=k, threads=1)
+        _, idx0 = _loss(ts, dy, k)
+        for ti, name in enumerate(names):
+            flat = ts[ti].view(-1)
+            checked = 0
+            for pos in rng.permutation(flat.numel())[:12]:
+                v = float(flat[pos])
+                flat[pos] = v + h
+                lp, ip = _loss(ts, dy, k)
+                flat[pos] = v - h
+                lm, im = _loss(ts, dy, k)
+                flat[pos] = v
+                if not (np.array_equal(ip, idx0) and np.array_equal(im, idx0)):
+                    continue
+                fd = (lp - lm) / (2 * h)
+                g = grads[name].reshape(-1)[pos]
+                assert abs(fd - g) <= 1e-5 * max(1.0, abs(g)), (k, name, pos, fd, g)
+                checked += 1
+            assert checked >= 6, (k, name, checked)
+        if k == 1:   # one pick: its weight is exactly 1, the router gets nothing
+            np.testing.assert_array_equal(grads["dw_gate"], 0.0)
+
+
+def pin_backward_special_cases():
+    """Identical experts make y independent of the router: dw_gate is zero
+    (up to rounding).  Doubling dy doubles every gradient exactly.  Top-1
+    with one expert per token: dx equals the single expert's gradient."""
+    inp = _rand_layer(T=10, d=16, f=24, seed=93, dtype=W.F32)
+    dy = np.random.default_rng(3).standard_normal((10, 16))
+    same = lambda m: m[:1].expand_as(m).contiguous()
+    g = oracle.backward(inp.x, inp.w_gate, same(inp.w1), same(inp.w3), same(inp.w2), dy,
+                        top_k=3)
+    assert np.abs(g["dw_gate"]).max() <= 1e-12 * np.abs(g["dw1"]).max()
+    g1 = oracle.backward(inp.x, inp.w_gate, inp.w1, inp.w3, inp.w2, dy)
+    g2 = oracle.backward(inp.x, inp.w_gate, inp.w1, inp.w3, inp.w2, 2 * dy)
+    for name in ("dx", "dw_gate", "dw1", "dw3", "dw2"):
+        np.testing.assert_array_equal(g2[name], 2 * g1[name])
+    # experts never picked get zero weight gradients
+    picked = np.unique(g1["idx"])
+    for e in range(8):
+        if e not in picked:
+            assert not g1["dw1"][e].any() and not g1["dw2"][e].any()
+
+
 PINS = [pin_worked_examples, pin_logits_match_numpy, pin_top2_brute_force,
         pin_weights_closed_form_and_page_form, pin_forward_matches_numpy_dense,
         pin_expert_rows_match_numpy, pin_identical_experts_equal_dense_swiglu,
@@ -503,7 +567,8 @@ PINS = [pin_worked_examples, pin_logits_match_numpy, pin_top2_brute_force,
         pin_expert_relabelling_and_token_permutation, pin_dispatch_is_stable_grouping,
         pin_rmsnorm_closed_forms, pin_rmsnorm_invariants, pin_block_identities,
         pin_topk_brute_force_and_special_weights, pin_topk_layer_special_cases,
-        pin_route_probs_page_form, pin_quantize_int8, pin_forward_w8_power_of_two_scales]
+        pin_route_probs_page_form, pin_quantize_int8, pin_forward_w8_power_of_two_scales,
+        pin_backward_finite_differences, pin_backward_special_cases]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -560,6 +625,14 @@ MUTANTS = {
                               "for (int m = 0; m < d; ++m) o[m] *= 1.0;"),
     "w8_gate_takes_up_scale": ("const double gn = (double)c->s1[(size_t)e * f + n] * g[n];",
                                "const double gn = (double)c->s3[(size_t)e * f + n] * g[n];"),
+    "bwd_silu_grad_sign": ("(1.0 + g[n] * (1.0 - sg))", "(1.0 - g[n] * (1.0 - sg))"),
+    "bwd_jacobian_mean_dropped": ("dlt[it[s]] = wt[s] * (dws[s] - mean);",
+                                  "dlt[it[s]] = wt[s] * dws[s];"),
+    "bwd_dw2_uses_gate_grad": ("const double an = c->a[r * f + n];",
+                               "const double an = c->dg[r * f + n];"),
+    "bwd_router_dx_transposed": ("v += dlt[e] * load_elem(c->wg, c->dtype, (size_t)j * E + e);",
+                                 "v += dlt[e] * load_elem(c->wg, c->dtype, (size_t)e * d + j);"),
+    "bwd_up_grad_without_silu": ("dur[n] = da[n] * g[n] * sg;", "dur[n] = da[n] * sg;"),
     "norm_sum_not_mean": ("sqrt(ss / (double)c->d + c->eps)", "sqrt(ss + c->eps)"),
     "norm_no_sqrt": ("sqrt(ss / (double)c->d + c->eps)", "(ss / (double)c->d + c->eps)"),
     "norm_eps_outside": ("1.0 / sqrt(ss / (double)c->d + c->eps)",
