@@ -253,6 +253,36 @@ int moe_forward_w8(const moe_shape_t *shape, const void *x, const void *w_gate,
                    const int8_t *q2, const float *s2, void *y, int32_t *topk_idx_opt,
                    float *topk_w_opt, void *ws, size_t ws_bytes, void *stream);
 
+/* ---- Backward ------------------------------------------------------------
+ * The pages train the router and the experts together ("Mixtral 8x7B --
+ * The Evolving Transformer", section 05) and name no loss, capacity or
+ * auxiliary term. moe_backward therefore returns the gradients of
+ * L = sum(dy * y), with y the layer's forward output and dy [T, d] given in
+ * the layer dtype. The top-k picks are a discrete choice and stay fixed;
+ * the router's gradient flows through the softmax over the picked logits:
+ *   dw_s = dy . o_s,  dl[e] = w_s (dw_s - sum_r w_r dw_r) at the picked e
+ *   do_s = w_s dy,    da = do_s W2[e]^T
+ *   dg = da * u * silu'(g),  du = da * silu(g)
+ *   dx = sum_s (dg W1[e]^T + du W3[e]^T) + dl w_gate^T     (layer dtype)
+ *   dw1[e] = sum over e's rows of x^T dg,  dw3[e] likewise with du,
+ *   dw2[e] = sum over e's rows of h^T do,  dw_gate = x^T dl  (all fp32)
+ * The call recomputes the forward pieces it needs (routing, g, u,
+ * h = silu(g) u, o), so nothing has to be kept between calls. With
+ * MOE_BF16, h, do, dg and du are rounded to bf16 before the products that
+ * use them. Every product accumulates in fp32 on the matrix cores, and
+ * every sum has a fixed order (no atomics).
+ *
+ * Outputs: dx [T, d] (layer dtype); dw_gate [d, E], dw1 and dw3 [E, d, f],
+ * dw2 [E, f, d], all fp32 and overwritten. An expert no token picked gets
+ * zero gradients. T = 0 writes zero weight gradients (x, dy and dx may
+ * then be NULL). Outputs must not
+ * overlap the inputs, each other or the workspace. ws / ws_bytes: at least
+ * moe_backward_workspace_bytes(shape), which is 0 for an invalid shape. */
+size_t moe_backward_workspace_bytes(const moe_shape_t *shape);
+int moe_backward(const moe_shape_t *shape, const void *x, const void *w_gate, const void *w1,
+                 const void *w3, const void *w2, const void *dy, void *dx, float *dw_gate,
+                 float *dw1, float *dw3, float *dw2, void *ws, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,7 +29,8 @@ EXPORTED = ["moe_status_str", "moe_workspace_bytes", "moe_route", "moe_route_pro
             "moe_dispatch",
             "moe_expert_gateup", "moe_expert_down", "moe_experts", "moe_combine",
             "moe_forward", "moe_rmsnorm_route", "moe_block_forward", "moe_quantize_int8",
-            "moe_expert_gateup_w8", "moe_expert_down_w8", "moe_forward_w8"]
+            "moe_expert_gateup_w8", "moe_expert_down_w8", "moe_forward_w8",
+            "moe_backward_workspace_bytes", "moe_backward"]
 
 
 class MoeShape(ctypes.Structure):
@@ -92,6 +93,10 @@ def load_library(path: Optional[str] = None):
     lib.moe_expert_down_w8.restype = I
     lib.moe_forward_w8.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
     lib.moe_forward_w8.restype = I
+    lib.moe_backward_workspace_bytes.argtypes = [S]
+    lib.moe_backward_workspace_bytes.restype = Z
+    lib.moe_backward.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
+    lib.moe_backward.restype = I
     if path is None:
         _lib = lib
     return lib
@@ -510,3 +515,47 @@ def forward_w8(x: torch.Tensor, w_gate: torch.Tensor, q1: torch.Tensor, s1: torc
                                        _stream(x.device))
     _check(st, "moe_forward_w8")
     return (y, idx, w) if return_routing else y
+
+
+# ---------------------------------------------------------------------------
+# Backward.
+
+def backward_workspace_bytes(T: int, d: int, f: int, E: int, dtype, top_k: int = 2) -> int:
+    shape = make_shape(T, d, f, E, dtype, top_k)
+    return int(load_library().moe_backward_workspace_bytes(ctypes.byref(shape)))
+
+
+def backward(x: torch.Tensor, w_gate: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor,
+             w2: torch.Tensor, dy: torch.Tensor, top_k: int = 2,
+             workspace: Optional[torch.Tensor] = None):
+    """Gradients of sum(dy * forward(x, ...)): returns (dx [T, d] in x's
+    dtype, dw_gate [d, E], dw1 [E, d, f], dw3 [E, d, f], dw2 [E, f, d], all
+    fp32)."""
+    _need(x, "x")
+    T, d = x.shape
+    _need(w_gate, "w_gate", x.dtype, x.device)
+    E = w_gate.shape[1]
+    _need(w_gate, "w_gate", shape=(d, E))
+    _need(w1, "w1", x.dtype, x.device)
+    f = w1.shape[2]
+    _need(w1, "w1", shape=(E, d, f))
+    _need(w3, "w3", x.dtype, x.device, (E, d, f))
+    _need(w2, "w2", x.dtype, x.device, (E, f, d))
+    _need(dy, "dy", x.dtype, x.device, (T, d))
+    n = backward_workspace_bytes(T, d, f, E, x.dtype, top_k)
+    if n == 0:
+        raise ValueError("invalid layer shape")
+    ws = workspace if workspace is not None else torch.empty(n, dtype=torch.uint8,
+                                                             device=x.device)
+    dev = x.device
+    dx = torch.empty_like(x)
+    dwg = torch.empty(d, E, dtype=torch.float32, device=dev)
+    dw1 = torch.empty(E, d, f, dtype=torch.float32, device=dev)
+    dw3 = torch.empty(E, d, f, dtype=torch.float32, device=dev)
+    dw2 = torch.empty(E, f, d, dtype=torch.float32, device=dev)
+    shape = make_shape(T, d, f, E, x.dtype, top_k)
+    st = load_library().moe_backward(ctypes.byref(shape), _ptr(x), _ptr(w_gate), _ptr(w1),
+                                     _ptr(w3), _ptr(w2), _ptr(dy), _ptr(dx), _ptr(dwg), _ptr(dw1),
+                                     _ptr(dw3), _ptr(dw2), _ptr(ws), ws.numel(), _stream(dev))
+    _check(st, "moe_backward")
+    return dx, dwg, dw1, dw3, dw2

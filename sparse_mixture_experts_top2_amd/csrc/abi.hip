@@ -443,4 +443,44 @@ int moe_forward_w8(const moe_shape_t *s, const void *x, const void *w_gate, cons
     return hip_status(e);
 }
 
+// ---- Backward --------------------------------------------------------------
+
+size_t moe_backward_workspace_bytes(const moe_shape_t *s) {
+    if (check_shape(s) != MOE_OK) return 0;
+    return plan_backward(*s).total;
+}
+
+int moe_backward(const moe_shape_t *s, const void *x, const void *w_gate, const void *w1,
+                 const void *w3, const void *w2, const void *dy, void *dx, float *dw_gate,
+                 float *dw1, float *dw3, float *dw2, void *ws, size_t ws_bytes, void *stream) {
+    int st = check_shape(s);
+    if (st) return st;
+    // With T = 0, x, dy and dx hold nothing and may be NULL; the weight
+    // gradients are still written (as zeros).
+    if (!w_gate || !w1 || !w3 || !w2 || !dw_gate || !dw1 || !dw3 || !dw2) return MOE_ERR_NULL;
+    if (s->T > 0 && (!x || !dy || !dx)) return MOE_ERR_NULL;
+    const void *ptrs[] = {x, w_gate, w1, w3, w2, dy, dx, dw_gate, dw1, dw3, dw2};
+    for (const void *p : ptrs)
+        if (misaligned(p)) return MOE_ERR_ALIGN;
+    const BackwardLayout L = plan_backward(*s);
+    if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    if (misaligned(ws)) return MOE_ERR_ALIGN;
+    const size_t eb = elem_bytes(s->dtype), T = (size_t)s->T, d = (size_t)s->d_model;
+    const size_t f = (size_t)s->d_ff, E = (size_t)s->n_experts;
+    const void *in[] = {x, w_gate, w1, w3, w2, dy};
+    const size_t inb[] = {T * d * eb, d * E * eb, E * d * f * eb, E * d * f * eb, E * f * d * eb,
+                          T * d * eb};
+    const void *out[] = {dx, dw_gate, dw1, dw3, dw2};
+    const size_t outb[] = {T * d * eb, d * E * 4, E * d * f * 4, E * d * f * 4, E * f * d * 4};
+    for (int i = 0; i < 5; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlap(out[i], outb[i], in[j], inb[j])) return MOE_ERR_ALIAS;
+        for (int j = i + 1; j < 5; ++j)
+            if (overlap(out[i], outb[i], out[j], outb[j])) return MOE_ERR_ALIAS;
+        if (overlap(out[i], outb[i], ws, L.total)) return MOE_ERR_ALIAS;
+    }
+    return hip_status(launch_backward(*s, x, w_gate, w1, w3, w2, dy, dx, dw_gate, dw1, dw3, dw2,
+                                      L, static_cast<char *>(ws), (hipStream_t)stream));
+}
+
 }  // extern "C"

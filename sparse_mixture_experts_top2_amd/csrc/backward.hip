@@ -1,0 +1,537 @@
+// Backward of the layer: gradients of L = sum(dy * y) with respect to x,
+// the router and the three expert matrices.  The pages train router and
+// experts jointly ("Mixtral 8x7B -- The Evolving Transformer", section 05,
+// and the remark that they are trained together) and specify no loss,
+// capacity or auxiliary term, so this is the gradient of the forward as
+// written, with the top-k picks held fixed (a discrete choice):
+//
+//   dw_s = dy . o_s,   dl_e = w_s (dw_s - sum_r w_r dw_r) at the picked e
+//   do_s = w_s dy,     da = do_s W2[e]^T
+//   dg = da * u * silu'(g),   du = da * silu(g)
+//   dx = sum_s (dg W1[e]^T + du W3[e]^T) + dl Wg^T
+//   dW1[e] = X_e^T dG_e,  dW3[e] = X_e^T dU_e,  dW2[e] = H_e^T dO_e,
+//   dWg = x^T dl
+//
+// The call recomputes what it needs of the forward (routing, grouped rows,
+// g, u, h = silu(g) u and the expert outputs o) rather than keeping state
+// between calls.  All products run on the matrix cores through one grouped
+// GEMM template (bf16: 32x32x16 MFMA, fp32: 32x32x2 MFMA) that takes each
+// operand either K-contiguous (read as is) or M/N-contiguous (transposed in
+// registers on its way into LDS), grouped either by rows (every expert's
+// rows times its own matrix) or by K (every expert's matrix reduced over
+// its rows), with fused epilogues for the SwiGLU forward and derivative.
+// Every sum has a fixed order; there are no atomics.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+__device__ __forceinline__ float to_f32(uint16_t v) { return bf16_to_f32(v); }
+__device__ __forceinline__ float to_f32(float v) { return v; }
+template <typename T>
+__device__ __forceinline__ T from_f32(float v);
+template <>
+__device__ __forceinline__ uint16_t from_f32<uint16_t>(float v) {
+    return (uint16_t)f32_to_bf16(v);
+}
+template <>
+__device__ __forceinline__ float from_f32<float>(float v) { return v; }
+
+__device__ __forceinline__ float sigmoid_f32(float g) { return 1.0f / (1.0f + expf(-g)); }
+
+constexpr int GBM = 128, GBN = 128, GBK = 32;   // tile and K step
+enum { OP_KC = 0, OP_MNC = 1 };                 // operand K-contiguous or M/N-contiguous
+enum { GROUP_ROWS = 0, GROUP_K = 1 };
+enum { EPI_STORE = 0, EPI_ADD = 1, EPI_UP = 2, EPI_DSWIGLU = 3 };
+
+// Operands of one grouped GEMM, strides in elements.
+//   A element (m, k): KC  -> A + m * lda + k;   MNC -> A + k * lda + m
+//   B element (k, n): KC  -> B_e + n * ldb + k; MNC -> B_e + k * ldb + n
+//   with B_e = B + e * b_estride.
+//   GROUP_ROWS: m runs over the routed rows (global), grouped by expert;
+//     the tile's expert selects B.  C + m * ldc + n.
+//   GROUP_K: m, n run over the whole M x N output of expert e, and k over
+//     the expert's rows [offsets[e], offsets[e] + counts[e]).
+//     C + e * c_estride + m * ldc + n.
+// Epilogues (C fp32 unless stated):
+//   EPI_STORE   C = acc
+//   EPI_ADD     C += acc
+//   EPI_UP      C = u = acc; C2 (layer dtype) = silu(G) * u       (G at C's index)
+//   EPI_DSWIGLU with da = acc, g = G, u = U at C's index:
+//               C (layer dtype) = da * u * silu'(g), C2 (layer dtype) = da * silu(g)
+struct GemmArgs {
+    const void *A;
+    long long lda;
+    const void *B;
+    long long ldb, b_estride;
+    void *C;
+    long long ldc, c_estride;
+    void *C2;
+    const float *G, *U;
+    const int32_t *counts, *offsets;
+    int E, M, N, K;
+};
+
+// r[i] holds row i of an 8 x 8 bf16 block (8 values along M/N, two per
+// dword, the lower index in the low half); out[c] receives column c: 8
+// values along K, row 0 in the low half of dword 0.
+__device__ __forceinline__ void transpose_b16(const uint4 (&r)[8], uint4 (&out)[8]) {
+    const uint32_t *w = reinterpret_cast<const uint32_t *>(r);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const int p = c >> 1;
+        uint32_t q[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t lo = w[4 * (2 * j) + p], hi = w[4 * (2 * j + 1) + p];
+            q[j] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+        }
+        out[c] = make_uint4(q[0], q[1], q[2], q[3]);
+    }
+}
+
+// The same for a 4 x 4 block of fp32.
+__device__ __forceinline__ void transpose_b32(const uint4 (&r)[4], uint4 (&out)[4]) {
+    out[0] = make_uint4(r[0].x, r[1].x, r[2].x, r[3].x);
+    out[1] = make_uint4(r[0].y, r[1].y, r[2].y, r[3].y);
+    out[2] = make_uint4(r[0].z, r[1].z, r[2].z, r[3].z);
+    out[3] = make_uint4(r[0].w, r[1].w, r[2].w, r[3].w);
+}
+
+template <typename T>
+struct OperandLoader;
+
+// 128 x 32 tile of one operand, staged through registers into LDS as 128
+// lines of 32 K values (pitch PITCH elements).
+template <typename T, int LAYOUT>
+struct TileLoad {
+    static constexpr int V = 16 / (int)sizeof(T);          // elements per 16 bytes
+    static constexpr int PITCH = GBK + V;                   // LDS line pitch
+    // KC: 128 lines x (32 / V) vectors; MNC: (32 / V) x (128 / V) blocks of V x V.
+    static constexpr int NKC = 128 * GBK / V / 256;         // vectors per thread (KC)
+    static constexpr int NBLK = (GBK / V) * (128 / V);      // blocks (MNC)
+    uint4 r[LAYOUT == OP_KC ? NKC : V];
+
+    // base points at element (line 0 of the tile, k = 0) for KC (lines are
+    // ld apart; line index clamped to line_lim - 1), or at element (k = 0,
+    // mn = 0) of the whole operand for MNC (k rows are ld apart; k valid in
+    // [k_lo, k_hi), mn valid below mn_lim).
+    __device__ __forceinline__ void load(const T *base, long long ld, int line0, int line_lim,
+                                         int k0, int k_hi, int k_lo, int mn0, int mn_lim) {
+        const int tid = threadIdx.x;
+        if constexpr (LAYOUT == OP_KC) {
+#pragma unroll
+            for (int i = 0; i < NKC; ++i) {
+                const int v = tid + 256 * i;
+                const int line = v / (GBK / V), kv = v % (GBK / V);
+                const int k = k0 + kv * V;
+                const T *p = base + (long long)min(line0 + line, line_lim - 1) * ld + k;
+                r[i] = k < k_hi ? *reinterpret_cast<const uint4 *>(p) : make_uint4(0, 0, 0, 0);
+            }
+        } else {
+            if (tid < NBLK) {
+                const int kb = tid % (GBK / V), mb = tid / (GBK / V);
+                const int mn = mn0 + mb * V;
+#pragma unroll
+                for (int i = 0; i < V; ++i) {
+                    const int k = k0 + kb * V + i;
+                    const bool ok = k >= k_lo && k < k_hi && mn < mn_lim;
+                    r[i] = ok ? *reinterpret_cast<const uint4 *>(base + (long long)k * ld + mn)
+                              : make_uint4(0, 0, 0, 0);
+                }
+            }
+        }
+    }
+    __device__ __forceinline__ void store(T *s) {
+        const int tid = threadIdx.x;
+        if constexpr (LAYOUT == OP_KC) {
+#pragma unroll
+            for (int i = 0; i < NKC; ++i) {
+                const int v = tid + 256 * i;
+                const int line = v / (GBK / V), kv = v % (GBK / V);
+                *reinterpret_cast<uint4 *>(s + line * PITCH + kv * V) = r[i];
+            }
+        } else {
+            if (tid < NBLK) {
+                const int kb = tid % (GBK / V), mb = tid / (GBK / V);
+                uint4 t[V];
+                if constexpr (V == 8) transpose_b16(r, t);
+                else transpose_b32(r, t);
+#pragma unroll
+                for (int c = 0; c < V; ++c)
+                    *reinterpret_cast<uint4 *>(s + (mb * V + c) * PITCH + kb * V) = t[c];
+            }
+        }
+    }
+};
+
+// One 128 x 128 output tile per workgroup, 4 wavefronts (2 x 2) of 64 x 64,
+// K step 32, LDS double-buffered through registers.
+template <typename T, int AL, int BL, int GROUP, int EPI>
+__global__ __launch_bounds__(256) void bwd_gemm_kernel(GemmArgs p) {
+    using LA = TileLoad<T, AL>;
+    using LB = TileLoad<T, BL>;
+    constexpr int PITCH = LA::PITCH;
+    __shared__ __attribute__((aligned(16))) T sA[2][GBM * PITCH];
+    __shared__ __attribute__((aligned(16))) T sB[2][GBN * PITCH];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    int e, m0, m_end, n0, k_lo, k_hi;
+    if constexpr (GROUP == GROUP_ROWS) {
+        const int n_tiles = (p.N + GBN - 1) / GBN;
+        const int mt = blockIdx.x / n_tiles, nt = blockIdx.x % n_tiles;
+        if (!find_row_tile(p.counts, p.offsets, p.E, GBM, mt, e, m0, m_end)) return;
+        n0 = nt * GBN;
+        k_lo = 0;
+        k_hi = p.K;
+    } else {
+        const int m_tiles = (p.M + GBM - 1) / GBM, n_tiles = (p.N + GBN - 1) / GBN;
+        e = blockIdx.x / (m_tiles * n_tiles);
+        const int rem = blockIdx.x % (m_tiles * n_tiles);
+        m0 = (rem / n_tiles) * GBM;
+        n0 = (rem % n_tiles) * GBN;
+        m_end = p.M;
+        k_lo = p.offsets[e];
+        k_hi = k_lo + p.counts[e];
+    }
+    const T *A = static_cast<const T *>(p.A);
+    const T *B = static_cast<const T *>(p.B) + (GROUP == GROUP_ROWS ? (long long)e * p.b_estride : 0);
+
+    LA la;
+    LB lb;
+    auto gload = [&](int k0) {
+        if constexpr (AL == OP_KC)
+            la.load(A, p.lda, m0, GROUP == GROUP_ROWS ? p.M : m_end, k0, k_hi, k_lo, 0, 0);
+        else
+            la.load(A, p.lda, 0, 0, k0, k_hi, k_lo, m0, GROUP == GROUP_ROWS ? p.M : m_end);
+        if constexpr (BL == OP_KC)
+            lb.load(B, p.ldb, n0, p.N, k0, k_hi, k_lo, 0, 0);
+        else
+            lb.load(B, p.ldb, 0, 0, k0, k_hi, k_lo, n0, p.N);
+    };
+
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+    const int nk = (k_hi - k_lo + GBK - 1) / GBK;
+    if (nk > 0) {
+        gload(k_lo);
+        la.store(sA[0]);
+        lb.store(sB[0]);
+        __syncthreads();
+    }
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < nk) gload(k_lo + (kt + 1) * GBK);
+        const T *As = sA[cur], *Bs = sB[cur];
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int kk = 0; kk < GBK; kk += 16) {
+                const int koff = kk + (lane >> 5) * 8;
+                bf16x8_t af[2], bfr[2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    af[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(
+                        &As[(wm * 64 + i * 32 + (lane & 31)) * PITCH + koff]));
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    bfr[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(
+                        &Bs[(wn * 64 + j * 32 + (lane & 31)) * PITCH + koff]));
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j],
+                                                                             acc[i][j], 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < GBK; kk += 2) {
+                const int koff = kk + (lane >> 5);
+                float af[2], bfr[2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) af[i] = As[(wm * 64 + i * 32 + (lane & 31)) * PITCH + koff];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) bfr[j] = Bs[(wn * 64 + j * 32 + (lane & 31)) * PITCH + koff];
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i], bfr[j], acc[i][j],
+                                                                         0, 0, 0);
+            }
+        }
+        if (kt + 1 < nk) {
+            la.store(sA[cur ^ 1]);
+            lb.store(sB[cur ^ 1]);
+        }
+        __syncthreads();
+    }
+
+    // Epilogue.  32x32 accumulator layout: value q of lane l is row
+    // 8*(q/4) + 4*(l/32) + q%4, column l%32 of the block.
+    const long long cbase = GROUP == GROUP_K ? (long long)e * p.c_estride : 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+            if (col >= p.N) continue;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int row = m0 + wm * 64 + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                if (row >= m_end) continue;
+                const long long ci = cbase + (long long)row * p.ldc + col;
+                const float v = acc[i][j][q];
+                if constexpr (EPI == EPI_STORE) {
+                    static_cast<float *>(p.C)[ci] = v;
+                } else if constexpr (EPI == EPI_ADD) {
+                    static_cast<float *>(p.C)[ci] += v;
+                } else if constexpr (EPI == EPI_UP) {
+                    const float g = p.G[ci];
+                    static_cast<float *>(p.C)[ci] = v;
+                    static_cast<T *>(p.C2)[ci] = from_f32<T>(g * sigmoid_f32(g) * v);
+                } else {
+                    const float g = p.G[ci], u = p.U[ci], sg = sigmoid_f32(g);
+                    static_cast<T *>(p.C)[ci] = from_f32<T>(v * u * sg * (1.0f + g * (1.0f - sg)));
+                    static_cast<T *>(p.C2)[ci] = from_f32<T>(v * g * sg);
+                }
+            }
+        }
+}
+
+// One workgroup per token t: for each slot s with row r = pos[t, s],
+//   dw_s = sum_i dy[t, i] o[r, i]     (fixed-order block reduction)
+//   dO[r, i] = w[t, s] dy[t, i]       (layer dtype)
+// then dl[t, :] = 0 except dl[t, idx_s] = w_s (dw_s - sum_r w_r dw_r).
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_route_grad_kernel(
+    const T *__restrict__ dy, const float *__restrict__ o, const int32_t *__restrict__ idx,
+    const float *__restrict__ w, const int32_t *__restrict__ pos, int d, int E, int k,
+    T *__restrict__ dO, float *__restrict__ dl) {
+    __shared__ float part[4][kMaxTopK];
+    const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    float dws[kMaxTopK];
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) {
+        if (s >= k) break;
+        const int r = pos[k * t + s];
+        const float ws = w[k * t + s];
+        float acc = 0.0f;
+        for (int i = tid; i < d; i += 256) {
+            const float g = to_f32(dy[(size_t)t * d + i]);
+            acc += g * o[(size_t)r * d + i];
+            dO[(size_t)r * d + i] = from_f32<T>(ws * g);
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+        if (lane == 0) part[wave][s] = acc;
+    }
+    __syncthreads();
+    if (tid != 0) return;
+    float mean = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) {
+        if (s >= k) break;
+        dws[s] = (part[0][s] + part[1][s]) + (part[2][s] + part[3][s]);
+        mean += w[k * t + s] * dws[s];
+    }
+    for (int e = 0; e < E; ++e) dl[(size_t)t * E + e] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) {
+        if (s >= k) break;
+        dl[(size_t)t * E + idx[k * t + s]] = w[k * t + s] * (dws[s] - mean);
+    }
+}
+
+// dx[t, i] = sum_s dXp[pos[t, s], i] (slot order) + sum_e dl[t, e] Wg[i, e],
+// rounded once to the layer dtype.  One workgroup per token.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_dx_kernel(const float *__restrict__ dxp,
+                                                     const int32_t *__restrict__ pos,
+                                                     const float *__restrict__ dl,
+                                                     const T *__restrict__ wg, int d, int E,
+                                                     int k, T *__restrict__ dx) {
+    __shared__ float dlt[kMaxExperts];
+    const int t = blockIdx.x, tid = threadIdx.x;
+    if (tid < E) dlt[tid] = dl[(size_t)t * E + tid];
+    __syncthreads();
+    int rows[kMaxTopK];
+#pragma unroll
+    for (int s = 0; s < kMaxTopK; ++s) rows[s] = s < k ? pos[k * t + s] : 0;
+    for (int i = tid; i < d; i += 256) {
+        float v = dxp[(size_t)rows[0] * d + i];
+#pragma unroll
+        for (int s = 1; s < kMaxTopK; ++s)
+            if (s < k) v += dxp[(size_t)rows[s] * d + i];
+        float r = 0.0f;
+        for (int e = 0; e < E; ++e) r += dlt[e] * to_f32(wg[(size_t)i * E + e]);
+        dx[(size_t)t * d + i] = from_f32<T>(v + r);
+    }
+}
+
+// dWg[i, e] = sum_t x[t, i] dl[t, e], t ascending; one thread per (i, e).
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_dwg_kernel(const T *__restrict__ x,
+                                                      const float *__restrict__ dl, int T_, int d,
+                                                      int E, float *__restrict__ dwg) {
+    const int id = blockIdx.x * 256 + threadIdx.x;
+    if (id >= d * E) return;
+    const int i = id / E, e = id % E;
+    float acc = 0.0f;
+    for (int t = 0; t < T_; ++t) acc += to_f32(x[(size_t)t * d + i]) * dl[(size_t)t * E + e];
+    dwg[id] = acc;
+}
+
+template <typename T, int AL, int BL, int GROUP, int EPI>
+hipError_t gemm(const GemmArgs &a, int tiles, hipStream_t stream) {
+    if (tiles <= 0) return hipSuccess;
+    hipLaunchKernelGGL((bwd_gemm_kernel<T, AL, BL, GROUP, EPI>), dim3(tiles), dim3(256), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+inline int row_tiles_bound(int rows, int E) { return (rows + GBM - 1) / GBM + E; }
+inline int tiles_of(int n) { return (n + GBN - 1) / GBN; }
+
+template <typename T>
+hipError_t run_backward_t(const moe_shape_t &s, const T *x, const T *wg, const T *w1,
+                          const T *w3, const T *w2, const T *dy, T *dx, float *dwg, float *dw1,
+                          float *dw3, float *dw2, const BackwardLayout &L, char *base,
+                          hipStream_t str) {
+    const int Tn = s.T, d = s.d_model, f = s.d_ff, E = s.n_experts, k = s.top_k;
+    const int R = routed_rows(s);
+    int32_t *idx = reinterpret_cast<int32_t *>(base + L.idx);
+    float *w = reinterpret_cast<float *>(base + L.w);
+    int32_t *counts = reinterpret_cast<int32_t *>(base + L.counts);
+    int32_t *offsets = reinterpret_cast<int32_t *>(base + L.offsets);
+    int32_t *pos = reinterpret_cast<int32_t *>(base + L.pos);
+    T *xp = reinterpret_cast<T *>(base + L.xp);
+    float *G = reinterpret_cast<float *>(base + L.g);
+    float *U = reinterpret_cast<float *>(base + L.u);
+    T *H = reinterpret_cast<T *>(base + L.h);
+    float *O = reinterpret_cast<float *>(base + L.o);      // later dXp
+    T *dO = reinterpret_cast<T *>(base + L.dout);
+    T *dG = reinterpret_cast<T *>(base + L.dg);
+    T *dU = reinterpret_cast<T *>(base + L.du);
+    float *dl = reinterpret_cast<float *>(base + L.dl);
+
+    hipError_t e = launch_route(s, x, wg, idx, w, str);
+    if (e == hipSuccess) e = launch_dispatch(s, x, idx, counts, offsets, pos, xp, str);
+    const int rt = row_tiles_bound(R, E);
+    GemmArgs a{};
+    a.counts = counts;
+    a.offsets = offsets;
+    a.E = E;
+    // g = xp W1[e], then u = xp W3[e] with h = silu(g) u
+    a.A = xp; a.lda = d; a.b_estride = (long long)d * f; a.ldb = f; a.ldc = f;
+    a.M = R; a.N = f; a.K = d;
+    a.B = w1; a.C = G;
+    if (e == hipSuccess) e = gemm<T, OP_KC, OP_MNC, GROUP_ROWS, EPI_STORE>(a, rt * tiles_of(f), str);
+    a.B = w3; a.C = U; a.C2 = H; a.G = G;
+    if (e == hipSuccess) e = gemm<T, OP_KC, OP_MNC, GROUP_ROWS, EPI_UP>(a, rt * tiles_of(f), str);
+    // o = h W2[e]
+    a = GemmArgs{};
+    a.counts = counts; a.offsets = offsets; a.E = E;
+    a.A = H; a.lda = f; a.B = w2; a.ldb = d; a.b_estride = (long long)f * d;
+    a.C = O; a.ldc = d; a.M = R; a.N = d; a.K = f;
+    if (e == hipSuccess) e = gemm<T, OP_KC, OP_MNC, GROUP_ROWS, EPI_STORE>(a, rt * tiles_of(d), str);
+    // routing-weight gradients, dO and dl
+    if (e == hipSuccess && Tn > 0) {
+        hipLaunchKernelGGL(bwd_route_grad_kernel<T>, dim3(Tn), dim3(256), 0, str, dy, O, idx, w,
+                           pos, d, E, k, dO, dl);
+        e = hipGetLastError();
+    }
+    // da = dO W2[e]^T, with dg, du in the epilogue
+    a = GemmArgs{};
+    a.counts = counts; a.offsets = offsets; a.E = E;
+    a.A = dO; a.lda = d; a.B = w2; a.ldb = d; a.b_estride = (long long)f * d;
+    a.C = dG; a.C2 = dU; a.G = G; a.U = U; a.ldc = f; a.M = R; a.N = f; a.K = d;
+    if (e == hipSuccess) e = gemm<T, OP_KC, OP_KC, GROUP_ROWS, EPI_DSWIGLU>(a, rt * tiles_of(f), str);
+    // dXp = dG W1[e]^T + dU W3[e]^T   (into the o region)
+    a = GemmArgs{};
+    a.counts = counts; a.offsets = offsets; a.E = E;
+    a.A = dG; a.lda = f; a.B = w1; a.ldb = f; a.b_estride = (long long)d * f;
+    a.C = O; a.ldc = d; a.M = R; a.N = d; a.K = f;
+    if (e == hipSuccess) e = gemm<T, OP_KC, OP_KC, GROUP_ROWS, EPI_STORE>(a, rt * tiles_of(d), str);
+    a.A = dU; a.B = w3;
+    if (e == hipSuccess) e = gemm<T, OP_KC, OP_KC, GROUP_ROWS, EPI_ADD>(a, rt * tiles_of(d), str);
+    // dx
+    if (e == hipSuccess && Tn > 0) {
+        hipLaunchKernelGGL(bwd_dx_kernel<T>, dim3(Tn), dim3(256), 0, str, O, pos, dl, wg, d, E, k,
+                           dx);
+        e = hipGetLastError();
+    }
+    // weight gradients: dW1[e] = xp_e^T dG_e, dW3[e] = xp_e^T dU_e, dW2[e] = h_e^T dO_e
+    a = GemmArgs{};
+    a.counts = counts; a.offsets = offsets; a.E = E;
+    a.A = xp; a.lda = d; a.B = dG; a.ldb = f; a.C = dw1; a.ldc = f;
+    a.c_estride = (long long)d * f; a.M = d; a.N = f;
+    const int wt13 = E * tiles_of(d) * tiles_of(f);
+    if (e == hipSuccess) e = gemm<T, OP_MNC, OP_MNC, GROUP_K, EPI_STORE>(a, wt13, str);
+    a.B = dU; a.C = dw3;
+    if (e == hipSuccess) e = gemm<T, OP_MNC, OP_MNC, GROUP_K, EPI_STORE>(a, wt13, str);
+    a.A = H; a.lda = f; a.B = dO; a.ldb = d; a.C = dw2; a.ldc = d;
+    a.c_estride = (long long)f * d; a.M = f; a.N = d;
+    if (e == hipSuccess)
+        e = gemm<T, OP_MNC, OP_MNC, GROUP_K, EPI_STORE>(a, E * tiles_of(f) * tiles_of(d), str);
+    // router gradient
+    if (e == hipSuccess) {
+        hipLaunchKernelGGL(bwd_dwg_kernel<T>, dim3((d * E + 255) / 256), dim3(256), 0, str, x, dl,
+                           Tn, d, E, dwg);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+}  // namespace
+
+BackwardLayout plan_backward(const moe_shape_t &s) {
+    auto a256 = [](size_t v) { return (v + 255) & ~(size_t)255; };
+    BackwardLayout L{};
+    const size_t T = (size_t)s.T, d = (size_t)s.d_model, f = (size_t)s.d_ff;
+    const size_t E = (size_t)s.n_experts, eb = elem_bytes(s.dtype);
+    const size_t R = (size_t)s.top_k * T;
+    size_t off = 0;
+    L.idx = off;     off += a256(R * 4);
+    L.w = off;       off += a256(R * 4);
+    L.counts = off;  off += a256(E * 4);
+    L.offsets = off; off += a256((E + 1) * 4);
+    L.pos = off;     off += a256(R * 4);
+    L.xp = off;      off += a256(R * d * eb);
+    L.g = off;       off += a256(R * f * 4);
+    L.u = off;       off += a256(R * f * 4);
+    L.h = off;       off += a256(R * f * eb);
+    L.o = off;       off += a256(R * d * 4);
+    L.dout = off;    off += a256(R * d * eb);
+    L.dg = off;      off += a256(R * f * eb);
+    L.du = off;      off += a256(R * f * eb);
+    L.dl = off;      off += a256(T * E * 4);
+    L.total = off;
+    return L;
+}
+
+hipError_t launch_backward(const moe_shape_t &s, const void *x, const void *wg, const void *w1,
+                           const void *w3, const void *w2, const void *dy, void *dx, float *dwg,
+                           float *dw1, float *dw3, float *dw2, const BackwardLayout &L,
+                           char *base, hipStream_t stream) {
+    if (s.dtype == MOE_BF16)
+        return run_backward_t<uint16_t>(
+            s, static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(wg),
+            static_cast<const uint16_t *>(w1), static_cast<const uint16_t *>(w3),
+            static_cast<const uint16_t *>(w2), static_cast<const uint16_t *>(dy),
+            static_cast<uint16_t *>(dx), dwg, dw1, dw3, dw2, L, base, stream);
+    return run_backward_t<float>(
+        s, static_cast<const float *>(x), static_cast<const float *>(wg),
+        static_cast<const float *>(w1), static_cast<const float *>(w3),
+        static_cast<const float *>(w2), static_cast<const float *>(dy), static_cast<float *>(dx),
+        dwg, dw1, dw3, dw2, L, base, stream);
+}
+
+}  // namespace moe

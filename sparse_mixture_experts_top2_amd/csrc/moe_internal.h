@@ -33,6 +33,18 @@ struct Layout {
 // Byte offsets of every workspace region for this shape (256-byte aligned).
 Layout plan_workspace(const moe_shape_t &s);
 
+// Workspace of the backward (backward.hip): routing, grouped rows xp, the
+// recomputed g, u (fp32) and h, the expert outputs o (later the per-row
+// input gradients), dO, dG, dU (layer dtype) and the router gradient dl.
+struct BackwardLayout {
+    size_t idx, w, counts, offsets, pos, xp, g, u, h, o, dout, dg, du, dl, total;
+};
+BackwardLayout plan_backward(const moe_shape_t &s);
+hipError_t launch_backward(const moe_shape_t &s, const void *x, const void *wg, const void *w1,
+                           const void *w3, const void *w2, const void *dy, void *dx, float *dwg,
+                           float *dw1, float *dw3, float *dw2, const BackwardLayout &L,
+                           char *base, hipStream_t stream);
+
 inline size_t elem_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
 // Routed rows: top_k per token.
 inline int routed_rows(const moe_shape_t &s) { return s.top_k * s.T; }

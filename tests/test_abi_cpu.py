@@ -219,3 +219,29 @@ def test_decode_workspace_holds_the_down_slices():
     lib = moe.load_library()
     s = shape(T=32, d=4096, f=14336, k=2)
     assert lib.moe_workspace_bytes(ctypes.byref(s)) >= 4 * 64 * 4096 * 4 + 64 * 14336 * 2
+
+
+def test_backward_checks():
+    lib = moe.load_library()
+    name = lambda st: moe.STATUS_NAMES[st]
+    s = shape(T=64)
+    need = lib.moe_backward_workspace_bytes(ctypes.byref(s))
+    assert need > lib.moe_workspace_bytes(ctypes.byref(s))
+    assert lib.moe_backward_workspace_bytes(ctypes.byref(shape(E=65))) == 0
+    # x, w_gate, w1, w3, w2, dy, dx, dwg, dw1, dw3, dw2 at distinct fake addresses
+    base = [ctypes.c_void_p(0x100000000 * (i + 1)) for i in range(11)]
+    ws = ctypes.c_void_p(0x2000000000)
+    B = lambda args, ws=ws, n=need: name(lib.moe_backward(ctypes.byref(s), *args, ws, n, None))
+    args = list(base)
+    bad = list(args); bad[6] = None
+    assert B(bad) == "MOE_ERR_NULL"
+    bad = list(args); bad[8] = P17
+    assert B(bad) == "MOE_ERR_ALIGN"
+    assert B(args, n=need - 1) == "MOE_ERR_WORKSPACE"
+    bad = list(args); bad[6] = base[5]            # dx over dy
+    assert B(bad) == "MOE_ERR_ALIAS"
+    bad = list(args); bad[9] = base[8]            # dw3 over dw1
+    assert B(bad) == "MOE_ERR_ALIAS"
+    assert B(args, ws=base[10]) == "MOE_ERR_ALIAS"   # workspace over dw2
+    assert name(lib.moe_backward(ctypes.byref(shape(k=5)), *args, ws, need, None)) == \
+        "MOE_ERR_UNSUPPORTED"

@@ -1,0 +1,142 @@
+"""GPU parity for the backward: every gradient of sum(dy * y) from the HIP
+library (moe_backward through its C interface) against the CPU oracle's,
+on the same seeded inputs.
+
+Bars (errors normalised by the reference's own scale: dx per token row,
+each weight gradient by its largest entry): 1e-5 for fp32 layers, 2e-2
+for bf16 layers, where h, do, dg and du are rounded to bf16 before the
+products that use them (the forward's rounding of h, applied to the
+gradients that play the same role).  With top-1 the router gradient is
+exactly zero on both sides.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_mixture_experts_top2_amd as moe
+from sparse_mixture_experts_top2_amd import workloads as W
+
+from helpers import checked_inputs, row_max_rel_err, to_f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = {W.F32: 1e-5, W.BF16: 2e-2}
+NAMES = ("dx", "dw_gate", "dw1", "dw3", "dw2")
+
+
+def announce(msg):
+    print(f"[gpu-bwd] {msg}", flush=True)
+
+
+def max_rel_err(got, ref) -> float:
+    got, ref = to_f64(got), np.asarray(ref, np.float64)
+    scale = np.abs(ref).max()
+    return float(np.abs(got - ref).max() / max(scale, 1e-30))
+
+
+def make_dy(wl, dtype):
+    gen = torch.Generator().manual_seed(wl.seed + 77)
+    dy = torch.randn(wl.T, wl.d, generator=gen)
+    return dy.to(torch.bfloat16) if dtype == W.BF16 else dy
+
+
+def run_backward_parity(inp, sample_rows=None):
+    wl = inp.wl
+    dy = make_dy(wl, wl.dtype)
+    g = inp.to(DEV)
+    grads = moe.backward(g.x, g.w_gate, g.w1, g.w3, g.w2, dy.to(DEV), top_k=wl.top_k)
+    torch.cuda.synchronize()
+    ref = oracle.backward(inp.x, inp.w_gate, inp.w1, inp.w3, inp.w2, dy, top_k=wl.top_k)
+    errs = {}
+    for name, got in zip(NAMES, grads):
+        r = ref[name]
+        errs[name] = row_max_rel_err(got, r) if name == "dx" else max_rel_err(got, r)
+    announce(f"{wl.name} " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()))
+    for name, err in errs.items():
+        assert err <= TOL[wl.dtype], (name, err)
+    return grads, ref
+
+
+sw = W.small_workload
+CASES = [
+    W.WORKLOADS["tiny_fp32"],
+    sw(40, 128, 256, seed=401),
+    sw(40, 128, 256, dtype=W.F32, seed=402),
+    sw(300, 256, 512, seed=403),                      # several row tiles per expert
+    sw(77, 200, 328, seed=404),                       # ragged tiles on every GEMM
+    sw(150, 128, 256, E=16, top_k=3, seed=405),
+    sw(90, 64, 136, E=5, top_k=4, dtype=W.F32, seed=406),
+    sw(600, 256, 384, E=32, seed=407),
+    sw(400, 192, 264, E=4, seed=408),                 # ~200 rows per expert: 2 row tiles
+    sw(400, 96, 200, E=4, dtype=W.F32, seed=409),
+]
+
+
+@pytest.mark.parametrize("wl", CASES, ids=lambda w: w.name)
+def test_backward(wl):
+    announce(f"backward {wl.name}")
+    run_backward_parity(checked_inputs(wl))
+
+
+@pytest.mark.parametrize("dtype", [W.F32, W.BF16])
+def test_top1_router_gradient_is_zero(dtype):
+    wl = sw(64, 128, 256, dtype=dtype, top_k=1, seed=410)
+    grads, ref = run_backward_parity(checked_inputs(wl))
+    assert not grads[1].any()
+    assert not ref["dw_gate"].any()
+
+
+def test_unpicked_expert_gets_zero_gradients():
+    wl = sw(100, 128, 256, seed=420)
+    bias = [0.0] * 8
+    bias[2] = -1000.0
+    bias[6] = -1000.0
+    inp = checked_inputs(wl.with_(bias=tuple(bias)))
+    grads, _ = run_backward_parity(inp)
+    for m in grads[2:]:
+        assert not m[2].any() and not m[6].any()
+
+
+def test_backward_reruns_are_bit_identical():
+    wl = sw(300, 256, 512, seed=430)
+    g = checked_inputs(wl).to(DEV)
+    dy = make_dy(wl, wl.dtype).to(DEV)
+    a = moe.backward(g.x, g.w_gate, g.w1, g.w3, g.w2, dy)
+    b = moe.backward(g.x, g.w_gate, g.w1, g.w3, g.w2, dy)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u.view(torch.int16) if u.dtype == torch.bfloat16 else u,
+                           v.view(torch.int16) if v.dtype == torch.bfloat16 else v)
+
+
+def test_zero_tokens_give_zero_weight_gradients():
+    wl = sw(4, 128, 256, seed=440)
+    g = W.make_inputs(wl).to(DEV)
+    dy = torch.zeros(0, 128, dtype=torch.bfloat16, device=DEV)
+    dx, dwg, dw1, dw3, dw2 = moe.backward(g.x[:0], g.w_gate, g.w1, g.w3, g.w2, dy)
+    torch.cuda.synchronize()
+    assert dx.shape == (0, 128)
+    for m in (dwg, dw1, dw3, dw2):
+        assert not m.any()
+
+
+@pytest.mark.slow
+def test_backward_prefill_size_sampled():
+    """The 8x7B shape at T = 512 tokens (about 128 rows per expert), in one
+    call: dx of a sample of tokens against the oracle run on those tokens
+    alone (a token's dx depends on no other token).  The weight gradients
+    sum over every token and are checked at the smaller sizes above."""
+    wl = W.WORKLOADS["prefill_8x7b"].with_(T=512)
+    announce("prefill-size backward: drawing inputs")
+    inp = checked_inputs(wl)
+    dy = make_dy(wl, wl.dtype)
+    g = inp.to(DEV)
+    dx, dwg, dw1, dw3, dw2 = moe.backward(g.x, g.w_gate, g.w1, g.w3, g.w2, dy.to(DEV))
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(0).choice(wl.T, 8, replace=False))
+    announce("prefill-size backward: oracle on 8 tokens")
+    ref = oracle.backward(inp.x[rows], inp.w_gate, inp.w1, inp.w3, inp.w2, dy[rows])
+    err = row_max_rel_err(dx[torch.as_tensor(rows, device=DEV)], ref["dx"])
+    announce(f"  dx (8 tokens) row-max-rel err {err:.3e}")
+    assert err <= TOL[wl.dtype], err
