@@ -28,6 +28,11 @@ fp32 scale per output column, quantized once before timing): step time,
 the layer's bytes (codes and scales of the experts that received tokens,
 x, y, router) over HBM peak, and the int8 gate/up kernel alone.
 
+``backward``: moe_backward (gradients of sum(dy * y) for x, the router and
+the expert matrices, recomputing the forward pieces it needs) on the
+prefill workload: step time and the fraction of bf16 MFMA peak for its
+nine grouped GEMMs, 9 * 2 * kT * d * f FLOPs.
+
 ``top_k``: the same workloads routed to 1 and to 4 experts per token
 (Mixtral uses 2), each with its layer roofline: bytes of the experts that
 received tokens for the decode step, 2 k T (3 d f) + 2 T d E FLOPs for the
@@ -69,6 +74,8 @@ def parse():
                     help="skip the top-1 / top-4 measurement")
     ap.add_argument("--no-w8", dest="w8", action="store_false",
                     help="skip the int8-weight decode measurement")
+    ap.add_argument("--no-backward", dest="backward", action="store_false",
+                    help="skip the backward measurement")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this size (for counter scaling)")
     return ap.parse_args()
@@ -290,6 +297,39 @@ def measure_w8(wl_name, steps, warmup):
             "expert_counts": c}
 
 
+def measure_backward(wl_name, steps, warmup):
+    """moe_backward on the workload (synthetic dy ~ N(0, 1))."""
+    import torch
+    import sparse_mixture_experts_top2_amd as moe
+    from sparse_mixture_experts_top2_amd import workloads as W
+
+    wl = W.WORKLOADS[wl_name]
+    dev = torch.device("cuda:0")
+    inp = W.make_inputs(wl, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(wl.seed + 900)
+    dy = torch.randn(wl.T, wl.d, generator=gen, device="cuda").to(inp.x.dtype)
+    ws = torch.empty(moe.backward_workspace_bytes(wl.T, wl.d, wl.f, wl.E, inp.x.dtype),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        moe.backward(inp.x, inp.w_gate, inp.w1, inp.w3, inp.w2, dy, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    ms = time_region(step, steps, stream)
+    R = 2 * wl.T
+    flops = 9 * 2.0 * R * wl.d * wl.f + 4.0 * wl.T * wl.d * wl.E
+    ach = flops / (ms * 1e-3) / 1e12
+    log(f"{wl_name} backward: {ms:.3f} ms/step ({wl.T / ms * 1e3:.0f} tokens/s); "
+        f"{ach:.0f} TFLOP/s = {ach / PEAK_BF16_TFLOPS * 100:.1f}% of bf16 peak")
+    return {"workload": wl_name, "value": round(wl.T / (ms * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_step": round(ms, 4), "steps": steps, "warmup": warmup,
+            "roofline": {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                         "algorithmic_flops_per_step": flops}}
+
+
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_gateup_8x7b.md")
 TRAFFIC_PROFILE_W8 = os.path.join(ROOT, "profiles", "hbm_traffic_gateup_w8_decode_8x7b.md")
 
@@ -390,6 +430,7 @@ def main():
         for k in (1, 4):
             topk.append(measure_topk(args.workload, k, max(20, steps // 2), warmup))
     sec = None
+    bwd = None
     if args.secondary:
         s_steps, s_warm = defaults(args.secondary)
         r = measure(args.secondary, s_steps, s_warm)
@@ -398,6 +439,8 @@ def main():
         if args.topk:
             for k in (1, 4):
                 topk.append(measure_topk(args.secondary, k, s_steps // 2 or 1, s_warm))
+        if args.backward:
+            bwd = measure_backward(args.secondary, max(5, s_steps // 3), 2)
         sec = {"workload": r["wl"].name, "value": round(r["tokens_per_s"], 1), "unit": "tokens/s",
                "ms_per_step": round(r["ms"], 5), "steps": s_steps, "warmup": s_warm,
                "config": {"T": r["wl"].T, "d_model": r["wl"].d, "d_ff": r["wl"].f,
@@ -434,6 +477,7 @@ def main():
         "block_boundary": blocks or None,
         "top_k": topk or None,
         "w8": w8,
+        "backward": bwd,
     }
     print(json.dumps(out), flush=True)
 

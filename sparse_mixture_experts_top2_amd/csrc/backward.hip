@@ -376,17 +376,55 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float *__restrict__ d
     }
 }
 
-// dWg[i, e] = sum_t x[t, i] dl[t, e], t ascending; one thread per (i, e).
-template <typename T>
+// dWg[i, e] = sum_t x[t, i] dl[t, e].  A workgroup takes 64 input rows i
+// (one per lane, reading x coalesced) and all E columns; its four
+// wavefronts take contiguous quarters of the tokens, each summing in token
+// order, and the quarters meet in a fixed order: (q0 + q1) + (q2 + q3).
+template <typename T, int EMAX>
 __global__ __launch_bounds__(256) void bwd_dwg_kernel(const T *__restrict__ x,
                                                       const float *__restrict__ dl, int T_, int d,
                                                       int E, float *__restrict__ dwg) {
-    const int id = blockIdx.x * 256 + threadIdx.x;
-    if (id >= d * E) return;
-    const int i = id / E, e = id % E;
-    float acc = 0.0f;
-    for (int t = 0; t < T_; ++t) acc += to_f32(x[(size_t)t * d + i]) * dl[(size_t)t * E + e];
-    dwg[id] = acc;
+    __shared__ float part[4][EMAX][64];
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int i = blockIdx.x * 64 + lane;
+    const int t0 = (int)((int64_t)T_ * wave / 4), t1 = (int)((int64_t)T_ * (wave + 1) / 4);
+    float acc[EMAX];
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) acc[e] = 0.0f;
+    // Slots e >= E read column E - 1 (a valid element) and are never
+    // stored; the clamp bound sits in a vector register so that the
+    // compiler does not hoist EMAX uniform compares into scalar registers.
+    int last;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(last) : "s"(E - 1));
+    if (i < d)
+        for (int t = t0; t < t1; ++t) {
+            const float xv = to_f32(x[(size_t)t * d + i]);
+            const float *dlt = dl + (size_t)t * E;
+#pragma unroll
+            for (int e = 0; e < EMAX; ++e) acc[e] += xv * dlt[min(e, last)];
+        }
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) part[wave][e][lane] = acc[e];
+    __syncthreads();
+    if (wave != 0 || i >= d) return;
+    for (int e = 0; e < E; ++e)
+        dwg[(size_t)i * E + e] = (part[0][e][lane] + part[1][e][lane]) +
+                                 (part[2][e][lane] + part[3][e][lane]);
+}
+
+template <typename T>
+hipError_t launch_dwg(const T *x, const float *dl, int T_, int d, int E, float *dwg,
+                      hipStream_t stream) {
+    const dim3 grid((d + 63) / 64), block(256);
+    if (E <= 8)
+        hipLaunchKernelGGL((bwd_dwg_kernel<T, 8>), grid, block, 0, stream, x, dl, T_, d, E, dwg);
+    else if (E <= 16)
+        hipLaunchKernelGGL((bwd_dwg_kernel<T, 16>), grid, block, 0, stream, x, dl, T_, d, E, dwg);
+    else if (E <= 32)
+        hipLaunchKernelGGL((bwd_dwg_kernel<T, 32>), grid, block, 0, stream, x, dl, T_, d, E, dwg);
+    else
+        hipLaunchKernelGGL((bwd_dwg_kernel<T, 64>), grid, block, 0, stream, x, dl, T_, d, E, dwg);
+    return hipGetLastError();
 }
 
 template <typename T, int AL, int BL, int GROUP, int EPI>
@@ -429,19 +467,39 @@ hipError_t run_backward_t(const moe_shape_t &s, const T *x, const T *wg, const T
     a.counts = counts;
     a.offsets = offsets;
     a.E = E;
-    // g = xp W1[e], then u = xp W3[e] with h = silu(g) u
-    a.A = xp; a.lda = d; a.b_estride = (long long)d * f; a.ldb = f; a.ldc = f;
-    a.M = R; a.N = f; a.K = d;
-    a.B = w1; a.C = G;
-    if (e == hipSuccess) e = gemm<T, OP_KC, OP_MNC, GROUP_ROWS, EPI_STORE>(a, rt * tiles_of(f), str);
-    a.B = w3; a.C = U; a.C2 = H; a.G = G;
-    if (e == hipSuccess) e = gemm<T, OP_KC, OP_MNC, GROUP_ROWS, EPI_UP>(a, rt * tiles_of(f), str);
-    // o = h W2[e]
-    a = GemmArgs{};
-    a.counts = counts; a.offsets = offsets; a.E = E;
-    a.A = H; a.lda = f; a.B = w2; a.ldb = d; a.b_estride = (long long)f * d;
-    a.C = O; a.ldc = d; a.M = R; a.N = d; a.K = f;
-    if (e == hipSuccess) e = gemm<T, OP_KC, OP_MNC, GROUP_ROWS, EPI_STORE>(a, rt * tiles_of(d), str);
+    // g = xp W1[e] and u = xp W3[e] (fp32), h = silu(g) u.  bf16 layers of
+    // prefill size take the forward's direct-to-LDS gate/up kernel in its
+    // variant that also stores g and u; other shapes the generic GEMM.
+    bool fused = false;
+    if constexpr (sizeof(T) == 2) {
+        if (e == hipSuccess) {
+            const hipError_t fe = launch_gateup_bf16_gu(s, xp, counts, offsets, w1, w3, H, G, U,
+                                                        str);
+            fused = fe == hipSuccess;
+            if (fe != hipErrorNotSupported && fe != hipSuccess) e = fe;
+        }
+    }
+    if (!fused) {
+        a.A = xp; a.lda = d; a.b_estride = (long long)d * f; a.ldb = f; a.ldc = f;
+        a.M = R; a.N = f; a.K = d;
+        a.B = w1; a.C = G;
+        if (e == hipSuccess)
+            e = gemm<T, OP_KC, OP_MNC, GROUP_ROWS, EPI_STORE>(a, rt * tiles_of(f), str);
+        a.B = w3; a.C = U; a.C2 = H; a.G = G;
+        if (e == hipSuccess)
+            e = gemm<T, OP_KC, OP_MNC, GROUP_ROWS, EPI_UP>(a, rt * tiles_of(f), str);
+    }
+    // o = h W2[e]: the forward's down kernels for bf16, the generic GEMM for fp32
+    if constexpr (sizeof(T) == 2) {
+        if (e == hipSuccess) e = launch_down_bf16(s, H, counts, offsets, w2, O, str);
+    } else {
+        a = GemmArgs{};
+        a.counts = counts; a.offsets = offsets; a.E = E;
+        a.A = H; a.lda = f; a.B = w2; a.ldb = d; a.b_estride = (long long)f * d;
+        a.C = O; a.ldc = d; a.M = R; a.N = d; a.K = f;
+        if (e == hipSuccess)
+            e = gemm<T, OP_KC, OP_MNC, GROUP_ROWS, EPI_STORE>(a, rt * tiles_of(d), str);
+    }
     // routing-weight gradients, dO and dl
     if (e == hipSuccess && Tn > 0) {
         hipLaunchKernelGGL(bwd_route_grad_kernel<T>, dim3(Tn), dim3(256), 0, str, dy, O, idx, w,
@@ -482,11 +540,7 @@ hipError_t run_backward_t(const moe_shape_t &s, const T *x, const T *wg, const T
     if (e == hipSuccess)
         e = gemm<T, OP_MNC, OP_MNC, GROUP_K, EPI_STORE>(a, E * tiles_of(f) * tiles_of(d), str);
     // router gradient
-    if (e == hipSuccess) {
-        hipLaunchKernelGGL(bwd_dwg_kernel<T>, dim3((d * E + 255) / 256), dim3(256), 0, str, x, dl,
-                           Tn, d, E, dwg);
-        e = hipGetLastError();
-    }
+    if (e == hipSuccess) e = launch_dwg<T>(x, dl, Tn, d, E, dwg, str);
     return e;
 }
 

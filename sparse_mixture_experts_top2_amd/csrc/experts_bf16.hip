@@ -341,11 +341,17 @@ __device__ __forceinline__ void static_for_from(F &&f) {
 template <int N, typename F>
 __device__ __forceinline__ void static_for(F &&f) { static_for_from<0, N>(f); }
 
-template <int NMAT>
-__global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_dma_kernel(
+// With NMAT = 2 and GU, the body also stores the gate and up products
+// themselves (fp32, row-major like h) to g_out / u_out, for the backward,
+// which needs them for the SwiGLU derivative.  Two kernels wrap it (below):
+// the forward's takes exactly the parameters it always had, so its
+// registers do not change.
+template <int NMAT, bool GU>
+__device__ __forceinline__ void prefill_dma_body(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B0,
     const uint16_t *__restrict__ B1, void *__restrict__ C, const int32_t *__restrict__ counts,
-    const int32_t *__restrict__ offsets, int E, int K, int N, int a_rows) {
+    const int32_t *__restrict__ offsets, int E, int K, int N, int a_rows,
+    float *__restrict__ g_out, float *__restrict__ u_out) {
     constexpr int NW = PWM * PWN;
     constexpr int TM = PBM / PWM, TN = PBN / PWN;
     constexpr int MB = TM / 32, NB = TN / 32;
@@ -576,6 +582,25 @@ __global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_dma_kernel(
                 }
         }
         __syncthreads();
+        if constexpr (GU) {
+            // 32x32 accumulator layout: value q of lane l is row
+            // 8*(q/4) + 4*(l/32) + q%4, column l%32 of the block.
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int j = 0; j < NB / 2; ++j) {
+                    const int col = n0 + wn * (TN / 2) + j * 32 + (lane & 31);
+#pragma unroll
+                    for (int qq = 0; qq < 16; ++qq) {
+                        const int row =
+                            row0 + wm * TM + i * 32 + 8 * (qq >> 2) + 4 * (lane >> 5) + (qq & 3);
+                        if (row < row_end) {
+                            g_out[(size_t)row * N + col] = acc[i][j][qq];
+                            u_out[(size_t)row * N + col] = acc[i][j + NB / 2][qq];
+                        }
+                    }
+                }
+        }
         constexpr int CH = BNM / 8;                      // 16-byte chunks per row
         uint16_t *H = static_cast<uint16_t *>(C);
         for (int v = tid; v < PBM * CH; v += NW * 64) {
@@ -601,6 +626,24 @@ __global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_dma_kernel(
                 }
             }
     }
+}
+
+template <int NMAT>
+__global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_dma_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B0,
+    const uint16_t *__restrict__ B1, void *__restrict__ C, const int32_t *__restrict__ counts,
+    const int32_t *__restrict__ offsets, int E, int K, int N, int a_rows) {
+    prefill_dma_body<NMAT, false>(A, B0, B1, C, counts, offsets, E, K, N, a_rows, nullptr,
+                                  nullptr);
+}
+
+// The gate/up kernel that also stores g and u (for the backward).
+__global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_dma_gu_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B0,
+    const uint16_t *__restrict__ B1, uint16_t *__restrict__ C, const int32_t *__restrict__ counts,
+    const int32_t *__restrict__ offsets, int E, int K, int N, int a_rows,
+    float *__restrict__ g_out, float *__restrict__ u_out) {
+    prefill_dma_body<2, true>(A, B0, B1, C, counts, offsets, E, K, N, a_rows, g_out, u_out);
 }
 
 // Grid for the prefill kernels: worst-case tile count (every expert may
@@ -759,6 +802,18 @@ hipError_t launch_gateup_bf16(const moe_shape_t &s, const uint16_t *xp, const in
             hipLaunchKernelGGL(prefill_gemm_kernel<2>, dim3(grid), dim3(PWM * PWN * 64), 0,
                                stream, xp, w1, w3, h, counts, offsets, E, d, f, rows);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_gateup_bf16_gu(const moe_shape_t &s, const uint16_t *xp,
+                                 const int32_t *counts, const int32_t *offsets,
+                                 const uint16_t *w1, const uint16_t *w3, uint16_t *h, float *g,
+                                 float *u, hipStream_t stream) {
+    const int d = s.d_model, f = s.d_ff, E = s.n_experts, rows = routed_rows(s);
+    if (s.T <= kDecodeMaxT || d % DBK != 0 || f % (PBN / 2) != 0) return hipErrorNotSupported;
+    const int grid = prefill_grid(rows, E, (f + PBN / 2 - 1) / (PBN / 2));
+    hipLaunchKernelGGL(prefill_dma_gu_kernel, dim3(grid), dim3(PWM * PWN * 64), 0, stream, xp,
+                       w1, w3, h, counts, offsets, E, d, f, rows, g, u);
     return hipGetLastError();
 }
 

@@ -118,6 +118,13 @@ hipError_t launch_down_f32(const moe_shape_t &s, const float *h, const int32_t *
 hipError_t launch_gateup_bf16(const moe_shape_t &s, const uint16_t *xp, const int32_t *counts,
                               const int32_t *offsets, const uint16_t *w1, const uint16_t *w3,
                               uint16_t *h, hipStream_t stream, const int32_t *src = nullptr);
+// The prefill gate/up kernel storing g and u (fp32 [kT, f]) beside h, for
+// the backward.  hipErrorNotSupported when the shape does not take the
+// direct-to-LDS kernel (T <= kDecodeMaxT, d % 64 or f % 128 not zero).
+hipError_t launch_gateup_bf16_gu(const moe_shape_t &s, const uint16_t *xp,
+                                 const int32_t *counts, const int32_t *offsets,
+                                 const uint16_t *w1, const uint16_t *w3, uint16_t *h, float *g,
+                                 float *u, hipStream_t stream);
 hipError_t launch_down_bf16(const moe_shape_t &s, const uint16_t *h, const int32_t *counts,
                             const int32_t *offsets, const uint16_t *w2, float *o,
                             hipStream_t stream);
