@@ -98,19 +98,25 @@ __device__ __forceinline__ void transpose_b32(const uint4 (&r)[4], uint4 (&out)[
     out[3] = make_uint4(r[0].w, r[1].w, r[2].w, r[3].w);
 }
 
-template <typename T>
-struct OperandLoader;
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
-// 128 x 32 tile of one operand, staged through registers into LDS as 128
-// lines of 32 K values (pitch PITCH elements).
+// 128 x 32 tile of one operand, staged through registers into LDS.
+//   KC, and MNC of fp32: 128 lines of 32 K values (pitch PITCH); an MNC
+//     tile is transposed in registers (V x V blocks) on the way.
+//   MNC of bf16 (TR): the tile's own layout, 32 K rows of 128 values
+//     (pitch TPITCH), copied with plain 16-byte vectors by every thread;
+//     MFMA fragments are read back with the LDS transpose read.
 template <typename T, int LAYOUT>
 struct TileLoad {
     static constexpr int V = 16 / (int)sizeof(T);          // elements per 16 bytes
-    static constexpr int PITCH = GBK + V;                   // LDS line pitch
+    static constexpr bool TR = LAYOUT == OP_MNC && V == 8;
+    static constexpr int PITCH = GBK + V;                   // LDS line pitch (KC / transposed)
+    static constexpr int TPITCH = 128 + 16;                 // LDS K-row pitch (TR): the 4 rows a
+                                                            // transpose read covers start 8 banks apart
     // KC: 128 lines x (32 / V) vectors; MNC: (32 / V) x (128 / V) blocks of V x V.
-    static constexpr int NKC = 128 * GBK / V / 256;         // vectors per thread (KC)
+    static constexpr int NKC = 128 * GBK / V / 256;         // vectors per thread (KC, TR)
     static constexpr int NBLK = (GBK / V) * (128 / V);      // blocks (MNC)
-    uint4 r[LAYOUT == OP_KC ? NKC : V];
+    uint4 r[(LAYOUT == OP_KC || TR) ? NKC : V];
 
     // base points at element (line 0 of the tile, k = 0) for KC (lines are
     // ld apart; line index clamped to line_lim - 1), or at element (k = 0,
@@ -128,6 +134,16 @@ struct TileLoad {
                 const T *p = base + (long long)min(line0 + line, line_lim - 1) * ld + k;
                 r[i] = k < k_hi ? *reinterpret_cast<const uint4 *>(p) : make_uint4(0, 0, 0, 0);
             }
+        } else if constexpr (TR) {
+#pragma unroll
+            for (int i = 0; i < NKC; ++i) {
+                const int v = tid + 256 * i;
+                const int kr = v / (128 / V), c = (v % (128 / V)) * V;
+                const int k = k0 + kr, mn = mn0 + c;
+                const bool ok = k >= k_lo && k < k_hi && mn < mn_lim;
+                r[i] = ok ? *reinterpret_cast<const uint4 *>(base + (long long)k * ld + mn)
+                          : make_uint4(0, 0, 0, 0);
+            }
         } else {
             if (tid < NBLK) {
                 const int kb = tid % (GBK / V), mb = tid / (GBK / V);
@@ -142,6 +158,29 @@ struct TileLoad {
             }
         }
     }
+    // The 32x32x16 bf16 operand of tile lines mb .. mb+31 at K offset kk:
+    // lane l holds line mb + l % 32, K values kk + 8 (l / 32) .. + 7.
+    __device__ __forceinline__ bf16x8_t frag(const T *s, int mb, int kk) const {
+        const int lane = threadIdx.x & 63;
+        if constexpr (TR) {
+            // Transpose read: within each 16-lane group G, lane 4 jq + q
+            // addresses K row r + jq, columns c .. c + 3, and lane j
+            // receives the 4 K values of column c0 + j.
+            const int G = lane >> 4, jq = (lane & 15) >> 2, q = lane & 3;
+            const int c = mb + 16 * (G & 1) + 4 * q;
+            const int r = kk + 8 * (G >> 1) + jq;
+            typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4 *)(s + r * TPITCH + c));
+            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4 *)(s + (r + 4) * TPITCH + c));
+            return __builtin_bit_cast(bf16x8_t,
+                                      __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else {
+            return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(
+                s + (mb + (lane & 31)) * PITCH + kk + (lane >> 5) * 8));
+        }
+    }
     __device__ __forceinline__ void store(T *s) {
         const int tid = threadIdx.x;
         if constexpr (LAYOUT == OP_KC) {
@@ -150,6 +189,13 @@ struct TileLoad {
                 const int v = tid + 256 * i;
                 const int line = v / (GBK / V), kv = v % (GBK / V);
                 *reinterpret_cast<uint4 *>(s + line * PITCH + kv * V) = r[i];
+            }
+        } else if constexpr (TR) {
+#pragma unroll
+            for (int i = 0; i < NKC; ++i) {
+                const int v = tid + 256 * i;
+                const int kr = v / (128 / V), c = (v % (128 / V)) * V;
+                *reinterpret_cast<uint4 *>(s + kr * TPITCH + c) = r[i];
             }
         } else {
             if (tid < NBLK) {
@@ -233,16 +279,11 @@ __global__ __launch_bounds__(256) void bwd_gemm_kernel(GemmArgs p) {
         if constexpr (sizeof(T) == 2) {
 #pragma unroll
             for (int kk = 0; kk < GBK; kk += 16) {
-                const int koff = kk + (lane >> 5) * 8;
                 bf16x8_t af[2], bfr[2];
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
-                    af[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(
-                        &As[(wm * 64 + i * 32 + (lane & 31)) * PITCH + koff]));
+                for (int i = 0; i < 2; ++i) af[i] = la.frag(As, wm * 64 + i * 32, kk);
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    bfr[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(
-                        &Bs[(wn * 64 + j * 32 + (lane & 31)) * PITCH + koff]));
+                for (int j = 0; j < 2; ++j) bfr[j] = lb.frag(Bs, wn * 64 + j * 32, kk);
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
 #pragma unroll
