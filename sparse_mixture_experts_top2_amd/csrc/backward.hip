@@ -547,20 +547,44 @@ hipError_t run_backward_t(const moe_shape_t &s, const T *x, const T *wg, const T
                            pos, d, E, k, dO, dl);
         e = hipGetLastError();
     }
-    // da = dO W2[e]^T, with dg, du in the epilogue
+    // da = dO W2[e]^T, with dg, du in the epilogue.  The weight matrices are
+    // read K-contiguous here (a row of W2[e] is a column of W2[e]^T); bf16
+    // layers whose sizes fit the forward's direct-to-LDS pipeline take its
+    // variant for such operands, other shapes the generic GEMM.
+    bool da_done = false, dxp_done = false;
+    if constexpr (sizeof(T) == 2) {
+        if (e == hipSuccess) {
+            const hipError_t fe = launch_bt_dswiglu_bf16(R, E, dO, w2, d, f, counts, offsets,
+                                                         G, U, dG, dU, str);
+            da_done = fe == hipSuccess;
+            if (fe != hipErrorNotSupported && fe != hipSuccess) e = fe;
+        }
+    }
     a = GemmArgs{};
     a.counts = counts; a.offsets = offsets; a.E = E;
     a.A = dO; a.lda = d; a.B = w2; a.ldb = d; a.b_estride = (long long)f * d;
     a.C = dG; a.C2 = dU; a.G = G; a.U = U; a.ldc = f; a.M = R; a.N = f; a.K = d;
-    if (e == hipSuccess) e = gemm<T, OP_KC, OP_KC, GROUP_ROWS, EPI_DSWIGLU>(a, rt * tiles_of(f), str);
-    // dXp = dG W1[e]^T + dU W3[e]^T   (into the o region)
+    if (e == hipSuccess && !da_done)
+        e = gemm<T, OP_KC, OP_KC, GROUP_ROWS, EPI_DSWIGLU>(a, rt * tiles_of(f), str);
+    // dXp = dG W1[e]^T + dU W3[e]^T   (into the o region): one pass over a
+    // reduction of 2 f on the pipeline above, else two generic GEMMs
+    if constexpr (sizeof(T) == 2) {
+        if (e == hipSuccess) {
+            const hipError_t fe = launch_bt_store_bf16(R, E, dG, w1, dU, w3, f, d, counts,
+                                                       offsets, O, str);
+            dxp_done = fe == hipSuccess;
+            if (fe != hipErrorNotSupported && fe != hipSuccess) e = fe;
+        }
+    }
     a = GemmArgs{};
     a.counts = counts; a.offsets = offsets; a.E = E;
     a.A = dG; a.lda = f; a.B = w1; a.ldb = f; a.b_estride = (long long)d * f;
     a.C = O; a.ldc = d; a.M = R; a.N = d; a.K = f;
-    if (e == hipSuccess) e = gemm<T, OP_KC, OP_KC, GROUP_ROWS, EPI_STORE>(a, rt * tiles_of(d), str);
+    if (e == hipSuccess && !dxp_done)
+        e = gemm<T, OP_KC, OP_KC, GROUP_ROWS, EPI_STORE>(a, rt * tiles_of(d), str);
     a.A = dU; a.B = w3;
-    if (e == hipSuccess) e = gemm<T, OP_KC, OP_KC, GROUP_ROWS, EPI_ADD>(a, rt * tiles_of(d), str);
+    if (e == hipSuccess && !dxp_done)
+        e = gemm<T, OP_KC, OP_KC, GROUP_ROWS, EPI_ADD>(a, rt * tiles_of(d), str);
     // dx
     if (e == hipSuccess && Tn > 0) {
         hipLaunchKernelGGL(bwd_dx_kernel<T>, dim3(Tn), dim3(256), 0, str, O, pos, dl, wg, d, E, k,

@@ -343,15 +343,29 @@ __device__ __forceinline__ void static_for(F &&f) { static_for_from<0, N>(f); }
 
 // With NMAT = 2 and GU, the body also stores the gate and up products
 // themselves (fp32, row-major like h) to g_out / u_out, for the backward,
-// which needs them for the SwiGLU derivative.  Two kernels wrap it (below):
-// the forward's takes exactly the parameters it always had, so its
-// registers do not change.
-template <int NMAT, bool GU>
+// which needs them for the SwiGLU derivative.
+//
+// BT (backward products, NMAT = 1): B is K-contiguous, B0 + e * N * K1 +
+// n * K1 + k (a transposed weight matrix), staged and read like A.  With A2
+// / B2 not NULL the reduction runs over K = 2 * K1: the first K1 from (A,
+// B0), the second from (A2, B2), all with row stride K1 (two products
+// added in one pass).  BT_STORE writes C fp32; BT_DSWIGLU takes the result
+// as da and writes dg = da * u * silu'(g) and du = da * silu(g) (bf16) from
+// g_in / u_in (fp32), all [rows, N].
+//
+// Kernels wrap the body (below); the forward's take exactly the parameters
+// they always had, so their registers and code do not change.
+enum { BT_NONE = 0, BT_STORE = 1, BT_DSWIGLU = 2 };
+template <int NMAT, bool GU, int BT = BT_NONE>
 __device__ __forceinline__ void prefill_dma_body(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B0,
     const uint16_t *__restrict__ B1, void *__restrict__ C, const int32_t *__restrict__ counts,
     const int32_t *__restrict__ offsets, int E, int K, int N, int a_rows,
-    float *__restrict__ g_out, float *__restrict__ u_out) {
+    float *__restrict__ g_out, float *__restrict__ u_out,
+    const uint16_t *__restrict__ A2 = nullptr, const uint16_t *__restrict__ B2 = nullptr,
+    int K1 = 0, const float *__restrict__ g_in = nullptr, const float *__restrict__ u_in = nullptr,
+    uint16_t *__restrict__ dg_out = nullptr, uint16_t *__restrict__ du_out = nullptr) {
+    static_assert(BT == BT_NONE || (NMAT == 1 && !GU), "backward products take one matrix");
     constexpr int NW = PWM * PWN;
     constexpr int TM = PBM / PWM, TN = PBN / PWN;
     constexpr int MB = TM / 32, NB = TN / 32;
@@ -416,20 +430,49 @@ __device__ __forceinline__ void prefill_dma_body(
     }
 
     auto issue_a = [&](uint8_t *sa, int k0) MOE_INLINE {
+        if constexpr (BT == BT_NONE) {
 #pragma unroll
-        for (int j = 0; j < AI; ++j) {
-            const int r = min(row0 + a_r0 + j * AROWS, a_rows - 1);
-            const uint16_t *src = A + (size_t)r * K + k0 + a_kc[j & 1] * 8;
-            __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(sa + (wave * AI + j) * 1024),
-                                             16, 0, 0);
+            for (int j = 0; j < AI; ++j) {
+                const int r = min(row0 + a_r0 + j * AROWS, a_rows - 1);
+                const uint16_t *src = A + (size_t)r * K + k0 + a_kc[j & 1] * 8;
+                __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(sa + (wave * AI + j) * 1024),
+                                                 16, 0, 0);
+            }
+        } else {
+            const uint16_t *Ab = A;
+            int ka = k0;
+            if (A2 && k0 >= K1) { Ab = A2; ka = k0 - K1; }
+#pragma unroll
+            for (int j = 0; j < AI; ++j) {
+                const int r = min(row0 + a_r0 + j * AROWS, a_rows - 1);
+                const uint16_t *src = Ab + (size_t)r * K1 + ka + a_kc[j & 1] * 8;
+                __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(sa + (wave * AI + j) * 1024),
+                                                 16, 0, 0);
+            }
         }
     };
     auto issue_b = [&](uint8_t *sb, int k0) MOE_INLINE {
+        if constexpr (BT == BT_NONE) {
 #pragma unroll
-        for (int j = 0; j < BI; ++j) {
-            const uint16_t *src = B0 + b_base[j & 3] + (size_t)(k0 + (j & ~3) * 2) * N;
-            __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(sb + (wave * BI + j) * 1024),
-                                             16, 0, 0);
+            for (int j = 0; j < BI; ++j) {
+                const uint16_t *src = B0 + b_base[j & 3] + (size_t)(k0 + (j & ~3) * 2) * N;
+                __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(sb + (wave * BI + j) * 1024),
+                                                 16, 0, 0);
+            }
+        } else {
+            // K-contiguous B: the tile's 256 columns are lines of 64 K values,
+            // staged exactly like A's rows (same swizzle).
+            const uint16_t *Bb = B0;
+            int kb = k0;
+            if (B2 && k0 >= K1) { Bb = B2; kb = k0 - K1; }
+            Bb += (size_t)e * N * K1;
+#pragma unroll
+            for (int j = 0; j < BI; ++j) {
+                const int n = min(n0 + a_r0 + j * AROWS, N - 1);
+                const uint16_t *src = Bb + (size_t)n * K1 + kb + a_kc[j & 1] * 8;
+                __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(sb + (wave * BI + j) * 1024),
+                                                 16, 0, 0);
+            }
         }
     };
 
@@ -456,6 +499,13 @@ __device__ __forceinline__ void prefill_dma_body(
             b_off[j][u] = r * 512 + ((((n >> 3) ^ bswz(r))) << 4) + (n & 7) * 2;
         }
     }
+
+    // K-contiguous B (BT): fragments read like A's, line wn * TN + 32 j + l % 32.
+    const int bt_row = wn * TN + (lane & 31);
+    int bt_off[KS];
+#pragma unroll
+    for (int h = 0; h < KS; ++h)
+        bt_off[h] = bt_row * (DBK * 2) + (((h * 2 + (lane >> 5)) ^ aswz(bt_row)) << 4);
 
     f32x16_t acc[MB][NB];
 #pragma unroll
@@ -488,12 +538,19 @@ __device__ __forceinline__ void prefill_dma_body(
                         sa + a_off[h] + i * 32 * (DBK * 2)));
 #pragma unroll
                 for (int j = 0; j < NB; ++j) {
-                    s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) s16x4_t *)(sb + b_off[j][0] + h * 8192));
-                    s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) s16x4_t *)(sb + b_off[j][1] + h * 8192));
-                    bfr[hh][j] = __builtin_bit_cast(
-                        bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    if constexpr (BT == BT_NONE) {
+                        s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) s16x4_t *)(sb + b_off[j][0] +
+                                                                          h * 8192));
+                        s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (__attribute__((address_space(3))) s16x4_t *)(sb + b_off[j][1] +
+                                                                          h * 8192));
+                        bfr[hh][j] = __builtin_bit_cast(
+                            bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    } else {
+                        bfr[hh][j] = as_bf16x8(*reinterpret_cast<const uint4 *>(
+                            sb + bt_off[h] + j * 32 * (DBK * 2)));
+                    }
                 }
             }
 #pragma unroll
@@ -516,7 +573,8 @@ __device__ __forceinline__ void prefill_dma_body(
     // to it (harmless re-reads into free slots), so the steady-state loop has
     // no branches and every wait count is a constant; the rings are drained
     // before the epilogue reuses them.
-    const int nk = K / DBK;
+    int nk = K / DBK;
+    if constexpr (BT != BT_NONE) nk = (A2 ? 2 * K1 : K1) / DBK;
     auto kclamp = [&](int kt) { return min(kt, nk - 1) * DBK; };
     constexpr int LA = DAS - 1, LB = DBS - 1;      // lookahead of each ring
     constexpr int WAIT = DAS > DBS ? AI : DBS > DAS ? BI : 0;
@@ -621,8 +679,17 @@ __device__ __forceinline__ void prefill_dma_body(
                 for (int qq = 0; qq < 16; ++qq) {
                     const int row =
                         row0 + wm * TM + i * 32 + 8 * (qq >> 2) + 4 * (lane >> 5) + (qq & 3);
-                    if (row < row_end)
-                        static_cast<float *>(C)[(size_t)row * N + col] = acc[i][j][qq];
+                    if constexpr (BT == BT_DSWIGLU) {
+                        if (row >= row_end) continue;
+                        const size_t ci = (size_t)row * N + col;
+                        const float da = acc[i][j][qq], g = g_in[ci], u = u_in[ci];
+                        const float sg = 1.0f / (1.0f + expf(-g));
+                        dg_out[ci] = (uint16_t)f32_to_bf16(da * u * sg * (1.0f + g * (1.0f - sg)));
+                        du_out[ci] = (uint16_t)f32_to_bf16(da * g * sg);
+                    } else {
+                        if (row < row_end)
+                            static_cast<float *>(C)[(size_t)row * N + col] = acc[i][j][qq];
+                    }
                 }
             }
     }
@@ -644,6 +711,24 @@ __global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_dma_gu_kernel(
     const int32_t *__restrict__ offsets, int E, int K, int N, int a_rows,
     float *__restrict__ g_out, float *__restrict__ u_out) {
     prefill_dma_body<2, true>(A, B0, B1, C, counts, offsets, E, K, N, a_rows, g_out, u_out);
+}
+
+// Backward products with a K-contiguous B (see prefill_dma_body).
+__global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_dma_bt_store_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, const uint16_t *__restrict__ A2,
+    const uint16_t *__restrict__ B2, float *__restrict__ C, const int32_t *__restrict__ counts,
+    const int32_t *__restrict__ offsets, int E, int K1, int N, int a_rows) {
+    prefill_dma_body<1, false, BT_STORE>(A, B, nullptr, C, counts, offsets, E, K1, N, a_rows,
+                                         nullptr, nullptr, A2, B2, K1);
+}
+__global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_dma_bt_dswiglu_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
+    const int32_t *__restrict__ counts, const int32_t *__restrict__ offsets, int E, int K1, int N,
+    int a_rows, const float *__restrict__ g_in, const float *__restrict__ u_in,
+    uint16_t *__restrict__ dg_out, uint16_t *__restrict__ du_out) {
+    prefill_dma_body<1, false, BT_DSWIGLU>(A, B, nullptr, nullptr, counts, offsets, E, K1, N,
+                                           a_rows, nullptr, nullptr, nullptr, nullptr, K1, g_in,
+                                           u_in, dg_out, du_out);
 }
 
 // Grid for the prefill kernels: worst-case tile count (every expert may
@@ -814,6 +899,32 @@ hipError_t launch_gateup_bf16_gu(const moe_shape_t &s, const uint16_t *xp,
     const int grid = prefill_grid(rows, E, (f + PBN / 2 - 1) / (PBN / 2));
     hipLaunchKernelGGL(prefill_dma_gu_kernel, dim3(grid), dim3(PWM * PWN * 64), 0, stream, xp,
                        w1, w3, h, counts, offsets, E, d, f, rows, g, u);
+    return hipGetLastError();
+}
+
+static bool bt_shape_ok(int rows, int K1, int N) {
+    return rows > 0 && K1 % DBK == 0 && N % PBN == 0;
+}
+
+hipError_t launch_bt_store_bf16(int rows, int E, const uint16_t *A, const uint16_t *B,
+                                const uint16_t *A2, const uint16_t *B2, int K1, int N,
+                                const int32_t *counts, const int32_t *offsets, float *C,
+                                hipStream_t stream) {
+    if (!bt_shape_ok(rows, K1, N)) return hipErrorNotSupported;
+    const int grid = prefill_grid(rows, E, N / PBN);
+    hipLaunchKernelGGL(prefill_dma_bt_store_kernel, dim3(grid), dim3(PWM * PWN * 64), 0, stream,
+                       A, B, A2, B2, C, counts, offsets, E, K1, N, rows);
+    return hipGetLastError();
+}
+
+hipError_t launch_bt_dswiglu_bf16(int rows, int E, const uint16_t *A, const uint16_t *B, int K1,
+                                  int N, const int32_t *counts, const int32_t *offsets,
+                                  const float *g, const float *u, uint16_t *dg, uint16_t *du,
+                                  hipStream_t stream) {
+    if (!bt_shape_ok(rows, K1, N)) return hipErrorNotSupported;
+    const int grid = prefill_grid(rows, E, N / PBN);
+    hipLaunchKernelGGL(prefill_dma_bt_dswiglu_kernel, dim3(grid), dim3(PWM * PWN * 64), 0,
+                       stream, A, B, counts, offsets, E, K1, N, rows, g, u, dg, du);
     return hipGetLastError();
 }
 

@@ -125,6 +125,21 @@ hipError_t launch_gateup_bf16_gu(const moe_shape_t &s, const uint16_t *xp,
                                  const int32_t *counts, const int32_t *offsets,
                                  const uint16_t *w1, const uint16_t *w3, uint16_t *h, float *g,
                                  float *u, hipStream_t stream);
+// Backward products on the prefill pipeline with a K-contiguous B (a
+// transposed expert matrix B[e] = B + e * N * K1, line n at n * K1), over
+// grouped rows (counts / offsets): C = A B[e]^T (+ A2 B2[e]^T when A2 / B2
+// are not NULL, the second K1 of a 2 * K1 reduction), or, for the dswiglu
+// form, da = A B[e]^T turned into dg, du (bf16) with g, u (fp32).  All
+// arrays have row stride K1 (A, A2) or N (C, g, u, dg, du).
+// hipErrorNotSupported unless K1 % 64 == 0 and N % 256 == 0.
+hipError_t launch_bt_store_bf16(int rows, int E, const uint16_t *A, const uint16_t *B,
+                                const uint16_t *A2, const uint16_t *B2, int K1, int N,
+                                const int32_t *counts, const int32_t *offsets, float *C,
+                                hipStream_t stream);
+hipError_t launch_bt_dswiglu_bf16(int rows, int E, const uint16_t *A, const uint16_t *B, int K1,
+                                  int N, const int32_t *counts, const int32_t *offsets,
+                                  const float *g, const float *u, uint16_t *dg, uint16_t *du,
+                                  hipStream_t stream);
 hipError_t launch_down_bf16(const moe_shape_t &s, const uint16_t *h, const int32_t *counts,
                             const int32_t *offsets, const uint16_t *w2, float *o,
                             hipStream_t stream);

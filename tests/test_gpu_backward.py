@@ -70,6 +70,8 @@ CASES = [
     sw(600, 256, 384, E=32, seed=407),
     sw(400, 192, 264, E=4, seed=408),                 # ~200 rows per expert: 2 row tiles
     sw(400, 96, 200, E=4, dtype=W.F32, seed=409),
+    sw(600, 256, 512, E=4, seed=411),                 # 2 row tiles per expert, both
+                                                      # K-contiguous-weight products
 ]
 
 
