@@ -21,6 +21,8 @@
 // rows times its own matrix) or by K (every expert's matrix reduced over
 // its rows), with fused epilogues for the SwiGLU forward and derivative.
 // Every sum has a fixed order; there are no atomics.
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -417,54 +419,136 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float *__restrict__ d
     }
 }
 
-// dWg[i, e] = sum_t x[t, i] dl[t, e].  A workgroup takes 64 input rows i
-// (one per lane, reading x coalesced) and all E columns; its four
-// wavefronts take contiguous quarters of the tokens, each summing in token
-// order, and the quarters meet in a fixed order: (q0 + q1) + (q2 + q3).
+// dWg[i, e] = sum_t x[t, i] dl[t, e], in two passes.  Pass 1: workgroup
+// (b, c) takes 2 * DWG_THREADS columns i (two adjacent ones per thread, so a
+// wavefront reads 128 consecutive elements of a token row in one load) and
+// chunk c of the tokens; each thread sums its chunk in token order into
+// part[c][i][e].  The chunk's dl rows are staged in LDS a block at a time,
+// padded with zeros to EMAX columns, and every lane reads the same LDS word
+// (a broadcast).  Pass 2 adds the chunks in the order c = 0, 1, ..., so the
+// result does not depend on scheduling.
+constexpr int DWG_THREADS = 256;
+constexpr int DWG_COLS = 2 * DWG_THREADS;  // columns per workgroup
+constexpr int DWG_SB = 64;                 // tokens per staged block of dl
+constexpr int DWG_PARTS = 512;             // chunks x EMAX at most (partial buffer size)
+
+inline int dwg_emax(int E) { return E <= 8 ? 8 : E <= 16 ? 16 : E <= 32 ? 32 : 64; }
+// Token chunks: about 32 tokens each, at most DWG_PARTS / EMAX of them.
+inline int dwg_chunks(int T_, int E) {
+    return std::max(1, std::min((T_ + 31) / 32, DWG_PARTS / dwg_emax(E)));
+}
+
+// Two adjacent elements (the first at an even index of a row of even length).
+__device__ __forceinline__ void load_pair(const uint16_t *p, float &a, float &b) {
+    const uint32_t v = *reinterpret_cast<const uint32_t *>(p);
+    a = __uint_as_float(v << 16);
+    b = __uint_as_float(v & 0xffff0000u);
+}
+__device__ __forceinline__ void load_pair(const float *p, float &a, float &b) {
+    const float2 v = *reinterpret_cast<const float2 *>(p);
+    a = v.x;
+    b = v.y;
+}
+
+// At most 4 wavefronts per SIMD: the scheduler then keeps the eight loads of
+// a step in flight instead of trading them for occupancy.
 template <typename T, int EMAX>
-__global__ __launch_bounds__(256) void bwd_dwg_kernel(const T *__restrict__ x,
-                                                      const float *__restrict__ dl, int T_, int d,
-                                                      int E, float *__restrict__ dwg) {
-    __shared__ float part[4][EMAX][64];
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int i = blockIdx.x * 64 + lane;
-    const int t0 = (int)((int64_t)T_ * wave / 4), t1 = (int)((int64_t)T_ * (wave + 1) / 4);
-    float acc[EMAX];
+__global__ __launch_bounds__(DWG_THREADS) __attribute__((amdgpu_waves_per_eu(1, 4)))
+void bwd_dwg_part_kernel(
+    const T *__restrict__ x, const float *__restrict__ dl, int T_, int d, int E, int chunks,
+    float *__restrict__ part) {
+    __shared__ float dls[DWG_SB][EMAX];
+    const int i = 2 * (blockIdx.x * DWG_THREADS + threadIdx.x);
+    const int xi = min(i, d - 2);       // columns past d load a valid pair, never stored
+    const int c = blockIdx.y;
+    const int t_beg = (int)((int64_t)T_ * c / chunks), t_end = (int)((int64_t)T_ * (c + 1) / chunks);
+    float acc[2][EMAX];
 #pragma unroll
-    for (int e = 0; e < EMAX; ++e) acc[e] = 0.0f;
-    // Slots e >= E read column E - 1 (a valid element) and are never
-    // stored; the clamp bound sits in a vector register so that the
-    // compiler does not hoist EMAX uniform compares into scalar registers.
-    int last;
-    asm volatile("v_mov_b32 %0, %1" : "=v"(last) : "s"(E - 1));
-    if (i < d)
-        for (int t = t0; t < t1; ++t) {
-            const float xv = to_f32(x[(size_t)t * d + i]);
-            const float *dlt = dl + (size_t)t * E;
-#pragma unroll
-            for (int e = 0; e < EMAX; ++e) acc[e] += xv * dlt[min(e, last)];
+    for (int e = 0; e < EMAX; ++e) acc[0][e] = acc[1][e] = 0.0f;
+    for (int t0 = t_beg; t0 < t_end; t0 += DWG_SB) {
+        const int n = min(DWG_SB, t_end - t0);
+        __syncthreads();
+        for (int j = threadIdx.x; j < DWG_SB * EMAX; j += DWG_THREADS) {
+            const int tt = j / EMAX, e = j % EMAX;
+            dls[tt][e] = (tt < n && e < E) ? dl[(size_t)(t0 + tt) * E + e] : 0.0f;
         }
+        __syncthreads();
+        const T *xr = x + (size_t)t0 * d + xi;
+        int tt = 0;
+        for (; tt + 8 <= n; tt += 8) {     // eight token rows in flight
+            float xa[8], xb[8];
 #pragma unroll
-    for (int e = 0; e < EMAX; ++e) part[wave][e][lane] = acc[e];
-    __syncthreads();
-    if (wave != 0 || i >= d) return;
-    for (int e = 0; e < E; ++e)
-        dwg[(size_t)i * E + e] = (part[0][e][lane] + part[1][e][lane]) +
-                                 (part[2][e][lane] + part[3][e][lane]);
+            for (int u = 0; u < 8; ++u) load_pair(xr + (size_t)(tt + u) * d, xa[u], xb[u]);
+            // issue the eight loads before any use (the scheduler would
+            // otherwise wait on each one in turn)
+            __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int e = 0; e < EMAX; ++e) {
+                    const float v = dls[tt + u][e];
+                    acc[0][e] += xa[u] * v;
+                    acc[1][e] += xb[u] * v;
+                }
+        }
+        for (; tt < n; ++tt) {
+            float xa, xb;
+            load_pair(xr + (size_t)tt * d, xa, xb);
+#pragma unroll
+            for (int e = 0; e < EMAX; ++e) {
+                const float v = dls[tt][e];
+                acc[0][e] += xa * v;
+                acc[1][e] += xb * v;
+            }
+        }
+    }
+    if (i >= d) return;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float *out = part + ((size_t)c * d + i + h) * E;
+#pragma unroll
+        for (int e = 0; e < EMAX; ++e)
+            if (e < E) out[e] = acc[h][e];
+    }
+}
+
+__global__ __launch_bounds__(256) void bwd_dwg_sum_kernel(const float *__restrict__ part,
+                                                          int chunks, size_t n,
+                                                          float *__restrict__ dwg) {
+    const size_t j = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (j >= n) return;
+    float s = 0.0f;
+    for (int c = 0; c < chunks; ++c) s += part[(size_t)c * n + j];
+    dwg[j] = s;
 }
 
 template <typename T>
-hipError_t launch_dwg(const T *x, const float *dl, int T_, int d, int E, float *dwg,
-                      hipStream_t stream) {
-    const dim3 grid((d + 63) / 64), block(256);
-    if (E <= 8)
-        hipLaunchKernelGGL((bwd_dwg_kernel<T, 8>), grid, block, 0, stream, x, dl, T_, d, E, dwg);
-    else if (E <= 16)
-        hipLaunchKernelGGL((bwd_dwg_kernel<T, 16>), grid, block, 0, stream, x, dl, T_, d, E, dwg);
-    else if (E <= 32)
-        hipLaunchKernelGGL((bwd_dwg_kernel<T, 32>), grid, block, 0, stream, x, dl, T_, d, E, dwg);
-    else
-        hipLaunchKernelGGL((bwd_dwg_kernel<T, 64>), grid, block, 0, stream, x, dl, T_, d, E, dwg);
+hipError_t launch_dwg(const T *x, const float *dl, int T_, int d, int E, float *part,
+                      float *dwg, hipStream_t stream) {
+    const int chunks = dwg_chunks(T_, E);
+    const dim3 grid((d + DWG_COLS - 1) / DWG_COLS, chunks), block(DWG_THREADS);
+    switch (dwg_emax(E)) {
+    case 8:
+        hipLaunchKernelGGL((bwd_dwg_part_kernel<T, 8>), grid, block, 0, stream, x, dl, T_, d, E,
+                           chunks, part);
+        break;
+    case 16:
+        hipLaunchKernelGGL((bwd_dwg_part_kernel<T, 16>), grid, block, 0, stream, x, dl, T_, d, E,
+                           chunks, part);
+        break;
+    case 32:
+        hipLaunchKernelGGL((bwd_dwg_part_kernel<T, 32>), grid, block, 0, stream, x, dl, T_, d, E,
+                           chunks, part);
+        break;
+    default:
+        hipLaunchKernelGGL((bwd_dwg_part_kernel<T, 64>), grid, block, 0, stream, x, dl, T_, d, E,
+                           chunks, part);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t n = (size_t)d * E;
+    hipLaunchKernelGGL(bwd_dwg_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                       part, chunks, n, dwg);
     return hipGetLastError();
 }
 
@@ -500,6 +584,7 @@ hipError_t run_backward_t(const moe_shape_t &s, const T *x, const T *wg, const T
     T *dG = reinterpret_cast<T *>(base + L.dg);
     T *dU = reinterpret_cast<T *>(base + L.du);
     float *dl = reinterpret_cast<float *>(base + L.dl);
+    float *dwgp = reinterpret_cast<float *>(base + L.dwgp);
 
     hipError_t e = launch_route(s, x, wg, idx, w, str);
     if (e == hipSuccess) e = launch_dispatch(s, x, idx, counts, offsets, pos, xp, str);
@@ -605,7 +690,7 @@ hipError_t run_backward_t(const moe_shape_t &s, const T *x, const T *wg, const T
     if (e == hipSuccess)
         e = gemm<T, OP_MNC, OP_MNC, GROUP_K, EPI_STORE>(a, E * tiles_of(f) * tiles_of(d), str);
     // router gradient
-    if (e == hipSuccess) e = launch_dwg<T>(x, dl, Tn, d, E, dwg, str);
+    if (e == hipSuccess) e = launch_dwg<T>(x, dl, Tn, d, E, dwgp, dwg, str);
     return e;
 }
 
@@ -632,6 +717,7 @@ BackwardLayout plan_backward(const moe_shape_t &s) {
     L.dg = off;      off += a256(R * f * eb);
     L.du = off;      off += a256(R * f * eb);
     L.dl = off;      off += a256(T * E * 4);
+    L.dwgp = off;    off += a256((size_t)DWG_PARTS * d * 4);   // chunks x E <= DWG_PARTS
     L.total = off;
     return L;
 }

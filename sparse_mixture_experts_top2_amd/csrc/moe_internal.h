@@ -37,7 +37,7 @@ Layout plan_workspace(const moe_shape_t &s);
 // recomputed g, u (fp32) and h, the expert outputs o (later the per-row
 // input gradients), dO, dG, dU (layer dtype) and the router gradient dl.
 struct BackwardLayout {
-    size_t idx, w, counts, offsets, pos, xp, g, u, h, o, dout, dg, du, dl, total;
+    size_t idx, w, counts, offsets, pos, xp, g, u, h, o, dout, dg, du, dl, dwgp, total;
 };
 BackwardLayout plan_backward(const moe_shape_t &s);
 hipError_t launch_backward(const moe_shape_t &s, const void *x, const void *wg, const void *w1,

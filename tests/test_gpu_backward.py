@@ -72,6 +72,8 @@ CASES = [
     sw(400, 96, 200, E=4, dtype=W.F32, seed=409),
     sw(600, 256, 512, E=4, seed=411),                 # 2 row tiles per expert, both
                                                       # K-contiguous-weight products
+    sw(2000, 64, 128, E=64, seed=412),                # router gradient: 8 token chunks
+                                                      # of 250, several staged blocks
 ]
 
 
