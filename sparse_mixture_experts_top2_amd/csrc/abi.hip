@@ -26,9 +26,13 @@ Layout plan_workspace(const moe_shape_t &s) {
     L.xn = off;      off += align256(T * d * eb);
     L.xp = off;      off += align256(rows * d * eb);
     L.h = off;       off += align256(rows * f * eb);
-    // o: at decode sizes room for the int8 path's K-slice partial sums
-    const size_t o_parts = T <= (size_t)kDecodeMaxT ? (size_t)kDownParts : 1;
+    // o: at decode sizes room for the int8 path's K-slice partial sums, at
+    // bf16 prefill sizes for the down product's K parts
+    const size_t o_parts = T <= (size_t)kDecodeMaxT ? (size_t)kDownParts
+                           : s.dtype == MOE_BF16    ? (size_t)kMaxDownSplit
+                                                    : 1;
     L.o = off;       off += align256(o_parts * rows * d * sizeof(float));
+    L.parts = off;   off += align256(sizeof(int32_t));
     L.total = off;
     return L;
 }
@@ -127,8 +131,20 @@ hipError_t run_layer(const moe_shape_t &s, const void *x, const void *g, float e
         if (e == hipSuccess) e = launch_dispatch(s, xin, idx, counts, offsets, pos, xp, str);
         if (e == hipSuccess) e = launch_gateup(s, xp, counts, offsets, w1, w3, h, str);
     }
-    if (e == hipSuccess) e = launch_down(s, h, counts, offsets, w2, o, str);
-    if (e == hipSuccess) e = launch_combine(s, o, pos, w, y, str, res);
+    // bf16 prefill: the down product may be cut into K parts (the kernel
+    // picks the count from the expert counts); the combine adds them.
+    const int *parts_dev = nullptr;
+    if (e == hipSuccess && s.dtype == MOE_BF16 && s.T > kDecodeMaxT) {
+        int *pd = reinterpret_cast<int *>(base + L.parts);
+        const hipError_t de = launch_down_split_bf16(
+            routed_rows(s), s.n_experts, static_cast<const uint16_t *>(h), counts, offsets,
+            static_cast<const uint16_t *>(w2), s.d_ff, s.d_model, 0,
+            (size_t)routed_rows(s) * s.d_model, o, pd, str);
+        if (de == hipSuccess) parts_dev = pd;
+        else if (de != hipErrorNotSupported) e = de;
+    }
+    if (e == hipSuccess && !parts_dev) e = launch_down(s, h, counts, offsets, w2, o, str);
+    if (e == hipSuccess) e = launch_combine(s, o, pos, w, y, str, res, 1, parts_dev);
     return e;
 }
 

@@ -22,14 +22,17 @@ namespace {
 // template parameter so that the slot loops are straight-line code.
 // With parts > 1, o holds that many partial sums (K slices of the down
 // projection), part_stride4 float4s apart; each expert row is their sum,
-// slice 0 first, before it is weighted.
+// slice 0 first, before it is weighted.  With parts_dev the count is read
+// from device memory (the prefill down kernel stores its choice there).
 template <bool BF16_OUT, int K>
 __global__ __launch_bounds__(256) void combine_kernel(const float4 *__restrict__ o,
                                                       const int32_t *__restrict__ pos,
                                                       const float *__restrict__ w, int n_tok,
                                                       int d4, int chunk4, const void *res,
                                                       void *y, int parts,
-                                                      size_t part_stride4) {
+                                                      size_t part_stride4,
+                                                      const int *__restrict__ parts_dev) {
+    if (parts_dev) parts = *parts_dev;
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= n_tok) return;
@@ -89,24 +92,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const float4 *__restrict__
 template <bool BF16_OUT>
 hipError_t launch_combine_t(const moe_shape_t &s, dim3 grid, const float4 *o, const int32_t *pos,
                             const float *w, int d4, int chunk4, const void *res, void *y,
-                            int parts, size_t ps4, hipStream_t stream) {
+                            int parts, size_t ps4, const int *parts_dev, hipStream_t stream) {
     const dim3 block(256);
     switch (s.top_k) {
     case 1:
         hipLaunchKernelGGL((combine_kernel<BF16_OUT, 1>), grid, block, 0, stream, o, pos, w, s.T,
-                           d4, chunk4, res, y, parts, ps4);
+                           d4, chunk4, res, y, parts, ps4, parts_dev);
         break;
     case 2:
         hipLaunchKernelGGL((combine_kernel<BF16_OUT, 2>), grid, block, 0, stream, o, pos, w, s.T,
-                           d4, chunk4, res, y, parts, ps4);
+                           d4, chunk4, res, y, parts, ps4, parts_dev);
         break;
     case 3:
         hipLaunchKernelGGL((combine_kernel<BF16_OUT, 3>), grid, block, 0, stream, o, pos, w, s.T,
-                           d4, chunk4, res, y, parts, ps4);
+                           d4, chunk4, res, y, parts, ps4, parts_dev);
         break;
     case 4:
         hipLaunchKernelGGL((combine_kernel<BF16_OUT, 4>), grid, block, 0, stream, o, pos, w, s.T,
-                           d4, chunk4, res, y, parts, ps4);
+                           d4, chunk4, res, y, parts, ps4, parts_dev);
         break;
     default:
         return hipErrorInvalidValue;
@@ -118,7 +121,7 @@ hipError_t launch_combine_t(const moe_shape_t &s, dim3 grid, const float4 *o, co
 
 hipError_t launch_combine(const moe_shape_t &s, const float *o, const int32_t *pos,
                           const float *w, void *y, hipStream_t stream, const void *res,
-                          int parts) {
+                          int parts, const int *parts_dev) {
     if (s.T == 0) return hipSuccess;
     const int d4 = s.d_model / 4;
     // Column chunks of whole 64-vector passes, enough for ~512 workgroups.
@@ -131,8 +134,9 @@ hipError_t launch_combine(const moe_shape_t &s, const float *o, const int32_t *p
     const size_t ps4 = (size_t)routed_rows(s) * d4;
     if (s.dtype == MOE_BF16)
         return launch_combine_t<true>(s, grid, o4, pos, w, d4, chunk4, res, y, parts, ps4,
-                                      stream);
-    return launch_combine_t<false>(s, grid, o4, pos, w, d4, chunk4, res, y, parts, ps4, stream);
+                                      parts_dev, stream);
+    return launch_combine_t<false>(s, grid, o4, pos, w, d4, chunk4, res, y, parts, ps4,
+                                   parts_dev, stream);
 }
 
 }  // namespace moe

@@ -22,6 +22,8 @@
 //    fixed tree order.  HBM-bound: only the selected experts' weights are
 //    read, each byte once.
 // Both fuse silu(g) * u into the gate/up epilogue and round h to bf16.
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -341,6 +343,31 @@ __device__ __forceinline__ void static_for_from(F &&f) {
 template <int N, typename F>
 __device__ __forceinline__ void static_for(F &&f) { static_for_from<0, N>(f); }
 
+// Parts for the prefill down product.  A launch runs ceil(tiles / 8) tiles
+// per XCD, cu_per_xcd at a time (one workgroup per CU); when the last round
+// is mostly empty, cutting every tile's reduction in S parts makes S times
+// as many tiles of 1/S the length, which fill the rounds better.  Each
+// extra part costs a pass over the fp32 partial sums (written here, read by
+// the combine), about a fifth of a round at the 8x7B shape.  Returns the S
+// in 1..kMaxDownSplit with the least estimated time (ties: fewer parts).
+__host__ __device__ inline int down_split_parts(int mt_total, int n_cols, int cu_per_xcd,
+                                                int k_stages) {
+    if (cu_per_xcd <= 0) return 1;
+    const int64_t tiles = (int64_t)mt_total * n_cols;
+    int best = 1;
+    float best_cost = 0.0f;
+    for (int S = 1; S <= kMaxDownSplit && S <= k_stages; ++S) {
+        const int64_t per_xcd = (tiles * S + 7) / 8;
+        const int64_t rounds = (per_xcd + cu_per_xcd - 1) / cu_per_xcd;
+        const float cost = (float)rounds / (float)S + 0.2f * (float)(S - 1);
+        if (S == 1 || cost < best_cost) {
+            best = S;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
 // With NMAT = 2 and GU, the body also stores the gate and up products
 // themselves (fp32, row-major like h) to g_out / u_out, for the backward,
 // which needs them for the SwiGLU derivative.
@@ -353,10 +380,18 @@ __device__ __forceinline__ void static_for(F &&f) { static_for_from<0, N>(f); }
 // as da and writes dg = da * u * silu'(g) and du = da * silu(g) (bf16) from
 // g_in / u_in (fp32), all [rows, N].
 //
+// KSPLIT (NMAT = 1): the reduction is cut into `parts` contiguous runs of
+// whole K stages, part p writing its fp32 partial sums to C + p *
+// part_stride.  The flat tile list treats (part, column tile) as one column
+// index, part slowest, so the parts of a tile run in the same tile group.
+// With parts = 0 the body picks the count itself from the expert counts
+// (down_split_parts, cu_per_xcd CUs per XCD) and workgroup 0 stores it to
+// parts_out for the combine.
+//
 // Kernels wrap the body (below); the forward's take exactly the parameters
 // they always had, so their registers and code do not change.
 enum { BT_NONE = 0, BT_STORE = 1, BT_DSWIGLU = 2 };
-template <int NMAT, bool GU, int BT = BT_NONE>
+template <int NMAT, bool GU, int BT = BT_NONE, bool KSPLIT = false>
 __device__ __forceinline__ void prefill_dma_body(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B0,
     const uint16_t *__restrict__ B1, void *__restrict__ C, const int32_t *__restrict__ counts,
@@ -364,8 +399,10 @@ __device__ __forceinline__ void prefill_dma_body(
     float *__restrict__ g_out, float *__restrict__ u_out,
     const uint16_t *__restrict__ A2 = nullptr, const uint16_t *__restrict__ B2 = nullptr,
     int K1 = 0, const float *__restrict__ g_in = nullptr, const float *__restrict__ u_in = nullptr,
-    uint16_t *__restrict__ dg_out = nullptr, uint16_t *__restrict__ du_out = nullptr) {
+    uint16_t *__restrict__ dg_out = nullptr, uint16_t *__restrict__ du_out = nullptr,
+    int parts = 1, size_t part_stride = 0, int cu_per_xcd = 0, int *parts_out = nullptr) {
     static_assert(BT == BT_NONE || (NMAT == 1 && !GU), "backward products take one matrix");
+    static_assert(!KSPLIT || (NMAT == 1 && BT == BT_NONE), "split reductions store fp32 C");
     constexpr int NW = PWM * PWN;
     constexpr int TM = PBM / PWM, TN = PBN / PWN;
     constexpr int MB = TM / 32, NB = TN / 32;
@@ -374,9 +411,23 @@ __device__ __forceinline__ void prefill_dma_body(
     constexpr int BI = DB_BYTES / 1024 / NW;   // B load instructions per wave per stage
     static_assert(NMAT == 1 || NB % 2 == 0, "gate/up blocks come in pairs");
 
-    const int n_tiles = N / BNM;
+    const int n_cols = N / BNM;
+    if constexpr (KSPLIT) {
+        if (parts == 0) {
+            int mt_total = 0;
+            for (int i = 0; i < E; ++i) mt_total += (counts[i] + PBM - 1) / PBM;
+            parts = down_split_parts(mt_total, n_cols, cu_per_xcd, K / DBK);
+            if (blockIdx.x == 0 && threadIdx.x == 0) *parts_out = parts;
+        }
+    }
+    const int n_tiles = KSPLIT ? n_cols * parts : n_cols;
     int e, row0, row_end, nt;
     if (!prefill_tile(counts, offsets, E, n_tiles, e, row0, row_end, nt)) return;
+    int part = 0;
+    if constexpr (KSPLIT) {
+        part = nt / n_cols;
+        nt -= part * n_cols;
+    }
     const int n0 = nt * BNM;
 
     // One array per ring slot: the compiler then knows that the LDS-DMA
@@ -573,9 +624,14 @@ __device__ __forceinline__ void prefill_dma_body(
     // to it (harmless re-reads into free slots), so the steady-state loop has
     // no branches and every wait count is a constant; the rings are drained
     // before the epilogue reuses them.
-    int nk = K / DBK;
+    int nk = K / DBK, kt0 = 0;
     if constexpr (BT != BT_NONE) nk = (A2 ? 2 * K1 : K1) / DBK;
-    auto kclamp = [&](int kt) { return min(kt, nk - 1) * DBK; };
+    if constexpr (KSPLIT) {
+        const int all = K / DBK;
+        kt0 = (int)((int64_t)all * part / parts);
+        nk = (int)((int64_t)all * (part + 1) / parts) - kt0;
+    }
+    auto kclamp = [&](int kt) { return (kt0 + min(kt, nk - 1)) * DBK; };
     constexpr int LA = DAS - 1, LB = DBS - 1;      // lookahead of each ring
     constexpr int WAIT = DAS > DBS ? AI : DBS > DAS ? BI : 0;
     auto issue_step = [&](auto s_c, int kt) MOE_INLINE {   // loads of step kt (slot s)
@@ -686,6 +742,10 @@ __device__ __forceinline__ void prefill_dma_body(
                         const float sg = 1.0f / (1.0f + expf(-g));
                         dg_out[ci] = (uint16_t)f32_to_bf16(da * u * sg * (1.0f + g * (1.0f - sg)));
                         du_out[ci] = (uint16_t)f32_to_bf16(da * g * sg);
+                    } else if constexpr (KSPLIT) {
+                        if (row < row_end)
+                            static_cast<float *>(C)[(size_t)part * part_stride +
+                                                    (size_t)row * N + col] = acc[i][j][qq];
                     } else {
                         if (row < row_end)
                             static_cast<float *>(C)[(size_t)row * N + col] = acc[i][j][qq];
@@ -711,6 +771,17 @@ __global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_dma_gu_kernel(
     const int32_t *__restrict__ offsets, int E, int K, int N, int a_rows,
     float *__restrict__ g_out, float *__restrict__ u_out) {
     prefill_dma_body<2, true>(A, B0, B1, C, counts, offsets, E, K, N, a_rows, g_out, u_out);
+}
+
+// The down product with its reduction cut into `parts` partial sums.
+__global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_dma_down_split_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, float *__restrict__ C,
+    const int32_t *__restrict__ counts, const int32_t *__restrict__ offsets, int E, int K, int N,
+    int a_rows, int parts, size_t part_stride, int cu_per_xcd, int *__restrict__ parts_out) {
+    prefill_dma_body<1, false, BT_NONE, true>(A, B, nullptr, C, counts, offsets, E, K, N, a_rows,
+                                              nullptr, nullptr, nullptr, nullptr, 0, nullptr,
+                                              nullptr, nullptr, nullptr, parts, part_stride,
+                                              cu_per_xcd, parts_out);
 }
 
 // Backward products with a K-contiguous B (see prefill_dma_body).
@@ -925,6 +996,28 @@ hipError_t launch_bt_dswiglu_bf16(int rows, int E, const uint16_t *A, const uint
     const int grid = prefill_grid(rows, E, N / PBN);
     hipLaunchKernelGGL(prefill_dma_bt_dswiglu_kernel, dim3(grid), dim3(PWM * PWN * 64), 0,
                        stream, A, B, counts, offsets, E, K1, N, rows, g, u, dg, du);
+    return hipGetLastError();
+}
+
+hipError_t launch_down_split_bf16(int rows, int E, const uint16_t *h, const int32_t *counts,
+                                  const int32_t *offsets, const uint16_t *w2, int K, int N,
+                                  int parts, size_t part_stride, float *o, int *parts_out,
+                                  hipStream_t stream) {
+    if (rows <= 0 || parts < 0 || parts > kMaxDownSplit || K % DBK != 0 ||
+        K / DBK < kMaxDownSplit || N % PBN != 0 || (parts == 0 && !parts_out))
+        return hipErrorNotSupported;
+    int cu_per_xcd = 0;
+    if (parts == 0) {
+        int dev = 0, cus = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        cu_per_xcd = std::max(1, cus / 8);
+    }
+    const int grid = prefill_grid(rows, E, (N / PBN) * (parts ? parts : kMaxDownSplit));
+    hipLaunchKernelGGL(prefill_dma_down_split_kernel, dim3(grid), dim3(PWM * PWN * 64), 0, stream,
+                       h, w2, o, counts, offsets, E, K, N, rows, parts, part_stride, cu_per_xcd,
+                       parts_out);
     return hipGetLastError();
 }
 

@@ -20,14 +20,17 @@ constexpr int kMaxTopK = 4;     // experts per token
 constexpr int kDecodeMaxT = 32;
 // K slices of the int8-weight down projection at decode sizes; the combine
 // adds the slices in order.  The workspace's o region holds this many
-// copies of o when T <= kDecodeMaxT.
+// copies of o when T <= kDecodeMaxT (kMaxDownSplit copies above it).
 #ifndef MOE_DOWN_PARTS
 #define MOE_DOWN_PARTS 4
 #endif
 constexpr int kDownParts = MOE_DOWN_PARTS;
+// Most K parts the prefill down product is cut into (see launch_down_split_bf16).
+constexpr int kMaxDownSplit = 2;
 
+// parts: one int32, the K part count the prefill down kernel chose.
 struct Layout {
-    size_t idx, w, counts, offsets, pos, src, xn, xp, h, o, total;
+    size_t idx, w, counts, offsets, pos, src, xn, xp, h, o, parts, total;
 };
 
 // Byte offsets of every workspace region for this shape (256-byte aligned).
@@ -87,9 +90,12 @@ hipError_t launch_down(const moe_shape_t &s, const void *h, const int32_t *count
 // y = w0 o[pos0] + w1 o[pos1] + ... (+ res when res is not NULL), rounded
 // once.  With parts > 1, o holds that many partial sums, each kT x d, one
 // after the other; every row is their sum in order before it is weighted.
+// parts_dev (device int32, may be NULL): the part count is read there
+// instead of taken from `parts`.
 hipError_t launch_combine(const moe_shape_t &s, const float *o, const int32_t *pos,
                           const float *w, void *y, hipStream_t stream,
-                          const void *res = nullptr, int parts = 1);
+                          const void *res = nullptr, int parts = 1,
+                          const int *parts_dev = nullptr);
 
 // Weight-only int8 (experts_w8.hip).  W [n_mat, K, N] (dtype) -> codes
 // q [n_mat, K, N] and per-column scales [n_mat, N].
@@ -139,6 +145,17 @@ hipError_t launch_bt_store_bf16(int rows, int E, const uint16_t *A, const uint16
 hipError_t launch_bt_dswiglu_bf16(int rows, int E, const uint16_t *A, const uint16_t *B, int K1,
                                   int N, const int32_t *counts, const int32_t *offsets,
                                   const float *g, const float *u, uint16_t *dg, uint16_t *du,
+                                  hipStream_t stream);
+// Prefill down product with the reduction over K cut into `parts` runs of
+// whole 64-wide stages: part p stores the sum over its run at o + p *
+// part_stride (fp32 [rows, N] each).  parts = 0 lets the kernel choose 1 to
+// kMaxDownSplit from the expert counts and the device's CU count, and store
+// its choice to *parts_out (device memory) for the combine.
+// hipErrorNotSupported unless K % 64 == 0, K / 64 >= kMaxDownSplit and
+// N % 256 == 0.
+hipError_t launch_down_split_bf16(int rows, int E, const uint16_t *h, const int32_t *counts,
+                                  const int32_t *offsets, const uint16_t *w2, int K, int N,
+                                  int parts, size_t part_stride, float *o, int *parts_out,
                                   hipStream_t stream);
 hipError_t launch_down_bf16(const moe_shape_t &s, const uint16_t *h, const int32_t *counts,
                             const int32_t *offsets, const uint16_t *w2, float *o,

@@ -160,11 +160,17 @@ def test_zero_tokens_is_a_valid_no_op():
 def test_workspace_grows_with_every_dimension():
     lib = moe.load_library()
     base = lib.moe_workspace_bytes(ctypes.byref(shape()))
-    for kw in (dict(T=65), dict(d=136), dict(f=264), dict(dtype=moe.MOE_F32)):
+    for kw in (dict(T=65), dict(d=136), dict(f=264)):
         assert lib.moe_workspace_bytes(ctypes.byref(shape(**kw))) > base, kw
     # decode shape: xp 64 x 4096 bf16, h 64 x 14336 bf16, o 64 x 4096 fp32 and small tables
     s = shape(T=32, d=4096, f=14336)
     assert lib.moe_workspace_bytes(ctypes.byref(s)) >= 64 * (4096 * 2 + 14336 * 2 + 4096 * 4)
+    # bf16 prefill: o holds the down product's two K parts
+    s = shape(T=4096, d=4096, f=14336)
+    assert lib.moe_workspace_bytes(ctypes.byref(s)) >= 8192 * (4096 * 2 + 14336 * 2 + 2 * 4096 * 4)
+    # fp32 prefill: one o, 4-byte xp and h
+    s = shape(T=4096, d=4096, f=14336, dtype=moe.MOE_F32)
+    assert lib.moe_workspace_bytes(ctypes.byref(s)) >= 8192 * (4096 * 4 + 14336 * 4 + 4096 * 4)
 
 
 def test_python_binding_refuses_cpu_tensors():
