@@ -120,13 +120,14 @@ def measure(wl_name, steps, warmup):
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     ms = ms_events
 
-    # The dominant kernel alone: gate/up over the same routed rows.
+    # The dominant step alone: gate/up over the same routed rows, with the
+    # layer's workspace so that it runs the layer's kernels.
     idx, w = moe.route(inp.x, inp.w_gate)
     counts, offsets, pos, xp = moe.dispatch(inp.x, idx, wl.E)
     h = torch.empty(2 * wl.T, wl.f, dtype=inp.x.dtype, device=dev)
 
     def gateup():
-        moe.expert_gateup(xp, counts, offsets, inp.w1, inp.w3, out=h)
+        moe.expert_gateup(xp, counts, offsets, inp.w1, inp.w3, out=h, workspace=ws)
 
     for _ in range(max(2, warmup)):
         gateup()

@@ -144,6 +144,19 @@ int moe_expert_gateup(const moe_shape_t *shape, const void *xp, const int32_t *c
                       const int32_t *offsets, const void *w1, const void *w3, void *h,
                       void *stream);
 
+/* moe_expert_gateup with the layer's workspace (ws / ws_bytes: at least
+ * moe_workspace_bytes(shape)), running exactly the kernels the layer runs
+ * for this step.  At bf16 decode sizes (T <= 32) the layer cuts the
+ * (expert, 128-column) units of the last round of workgroups in two halves
+ * along d_model and adds the halves' fp32 partial sums (kept in the
+ * workspace) before the SiLU; elsewhere this is moe_expert_gateup.  Same
+ * result as moe_expert_gateup up to the order of that one addition.  The
+ * workspace region written must not overlap xp, h, counts or offsets
+ * (MOE_ERR_ALIAS). */
+int moe_expert_gateup_ws(const moe_shape_t *shape, const void *xp, const int32_t *counts,
+                         const int32_t *offsets, const void *w1, const void *w3, void *h,
+                         void *ws, size_t ws_bytes, void *stream);
+
 /* Expert down: the second half of section 04's SwiGLU block,
  *   o[r, :] = h[r] w2[e]   for r in [offsets[e], offsets[e+1]),
  * fp32 accumulation, o fp32 [R, d].  o must not overlap h. */

@@ -27,7 +27,8 @@ STATUS_NAMES = ["MOE_OK", "MOE_ERR_NULL", "MOE_ERR_SHAPE", "MOE_ERR_DTYPE", "MOE
                 "MOE_ERR_ALIAS", "MOE_ERR_WORKSPACE", "MOE_ERR_UNSUPPORTED", "MOE_ERR_HIP"]
 EXPORTED = ["moe_status_str", "moe_workspace_bytes", "moe_route", "moe_route_probs",
             "moe_dispatch",
-            "moe_expert_gateup", "moe_expert_down", "moe_experts", "moe_combine",
+            "moe_expert_gateup", "moe_expert_gateup_ws", "moe_expert_down", "moe_experts",
+            "moe_combine",
             "moe_forward", "moe_rmsnorm_route", "moe_block_forward", "moe_quantize_int8",
             "moe_expert_gateup_w8", "moe_expert_down_w8", "moe_forward_w8",
             "moe_backward_workspace_bytes", "moe_backward"]
@@ -72,6 +73,8 @@ def load_library(path: Optional[str] = None):
     lib.moe_dispatch.restype = I
     lib.moe_expert_gateup.argtypes = [S, P, P, P, P, P, P, P]
     lib.moe_expert_gateup.restype = I
+    lib.moe_expert_gateup_ws.argtypes = [S, P, P, P, P, P, P, P, Z, P]
+    lib.moe_expert_gateup_ws.restype = I
     lib.moe_expert_down.argtypes = [S, P, P, P, P, P, P]
     lib.moe_expert_down.restype = I
     lib.moe_experts.argtypes = [S, P, P, P, P, P, P, P, P, Z, P]
@@ -252,8 +255,10 @@ def _expert_args(xp, counts, offsets, w, w_name, top_k):
 
 def expert_gateup(xp: torch.Tensor, counts: torch.Tensor, offsets: torch.Tensor,
                   w1: torch.Tensor, w3: torch.Tensor, out: Optional[torch.Tensor] = None,
-                  top_k: int = 2):
-    """h = silu(xp w1[e]) * (xp w3[e]) per expert row group; [kT, f]."""
+                  top_k: int = 2, workspace: Optional[torch.Tensor] = None):
+    """h = silu(xp w1[e]) * (xp w3[e]) per expert row group; [kT, f].  With
+    a workspace (alloc_workspace) the call runs exactly the layer's kernels
+    for this step (moe_expert_gateup_ws)."""
     T, d, E = _expert_args(xp, counts, offsets, w1, "w1", top_k)
     R = xp.shape[0]
     f = w1.shape[2]
@@ -262,10 +267,17 @@ def expert_gateup(xp: torch.Tensor, counts: torch.Tensor, offsets: torch.Tensor,
     h = out if out is not None else torch.empty(R, f, dtype=xp.dtype, device=xp.device)
     _need(h, "h", xp.dtype, xp.device, (R, f))
     shape = make_shape(T, d, f, E, xp.dtype, top_k)
-    st = load_library().moe_expert_gateup(ctypes.byref(shape), _ptr(xp), _ptr(counts),
-                                          _ptr(offsets), _ptr(w1), _ptr(w3), _ptr(h),
-                                          _stream(xp.device))
-    _check(st, "moe_expert_gateup")
+    lib = load_library()
+    if workspace is None:
+        st = lib.moe_expert_gateup(ctypes.byref(shape), _ptr(xp), _ptr(counts), _ptr(offsets),
+                                   _ptr(w1), _ptr(w3), _ptr(h), _stream(xp.device))
+        _check(st, "moe_expert_gateup")
+    else:
+        _need(workspace, "workspace", torch.uint8, xp.device)
+        st = lib.moe_expert_gateup_ws(ctypes.byref(shape), _ptr(xp), _ptr(counts),
+                                      _ptr(offsets), _ptr(w1), _ptr(w3), _ptr(h),
+                                      _ptr(workspace), workspace.numel(), _stream(xp.device))
+        _check(st, "moe_expert_gateup_ws")
     return h
 
 

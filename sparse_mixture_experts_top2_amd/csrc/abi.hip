@@ -33,6 +33,9 @@ Layout plan_workspace(const moe_shape_t &s) {
                                                     : 1;
     L.o = off;       off += align256(o_parts * rows * d * sizeof(float));
     L.parts = off;   off += align256(sizeof(int32_t));
+    // gpart: partial sums of the decode gate/up units cut in K halves
+    const bool dec16 = T <= (size_t)kDecodeMaxT && s.dtype == MOE_BF16;
+    L.gpart = off;   off += dec16 ? align256(kDecodeTailBytes) : 0;
     L.total = off;
     return L;
 }
@@ -126,7 +129,8 @@ hipError_t run_layer(const moe_shape_t &s, const void *x, const void *g, float e
             e = launch_gateup_bf16(s, static_cast<const uint16_t *>(xin), counts, offsets,
                                    static_cast<const uint16_t *>(w1),
                                    static_cast<const uint16_t *>(w3),
-                                   static_cast<uint16_t *>(h), str, src);
+                                   static_cast<uint16_t *>(h), str, src,
+                                   reinterpret_cast<float *>(base + L.gpart));
     } else {
         if (e == hipSuccess) e = launch_dispatch(s, xin, idx, counts, offsets, pos, xp, str);
         if (e == hipSuccess) e = launch_gateup(s, xp, counts, offsets, w1, w3, h, str);
@@ -245,6 +249,37 @@ int moe_expert_gateup(const moe_shape_t *s, const void *xp, const int32_t *count
     if (overlap(h, R * s->d_ff * eb, xp, R * s->d_model * eb))
         return MOE_ERR_ALIAS;
     return hip_status(launch_gateup(*s, xp, counts, offsets, w1, w3, h, (hipStream_t)stream));
+}
+
+int moe_expert_gateup_ws(const moe_shape_t *s, const void *xp, const int32_t *counts,
+                         const int32_t *offsets, const void *w1, const void *w3, void *h,
+                         void *ws, size_t ws_bytes, void *stream) {
+    int st = check_shape(s);
+    if (st) return st;
+    if (s->T == 0) return MOE_OK;  // nothing to read or write
+    if (!xp || !counts || !offsets || !w1 || !w3 || !h || !ws) return MOE_ERR_NULL;
+    if (misaligned(xp) || misaligned(counts) || misaligned(offsets) || misaligned(w1) ||
+        misaligned(w3) || misaligned(h) || misaligned(ws))
+        return MOE_ERR_ALIGN;
+    const Layout L = plan_workspace(*s);
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    const size_t eb = elem_bytes(s->dtype);
+    const size_t R = (size_t)routed_rows(*s);
+    if (overlap(h, R * s->d_ff * eb, xp, R * s->d_model * eb)) return MOE_ERR_ALIAS;
+    if (!(s->dtype == MOE_BF16 && s->T <= kDecodeMaxT))
+        return hip_status(launch_gateup(*s, xp, counts, offsets, w1, w3, h, (hipStream_t)stream));
+    // the only workspace region written: the decode kernel's partial sums
+    char *gp = static_cast<char *>(ws) + L.gpart;
+    const size_t gb = kDecodeTailBytes;
+    const size_t E = (size_t)s->n_experts;
+    if (overlap(gp, gb, xp, R * s->d_model * eb) || overlap(gp, gb, h, R * s->d_ff * eb) ||
+        overlap(gp, gb, counts, E * 4) || overlap(gp, gb, offsets, (E + 1) * 4))
+        return MOE_ERR_ALIAS;
+    return hip_status(launch_gateup_bf16(*s, static_cast<const uint16_t *>(xp), counts, offsets,
+                                         static_cast<const uint16_t *>(w1),
+                                         static_cast<const uint16_t *>(w3),
+                                         static_cast<uint16_t *>(h), (hipStream_t)stream, nullptr,
+                                         reinterpret_cast<float *>(gp)));
 }
 
 int moe_expert_down(const moe_shape_t *s, const void *h, const int32_t *counts,

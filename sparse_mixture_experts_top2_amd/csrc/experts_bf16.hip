@@ -815,20 +815,44 @@ inline int prefill_grid(int rows, int E, int n_tiles) {
 constexpr int DWAVES = 8;     // wavefronts per workgroup, splitting K
 constexpr int DCOLS = 128;    // weight columns per workgroup
 
-template <int MB, int NMAT>
+// Decode workgroup units are (expert, column block) pairs, unit u = e * nb +
+// column block.  TAIL (gate/up): a 1-D grid where the first n_full units run
+// whole and the rest are cut in two K halves (workgroups n_full + 2 j and
+// n_full + 2 j + 1 for unit n_full + j), which store their fp32 sums of
+// x W1 and x W3 to part slot j (see decode_tail_slot) for
+// decode_tail_finish_kernel.  One workgroup per CU at a time: when the
+// units leave the last round at most half full, its units cut in halves
+// fill one round of half the length.
+constexpr int DTAIL_ROWS = 32;   // rows of a part slot (an expert's rows at decode sizes)
+__device__ __forceinline__ size_t decode_tail_slot(int j, int half, int m) {
+    return ((size_t)(j * 2 + half) * 2 + m) * DTAIL_ROWS * DCOLS;
+}
+template <int MB, int NMAT, bool TAIL = false>
 __global__ __launch_bounds__(DWAVES * 64) void decode_gemm_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B0,
     const uint16_t *__restrict__ B1, void *__restrict__ C, const int32_t *__restrict__ counts,
     const int32_t *__restrict__ offsets, int K, int N, int a_rows,
-    const int32_t *__restrict__ src) {
-    const int e = blockIdx.y;
+    const int32_t *__restrict__ src, float *__restrict__ part = nullptr, int n_full = 0,
+    int nb_cols = 0) {
+    static_assert(!TAIL || (NMAT == 2 && MB * 16 <= DTAIL_ROWS), "the tail split is for gate/up");
+    int e = blockIdx.y, cblk = blockIdx.x, half = -1, slot = 0;
+    if constexpr (TAIL) {
+        int unit = blockIdx.x;
+        if (unit >= n_full) {
+            slot = (unit - n_full) >> 1;
+            half = (unit - n_full) & 1;
+            unit = n_full + slot;
+        }
+        e = unit / nb_cols;
+        cblk = unit - e * nb_cols;
+    }
     const int Me = counts[e];
     if (Me == 0) return;  // an expert no token chose: its weights are never read
     const int r0 = offsets[e];
     const int nmb = min(MB, (Me + 15) >> 4);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int kg = lane >> 4, nb = lane & 15;
-    const int col = blockIdx.x * DCOLS + nb * 8;
+    const int col = cblk * DCOLS + nb * 8;
     const bool col_ok = col < N;
 
     const uint16_t *Bp[NMAT];
@@ -852,8 +876,15 @@ __global__ __launch_bounds__(DWAVES * 64) void decode_gemm_kernel(
 #pragma unroll
             for (int c = 0; c < 8; ++c) acc[m][i][c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int nks = (K + 31) >> 5;
-    const int ks0 = (nks * wave) / DWAVES, ks1 = (nks * (wave + 1)) / DWAVES;
+    int nks = (K + 31) >> 5, kbase = 0;
+    if constexpr (TAIL) {
+        if (half >= 0) {
+            const int all = nks;
+            kbase = (all * half) / 2;
+            nks = (all * (half + 1)) / 2 - kbase;
+        }
+    }
+    const int ks0 = kbase + (nks * wave) / DWAVES, ks1 = kbase + (nks * (wave + 1)) / DWAVES;
     for (int ks = ks0; ks < ks1; ++ks) {
         const int k = ks * 32 + kg * 8;
         uint4 rb[NMAT][8];
@@ -912,7 +943,19 @@ __global__ __launch_bounds__(DWAVES * 64) void decode_gemm_kernel(
         for (int j = 0; j < 4; ++j) {
             const int row = i * 16 + 4 * kg + j;
             if (row >= Me) continue;
-            if (NMAT == 2) {
+            if (TAIL && half >= 0) {
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    float *dst = part + decode_tail_slot(slot, half, m) + (size_t)row * DCOLS +
+                                 nb * 8;
+                    *reinterpret_cast<float4 *>(dst) =
+                        make_float4(acc[m][i][0][j], acc[m][i][1][j], acc[m][i][2][j],
+                                    acc[m][i][3][j]);
+                    *reinterpret_cast<float4 *>(dst + 4) =
+                        make_float4(acc[m][i][4][j], acc[m][i][5][j], acc[m][i][6][j],
+                                    acc[m][i][7][j]);
+                }
+            } else if (NMAT == 2) {
                 uint32_t p[4];
 #pragma unroll
                 for (int c = 0; c < 8; c += 2) {
@@ -933,20 +976,77 @@ __global__ __launch_bounds__(DWAVES * 64) void decode_gemm_kernel(
     }
 }
 
+// h = silu(g0 + g1) * (u0 + u1) for the units a TAIL launch cut in two:
+// workgroup j takes part slot j (unit n_full + j).
+__global__ __launch_bounds__(256) void decode_tail_finish_kernel(
+    const float *__restrict__ part, const int32_t *__restrict__ counts,
+    const int32_t *__restrict__ offsets, int n_full, int nb_cols, int N,
+    uint16_t *__restrict__ h) {
+    const int j = blockIdx.x, unit = n_full + j;
+    const int e = unit / nb_cols, cblk = unit - e * nb_cols;
+    const int Me = counts[e], r0 = offsets[e];
+    const float *g0 = part + decode_tail_slot(j, 0, 0), *u0 = part + decode_tail_slot(j, 0, 1);
+    const float *g1 = part + decode_tail_slot(j, 1, 0), *u1 = part + decode_tail_slot(j, 1, 1);
+    for (int i = threadIdx.x; i < Me * DCOLS; i += 256) {
+        const int row = i / DCOLS, c = i % DCOLS, col = cblk * DCOLS + c;
+        if (col >= N) continue;
+        const float g = g0[i] + g1[i], u = u0[i] + u1[i];
+        h[(size_t)(r0 + row) * N + col] = (uint16_t)f32_to_bf16(silu_f32(g) * u);
+    }
+}
+
+// Units of a decode gate/up to run whole (the rest are cut in K halves),
+// or -1 for none cut: with every expert holding rows (as at decode sizes)
+// a launch has E * ceil(f / 128) units, one per CU at a time; cutting pays
+// when the last round would be at most half full.
+int decode_tail_full_units(int f, int E) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        return -1;
+    const int units = (f + DCOLS - 1) / DCOLS * E;
+    const int rem = units % cus;
+    if (units <= cus || rem == 0 || 2 * rem > cus || rem > kDecodeTailMaxUnits) return -1;
+    return units - rem;
+}
+
+template <int MB>
+hipError_t launch_decode_gateup(const moe_shape_t &s, const uint16_t *xp,
+                                const int32_t *counts, const int32_t *offsets,
+                                const uint16_t *w1, const uint16_t *w3, uint16_t *h,
+                                hipStream_t stream, const int32_t *src, float *gpart) {
+    const int d = s.d_model, f = s.d_ff, E = s.n_experts, rows = routed_rows(s);
+    const int nb_cols = (f + DCOLS - 1) / DCOLS;
+    const int n_full = gpart ? decode_tail_full_units(f, E) : -1;
+    if (n_full >= 0) {
+        const int n_cut = nb_cols * E - n_full;
+        hipLaunchKernelGGL((decode_gemm_kernel<MB, 2, true>), dim3(n_full + 2 * n_cut),
+                           dim3(DWAVES * 64), 0, stream, xp, w1, w3, h, counts, offsets, d, f,
+                           rows, src, gpart, n_full, nb_cols);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(decode_tail_finish_kernel, dim3(n_cut), dim3(256), 0, stream, gpart,
+                           counts, offsets, n_full, nb_cols, f, h);
+    } else {
+        hipLaunchKernelGGL((decode_gemm_kernel<MB, 2>), dim3(nb_cols, E), dim3(DWAVES * 64), 0,
+                           stream, xp, w1, w3, h, counts, offsets, d, f, rows, src, nullptr, 0,
+                           0);
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gateup_bf16(const moe_shape_t &s, const uint16_t *xp, const int32_t *counts,
                               const int32_t *offsets, const uint16_t *w1, const uint16_t *w3,
-                              uint16_t *h, hipStream_t stream, const int32_t *src) {
+                              uint16_t *h, hipStream_t stream, const int32_t *src,
+                              float *gpart) {
     const int d = s.d_model, f = s.d_ff, E = s.n_experts, rows = routed_rows(s);
     if (s.T <= 16) {
-        hipLaunchKernelGGL((decode_gemm_kernel<1, 2>), dim3((f + DCOLS - 1) / DCOLS, E),
-                           dim3(DWAVES * 64), 0, stream, xp, w1, w3, h, counts, offsets, d, f,
-                           rows, src);
+        return launch_decode_gateup<1>(s, xp, counts, offsets, w1, w3, h, stream, src, gpart);
     } else if (s.T <= kDecodeMaxT) {
-        hipLaunchKernelGGL((decode_gemm_kernel<2, 2>), dim3((f + DCOLS - 1) / DCOLS, E),
-                           dim3(DWAVES * 64), 0, stream, xp, w1, w3, h, counts, offsets, d, f,
-                           rows, src);
+        return launch_decode_gateup<2>(s, xp, counts, offsets, w1, w3, h, stream, src, gpart);
     } else if (src) {
         return hipErrorInvalidValue;   // the gather is only built into the decode kernels
     } else {

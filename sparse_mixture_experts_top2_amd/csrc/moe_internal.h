@@ -27,10 +27,16 @@ constexpr int kDecodeMaxT = 32;
 constexpr int kDownParts = MOE_DOWN_PARTS;
 // Most K parts the prefill down product is cut into (see launch_down_split_bf16).
 constexpr int kMaxDownSplit = 2;
+// Decode gate/up: most (expert, 128-column) units cut in K halves to fill the
+// last round of workgroups, and the fp32 partial sums they need (2 halves x
+// 2 matrices x 32 rows x 128 columns each).
+constexpr int kDecodeTailMaxUnits = 256;
+constexpr size_t kDecodeTailBytes = (size_t)kDecodeTailMaxUnits * 2 * 2 * 32 * 128 * 4;
 
 // parts: one int32, the K part count the prefill down kernel chose.
+// gpart: at bf16 decode sizes, the decode gate/up's K-half partial sums.
 struct Layout {
-    size_t idx, w, counts, offsets, pos, src, xn, xp, h, o, parts, total;
+    size_t idx, w, counts, offsets, pos, src, xn, xp, h, o, parts, gpart, total;
 };
 
 // Byte offsets of every workspace region for this shape (256-byte aligned).
@@ -120,10 +126,13 @@ hipError_t launch_down_f32(const moe_shape_t &s, const float *h, const int32_t *
                            const int32_t *offsets, const float *w2, float *o,
                            hipStream_t stream);
 // With src not NULL (only for T <= kDecodeMaxT), row r of the activations
-// is read from xp + src[r] * d_model, i.e. xp is x itself.
+// is read from xp + src[r] * d_model, i.e. xp is x itself.  gpart (fp32,
+// kDecodeTailBytes, may be NULL): room for the K halves' partial sums of
+// the units the decode kernel cuts to fill its last round of workgroups.
 hipError_t launch_gateup_bf16(const moe_shape_t &s, const uint16_t *xp, const int32_t *counts,
                               const int32_t *offsets, const uint16_t *w1, const uint16_t *w3,
-                              uint16_t *h, hipStream_t stream, const int32_t *src = nullptr);
+                              uint16_t *h, hipStream_t stream, const int32_t *src = nullptr,
+                              float *gpart = nullptr);
 // The prefill gate/up kernel storing g and u (fp32 [kT, f]) beside h, for
 // the backward.  hipErrorNotSupported when the shape does not take the
 // direct-to-LDS kernel (T <= kDecodeMaxT, d % 64 or f % 128 not zero).

@@ -173,6 +173,29 @@ def test_workspace_grows_with_every_dimension():
     assert lib.moe_workspace_bytes(ctypes.byref(s)) >= 8192 * (4096 * 4 + 14336 * 4 + 4096 * 4)
 
 
+def test_gateup_with_workspace_checks():
+    lib = moe.load_library()
+    name = lambda st: moe.STATUS_NAMES[st]
+    s = shape(T=32, d=256, f=512)
+    need = lib.moe_workspace_bytes(ctypes.byref(s))
+    W0 = 0x40000000
+    tail = ctypes.c_void_p(W0 + need - 1024)   # inside the partial-sum region (last)
+
+    def G(xp=P16, c=P16, o=P16, h=P16B, ws=ctypes.c_void_p(W0), n=need, sh=s):
+        return name(lib.moe_expert_gateup_ws(ctypes.byref(sh), xp, c, o, P16, P16, h, ws, n,
+                                             None))
+    assert G(ws=None) == "MOE_ERR_NULL"
+    assert G(h=None) == "MOE_ERR_NULL"
+    assert G(ws=P17) == "MOE_ERR_ALIGN"
+    assert G(n=need - 1) == "MOE_ERR_WORKSPACE"
+    assert G(h=P16) == "MOE_ERR_ALIAS"        # h over xp
+    assert G(h=tail) == "MOE_ERR_ALIAS"       # h inside the region the call writes
+    assert G(c=tail) == "MOE_ERR_ALIAS"       # counts there
+    assert G(o=tail) == "MOE_ERR_ALIAS"       # offsets there
+    assert G(xp=tail) == "MOE_ERR_ALIAS"      # xp there
+    assert G(sh=shape(T=0)) == "MOE_OK"
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(4, 16, dtype=torch.bfloat16)

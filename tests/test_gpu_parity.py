@@ -127,6 +127,50 @@ def test_each_step(wl):
     assert err <= (2 ** -8 if wl.dtype == W.BF16 else 1e-6), err
 
 
+# Decode shapes whose gate/up cuts its last round of (expert, 128-column)
+# units in two K halves on a 256-CU device: 40 experts x 8 column blocks =
+# 320 units, 64 past the first full round.
+TAIL_CASES = [
+    W.small_workload(32, 128, 1024, E=40, seed=21),
+    W.small_workload(12, 256, 1024, E=40, seed=22),
+    W.small_workload(32, 200, 1016, E=40, seed=23),            # ragged last column block
+]
+
+
+def tail_cut_applies(wl) -> bool:
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    units = wl.E * ((wl.f + 127) // 128)
+    rem = units % cus
+    return units > cus and 0 < rem and 2 * rem <= cus
+
+
+@pytest.mark.parametrize("wl", TAIL_CASES, ids=lambda w: w.name)
+def test_decode_tail_cut(wl):
+    """The layer and the gate/up stage with a workspace (which cut the last
+    round's units in K halves) against the oracle."""
+    if not tail_cut_applies(wl):
+        pytest.skip("this device's CU count does not cut these units")
+    announce(f"decode tail cut {wl.name}")
+    inp = checked_inputs(wl)
+    run_forward_parity(inp)
+    k = wl.top_k
+    g = inp.to(DEV)
+    idx_o, _ = oracle.route(inp.x, inp.w_gate, top_k=k)
+    c_o, off_o, _, src_o = oracle.dispatch(idx_o, wl.E)
+    xp_o = inp.x[torch.as_tensor(src_o // k)].contiguous()
+    expert_of_row = np.repeat(np.arange(wl.E, dtype=np.int32), c_o)
+    c_d = torch.as_tensor(c_o, device=DEV)
+    off_d = torch.as_tensor(off_o, device=DEV)
+    ws = moe.alloc_workspace(wl.T, wl.d, wl.f, wl.E, g.x.dtype, DEV, top_k=k)
+    h_ws = moe.expert_gateup(xp_o.to(DEV), c_d, off_d, g.w1, g.w3, top_k=k, workspace=ws)
+    h = moe.expert_gateup(xp_o.to(DEV), c_d, off_d, g.w1, g.w3, top_k=k)
+    h_ref = oracle.expert_hidden(xp_o, expert_of_row, inp.w1, inp.w3)
+    for name, got in (("with workspace", h_ws), ("without", h)):
+        err = row_max_rel_err(got, h_ref)
+        announce(f"  gate/up {name} row-max-rel err {err:.3e}")
+        assert err <= 1e-2, (name, err)
+
+
 def _biased(wl, bias_col, screen=True):
     """A constant input column with router weights `bias_col` on it (folded
     in by the generator, before any near-tie screening)."""
