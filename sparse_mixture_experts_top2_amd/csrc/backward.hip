@@ -357,9 +357,11 @@ template <typename T>
 __global__ __launch_bounds__(256) void bwd_route_grad_kernel(
     const T *__restrict__ dy, const float *__restrict__ o, const int32_t *__restrict__ idx,
     const float *__restrict__ w, const int32_t *__restrict__ pos, int d, int E, int k,
-    T *__restrict__ dO, float *__restrict__ dl) {
+    T *__restrict__ dO, float *__restrict__ dl, const int *__restrict__ o_parts,
+    size_t part_stride) {
     __shared__ float part[4][kMaxTopK];
     const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const bool two = o_parts && *o_parts == 2;   // o = part 0 + part 1
     float dws[kMaxTopK];
 #pragma unroll
     for (int s = 0; s < kMaxTopK; ++s) {
@@ -369,7 +371,9 @@ __global__ __launch_bounds__(256) void bwd_route_grad_kernel(
         float acc = 0.0f;
         for (int i = tid; i < d; i += 256) {
             const float g = to_f32(dy[(size_t)t * d + i]);
-            acc += g * o[(size_t)r * d + i];
+            float ov = o[(size_t)r * d + i];
+            if (two) ov += o[part_stride + (size_t)r * d + i];
+            acc += g * ov;
             dO[(size_t)r * d + i] = from_f32<T>(ws * g);
         }
 #pragma unroll
@@ -400,19 +404,27 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float *__restrict__ d
                                                      const int32_t *__restrict__ pos,
                                                      const float *__restrict__ dl,
                                                      const T *__restrict__ wg, int d, int E,
-                                                     int k, T *__restrict__ dx) {
+                                                     int k, T *__restrict__ dx,
+                                                     const int *__restrict__ dxp_parts,
+                                                     size_t part_stride) {
     __shared__ float dlt[kMaxExperts];
     const int t = blockIdx.x, tid = threadIdx.x;
+    const bool two = dxp_parts && *dxp_parts == 2;   // dXp = part 0 + part 1
     if (tid < E) dlt[tid] = dl[(size_t)t * E + tid];
     __syncthreads();
     int rows[kMaxTopK];
 #pragma unroll
     for (int s = 0; s < kMaxTopK; ++s) rows[s] = s < k ? pos[k * t + s] : 0;
+    auto row_value = [&](int r, int i) {
+        float v = dxp[(size_t)r * d + i];
+        if (two) v += dxp[part_stride + (size_t)r * d + i];
+        return v;
+    };
     for (int i = tid; i < d; i += 256) {
-        float v = dxp[(size_t)rows[0] * d + i];
+        float v = row_value(rows[0], i);
 #pragma unroll
         for (int s = 1; s < kMaxTopK; ++s)
-            if (s < k) v += dxp[(size_t)rows[s] * d + i];
+            if (s < k) v += row_value(rows[s], i);
         float r = 0.0f;
         for (int e = 0; e < E; ++e) r += dlt[e] * to_f32(wg[(size_t)i * E + e]);
         dx[(size_t)t * d + i] = from_f32<T>(v + r);
@@ -585,6 +597,8 @@ hipError_t run_backward_t(const moe_shape_t &s, const T *x, const T *wg, const T
     T *dU = reinterpret_cast<T *>(base + L.du);
     float *dl = reinterpret_cast<float *>(base + L.dl);
     float *dwgp = reinterpret_cast<float *>(base + L.dwgp);
+    int *nparts = reinterpret_cast<int *>(base + L.nparts);   // o, dXp
+    const size_t pstride = (size_t)R * d;                       // floats between parts
 
     hipError_t e = launch_route(s, x, wg, idx, w, str);
     if (e == hipSuccess) e = launch_dispatch(s, x, idx, counts, offsets, pos, xp, str);
@@ -615,9 +629,18 @@ hipError_t run_backward_t(const moe_shape_t &s, const T *x, const T *wg, const T
         if (e == hipSuccess)
             e = gemm<T, OP_KC, OP_MNC, GROUP_ROWS, EPI_UP>(a, rt * tiles_of(f), str);
     }
-    // o = h W2[e]: the forward's down kernels for bf16, the generic GEMM for fp32
+    // o = h W2[e]: the forward's down kernels for bf16 (at prefill sizes the
+    // variant that cuts the reduction in parts; route_grad adds them), the
+    // generic GEMM for fp32
+    const int *o_parts = nullptr;
     if constexpr (sizeof(T) == 2) {
-        if (e == hipSuccess) e = launch_down_bf16(s, H, counts, offsets, w2, O, str);
+        if (e == hipSuccess) {
+            const hipError_t de = launch_down_split_bf16(R, E, H, counts, offsets, w2, f, d, 0,
+                                                         pstride, O, nparts, str);
+            if (de == hipSuccess) o_parts = nparts;
+            else if (de == hipErrorNotSupported) e = launch_down_bf16(s, H, counts, offsets, w2, O, str);
+            else e = de;
+        }
     } else {
         a = GemmArgs{};
         a.counts = counts; a.offsets = offsets; a.E = E;
@@ -629,7 +652,7 @@ hipError_t run_backward_t(const moe_shape_t &s, const T *x, const T *wg, const T
     // routing-weight gradients, dO and dl
     if (e == hipSuccess && Tn > 0) {
         hipLaunchKernelGGL(bwd_route_grad_kernel<T>, dim3(Tn), dim3(256), 0, str, dy, O, idx, w,
-                           pos, d, E, k, dO, dl);
+                           pos, d, E, k, dO, dl, o_parts, pstride);
         e = hipGetLastError();
     }
     // da = dO W2[e]^T, with dg, du in the epilogue.  The weight matrices are
@@ -652,12 +675,15 @@ hipError_t run_backward_t(const moe_shape_t &s, const T *x, const T *wg, const T
     if (e == hipSuccess && !da_done)
         e = gemm<T, OP_KC, OP_KC, GROUP_ROWS, EPI_DSWIGLU>(a, rt * tiles_of(f), str);
     // dXp = dG W1[e]^T + dU W3[e]^T   (into the o region): one pass over a
-    // reduction of 2 f on the pipeline above, else two generic GEMMs
+    // reduction of 2 f on the pipeline above (cut in parts that the dx
+    // kernel adds), else two generic GEMMs
+    const int *dxp_parts = nullptr;
     if constexpr (sizeof(T) == 2) {
         if (e == hipSuccess) {
-            const hipError_t fe = launch_bt_store_bf16(R, E, dG, w1, dU, w3, f, d, counts,
-                                                       offsets, O, str);
+            const hipError_t fe = launch_bt_store_split_bf16(R, E, dG, w1, dU, w3, f, d, counts,
+                                                             offsets, O, pstride, nparts + 1, str);
             dxp_done = fe == hipSuccess;
+            if (dxp_done) dxp_parts = nparts + 1;
             if (fe != hipErrorNotSupported && fe != hipSuccess) e = fe;
         }
     }
@@ -673,7 +699,7 @@ hipError_t run_backward_t(const moe_shape_t &s, const T *x, const T *wg, const T
     // dx
     if (e == hipSuccess && Tn > 0) {
         hipLaunchKernelGGL(bwd_dx_kernel<T>, dim3(Tn), dim3(256), 0, str, O, pos, dl, wg, d, E, k,
-                           dx);
+                           dx, dxp_parts, pstride);
         e = hipGetLastError();
     }
     // weight gradients: dW1[e] = xp_e^T dG_e, dW3[e] = xp_e^T dU_e, dW2[e] = h_e^T dO_e
@@ -712,12 +738,13 @@ BackwardLayout plan_backward(const moe_shape_t &s) {
     L.g = off;       off += a256(R * f * 4);
     L.u = off;       off += a256(R * f * 4);
     L.h = off;       off += a256(R * f * eb);
-    L.o = off;       off += a256(R * d * 4);
+    L.o = off;       off += a256((size_t)kMaxDownSplit * R * d * 4);
     L.dout = off;    off += a256(R * d * eb);
     L.dg = off;      off += a256(R * f * eb);
     L.du = off;      off += a256(R * f * eb);
     L.dl = off;      off += a256(T * E * 4);
     L.dwgp = off;    off += a256((size_t)DWG_PARTS * d * 4);   // chunks x E <= DWG_PARTS
+    L.nparts = off;  off += a256(2 * sizeof(int32_t));
     L.total = off;
     return L;
 }

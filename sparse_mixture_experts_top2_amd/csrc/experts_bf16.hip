@@ -402,7 +402,7 @@ __device__ __forceinline__ void prefill_dma_body(
     uint16_t *__restrict__ dg_out = nullptr, uint16_t *__restrict__ du_out = nullptr,
     int parts = 1, size_t part_stride = 0, int cu_per_xcd = 0, int *parts_out = nullptr) {
     static_assert(BT == BT_NONE || (NMAT == 1 && !GU), "backward products take one matrix");
-    static_assert(!KSPLIT || (NMAT == 1 && BT == BT_NONE), "split reductions store fp32 C");
+    static_assert(!KSPLIT || (NMAT == 1 && BT != BT_DSWIGLU), "split reductions store fp32 C");
     constexpr int NW = PWM * PWN;
     constexpr int TM = PBM / PWM, TN = PBN / PWN;
     constexpr int MB = TM / 32, NB = TN / 32;
@@ -416,7 +416,8 @@ __device__ __forceinline__ void prefill_dma_body(
         if (parts == 0) {
             int mt_total = 0;
             for (int i = 0; i < E; ++i) mt_total += (counts[i] + PBM - 1) / PBM;
-            parts = down_split_parts(mt_total, n_cols, cu_per_xcd, K / DBK);
+            const int stages = (BT != BT_NONE ? (A2 ? 2 * K1 : K1) : K) / DBK;
+            parts = down_split_parts(mt_total, n_cols, cu_per_xcd, stages);
             if (blockIdx.x == 0 && threadIdx.x == 0) *parts_out = parts;
         }
     }
@@ -627,7 +628,7 @@ __device__ __forceinline__ void prefill_dma_body(
     int nk = K / DBK, kt0 = 0;
     if constexpr (BT != BT_NONE) nk = (A2 ? 2 * K1 : K1) / DBK;
     if constexpr (KSPLIT) {
-        const int all = K / DBK;
+        const int all = nk;
         kt0 = (int)((int64_t)all * part / parts);
         nk = (int)((int64_t)all * (part + 1) / parts) - kt0;
     }
@@ -782,6 +783,19 @@ __global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_dma_down_split_kern
                                               nullptr, nullptr, nullptr, nullptr, 0, nullptr,
                                               nullptr, nullptr, nullptr, parts, part_stride,
                                               cu_per_xcd, parts_out);
+}
+
+// dXp-style product (K-contiguous B, optional second operand pair) with its
+// reduction cut into parts, as the down product above.
+__global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_dma_bt_store_split_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, const uint16_t *__restrict__ A2,
+    const uint16_t *__restrict__ B2, float *__restrict__ C, const int32_t *__restrict__ counts,
+    const int32_t *__restrict__ offsets, int E, int K1, int N, int a_rows, size_t part_stride,
+    int cu_per_xcd, int *__restrict__ parts_out) {
+    prefill_dma_body<1, false, BT_STORE, true>(A, B, nullptr, C, counts, offsets, E, K1, N,
+                                               a_rows, nullptr, nullptr, A2, B2, K1, nullptr,
+                                               nullptr, nullptr, nullptr, 0, part_stride,
+                                               cu_per_xcd, parts_out);
 }
 
 // Backward products with a K-contiguous B (see prefill_dma_body).
@@ -1088,6 +1102,28 @@ hipError_t launch_bt_store_bf16(int rows, int E, const uint16_t *A, const uint16
     return hipGetLastError();
 }
 
+static int cus_per_xcd() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return -1;
+    return std::max(1, cus / 8);
+}
+
+hipError_t launch_bt_store_split_bf16(int rows, int E, const uint16_t *A, const uint16_t *B,
+                                      const uint16_t *A2, const uint16_t *B2, int K1, int N,
+                                      const int32_t *counts, const int32_t *offsets, float *C,
+                                      size_t part_stride, int *parts_out, hipStream_t stream) {
+    if (!bt_shape_ok(rows, K1, N) || !parts_out) return hipErrorNotSupported;
+    const int cpx = cus_per_xcd();
+    if (cpx < 0) return hipErrorNotSupported;
+    const int grid = prefill_grid(rows, E, (N / PBN) * kMaxDownSplit);
+    hipLaunchKernelGGL(prefill_dma_bt_store_split_kernel, dim3(grid), dim3(PWM * PWN * 64), 0,
+                       stream, A, B, A2, B2, C, counts, offsets, E, K1, N, rows, part_stride, cpx,
+                       parts_out);
+    return hipGetLastError();
+}
+
 hipError_t launch_bt_dswiglu_bf16(int rows, int E, const uint16_t *A, const uint16_t *B, int K1,
                                   int N, const int32_t *counts, const int32_t *offsets,
                                   const float *g, const float *u, uint16_t *dg, uint16_t *du,
@@ -1108,11 +1144,8 @@ hipError_t launch_down_split_bf16(int rows, int E, const uint16_t *h, const int3
         return hipErrorNotSupported;
     int cu_per_xcd = 0;
     if (parts == 0) {
-        int dev = 0, cus = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
-        cu_per_xcd = std::max(1, cus / 8);
+        cu_per_xcd = cus_per_xcd();
+        if (cu_per_xcd < 0) return hipErrorNotSupported;
     }
     const int grid = prefill_grid(rows, E, (N / PBN) * (parts ? parts : kMaxDownSplit));
     hipLaunchKernelGGL(prefill_dma_down_split_kernel, dim3(grid), dim3(PWM * PWN * 64), 0, stream,

@@ -45,8 +45,10 @@ Layout plan_workspace(const moe_shape_t &s);
 // Workspace of the backward (backward.hip): routing, grouped rows xp, the
 // recomputed g, u (fp32) and h, the expert outputs o (later the per-row
 // input gradients), dO, dG, dU (layer dtype) and the router gradient dl.
+// o holds kMaxDownSplit partial sums (the split products' K parts); nparts
+// two int32, the part counts the o and dXp products chose.
 struct BackwardLayout {
-    size_t idx, w, counts, offsets, pos, xp, g, u, h, o, dout, dg, du, dl, dwgp, total;
+    size_t idx, w, counts, offsets, pos, xp, g, u, h, o, dout, dg, du, dl, dwgp, nparts, total;
 };
 BackwardLayout plan_backward(const moe_shape_t &s);
 hipError_t launch_backward(const moe_shape_t &s, const void *x, const void *wg, const void *w1,
@@ -151,6 +153,13 @@ hipError_t launch_bt_store_bf16(int rows, int E, const uint16_t *A, const uint16
                                 const uint16_t *A2, const uint16_t *B2, int K1, int N,
                                 const int32_t *counts, const int32_t *offsets, float *C,
                                 hipStream_t stream);
+// launch_bt_store_bf16 with the reduction (K1 or 2 K1 stages) cut into
+// 1..kMaxDownSplit parts chosen on the device from the expert counts, part
+// p stored at C + p * part_stride, the count stored to *parts_out.
+hipError_t launch_bt_store_split_bf16(int rows, int E, const uint16_t *A, const uint16_t *B,
+                                      const uint16_t *A2, const uint16_t *B2, int K1, int N,
+                                      const int32_t *counts, const int32_t *offsets, float *C,
+                                      size_t part_stride, int *parts_out, hipStream_t stream);
 hipError_t launch_bt_dswiglu_bf16(int rows, int E, const uint16_t *A, const uint16_t *B, int K1,
                                   int N, const int32_t *counts, const int32_t *offsets,
                                   const float *g, const float *u, uint16_t *dg, uint16_t *du,
