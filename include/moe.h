@@ -57,6 +57,10 @@
 extern "C" {
 #endif
 
+/* The library is built with hidden visibility; these declarations are its
+ * only exported symbols. */
+#pragma GCC visibility push(default)
+
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
 
 typedef enum {
@@ -295,6 +299,8 @@ size_t moe_backward_workspace_bytes(const moe_shape_t *shape);
 int moe_backward(const moe_shape_t *shape, const void *x, const void *w_gate, const void *w1,
                  const void *w3, const void *w2, const void *dy, void *dx, float *dw_gate,
                  float *dw1, float *dw3, float *dw2, void *ws, size_t ws_bytes, void *stream);
+
+#pragma GCC visibility pop
 
 #ifdef __cplusplus
 }

@@ -31,8 +31,8 @@ def hipcc() -> str:
 
 
 def compile_flags():
-    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}",
-            "-Wall", "-Wno-unused-function",
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
+            f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 

@@ -35,6 +35,9 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert name in exported, name
         assert hasattr(moe.load_library(), name)
+    # and nothing else: the C++ internals are built with hidden visibility
+    code = set(re.findall(r"\b[TW] (\S+)", out))
+    assert code == set(declared_functions()), sorted(code - set(declared_functions()))
 
 
 def shape(T=64, d=128, f=256, E=8, k=2, dtype=moe.MOE_BF16):
