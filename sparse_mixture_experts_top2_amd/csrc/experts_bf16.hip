@@ -732,17 +732,36 @@ __device__ __forceinline__ void prefill_dma_body(
 #pragma unroll
             for (int j = 0; j < NB; ++j) {
                 const int col = n0 + wn * TN + j * 32 + (lane & 31);
+                // dswiglu: the block's 16 g and 16 u values are loaded
+                // first, unconditionally (rows clamped into the tile), so
+                // they are all in flight at once; only the stores depend on
+                // the row being inside the tile.
+                float gv[16], uv[16];
+                if constexpr (BT == BT_DSWIGLU) {
+#pragma unroll
+                    for (int qq = 0; qq < 16; ++qq) {
+                        const int row = min(row0 + wm * TM + i * 32 + 8 * (qq >> 2) +
+                                                4 * (lane >> 5) + (qq & 3),
+                                            row_end - 1);
+                        gv[qq] = g_in[(size_t)row * N + col];
+                        uv[qq] = u_in[(size_t)row * N + col];
+                    }
+                }
 #pragma unroll
                 for (int qq = 0; qq < 16; ++qq) {
                     const int row =
                         row0 + wm * TM + i * 32 + 8 * (qq >> 2) + 4 * (lane >> 5) + (qq & 3);
                     if constexpr (BT == BT_DSWIGLU) {
-                        if (row >= row_end) continue;
-                        const size_t ci = (size_t)row * N + col;
-                        const float da = acc[i][j][qq], g = g_in[ci], u = u_in[ci];
+                        const float da = acc[i][j][qq], g = gv[qq], u = uv[qq];
                         const float sg = 1.0f / (1.0f + expf(-g));
-                        dg_out[ci] = (uint16_t)f32_to_bf16(da * u * sg * (1.0f + g * (1.0f - sg)));
-                        du_out[ci] = (uint16_t)f32_to_bf16(da * g * sg);
+                        const uint16_t dgv =
+                            (uint16_t)f32_to_bf16(da * u * sg * (1.0f + g * (1.0f - sg)));
+                        const uint16_t duv = (uint16_t)f32_to_bf16(da * g * sg);
+                        if (row < row_end) {
+                            const size_t ci = (size_t)row * N + col;
+                            dg_out[ci] = dgv;
+                            du_out[ci] = duv;
+                        }
                     } else if constexpr (KSPLIT) {
                         if (row < row_end)
                             static_cast<float *>(C)[(size_t)part * part_stride +
