@@ -127,11 +127,12 @@ def test_zero_tokens_give_zero_weight_gradients():
 
 @pytest.mark.slow
 def test_backward_prefill_size_sampled():
-    """The 8x7B shape at T = 512 tokens (about 128 rows per expert), in one
-    call: dx of a sample of tokens against the oracle run on those tokens
-    alone (a token's dx depends on no other token).  The weight gradients
-    sum over every token and are checked at the smaller sizes above."""
-    wl = W.WORKLOADS["prefill_8x7b"].with_(T=512)
+    """The 8x7B prefill step the benchmark times (T = 4096, about 1024 rows
+    per expert, the K-parts and K-contiguous-weight kernels), in one call:
+    dx of a sample of tokens against the oracle run on those tokens alone (a
+    token's dx depends on no other token).  The weight gradients sum over
+    every token and are checked at the smaller sizes above."""
+    wl = W.WORKLOADS["prefill_8x7b"]
     announce("prefill-size backward: drawing inputs")
     inp = checked_inputs(wl)
     dy = make_dy(wl, wl.dtype)
