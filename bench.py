@@ -38,6 +38,14 @@ nine grouped GEMMs, 9 * 2 * kT * d * f FLOPs.
 received tokens for the decode step, 2 k T (3 d f) + 2 T d E FLOPs for the
 prefill.
 
+``other_configs``: the remaining workloads measured the same way (the tiny
+fp32 layer, whose kernels run on the vector ALUs, the skewed-routing 8x7B
+prefill and the larger-expert prefill), step time and layer roofline each.
+
+``ceilings``: context, not targets: what torch reaches on this GPU for a
+plain device copy (bytes read + written per second) and for one bf16
+matmul of the prefill's per-step expert shape [8192 x 4096] x [4096 x 14336].
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
 import argparse
@@ -53,6 +61,7 @@ if ROOT not in sys.path:
 METRIC = "MoE-layer tokens/s (8x7B shape, T=32 & T=4096); % of HBM / MFMA peak"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 vector ALU, TFLOP/s
 
 
 def log(msg):
@@ -76,6 +85,8 @@ def parse():
                     help="skip the int8-weight decode measurement")
     ap.add_argument("--no-backward", dest="backward", action="store_false",
                     help="skip the backward measurement")
+    ap.add_argument("--no-others", dest="others", action="store_false",
+                    help="skip the other workloads and the torch ceilings")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this size (for counter scaling)")
     return ap.parse_args()
@@ -140,8 +151,19 @@ def measure(wl_name, steps, warmup):
     gu_flops = 2.0 * (2 * wl.T) * wl.d * (2 * wl.f)
     layer_flops = wl.T * (2.0 * 2 * 3 * wl.d * wl.f + 2.0 * wl.d * wl.E)
     layer_bytes = active * 3 * wl.d * wl.f * eb + 2 * wl.T * wl.d * eb + wl.d * wl.E * eb
-    hbm_bound = wl.T <= 32
-    if hbm_bound:
+    hbm_bound = wl.T <= 32 and wl.dtype == W.BF16
+    if wl.dtype == W.F32:
+        # fp32 layers run on the vector ALUs (FMA), not the matrix cores
+        ach = gu_flops / (k_ms * 1e-3) / 1e12
+        roof = {"kernel": "expert gate/up (fp32 LDS-tiled FMA)", "bound": "alu",
+                "achieved": round(ach, 3), "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_FP32_TFLOPS, 5), "traffic": None,
+                "algorithmic_flops_per_launch": gu_flops, "avg_launch_ms": round(k_ms, 5)}
+        lay = layer_flops / (ms * 1e-3) / 1e12
+        layer = {"bound": "alu", "achieved": round(lay, 3), "peak": PEAK_FP32_TFLOPS,
+                 "unit": "TFLOP/s", "frac": round(lay / PEAK_FP32_TFLOPS, 5),
+                 "algorithmic_flops_per_step": layer_flops}
+    elif hbm_bound:
         ach = gu_bytes / (k_ms * 1e-3) / 1e9
         roof = {"kernel": "expert gate/up (weight-streaming MFMA)", "bound": "hbm",
                 "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -398,6 +420,52 @@ def copy_calibration(mib, steps):
                       "ms": round(ms, 5), "GBps_rw": round(2 * n * 4 / ms / 1e6, 1)}), flush=True)
 
 
+def measure_other(wl_name, steps, warmup):
+    """One more workload measured like the headline one, in brief."""
+    import torch
+    r = measure(wl_name, steps, warmup)
+    wl = r["wl"]
+    out = {"workload": wl_name, "value": round(r["tokens_per_s"], 1), "unit": "tokens/s",
+           "ms_per_step": round(r["ms"], 5), "steps": steps, "warmup": warmup,
+           "dtype": wl.dtype, "config": {"T": wl.T, "d_model": wl.d, "d_ff": wl.f,
+                                         "n_experts": wl.E, "top_k": 2},
+           "roofline": r["roofline"], "layer_roofline": r["layer_roofline"],
+           "expert_counts": r["counts"]}
+    del r
+    torch.cuda.empty_cache()
+    return out
+
+
+def measure_ceilings():
+    """torch on this GPU, for context: a 2 GiB device copy and a bf16 matmul
+    of the prefill's expert shape."""
+    import torch
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    n = (2 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    ms = time_region(lambda: dst.copy_(src), 20, stream)
+    copy_gbs = 2 * n * 4 / (ms * 1e-3) / 1e9
+    del src, dst
+    gen = torch.Generator(device=dev).manual_seed(7)
+    a = torch.randn(8192, 4096, generator=gen, device=dev).to(torch.bfloat16)
+    b = (torch.randn(4096, 14336, generator=gen, device=dev) * 0.015).to(torch.bfloat16)
+    c = torch.empty(8192, 14336, dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    mm_ms = time_region(lambda: torch.matmul(a, b, out=c), 20, stream)
+    mm_tf = 2.0 * 8192 * 4096 * 14336 / (mm_ms * 1e-3) / 1e12
+    del a, b, c
+    torch.cuda.empty_cache()
+    log(f"ceilings: copy {copy_gbs:.0f} GB/s (read + write); bf16 matmul {mm_tf:.0f} TFLOP/s")
+    return {"device_copy_GBps_read_plus_write": round(copy_gbs, 1),
+            "torch_matmul_bf16_8192x4096x14336_TFLOPs": round(mm_tf, 1),
+            "note": "context only: torch's own kernels on this GPU, not targets"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -450,6 +518,13 @@ def main():
                "expert_counts": r["counts"]}
         del r
         torch.cuda.empty_cache()
+    others = None
+    ceilings = None
+    if args.others:
+        others = [measure_other("tiny_fp32", 200, 20),
+                  measure_other("skewed_8x7b", 10, 3),
+                  measure_other("larger_expert", 10, 3)]
+        ceilings = measure_ceilings()
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(main_res, args.cpu_seconds)
@@ -479,6 +554,8 @@ def main():
         "top_k": topk or None,
         "w8": w8,
         "backward": bwd,
+        "other_configs": others,
+        "ceilings": ceilings,
     }
     print(json.dumps(out), flush=True)
 
