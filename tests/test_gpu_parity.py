@@ -171,6 +171,22 @@ def test_decode_tail_cut(wl):
         assert err <= 1e-2, (name, err)
 
 
+@pytest.mark.parametrize("wl", [SMALL[9], SMALL[1]], ids=lambda w: w.name)
+def test_gateup_with_workspace_off_decode_sizes(wl):
+    """Above decode sizes (and for fp32) the gate/up stage with a workspace
+    runs the same kernels as without one: bit-identical h."""
+    inp = checked_inputs(wl)
+    g = inp.to(DEV)
+    idx, _ = moe.route(g.x, g.w_gate)
+    counts, offsets, _, xp = moe.dispatch(g.x, idx, wl.E)
+    ws = moe.alloc_workspace(wl.T, wl.d, wl.f, wl.E, g.x.dtype, DEV)
+    h_ws = moe.expert_gateup(xp, counts, offsets, g.w1, g.w3, workspace=ws)
+    h = moe.expert_gateup(xp, counts, offsets, g.w1, g.w3)
+    torch.cuda.synchronize()
+    as_bits = (lambda t: t.view(torch.int16)) if g.x.dtype == torch.bfloat16 else (lambda t: t)
+    assert torch.equal(as_bits(h_ws), as_bits(h))
+
+
 def _biased(wl, bias_col, screen=True):
     """A constant input column with router weights `bias_col` on it (folded
     in by the generator, before any near-tie screening)."""
