@@ -232,17 +232,22 @@ int moe_block_forward(const moe_shape_t *shape, const void *h, const void *rms_w
  * accumulates in fp32 on the bf16 matrix cores. The scale multiplies the
  * finished sum of each output column.
  *
- * Codes have the weights' layout: q1, q3 int8 [E, d, f] and q2 int8
- * [E, f, d]. Scales are s1, s3 fp32 [E, f] and s2 fp32 [E, d]. */
+ * Codes of a matrix W [K, N] are stored with pairs of rows interleaved in
+ * groups of 8 columns, so that one 16-byte load holds 8 columns of two
+ * consecutive rows: the code of W[j, n] is byte
+ *   ((j / 2) * (N / 8) + n / 8) * 16 + (j % 2) * 8 + n % 8
+ * of the matrix, i.e. the array is int8 [K/2][N/8][2][8]. q1, q3 hold E
+ * such matrices of d x f, q2 E of f x d. Scales are s1, s3 fp32 [E, f] and
+ * s2 fp32 [E, d]. */
 
 /* Quantize n_mat matrices W [n_mat, K, N] (dtype MOE_F32 or MOE_BF16)
- * into codes q int8 [n_mat, K, N] and scales fp32 [n_mat, N]. Per column
- * n of each matrix:
+ * into codes q (n_mat K N bytes, in the row-pair layout above) and scales
+ * fp32 [n_mat, N]. Per column n of each matrix:
  *   s[n]   = max_j |W[j,n]| / 127                       (fp32 division)
  *   q[j,n] = rint(W[j,n] / s[n]) clamped to [-127, 127] (fp32 division,
  *            round half to even)
- * A zero column gets s = 0 and q = 0. N must be a positive multiple of 8
- * and n_mat at most 65535. Outputs must not overlap W or each other. The
+ * A zero column gets s = 0 and q = 0. K must be even and positive, N a
+ * positive multiple of 8, and n_mat at most 65535. Outputs must not overlap W or each other. The
  * call is a one-time preparation and runs on `stream` like every other
  * call. */
 int moe_quantize_int8(int n_mat, int K, int N, int dtype, const void *w, int8_t *q,

@@ -435,14 +435,18 @@ def block_forward(h: torch.Tensor, rms_weight: torch.Tensor, eps: float, w_gate:
 # Weight-only int8 expert weights (decode sizes: bf16 layers, T <= 32).
 
 def quantize_int8(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
-    """W [n, K, N] (bf16 or fp32) -> (codes int8 [n, K, N], scales fp32
-    [n, N]): one symmetric scale per output column, s = max|W| / 127,
-    q = rint(W / s) clamped to [-127, 127]."""
+    """W [n, K, N] (bf16 or fp32) -> (codes, scales fp32 [n, N]): one
+    symmetric scale per output column, s = max|W| / 127, q = rint(W / s)
+    clamped to [-127, 127].  The codes come in the kernels' row-pair layout,
+    int8 [n, K/2, N/8, 2, 8] (element [m, j//2, c//8, j%2, c%8] is the code
+    of W[m, j, c]); unpack_int8 gives them as [n, K, N]."""
     _need(w, "w")
     if w.dim() != 3:
         raise ValueError(f"w must be [n, K, N], got {tuple(w.shape)}")
     n, K, N = w.shape
-    q = torch.empty(n, K, N, dtype=torch.int8, device=w.device)
+    if K % 2 or N % 8:
+        raise ValueError(f"K must be even and N a multiple of 8, got K={K}, N={N}")
+    q = torch.empty(n, K // 2, N // 8, 2, 8, dtype=torch.int8, device=w.device)
     sc = torch.empty(n, N, dtype=torch.float32, device=w.device)
     st = load_library().moe_quantize_int8(n, K, N, _dtype_code(w.dtype), _ptr(w), _ptr(q),
                                           _ptr(sc), _stream(w.device))
@@ -450,8 +454,24 @@ def quantize_int8(w: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
     return q, sc
 
 
+def unpack_int8(q: torch.Tensor) -> torch.Tensor:
+    """Codes in the row-pair layout [n, K/2, N/8, 2, 8] -> [n, K, N]."""
+    n, kh, ng, two, eight = q.shape
+    if (two, eight) != (2, 8):
+        raise ValueError(f"not row-pair codes: {tuple(q.shape)}")
+    return q.permute(0, 1, 3, 2, 4).reshape(n, 2 * kh, 8 * ng)
+
+
+def _w8_dims(q: torch.Tensor, name: str):
+    """(E, K, N) of row-pair codes."""
+    if q.dim() != 5 or tuple(q.shape[3:]) != (2, 8):
+        raise ValueError(f"q{name} must be row-pair codes [E, K/2, N/8, 2, 8] "
+                         f"(quantize_int8), got {tuple(q.shape)}")
+    return q.shape[0], 2 * q.shape[1], 8 * q.shape[2]
+
+
 def _need_w8(q, sc, name, device, E, K, N):
-    _need(q, f"q{name}", torch.int8, device, (E, K, N))
+    _need(q, f"q{name}", torch.int8, device, (E, K // 2, N // 8, 2, 8))
     _need(sc, f"s{name}", torch.float32, device, (E, N))
 
 
@@ -462,7 +482,7 @@ def expert_gateup_w8(xp: torch.Tensor, counts: torch.Tensor, offsets: torch.Tens
     _need(xp, "xp", torch.bfloat16)
     R, d = xp.shape
     T = _routed_tokens(R, top_k, "xp")
-    E, _, f = q1.shape
+    E, _, f = _w8_dims(q1, "1")
     _need_w8(q1, s1, "1", xp.device, E, d, f)
     _need_w8(q3, s3, "3", xp.device, E, d, f)
     _need(counts, "counts", torch.int32, xp.device, (E,))
@@ -484,7 +504,7 @@ def expert_down_w8(h: torch.Tensor, counts: torch.Tensor, offsets: torch.Tensor,
     _need(h, "h", torch.bfloat16)
     R, f = h.shape
     T = _routed_tokens(R, top_k, "h")
-    E, _, d = q2.shape
+    E, _, d = _w8_dims(q2, "2")
     _need_w8(q2, s2, "2", h.device, E, f, d)
     _need(counts, "counts", torch.int32, h.device, (E,))
     _need(offsets, "offsets", torch.int32, h.device, (E + 1,))
@@ -509,7 +529,7 @@ def forward_w8(x: torch.Tensor, w_gate: torch.Tensor, q1: torch.Tensor, s1: torc
     _need(w_gate, "w_gate", x.dtype, x.device)
     E = w_gate.shape[1]
     _need(w_gate, "w_gate", shape=(d, E))
-    f = q1.shape[2]
+    f = _w8_dims(q1, "1")[2]
     _need_w8(q1, s1, "1", x.device, E, d, f)
     _need_w8(q3, s3, "3", x.device, E, d, f)
     _need_w8(q2, s2, "2", x.device, E, f, d)

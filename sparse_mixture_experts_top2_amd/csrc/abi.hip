@@ -411,7 +411,8 @@ int moe_block_forward(const moe_shape_t *s, const void *h, const void *rms_weigh
 int moe_quantize_int8(int n_mat, int K, int N, int dtype, const void *w, int8_t *q,
                       float *scale, void *stream) {
     if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_DTYPE;
-    if (n_mat < 1 || n_mat > 65535 || K < 1 || N < 8 || N % 8 != 0) return MOE_ERR_SHAPE;
+    if (n_mat < 1 || n_mat > 65535 || K < 2 || K % 2 != 0 || N < 8 || N % 8 != 0)
+        return MOE_ERR_SHAPE;
     if (!w || !q || !scale) return MOE_ERR_NULL;
     if (misaligned(w) || misaligned(q) || misaligned(scale)) return MOE_ERR_ALIGN;
     const size_t n = (size_t)n_mat * K * N;

@@ -13,7 +13,9 @@
 //
 //  * quantize_int8_kernel: s[n] = max_j |W[j, n]| / 127 and
 //    q = rint(W / s) clamped to [-127, 127], in fp32 (s = 0, q = 0 for a
-//    zero column).  One pass for the maxima, one for the codes.
+//    zero column).  One pass for the maxima, one for the codes.  Codes are
+//    stored with row pairs interleaved in 8-column groups (code_offset), so
+//    that a 16-byte load gives the 8 columns of two rows.
 //  * decode_w8_kernel: a workgroup streams a 256-column slab of one
 //    expert's codes (256-byte row segments, read once, non-temporal) over
 //    its K range.  Eight wavefronts: two column halves of 128 times four K
@@ -57,11 +59,11 @@ __device__ __forceinline__ bf16x8_t column_operand(const uint2 (&r)[8], int c) {
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// 8-byte load with the non-temporal hint: each code is read exactly once.
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint2 load_stream8(const int8_t *p) {
-    const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
-    return make_uint2(v[0], v[1]);
+// 16-byte load with the non-temporal hint: each code is read exactly once.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream16(const int8_t *p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
 template <typename T>
@@ -76,6 +78,11 @@ __device__ __forceinline__ void load4<uint16_t>(const uint16_t *p, float (&v)[4]
     const uint2 a = *reinterpret_cast<const uint2 *>(p);
     v[0] = bf16_to_f32(a.x & 0xffffu); v[1] = bf16_to_f32(a.x >> 16);
     v[2] = bf16_to_f32(a.y & 0xffffu); v[3] = bf16_to_f32(a.y >> 16);
+}
+
+// Byte offset of code (j, n) inside a K x N matrix: [K/2][N/8][2][8].
+__device__ __forceinline__ size_t code_offset(int j, int n, int N) {
+    return ((size_t)(j >> 1) * (N >> 3) + (n >> 3)) * 16 + (j & 1) * 8 + (n & 7);
 }
 
 // grid (ceil(N / 256), n_mat), 256 threads: thread (kp, lane) owns columns
@@ -123,7 +130,8 @@ __global__ __launch_bounds__(256) void quantize_int8_kernel(const T *__restrict_
             if (s[c] > 0.0f) code = (int)fminf(fmaxf(rintf(v[c] / s[c]), -127.0f), 127.0f);
             packed |= (uint32_t)(code & 0xff) << (8 * c);
         }
-        *reinterpret_cast<uint32_t *>(Q + base + (size_t)j * N) = packed;
+        // columns col .. col + 3 of row j: 4 bytes inside one 8-column group
+        *reinterpret_cast<uint32_t *>(Q + (size_t)e * K * N + code_offset(j, col, N)) = packed;
     }
 }
 
@@ -135,8 +143,8 @@ __global__ __launch_bounds__(256) void quantize_int8_kernel(const T *__restrict_
 //
 // Wavefront w covers column half w % 2 (128 columns) and K part w / 2.
 // Lane l loads 8 columns (8 * (l % 16) ..) of 8 rows (8 * (l / 16) ..) of
-// each 32-row step; the two halves of a workgroup read each 256-byte row
-// segment together.  A lane's 8 columns give 8 MFMA B operands; block c of
+// each 32-row step, as four 16-byte loads of two rows each (the codes'
+// row-pair layout); 16 lanes read 256 contiguous bytes.  A lane's 8 columns give 8 MFMA B operands; block c of
 // the accumulators holds weight columns 8 * (l % 16) + c.  (Measured: one
 // wavefront per SIMD streaming whole 256-byte segments hides less latency,
 // and 128-column workgroups reading 128-byte segments stream slower.)
@@ -193,18 +201,23 @@ __global__ __launch_bounds__(W8_WAVES * 64) void decode_w8_kernel(
         // exact: rows past K (K % 8 == 0, so a lane's 8 rows are all in or
         // all out) meet activations set to zero; lanes past N are not
         // stored.
-        uint2 rb[2][NMAT][8];
+        uint2 rb[2][NMAT][8];   // row i of the lane's 8 x 8 block
         uint4 ar[2][MB];
         uint32_t keep[2];   // all ones, or zero for rows past K (applied at use)
         auto load_step = [&](int b, int ks) __attribute__((always_inline)) {
             const int k = ks * 32 + kg * 8;
             const int kr = min(k, K - 8);
-            const uint32_t off = (uint32_t)kr * (uint32_t)N + lane_col;
+            // rows kr + 2p, kr + 2p + 1 of the lane's 8 columns: 16 bytes at
+            // (kr / 2 + p) * 2N + 2 * col (kr and col are multiples of 8)
+            const uint32_t off = (uint32_t)kr * (uint32_t)N + 2u * lane_col;
 #pragma unroll
             for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    rb[b][m][i] = load_stream8(Qb[m] + off + (uint32_t)i * (uint32_t)N);
+                for (int pr = 0; pr < 4; ++pr) {
+                    const uint4 v = load_stream16(Qb[m] + off + (uint32_t)(2 * pr) * (uint32_t)N);
+                    rb[b][m][2 * pr] = make_uint2(v.x, v.y);
+                    rb[b][m][2 * pr + 1] = make_uint2(v.z, v.w);
+                }
 #pragma unroll
             for (int i = 0; i < MB; ++i) ar[b][i] = *reinterpret_cast<const uint4 *>(Arow[i] + kr);
             keep[b] = k < K ? 0xffffffffu : 0u;

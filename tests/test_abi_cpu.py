@@ -206,6 +206,21 @@ def test_python_binding_refuses_cpu_tensors():
         moe.route(x, torch.zeros(16, 8, dtype=torch.bfloat16))
 
 
+def test_int8_row_pair_layout():
+    """unpack_int8 inverts the byte layout the header documents: code of
+    W[m, j, n] at byte m*K*N + ((j/2)*(N/8) + n/8)*16 + (j%2)*8 + n%8."""
+    import torch
+    n, K, N = 2, 6, 24
+    plain = (torch.arange(n * K * N, dtype=torch.int32) % 251 - 125).to(torch.int8).reshape(n, K, N)
+    packed = torch.empty(n * K * N, dtype=torch.int8)
+    for m in range(n):
+        for j in range(K):
+            for c in range(N):
+                at = m * K * N + ((j // 2) * (N // 8) + c // 8) * 16 + (j % 2) * 8 + c % 8
+                packed[at] = plain[m, j, c]
+    assert torch.equal(moe.unpack_int8(packed.reshape(n, K // 2, N // 8, 2, 8)), plain)
+
+
 def test_int8_weight_checks():
     lib = moe.load_library()
     name = lambda st: moe.STATUS_NAMES[st]
@@ -215,6 +230,7 @@ def test_int8_weight_checks():
     assert Q(0, 64, 256, moe.MOE_BF16, A, B, C, None) == "MOE_ERR_SHAPE"
     assert Q(2, 64, 12, moe.MOE_BF16, A, B, C, None) == "MOE_ERR_SHAPE"
     assert Q(2, 0, 256, moe.MOE_BF16, A, B, C, None) == "MOE_ERR_SHAPE"
+    assert Q(2, 63, 256, moe.MOE_BF16, A, B, C, None) == "MOE_ERR_SHAPE"   # K odd: no row pairs
     assert Q(70000, 8, 8, moe.MOE_BF16, A, B, C, None) == "MOE_ERR_SHAPE"
     assert Q(2, 64, 256, moe.MOE_BF16, None, B, C, None) == "MOE_ERR_NULL"
     assert Q(2, 64, 256, moe.MOE_BF16, A, P17, C, None) == "MOE_ERR_ALIGN"

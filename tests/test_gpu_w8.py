@@ -26,13 +26,14 @@ def announce(msg):
 
 def quantized(inp):
     """Codes and scales of w1, w3, w2 from the GPU quantizer, checked
-    bit-exact against the oracle's; returned on the GPU and on the host."""
+    bit-exact against the oracle's; returned on the GPU (the kernels'
+    row-pair layout) and on the host (plain [E, K, N], for the oracle)."""
     dev, host = [], []
     for w in (inp.w1, inp.w3, inp.w2):
         q, sc = moe.quantize_int8(w.to(DEV))
         torch.cuda.synchronize()
         q_o, sc_o = oracle.quantize_int8(w)
-        np.testing.assert_array_equal(q.cpu().numpy(), q_o)
+        np.testing.assert_array_equal(moe.unpack_int8(q).cpu().numpy(), q_o)
         np.testing.assert_array_equal(sc.cpu().numpy(), sc_o)
         dev += [q, sc]
         host += [q_o, sc_o]
@@ -52,7 +53,7 @@ def test_quantize_matches_oracle(dtype, shape):
     q, sc = moe.quantize_int8(w.to(DEV))
     torch.cuda.synchronize()
     q_o, sc_o = oracle.quantize_int8(w)
-    np.testing.assert_array_equal(q.cpu().numpy(), q_o)
+    np.testing.assert_array_equal(moe.unpack_int8(q).cpu().numpy(), q_o)
     np.testing.assert_array_equal(sc.cpu().numpy(), sc_o)
     assert sc_o[0, 3] == 0.0 and not q_o[0, :, 3].any()
 
@@ -176,7 +177,7 @@ def test_full_size_decode_w8():
     for name, w in (("w1", inp.w1), ("w3", inp.w3), ("w2", inp.w2)):
         q, sc = moe.quantize_int8(w.to(DEV))
         torch.cuda.synchronize()
-        qh, sch = q.cpu().numpy(), sc.cpu().numpy()
+        qh, sch = moe.unpack_int8(q).cpu().numpy(), sc.cpu().numpy()
         cols = np.sort(rng.choice(w.shape[2], 24, replace=False))
         q_o, sc_o = oracle.quantize_int8(w[:, :, cols].contiguous())
         np.testing.assert_array_equal(qh[:, :, cols], q_o)
