@@ -818,13 +818,6 @@ __global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_dma_bt_store_split_
 }
 
 // Backward products with a K-contiguous B (see prefill_dma_body).
-__global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_dma_bt_store_kernel(
-    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, const uint16_t *__restrict__ A2,
-    const uint16_t *__restrict__ B2, float *__restrict__ C, const int32_t *__restrict__ counts,
-    const int32_t *__restrict__ offsets, int E, int K1, int N, int a_rows) {
-    prefill_dma_body<1, false, BT_STORE>(A, B, nullptr, C, counts, offsets, E, K1, N, a_rows,
-                                         nullptr, nullptr, A2, B2, K1);
-}
 __global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_dma_bt_dswiglu_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     const int32_t *__restrict__ counts, const int32_t *__restrict__ offsets, int E, int K1, int N,
@@ -1108,17 +1101,6 @@ hipError_t launch_gateup_bf16_gu(const moe_shape_t &s, const uint16_t *xp,
 
 static bool bt_shape_ok(int rows, int K1, int N) {
     return rows > 0 && K1 % DBK == 0 && N % PBN == 0;
-}
-
-hipError_t launch_bt_store_bf16(int rows, int E, const uint16_t *A, const uint16_t *B,
-                                const uint16_t *A2, const uint16_t *B2, int K1, int N,
-                                const int32_t *counts, const int32_t *offsets, float *C,
-                                hipStream_t stream) {
-    if (!bt_shape_ok(rows, K1, N)) return hipErrorNotSupported;
-    const int grid = prefill_grid(rows, E, N / PBN);
-    hipLaunchKernelGGL(prefill_dma_bt_store_kernel, dim3(grid), dim3(PWM * PWN * 64), 0, stream,
-                       A, B, A2, B2, C, counts, offsets, E, K1, N, rows);
-    return hipGetLastError();
 }
 
 static int cus_per_xcd() {

@@ -144,18 +144,14 @@ hipError_t launch_gateup_bf16_gu(const moe_shape_t &s, const uint16_t *xp,
                                  float *u, hipStream_t stream);
 // Backward products on the prefill pipeline with a K-contiguous B (a
 // transposed expert matrix B[e] = B + e * N * K1, line n at n * K1), over
-// grouped rows (counts / offsets): C = A B[e]^T (+ A2 B2[e]^T when A2 / B2
-// are not NULL, the second K1 of a 2 * K1 reduction), or, for the dswiglu
-// form, da = A B[e]^T turned into dg, du (bf16) with g, u (fp32).  All
-// arrays have row stride K1 (A, A2) or N (C, g, u, dg, du).
-// hipErrorNotSupported unless K1 % 64 == 0 and N % 256 == 0.
-hipError_t launch_bt_store_bf16(int rows, int E, const uint16_t *A, const uint16_t *B,
-                                const uint16_t *A2, const uint16_t *B2, int K1, int N,
-                                const int32_t *counts, const int32_t *offsets, float *C,
-                                hipStream_t stream);
-// launch_bt_store_bf16 with the reduction (K1 or 2 K1 stages) cut into
-// 1..kMaxDownSplit parts chosen on the device from the expert counts, part
-// p stored at C + p * part_stride, the count stored to *parts_out.
+// grouped rows (counts / offsets).  The store form: C = A B[e]^T (+ A2
+// B2[e]^T when A2 / B2 are not NULL, the second K1 of a 2 * K1 reduction),
+// with the reduction cut into 1..kMaxDownSplit parts chosen on the device
+// from the expert counts, part p stored at C + p * part_stride and the
+// count stored to *parts_out.  The dswiglu form: da = A B[e]^T turned into
+// dg, du (bf16) with g, u (fp32).  All arrays have row stride K1 (A, A2) or
+// N (C, g, u, dg, du).  hipErrorNotSupported unless K1 % 64 == 0 and
+// N % 256 == 0.
 hipError_t launch_bt_store_split_bf16(int rows, int E, const uint16_t *A, const uint16_t *B,
                                       const uint16_t *A2, const uint16_t *B2, int K1, int N,
                                       const int32_t *counts, const int32_t *offsets, float *C,
