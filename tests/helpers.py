@@ -50,3 +50,20 @@ def row_max_rel_err(y, ref) -> float:
 
 def bf16_bits(t: torch.Tensor) -> torch.Tensor:
     return t.contiguous().view(torch.int16)
+
+
+def down_split_parts(counts, n_cols, cus, k_stages, max_parts=2):
+    """The part count the prefill down kernel picks (its estimate: rounds of
+    one workgroup per CU over 8 XCDs, plus a fifth of a round per extra
+    part), written out here to choose a test shape."""
+    tiles = sum(-(-int(c) // 256) for c in counts) * n_cols
+    cpx = cus // 8
+    best, best_cost = 1, None
+    for parts in range(1, max_parts + 1):
+        if parts > k_stages:
+            break
+        per_xcd = -(-tiles * parts // 8)
+        cost = -(-per_xcd // cpx) / parts + 0.2 * (parts - 1)
+        if best_cost is None or cost < best_cost:
+            best, best_cost = parts, cost
+    return best

@@ -17,7 +17,7 @@ import oracle
 import sparse_mixture_experts_top2_amd as moe
 from sparse_mixture_experts_top2_amd import workloads as W
 
-from helpers import checked_inputs, row_max_rel_err, to_f64
+from helpers import checked_inputs, down_split_parts, row_max_rel_err, to_f64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -123,6 +123,24 @@ def test_zero_tokens_give_zero_weight_gradients():
     assert dx.shape == (0, 128)
     for m in (dwg, dw1, dw3, dw2):
         assert not m.any()
+
+
+def test_backward_products_in_one_part():
+    """8 experts of about 1900 rows each (8 row tiles) with d = 1024: the
+    forward's down product and the dXp product each have 256 tiles, one
+    full round of the CUs, so both keep their reduction whole.  Every
+    gradient against the oracle; the weight gradients reduce over about
+    1900 rows per expert here."""
+    wl = sw(7680, 1024, 512, seed=24)
+    inp = checked_inputs(wl)
+    idx_o, _ = oracle.route(inp.x, inp.w_gate)
+    c_o, _, _, _ = oracle.dispatch(idx_o, wl.E)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if (down_split_parts(c_o, wl.d // 256, cus, wl.f // 64) != 1
+            or down_split_parts(c_o, wl.d // 256, cus, 2 * wl.f // 64) != 1):
+        pytest.skip(f"counts {list(c_o)} on {cus} CUs pick more than one part")
+    announce(f"one-part products {wl.name} counts {list(c_o)}")
+    run_backward_parity(inp)
 
 
 @pytest.mark.slow

@@ -13,7 +13,7 @@ import oracle
 import sparse_mixture_experts_top2_amd as moe
 from sparse_mixture_experts_top2_amd import workloads as W
 
-from helpers import RW_TOL, Y_TOL, checked_inputs, row_max_rel_err, to_f64
+from helpers import RW_TOL, Y_TOL, checked_inputs, down_split_parts, row_max_rel_err, to_f64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -185,6 +185,22 @@ def test_gateup_with_workspace_off_decode_sizes(wl):
     torch.cuda.synchronize()
     as_bits = (lambda t: t.view(torch.int16)) if g.x.dtype == torch.bfloat16 else (lambda t: t)
     assert torch.equal(as_bits(h_ws), as_bits(h))
+
+
+def test_prefill_down_in_one_part():
+    """A prefill layer whose down tiles fill the CUs' rounds exactly (8
+    experts x 8 row tiles x 4 column tiles = 256 tiles), so the down kernel
+    keeps its reduction whole and the combine reads one part: every token
+    against the oracle."""
+    wl = W.small_workload(7680, 1024, 512, seed=24)
+    inp = checked_inputs(wl)
+    idx_o, _ = oracle.route(inp.x, inp.w_gate)
+    c_o, _, _, _ = oracle.dispatch(idx_o, wl.E)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if down_split_parts(c_o, wl.d // 256, cus, wl.f // 64) != 1:
+        pytest.skip(f"counts {list(c_o)} on {cus} CUs pick more than one part")
+    announce(f"down in one part {wl.name} counts {list(c_o)}")
+    run_forward_parity(inp)
 
 
 def _biased(wl, bias_col, screen=True):
