@@ -33,6 +33,12 @@
  * Memory   every array argument is a device pointer owned by the caller,
  *          16-byte aligned.  The library allocates and frees nothing; the
  *          scratch it needs comes from the caller's workspace.
+ * Aliasing an output must not overlap an input, another output or the
+ *          workspace, and the workspace must not overlap an input
+ *          (MOE_ERR_ALIAS; the byte ranges checked are the ones the call
+ *          reads or writes).  Inputs may overlap one another.  The one
+ *          exception is moe_block_forward, whose out may be exactly h or
+ *          exactly the residual.
  * Streams  `stream` is a hipStream_t (NULL = the null stream).  Calls only
  *          enqueue work on it and return; results are valid once the
  *          stream has been synchronised.  There is no host/device

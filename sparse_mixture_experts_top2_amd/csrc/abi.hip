@@ -93,6 +93,49 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// A caller buffer: its start and the bytes a call reads or writes there.
+struct Buf {
+    const void *p;
+    size_t n;
+};
+
+// Whether an output overlaps an input, another output or the workspace, or
+// the workspace overlaps an input.  NULL or empty buffers overlap nothing;
+// inputs may overlap one another.
+template <size_t NI, size_t NO>
+bool aliased(const Buf (&in)[NI], const Buf (&out)[NO], Buf ws = Buf{nullptr, 0}) {
+    auto hit = [](Buf a, Buf b) { return a.p && b.p && a.n && b.n && overlap(a.p, a.n, b.p, b.n); };
+    for (size_t i = 0; i < NO; ++i) {
+        for (size_t j = 0; j < NI; ++j)
+            if (hit(out[i], in[j])) return true;
+        for (size_t j = i + 1; j < NO; ++j)
+            if (hit(out[i], out[j])) return true;
+        if (hit(out[i], ws)) return true;
+    }
+    for (size_t j = 0; j < NI; ++j)
+        if (hit(ws, in[j])) return true;
+    return false;
+}
+
+// Byte sizes of a layer's arrays.
+struct Sizes {
+    size_t act, wg, w13, w2, topk, rows_d, rows_f, o, cnt, off;
+    explicit Sizes(const moe_shape_t &s) {
+        const size_t eb = elem_bytes(s.dtype), T = (size_t)s.T, d = (size_t)s.d_model;
+        const size_t f = (size_t)s.d_ff, E = (size_t)s.n_experts, R = T * s.top_k;
+        act = T * d * eb;          // x, y
+        wg = d * E * eb;           // w_gate
+        w13 = E * d * f * eb;      // w1, w3
+        w2 = E * f * d * eb;       // w2
+        topk = R * 4;              // topk_idx, topk_w, pos
+        rows_d = R * d * eb;       // xp
+        rows_f = R * f * eb;       // h
+        o = R * d * 4;             // o
+        cnt = E * 4;               // counts
+        off = (E + 1) * 4;         // offsets
+    }
+};
+
 // Overlap that is not an exact alias (same start, same size).
 bool partial_overlap(const void *a, const void *b, size_t n) {
     return a != b && overlap(a, n, b, n);
@@ -192,6 +235,9 @@ int moe_route(const moe_shape_t *s, const void *x, const void *w_gate, int32_t *
     if (!x || !w_gate || !topk_idx || !topk_w) return MOE_ERR_NULL;
     if (misaligned(x) || misaligned(w_gate) || misaligned(topk_idx) || misaligned(topk_w))
         return MOE_ERR_ALIGN;
+    const Sizes z(*s);
+    if (aliased({Buf{x, z.act}, Buf{w_gate, z.wg}}, {Buf{topk_idx, z.topk}, Buf{topk_w, z.topk}}))
+        return MOE_ERR_ALIAS;
     return hip_status(launch_route(*s, x, w_gate, topk_idx, topk_w, (hipStream_t)stream));
 }
 
@@ -204,17 +250,11 @@ int moe_route_probs(const moe_shape_t *s, const void *x, const void *w_gate, flo
     if (misaligned(x) || misaligned(w_gate) || misaligned(topk_idx) || misaligned(topk_w) ||
         misaligned(probs_opt))
         return MOE_ERR_ALIGN;
-    const size_t eb = elem_bytes(s->dtype), T = (size_t)s->T, E = (size_t)s->n_experts;
-    const size_t kb = T * s->top_k * 4, pb = probs_opt ? T * E * 4 : 0;
-    const size_t xb = T * s->d_model * eb, gb = (size_t)s->d_model * E * eb;
-    const void *outs[3] = {probs_opt, topk_idx, topk_w};
-    const size_t ob[3] = {pb, kb, kb};
-    for (int i = 0; i < 3; ++i) {
-        if (overlap(outs[i], ob[i], x, xb) || overlap(outs[i], ob[i], w_gate, gb))
-            return MOE_ERR_ALIAS;
-        for (int j = i + 1; j < 3; ++j)
-            if (overlap(outs[i], ob[i], outs[j], ob[j])) return MOE_ERR_ALIAS;
-    }
+    const Sizes z(*s);
+    const size_t pb = (size_t)s->T * s->n_experts * 4;
+    if (aliased({Buf{x, z.act}, Buf{w_gate, z.wg}},
+                {Buf{probs_opt, pb}, Buf{topk_idx, z.topk}, Buf{topk_w, z.topk}}))
+        return MOE_ERR_ALIAS;
     return hip_status(
         launch_route_probs(*s, x, w_gate, probs_opt, topk_idx, topk_w, (hipStream_t)stream));
 }
@@ -228,8 +268,10 @@ int moe_dispatch(const moe_shape_t *s, const void *x, const int32_t *topk_idx, i
     if (misaligned(x) || misaligned(topk_idx) || misaligned(counts) || misaligned(offsets) ||
         misaligned(pos) || misaligned(xp))
         return MOE_ERR_ALIGN;
-    const size_t row = (size_t)s->d_model * elem_bytes(s->dtype);
-    if (overlap(xp, (size_t)routed_rows(*s) * row, x, (size_t)s->T * row)) return MOE_ERR_ALIAS;
+    const Sizes z(*s);
+    if (aliased({Buf{x, z.act}, Buf{topk_idx, z.topk}},
+                {Buf{counts, z.cnt}, Buf{offsets, z.off}, Buf{pos, z.topk}, Buf{xp, z.rows_d}}))
+        return MOE_ERR_ALIAS;
     return hip_status(
         launch_dispatch(*s, x, topk_idx, counts, offsets, pos, xp, (hipStream_t)stream));
 }
@@ -244,9 +286,10 @@ int moe_expert_gateup(const moe_shape_t *s, const void *xp, const int32_t *count
     if (misaligned(xp) || misaligned(counts) || misaligned(offsets) || misaligned(w1) ||
         misaligned(w3) || misaligned(h))
         return MOE_ERR_ALIGN;
-    const size_t eb = elem_bytes(s->dtype);
-    const size_t R = (size_t)routed_rows(*s);
-    if (overlap(h, R * s->d_ff * eb, xp, R * s->d_model * eb))
+    const Sizes z(*s);
+    if (aliased({Buf{xp, z.rows_d}, Buf{counts, z.cnt}, Buf{offsets, z.off}, Buf{w1, z.w13},
+                 Buf{w3, z.w13}},
+                {Buf{h, z.rows_f}}))
         return MOE_ERR_ALIAS;
     return hip_status(launch_gateup(*s, xp, counts, offsets, w1, w3, h, (hipStream_t)stream));
 }
@@ -263,18 +306,16 @@ int moe_expert_gateup_ws(const moe_shape_t *s, const void *xp, const int32_t *co
         return MOE_ERR_ALIGN;
     const Layout L = plan_workspace(*s);
     if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
-    const size_t eb = elem_bytes(s->dtype);
-    const size_t R = (size_t)routed_rows(*s);
-    if (overlap(h, R * s->d_ff * eb, xp, R * s->d_model * eb)) return MOE_ERR_ALIAS;
-    if (!(s->dtype == MOE_BF16 && s->T <= kDecodeMaxT))
-        return hip_status(launch_gateup(*s, xp, counts, offsets, w1, w3, h, (hipStream_t)stream));
     // the only workspace region written: the decode kernel's partial sums
+    const bool dec = s->dtype == MOE_BF16 && s->T <= kDecodeMaxT;
     char *gp = static_cast<char *>(ws) + L.gpart;
-    const size_t gb = kDecodeTailBytes;
-    const size_t E = (size_t)s->n_experts;
-    if (overlap(gp, gb, xp, R * s->d_model * eb) || overlap(gp, gb, h, R * s->d_ff * eb) ||
-        overlap(gp, gb, counts, E * 4) || overlap(gp, gb, offsets, (E + 1) * 4))
+    const Sizes z(*s);
+    if (aliased({Buf{xp, z.rows_d}, Buf{counts, z.cnt}, Buf{offsets, z.off}, Buf{w1, z.w13},
+                 Buf{w3, z.w13}},
+                {Buf{h, z.rows_f}}, Buf{dec ? gp : nullptr, kDecodeTailBytes}))
         return MOE_ERR_ALIAS;
+    if (!dec)
+        return hip_status(launch_gateup(*s, xp, counts, offsets, w1, w3, h, (hipStream_t)stream));
     return hip_status(launch_gateup_bf16(*s, static_cast<const uint16_t *>(xp), counts, offsets,
                                          static_cast<const uint16_t *>(w1),
                                          static_cast<const uint16_t *>(w3),
@@ -291,9 +332,9 @@ int moe_expert_down(const moe_shape_t *s, const void *h, const int32_t *counts,
     if (misaligned(h) || misaligned(counts) || misaligned(offsets) || misaligned(w2) ||
         misaligned(o))
         return MOE_ERR_ALIGN;
-    const size_t eb = elem_bytes(s->dtype);
-    const size_t R = (size_t)routed_rows(*s);
-    if (overlap(o, R * s->d_model * sizeof(float), h, R * s->d_ff * eb))
+    const Sizes z(*s);
+    if (aliased({Buf{h, z.rows_f}, Buf{counts, z.cnt}, Buf{offsets, z.off}, Buf{w2, z.w2}},
+                {Buf{o, z.o}}))
         return MOE_ERR_ALIAS;
     return hip_status(launch_down(*s, h, counts, offsets, w2, o, (hipStream_t)stream));
 }
@@ -311,9 +352,10 @@ int moe_experts(const moe_shape_t *s, const void *xp, const int32_t *counts,
     const Layout L = plan_workspace(*s);
     if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
     if (misaligned(ws)) return MOE_ERR_ALIGN;
-    const size_t R = (size_t)routed_rows(*s);
-    const size_t o_bytes = R * s->d_model * sizeof(float);
-    if (overlap(o, o_bytes, xp, R * s->d_model * elem_bytes(s->dtype)))
+    const Sizes z(*s);
+    if (aliased({Buf{xp, z.rows_d}, Buf{counts, z.cnt}, Buf{offsets, z.off}, Buf{w1, z.w13},
+                 Buf{w3, z.w13}, Buf{w2, z.w2}},
+                {Buf{o, z.o}}, Buf{ws, L.total}))
         return MOE_ERR_ALIAS;
     void *h = static_cast<char *>(ws) + L.h;
     hipStream_t str = (hipStream_t)stream;
@@ -330,8 +372,8 @@ int moe_combine(const moe_shape_t *s, const float *o, const int32_t *pos, const 
     if (!o || !pos || !topk_w || !y) return MOE_ERR_NULL;
     if (misaligned(o) || misaligned(pos) || misaligned(topk_w) || misaligned(y))
         return MOE_ERR_ALIGN;
-    const size_t y_bytes = (size_t)s->T * s->d_model * elem_bytes(s->dtype);
-    if (overlap(y, y_bytes, o, (size_t)routed_rows(*s) * s->d_model * sizeof(float)))
+    const Sizes z(*s);
+    if (aliased({Buf{o, z.o}, Buf{pos, z.topk}, Buf{topk_w, z.topk}}, {Buf{y, z.act}}))
         return MOE_ERR_ALIAS;
     return hip_status(launch_combine(*s, o, pos, topk_w, y, (hipStream_t)stream));
 }
@@ -349,8 +391,12 @@ int moe_forward(const moe_shape_t *s, const void *x, const void *w_gate, const v
     const Layout L = plan_workspace(*s);
     if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
     if (misaligned(ws)) return MOE_ERR_ALIGN;
-    const size_t act = (size_t)s->T * s->d_model * elem_bytes(s->dtype);
-    if (overlap(y, act, x, act)) return MOE_ERR_ALIAS;
+    const Sizes z(*s);
+    if (aliased({Buf{x, z.act}, Buf{w_gate, z.wg}, Buf{w1, z.w13}, Buf{w3, z.w13},
+                 Buf{w2, z.w2}},
+                {Buf{y, z.act}, Buf{topk_idx_opt, z.topk}, Buf{topk_w_opt, z.topk}},
+                Buf{ws, L.total}))
+        return MOE_ERR_ALIAS;
 
     char *base = static_cast<char *>(ws);
     int32_t *idx = topk_idx_opt ? topk_idx_opt : reinterpret_cast<int32_t *>(base + L.idx);
@@ -370,8 +416,11 @@ int moe_rmsnorm_route(const moe_shape_t *s, const void *h, const void *rms_weigh
     if (misaligned(h) || misaligned(rms_weight) || misaligned(w_gate) || misaligned(xn) ||
         misaligned(topk_idx) || misaligned(topk_w))
         return MOE_ERR_ALIGN;
-    const size_t act = (size_t)s->T * s->d_model * elem_bytes(s->dtype);
-    if (overlap(xn, act, h, act)) return MOE_ERR_ALIAS;
+    const Sizes z(*s);
+    const size_t gb = (size_t)s->d_model * elem_bytes(s->dtype);
+    if (aliased({Buf{h, z.act}, Buf{rms_weight, gb}, Buf{w_gate, z.wg}},
+                {Buf{xn, z.act}, Buf{topk_idx, z.topk}, Buf{topk_w, z.topk}}))
+        return MOE_ERR_ALIAS;
     return hip_status(launch_route_norm(*s, h, rms_weight, eps, w_gate, xn, topk_idx, topk_w,
                                         (hipStream_t)stream));
 }
@@ -395,8 +444,18 @@ int moe_block_forward(const moe_shape_t *s, const void *h, const void *rms_weigh
     // out may be h or the residual itself (an in-place block update): h is
     // read only by the first kernel, and the combine reads each residual
     // element before writing it.  Partial overlaps are refused.
-    const size_t act = (size_t)s->T * s->d_model * elem_bytes(s->dtype);
-    if (partial_overlap(out, h, act) || (residual && partial_overlap(out, residual, act)))
+    // Every other overlap is refused as in moe_forward.
+    const Sizes z(*s);
+    const size_t gb = (size_t)s->d_model * elem_bytes(s->dtype);
+    if (partial_overlap(out, h, z.act) || (residual && partial_overlap(out, residual, z.act)))
+        return MOE_ERR_ALIAS;
+    const Buf wts[] = {Buf{rms_weight, gb}, Buf{w_gate, z.wg}, Buf{w1, z.w13}, Buf{w3, z.w13},
+                       Buf{w2, z.w2}};
+    if (aliased({Buf{h, z.act}, Buf{residual, z.act}, wts[0], wts[1], wts[2], wts[3], wts[4]},
+                {Buf{topk_idx_opt, z.topk}, Buf{topk_w_opt, z.topk}}, Buf{ws, L.total}) ||
+        aliased({wts[0], wts[1], wts[2], wts[3], wts[4], Buf{topk_idx_opt, z.topk},
+                 Buf{topk_w_opt, z.topk}},
+                {Buf{out, z.act}}, Buf{ws, L.total}))
         return MOE_ERR_ALIAS;
 
     char *base = static_cast<char *>(ws);
@@ -432,8 +491,12 @@ int moe_expert_gateup_w8(const moe_shape_t *s, const void *xp, const int32_t *co
     if (misaligned(xp) || misaligned(counts) || misaligned(offsets) || misaligned(q1) ||
         misaligned(s1) || misaligned(q3) || misaligned(s3) || misaligned(h))
         return MOE_ERR_ALIGN;
-    const size_t R = (size_t)routed_rows(*s);
-    if (overlap(h, R * s->d_ff * 2, xp, R * s->d_model * 2)) return MOE_ERR_ALIAS;
+    const Sizes z(*s);
+    const size_t qb = z.w13 / 2, sb = (size_t)s->n_experts * s->d_ff * 4;
+    if (aliased({Buf{xp, z.rows_d}, Buf{counts, z.cnt}, Buf{offsets, z.off}, Buf{q1, qb},
+                 Buf{s1, sb}, Buf{q3, qb}, Buf{s3, sb}},
+                {Buf{h, z.rows_f}}))
+        return MOE_ERR_ALIAS;
     return hip_status(launch_gateup_w8(*s, static_cast<const uint16_t *>(xp), counts, offsets,
                                        q1, s1, q3, s3, static_cast<uint16_t *>(h),
                                        (hipStream_t)stream));
@@ -449,8 +512,12 @@ int moe_expert_down_w8(const moe_shape_t *s, const void *h, const int32_t *count
     if (misaligned(h) || misaligned(counts) || misaligned(offsets) || misaligned(q2) ||
         misaligned(s2) || misaligned(o))
         return MOE_ERR_ALIGN;
-    const size_t R = (size_t)routed_rows(*s);
-    if (overlap(o, R * s->d_model * sizeof(float), h, R * s->d_ff * 2)) return MOE_ERR_ALIAS;
+    const Sizes z(*s);
+    const size_t qb = z.w2 / 2, sb = (size_t)s->n_experts * s->d_model * 4;
+    if (aliased({Buf{h, z.rows_f}, Buf{counts, z.cnt}, Buf{offsets, z.off}, Buf{q2, qb},
+                 Buf{s2, sb}},
+                {Buf{o, z.o}}))
+        return MOE_ERR_ALIAS;
     return hip_status(launch_down_w8(*s, static_cast<const uint16_t *>(h), counts, offsets, q2,
                                      s2, o, 1, (hipStream_t)stream));
 }
@@ -470,8 +537,14 @@ int moe_forward_w8(const moe_shape_t *s, const void *x, const void *w_gate, cons
     const Layout L = plan_workspace(*s);
     if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
     if (misaligned(ws)) return MOE_ERR_ALIGN;
-    const size_t act = (size_t)s->T * s->d_model * 2;
-    if (overlap(y, act, x, act)) return MOE_ERR_ALIAS;
+    const Sizes z(*s);
+    const size_t q13 = z.w13 / 2, q2b = z.w2 / 2;
+    const size_t s13 = (size_t)s->n_experts * s->d_ff * 4, s2b = (size_t)s->n_experts * s->d_model * 4;
+    if (aliased({Buf{x, z.act}, Buf{w_gate, z.wg}, Buf{q1, q13}, Buf{s1, s13}, Buf{q3, q13},
+                 Buf{s3, s13}, Buf{q2, q2b}, Buf{s2, s2b}},
+                {Buf{y, z.act}, Buf{topk_idx_opt, z.topk}, Buf{topk_w_opt, z.topk}},
+                Buf{ws, L.total}))
+        return MOE_ERR_ALIAS;
 
     char *base = static_cast<char *>(ws);
     int32_t *idx = topk_idx_opt ? topk_idx_opt : reinterpret_cast<int32_t *>(base + L.idx);
@@ -519,18 +592,12 @@ int moe_backward(const moe_shape_t *s, const void *x, const void *w_gate, const 
     if (misaligned(ws)) return MOE_ERR_ALIGN;
     const size_t eb = elem_bytes(s->dtype), T = (size_t)s->T, d = (size_t)s->d_model;
     const size_t f = (size_t)s->d_ff, E = (size_t)s->n_experts;
-    const void *in[] = {x, w_gate, w1, w3, w2, dy};
-    const size_t inb[] = {T * d * eb, d * E * eb, E * d * f * eb, E * d * f * eb, E * f * d * eb,
-                          T * d * eb};
-    const void *out[] = {dx, dw_gate, dw1, dw3, dw2};
-    const size_t outb[] = {T * d * eb, d * E * 4, E * d * f * 4, E * d * f * 4, E * f * d * 4};
-    for (int i = 0; i < 5; ++i) {
-        for (int j = 0; j < 6; ++j)
-            if (overlap(out[i], outb[i], in[j], inb[j])) return MOE_ERR_ALIAS;
-        for (int j = i + 1; j < 5; ++j)
-            if (overlap(out[i], outb[i], out[j], outb[j])) return MOE_ERR_ALIAS;
-        if (overlap(out[i], outb[i], ws, L.total)) return MOE_ERR_ALIAS;
-    }
+    if (aliased({Buf{x, T * d * eb}, Buf{w_gate, d * E * eb}, Buf{w1, E * d * f * eb},
+                 Buf{w3, E * d * f * eb}, Buf{w2, E * f * d * eb}, Buf{dy, T * d * eb}},
+                {Buf{dx, T * d * eb}, Buf{dw_gate, d * E * 4}, Buf{dw1, E * d * f * 4},
+                 Buf{dw3, E * d * f * 4}, Buf{dw2, E * f * d * 4}},
+                Buf{ws, L.total}))
+        return MOE_ERR_ALIAS;
     return hip_status(launch_backward(*s, x, w_gate, w1, w3, w2, dy, dx, dw_gate, dw1, dw3, dw2,
                                       L, static_cast<char *>(ws), (hipStream_t)stream));
 }

@@ -293,3 +293,60 @@ def test_backward_checks():
     assert B(args, ws=base[10]) == "MOE_ERR_ALIAS"   # workspace over dw2
     assert name(lib.moe_backward(ctypes.byref(shape(k=5)), *args, ws, need, None)) == \
         "MOE_ERR_UNSUPPORTED"
+
+
+# Every entry point's buffers by role: "i" input, "o" output, "w" workspace
+# (with ws_bytes after it), "f" a float argument.  Outputs may not overlap
+# inputs, other outputs or the workspace, and the workspace may not overlap
+# inputs; moe_block_forward alone takes out == h or out == residual.
+ALIAS_CASES = [
+    ("moe_route", "iioo", {}),
+    ("moe_route_probs", "iiooo", {}),
+    ("moe_dispatch", "iioooo", {}),
+    ("moe_expert_gateup", "iiiiio", {}),
+    ("moe_expert_down", "iiiio", {}),
+    ("moe_experts", "iiiiiiow", {}),
+    ("moe_combine", "iiio", {}),
+    ("moe_forward", "iiiiiooow", {}),
+    ("moe_rmsnorm_route", "iifiooo", {}),
+    ("moe_block_forward", "iifiiiiiooow", {"allowed": {(8, 0), (8, 3)}}),
+    ("moe_expert_gateup_w8", "iiiiiiio", {"T": 16}),
+    ("moe_expert_down_w8", "iiiiio", {"T": 16}),
+    ("moe_forward_w8", "iiiiiiiiooow", {"T": 16}),
+    ("moe_backward", "iiiiiiooooow", {}),
+]
+
+
+@pytest.mark.parametrize("fn,roles,opt", ALIAS_CASES, ids=[c[0] for c in ALIAS_CASES])
+def test_every_overlap_is_refused(fn, roles, opt):
+    lib = moe.load_library()
+    s = shape(T=opt.get("T", 64))
+    call = getattr(lib, fn)
+    spaced = [ctypes.c_void_p(0x100000000 * (i + 1)) for i in range(len(roles))]
+
+    def run(ptrs):
+        args = [ctypes.byref(s)]
+        for r, p in zip(roles, ptrs):
+            if r == "f":
+                args.append(1e-5)
+            elif r == "w":
+                args += [p, 1 << 40]
+            else:
+                args.append(p)
+        args.append(None)                      # stream
+        return moe.STATUS_NAMES[call(*args)]
+
+    idx = {r: [i for i, x in enumerate(roles) if x == r] for r in "iow"}
+    pairs = [(o, j) for o in idx["o"] for j in idx["i"] + idx["w"]]
+    pairs += [(o, j) for o in idx["o"] for j in idx["o"] if j > o]
+    pairs += [(w, j) for w in idx["w"] for j in idx["i"]]
+    assert pairs
+    for a, b in pairs:
+        if (a, b) in opt.get("allowed", ()):
+            continue
+        ptrs = list(spaced)
+        ptrs[a] = spaced[b]
+        assert run(ptrs) == "MOE_ERR_ALIAS", (fn, a, b)
+        # a buffer that starts just inside another one overlaps it too
+        ptrs[a] = ctypes.c_void_p(spaced[b].value + 16)
+        assert run(ptrs) == "MOE_ERR_ALIAS", (fn, a, b, "+16")
