@@ -234,7 +234,9 @@ int moe_block_forward(const moe_shape_t *shape, const void *h, const void *rms_w
  * selected experts' weights, so the codes halve the bytes of the step.
  * Activations, router and outputs keep the layer dtype, which must be
  * MOE_BF16. The layer calls take T <= 32 (decode sizes); other shapes
- * return MOE_ERR_UNSUPPORTED. Codes become bf16 exactly, and each product
+ * return MOE_ERR_UNSUPPORTED. They also need d_model * d_ff < 2^31 (one
+ * expert matrix of codes is addressed with 32-bit offsets), else
+ * MOE_ERR_SHAPE. Codes become bf16 exactly, and each product
  * accumulates in fp32 on the bf16 matrix cores. The scale multiplies the
  * finished sum of each output column.
  *

@@ -200,6 +200,8 @@ int check_w8(const moe_shape_t *s) {
     int st = check_shape(s);
     if (st) return st;
     if (s->dtype != MOE_BF16 || s->T > kDecodeMaxT) return MOE_ERR_UNSUPPORTED;
+    // the decode kernel addresses one expert's codes with 32-bit offsets
+    if ((int64_t)s->d_model * s->d_ff >= ((int64_t)1 << 31)) return MOE_ERR_SHAPE;
     return MOE_OK;
 }
 
@@ -211,7 +213,7 @@ const char *moe_status_str(int status) {
     switch (status) {
     case MOE_OK: return "MOE_OK";
     case MOE_ERR_NULL: return "MOE_ERR_NULL: a required pointer is NULL";
-    case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE: T < 0, or d_model / d_ff not a positive multiple of 8";
+    case MOE_ERR_SHAPE: return "MOE_ERR_SHAPE: T < 0, d_model / d_ff not a positive multiple of 8, or a size past a documented limit";
     case MOE_ERR_DTYPE: return "MOE_ERR_DTYPE: dtype must be MOE_F32 or MOE_BF16";
     case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN: device pointers must be 16-byte aligned";
     case MOE_ERR_ALIAS: return "MOE_ERR_ALIAS: an output overlaps an input";

@@ -245,6 +245,8 @@ def test_int8_weight_checks():
     assert F(shape(T=16, dtype=moe.MOE_F32)) == "MOE_ERR_UNSUPPORTED"
     assert F(shape(T=16, k=5)) == "MOE_ERR_UNSUPPORTED"
     assert F(shape(T=0)) == "MOE_OK"
+    assert F(shape(T=16, d=32768, f=65536)) == "MOE_ERR_SHAPE"   # codes past 32-bit offsets
+    assert F(shape(T=0, d=32768, f=65536)) == "MOE_ERR_SHAPE"
     s = shape(T=16)
     assert name(lib.moe_forward_w8(ctypes.byref(s), P16, P16, None, P16, P16, P16, P16, P16,
                                    P16B, None, None, P16, 1 << 40, None)) == "MOE_ERR_NULL"
