@@ -318,6 +318,18 @@ FULL = [("decode_8x7b", None), ("prefill_8x7b", 24), ("skewed_8x7b", 24),
 
 
 @pytest.mark.slow
+def test_decode_at_the_larger_expert_shape():
+    """A 32-token decode step on the larger expert shape (d = 6144, f =
+    16384): the decode kernels with 128 gate/up units per expert (4 full
+    rounds, no tail cut) and 48 down units per expert.  Every token against
+    the oracle."""
+    wl = W.WORKLOADS["larger_expert"].with_(name="larger_expert_decode", T=32)
+    announce("larger-expert decode: drawing inputs")
+    y, idx_o = run_forward_parity(checked_inputs(wl))
+    announce(f"larger-expert decode: counts {np.bincount(idx_o.ravel(), minlength=wl.E).tolist()}")
+
+
+@pytest.mark.slow
 @pytest.mark.parametrize("name,n_sample", FULL, ids=[f[0] for f in FULL])
 def test_full_size(name, n_sample):
     wl = W.WORKLOADS[name]

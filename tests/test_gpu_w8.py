@@ -165,11 +165,13 @@ def test_w8_refuses_prefill_sizes_and_fp32():
 
 
 @pytest.mark.slow
-def test_full_size_decode_w8():
-    """The 8x7B decode step (T = 32) in the launch configuration the
-    benchmark times: codes of sampled columns of every matrix against the
-    oracle, then the whole layer against the oracle on all 32 tokens."""
-    wl = W.WORKLOADS["decode_8x7b"]
+@pytest.mark.parametrize("name", ["decode_8x7b", "larger_expert"])
+def test_full_size_decode_w8(name):
+    """A decode step (T = 32) at a full layer shape (the 8x7B one, in the
+    launch configuration the benchmark times, and the larger expert shape):
+    codes of sampled columns of every matrix against the oracle, then the
+    whole layer against the oracle on all 32 tokens."""
+    wl = W.WORKLOADS[name].with_(T=32)
     announce("full decode w8: drawing inputs")
     inp = checked_inputs(wl)
     rng = np.random.default_rng(0)
