@@ -40,7 +40,8 @@ prefill.
 
 ``other_configs``: the remaining workloads measured the same way (the tiny
 fp32 layer, whose kernels run on the vector ALUs, the skewed-routing 8x7B
-prefill and the larger-expert prefill), step time and layer roofline each.
+prefill, and the larger expert shape at prefill and at decode), step time
+and layer roofline each.
 
 ``ceilings``: context, not targets: what torch reaches on this GPU for a
 plain device copy (bytes read + written per second) and for one bf16
@@ -523,7 +524,8 @@ def main():
     if args.others:
         others = [measure_other("tiny_fp32", 200, 20),
                   measure_other("skewed_8x7b", 10, 3),
-                  measure_other("larger_expert", 10, 3)]
+                  measure_other("larger_expert", 10, 3),
+                  measure_other("larger_expert_decode", 100, 10)]
         ceilings = measure_ceilings()
     cpu = None
     if args.cpu_seconds > 0:

@@ -53,7 +53,7 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-# The five layer shapes this library is measured and checked on.
+# The layer shapes this library is measured and checked on.
 WORKLOADS = {
     "tiny_fp32": Workload(
         "tiny_fp32", T=64, d=128, f=256, dtype=F32,
@@ -73,6 +73,10 @@ WORKLOADS = {
         "larger_expert", T=8192, d=6144, f=16384, dtype=BF16,
         router_std=1.0 / math.sqrt(6144), seed=1004,
         note="8x22B-sized expert tiles, ~4.8 GB of expert weights"),
+    "larger_expert_decode": Workload(
+        "larger_expert_decode", T=32, d=6144, f=16384, dtype=BF16,
+        router_std=1.0 / math.sqrt(6144), seed=1005,
+        note="one decode step of 32 tokens on the larger expert shape (HBM-bound)"),
 }
 
 

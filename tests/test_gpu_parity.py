@@ -323,7 +323,7 @@ def test_decode_at_the_larger_expert_shape():
     16384): the decode kernels with 128 gate/up units per expert (4 full
     rounds, no tail cut) and 48 down units per expert.  Every token against
     the oracle."""
-    wl = W.WORKLOADS["larger_expert"].with_(name="larger_expert_decode", T=32)
+    wl = W.WORKLOADS["larger_expert_decode"]
     announce("larger-expert decode: drawing inputs")
     y, idx_o = run_forward_parity(checked_inputs(wl))
     announce(f"larger-expert decode: counts {np.bincount(idx_o.ravel(), minlength=wl.E).tolist()}")

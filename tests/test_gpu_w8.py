@@ -165,13 +165,13 @@ def test_w8_refuses_prefill_sizes_and_fp32():
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name", ["decode_8x7b", "larger_expert"])
+@pytest.mark.parametrize("name", ["decode_8x7b", "larger_expert_decode"])
 def test_full_size_decode_w8(name):
     """A decode step (T = 32) at a full layer shape (the 8x7B one, in the
     launch configuration the benchmark times, and the larger expert shape):
     codes of sampled columns of every matrix against the oracle, then the
     whole layer against the oracle on all 32 tokens."""
-    wl = W.WORKLOADS[name].with_(T=32)
+    wl = W.WORKLOADS[name]
     announce("full decode w8: drawing inputs")
     inp = checked_inputs(wl)
     rng = np.random.default_rng(0)
