@@ -38,6 +38,10 @@ nine grouped GEMMs, 9 * 2 * kT * d * f FLOPs.
 received tokens for the decode step, 2 k T (3 d f) + 2 T d E FLOPs for the
 prefill.
 
+``graph_replay``: the headline step again, captured once as a HIP graph and
+replayed per step (the library only enqueues kernels, so the whole call
+captures).
+
 ``other_configs``: the remaining workloads measured the same way (the tiny
 fp32 layer, whose kernels run on the vector ALUs, the skewed-routing 8x7B
 prefill, and the larger expert shape at prefill and at decode), step time
@@ -86,6 +90,8 @@ def parse():
                     help="skip the int8-weight decode measurement")
     ap.add_argument("--no-backward", dest="backward", action="store_false",
                     help="skip the backward measurement")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="skip the headline step replayed as a captured HIP graph")
     ap.add_argument("--no-others", dest="others", action="store_false",
                     help="skip the other workloads and the torch ceilings")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -188,6 +194,40 @@ def measure(wl_name, steps, warmup):
     return dict(wl=wl, inp=inp, ms=ms, ms_events=ms_events, wall_ms=wall_ms,
                 tokens_per_s=wl.T / (ms * 1e-3), roofline=roof, layer_roofline=layer,
                 counts=c, active_experts=active)
+
+
+def measure_graph(res, steps, warmup):
+    """The same layer step launched as one captured HIP graph per step (the
+    library enqueues kernels only, so the whole call captures): what a
+    launch-bound caller such as a decode loop would see."""
+    import torch
+    import sparse_mixture_experts_top2_amd as moe
+    wl, inp = res["wl"], res["inp"]
+    dev = torch.device("cuda:0")
+    ws = moe.alloc_workspace(wl.T, wl.d, wl.f, wl.E, inp.x.dtype, dev)
+    y = torch.empty(wl.T, wl.d, dtype=inp.x.dtype, device=dev)
+
+    def step():
+        moe.forward(inp.x, inp.w_gate, inp.w1, inp.w3, inp.w2, workspace=ws, out=y)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(warmup):
+        graph.replay()
+    ms = time_region(graph.replay, steps, torch.cuda.current_stream(dev))
+    log(f"{wl.name} as a HIP graph: {ms:.4f} ms/step ({wl.T / ms * 1e3:.0f} tokens/s)")
+    del graph, ws, y
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "value": round(wl.T / (ms * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_step": round(ms, 5), "steps": steps, "warmup": warmup,
+            "launch": "one captured HIP graph replayed per step"}
 
 
 def measure_block(wl_name, steps, warmup, plain_ms):
@@ -488,6 +528,7 @@ def main():
 
     steps, warmup = defaults(args.workload)
     main_res = measure(args.workload, steps, warmup)
+    graph = measure_graph(main_res, steps, warmup) if args.graph else None
     blocks = []
     if args.block:
         blocks.append(measure_block(args.workload, steps, warmup, main_res["ms"]))
@@ -552,6 +593,7 @@ def main():
         "expert_counts": main_res["counts"],
         "cpu_baseline": cpu,
         "secondary": sec,
+        "graph_replay": graph,
         "block_boundary": blocks or None,
         "top_k": topk or None,
         "w8": w8,
