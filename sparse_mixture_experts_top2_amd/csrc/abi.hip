@@ -55,13 +55,14 @@ hipError_t launch_gateup(const moe_shape_t &s, const void *xp, const int32_t *co
 }
 
 hipError_t launch_down(const moe_shape_t &s, const void *h, const int32_t *counts,
-                       const int32_t *offsets, const void *w2, float *o, hipStream_t stream) {
+                       const int32_t *offsets, const void *w2, float *o, hipStream_t stream,
+                       float *gpart) {
     if (s.T == 0) return hipSuccess;
     if (s.dtype == MOE_F32)
         return launch_down_f32(s, static_cast<const float *>(h), counts, offsets,
                                static_cast<const float *>(w2), o, stream);
     return launch_down_bf16(s, static_cast<const uint16_t *>(h), counts, offsets,
-                            static_cast<const uint16_t *>(w2), o, stream);
+                            static_cast<const uint16_t *>(w2), o, stream, gpart);
 }
 
 }  // namespace moe
@@ -190,7 +191,11 @@ hipError_t run_layer(const moe_shape_t &s, const void *x, const void *g, float e
         if (de == hipSuccess) parts_dev = pd;
         else if (de != hipErrorNotSupported) e = de;
     }
-    if (e == hipSuccess && !parts_dev) e = launch_down(s, h, counts, offsets, w2, o, str);
+    // bf16 decode: the down product may cut its last round like gate/up,
+    // reusing the partial-sum region (the gate/up finish has read it by then)
+    float *dpart = nullptr;
+    if (s.dtype == MOE_BF16 && s.T <= kDecodeMaxT) dpart = reinterpret_cast<float *>(base + L.gpart);
+    if (e == hipSuccess && !parts_dev) e = launch_down(s, h, counts, offsets, w2, o, str, dpart);
     if (e == hipSuccess) e = launch_combine(s, o, pos, w, y, str, res, 1, parts_dev);
     return e;
 }

@@ -842,13 +842,13 @@ constexpr int DWAVES = 8;     // wavefronts per workgroup, splitting K
 constexpr int DCOLS = 128;    // weight columns per workgroup
 
 // Decode workgroup units are (expert, column block) pairs, unit u = e * nb +
-// column block.  TAIL (gate/up): a 1-D grid where the first n_full units run
-// whole and the rest are cut in two K halves (workgroups n_full + 2 j and
-// n_full + 2 j + 1 for unit n_full + j), which store their fp32 sums of
-// x W1 and x W3 to part slot j (see decode_tail_slot) for
-// decode_tail_finish_kernel.  One workgroup per CU at a time: when the
-// units leave the last round at most half full, its units cut in halves
-// fill one round of half the length.
+// column block.  TAIL: a 1-D grid where the first n_full units run whole
+// and the rest are cut in two K halves (workgroups n_full + 2 j and
+// n_full + 2 j + 1 for unit n_full + j), which store their fp32 sums (of
+// x W1 and x W3 for gate/up, of h W2 for down) to part slot j (see
+// decode_tail_slot) for decode_tail_finish_kernel.  One workgroup per CU at
+// a time: when the units leave the last round at most half full, its units
+// cut in halves fill one round of half the length.
 constexpr int DTAIL_ROWS = 32;   // rows of a part slot (an expert's rows at decode sizes)
 __device__ __forceinline__ size_t decode_tail_slot(int j, int half, int m) {
     return ((size_t)(j * 2 + half) * 2 + m) * DTAIL_ROWS * DCOLS;
@@ -860,7 +860,7 @@ __global__ __launch_bounds__(DWAVES * 64) void decode_gemm_kernel(
     const int32_t *__restrict__ offsets, int K, int N, int a_rows,
     const int32_t *__restrict__ src, float *__restrict__ part = nullptr, int n_full = 0,
     int nb_cols = 0) {
-    static_assert(!TAIL || (NMAT == 2 && MB * 16 <= DTAIL_ROWS), "the tail split is for gate/up");
+    static_assert(!TAIL || MB * 16 <= DTAIL_ROWS, "a part slot holds an expert's rows");
     int e = blockIdx.y, cblk = blockIdx.x, half = -1, slot = 0;
     if constexpr (TAIL) {
         int unit = blockIdx.x;
@@ -971,7 +971,7 @@ __global__ __launch_bounds__(DWAVES * 64) void decode_gemm_kernel(
             if (row >= Me) continue;
             if (TAIL && half >= 0) {
 #pragma unroll
-                for (int m = 0; m < 2; ++m) {
+                for (int m = 0; m < NMAT; ++m) {
                     float *dst = part + decode_tail_slot(slot, half, m) + (size_t)row * DCOLS +
                                  nb * 8;
                     *reinterpret_cast<float4 *>(dst) =
@@ -1002,36 +1002,42 @@ __global__ __launch_bounds__(DWAVES * 64) void decode_gemm_kernel(
     }
 }
 
-// h = silu(g0 + g1) * (u0 + u1) for the units a TAIL launch cut in two:
-// workgroup j takes part slot j (unit n_full + j).
+// The units a TAIL launch cut in two: workgroup j takes part slot j (unit
+// n_full + j) and adds its halves, half 0 first.  Gate/up (NMAT = 2):
+// h = silu(g0 + g1) * (u0 + u1), bf16.  Down (NMAT = 1): o = o0 + o1, fp32.
+template <int NMAT>
 __global__ __launch_bounds__(256) void decode_tail_finish_kernel(
     const float *__restrict__ part, const int32_t *__restrict__ counts,
-    const int32_t *__restrict__ offsets, int n_full, int nb_cols, int N,
-    uint16_t *__restrict__ h) {
+    const int32_t *__restrict__ offsets, int n_full, int nb_cols, int N, void *__restrict__ out) {
     const int j = blockIdx.x, unit = n_full + j;
     const int e = unit / nb_cols, cblk = unit - e * nb_cols;
     const int Me = counts[e], r0 = offsets[e];
-    const float *g0 = part + decode_tail_slot(j, 0, 0), *u0 = part + decode_tail_slot(j, 0, 1);
-    const float *g1 = part + decode_tail_slot(j, 1, 0), *u1 = part + decode_tail_slot(j, 1, 1);
+    const float *g0 = part + decode_tail_slot(j, 0, 0), *g1 = part + decode_tail_slot(j, 1, 0);
     for (int i = threadIdx.x; i < Me * DCOLS; i += 256) {
         const int row = i / DCOLS, c = i % DCOLS, col = cblk * DCOLS + c;
         if (col >= N) continue;
-        const float g = g0[i] + g1[i], u = u0[i] + u1[i];
-        h[(size_t)(r0 + row) * N + col] = (uint16_t)f32_to_bf16(silu_f32(g) * u);
+        const float g = g0[i] + g1[i];
+        if constexpr (NMAT == 2) {
+            const float u = part[decode_tail_slot(j, 0, 1) + i] + part[decode_tail_slot(j, 1, 1) + i];
+            static_cast<uint16_t *>(out)[(size_t)(r0 + row) * N + col] =
+                (uint16_t)f32_to_bf16(silu_f32(g) * u);
+        } else {
+            static_cast<float *>(out)[(size_t)(r0 + row) * N + col] = g;
+        }
     }
 }
 
-// Units of a decode gate/up to run whole (the rest are cut in K halves),
+// Units of a decode product to run whole (the rest are cut in K halves),
 // or -1 for none cut: with every expert holding rows (as at decode sizes)
-// a launch has E * ceil(f / 128) units, one per CU at a time; cutting pays
+// a launch has E * ceil(N / 128) units, one per CU at a time; cutting pays
 // when the last round would be at most half full.
-int decode_tail_full_units(int f, int E) {
+int decode_tail_full_units(int N, int E) {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
         return -1;
-    const int units = (f + DCOLS - 1) / DCOLS * E;
+    const int units = (N + DCOLS - 1) / DCOLS * E;
     const int rem = units % cus;
     if (units <= cus || rem == 0 || 2 * rem > cus || rem > kDecodeTailMaxUnits) return -1;
     return units - rem;
@@ -1052,12 +1058,37 @@ hipError_t launch_decode_gateup(const moe_shape_t &s, const uint16_t *xp,
                            rows, src, gpart, n_full, nb_cols);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(decode_tail_finish_kernel, dim3(n_cut), dim3(256), 0, stream, gpart,
-                           counts, offsets, n_full, nb_cols, f, h);
+        hipLaunchKernelGGL(decode_tail_finish_kernel<2>, dim3(n_cut), dim3(256), 0, stream,
+                           gpart, counts, offsets, n_full, nb_cols, f, h);
     } else {
         hipLaunchKernelGGL((decode_gemm_kernel<MB, 2>), dim3(nb_cols, E), dim3(DWAVES * 64), 0,
                            stream, xp, w1, w3, h, counts, offsets, d, f, rows, src, nullptr, 0,
                            0);
+    }
+    return hipGetLastError();
+}
+
+// The decode down product, o = h W2[e]: with gpart, the units past the last
+// full round are cut in K halves as in launch_decode_gateup.
+template <int MB>
+hipError_t launch_decode_down(const moe_shape_t &s, const uint16_t *h, const int32_t *counts,
+                              const int32_t *offsets, const uint16_t *w2, float *o,
+                              hipStream_t stream, float *gpart) {
+    const int d = s.d_model, f = s.d_ff, E = s.n_experts, rows = routed_rows(s);
+    const int nb_cols = (d + DCOLS - 1) / DCOLS;
+    const int n_full = gpart ? decode_tail_full_units(d, E) : -1;
+    if (n_full >= 0) {
+        const int n_cut = nb_cols * E - n_full;
+        hipLaunchKernelGGL((decode_gemm_kernel<MB, 1, true>), dim3(n_full + 2 * n_cut),
+                           dim3(DWAVES * 64), 0, stream, h, w2, nullptr, o, counts, offsets, f,
+                           d, rows, nullptr, gpart, n_full, nb_cols);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(decode_tail_finish_kernel<1>, dim3(n_cut), dim3(256), 0, stream,
+                           gpart, counts, offsets, n_full, nb_cols, d, o);
+    } else {
+        hipLaunchKernelGGL((decode_gemm_kernel<MB, 1>), dim3(nb_cols, E), dim3(DWAVES * 64), 0,
+                           stream, h, w2, nullptr, o, counts, offsets, f, d, rows, nullptr);
     }
     return hipGetLastError();
 }
@@ -1157,16 +1188,12 @@ hipError_t launch_down_split_bf16(int rows, int E, const uint16_t *h, const int3
 
 hipError_t launch_down_bf16(const moe_shape_t &s, const uint16_t *h, const int32_t *counts,
                             const int32_t *offsets, const uint16_t *w2, float *o,
-                            hipStream_t stream) {
+                            hipStream_t stream, float *gpart) {
     const int d = s.d_model, f = s.d_ff, E = s.n_experts, rows = routed_rows(s);
     if (s.T <= 16) {
-        hipLaunchKernelGGL((decode_gemm_kernel<1, 1>), dim3((d + DCOLS - 1) / DCOLS, E),
-                           dim3(DWAVES * 64), 0, stream, h, w2, nullptr, o, counts, offsets, f,
-                           d, rows, nullptr);
+        return launch_decode_down<1>(s, h, counts, offsets, w2, o, stream, gpart);
     } else if (s.T <= kDecodeMaxT) {
-        hipLaunchKernelGGL((decode_gemm_kernel<2, 1>), dim3((d + DCOLS - 1) / DCOLS, E),
-                           dim3(DWAVES * 64), 0, stream, h, w2, nullptr, o, counts, offsets, f,
-                           d, rows, nullptr);
+        return launch_decode_down<2>(s, h, counts, offsets, w2, o, stream, gpart);
     } else {
         const int grid = prefill_grid(rows, E, (d + PBN - 1) / PBN);
         if (f % DBK == 0 && d % PBN == 0)

@@ -92,8 +92,10 @@ hipError_t launch_rank(const moe_shape_t &s, const int32_t *idx, int32_t *counts
 hipError_t launch_gateup(const moe_shape_t &s, const void *xp, const int32_t *counts,
                          const int32_t *offsets, const void *w1, const void *w3, void *h,
                          hipStream_t stream);
+// gpart as for launch_gateup_bf16 (bf16 decode sizes only; may be NULL).
 hipError_t launch_down(const moe_shape_t &s, const void *h, const int32_t *counts,
-                       const int32_t *offsets, const void *w2, float *o, hipStream_t stream);
+                       const int32_t *offsets, const void *w2, float *o, hipStream_t stream,
+                       float *gpart = nullptr);
 
 // y = w0 o[pos0] + w1 o[pos1] + ... (+ res when res is not NULL), rounded
 // once.  With parts > 1, o holds that many partial sums, each kT x d, one
@@ -171,9 +173,11 @@ hipError_t launch_down_split_bf16(int rows, int E, const uint16_t *h, const int3
                                   const int32_t *offsets, const uint16_t *w2, int K, int N,
                                   int parts, size_t part_stride, float *o, int *parts_out,
                                   hipStream_t stream);
+// gpart: as for launch_gateup_bf16 (decode sizes; the down product's last
+// round cut the same way).
 hipError_t launch_down_bf16(const moe_shape_t &s, const uint16_t *h, const int32_t *counts,
                             const int32_t *offsets, const uint16_t *w2, float *o,
-                            hipStream_t stream);
+                            hipStream_t stream, float *gpart = nullptr);
 
 // ---------------------------------------------------------------------------
 // Device helpers.

@@ -171,6 +171,27 @@ def test_decode_tail_cut(wl):
         assert err <= 1e-2, (name, err)
 
 
+# Decode shapes whose down product cuts its last round the same way: 40
+# experts x ceil(d / 128) = 8 column blocks of the output.
+DOWN_TAIL_CASES = [
+    W.small_workload(32, 1024, 256, E=40, seed=25),            # down cut only
+    W.small_workload(16, 1016, 256, E=40, seed=26),            # one row block, ragged d
+    W.small_workload(32, 1024, 1024, E=40, seed=27),           # gate/up and down both cut
+]
+
+
+@pytest.mark.parametrize("wl", DOWN_TAIL_CASES, ids=lambda w: w.name)
+def test_decode_down_tail_cut(wl):
+    """The layer whose decode down product cuts its last round's units in K
+    halves (and adds them in a finishing kernel) against the oracle, every
+    token."""
+    down = wl.with_(f=(wl.d + 127) // 128 * 128)   # units of the down product: E x ceil(d/128)
+    if not tail_cut_applies(down):
+        pytest.skip("this device's CU count does not cut these units")
+    announce(f"decode down tail cut {wl.name} (gate/up cut too: {tail_cut_applies(wl)})")
+    run_forward_parity(checked_inputs(wl))
+
+
 @pytest.mark.parametrize("wl", [SMALL[9], SMALL[1]], ids=lambda w: w.name)
 def test_gateup_with_workspace_off_decode_sizes(wl):
     """Above decode sizes (and for fp32) the gate/up stage with a workspace
