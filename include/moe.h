@@ -192,7 +192,13 @@ int moe_combine(const moe_shape_t *shape, const float *o, const int32_t *pos,
 /* The whole layer: route, dispatch, experts, combine, enqueued back to back
  * on `stream`.  topk_idx_opt / topk_w_opt (int32 [T,k], fp32 [T,k]) receive
  * the routing when non-NULL.  y must not overlap x.
- * ws / ws_bytes: workspace of at least moe_workspace_bytes(shape). */
+ * ws / ws_bytes: workspace of at least moe_workspace_bytes(shape).
+ * At bf16 decode sizes (T <= 32) both expert products may cut the units of
+ * their last round of workgroups in two halves along the reduction, as
+ * moe_expert_gateup_ws describes; at bf16 prefill sizes the down product
+ * may split its reduction in parts that the combine adds.  Either way the
+ * result differs from the unsplit stages only in the order of those
+ * additions. */
 int moe_forward(const moe_shape_t *shape, const void *x, const void *w_gate,
                 const void *w1, const void *w3, const void *w2, void *y,
                 int32_t *topk_idx_opt, float *topk_w_opt,
