@@ -120,3 +120,30 @@ def test_block_forward_replays_in_a_graph():
         ref = moe.block_forward(h, rms_w, 1e-5, g.w_gate, g.w1, g.w3, g.w2, residual=res)
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.uint8), ref.view(torch.uint8)), i
+
+
+@pytest.mark.parametrize("wl", [W.small_workload(600, 256, 512, E=4, seed=78),
+                                W.small_workload(40, 128, 256, dtype=W.F32, seed=79)],
+                         ids=lambda w: w.name)
+def test_backward_replays_in_a_graph(wl):
+    announce(f"backward {wl.name}")
+    g = checked_inputs(wl).to(DEV)
+    gen = torch.Generator().manual_seed(wl.seed + 7)
+    dy = torch.randn(wl.T, wl.d, generator=gen).to(g.x.dtype).to(DEV)
+    ws = torch.empty(moe.backward_workspace_bytes(wl.T, wl.d, wl.f, wl.E, g.x.dtype),
+                     dtype=torch.uint8, device=DEV)
+    x = g.x.clone()
+    outs = []
+    graph = capture(lambda: outs.append(moe.backward(x, g.w_gate, g.w1, g.w3, g.w2, dy,
+                                                     workspace=ws)))
+    grads = outs[-1]                      # the captured call's outputs, refilled by each replay
+    for i in range(REPLAYS):
+        x.copy_(fresh_x(wl, i).to(DEV))
+        for t in grads:
+            t.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = moe.backward(x, g.w_gate, g.w1, g.w3, g.w2, dy)
+        torch.cuda.synchronize()
+        for name, got, want in zip(("dx", "dw_gate", "dw1", "dw3", "dw2"), grads, ref):
+            assert torch.equal(got.view(torch.uint8), want.view(torch.uint8)), (name, i)
