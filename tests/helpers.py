@@ -67,3 +67,39 @@ def down_split_parts(counts, n_cols, cus, k_stages, max_parts=2):
         if best_cost is None or cost < best_cost:
             best, best_cost = parts, cost
     return best
+
+
+def tile_sample(idx, n_experts, tile=256, seed=0, extra=()):
+    """Tokens to check at full size, chosen from the grouped order of the
+    routing `idx` [T, k] (the oracle's stable grouping) so that every row
+    tile of every expert is hit: the first and the last grouped row of
+    each expert (its last tile is the ragged one), the first row of its
+    last tile, and one random row inside each of its tiles.  Tokens 0 and
+    T - 1 and `extra` are added.  Returns sorted unique token indices."""
+    counts, offsets, _, src = oracle.dispatch(idx, n_experts)
+    T, k = np.asarray(idx).shape
+    rng = np.random.default_rng(seed)
+    rows = []
+    for e in range(n_experts):
+        c, o = int(counts[e]), int(offsets[e])
+        if c == 0:
+            continue
+        n_tiles = -(-c // tile)
+        rows += [o, o + c - 1, o + (n_tiles - 1) * tile]
+        for i in range(n_tiles):
+            lo = i * tile
+            rows.append(o + lo + int(rng.integers(0, min(tile, c - lo))))
+    toks = {int(src[r]) // k for r in rows} | {0, T - 1} | {int(t) for t in extra}
+    return np.array(sorted(toks), dtype=np.int64)
+
+
+def tile_columns(n, tile=128, seed=0, per_tile=1):
+    """Column indices of an n-column matrix that hit both edges of every
+    `tile`-wide column tile, and `per_tile` random columns inside each."""
+    rng = np.random.default_rng(seed)
+    cols = set()
+    for lo in range(0, n, tile):
+        hi = min(n, lo + tile)
+        cols |= {lo, hi - 1}
+        cols |= {int(c) for c in rng.integers(lo, hi, per_tile)}
+    return np.array(sorted(cols), dtype=np.int64)

@@ -17,7 +17,7 @@ import oracle
 import sparse_mixture_experts_top2_amd as moe
 from sparse_mixture_experts_top2_amd import workloads as W
 
-from helpers import checked_inputs, down_split_parts, row_max_rel_err, to_f64
+from helpers import checked_inputs, down_split_parts, row_max_rel_err, tile_sample, to_f64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -74,6 +74,12 @@ CASES = [
                                                       # K-contiguous-weight products
     sw(2000, 64, 128, E=64, seed=412),                # router gradient: 8 token chunks
                                                       # of 250, several staged blocks
+    # decode sizes (T <= 32): gate/up through the generic GEMM, then the
+    # down product on a few rows and the K-contiguous dswiglu / dXp kernels
+    sw(1, 256, 512, seed=413),
+    sw(16, 256, 512, seed=414),
+    sw(32, 512, 768, seed=415),                       # d a multiple of 256
+    sw(32, 200, 328, seed=416),                       # d not a multiple of 256
 ]
 
 
@@ -146,10 +152,21 @@ def test_backward_products_in_one_part():
 @pytest.mark.slow
 def test_backward_prefill_size_sampled():
     """The 8x7B prefill step the benchmark times (T = 4096, about 1024 rows
-    per expert, the K-parts and K-contiguous-weight kernels), in one call:
-    dx of a sample of tokens against the oracle run on those tokens alone (a
-    token's dx depends on no other token).  The weight gradients sum over
-    every token and are checked at the smaller sizes above."""
+    per expert, the K-parts and K-contiguous-weight kernels), in one call.
+
+    * dx of tokens chosen from the oracle's grouped order so that every
+      expert's row tiles are reached, against the oracle run on those
+      tokens alone (a token's dx depends on no other token).
+    * The three expert-weight gradients on a sample of d_ff indices n
+      hitting the edges of the column tiles, over all d rows (dw1, dw3)
+      or columns (dw2) and all tokens.  Column n of dw1 and dw3 and row n
+      of dw2 depend on the expert matrices only through column n of w1 and
+      w3 and row n of w2 (the routing depends on x and the router alone),
+      so they equal the gradients of the layer restricted to those d_ff
+      indices, which the oracle computes over every token.
+
+    dw_gate sums the router gradient of every token through the full
+    expert outputs; it is checked at the smaller sizes above."""
     wl = W.WORKLOADS["prefill_8x7b"]
     announce("prefill-size backward: drawing inputs")
     inp = checked_inputs(wl)
@@ -157,9 +174,23 @@ def test_backward_prefill_size_sampled():
     g = inp.to(DEV)
     dx, dwg, dw1, dw3, dw2 = moe.backward(g.x, g.w_gate, g.w1, g.w3, g.w2, dy.to(DEV))
     torch.cuda.synchronize()
-    rows = np.sort(np.random.default_rng(0).choice(wl.T, 8, replace=False))
-    announce("prefill-size backward: oracle on 8 tokens")
+    idx_all, _ = oracle.route(inp.x, inp.w_gate)
+    rows = tile_sample(idx_all, wl.E, seed=wl.seed)
+    announce(f"prefill-size backward: oracle dx on {len(rows)} tokens")
     ref = oracle.backward(inp.x[rows], inp.w_gate, inp.w1, inp.w3, inp.w2, dy[rows])
     err = row_max_rel_err(dx[torch.as_tensor(rows, device=DEV)], ref["dx"])
-    announce(f"  dx (8 tokens) row-max-rel err {err:.3e}")
+    announce(f"  dx ({len(rows)} tokens) row-max-rel err {err:.3e}")
     assert err <= TOL[wl.dtype], err
+    f = wl.f
+    cols = np.array(sorted({0, 1, 127, 128, 255, 256, 511, 512, 4173, f // 2, f - 257,
+                            f - 256, f - 129, f - 128, f - 2, f - 1}), dtype=np.int64)
+    announce(f"prefill-size backward: oracle weight gradients on {len(cols)} d_ff indices")
+    sub = oracle.backward(inp.x, inp.w_gate, inp.w1[:, :, cols].contiguous(),
+                          inp.w3[:, :, cols].contiguous(), inp.w2[:, cols, :].contiguous(), dy)
+    np.testing.assert_array_equal(sub["idx"], idx_all)
+    ct = torch.as_tensor(cols, device=DEV)
+    for name, got, r in (("dw1", dw1[:, :, ct], sub["dw1"]), ("dw3", dw3[:, :, ct], sub["dw3"]),
+                         ("dw2", dw2[:, ct, :], sub["dw2"])):
+        e = max_rel_err(got, r)
+        announce(f"  {name} ({len(cols)} d_ff indices) max-rel err {e:.3e}")
+        assert e <= TOL[wl.dtype], (name, e)

@@ -16,7 +16,7 @@ import oracle
 import sparse_mixture_experts_top2_amd as moe
 from sparse_mixture_experts_top2_amd import workloads as W
 
-from helpers import RW_TOL, Y_TOL, checked_block_inputs, row_max_rel_err, to_f64
+from helpers import RW_TOL, Y_TOL, checked_block_inputs, row_max_rel_err, tile_sample, to_f64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -117,11 +117,13 @@ def test_block_zero_tokens():
     _ = wl
 
 
-@pytest.mark.parametrize("name,n_sample", [("decode_8x7b", 32), ("prefill_8x7b", 24)])
-def test_block_full_size(name, n_sample):
+@pytest.mark.parametrize("name", ["decode_8x7b", "prefill_8x7b"])
+def test_block_full_size(name):
     """The 8x7B shapes in the launch configuration the benchmark times
-    (decode: rows gathered from the normalised input; prefill: the 256x256
-    tile kernels), checked on sampled tokens."""
+    (decode: rows gathered from the normalised input, all 32 tokens
+    checked; prefill: the 256x256 tile kernels, checked on tokens chosen
+    from the oracle's grouped order so that every expert's row tiles, its
+    ragged last one included, are reached)."""
     wl = W.WORKLOADS[name]
     announce(f"block full size {name}")
     inp, g = _inputs(wl)
@@ -130,8 +132,12 @@ def test_block_full_size(name, n_sample):
     out, idx, _ = moe.block_forward(d.x, gd, EPS, d.w_gate, d.w1, d.w3, d.w2, residual=d.x,
                                     return_routing=True)
     torch.cuda.synchronize()
-    rows = np.sort(np.random.default_rng(wl.seed).choice(wl.T, min(n_sample, wl.T),
-                                                         replace=False))
+    if wl.T <= 32:
+        rows = np.arange(wl.T)
+    else:
+        xn_o, _ = oracle.rmsnorm(inp.x, g, EPS)
+        idx_all, _ = oracle.route(xn_o, inp.w_gate)
+        rows = tile_sample(idx_all, wl.E, seed=wl.seed)
     out_o, idx_o, _, _ = oracle.block_forward(inp.x[rows], g, EPS, inp.w_gate, inp.w1, inp.w3,
                                               inp.w2, residual=inp.x[rows])
     np.testing.assert_array_equal(idx.cpu().numpy()[rows], idx_o)

@@ -13,7 +13,8 @@ import oracle
 import sparse_mixture_experts_top2_amd as moe
 from sparse_mixture_experts_top2_amd import workloads as W
 
-from helpers import RW_TOL, Y_TOL, checked_inputs, down_split_parts, row_max_rel_err, to_f64
+from helpers import (RW_TOL, Y_TOL, checked_inputs, down_split_parts, row_max_rel_err,
+                     tile_sample, to_f64)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -334,8 +335,8 @@ def test_power_of_two_scaling_is_exact():
 # The oracle runs on a sample of tokens (each token is independent); routing
 # is checked for every token.
 
-FULL = [("decode_8x7b", None), ("prefill_8x7b", 24), ("skewed_8x7b", 24),
-        ("larger_expert", 12)]
+FULL = [("decode_8x7b", False), ("prefill_8x7b", True), ("skewed_8x7b", True),
+        ("larger_expert", True)]
 
 
 @pytest.mark.slow
@@ -351,17 +352,22 @@ def test_decode_at_the_larger_expert_shape():
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name,n_sample", FULL, ids=[f[0] for f in FULL])
-def test_full_size(name, n_sample):
+@pytest.mark.parametrize("name,sampled", FULL, ids=[f[0] for f in FULL])
+def test_full_size(name, sampled):
+    """Every token's routing and dispatch integers, and the output of a
+    token sample chosen from the oracle's grouped order so that it reaches
+    into every 256-row tile of every expert, its ragged last tile included
+    (for the skewed shape: expert 0's 64 tiles and the three ~3% experts).
+    The decode shape checks all 32 tokens."""
     wl = W.WORKLOADS[name]
     announce(f"full {name}: drawing inputs")
     inp = checked_inputs(wl)
     announce(f"full {name}: {inp.redrawn_rows} rows redrawn; running")
     sample = None
-    if n_sample is not None:
-        rng = np.random.default_rng(0)
-        sample = np.sort(rng.choice(wl.T, size=n_sample, replace=False))
-        sample[0], sample[-1] = 0, wl.T - 1
+    if sampled:
+        idx_all, _ = oracle.route(inp.x, inp.w_gate)
+        sample = tile_sample(idx_all, wl.E, seed=wl.seed)
+        announce(f"full {name}: {len(sample)} tokens cover every expert's row tiles")
     y, idx_o = run_forward_parity(inp, sample)
     # dispatch integers over every token
     g_idx = torch.as_tensor(idx_o, device=DEV)

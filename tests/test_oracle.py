@@ -187,6 +187,24 @@ def pin_expert_rows_match_numpy():
         np.testing.assert_allclose(out[r], (g / (1 + np.exp(-g)) * u) @ w2[e], rtol=1e-12, atol=1e-13)
 
 
+def pin_expert_stages_match_numpy():
+    """The two halves of an expert on their own, against numpy fp64:
+    expert_hidden = silu(x W1[e]) * (x W3[e]) and expert_down = h W2[e],
+    each row with its own expert, d != f so that a swapped width shows."""
+    for seed, dtype in ((22, W.F32), (23, W.BF16)):
+        inp = _rand_layer(T=26, d=16, f=40, E=5, seed=seed, dtype=dtype)
+        ex = ((np.arange(26) * 3) % 5).astype(np.int32)
+        x, w1, w3, w2 = _f64(inp.x), _f64(inp.w1), _f64(inp.w3), _f64(inp.w2)
+        hid = oracle.expert_hidden(inp.x, ex, inp.w1, inp.w3)
+        g = np.einsum("rj,rjn->rn", x, w1[ex])
+        u = np.einsum("rj,rjn->rn", x, w3[ex])
+        np.testing.assert_allclose(hid, g / (1.0 + np.exp(-g)) * u, rtol=1e-12, atol=1e-14)
+        h_in = torch.from_numpy(hid).to(inp.x.dtype)
+        out = oracle.expert_down(h_in, ex, inp.w2)
+        ref = np.einsum("rn,rnm->rm", _f64(h_in), w2[ex])
+        np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-14)
+
+
 def pin_identical_experts_equal_dense_swiglu():
     """All experts equal => the layer is one dense SwiGLU block (the page's
     dense Mistral FFN), because the two routing weights sum to one."""
@@ -562,7 +580,8 @@ def pin_backward_special_cases():
 
 PINS = [pin_worked_examples, pin_logits_match_numpy, pin_top2_brute_force,
         pin_weights_closed_form_and_page_form, pin_forward_matches_numpy_dense,
-        pin_expert_rows_match_numpy, pin_identical_experts_equal_dense_swiglu,
+        pin_expert_rows_match_numpy, pin_expert_stages_match_numpy,
+        pin_identical_experts_equal_dense_swiglu,
         pin_forced_one_hot_router, pin_power_of_two_scaling,
         pin_expert_relabelling_and_token_permutation, pin_dispatch_is_stable_grouping,
         pin_rmsnorm_closed_forms, pin_rmsnorm_invariants, pin_block_identities,
@@ -640,6 +659,10 @@ MUTANTS = {
     "norm_weight_dropped": ("load_elem(c->h, c->dtype, row + j) * r * load_elem(c->g, c->dtype, j)",
                             "load_elem(c->h, c->dtype, row + j) * r"),
     "norm_rounds_toward_zero": ("nearbyint(ldexp(m, 8))", "trunc(ldexp(m, 8))"),
+    "stage_down_reads_model_width": ("int in_w = c->mode == 0 ? c->d : c->f;",
+                                     "int in_w = c->d;"),
+    "stage_hidden_drops_up": ("c->out + (size_t)r * c->f, u);\n        else\n            swiglu_down(c->d, c->f, xr, c->expert[r], c->w2, c->dtype,\n                        c->out + (size_t)r * c->d);\n    }\n    free(xr); free(u);",
+                              "c->out + (size_t)r * c->f, c->out + (size_t)r * c->f);\n        else\n            swiglu_down(c->d, c->f, xr, c->expert[r], c->w2, c->dtype,\n                        c->out + (size_t)r * c->d);\n    }\n    free(xr); free(u);"),
 }
 
 
