@@ -79,7 +79,9 @@ typedef enum {
     MOE_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than moe_workspace_bytes */
     MOE_ERR_UNSUPPORTED = 7, /* E outside [2, 64], top_k outside [1, min(4, E)],
                                  or an int8-weight call off bf16 / T <= 32          */
-    MOE_ERR_HIP = 8          /* a HIP launch failed                               */
+    MOE_ERR_HIP = 8,         /* a HIP launch failed                               */
+    MOE_ERR_SCRATCH = 9      /* moe_forward_noalloc: the shape needs more than
+                                 MOE_SCRATCH_BYTES of workspace                     */
 } moe_status_t;
 
 typedef struct {
@@ -203,6 +205,32 @@ int moe_forward(const moe_shape_t *shape, const void *x, const void *w_gate,
                 const void *w1, const void *w3, const void *w2, void *y,
                 int32_t *topk_idx_opt, float *topk_w_opt,
                 void *ws, size_t ws_bytes, void *stream);
+
+/* ---- The layer without a caller workspace ---------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * moe_forward_noalloc is moe_forward (same kernels, same launch sequence,
+ * bit-identical outputs) with its workspace taken from a fixed array in the
+ * library's own device memory instead of a caller buffer.
+ *   - The array holds MOE_SCRATCH_BYTES (64 MiB: a decode step of the 8x7B
+ *     and larger expert shapes needs about 23-26 MiB).  A shape with
+ *     moe_workspace_bytes(shape) > MOE_SCRATCH_BYTES returns
+ *     MOE_ERR_SCRATCH and enqueues nothing.
+ *   - Each GPU the library runs on holds its own copy of the array until
+ *     the process ends.  The call's first use on a device looks the
+ *     array's device address up (hipGetSymbolAddress); no call allocates,
+ *     frees or memsets anything.
+ *   - Nothing in the array has to start at zero: every call writes each
+ *     workspace entry it reads.
+ *   - All calls on one GPU share that GPU's array, so calls that overlap
+ *     in time on one GPU (two streams, two threads) race and give undefined
+ *     results; order them on one stream.
+ * Arguments, outputs and errors as moe_forward (no ws / ws_bytes); y and
+ * the routing outputs must not overlap the inputs or each other. */
+#define MOE_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_forward_noalloc(const moe_shape_t *shape, const void *x, const void *w_gate,
+                        const void *w1, const void *w3, const void *w2, void *y,
+                        int32_t *topk_idx_opt, float *topk_w_opt, void *stream);
 
 /* ---- Block boundary ----------------------------------------------------
  * The Mistral block of "Mixtral 8x7B -- The Evolving Transformer", section

@@ -24,14 +24,16 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 MOE_F32, MOE_BF16 = 0, 1
 MOE_OK = 0
 STATUS_NAMES = ["MOE_OK", "MOE_ERR_NULL", "MOE_ERR_SHAPE", "MOE_ERR_DTYPE", "MOE_ERR_ALIGN",
-                "MOE_ERR_ALIAS", "MOE_ERR_WORKSPACE", "MOE_ERR_UNSUPPORTED", "MOE_ERR_HIP"]
+                "MOE_ERR_ALIAS", "MOE_ERR_WORKSPACE", "MOE_ERR_UNSUPPORTED", "MOE_ERR_HIP",
+                "MOE_ERR_SCRATCH"]
+SCRATCH_BYTES = 64 << 20      # MOE_SCRATCH_BYTES: moe_forward_noalloc's fixed workspace
 EXPORTED = ["moe_status_str", "moe_workspace_bytes", "moe_route", "moe_route_probs",
             "moe_dispatch",
             "moe_expert_gateup", "moe_expert_gateup_ws", "moe_expert_down", "moe_experts",
             "moe_combine",
             "moe_forward", "moe_rmsnorm_route", "moe_block_forward", "moe_quantize_int8",
             "moe_expert_gateup_w8", "moe_expert_down_w8", "moe_forward_w8",
-            "moe_backward_workspace_bytes", "moe_backward"]
+            "moe_backward_workspace_bytes", "moe_backward", "moe_forward_noalloc"]
 
 
 class MoeShape(ctypes.Structure):
@@ -83,6 +85,8 @@ def load_library(path: Optional[str] = None):
     lib.moe_combine.restype = I
     lib.moe_forward.argtypes = [S, P, P, P, P, P, P, P, P, P, Z, P]
     lib.moe_forward.restype = I
+    lib.moe_forward_noalloc.argtypes = [S, P, P, P, P, P, P, P, P, P]
+    lib.moe_forward_noalloc.restype = I
     F = ctypes.c_float
     lib.moe_rmsnorm_route.argtypes = [S, P, P, F, P, P, P, P, P]
     lib.moe_rmsnorm_route.restype = I
@@ -371,6 +375,40 @@ def forward(x: torch.Tensor, w_gate: torch.Tensor, w1: torch.Tensor, w3: torch.T
                                     _stream(x.device))
     _check(st, "moe_forward")
     return (y, idx, w) if return_routing else y
+
+
+def forward_noalloc(x: torch.Tensor, w_gate: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor,
+                    w2: torch.Tensor, out: Optional[torch.Tensor] = None,
+                    routing_out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+                    top_k: int = 2):
+    """The whole layer through moe_forward_noalloc: no workspace argument
+    (the library's fixed device array, SCRATCH_BYTES, serves as one).
+    Returns y [T, d].  Pass ``out`` (and ``routing_out`` = (topk_idx int32
+    [T, k], topk_w fp32 [T, k]) to receive the routing) so that the call
+    allocates nothing, not even in this wrapper."""
+    _need(x, "x")
+    T, d = x.shape
+    _need(w_gate, "w_gate", x.dtype, x.device)
+    E = w_gate.shape[1]
+    _need(w_gate, "w_gate", shape=(d, E))
+    _need(w1, "w1", x.dtype, x.device)
+    f = w1.shape[2]
+    _need(w1, "w1", shape=(E, d, f))
+    _need(w3, "w3", x.dtype, x.device, (E, d, f))
+    _need(w2, "w2", x.dtype, x.device, (E, f, d))
+    y = out if out is not None else torch.empty(T, d, dtype=x.dtype, device=x.device)
+    _need(y, "out", x.dtype, x.device, (T, d))
+    idx = w = None
+    if routing_out is not None:
+        idx, w = routing_out
+        _need(idx, "topk_idx", torch.int32, x.device, (T, top_k))
+        _need(w, "topk_w", torch.float32, x.device, (T, top_k))
+    shape = make_shape(T, d, f, E, x.dtype, top_k)
+    st = load_library().moe_forward_noalloc(ctypes.byref(shape), _ptr(x), _ptr(w_gate),
+                                            _ptr(w1), _ptr(w3), _ptr(w2), _ptr(y), _ptr(idx),
+                                            _ptr(w), _stream(x.device))
+    _check(st, "moe_forward_noalloc")
+    return y
 
 
 def rmsnorm_route(h: torch.Tensor, rms_weight: torch.Tensor, eps: float, w_gate: torch.Tensor,

@@ -5,6 +5,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -210,6 +212,28 @@ int check_w8(const moe_shape_t *s) {
     return MOE_OK;
 }
 
+// moe_forward_noalloc's workspace: one copy per device, in the library's
+// own device memory.  Host code never passes `scratch` itself (its host
+// name is only a stand-in for the symbol); it uses the device address that
+// scratch_ptr() looks up once per device.
+static __device__ __align__(256) char scratch[MOE_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxScratchDevices];
+
+// Device address of the current device's `scratch`, looked up on the
+// first call on that device (nullptr if the lookup fails).  Two threads
+// racing on the first call both store the same address.
+void *scratch_ptr() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+    return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -225,6 +249,7 @@ const char *moe_status_str(int status) {
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or smaller than moe_workspace_bytes";
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: n_experts must be in [2, 64] and top_k in [1, min(4, n_experts)]; the int8-weight calls take bf16 layers with T <= 32";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP kernel launch failed";
+    case MOE_ERR_SCRATCH: return "MOE_ERR_SCRATCH: the shape needs more workspace than the library's fixed scratch array (MOE_SCRATCH_BYTES)";
     default: return "unknown moe status";
     }
 }
@@ -406,6 +431,31 @@ int moe_forward(const moe_shape_t *s, const void *x, const void *w_gate, const v
         return MOE_ERR_ALIAS;
 
     char *base = static_cast<char *>(ws);
+    int32_t *idx = topk_idx_opt ? topk_idx_opt : reinterpret_cast<int32_t *>(base + L.idx);
+    float *w = topk_w_opt ? topk_w_opt : reinterpret_cast<float *>(base + L.w);
+    return hip_status(run_layer(*s, x, nullptr, 0.0f, w_gate, w1, w3, w2, y, nullptr, idx, w, L,
+                                base, (hipStream_t)stream));
+}
+
+int moe_forward_noalloc(const moe_shape_t *s, const void *x, const void *w_gate,
+                        const void *w1, const void *w3, const void *w2, void *y,
+                        int32_t *topk_idx_opt, float *topk_w_opt, void *stream) {
+    int st = check_shape(s);
+    if (st) return st;
+    if (s->T == 0) return MOE_OK;  // nothing to read or write
+    if (!x || !w_gate || !w1 || !w3 || !w2 || !y) return MOE_ERR_NULL;
+    if (misaligned(x) || misaligned(w_gate) || misaligned(w1) || misaligned(w3) ||
+        misaligned(w2) || misaligned(y) || misaligned(topk_idx_opt) || misaligned(topk_w_opt))
+        return MOE_ERR_ALIGN;
+    const Layout L = plan_workspace(*s);
+    if (L.total > MOE_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+    const Sizes z(*s);
+    if (aliased({Buf{x, z.act}, Buf{w_gate, z.wg}, Buf{w1, z.w13}, Buf{w3, z.w13},
+                 Buf{w2, z.w2}},
+                {Buf{y, z.act}, Buf{topk_idx_opt, z.topk}, Buf{topk_w_opt, z.topk}}))
+        return MOE_ERR_ALIAS;
+    char *base = static_cast<char *>(scratch_ptr());
+    if (!base) return MOE_ERR_HIP;
     int32_t *idx = topk_idx_opt ? topk_idx_opt : reinterpret_cast<int32_t *>(base + L.idx);
     float *w = topk_w_opt ? topk_w_opt : reinterpret_cast<float *>(base + L.w);
     return hip_status(run_layer(*s, x, nullptr, 0.0f, w_gate, w1, w3, w2, y, nullptr, idx, w, L,

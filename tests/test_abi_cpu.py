@@ -310,6 +310,7 @@ ALIAS_CASES = [
     ("moe_experts", "iiiiiiow", {}),
     ("moe_combine", "iiio", {}),
     ("moe_forward", "iiiiiooow", {}),
+    ("moe_forward_noalloc", "iiiiiooo", {}),
     ("moe_rmsnorm_route", "iifiooo", {}),
     ("moe_block_forward", "iifiiiiiooow", {"allowed": {(8, 0), (8, 3)}}),
     ("moe_expert_gateup_w8", "iiiiiiio", {"T": 16}),
@@ -352,3 +353,26 @@ def test_every_overlap_is_refused(fn, roles, opt):
         # a buffer that starts just inside another one overlaps it too
         ptrs[a] = ctypes.c_void_p(spaced[b].value + 16)
         assert run(ptrs) == "MOE_ERR_ALIAS", (fn, a, b, "+16")
+
+
+def test_noalloc_checks():
+    """moe_forward_noalloc: moe_forward's checks, and MOE_ERR_SCRATCH for a
+    shape whose workspace exceeds the library's fixed array (returned before
+    the array is looked up, so no GPU is needed to see it)."""
+    lib = moe.load_library()
+    name = lambda st: moe.STATUS_NAMES[st]
+    call = lambda s, x=P16, y=P16B: lib.moe_forward_noalloc(
+        ctypes.byref(s) if s is not None else None, x, P16, P16, P16, P16, y, None, None, None)
+    assert name(call(None)) == "MOE_ERR_NULL"
+    assert name(call(shape(), x=None)) == "MOE_ERR_NULL"
+    assert name(call(shape(), x=P17)) == "MOE_ERR_ALIGN"
+    assert name(call(shape(), y=P16)) == "MOE_ERR_ALIAS"
+    assert name(call(shape(k=5))) == "MOE_ERR_UNSUPPORTED"
+    assert call(shape(T=0)) == moe.MOE_OK
+    big = shape(T=4096, d=4096, f=14336)
+    assert lib.moe_workspace_bytes(ctypes.byref(big)) > moe.SCRATCH_BYTES
+    assert name(call(big)) == "MOE_ERR_SCRATCH"
+    # the decode steps of the 8x7B and larger expert shapes fit
+    for d, f in ((4096, 14336), (6144, 16384)):
+        s = shape(T=32, d=d, f=f)
+        assert 0 < lib.moe_workspace_bytes(ctypes.byref(s)) <= moe.SCRATCH_BYTES
