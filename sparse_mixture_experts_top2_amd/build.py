@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 SOURCES = ["abi.hip", "route.hip", "dispatch.hip", "combine.hip", "experts_f32.hip",
-           "experts_bf16.hip", "experts_w8.hip", "backward.hip"]
+           "experts_bf16.hip", "gemm_bf16.hip", "experts_w8.hip", "backward.hip"]
 ARCH = "gfx950"
 
 

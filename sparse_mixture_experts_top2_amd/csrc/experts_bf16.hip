@@ -94,7 +94,10 @@ constexpr int PGM = MOE_PREFILL_PGM;   // row tiles per scheduling group (see pr
 #ifndef MOE_PREFILL_WN
 #define MOE_PREFILL_WN 4
 #endif
-constexpr int PWM = 2, PWN = MOE_PREFILL_WN;
+#ifndef MOE_PREFILL_WM
+#define MOE_PREFILL_WM 2
+#endif
+constexpr int PWM = MOE_PREFILL_WM, PWN = MOE_PREFILL_WN;
 
 // Work decomposition shared by the prefill kernels.  Row tiles of PBM rows
 // are numbered expert after expert; the flat tile list orders them in
@@ -1108,7 +1111,10 @@ hipError_t launch_gateup_bf16(const moe_shape_t &s, const uint16_t *xp, const in
         return hipErrorInvalidValue;   // the gather is only built into the decode kernels
     } else {
         const int grid = prefill_grid(rows, E, (f + PBN / 2 - 1) / (PBN / 2));
-        if (d % DBK == 0 && f % (PBN / 2) == 0)
+        if (q_gateup_supported(rows, d, f))
+            return q_launch_gateup(rows, E, xp, counts, offsets, w1, w3, d, f, h, nullptr,
+                                   nullptr, stream);
+        else if (d % DBK == 0 && f % (PBN / 2) == 0)
             hipLaunchKernelGGL(prefill_dma_kernel<2>, dim3(grid), dim3(PWM * PWN * 64), 0,
                                stream, xp, w1, w3, h, counts, offsets, E, d, f, rows);
         else
@@ -1124,6 +1130,8 @@ hipError_t launch_gateup_bf16_gu(const moe_shape_t &s, const uint16_t *xp,
                                  float *u, hipStream_t stream) {
     const int d = s.d_model, f = s.d_ff, E = s.n_experts, rows = routed_rows(s);
     if (s.T <= kDecodeMaxT || d % DBK != 0 || f % (PBN / 2) != 0) return hipErrorNotSupported;
+    if (q_gateup_supported(rows, d, f))
+        return q_launch_gateup(rows, E, xp, counts, offsets, w1, w3, d, f, h, g, u, stream);
     const int grid = prefill_grid(rows, E, (f + PBN / 2 - 1) / (PBN / 2));
     hipLaunchKernelGGL(prefill_dma_gu_kernel, dim3(grid), dim3(PWM * PWN * 64), 0, stream, xp,
                        w1, w3, h, counts, offsets, E, d, f, rows, g, u);
@@ -1179,6 +1187,9 @@ hipError_t launch_down_split_bf16(int rows, int E, const uint16_t *h, const int3
         cu_per_xcd = cus_per_xcd();
         if (cu_per_xcd < 0) return hipErrorNotSupported;
     }
+    if (q_down_supported(rows, K, N))
+        return q_launch_down(rows, E, h, counts, offsets, w2, K, N, o, parts, part_stride,
+                             cu_per_xcd, parts_out, stream);
     const int grid = prefill_grid(rows, E, (N / PBN) * (parts ? parts : kMaxDownSplit));
     hipLaunchKernelGGL(prefill_dma_down_split_kernel, dim3(grid), dim3(PWM * PWN * 64), 0, stream,
                        h, w2, o, counts, offsets, E, K, N, rows, parts, part_stride, cu_per_xcd,
@@ -1196,7 +1207,10 @@ hipError_t launch_down_bf16(const moe_shape_t &s, const uint16_t *h, const int32
         return launch_decode_down<2>(s, h, counts, offsets, w2, o, stream, gpart);
     } else {
         const int grid = prefill_grid(rows, E, (d + PBN - 1) / PBN);
-        if (f % DBK == 0 && d % PBN == 0)
+        if (q_down_supported(rows, f, d))
+            return q_launch_down(rows, E, h, counts, offsets, w2, f, d, o, 1, 0, 0, nullptr,
+                                 stream);
+        else if (f % DBK == 0 && d % PBN == 0)
             hipLaunchKernelGGL(prefill_dma_kernel<1>, dim3(grid), dim3(PWM * PWN * 64), 0,
                                stream, h, w2, nullptr, o, counts, offsets, E, f, d, rows);
         else

@@ -1,0 +1,623 @@
+// Prefill grouped GEMMs on the CDNA4 matrix cores, software-pipelined for
+// one wavefront per SIMD.  These are the two products of the SwiGLU expert
+// of "Mixtral 8x7B -- The Evolving Transformer", section 04
+// (down(silu(gate x) * up x)), applied to the per-expert row batches of
+// section 05: gate/up (h = silu(A W1[e]) * (A W3[e]), bf16) and down
+// (o = h W2[e], fp32, optionally in K parts).
+//
+// Tile and wavefront layout.  A workgroup computes a 256-row x 256-column
+// output tile (gate/up: 128 gate + the same 128 up columns) with four
+// wavefronts, one per SIMD.  Each wavefront owns ALL 256 rows and 64
+// columns (gate/up: 32 gate + the matching 32 up columns), i.e. 8 x 2
+// blocks of v_mfma_f32_32x32x16_bf16 with 256 fp32 accumulators held in
+// AGPRs.  Every weight fragment is therefore read from LDS by exactly one
+// wavefront (the transpose read ds_read_b64_tr_b16 is the expensive LDS
+// read), and every activation fragment by four.  Per 16-deep K step a
+// wavefront issues 16 MFMAs (512 cycles of its SIMD's matrix core), 8
+// ds_read_b128 and 4 ds_read_b64_tr_b16.
+//
+// Schedule.  With one wavefront per SIMD nothing else hides LDS latency,
+// so the K loop is written as an explicit pipeline: the 12 fragment reads
+// of step k+1 are interleaved one per MFMA with the 16 MFMAs of step k
+// (double-buffered fragment registers), and the global->LDS copies of later
+// stages go into the remaining MFMA slots.  sched_barrier pins that order.
+// Each 64-deep stage has one workgroup barrier, placed after the first MFMA
+// of the stage's last step, so that it and the first reads of the next
+// stage run while the matrix core is busy.
+//
+// Operands reach LDS by buffer_load ... lds (no registers, no VALU): the
+// activations in a 2-slot ring and the weights (mostly fetched from beyond
+// L2) in a 3-slot ring, five 32 KiB slots filling the 160 KiB of LDS.  The
+// buffer resource of the activations ends at their last row, so rows past
+// it read as zeros.  Loads past the last stage re-read the last stage into
+// a free slot, so every wait count in the loop is a constant.
+#include <algorithm>
+#include <type_traits>
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int QBM = 256;               // rows per tile
+constexpr int QBN = 256;               // columns per tile
+constexpr int QBK = 64;                // reduction depth of one stage
+constexpr int QW = 4;                  // wavefronts per workgroup
+constexpr int QT = QW * 64;            // threads per workgroup
+constexpr int QSLOT = QBM * QBK * 2;   // bytes of one stage of either operand: 32 KiB
+constexpr int QAS = 2, QBS = 3;        // ring depths (activations, weights)
+constexpr int QU = 6;                  // stages per unrolled loop body (lcm of the depths)
+constexpr int QPGM = 4;                // row tiles per scheduling group
+constexpr int QMAXSPLIT = kMaxDownSplit;
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+#define Q_INLINE __attribute__((always_inline))
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void q_for_from(F &&f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        q_for_from<I + 1, N>(f);
+    }
+}
+// f(integral_constant<int, i>) for i = 0 .. N-1.
+template <int N, typename F>
+__device__ __forceinline__ void q_for(F &&f) { q_for_from<0, N>(f); }
+
+// Raw buffer resource over `bytes` bytes at `base` (gfx9 word 3: 32-bit
+// untyped data).  Offsets at or past `bytes` read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t q_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+// 16 bytes per lane from rsrc + voffset + soffset into LDS at dst + 16 * lane.
+__device__ __forceinline__ void q_dma(__amdgpu_buffer_rsrc_t r, uint8_t *dst, uint32_t voff,
+                                      uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)dst, 16, (int)voff, (int)soff, 0, 0);
+}
+
+// Swizzles (16-byte chunk index XOR a function of the LDS row) that keep
+// the fragment reads of consecutive rows on distinct banks.
+//   activations: 8 chunks per 128-byte row;
+//   weights, one matrix: 32 chunks per 512-byte row;
+//   weights, gate | up: two sub-tiles of 16 chunks per 256-byte row.
+__device__ __forceinline__ int q_aswz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+__device__ __forceinline__ int q_bswz1(int r) { return (r & 7) << 2; }
+__device__ __forceinline__ int q_bswz2(int r) { return (r & 3) << 2; }
+
+// Workgroup barrier of the rings: this wavefront's LDS copies up to the
+// last N issued have landed and its LDS reads have returned, then all
+// wavefronts meet.  (__syncthreads would wait for every outstanding copy.)
+// gfx9 s_waitcnt: vmcnt bits 3:0 and 15:14, expcnt 6:4 (left at its
+// maximum), lgkmcnt 11:8 (zero).
+template <int N>
+__device__ __forceinline__ void q_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
+// Persistent schedule.  The grid is one workgroup per CU (8 XCDs x
+// cu_per_xcd); each workgroup runs a list of tiles.
+//
+// Row tiles (256 rows of one expert) fall into three classes by the 32-row
+// blocks they need: class 0 (more than 128 rows: 8 blocks), class 1 (65 to
+// 128 rows: 4 blocks) and class 2 (at most 64 rows: 2 blocks), so that an
+// expert's short last tile costs about a quarter of a full one instead of
+// a whole one.  Within a class the tiles are listed in groups of QPGM row
+// tiles, all column tiles of a group before the next (row tile fastest),
+// so that tiles next to each other in the list share weight and activation
+// tiles.  Each class list is cut into 8 contiguous chunks, one per XCD
+// (workgroup b runs on XCD b % 8); XCD x's list is its class 0 chunk, then
+// its class 1 and class 2 chunks, and its workgroups take that list round
+// robin (workgroup j of the XCD: entries j, j + cu_per_xcd, ...).  The
+// workgroups resident on one XCD therefore work on neighbouring tiles at
+// any time, and the cheap tiles come last, after the full ones, filling
+// the end of the schedule.
+constexpr float QCOST[3] = {1.0f, 0.6f, 0.4f};   // rough cost of a tile of each class
+
+__device__ __forceinline__ int q_class(int rows) { return rows > 128 ? 0 : rows > 64 ? 1 : 2; }
+
+// Row tiles of class c per expert: class 0 takes the full tiles and a last
+// tile of more than 128 rows; classes 1 and 2 a last tile of their size.
+__device__ __forceinline__ int q_class_tiles(int count, int c) {
+    const int full = count / QBM, tail = count % QBM;
+    return (c == 0 ? full : 0) + (tail > 0 && q_class(tail) == c ? 1 : 0);
+}
+
+// Row tile mt of class c -> (expert, first row, end of the expert's rows).
+__device__ __forceinline__ void q_row_tile(const int32_t *counts, const int32_t *offsets, int E,
+                                           int c, int mt, int &e_out, int &row0, int &row_end) {
+    int acc = 0;
+    for (int e = 0; e < E; ++e) {
+        const int cnt = counts[e];
+        const int n = q_class_tiles(cnt, c);
+        if (mt < acc + n) {
+            const int k = mt - acc;
+            e_out = e;
+            row0 = offsets[e] + (c == 0 && k < cnt / QBM ? k : cnt / QBM) * QBM;
+            row_end = offsets[e] + cnt;
+            return;
+        }
+        acc += n;
+    }
+    e_out = 0;
+    row0 = row_end = 0;   // not reached for mt < the class's tile count
+}
+
+// Entry `idx` of a class list with n_tiles column tiles: (row tile, column tile).
+__device__ __forceinline__ void q_group_pos(int idx, int m_c, int n_tiles, int &mt, int &nt) {
+    const int group = idx / (QPGM * n_tiles);
+    const int first = group * QPGM;
+    const int gm = min(QPGM, m_c - first);
+    const int within = idx - group * QPGM * n_tiles;
+    mt = first + within % gm;
+    nt = within / gm;
+}
+
+// Estimated time of the schedule, in full-tile units, for tiles cut in S
+// parts along K: the busiest workgroup of an XCD carries about
+// max(ceil(full / cpx), all / cpx + one tile) plus a fifth of a tile per
+// extra part (writing and re-reading the fp32 partial sums).
+__device__ __forceinline__ float q_makespan(const int (&m)[3], int n_cols, int S, int cpx) {
+    const float n0 = (float)m[0] * n_cols * S / 8.0f;
+    const float all = (QCOST[0] * m[0] + QCOST[1] * m[1] + QCOST[2] * m[2]) * n_cols * S / 8.0f;
+    const float a = ceilf(n0 / cpx), b = all / cpx + 1.0f;
+    return (a > b ? a : b) / S + 0.2f * (S - 1);
+}
+
+// The GEMM body.
+//   NMAT = 2: C = h = bf16(silu(A B0[e]) * (A B1[e])), [a_rows, N] with N = d_ff;
+//             with GU also g = A B0[e], u = A B1[e] (fp32 [a_rows, N]).
+//   NMAT = 1: C = o = fp32(A B0[e]), [a_rows, N]; with KSPLIT the reduction is
+//             cut into `parts` runs of whole stages, part p stored at
+//             C + p * part_stride (parts = 0: chosen here from the counts,
+//             stored to *parts_out by workgroup 0).
+// A [a_rows, K] row-major (expert-grouped rows), B0/B1 [E, K, N] row-major.
+// Requires K % 64 == 0, N % (256 / NMAT) == 0, a_rows * K * 2 < 2^32 and
+// K * N * 2 < 2^32 (checked by the launchers).
+struct QSlots {
+    uint8_t *a0, *a1, *b0, *b1, *b2;
+};
+
+struct QArgs {
+    const uint16_t *A, *B0, *B1;
+    void *C;
+    int K, N, a_rows;
+    float *g_out, *u_out;
+    size_t part_stride;
+};
+
+// One output tile with MBE 32-row blocks per wavefront: rows row0 ..
+// row0 + 32 MBE (stored up to row_end), columns n0 .. of expert e,
+// reduction stages kt0 .. kt0 + nk.
+template <int NMAT, bool GU, bool KSPLIT, int MBE>
+__device__ __forceinline__ void q_tile_run(const QSlots &S, const QArgs &g, int e, int row0,
+                                           int row_end, int n0, int kt0, int nk, int part) {
+    constexpr int BNM = QBN / NMAT;
+    const int K = g.K, N = g.N;
+    auto slot_a = [&](auto i_c) Q_INLINE {
+        constexpr int i = decltype(i_c)::value % QAS;
+        if constexpr (i == 0) return S.a0;
+        else return S.a1;
+    };
+    auto slot_b = [&](auto i_c) Q_INLINE {
+        constexpr int i = decltype(i_c)::value % QBS;
+        if constexpr (i == 0) return S.b0;
+        else if constexpr (i == 1) return S.b1;
+        else return S.b2;
+    };
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // ---- global -> LDS copies (1 KiB instructions: 64 lanes x 16 B).
+    // Activations: the tile's 32 MBE rows are 4 MBE instructions of 8 rows,
+    // MBE per wavefront (instruction g = MBE w + j: rows 8 g .. 8 g + 7),
+    // lane l row 8 g + l / 8, LDS chunk l % 8 = K chunk c ^ aswz(row).
+    const __amdgpu_buffer_rsrc_t ra = q_rsrc(g.A, (uint32_t)((size_t)g.a_rows * K * 2));
+    uint32_t a_vo[MBE];
+#pragma unroll
+    for (int j = 0; j < MBE; ++j) {
+        const int r = 8 * (wave * MBE + j) + (lane >> 3);
+        const int c = (lane & 7) ^ q_aswz(r);
+        a_vo[j] = (uint32_t)(((size_t)(row0 + r) * K + c * 8) * 2);
+    }
+    // Weights, 32 instructions per stage, 8 per wavefront.  NMAT = 1:
+    // instruction g holds K rows 2 g, 2 g + 1 (512 B each), lane l row
+    // 2 g + l / 32, LDS chunk l % 32 = column chunk c ^ bswz1(row).  NMAT = 2:
+    // instructions 0..15 the gate sub-tile, 16..31 the up sub-tile (waves
+    // 0, 1 and 2, 3), each 4 K rows of 256 B, lane l row 4 (g % 16) + l / 16,
+    // LDS chunk l % 16 = c ^ bswz2(row).
+    const uint16_t *Bw = (NMAT == 2 && wave >= 2) ? g.B1 : g.B0;
+    const __amdgpu_buffer_rsrc_t rb =
+        q_rsrc(Bw + (size_t)e * K * N, (uint32_t)((size_t)K * N * 2));
+    uint32_t b_vo[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        int r, c;
+        if constexpr (NMAT == 2) {
+            r = 4 * (((wave & 1) << 3) + j) + (lane >> 4);
+            c = (lane & 15) ^ q_bswz2(r);
+        } else {
+            r = 2 * (wave * 8 + j) + (lane >> 5);
+            c = (lane & 31) ^ q_bswz1(r);
+        }
+        b_vo[j] = (uint32_t)(((size_t)r * N + n0 + c * 8) * 2);
+    }
+    auto b_dst = [&](int j) Q_INLINE {
+        if constexpr (NMAT == 2) return (wave >> 1) * (QSLOT / 2) + (((wave & 1) << 3) + j) * 1024;
+        else return (wave * 8 + j) * 1024;
+    };
+    // Copies of stage s (clamped to the last stage: harmless re-reads).
+    auto a_copy = [&](uint8_t *slot, int s, int j) Q_INLINE {
+        const int k0 = (kt0 + min(s, nk - 1)) * QBK;
+        q_dma(ra, slot + (wave * MBE + j) * 1024, a_vo[j], (uint32_t)(k0 * 2));
+    };
+    auto b_copy = [&](uint8_t *slot, int s, int j) Q_INLINE {
+        const int k0 = (kt0 + min(s, nk - 1)) * QBK;
+        q_dma(rb, slot + b_dst(j), b_vo[j], (uint32_t)((size_t)k0 * N * 2));
+    };
+
+    // ---- fragment reads.
+    // A block i, step h (16 K values): row 32 i + l % 32, K chunk 2 h + l / 32.
+    int a_off[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+        a_off[h] = (lane & 31) * 128 + (((2 * h + (lane >> 5)) ^ q_aswz(lane & 31)) << 4);
+    // B block j (transpose read): lane l of 16-lane group G gets column
+    // 16 (G & 1) + l % 16 of K rows 8 (G >> 1) + 4 u + 0..3 (u = 0, 1 the two
+    // halves of its 8 K values).
+    int b_off[2][2];
+    {
+        const int G = lane >> 4, ii = (lane & 15) >> 2, q = lane & 3;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int r = 8 * (G >> 1) + 4 * u + ii;   // + 16 h
+                if constexpr (NMAT == 2) {
+                    const int n = wave * 32 + 16 * (G & 1) + 4 * q;
+                    b_off[j][u] = j * (QSLOT / 2) + r * 256 + (((n >> 3) ^ q_bswz2(r)) << 4) +
+                                  (n & 7) * 2;
+                } else {
+                    const int n = wave * 64 + 32 * j + 16 * (G & 1) + 4 * q;
+                    b_off[j][u] = r * 512 + (((n >> 3) ^ q_bswz1(r)) << 4) + (n & 7) * 2;
+                }
+            }
+    }
+    constexpr int BSTEP = NMAT == 2 ? 16 * 256 : 16 * 512;   // bytes per 16 K rows
+
+    bf16x8_t fa[2][MBE];
+    s16x4_t fb[2][2][2];
+    f32x16_t acc[MBE][2];
+#pragma unroll
+    for (int i = 0; i < MBE; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+    // Read item r (0 .. MBE + 3) of a step into buffer `buf`: 0, 1 the
+    // halves of B block 0, 2 .. MBE + 1 the A blocks, then the halves of B
+    // block 1 (the order the next step's MFMAs use them in).
+    constexpr int NR = MBE + 4;
+    auto read_item = [&](auto buf_c, auto r_c, const uint8_t *sa, const uint8_t *sb,
+                         int h) Q_INLINE {
+        constexpr int bf = decltype(buf_c)::value, r = decltype(r_c)::value;
+        if constexpr (r >= 2 && r < MBE + 2) {
+            fa[bf][r - 2] = __builtin_bit_cast(
+                bf16x8_t, *reinterpret_cast<const uint4 *>(sa + a_off[h] + (r - 2) * 32 * 128));
+        } else {
+            constexpr int j = r < 2 ? 0 : 1, u = r < 2 ? r : r - MBE - 2;
+            fb[bf][j][u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4_t *)(sb + b_off[j][u] + h * BSTEP));
+        }
+    };
+    // MFMA m of a step: block (i, j) = (m % MBE, m / MBE).
+    constexpr int NM = 2 * MBE;
+    auto mfma_item = [&](auto buf_c, auto m_c) Q_INLINE {
+        constexpr int bf = decltype(buf_c)::value, m = decltype(m_c)::value;
+        constexpr int j = m / MBE, i = m % MBE;
+        const bf16x8_t b = __builtin_bit_cast(
+            bf16x8_t, __builtin_shufflevector(fb[bf][j][0], fb[bf][j][1], 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[bf][i], b, acc[i][j], 0, 0, 0);
+    };
+
+    // Stage s (ring position t = s mod QU), steps h = 0..3.  Copies issued
+    // in the window that follows the barrier of stage s - 1 (step (s-1, 3)
+    // after the barrier, steps (s, 0) and (s, 1)): activations of stage
+    // s + 1, then weights of stage s + 2, into the slots stage s - 1 has
+    // left.  At the barrier of stage s (in its step 3) the activations and
+    // weights of stage s + 1 must have landed; only the 8 weight copies of
+    // stage s + 2 may still be in flight.  Each step's items (the next
+    // step's fragment reads, then its copies) are spread evenly over its
+    // MFMAs.
+    auto stage = [&](auto t_c, int s) Q_INLINE {
+        constexpr int t = decltype(t_c)::value;
+        const uint8_t *sa = slot_a(t_c), *sb = slot_b(t_c);
+        const uint8_t *sa_n = slot_a(std::integral_constant<int, t + 1>{});
+        const uint8_t *sb_n = slot_b(std::integral_constant<int, t + 1>{});
+        uint8_t *wa = slot_a(std::integral_constant<int, t + 2>{});   // activations, stage s + 2
+        uint8_t *wb = slot_b(std::integral_constant<int, t + 2>{});   // weights, stage s + 2
+        q_for<4>([&](auto h_c) Q_INLINE {
+            constexpr int h = decltype(h_c)::value;
+            constexpr int cur = h & 1, nxt = cur ^ 1;
+            constexpr int NC = h == 3 ? MBE : h < 2 ? 4 : 0;    // copies in this step
+            constexpr int NI = NR + NC;
+            q_for<NM>([&](auto m_c) Q_INLINE {
+                constexpr int m = decltype(m_c)::value;
+                mfma_item(std::integral_constant<int, cur>{}, m_c);
+                if constexpr (h == 3 && m == 0) q_barrier<8>();
+                constexpr int lo = m * NI / NM, hi = (m + 1) * NI / NM;
+                q_for<NI>([&](auto it_c) Q_INLINE {
+                    constexpr int it = decltype(it_c)::value;
+                    if constexpr (it >= lo && it < hi) {
+                        if constexpr (it < NR) {
+                            if constexpr (h < 3)
+                                read_item(std::integral_constant<int, nxt>{}, it_c, sa, sb, h + 1);
+                            else
+                                read_item(std::integral_constant<int, nxt>{},
+                                          std::integral_constant<int, it>{}, sa_n, sb_n, 0);
+                        } else if constexpr (h == 3) {
+                            a_copy(wa, s + 2, it - NR);
+                        } else {
+                            b_copy(wb, s + 2, it - NR + 4 * h);
+                        }
+                    }
+                });
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        });
+    };
+
+    // Prologue: what the windows of stages -2 and -1 would have issued, then
+    // the fragments of step (0, 0).
+#pragma unroll
+    for (int j = 0; j < MBE; ++j) a_copy(slot_a(std::integral_constant<int, 0>{}), 0, j);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) b_copy(slot_b(std::integral_constant<int, 0>{}), 0, j);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) b_copy(slot_b(std::integral_constant<int, 1>{}), 1, j);
+#pragma unroll
+    for (int j = 0; j < MBE; ++j) a_copy(slot_a(std::integral_constant<int, 1>{}), 1, j);
+    q_barrier<8 + MBE>();
+    q_for<NR>([&](auto r_c) Q_INLINE {
+        read_item(std::integral_constant<int, 0>{}, r_c, slot_a(std::integral_constant<int, 0>{}),
+                  slot_b(std::integral_constant<int, 0>{}), 0);
+    });
+
+    int kt = 0;
+    for (; kt + QU <= nk; kt += QU)
+        q_for<QU>([&](auto t_c) Q_INLINE { stage(t_c, kt + decltype(t_c)::value); });
+    q_for<QU - 1>([&](auto t_c) Q_INLINE {
+        if (kt + decltype(t_c)::value < nk) stage(t_c, kt + decltype(t_c)::value);
+    });
+    // Every copy has landed and every wavefront is done with the rings
+    // before the next tile's prologue refills them.
+    q_barrier<0>();
+
+    // 32x32 accumulator layout: value q of lane l is row 8 (q / 4) + 4 (l / 32)
+    // + q % 4, column l % 32 of the block.
+    if constexpr (NMAT == 2) {
+        // h = silu(g) u in bf16, stored straight from the accumulators as
+        // 4-byte column pairs: lanes l and l ^ 1 hold neighbouring columns
+        // of the same rows and swap one value (a DPP quad permutation), so
+        // that the even lane stores row q and the odd lane row q + 1.
+        uint16_t *H = static_cast<uint16_t *>(g.C);
+        const int odd = lane & 1;
+        const int col = n0 + wave * 32 + (lane & 31) - odd;
+#pragma unroll
+        for (int i = 0; i < MBE; ++i)
+#pragma unroll
+            for (int q = 0; q < 16; q += 2) {
+                auto hval = [&](int qq) Q_INLINE {
+                    const float gv = acc[i][0][qq], uv = acc[i][1][qq];
+                    return f32_to_bf16(gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv);
+                };
+                const uint32_t h0 = hval(q), h1 = hval(q + 1);
+                const uint32_t x = odd ? h0 : h1;
+                const uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);
+                const uint32_t packed = odd ? (y | (h1 << 16)) : (h0 | (y << 16));
+                const int row = row0 + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3) + odd;
+                if (row < row_end)
+                    __builtin_nontemporal_store(packed,
+                                                reinterpret_cast<uint32_t *>(H + (size_t)row * N + col));
+            }
+        if constexpr (GU) {
+            const int gcol = n0 + wave * 32 + (lane & 31);
+#pragma unroll
+            for (int i = 0; i < MBE; ++i)
+#pragma unroll
+                for (int qq = 0; qq < 16; ++qq) {
+                    const int row = row0 + i * 32 + 8 * (qq >> 2) + 4 * (lane >> 5) + (qq & 3);
+                    if (row < row_end) {
+                        g.g_out[(size_t)row * N + gcol] = acc[i][0][qq];
+                        g.u_out[(size_t)row * N + gcol] = acc[i][1][qq];
+                    }
+                }
+        }
+    } else {
+        float *O = static_cast<float *>(g.C) + (KSPLIT ? (size_t)part * g.part_stride : 0);
+#pragma unroll
+        for (int i = 0; i < MBE; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int col = n0 + wave * 64 + j * 32 + (lane & 31);
+#pragma unroll
+                for (int qq = 0; qq < 16; ++qq) {
+                    const int row = row0 + i * 32 + 8 * (qq >> 2) + 4 * (lane >> 5) + (qq & 3);
+                    if (row < row_end) O[(size_t)row * N + col] = acc[i][j][qq];
+                }
+            }
+    }
+}
+
+template <int NMAT, bool GU, bool KSPLIT>
+__device__ __forceinline__ void q_body(const QArgs &g, const int32_t *__restrict__ counts,
+                                       const int32_t *__restrict__ offsets, int E, int parts,
+                                       int cu_per_xcd, int *__restrict__ parts_out) {
+    static_assert(NMAT == 1 || NMAT == 2, "one or two weight matrices");
+    static_assert(!GU || NMAT == 2, "g and u exist for gate/up only");
+    static_assert(!KSPLIT || NMAT == 1, "the down product is the one cut in parts");
+    constexpr int BNM = QBN / NMAT;
+    const int n_cols = g.N / BNM;
+    int m[3] = {0, 0, 0};
+    for (int i = 0; i < E; ++i) {
+        const int c = counts[i];
+#pragma unroll
+        for (int k = 0; k < 3; ++k) m[k] += q_class_tiles(c, k);
+    }
+    if constexpr (KSPLIT) {
+        if (parts == 0) {
+            parts = 1;
+            float best = q_makespan(m, n_cols, 1, cu_per_xcd);
+            for (int S = 2; S <= QMAXSPLIT && S <= g.K / QBK; ++S) {
+                const float t = q_makespan(m, n_cols, S, cu_per_xcd);
+                if (t < best) { best = t; parts = S; }
+            }
+            if (blockIdx.x == 0 && threadIdx.x == 0) *parts_out = parts;
+        }
+    }
+    const int n_tiles = KSPLIT ? n_cols * parts : n_cols;
+
+    __shared__ __attribute__((aligned(1024))) uint8_t sa0[QSLOT];
+    __shared__ __attribute__((aligned(1024))) uint8_t sa1[QSLOT];
+    __shared__ __attribute__((aligned(1024))) uint8_t sb0[QSLOT];
+    __shared__ __attribute__((aligned(1024))) uint8_t sb1[QSLOT];
+    __shared__ __attribute__((aligned(1024))) uint8_t sb2[QSLOT];
+    const QSlots S{sa0, sa1, sb0, sb1, sb2};
+
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    int lo[3], len[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const int64_t T = (int64_t)m[k] * n_tiles;
+        lo[k] = (int)(T * xcd / 8);
+        len[k] = (int)(T * (xcd + 1) / 8) - lo[k];
+    }
+    const int total = len[0] + len[1] + len[2];
+    const int nk_all = g.K / QBK;
+    for (int idx = j; idx < total; idx += cu_per_xcd) {
+        int c = 0, f = idx;
+        if (f >= len[0]) {
+            f -= len[0];
+            c = 1;
+            if (f >= len[1]) {
+                f -= len[1];
+                c = 2;
+            }
+        }
+        int mt, nt, e, row0, row_end;
+        q_group_pos(lo[c] + f, m[c], n_tiles, mt, nt);
+        q_row_tile(counts, offsets, E, c, mt, e, row0, row_end);
+        int part = 0, kt0 = 0, nk = nk_all;
+        if constexpr (KSPLIT) {
+            part = nt / n_cols;
+            nt -= part * n_cols;
+            kt0 = (int)((int64_t)nk_all * part / parts);
+            nk = (int)((int64_t)nk_all * (part + 1) / parts) - kt0;
+        }
+        const int n0 = nt * BNM;
+        if (c == 0)
+            q_tile_run<NMAT, GU, KSPLIT, 8>(S, g, e, row0, row_end, n0, kt0, nk, part);
+        else if (c == 1)
+            q_tile_run<NMAT, GU, KSPLIT, 4>(S, g, e, row0, row_end, n0, kt0, nk, part);
+        else
+            q_tile_run<NMAT, GU, KSPLIT, 2>(S, g, e, row0, row_end, n0, kt0, nk, part);
+    }
+}
+
+__global__ __launch_bounds__(QT, 1) void q_gateup_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B0,
+    const uint16_t *__restrict__ B1, uint16_t *__restrict__ C, const int32_t *__restrict__ counts,
+    const int32_t *__restrict__ offsets, int E, int K, int N, int a_rows, int cu_per_xcd) {
+    const QArgs g{A, B0, B1, C, K, N, a_rows, nullptr, nullptr, 0};
+    q_body<2, false, false>(g, counts, offsets, E, 1, cu_per_xcd, nullptr);
+}
+
+__global__ __launch_bounds__(QT, 1) void q_gateup_gu_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B0,
+    const uint16_t *__restrict__ B1, uint16_t *__restrict__ C, const int32_t *__restrict__ counts,
+    const int32_t *__restrict__ offsets, int E, int K, int N, int a_rows, int cu_per_xcd,
+    float *__restrict__ gp, float *__restrict__ up) {
+    const QArgs g{A, B0, B1, C, K, N, a_rows, gp, up, 0};
+    q_body<2, true, false>(g, counts, offsets, E, 1, cu_per_xcd, nullptr);
+}
+
+__global__ __launch_bounds__(QT, 1) void q_down_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, float *__restrict__ C,
+    const int32_t *__restrict__ counts, const int32_t *__restrict__ offsets, int E, int K, int N,
+    int a_rows, int cu_per_xcd) {
+    const QArgs g{A, B, nullptr, C, K, N, a_rows, nullptr, nullptr, 0};
+    q_body<1, false, false>(g, counts, offsets, E, 1, cu_per_xcd, nullptr);
+}
+
+__global__ __launch_bounds__(QT, 1) void q_down_split_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, float *__restrict__ C,
+    const int32_t *__restrict__ counts, const int32_t *__restrict__ offsets, int E, int K, int N,
+    int a_rows, int parts, size_t part_stride, int cu_per_xcd, int *__restrict__ parts_out) {
+    const QArgs g{A, B, nullptr, C, K, N, a_rows, nullptr, nullptr, part_stride};
+    q_body<1, false, true>(g, counts, offsets, E, parts, cu_per_xcd, parts_out);
+}
+
+bool q_fits(int rows, int K, int N, int bnm) {
+    return rows > 0 && K % QBK == 0 && K / QBK >= 1 && N % bnm == 0 &&
+           (uint64_t)rows * K * 2 < ((uint64_t)1 << 32) &&
+           (uint64_t)K * N * 2 < ((uint64_t)1 << 32);
+}
+
+// CUs per XCD of the current device (the persistent grid is 8 times that).
+int q_cus_per_xcd() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return -1;
+    return std::max(1, cus / 8);
+}
+
+}  // namespace
+
+bool q_gateup_supported(int rows, int K, int N) { return q_fits(rows, K, N, QBN / 2); }
+bool q_down_supported(int rows, int K, int N) { return q_fits(rows, K, N, QBN); }
+
+hipError_t q_launch_gateup(int rows, int E, const uint16_t *xp, const int32_t *counts,
+                           const int32_t *offsets, const uint16_t *w1, const uint16_t *w3, int K,
+                           int N, uint16_t *h, float *g, float *u, hipStream_t stream) {
+    if (!q_gateup_supported(rows, K, N)) return hipErrorNotSupported;
+    const int cpx = q_cus_per_xcd();
+    if (cpx < 0) return hipErrorNotSupported;
+    if (g)
+        hipLaunchKernelGGL(q_gateup_gu_kernel, dim3(8 * cpx), dim3(QT), 0, stream, xp, w1, w3, h,
+                           counts, offsets, E, K, N, rows, cpx, g, u);
+    else
+        hipLaunchKernelGGL(q_gateup_kernel, dim3(8 * cpx), dim3(QT), 0, stream, xp, w1, w3, h,
+                           counts, offsets, E, K, N, rows, cpx);
+    return hipGetLastError();
+}
+
+hipError_t q_launch_down(int rows, int E, const uint16_t *h, const int32_t *counts,
+                         const int32_t *offsets, const uint16_t *w2, int K, int N, float *o,
+                         int parts, size_t part_stride, int /*cu_per_xcd*/, int *parts_out,
+                         hipStream_t stream) {
+    if (!q_down_supported(rows, K, N)) return hipErrorNotSupported;
+    const int cpx = q_cus_per_xcd();
+    if (cpx < 0) return hipErrorNotSupported;
+    if (parts == 1 && !parts_out) {
+        hipLaunchKernelGGL(q_down_kernel, dim3(8 * cpx), dim3(QT), 0, stream, h, w2, o, counts,
+                           offsets, E, K, N, rows, cpx);
+        return hipGetLastError();
+    }
+    if (K / QBK < QMAXSPLIT) return hipErrorNotSupported;
+    hipLaunchKernelGGL(q_down_split_kernel, dim3(8 * cpx), dim3(QT), 0, stream, h, w2, o, counts,
+                       offsets, E, K, N, rows, parts, part_stride, cpx, parts_out);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -173,6 +173,23 @@ hipError_t launch_down_split_bf16(int rows, int E, const uint16_t *h, const int3
                                   const int32_t *offsets, const uint16_t *w2, int K, int N,
                                   int parts, size_t part_stride, float *o, int *parts_out,
                                   hipStream_t stream);
+// The software-pipelined prefill GEMMs (gemm_bf16.hip), over grouped rows
+// (counts / offsets, `rows` = kT rows of xp / h).  Gate/up: h = silu(xp
+// w1[e]) * (xp w3[e]) (bf16), with g, u not NULL also g = xp w1[e], u = xp
+// w3[e] (fp32).  Down: o = h w2[e] (fp32); parts = 1 with parts_out NULL is
+// the plain product, otherwise the split form of launch_down_split_bf16
+// (cu_per_xcd: the device's CUs per XCD, for parts = 0).
+// hipErrorNotSupported unless K % 64 == 0, N a multiple of 128 (gate/up)
+// or 256 (down), rows * K * 2 < 2^32 and K * N * 2 < 2^32.
+bool q_gateup_supported(int rows, int K, int N);
+bool q_down_supported(int rows, int K, int N);
+hipError_t q_launch_gateup(int rows, int E, const uint16_t *xp, const int32_t *counts,
+                           const int32_t *offsets, const uint16_t *w1, const uint16_t *w3, int K,
+                           int N, uint16_t *h, float *g, float *u, hipStream_t stream);
+hipError_t q_launch_down(int rows, int E, const uint16_t *h, const int32_t *counts,
+                         const int32_t *offsets, const uint16_t *w2, int K, int N, float *o,
+                         int parts, size_t part_stride, int cu_per_xcd, int *parts_out,
+                         hipStream_t stream);
 // gpart: as for launch_gateup_bf16 (decode sizes; the down product's last
 // round cut the same way).
 hipError_t launch_down_bf16(const moe_shape_t &s, const uint16_t *h, const int32_t *counts,
