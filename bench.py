@@ -16,8 +16,10 @@ bound: the selected experts' w1/w3 plus xp read and h written) or FLOPs
 rocprofv3 counter summary under profiles/ (null once the kernels' source no
 longer matches the one the counters were taken on).
 
-The CPU baseline is the plain oracle (fp64, all host threads up to 16) run
-on the decode tokens for a bounded time.
+The CPU baseline is the plain oracle (fp64, on the host cores this process
+may use, up to 16: one GPU's share of the host) run on the decode tokens
+for a bounded time; the line reports the threads used and the host's core
+counts.
 
 ``block_boundary``: the same workloads through moe_block_forward (RMSNorm
 fused into the router, residual add into the combine), with the time the
@@ -65,7 +67,7 @@ if ROOT not in sys.path:
 
 METRIC = "MoE-layer tokens/s (8x7B shape, T=32 & T=4096); % of HBM / MFMA peak"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
-PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA, TFLOP/s (256 CUs x 2.4 GHz x 4096 FLOP/clk)
 PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 vector ALU, TFLOP/s
 
 
@@ -426,9 +428,12 @@ def counter_traffic(wl_name, profile=None):
 
 
 def cpu_baseline(res, budget_s):
-    """The oracle as it stands, on the decode tokens, for about budget_s."""
+    """The oracle as it stands, on the decode tokens, for about budget_s.
+    It runs on every host core this process may use, up to the 16 that
+    are this GPU's share of the host; both counts are reported."""
     import oracle
-    threads = min(16, oracle.default_threads())
+    visible = oracle.default_threads()
+    threads = min(16, visible)
     inp = res["inp"]
     log(f"cpu baseline: copying inputs to host, oracle on {threads} threads")
     host = [t.cpu() for t in (inp.x, inp.w_gate, inp.w1, inp.w3, inp.w2)]
@@ -444,8 +449,11 @@ def cpu_baseline(res, budget_s):
             break
     el = time.perf_counter() - t0
     return {"value": round(done / el, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "host_cores_visible": visible, "host_cpu_count": os.cpu_count(),
             "sample": f"{done} token-evaluations of {inp.wl.name} (its {T} tokens in chunks of "
-                      f"{chunk}, repeated) in {el:.1f} s; fp64 per-token loop"}
+                      f"{chunk}, repeated) in {el:.1f} s; fp64 per-token loop on {threads} "
+                      f"threads ({visible} host cores in this process's affinity set, "
+                      f"{os.cpu_count()} on the host; 16 is one GPU's share of the host)"}
 
 
 def copy_calibration(mib, steps):

@@ -233,9 +233,9 @@ int moe_forward_noalloc(const moe_shape_t *shape, const void *x, const void *w_g
                         int32_t *topk_idx_opt, float *topk_w_opt, void *stream);
 
 /* ---- Block boundary ----------------------------------------------------
- * The Mistral block of "Mixtral 8x7B -- The Evolving Transformer", section
- * 03 MISTRAL BLOCK, runs the layer on rms_2 of the residual stream and adds
- * its output back onto the stream.  These calls fuse both into the layer:
+ * The block of "Mixtral 8x7B -- The Evolving Transformer", section 06
+ * BLOCK, runs the layer on rms_2 (section 03 RMSNORM) of the residual
+ * stream and adds its output back onto the stream.  These calls fuse both into the layer:
  *   rstd[t]  = 1 / sqrt( (1/d) sum_j h[t,j]^2 + eps )        (fp32)
  *   xn[t,j]  = h[t,j] * rstd[t] * rms_weight[j], rounded to the layer dtype
  *   out[t]   = residual[t] + layer(xn)[t], rounded once to the layer dtype
@@ -261,9 +261,9 @@ int moe_block_forward(const moe_shape_t *shape, const void *h, const void *rms_w
                       float *topk_w_opt, void *ws, size_t ws_bytes, void *stream);
 
 /* ---- Weight-only int8 expert weights (decode) ----------------------------
- * The KerasFormers Mixtral page offers int8 weight quantization for this
- * model, and the Hugging Face page offers low-memory loading. Neither gives
- * a scheme. These calls use symmetric int8 with one fp32 scale per output
+ * The KerasFormers Mixtral page's loading example offers int8 weight
+ * quantization with low-memory loading for this model but gives no
+ * scheme. These calls use symmetric int8 with one fp32 scale per output
  * channel of each expert matrix: W[j,n] ~ s[n] q[j,n]. Decode streams the
  * selected experts' weights, so the codes halve the bytes of the step.
  * Activations, router and outputs keep the layer dtype, which must be

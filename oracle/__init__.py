@@ -316,9 +316,9 @@ def forward(x, w_gate, w1, w3, w2, threads: Optional[int] = None, return_logits=
 
 
 # ---------------------------------------------------------------------------
-# Block boundary ("Mixtral 8x7B -- The Evolving Transformer", section 03
-# MISTRAL BLOCK): the layer runs on rms_2 of the residual stream h and its
-# output is added back onto the stream.
+# Block boundary ("Mixtral 8x7B -- The Evolving Transformer", section 06
+# BLOCK, with the norm of section 03 RMSNORM): the layer runs on rms_2 of
+# the residual stream h and its output is added back onto the stream.
 
 def rmsnorm(h, g, eps: float, threads: Optional[int] = None):
     """xn = h * rstd * g, rounded once to h's dtype (RNE), with

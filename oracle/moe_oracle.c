@@ -40,9 +40,9 @@
  * Threads split the tokens; each token's arithmetic is the same sequential
  * loop whichever thread runs it.
  *
- * Block boundary (the same page, section 03 MISTRAL BLOCK and the Block
- * module: the layer's input is rms_2 of the residual stream, and the
- * layer's output is added back onto it):
+ * Block boundary (the same page, section 06 BLOCK, with the norm of
+ * section 03 RMSNORM: the layer's input is rms_2 of the residual stream,
+ * and the layer's output is added back onto it):
  *
  *   r[t]    = 1 / sqrt( (1/d) sum_j h[t,j]^2 + eps )
  *   xn[t,j] = h[t,j] * r[t] * g[j], rounded once to the layer dtype
@@ -598,7 +598,7 @@ out:
  * Weight-only int8 expert weights.
  *
  * The pages name weight-only int8 loading for this model (the KerasFormers
- * Mixtral page's quantization option; the Hugging Face page's low-memory
+ * Mixtral page's loading example: quantization="int8" with low-memory
  * loading) but give no scheme.  The plainest one is used: symmetric, one
  * scale per output channel of each expert matrix.  For a matrix W [K, N]
  * (K = input, N = output channel) and each column n:

@@ -17,7 +17,7 @@ namespace {
 
 // With res (the residual stream, same dtype as y), y = res + combine: the
 // block's residual add ("Mixtral 8x7B -- The Evolving Transformer", section
-// 03 MISTRAL BLOCK), still rounded once.  y may be res itself: each element
+// 06 BLOCK), still rounded once.  y may be res itself: each element
 // is read before the same thread writes it.  K (slots per token) is a
 // template parameter so that the slot loops are straight-line code.
 // With parts > 1, o holds that many partial sums (K slices of the down

@@ -87,17 +87,8 @@ constexpr int PBM = 256, PBN = 256, PBK = 64;
 constexpr int PLD = PBK + 8;  // LDS row pitch in bf16 (144 bytes): consecutive rows start
                               // 16 bytes apart modulo 128, so 8-lane groups of 16-byte
                               // reads and writes fall on distinct banks
-#ifndef MOE_PREFILL_PGM
-#define MOE_PREFILL_PGM 4
-#endif
-constexpr int PGM = MOE_PREFILL_PGM;   // row tiles per scheduling group (see prefill_tile)
-#ifndef MOE_PREFILL_WN
-#define MOE_PREFILL_WN 4
-#endif
-#ifndef MOE_PREFILL_WM
-#define MOE_PREFILL_WM 2
-#endif
-constexpr int PWM = MOE_PREFILL_WM, PWN = MOE_PREFILL_WN;
+constexpr int PGM = 4;                 // row tiles per scheduling group (see prefill_tile)
+constexpr int PWM = 2, PWN = 4;        // wavefront rows x columns
 
 // Work decomposition shared by the prefill kernels.  Row tiles of PBM rows
 // are numbered expert after expert; the flat tile list orders them in
@@ -290,14 +281,8 @@ __global__ __launch_bounds__(PWM * PWN * 64, 1) void prefill_gemm_kernel(
 
 constexpr int DBK = 64;                       // K per stage: every A row segment is
                                               // one full 128-byte line
-#ifndef MOE_DMA_ASTAGES
-#define MOE_DMA_ASTAGES 2
-#endif
-#ifndef MOE_DMA_BSTAGES
-#define MOE_DMA_BSTAGES 3
-#endif
-constexpr int DAS = MOE_DMA_ASTAGES;          // A ring depth
-constexpr int DBS = MOE_DMA_BSTAGES;          // B ring depth
+constexpr int DAS = 2;                        // A ring depth
+constexpr int DBS = 3;                        // B ring depth
 static_assert(DAS >= 2 && DBS >= 2 && DAS + DBS <= 5, "five 32 KiB slots fit in LDS");
 constexpr int DA_BYTES = PBM * DBK * 2;       // 32 KiB
 constexpr int DB_BYTES = DBK * PBN * 2;       // 32 KiB
@@ -574,10 +559,7 @@ __device__ __forceinline__ void prefill_dma_body(
     // read first (in step order, so the waits before each step's MFMAs are
     // partial), and the scheduler interleaves the reads of one half with
     // the MFMAs of the other (iglp strategy 0).
-#ifndef MOE_DMA_KH
-#define MOE_DMA_KH 1
-#endif
-    constexpr int KH = MOE_DMA_KH;
+    constexpr int KH = 1;
     static_assert(KS % KH == 0, "whole halves");
     auto compute = [&](const uint8_t *sa, const uint8_t *sb) MOE_INLINE {
         __builtin_amdgcn_iglp_opt(0);

@@ -1,6 +1,6 @@
 // Weight-only int8 expert weights for the decode path.  The KerasFormers
-// Mixtral page offers int8 weight quantization for this model, and the
-// Hugging Face page low-memory loading; neither gives a scheme, so the
+// Mixtral page's loading example offers int8 weight quantization with
+// low-memory loading for this model but gives no scheme, so the
 // plainest is used: symmetric int8 with one fp32 scale per output channel
 // of each expert matrix, W[j, n] ~ s[n] * q[j, n].
 //

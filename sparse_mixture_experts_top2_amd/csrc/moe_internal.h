@@ -21,10 +21,7 @@ constexpr int kDecodeMaxT = 32;
 // K slices of the int8-weight down projection at decode sizes; the combine
 // adds the slices in order.  The workspace's o region holds this many
 // copies of o when T <= kDecodeMaxT (kMaxDownSplit copies above it).
-#ifndef MOE_DOWN_PARTS
-#define MOE_DOWN_PARTS 4
-#endif
-constexpr int kDownParts = MOE_DOWN_PARTS;
+constexpr int kDownParts = 4;
 // Most K parts the prefill down product is cut into (see launch_down_split_bf16).
 constexpr int kMaxDownSplit = 2;
 // Decode gate/up: most (expert, 128-column) units cut in K halves to fill the

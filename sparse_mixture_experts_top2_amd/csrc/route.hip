@@ -180,7 +180,8 @@ __device__ __forceinline__ void finish_token(Row &l, int E, int k, int page, flo
 // wavefronts in LDS, in a fixed order.
 //
 // NORM: the router input is the RMSNorm of the rows ("Mixtral 8x7B -- The
-// Evolving Transformer", section 03 MISTRAL BLOCK: rms_2 before the MoE).
+// Evolving Transformer", section 03 RMSNORM; section 06 BLOCK applies
+// rms_2 before the MoE).
 // A first pass sums each row's squares (fixed-order reduction as above),
 // rstd = 1/sqrt(sum/d + eps); the second pass re-reads the row (from L2),
 // forms xn = round(x * rstd * g) in the element type, writes it to xn_out

@@ -277,7 +277,8 @@ def _bf16(vals):
 
 def pin_rmsnorm_closed_forms():
     """Hand-derived rows ("Mixtral 8x7B -- The Evolving Transformer",
-    section 03: rms_2 before the MoE).  A row of 3s with eps = 7 has mean
+    section 03 RMSNORM for the norm, section 06 BLOCK: rms_2 before the
+    MoE).  A row of 3s with eps = 7 has mean
     square 9, so rstd = 1/sqrt(16) = 1/4 and xn = 0.75 * g, exact in bf16.
     The row (3, 4, 0, 0) has mean square 25/4, so with eps = 0 rstd = 2/5
     and xn = (1.2, 1.6, 0, 0) * g, rounded once to bf16.  A zero row gives
