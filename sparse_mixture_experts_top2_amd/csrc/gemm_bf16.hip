@@ -162,14 +162,27 @@ __device__ __forceinline__ void q_group_pos(int idx, int m_c, int n_tiles, int &
 }
 
 // Estimated time of the schedule, in full-tile units, for tiles cut in S
-// parts along K: the busiest workgroup of an XCD carries about
-// max(ceil(full / cpx), all / cpx + one tile) plus a fifth of a tile per
-// extra part (writing and re-reading the fp32 partial sums).
+// parts along K: the load of workgroup 0 of the busiest XCD (it takes
+// entries 0, cpx, 2 cpx, ... of its XCD's list, the most and the costliest
+// of any workgroup there), each entry costing its class's share over S
+// plus a fixed per-tile overhead, and a tenth of a tile per extra part for
+// writing and re-reading the fp32 partial sums.
 __device__ __forceinline__ float q_makespan(const int (&m)[3], int n_cols, int S, int cpx) {
-    const float n0 = (float)m[0] * n_cols * S / 8.0f;
-    const float all = (QCOST[0] * m[0] + QCOST[1] * m[1] + QCOST[2] * m[2]) * n_cols * S / 8.0f;
-    const float a = ceilf(n0 / cpx), b = all / cpx + 1.0f;
-    return (a > b ? a : b) / S + 0.2f * (S - 1);
+    float worst = 0.0f;
+    for (int x = 0; x < 8; ++x) {
+        int before = 0, k_done = 0;
+        float load = 0.0f;
+        for (int c = 0; c < 3; ++c) {
+            const int64_t T = (int64_t)m[c] * n_cols * S;
+            const int len = (int)(T * (x + 1) / 8 - T * x / 8);
+            before += len;
+            const int k_end = (before + cpx - 1) / cpx;   // entries k cpx < before
+            load += (float)(k_end - k_done) * (QCOST[c] / S + 0.03f);
+            k_done = k_end;
+        }
+        worst = fmaxf(worst, load);
+    }
+    return worst + 0.1f * (S - 1);
 }
 
 // The GEMM body.
@@ -410,6 +423,9 @@ __device__ __forceinline__ void q_tile_run(const QSlots &S, const QArgs &g, int 
         // 4-byte column pairs: lanes l and l ^ 1 hold neighbouring columns
         // of the same rows and swap one value (a DPP quad permutation), so
         // that the even lane stores row q and the odd lane row q + 1.
+        // silu(g) = g / (1 + 2^(-g log2 e)) with the hardware exp2 and
+        // reciprocal; each lane's two rows are rounded to bf16 (nearest
+        // even) by one v_cvt_pk_bf16_f32 before the swap.
         uint16_t *H = static_cast<uint16_t *>(g.C);
         const int odd = lane & 1;
         const int col = n0 + wave * 32 + (lane & 31) - odd;
@@ -417,14 +433,20 @@ __device__ __forceinline__ void q_tile_run(const QSlots &S, const QArgs &g, int 
         for (int i = 0; i < MBE; ++i)
 #pragma unroll
             for (int q = 0; q < 16; q += 2) {
+                typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+                typedef float f32x2_t __attribute__((ext_vector_type(2)));
                 auto hval = [&](int qq) Q_INLINE {
                     const float gv = acc[i][0][qq], uv = acc[i][1][qq];
-                    return f32_to_bf16(gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv);
+                    const float den = 1.0f + __builtin_amdgcn_exp2f(gv * -1.44269504088896341f);
+                    return gv * __builtin_amdgcn_rcpf(den) * uv;
                 };
-                const uint32_t h0 = hval(q), h1 = hval(q + 1);
-                const uint32_t x = odd ? h0 : h1;
+                const float h0 = hval(q), h1 = hval(q + 1);
+                // hp = h(row q) | h(row q + 1) << 16 of this lane's column
+                const uint32_t hp =
+                    __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{h0, h1}, bf16x2_t));
+                const uint32_t x = odd ? hp : (hp >> 16);
                 const uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);
-                const uint32_t packed = odd ? (y | (h1 << 16)) : (h0 | (y << 16));
+                const uint32_t packed = odd ? ((y & 0xffffu) | (hp & 0xffff0000u)) : ((hp & 0xffffu) | (y << 16));
                 const int row = row0 + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3) + odd;
                 if (row < row_end)
                     __builtin_nontemporal_store(packed,
