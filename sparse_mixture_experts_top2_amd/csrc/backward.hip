@@ -702,7 +702,36 @@ hipError_t run_backward_t(const moe_shape_t &s, const T *x, const T *wg, const T
                            dx, dxp_parts, pstride);
         e = hipGetLastError();
     }
-    // weight gradients: dW1[e] = xp_e^T dG_e, dW3[e] = xp_e^T dU_e, dW2[e] = h_e^T dO_e
+    // weight gradients: dW1[e] = xp_e^T dG_e, dW3[e] = xp_e^T dU_e, dW2[e] = h_e^T dO_e.
+    // bf16 layers whose sizes fit: K-contiguous padded copies of the five
+    // operands, then the pipelined GEMMs reduce over each expert's rows
+    // (dW1 and dW3 in one pass sharing the xp tiles).
+    if constexpr (sizeof(T) == 2) {
+        if (L.ldk > 0 && R > 0) {
+            const int ldk = L.ldk;
+            uint16_t *xpT = reinterpret_cast<uint16_t *>(base + L.xpT);
+            uint16_t *hT = reinterpret_cast<uint16_t *>(base + L.hT);
+            uint16_t *dOT = reinterpret_cast<uint16_t *>(base + L.dOT);
+            uint16_t *dGT = reinterpret_cast<uint16_t *>(base + L.dGT);
+            uint16_t *dUT = reinterpret_cast<uint16_t *>(base + L.dUT);
+            auto tp = [&](const T *src, int C, uint16_t *dst) {
+                if (e == hipSuccess)
+                    e = q_launch_transpose_pad(reinterpret_cast<const uint16_t *>(src), R, C,
+                                               counts, offsets, E, dst, ldk, str);
+            };
+            tp(xp, d, xpT);
+            tp(dG, f, dGT);
+            tp(dU, f, dUT);
+            tp(H, f, hT);
+            tp(dO, d, dOT);
+            if (e == hipSuccess)
+                e = q_launch_dw(2, xpT, dGT, dUT, dw1, dw3, counts, E, d, f, ldk, str);
+            if (e == hipSuccess)
+                e = q_launch_dw(1, hT, dOT, nullptr, dw2, nullptr, counts, E, f, d, ldk, str);
+            if (e == hipSuccess) e = launch_dwg<T>(x, dl, Tn, d, E, dwgp, dwg, str);
+            return e;
+        }
+    }
     a = GemmArgs{};
     a.counts = counts; a.offsets = offsets; a.E = E;
     a.A = xp; a.lda = d; a.B = dG; a.ldb = f; a.C = dw1; a.ldc = f;
@@ -745,6 +774,17 @@ BackwardLayout plan_backward(const moe_shape_t &s) {
     L.dl = off;      off += a256(T * E * 4);
     L.dwgp = off;    off += a256((size_t)DWG_PARTS * d * 4);   // chunks x E <= DWG_PARTS
     L.nparts = off;  off += a256(2 * sizeof(int32_t));
+    L.ldk = 0;
+    L.xpT = L.hT = L.dOT = L.dGT = L.dUT = off;
+    if (s.dtype == MOE_BF16 && q_dw_supported((int)R, (int)E, (int)d, (int)f)) {
+        L.ldk = q_dw_ldk((int)R, (int)E);
+        const size_t ldk = (size_t)L.ldk;
+        L.xpT = off;     off += a256(d * ldk * 2);
+        L.hT = off;      off += a256(f * ldk * 2);
+        L.dOT = off;     off += a256(d * ldk * 2);
+        L.dGT = off;     off += a256(f * ldk * 2);
+        L.dUT = off;     off += a256(f * ldk * 2);
+    }
     L.total = off;
     return L;
 }

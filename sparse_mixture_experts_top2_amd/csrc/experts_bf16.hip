@@ -1137,6 +1137,11 @@ hipError_t launch_bt_store_split_bf16(int rows, int E, const uint16_t *A, const 
                                       const int32_t *counts, const int32_t *offsets, float *C,
                                       size_t part_stride, int *parts_out, hipStream_t stream) {
     if (!bt_shape_ok(rows, K1, N) || !parts_out) return hipErrorNotSupported;
+    {
+        const hipError_t qe = q_launch_bt_store_split(rows, E, A, B, A2, B2, K1, N, counts,
+                                                      offsets, C, part_stride, parts_out, stream);
+        if (qe != hipErrorNotSupported) return qe;
+    }
     const int cpx = cus_per_xcd();
     if (cpx < 0) return hipErrorNotSupported;
     const int grid = prefill_grid(rows, E, (N / PBN) * kMaxDownSplit);
@@ -1151,6 +1156,11 @@ hipError_t launch_bt_dswiglu_bf16(int rows, int E, const uint16_t *A, const uint
                                   const float *g, const float *u, uint16_t *dg, uint16_t *du,
                                   hipStream_t stream) {
     if (!bt_shape_ok(rows, K1, N)) return hipErrorNotSupported;
+    {
+        const hipError_t qe =
+            q_launch_bt_dswiglu(rows, E, A, B, K1, N, counts, offsets, g, u, dg, du, stream);
+        if (qe != hipErrorNotSupported) return qe;
+    }
     const int grid = prefill_grid(rows, E, N / PBN);
     hipLaunchKernelGGL(prefill_dma_bt_dswiglu_kernel, dim3(grid), dim3(PWM * PWN * 64), 0,
                        stream, A, B, counts, offsets, E, K1, N, rows, g, u, dg, du);

@@ -44,8 +44,14 @@ Layout plan_workspace(const moe_shape_t &s);
 // input gradients), dO, dG, dU (layer dtype) and the router gradient dl.
 // o holds kMaxDownSplit partial sums (the split products' K parts); nparts
 // two int32, the part counts the o and dXp products chose.
+// At bf16 sizes the weight-gradient GEMMs take, xpT, hT, dOT, dGT and dUT
+// hold K-contiguous copies of xp, h, dO, dG and dU whose columns are the
+// grouped rows padded per expert to a multiple of 64 (q_dw_ldk columns);
+// otherwise those regions are empty.
 struct BackwardLayout {
-    size_t idx, w, counts, offsets, pos, xp, g, u, h, o, dout, dg, du, dl, dwgp, nparts, total;
+    size_t idx, w, counts, offsets, pos, xp, g, u, h, o, dout, dg, du, dl, dwgp, nparts;
+    size_t xpT, hT, dOT, dGT, dUT, total;
+    int ldk;   // row length of the K-contiguous copies (0: not used)
 };
 BackwardLayout plan_backward(const moe_shape_t &s);
 hipError_t launch_backward(const moe_shape_t &s, const void *x, const void *wg, const void *w1,
@@ -170,7 +176,7 @@ hipError_t launch_down_split_bf16(int rows, int E, const uint16_t *h, const int3
                                   const int32_t *offsets, const uint16_t *w2, int K, int N,
                                   int parts, size_t part_stride, float *o, int *parts_out,
                                   hipStream_t stream);
-// The software-pipelined prefill GEMMs (gemm_bf16.hip), over grouped rows
+// The software-pipelined prefill GEMMs (gemm_bf16.h and its gemm_*.hip units), over grouped rows
 // (counts / offsets, `rows` = kT rows of xp / h).  Gate/up: h = silu(xp
 // w1[e]) * (xp w3[e]) (bf16), with g, u not NULL also g = xp w1[e], u = xp
 // w3[e] (fp32).  Down: o = h w2[e] (fp32); parts = 1 with parts_out NULL is
@@ -187,6 +193,34 @@ hipError_t q_launch_down(int rows, int E, const uint16_t *h, const int32_t *coun
                          const int32_t *offsets, const uint16_t *w2, int K, int N, float *o,
                          int parts, size_t part_stride, int cu_per_xcd, int *parts_out,
                          hipStream_t stream);
+// The backward's products on the same pipeline.  bt_dswiglu: da = dO
+// w2[e]^T (w2[e] [N, K1] read along K1), turned into dg, du (bf16) with g,
+// u (fp32), all [rows, N].  bt_store_split: C = A B[e]^T + A2 B2[e]^T
+// (B[e], B2[e] [N, K1]), the 2 K1 reduction cut into parts chosen from
+// the counts (count to *parts_out, part p at C + p * part_stride).
+// hipErrorNotSupported unless K1 % 64 == 0, N % 256 == 0 and the operands
+// fit 32-bit offsets.
+hipError_t q_launch_bt_dswiglu(int rows, int E, const uint16_t *dO, const uint16_t *w2, int K1,
+                               int N, const int32_t *counts, const int32_t *offsets,
+                               const float *g, const float *u, uint16_t *dg, uint16_t *du,
+                               hipStream_t stream);
+hipError_t q_launch_bt_store_split(int rows, int E, const uint16_t *A, const uint16_t *B,
+                                   const uint16_t *A2, const uint16_t *B2, int K1, int N,
+                                   const int32_t *counts, const int32_t *offsets, float *C,
+                                   size_t part_stride, int *parts_out, hipStream_t stream);
+// Weight gradients from K-contiguous copies whose columns hold each
+// expert's rows padded to a multiple of 64 with zeros (row length
+// q_dw_ldk).  transpose_pad: dst [C, ldk] from src [rows, C] (grouped
+// rows).  dw (nmat = 2): C[e] = At_e^T B0t_e, C2[e] = At_e^T B1t_e; (nmat =
+// 1): C[e] = At_e^T B0t_e; At [M, ldk], B [N, ldk], C [E, M, N] fp32.
+int q_dw_ldk(int rows, int E);
+bool q_dw_supported(int rows, int E, int d, int f);
+hipError_t q_launch_transpose_pad(const uint16_t *src, int rows, int C, const int32_t *counts,
+                                  const int32_t *offsets, int E, uint16_t *dst, int ldk,
+                                  hipStream_t stream);
+hipError_t q_launch_dw(int nmat, const uint16_t *At, const uint16_t *B0t, const uint16_t *B1t,
+                       float *C, float *C2, const int32_t *counts, int E, int M, int N, int ldk,
+                       hipStream_t stream);
 // gpart: as for launch_gateup_bf16 (decode sizes; the down product's last
 // round cut the same way).
 hipError_t launch_down_bf16(const moe_shape_t &s, const uint16_t *h, const int32_t *counts,
