@@ -88,9 +88,26 @@ def _bind(path: str):
     return lib
 
 
+def build_sanitized(out_path: str, cc: str) -> str:
+    """The same source built with AddressSanitizer and UndefinedBehaviorSanitizer
+    (``cc``: a clang whose runtime the test process preloads), for the
+    sanitizer run of the CPU tests; loaded in place of the plain build when
+    the environment names it in MOE_ORACLE_LIB."""
+    cmd = [cc, "-O1", "-g", "-fno-omit-frame-pointer", "-std=c11", "-fPIC", "-shared",
+           "-pthread", "-ffp-contract=off", "-fno-fast-math",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-shared-libasan",
+           _SRC, "-lm", "-o", out_path]
+    subprocess.run(cmd, check=True)
+    return out_path
+
+
 def _load():
     global _lib
     if _lib is not None:
+        return _lib
+    override = os.environ.get("MOE_ORACLE_LIB")
+    if override:
+        _lib = _bind(override)
         return _lib
     if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
         build()

@@ -19,7 +19,9 @@ from typing import Optional, Tuple
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmoe.so")
+# MOE_LIB names another build of the same sources (the sanitizer build of
+# the host code, for the CPU tests); there is no other library and no fallback.
+LIB_PATH = os.environ.get("MOE_LIB") or os.path.join(_PKG, "libmoe.so")
 
 MOE_F32, MOE_BF16 = 0, 1
 MOE_OK = 0
