@@ -169,14 +169,15 @@ hipError_t run_layer(const moe_shape_t &s, const void *x, const void *g, float e
     if (s.dtype == MOE_BF16 && s.T <= kDecodeMaxT) {
         // Few tokens: the gate/up kernel gathers its rows straight from the
         // layer input through the row -> token table, so no xp copy is made.
+        // The ranking runs inside the gate/up kernel (no launch of its own).
         int32_t *src = reinterpret_cast<int32_t *>(base + L.src);
-        if (e == hipSuccess) e = launch_rank(s, idx, counts, offsets, pos, src, str);
+        const DecodeRank rk{idx, routed_rows(s), s.top_k, counts, offsets, pos, src};
         if (e == hipSuccess)
             e = launch_gateup_bf16(s, static_cast<const uint16_t *>(xin), counts, offsets,
                                    static_cast<const uint16_t *>(w1),
                                    static_cast<const uint16_t *>(w3),
                                    static_cast<uint16_t *>(h), str, src,
-                                   reinterpret_cast<float *>(base + L.gpart));
+                                   reinterpret_cast<float *>(base + L.gpart), &rk);
     } else {
         if (e == hipSuccess) e = launch_dispatch(s, xin, idx, counts, offsets, pos, xp, str);
         if (e == hipSuccess) e = launch_gateup(s, xp, counts, offsets, w1, w3, h, str);
@@ -613,13 +614,14 @@ int moe_forward_w8(const moe_shape_t *s, const void *x, const void *w_gate, cons
     uint16_t *h = reinterpret_cast<uint16_t *>(base + L.h);
     float *o = reinterpret_cast<float *>(base + L.o);
     const hipStream_t str = (hipStream_t)stream;
-    // Route, rank with the row -> token table, gate/up gathering its rows
-    // from x, down in kDownParts K slices, combine adding the slices.
+    // Route; gate/up ranks the picks itself (with the row -> token table)
+    // and gathers its rows from x; down in kDownParts K slices; the combine
+    // adds the slices.
     hipError_t e = launch_route(*s, x, w_gate, idx, w, str);
-    if (e == hipSuccess) e = launch_rank(*s, idx, counts, offsets, pos, src, str);
+    const DecodeRank rk{idx, routed_rows(*s), s->top_k, counts, offsets, pos, src};
     if (e == hipSuccess)
         e = launch_gateup_w8(*s, static_cast<const uint16_t *>(x), counts, offsets, q1, s1, q3,
-                             s3, h, str, src);
+                             s3, h, str, src, &rk);
     if (e == hipSuccess) e = launch_down_w8(*s, h, counts, offsets, q2, s2, o, kDownParts, str);
     if (e == hipSuccess) e = launch_combine(*s, o, pos, w, y, str, nullptr, kDownParts);
     return hip_status(e);

@@ -838,14 +838,15 @@ constexpr int DTAIL_ROWS = 32;   // rows of a part slot (an expert's rows at dec
 __device__ __forceinline__ size_t decode_tail_slot(int j, int half, int m) {
     return ((size_t)(j * 2 + half) * 2 + m) * DTAIL_ROWS * DCOLS;
 }
-template <int MB, int NMAT, bool TAIL = false>
+template <int MB, int NMAT, bool TAIL = false, bool RANK = false>
 __global__ __launch_bounds__(DWAVES * 64) void decode_gemm_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B0,
     const uint16_t *__restrict__ B1, void *__restrict__ C, const int32_t *__restrict__ counts,
     const int32_t *__restrict__ offsets, int K, int N, int a_rows,
     const int32_t *__restrict__ src, float *__restrict__ part = nullptr, int n_full = 0,
-    int nb_cols = 0) {
+    int nb_cols = 0, DecodeRank rk = DecodeRank{}, int n_exp = 0) {
     static_assert(!TAIL || MB * 16 <= DTAIL_ROWS, "a part slot holds an expert's rows");
+    static_assert(kDecodeMaxT * kMaxTopK <= 128 && kMaxExperts <= 64, "one wavefront ranks");
     int e = blockIdx.y, cblk = blockIdx.x, half = -1, slot = 0;
     if constexpr (TAIL) {
         int unit = blockIdx.x;
@@ -857,11 +858,22 @@ __global__ __launch_bounds__(DWAVES * 64) void decode_gemm_kernel(
         e = unit / nb_cols;
         cblk = unit - e * nb_cols;
     }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __shared__ int32_t s_counts[RANK ? kMaxExperts : 1], s_offsets[RANK ? kMaxExperts + 1 : 1];
+    __shared__ int32_t s_src[RANK ? kDecodeMaxT * kMaxTopK : 1];
+    if constexpr (RANK) {
+        if (wave == 0)
+            decode_rank_wave(rk, n_exp, lane, s_counts, s_offsets, s_src,
+                             blockIdx.x == 0 && blockIdx.y == 0);
+        __syncthreads();
+        counts = s_counts;
+        offsets = s_offsets;
+        src = s_src;
+    }
     const int Me = counts[e];
     if (Me == 0) return;  // an expert no token chose: its weights are never read
     const int r0 = offsets[e];
     const int nmb = min(MB, (Me + 15) >> 4);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int kg = lane >> 4, nb = lane & 15;
     const int col = cblk * DCOLS + nb * 8;
     const bool col_ok = col < N;
@@ -1028,27 +1040,28 @@ int decode_tail_full_units(int N, int E) {
     return units - rem;
 }
 
-template <int MB>
+template <int MB, bool RANK>
 hipError_t launch_decode_gateup(const moe_shape_t &s, const uint16_t *xp,
                                 const int32_t *counts, const int32_t *offsets,
                                 const uint16_t *w1, const uint16_t *w3, uint16_t *h,
-                                hipStream_t stream, const int32_t *src, float *gpart) {
+                                hipStream_t stream, const int32_t *src, float *gpart,
+                                const DecodeRank &rk) {
     const int d = s.d_model, f = s.d_ff, E = s.n_experts, rows = routed_rows(s);
     const int nb_cols = (f + DCOLS - 1) / DCOLS;
     const int n_full = gpart ? decode_tail_full_units(f, E) : -1;
     if (n_full >= 0) {
         const int n_cut = nb_cols * E - n_full;
-        hipLaunchKernelGGL((decode_gemm_kernel<MB, 2, true>), dim3(n_full + 2 * n_cut),
+        hipLaunchKernelGGL((decode_gemm_kernel<MB, 2, true, RANK>), dim3(n_full + 2 * n_cut),
                            dim3(DWAVES * 64), 0, stream, xp, w1, w3, h, counts, offsets, d, f,
-                           rows, src, gpart, n_full, nb_cols);
+                           rows, src, gpart, n_full, nb_cols, rk, E);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(decode_tail_finish_kernel<2>, dim3(n_cut), dim3(256), 0, stream,
                            gpart, counts, offsets, n_full, nb_cols, f, h);
     } else {
-        hipLaunchKernelGGL((decode_gemm_kernel<MB, 2>), dim3(nb_cols, E), dim3(DWAVES * 64), 0,
-                           stream, xp, w1, w3, h, counts, offsets, d, f, rows, src, nullptr, 0,
-                           0);
+        hipLaunchKernelGGL((decode_gemm_kernel<MB, 2, false, RANK>), dim3(nb_cols, E),
+                           dim3(DWAVES * 64), 0, stream, xp, w1, w3, h, counts, offsets, d, f,
+                           rows, src, nullptr, 0, 0, rk, E);
     }
     return hipGetLastError();
 }
@@ -1083,12 +1096,22 @@ hipError_t launch_decode_down(const moe_shape_t &s, const uint16_t *h, const int
 hipError_t launch_gateup_bf16(const moe_shape_t &s, const uint16_t *xp, const int32_t *counts,
                               const int32_t *offsets, const uint16_t *w1, const uint16_t *w3,
                               uint16_t *h, hipStream_t stream, const int32_t *src,
-                              float *gpart) {
+                              float *gpart, const DecodeRank *rank) {
     const int d = s.d_model, f = s.d_ff, E = s.n_experts, rows = routed_rows(s);
+    if (rank && (s.T > kDecodeMaxT || !src || s.n_experts > kMaxExperts ||
+                 rank->n_assign > kDecodeMaxT * kMaxTopK))
+        return hipErrorInvalidValue;
+    const DecodeRank rk = rank ? *rank : DecodeRank{};
     if (s.T <= 16) {
-        return launch_decode_gateup<1>(s, xp, counts, offsets, w1, w3, h, stream, src, gpart);
+        return rank ? launch_decode_gateup<1, true>(s, xp, counts, offsets, w1, w3, h, stream,
+                                                    src, gpart, rk)
+                    : launch_decode_gateup<1, false>(s, xp, counts, offsets, w1, w3, h, stream,
+                                                     src, gpart, rk);
     } else if (s.T <= kDecodeMaxT) {
-        return launch_decode_gateup<2>(s, xp, counts, offsets, w1, w3, h, stream, src, gpart);
+        return rank ? launch_decode_gateup<2, true>(s, xp, counts, offsets, w1, w3, h, stream,
+                                                    src, gpart, rk)
+                    : launch_decode_gateup<2, false>(s, xp, counts, offsets, w1, w3, h, stream,
+                                                     src, gpart, rk);
     } else if (src) {
         return hipErrorInvalidValue;   // the gather is only built into the decode kernels
     } else {

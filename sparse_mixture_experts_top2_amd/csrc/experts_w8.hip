@@ -148,20 +148,34 @@ __global__ __launch_bounds__(256) void quantize_int8_kernel(const T *__restrict_
 // the accumulators holds weight columns 8 * (l % 16) + c.  (Measured: one
 // wavefront per SIMD streaming whole 256-byte segments hides less latency,
 // and 128-column workgroups reading 128-byte segments stream slower.)
-template <int MB, int NMAT>
+// RANK: counts, offsets and src come from rk.idx, ranked by the first
+// wavefront of every workgroup (DecodeRank).
+template <int MB, int NMAT, bool RANK = false>
 __global__ __launch_bounds__(W8_WAVES * 64) void decode_w8_kernel(
     const uint16_t *__restrict__ A, const int8_t *__restrict__ Q0, const float *__restrict__ S0,
     const int8_t *__restrict__ Q1, const float *__restrict__ S1, void *__restrict__ C,
     const int32_t *__restrict__ counts, const int32_t *__restrict__ offsets, int K, int N,
-    int a_rows, const int32_t *__restrict__ src, size_t part_stride) {
+    int a_rows, const int32_t *__restrict__ src, size_t part_stride,
+    DecodeRank rk = DecodeRank{}, int n_exp = 0) {
     const int e = blockIdx.y;
+    // The wavefront index is uniform: read it into a scalar so that the K
+    // loop bounds are scalar and the loop is not taken for a divergent one.
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    __shared__ int32_t s_counts[RANK ? kMaxExperts : 1], s_offsets[RANK ? kMaxExperts + 1 : 1];
+    __shared__ int32_t s_src[RANK ? kDecodeMaxT * kMaxTopK : 1];
+    if constexpr (RANK) {
+        if (wave == 0)
+            decode_rank_wave(rk, n_exp, lane, s_counts, s_offsets, s_src,
+                             blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0);
+        __syncthreads();
+        counts = s_counts;
+        offsets = s_offsets;
+        src = s_src;
+    }
     const int Me = counts[e];
     if (Me == 0) return;  // an expert no token chose: its codes are never read
     const int r0 = offsets[e];
     const int nmb = min(MB, (Me + 15) >> 4);
-    // The wavefront index is uniform: read it into a scalar so that the K
-    // loop bounds are scalar and the loop is not taken for a divergent one.
-    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int half = wave % W8_HALVES, kp = wave / W8_HALVES;
     const int kg = lane >> 4, nb = lane & 15;
     const int col = blockIdx.x * W8_COLS + half * W8_HALF + nb * 8;
@@ -342,17 +356,24 @@ hipError_t launch_quantize_int8(int n_mat, int K, int N, int dtype, const void *
 hipError_t launch_gateup_w8(const moe_shape_t &s, const uint16_t *xp, const int32_t *counts,
                             const int32_t *offsets, const int8_t *q1, const float *s1,
                             const int8_t *q3, const float *s3, uint16_t *h, hipStream_t stream,
-                            const int32_t *src) {
+                            const int32_t *src, const DecodeRank *rank) {
     const int d = s.d_model, f = s.d_ff, E = s.n_experts, rows = routed_rows(s);
     const dim3 grid((f + W8_COLS - 1) / W8_COLS, E, 1), block(W8_WAVES * 64);
-    if (s.T <= 16)
-        hipLaunchKernelGGL((decode_w8_kernel<1, 2>), grid, block, 0, stream, xp, q1, s1, q3, s3,
-                           h, counts, offsets, d, f, rows, src, (size_t)0);
-    else if (s.T <= kDecodeMaxT)
-        hipLaunchKernelGGL((decode_w8_kernel<2, 2>), grid, block, 0, stream, xp, q1, s1, q3, s3,
-                           h, counts, offsets, d, f, rows, src, (size_t)0);
-    else
+    if (s.T > kDecodeMaxT || (rank && (!src || E > kMaxExperts)))
         return hipErrorInvalidValue;
+    const DecodeRank rk = rank ? *rank : DecodeRank{};
+    if (s.T <= 16 && rank)
+        hipLaunchKernelGGL((decode_w8_kernel<1, 2, true>), grid, block, 0, stream, xp, q1, s1, q3,
+                           s3, h, counts, offsets, d, f, rows, src, (size_t)0, rk, E);
+    else if (s.T <= 16)
+        hipLaunchKernelGGL((decode_w8_kernel<1, 2>), grid, block, 0, stream, xp, q1, s1, q3, s3,
+                           h, counts, offsets, d, f, rows, src, (size_t)0, rk, E);
+    else if (rank)
+        hipLaunchKernelGGL((decode_w8_kernel<2, 2, true>), grid, block, 0, stream, xp, q1, s1, q3,
+                           s3, h, counts, offsets, d, f, rows, src, (size_t)0, rk, E);
+    else
+        hipLaunchKernelGGL((decode_w8_kernel<2, 2>), grid, block, 0, stream, xp, q1, s1, q3, s3,
+                           h, counts, offsets, d, f, rows, src, (size_t)0, rk, E);
     return hipGetLastError();
 }
 
@@ -364,10 +385,12 @@ hipError_t launch_down_w8(const moe_shape_t &s, const uint16_t *h, const int32_t
     const dim3 grid((d + W8_COLS - 1) / W8_COLS, E, parts), block(W8_WAVES * 64);
     if (s.T <= 16)
         hipLaunchKernelGGL((decode_w8_kernel<1, 1>), grid, block, 0, stream, h, q2, s2, nullptr,
-                           nullptr, o, counts, offsets, f, d, rows, nullptr, part_stride);
+                           nullptr, o, counts, offsets, f, d, rows, nullptr, part_stride,
+                           DecodeRank{}, 0);
     else if (s.T <= kDecodeMaxT)
         hipLaunchKernelGGL((decode_w8_kernel<2, 1>), grid, block, 0, stream, h, q2, s2, nullptr,
-                           nullptr, o, counts, offsets, f, d, rows, nullptr, part_stride);
+                           nullptr, o, counts, offsets, f, d, rows, nullptr, part_stride,
+                           DecodeRank{}, 0);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

@@ -43,7 +43,9 @@ __global__ __launch_bounds__(256) void q_transpose_pad_kernel(
     }
     if (e < 0) return;
     const int c0 = blockIdx.y * 64, r_lo = lt * 64, cnt = counts[e], s0 = offsets[e];
-    __shared__ uint16_t tile[64][72];
+    // Row pitch 65 (130 bytes): the column reads of 8 rows 8 apart fall on
+    // distinct banks (the writes at most 2 to a bank).
+    __shared__ uint16_t tile[64][65];
     const int tid = threadIdx.x;
 #pragma unroll
     for (int ch = tid; ch < 512; ch += 256) {

@@ -88,6 +88,80 @@ hipError_t launch_dispatch(const moe_shape_t &s, const void *x, const int32_t *i
 // gather their rows from x instead of reading xp.
 hipError_t launch_rank(const moe_shape_t &s, const int32_t *idx, int32_t *counts,
                        int32_t *offsets, int32_t *pos, int32_t *src, hipStream_t stream);
+// The same ranking, computed inside the decode gate/up kernel (T <= kDecodeMaxT:
+// at most kDecodeMaxT * kMaxTopK assignments) instead of by its own launch:
+// every workgroup ranks the routing picks idx for itself (one wavefront, from
+// L2), and workgroup 0 also stores counts, offsets, pos and src for the
+// kernels after it.
+struct DecodeRank {
+    const int32_t *idx;   // [T * top_k] routing picks
+    int n_assign, top_k;
+    int32_t *counts, *offsets, *pos, *src;
+};
+
+// DecodeRank's ranking by one wavefront (at most 128 assignments, E <= 64):
+// lane x counts expert x's picks in each 64-pick batch (ballots), an
+// inclusive scan over the lanes gives the offsets, and each pick's grouped
+// row is its expert's offset + the expert's picks in earlier batches + those
+// on lower lanes of its own batch -- the stable order of dispatch_rank_kernel.
+// s_counts / s_offsets / s_src get the result (the caller's barrier makes it
+// visible); with to_global the outputs of DecodeRank are written too.
+__device__ __forceinline__ void decode_rank_wave(const DecodeRank &rk, int E, int lane,
+                                                 int32_t *s_counts, int32_t *s_offsets,
+                                                 int32_t *s_src, bool to_global) {
+    const uint64_t lower = (1ull << lane) - 1ull;
+    int ev[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int a = 64 * b + lane;
+        ev[b] = a < rk.n_assign ? (int)min((unsigned)rk.idx[a], (unsigned)(E - 1)) : -1;
+    }
+    int c0 = 0, c1 = 0;
+    uint64_t mine0 = 0, mine1 = 0;
+    for (int x = 0; x < E; ++x) {
+        const uint64_t m0 = __ballot(ev[0] == x), m1 = __ballot(ev[1] == x);
+        if (lane == x) {
+            c0 = __popcll(m0);
+            c1 = __popcll(m1);
+        }
+        if (ev[0] == x) mine0 = m0;
+        if (ev[1] == x) mine1 = m1;
+    }
+    const int tot = c0 + c1;
+    int inc = tot;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int u = __shfl_up(inc, off, 64);
+        if (lane >= off) inc += u;
+    }
+    const int excl = inc - tot;
+    if (lane < E) {
+        s_counts[lane] = tot;
+        s_offsets[lane] = excl;
+        if (to_global) {
+            rk.counts[lane] = tot;
+            rk.offsets[lane] = excl;
+        }
+    }
+    if (lane == E - 1) {
+        s_offsets[E] = inc;
+        if (to_global) rk.offsets[E] = inc;
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int e = ev[b] < 0 ? 0 : ev[b];
+        const int first = __shfl(excl, e, 64) + (b == 1 ? __shfl(c0, e, 64) : 0);
+        if (ev[b] >= 0) {
+            const int a = 64 * b + lane;
+            const int p = first + __popcll((b == 0 ? mine0 : mine1) & lower);
+            s_src[p] = a / rk.top_k;
+            if (to_global) {
+                rk.pos[a] = p;
+                rk.src[p] = a / rk.top_k;
+            }
+        }
+    }
+}
 
 // Grouped SwiGLU over expert-sorted rows, in two launches:
 //   gate/up: h = silu(xp w1[e]) * (xp w3[e])    (h in the layer dtype)
@@ -116,10 +190,12 @@ hipError_t launch_quantize_int8(int n_mat, int K, int N, int dtype, const void *
                                 float *scale, hipStream_t stream);
 // Gate/up and down on int8 codes, T <= kDecodeMaxT only (bf16 activations).
 // Down writes `parts` K-slice partial sums, each kT x d, one after another.
+// Gate/up with rank (and src): it ranks the picks itself, as
+// launch_gateup_bf16 does.
 hipError_t launch_gateup_w8(const moe_shape_t &s, const uint16_t *xp, const int32_t *counts,
                             const int32_t *offsets, const int8_t *q1, const float *s1,
                             const int8_t *q3, const float *s3, uint16_t *h, hipStream_t stream,
-                            const int32_t *src = nullptr);
+                            const int32_t *src = nullptr, const DecodeRank *rank = nullptr);
 hipError_t launch_down_w8(const moe_shape_t &s, const uint16_t *h, const int32_t *counts,
                           const int32_t *offsets, const int8_t *q2, const float *s2, float *o,
                           int parts, hipStream_t stream);
@@ -136,10 +212,12 @@ hipError_t launch_down_f32(const moe_shape_t &s, const float *h, const int32_t *
 // is read from xp + src[r] * d_model, i.e. xp is x itself.  gpart (fp32,
 // kDecodeTailBytes, may be NULL): room for the K halves' partial sums of
 // the units the decode kernel cuts to fill its last round of workgroups.
+// rank not NULL (decode sizes, with src): counts, offsets and src are
+// outputs, made by the kernel from rank->idx (see DecodeRank).
 hipError_t launch_gateup_bf16(const moe_shape_t &s, const uint16_t *xp, const int32_t *counts,
                               const int32_t *offsets, const uint16_t *w1, const uint16_t *w3,
                               uint16_t *h, hipStream_t stream, const int32_t *src = nullptr,
-                              float *gpart = nullptr);
+                              float *gpart = nullptr, const DecodeRank *rank = nullptr);
 // The prefill gate/up kernel storing g and u (fp32 [kT, f]) beside h, for
 // the backward.  hipErrorNotSupported when the shape does not take the
 // direct-to-LDS kernel (T <= kDecodeMaxT, d % 64 or f % 128 not zero).
