@@ -333,7 +333,7 @@ def measure_w8(wl_name, steps, warmup):
     h = torch.empty(2 * wl.T, wl.f, dtype=inp.x.dtype, device=dev)
 
     def gateup():
-        moe.expert_gateup_w8(xp, counts, offsets, q1, s1, q3, s3, out=h)
+        moe.expert_gateup_w8(xp, counts, offsets, q1, s1, q3, s3, out=h, workspace=ws)
 
     for _ in range(max(2, warmup)):
         gateup()

@@ -301,6 +301,20 @@ int moe_expert_gateup_w8(const moe_shape_t *shape, const void *xp, const int32_t
                          const int32_t *offsets, const int8_t *q1, const float *s1,
                          const int8_t *q3, const float *s3, void *h, void *stream);
 
+/* moe_expert_gateup_w8 with the layer's workspace (ws / ws_bytes: at least
+ * moe_workspace_bytes(shape)), running exactly the kernels moe_forward_w8
+ * runs for this step.  When the (expert, 256-column) slabs leave the last
+ * round of workgroups part-filled, the slabs past the whole rounds run as
+ * column halves and as quarters (a column half over one half of d_model),
+ * and a small kernel adds each quarter pair's fp32 partial sums (kept in
+ * the workspace) before the SiLU.  Same result as moe_expert_gateup_w8 up
+ * to the order of the additions.  The workspace region written must not
+ * overlap xp, h, counts or offsets (MOE_ERR_ALIAS). */
+int moe_expert_gateup_w8_ws(const moe_shape_t *shape, const void *xp, const int32_t *counts,
+                            const int32_t *offsets, const int8_t *q1, const float *s1,
+                            const int8_t *q3, const float *s3, void *h, void *ws,
+                            size_t ws_bytes, void *stream);
+
 /* moe_expert_down on int8 codes:
  *   o[r, :] = s2[e] * (h[r] q2[e]), fp32 [R, d]. */
 int moe_expert_down_w8(const moe_shape_t *shape, const void *h, const int32_t *counts,
@@ -308,7 +322,7 @@ int moe_expert_down_w8(const moe_shape_t *shape, const void *h, const int32_t *c
                        void *stream);
 
 /* The whole layer with int8 expert weights: route and dispatch as in
- * moe_forward. Gate/up reads its rows straight from x. Down runs in four K
+ * moe_forward. Gate/up reads its rows straight from x. Down runs in two K
  * slices, and the combine adds the slices in order before it weights the
  * slots. y [T, d] bf16. ws / ws_bytes: at least moe_workspace_bytes(shape).
  * y must not overlap x. */

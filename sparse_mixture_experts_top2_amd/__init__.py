@@ -34,7 +34,8 @@ EXPORTED = ["moe_status_str", "moe_workspace_bytes", "moe_route", "moe_route_pro
             "moe_expert_gateup", "moe_expert_gateup_ws", "moe_expert_down", "moe_experts",
             "moe_combine",
             "moe_forward", "moe_rmsnorm_route", "moe_block_forward", "moe_quantize_int8",
-            "moe_expert_gateup_w8", "moe_expert_down_w8", "moe_forward_w8",
+            "moe_expert_gateup_w8", "moe_expert_gateup_w8_ws", "moe_expert_down_w8",
+            "moe_forward_w8",
             "moe_backward_workspace_bytes", "moe_backward", "moe_forward_noalloc"]
 
 
@@ -98,6 +99,8 @@ def load_library(path: Optional[str] = None):
     lib.moe_quantize_int8.restype = I
     lib.moe_expert_gateup_w8.argtypes = [S, P, P, P, P, P, P, P, P, P]
     lib.moe_expert_gateup_w8.restype = I
+    lib.moe_expert_gateup_w8_ws.argtypes = [S, P, P, P, P, P, P, P, P, P, Z, P]
+    lib.moe_expert_gateup_w8_ws.restype = I
     lib.moe_expert_down_w8.argtypes = [S, P, P, P, P, P, P, P]
     lib.moe_expert_down_w8.restype = I
     lib.moe_forward_w8.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, Z, P]
@@ -517,8 +520,11 @@ def _need_w8(q, sc, name, device, E, K, N):
 
 def expert_gateup_w8(xp: torch.Tensor, counts: torch.Tensor, offsets: torch.Tensor,
                      q1: torch.Tensor, s1: torch.Tensor, q3: torch.Tensor, s3: torch.Tensor,
-                     top_k: int = 2, out: Optional[torch.Tensor] = None):
-    """h = silu(s1 * (xp q1[e])) * (s3 * (xp q3[e])) per expert row group."""
+                     top_k: int = 2, out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None):
+    """h = silu(s1 * (xp q1[e])) * (s3 * (xp q3[e])) per expert row group.
+    With the layer's workspace it runs exactly the kernels the layer runs
+    for this step (moe_expert_gateup_w8_ws)."""
     _need(xp, "xp", torch.bfloat16)
     R, d = xp.shape
     T = _routed_tokens(R, top_k, "xp")
@@ -530,10 +536,18 @@ def expert_gateup_w8(xp: torch.Tensor, counts: torch.Tensor, offsets: torch.Tens
     h = out if out is not None else torch.empty(R, f, dtype=torch.bfloat16, device=xp.device)
     _need(h, "h", torch.bfloat16, xp.device, (R, f))
     shape = make_shape(T, d, f, E, torch.bfloat16, top_k)
-    st = load_library().moe_expert_gateup_w8(ctypes.byref(shape), _ptr(xp), _ptr(counts),
-                                             _ptr(offsets), _ptr(q1), _ptr(s1), _ptr(q3),
-                                             _ptr(s3), _ptr(h), _stream(xp.device))
-    _check(st, "moe_expert_gateup_w8")
+    if workspace is None:
+        st = load_library().moe_expert_gateup_w8(ctypes.byref(shape), _ptr(xp), _ptr(counts),
+                                                 _ptr(offsets), _ptr(q1), _ptr(s1), _ptr(q3),
+                                                 _ptr(s3), _ptr(h), _stream(xp.device))
+        _check(st, "moe_expert_gateup_w8")
+    else:
+        _need(workspace, "workspace", torch.uint8, xp.device)
+        st = load_library().moe_expert_gateup_w8_ws(ctypes.byref(shape), _ptr(xp), _ptr(counts),
+                                                    _ptr(offsets), _ptr(q1), _ptr(s1), _ptr(q3),
+                                                    _ptr(s3), _ptr(h), _ptr(workspace),
+                                                    workspace.numel(), _stream(xp.device))
+        _check(st, "moe_expert_gateup_w8_ws")
     return h
 
 

@@ -158,6 +158,7 @@ hipError_t run_layer(const moe_shape_t &s, const void *x, const void *g, float e
     void *h = base + L.h;
     float *o = reinterpret_cast<float *>(base + L.o);
 
+    const bool dec = s.dtype == MOE_BF16 && s.T <= kDecodeMaxT;
     hipError_t e;
     const void *xin = x;
     if (g) {
@@ -166,7 +167,7 @@ hipError_t run_layer(const moe_shape_t &s, const void *x, const void *g, float e
     } else {
         e = launch_route(s, x, w_gate, idx, w, str);
     }
-    if (s.dtype == MOE_BF16 && s.T <= kDecodeMaxT) {
+    if (dec) {
         // Few tokens: the gate/up kernel gathers its rows straight from the
         // layer input through the row -> token table, so no xp copy is made.
         // The ranking runs inside the gate/up kernel (no launch of its own).
@@ -196,9 +197,9 @@ hipError_t run_layer(const moe_shape_t &s, const void *x, const void *g, float e
     }
     // bf16 decode: the down product may cut its last round like gate/up,
     // reusing the partial-sum region (the gate/up finish has read it by then)
-    float *dpart = nullptr;
-    if (s.dtype == MOE_BF16 && s.T <= kDecodeMaxT) dpart = reinterpret_cast<float *>(base + L.gpart);
-    if (e == hipSuccess && !parts_dev) e = launch_down(s, h, counts, offsets, w2, o, str, dpart);
+    float *dpart = dec ? reinterpret_cast<float *>(base + L.gpart) : nullptr;
+    if (e == hipSuccess && !parts_dev)
+        e = launch_down(s, h, counts, offsets, w2, o, str, dpart);
     if (e == hipSuccess) e = launch_combine(s, o, pos, w, y, str, res, 1, parts_dev);
     return e;
 }
@@ -560,6 +561,33 @@ int moe_expert_gateup_w8(const moe_shape_t *s, const void *xp, const int32_t *co
                                        (hipStream_t)stream));
 }
 
+int moe_expert_gateup_w8_ws(const moe_shape_t *s, const void *xp, const int32_t *counts,
+                            const int32_t *offsets, const int8_t *q1, const float *s1,
+                            const int8_t *q3, const float *s3, void *h, void *ws,
+                            size_t ws_bytes, void *stream) {
+    int st = check_w8(s);
+    if (st) return st;
+    if (s->T == 0) return MOE_OK;  // nothing to read or write
+    if (!xp || !counts || !offsets || !q1 || !s1 || !q3 || !s3 || !h || !ws) return MOE_ERR_NULL;
+    if (misaligned(xp) || misaligned(counts) || misaligned(offsets) || misaligned(q1) ||
+        misaligned(s1) || misaligned(q3) || misaligned(s3) || misaligned(h) || misaligned(ws))
+        return MOE_ERR_ALIGN;
+    const Layout L = plan_workspace(*s);
+    if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    // the only workspace region written: the cut slabs' partial sums
+    char *gp = static_cast<char *>(ws) + L.gpart;
+    const Sizes z(*s);
+    const size_t qb = z.w13 / 2, sb = (size_t)s->n_experts * s->d_ff * 4;
+    if (aliased({Buf{xp, z.rows_d}, Buf{counts, z.cnt}, Buf{offsets, z.off}, Buf{q1, qb},
+                 Buf{s1, sb}, Buf{q3, qb}, Buf{s3, sb}},
+                {Buf{h, z.rows_f}}, Buf{gp, kDecodeTailBytes}))
+        return MOE_ERR_ALIAS;
+    return hip_status(launch_gateup_w8(*s, static_cast<const uint16_t *>(xp), counts, offsets,
+                                       q1, s1, q3, s3, static_cast<uint16_t *>(h),
+                                       (hipStream_t)stream, nullptr, nullptr,
+                                       reinterpret_cast<float *>(gp)));
+}
+
 int moe_expert_down_w8(const moe_shape_t *s, const void *h, const int32_t *counts,
                        const int32_t *offsets, const int8_t *q2, const float *s2, float *o,
                        void *stream) {
@@ -621,7 +649,7 @@ int moe_forward_w8(const moe_shape_t *s, const void *x, const void *w_gate, cons
     const DecodeRank rk{idx, routed_rows(*s), s->top_k, counts, offsets, pos, src};
     if (e == hipSuccess)
         e = launch_gateup_w8(*s, static_cast<const uint16_t *>(x), counts, offsets, q1, s1, q3,
-                             s3, h, str, src, &rk);
+                             s3, h, str, src, &rk, reinterpret_cast<float *>(base + L.gpart));
     if (e == hipSuccess) e = launch_down_w8(*s, h, counts, offsets, q2, s2, o, kDownParts, str);
     if (e == hipSuccess) e = launch_combine(*s, o, pos, w, y, str, nullptr, kDownParts);
     return hip_status(e);

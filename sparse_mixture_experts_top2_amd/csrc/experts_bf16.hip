@@ -844,7 +844,7 @@ __global__ __launch_bounds__(DWAVES * 64) void decode_gemm_kernel(
     const uint16_t *__restrict__ B1, void *__restrict__ C, const int32_t *__restrict__ counts,
     const int32_t *__restrict__ offsets, int K, int N, int a_rows,
     const int32_t *__restrict__ src, float *__restrict__ part = nullptr, int n_full = 0,
-    int nb_cols = 0, DecodeRank rk = DecodeRank{}, int n_exp = 0) {
+    int nb_cols = 0, DecodeRank rk = DecodeRank{}, int n_exp = 0, int early = 0) {
     static_assert(!TAIL || MB * 16 <= DTAIL_ROWS, "a part slot holds an expert's rows");
     static_assert(kDecodeMaxT * kMaxTopK <= 128 && kMaxExperts <= 64, "one wavefront ranks");
     int e = blockIdx.y, cblk = blockIdx.x, half = -1, slot = 0;
@@ -859,6 +859,38 @@ __global__ __launch_bounds__(DWAVES * 64) void decode_gemm_kernel(
         cblk = unit - e * nb_cols;
     }
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int kg = lane >> 4, nb = lane & 15;
+    const int col = cblk * DCOLS + nb * 8;
+    const bool col_ok = col < N;
+
+    const uint16_t *Bp[NMAT];
+    Bp[0] = B0 + (size_t)e * K * N + (col_ok ? col : 0);
+    if (NMAT == 2) Bp[NMAT - 1] = B1 + (size_t)e * K * N + (col_ok ? col : 0);
+    int nks = (K + 31) >> 5, kbase = 0;
+    if constexpr (TAIL) {
+        if (half >= 0) {
+            const int all = nks;
+            kbase = (all * half) / 2;
+            nks = (all * (half + 1)) / 2 - kbase;
+        }
+    }
+    const int ks0 = kbase + (nks * wave) / DWAVES, ks1 = kbase + (nks * (wave + 1)) / DWAVES;
+    auto load_b = [&](uint4 (&rb)[NMAT][8], int ks) __attribute__((always_inline)) {
+        const int k = ks * 32 + kg * 8;
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                rb[m][i] = (k + i < K && col_ok) ? load_stream16(Bp[m] + (size_t)(k + i) * N)
+                                                 : zero4();
+    };
+    // early: the weights of this wavefront's first step are requested before
+    // the routing is read (they do not depend on it), so that the routing's
+    // latency overlaps theirs.  The launcher sets it only when nearly every
+    // expert holds rows; an expert with none wastes that one step.
+    uint4 rb0[NMAT][8];
+    const bool pre = early && ks0 < ks1;
+    if (pre) load_b(rb0, ks0);
     __shared__ int32_t s_counts[RANK ? kMaxExperts : 1], s_offsets[RANK ? kMaxExperts + 1 : 1];
     __shared__ int32_t s_src[RANK ? kDecodeMaxT * kMaxTopK : 1];
     if constexpr (RANK) {
@@ -874,13 +906,6 @@ __global__ __launch_bounds__(DWAVES * 64) void decode_gemm_kernel(
     if (Me == 0) return;  // an expert no token chose: its weights are never read
     const int r0 = offsets[e];
     const int nmb = min(MB, (Me + 15) >> 4);
-    const int kg = lane >> 4, nb = lane & 15;
-    const int col = cblk * DCOLS + nb * 8;
-    const bool col_ok = col < N;
-
-    const uint16_t *Bp[NMAT];
-    Bp[0] = B0 + (size_t)e * K * N + (col_ok ? col : 0);
-    if (NMAT == 2) Bp[NMAT - 1] = B1 + (size_t)e * K * N + (col_ok ? col : 0);
     // Row i*16 + lane%16 of this expert; rows past the end of A are clamped
     // onto its last row (their results are never stored).  With src, grouped
     // row r is row src[r] of A (A is then x itself: a gather, no copy).
@@ -899,24 +924,8 @@ __global__ __launch_bounds__(DWAVES * 64) void decode_gemm_kernel(
 #pragma unroll
             for (int c = 0; c < 8; ++c) acc[m][i][c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    int nks = (K + 31) >> 5, kbase = 0;
-    if constexpr (TAIL) {
-        if (half >= 0) {
-            const int all = nks;
-            kbase = (all * half) / 2;
-            nks = (all * (half + 1)) / 2 - kbase;
-        }
-    }
-    const int ks0 = kbase + (nks * wave) / DWAVES, ks1 = kbase + (nks * (wave + 1)) / DWAVES;
-    for (int ks = ks0; ks < ks1; ++ks) {
+    auto step = [&](const uint4 (&rb)[NMAT][8], int ks) __attribute__((always_inline)) {
         const int k = ks * 32 + kg * 8;
-        uint4 rb[NMAT][8];
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                rb[m][i] = (k + i < K && col_ok) ? load_stream16(Bp[m] + (size_t)(k + i) * N)
-                                                 : zero4();
         bf16x8_t af[MB];
 #pragma unroll
         for (int i = 0; i < MB; ++i)
@@ -936,7 +945,36 @@ __global__ __launch_bounds__(DWAVES * 64) void decode_gemm_kernel(
                         af[i], as_bf16x8(tb[c]), acc[m][i][c], 0, 0, 0);
             }
         }
+    };
+    int ks = ks0;
+    if (pre) step(rb0, ks++);
+    for (; ks < ks1; ++ks) {
+        uint4 rb[NMAT][8];
+        load_b(rb, ks);
+        step(rb, ks);
     }
+
+    // Output row `row` (of this expert) from block i, value j of this lane's
+    // accumulators: h = bf16(silu(g) * u) for gate/up, o fp32 for down.
+    auto store_out = [&](int i, int j, int row) __attribute__((always_inline)) {
+        if constexpr (NMAT == 2) {
+            uint32_t p[4];
+#pragma unroll
+            for (int c = 0; c < 8; c += 2) {
+                const float h0 = silu_f32(acc[0][i][c][j]) * acc[NMAT - 1][i][c][j];
+                const float h1 = silu_f32(acc[0][i][c + 1][j]) * acc[NMAT - 1][i][c + 1][j];
+                p[c >> 1] = f32_to_bf16(h0) | (f32_to_bf16(h1) << 16);
+            }
+            *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(C) + (size_t)(r0 + row) * N +
+                                       col) = make_uint4(p[0], p[1], p[2], p[3]);
+        } else {
+            float *dst = static_cast<float *>(C) + (size_t)(r0 + row) * N + col;
+            *reinterpret_cast<float4 *>(dst) =
+                make_float4(acc[0][i][0][j], acc[0][i][1][j], acc[0][i][2][j], acc[0][i][3][j]);
+            *reinterpret_cast<float4 *>(dst + 4) =
+                make_float4(acc[0][i][4][j], acc[0][i][5][j], acc[0][i][6][j], acc[0][i][7][j]);
+        }
+    };
 
     // Fixed-order tree over the eight wavefronts' partial sums:
     // ((w0+w4)+(w2+w6)) + ((w1+w5)+(w3+w7)).
@@ -978,22 +1016,8 @@ __global__ __launch_bounds__(DWAVES * 64) void decode_gemm_kernel(
                         make_float4(acc[m][i][4][j], acc[m][i][5][j], acc[m][i][6][j],
                                     acc[m][i][7][j]);
                 }
-            } else if (NMAT == 2) {
-                uint32_t p[4];
-#pragma unroll
-                for (int c = 0; c < 8; c += 2) {
-                    const float h0 = silu_f32(acc[0][i][c][j]) * acc[NMAT - 1][i][c][j];
-                    const float h1 = silu_f32(acc[0][i][c + 1][j]) * acc[NMAT - 1][i][c + 1][j];
-                    p[c >> 1] = f32_to_bf16(h0) | (f32_to_bf16(h1) << 16);
-                }
-                *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(C) + (size_t)(r0 + row) * N +
-                                           col) = make_uint4(p[0], p[1], p[2], p[3]);
             } else {
-                float *dst = static_cast<float *>(C) + (size_t)(r0 + row) * N + col;
-                *reinterpret_cast<float4 *>(dst) =
-                    make_float4(acc[0][i][0][j], acc[0][i][1][j], acc[0][i][2][j], acc[0][i][3][j]);
-                *reinterpret_cast<float4 *>(dst + 4) =
-                    make_float4(acc[0][i][4][j], acc[0][i][5][j], acc[0][i][6][j], acc[0][i][7][j]);
+                store_out(i, j, row);
             }
         }
     }
@@ -1009,17 +1033,27 @@ __global__ __launch_bounds__(256) void decode_tail_finish_kernel(
     const int j = blockIdx.x, unit = n_full + j;
     const int e = unit / nb_cols, cblk = unit - e * nb_cols;
     const int Me = counts[e], r0 = offsets[e];
-    const float *g0 = part + decode_tail_slot(j, 0, 0), *g1 = part + decode_tail_slot(j, 1, 0);
-    for (int i = threadIdx.x; i < Me * DCOLS; i += 256) {
-        const int row = i / DCOLS, c = i % DCOLS, col = cblk * DCOLS + c;
+    // four consecutive columns per thread (N % 8 == 0: all in or all out)
+    const float4 *g0 = reinterpret_cast<const float4 *>(part + decode_tail_slot(j, 0, 0));
+    const float4 *g1 = reinterpret_cast<const float4 *>(part + decode_tail_slot(j, 1, 0));
+    const float4 *u0 = reinterpret_cast<const float4 *>(part + decode_tail_slot(j, 0, 1));
+    const float4 *u1 = reinterpret_cast<const float4 *>(part + decode_tail_slot(j, 1, 1));
+    for (int i = threadIdx.x; i < Me * (DCOLS / 4); i += 256) {
+        const int row = i / (DCOLS / 4), col = cblk * DCOLS + 4 * (i % (DCOLS / 4));
         if (col >= N) continue;
-        const float g = g0[i] + g1[i];
+        const float4 a = g0[i], b = g1[i];
+        const float g[4] = {a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w};
         if constexpr (NMAT == 2) {
-            const float u = part[decode_tail_slot(j, 0, 1) + i] + part[decode_tail_slot(j, 1, 1) + i];
-            static_cast<uint16_t *>(out)[(size_t)(r0 + row) * N + col] =
-                (uint16_t)f32_to_bf16(silu_f32(g) * u);
+            const float4 c = u0[i], d = u1[i];
+            const float u[4] = {c.x + d.x, c.y + d.y, c.z + d.z, c.w + d.w};
+            uint32_t hv[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) hv[q] = f32_to_bf16(silu_f32(g[q]) * u[q]);
+            *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(out) + (size_t)(r0 + row) * N +
+                                       col) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
         } else {
-            static_cast<float *>(out)[(size_t)(r0 + row) * N + col] = g;
+            *reinterpret_cast<float4 *>(static_cast<float *>(out) + (size_t)(r0 + row) * N + col) =
+                make_float4(g[0], g[1], g[2], g[3]);
         }
     }
 }
@@ -1049,11 +1083,12 @@ hipError_t launch_decode_gateup(const moe_shape_t &s, const uint16_t *xp,
     const int d = s.d_model, f = s.d_ff, E = s.n_experts, rows = routed_rows(s);
     const int nb_cols = (f + DCOLS - 1) / DCOLS;
     const int n_full = gpart ? decode_tail_full_units(f, E) : -1;
+    const int early = decode_early_weights(rows, E);
     if (n_full >= 0) {
         const int n_cut = nb_cols * E - n_full;
         hipLaunchKernelGGL((decode_gemm_kernel<MB, 2, true, RANK>), dim3(n_full + 2 * n_cut),
                            dim3(DWAVES * 64), 0, stream, xp, w1, w3, h, counts, offsets, d, f,
-                           rows, src, gpart, n_full, nb_cols, rk, E);
+                           rows, src, gpart, n_full, nb_cols, rk, E, early);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(decode_tail_finish_kernel<2>, dim3(n_cut), dim3(256), 0, stream,
@@ -1061,7 +1096,7 @@ hipError_t launch_decode_gateup(const moe_shape_t &s, const uint16_t *xp,
     } else {
         hipLaunchKernelGGL((decode_gemm_kernel<MB, 2, false, RANK>), dim3(nb_cols, E),
                            dim3(DWAVES * 64), 0, stream, xp, w1, w3, h, counts, offsets, d, f,
-                           rows, src, nullptr, 0, 0, rk, E);
+                           rows, src, nullptr, 0, 0, rk, E, early);
     }
     return hipGetLastError();
 }
@@ -1075,18 +1110,20 @@ hipError_t launch_decode_down(const moe_shape_t &s, const uint16_t *h, const int
     const int d = s.d_model, f = s.d_ff, E = s.n_experts, rows = routed_rows(s);
     const int nb_cols = (d + DCOLS - 1) / DCOLS;
     const int n_full = gpart ? decode_tail_full_units(d, E) : -1;
+    const int early = decode_early_weights(rows, E);
     if (n_full >= 0) {
         const int n_cut = nb_cols * E - n_full;
         hipLaunchKernelGGL((decode_gemm_kernel<MB, 1, true>), dim3(n_full + 2 * n_cut),
                            dim3(DWAVES * 64), 0, stream, h, w2, nullptr, o, counts, offsets, f,
-                           d, rows, nullptr, gpart, n_full, nb_cols);
+                           d, rows, nullptr, gpart, n_full, nb_cols, DecodeRank{}, 0, early);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(decode_tail_finish_kernel<1>, dim3(n_cut), dim3(256), 0, stream,
                            gpart, counts, offsets, n_full, nb_cols, d, o);
     } else {
         hipLaunchKernelGGL((decode_gemm_kernel<MB, 1>), dim3(nb_cols, E), dim3(DWAVES * 64), 0,
-                           stream, h, w2, nullptr, o, counts, offsets, f, d, rows, nullptr);
+                           stream, h, w2, nullptr, o, counts, offsets, f, d, rows, nullptr,
+                           nullptr, 0, 0, DecodeRank{}, 0, early);
     }
     return hipGetLastError();
 }

@@ -21,7 +21,7 @@ constexpr int kDecodeMaxT = 32;
 // K slices of the int8-weight down projection at decode sizes; the combine
 // adds the slices in order.  The workspace's o region holds this many
 // copies of o when T <= kDecodeMaxT (kMaxDownSplit copies above it).
-constexpr int kDownParts = 4;
+constexpr int kDownParts = 2;
 // Most K parts the prefill down product is cut into (see launch_down_split_bf16).
 constexpr int kMaxDownSplit = 2;
 // Decode gate/up: most (expert, 128-column) units cut in K halves to fill the
@@ -29,6 +29,13 @@ constexpr int kMaxDownSplit = 2;
 // 2 matrices x 32 rows x 128 columns each).
 constexpr int kDecodeTailMaxUnits = 256;
 constexpr size_t kDecodeTailBytes = (size_t)kDecodeTailMaxUnits * 2 * 2 * 32 * 128 * 4;
+
+// Whether the decode kernels request their first weights before reading
+// the routing (which they need only for the activation rows): when the
+// routed rows are at least twice the experts, an expert holds no rows with
+// probability about exp(-2) or less under near-uniform routing, and each
+// such expert's workgroups waste one K step of their weights.
+inline int decode_early_weights(int rows, int E) { return rows >= 2 * E ? 1 : 0; }
 
 // parts: one int32, the K part count the prefill down kernel chose.
 // gpart: at bf16 decode sizes, the decode gate/up's K-half partial sums.
@@ -191,11 +198,13 @@ hipError_t launch_quantize_int8(int n_mat, int K, int N, int dtype, const void *
 // Gate/up and down on int8 codes, T <= kDecodeMaxT only (bf16 activations).
 // Down writes `parts` K-slice partial sums, each kT x d, one after another.
 // Gate/up with rank (and src): it ranks the picks itself, as
-// launch_gateup_bf16 does.
+// launch_gateup_bf16 does.  part (fp32, kDecodeTailBytes, may be NULL):
+// room for the partial sums of the slabs cut to fill the last round.
 hipError_t launch_gateup_w8(const moe_shape_t &s, const uint16_t *xp, const int32_t *counts,
                             const int32_t *offsets, const int8_t *q1, const float *s1,
                             const int8_t *q3, const float *s3, uint16_t *h, hipStream_t stream,
-                            const int32_t *src = nullptr, const DecodeRank *rank = nullptr);
+                            const int32_t *src = nullptr, const DecodeRank *rank = nullptr,
+                            float *part = nullptr);
 hipError_t launch_down_w8(const moe_shape_t &s, const uint16_t *h, const int32_t *counts,
                           const int32_t *offsets, const int8_t *q2, const float *s2, float *o,
                           int parts, hipStream_t stream);

@@ -198,6 +198,24 @@ def test_gateup_with_workspace_checks():
     assert G(xp=tail) == "MOE_ERR_ALIAS"      # xp there
     assert G(sh=shape(T=0)) == "MOE_OK"
 
+    # the int8 gate/up stage with the workspace: the same checks, plus the
+    # int8 calls' own limits (decode sizes, bf16 activations)
+    def G8(xp=P16, c=P16, o=P16, h=P16B, ws=ctypes.c_void_p(W0), n=need, sh=s):
+        return name(lib.moe_expert_gateup_w8_ws(ctypes.byref(sh), xp, c, o, P16, P16, P16, P16,
+                                                h, ws, n, None))
+    assert G8(ws=None) == "MOE_ERR_NULL"
+    assert G8(h=None) == "MOE_ERR_NULL"
+    assert G8(ws=P17) == "MOE_ERR_ALIGN"
+    assert G8(n=need - 1) == "MOE_ERR_WORKSPACE"
+    assert G8(h=P16) == "MOE_ERR_ALIAS"
+    assert G8(h=tail) == "MOE_ERR_ALIAS"
+    assert G8(c=tail) == "MOE_ERR_ALIAS"
+    assert G8(o=tail) == "MOE_ERR_ALIAS"
+    assert G8(xp=tail) == "MOE_ERR_ALIAS"
+    assert G8(sh=shape(T=0)) == "MOE_OK"
+    assert G8(sh=shape(T=40)) == "MOE_ERR_UNSUPPORTED"
+    assert G8(sh=shape(T=16, dtype=moe.MOE_F32)) == "MOE_ERR_UNSUPPORTED"
+
 
 def test_python_binding_refuses_cpu_tensors():
     import torch
@@ -265,10 +283,10 @@ def test_int8_weight_checks():
 
 
 def test_decode_workspace_holds_the_down_slices():
-    # T <= 32: o holds four K-slice partial sums of kT x d fp32
+    # T <= 32: o holds two K-slice partial sums of kT x d fp32
     lib = moe.load_library()
     s = shape(T=32, d=4096, f=14336, k=2)
-    assert lib.moe_workspace_bytes(ctypes.byref(s)) >= 4 * 64 * 4096 * 4 + 64 * 14336 * 2
+    assert lib.moe_workspace_bytes(ctypes.byref(s)) >= 2 * 64 * 4096 * 4 + 64 * 14336 * 2
 
 
 def test_backward_checks():

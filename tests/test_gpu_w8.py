@@ -121,6 +121,45 @@ def test_each_stage_w8(wl):
     assert err <= 1e-4, err
 
 
+def w8_tail_plan(units, cus):
+    """How the int8 decode gate/up fills its last round of workgroups
+    (mirrors the launcher): (whole slabs, column-half slabs, quarter slabs)
+    or None when every slab runs whole."""
+    if units <= cus or units % cus == 0:
+        return None
+    rem = units % cus
+    if 4 * rem <= cus:
+        plan = (units - rem, 0, rem)
+    elif 2 * rem <= cus:
+        plan = (units - rem, rem, 0)
+    elif 4 * rem <= 3 * cus:
+        plan = (units - rem, cus // 2, rem - cus // 2)
+    else:
+        return None
+    return plan if 2 * plan[2] <= 256 else None
+
+
+@pytest.mark.parametrize("wl,kind", [
+    (sw(32, 200, 1928, E=56, seed=350), "halves+quarters"),  # ragged K halves, ragged last slab
+    (sw(32, 264, 2048, E=40, top_k=3, seed=351), "quarters"),
+    (sw(29, 128, 2048, E=48, seed=352), "halves"),
+], ids=lambda v: v if isinstance(v, str) else v.name)
+def test_w8_gateup_fills_last_round(wl, kind):
+    """Layers whose int8 gate/up slabs (E x ceil(f / 256)) leave the last
+    round of CUs part-filled, so that the launcher cuts them into column
+    halves and quarters (a quarter's two K halves added by a small kernel):
+    every token against the oracle."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    plan = w8_tail_plan(wl.E * ((wl.f + 255) // 256), cus)
+    want = {"halves+quarters": lambda p: p[1] > 0 and p[2] > 0,
+            "quarters": lambda p: p[1] == 0 and p[2] > 0,
+            "halves": lambda p: p[1] > 0 and p[2] == 0}[kind]
+    if plan is None or not want(plan):
+        pytest.skip(f"{cus} CUs give plan {plan} for this shape, not {kind}")
+    announce(f"w8 last-round pieces {wl.name}: plan {plan}")
+    run_w8_parity(checked_inputs(wl))
+
+
 def test_int8_layer_stays_near_the_bf16_layer():
     """Per-column int8 codes change the layer by the quantization error
     only: the int8 layer's output is close to the bf16 layer's."""
