@@ -403,8 +403,12 @@ TRAFFIC_PROFILE_W8 = os.path.join(ROOT, "profiles", "hbm_traffic_gateup_w8_decod
 def counter_traffic(wl_name, profile=None):
     """HBM bytes per gate/up launch from the committed rocprofv3 counter
     summary (FETCH_SIZE and WRITE_SIZE, each scaled by a copy kernel of known
-    size), or None when there is no entry for this workload or the kernels'
-    source has changed since the counters were taken."""
+    size), or None when there is no entry for this workload or any source
+    file of its kernels has changed since the counters were taken.
+
+    The summary's last fenced block holds `fetch_scale`, `write_scale` and,
+    per workload W, `W: fetch_kib=... write_kib=...` and
+    `W_sources: path=sha256 path=sha256 ...`."""
     import hashlib
     try:
         text = open(profile or TRAFFIC_PROFILE).read()
@@ -417,9 +421,13 @@ def counter_traffic(wl_name, profile=None):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
     try:
-        src = os.path.join(ROOT, kv["source_file"])
-        if hashlib.sha256(open(src, "rb").read()).hexdigest() != kv["source_sha256"]:
+        sources = [f.split("=") for f in kv[wl_name + "_sources"].split()]
+        if not sources:
             return None
+        for path, sha in sources:
+            with open(os.path.join(ROOT, path), "rb") as fh:
+                if hashlib.sha256(fh.read()).hexdigest() != sha:
+                    return None
         fields = dict(f.split("=") for f in kv[wl_name].split())
         return int(round((float(fields["fetch_kib"]) * float(kv["fetch_scale"]) +
                           float(fields["write_kib"]) * float(kv["write_scale"])) * 1024))
