@@ -661,18 +661,29 @@ __device__ __forceinline__ void q_tile_run(const QSlots &S, const QArgs &g, cons
             __builtin_amdgcn_sched_barrier(0);
         });
     } else if constexpr (EPI == QE_F32) {
+        // fp32 sums as 16-byte row segments: each 4 x 4 block of a lane
+        // quad is quad-transposed so that a lane holds 4 consecutive
+        // columns of one row (a quarter of the store instructions of
+        // 4-byte column stores).
+        static_assert(NMAT == 1, "fp32 stores of one matrix");
         float *O = static_cast<float *>(g.C) + (Mode::KSPLIT ? (size_t)t.part * g.part_stride : 0);
 #pragma unroll
         for (int i = 0; i < MBE; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int col = n0 + wave * 64 + j * 32 + (lane & 31);
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int qq = 0; qq < 16; ++qq) {
-                    const int row = row0 + i * 32 + 8 * (qq >> 2) + 4 * (lane >> 5) + (qq & 3);
-                    if (row < row_end) O[(size_t)row * N + col] = acc[i][j][qq];
+                for (int grp = 0; grp < 4; ++grp) {
+                    float v[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) v[k] = acc[i][j][4 * grp + k];
+                    q_quad_transpose(v, lane & 3);
+                    const int row = row0 + i * 32 + 8 * grp + 4 * (lane >> 5) + (lane & 3);
+                    const int c4 = n0 + wave * 64 + j * 32 + ((lane & 31) & ~3);
+                    if (row < row_end)
+                        *reinterpret_cast<f32x4_t *>(O + (size_t)row * N + c4) =
+                            f32x4_t{v[0], v[1], v[2], v[3]};
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-            }
     } else {
         // The fp32 sums of expert e (C[e], and C2[e] for the second matrix,
         // [M, N]) as 16-byte row segments (quad transposes), streamed
