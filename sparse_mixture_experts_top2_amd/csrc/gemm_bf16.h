@@ -572,9 +572,12 @@ __device__ __forceinline__ void q_tile_run(const QSlots &S, const QArgs &g, cons
             __builtin_nontemporal_store(
                 packed, reinterpret_cast<uint32_t *>(dst + (size_t)row * N + col - odd));
     };
-    if constexpr (EPI == QE_SWIGLU) {
+    if constexpr (EPI == QE_SWIGLU && !Mode::GU) {
         // h = silu(g) u, silu(g) = g / (1 + 2^(-g log2 e)) with the hardware
-        // exp2 and reciprocal.
+        // exp2 and reciprocal, stored as bf16 column pairs.  (Quad-transposed
+        // 8-byte row segments, as the GU form below stores, measured 2 %
+        // slower here: the transposes lengthen the epilogue more than the
+        // halved store count saves.)
         uint16_t *H = static_cast<uint16_t *>(g.C);
         const int col = n0 + wave * 32 + (lane & 31);
 #pragma unroll
@@ -589,19 +592,44 @@ __device__ __forceinline__ void q_tile_run(const QSlots &S, const QArgs &g, cons
                 const int row_q = row0 + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
                 store_pair(H, row_q, col, hval(q), hval(q + 1));
             }
-        if constexpr (Mode::GU) {
-            const int gcol = n0 + wave * 32 + (lane & 31);
+    } else if constexpr (EPI == QE_SWIGLU) {
+        // GU: h as above, and g and u themselves in fp32.  Each 4 x 4 block
+        // of h, g and u is quad-transposed so that a lane holds 4
+        // consecutive columns of one row: h is stored as 8-byte row segments
+        // (4 bf16, rounded to nearest even), g and u as 16-byte segments (a
+        // quarter of the store instructions of column stores).
+        typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+        uint16_t *H = static_cast<uint16_t *>(g.C);
+        const int c4 = n0 + wave * 32 + ((lane & 31) & ~3);
 #pragma unroll
-            for (int i = 0; i < MBE; ++i)
+        for (int i = 0; i < MBE; ++i)
 #pragma unroll
-                for (int qq = 0; qq < 16; ++qq) {
-                    const int row = row0 + i * 32 + 8 * (qq >> 2) + 4 * (lane >> 5) + (qq & 3);
-                    if (row < row_end) {
-                        g.g_out[(size_t)row * N + gcol] = acc[i][0][qq];
-                        g.u_out[(size_t)row * N + gcol] = acc[i][1][qq];
-                    }
+            for (int grp = 0; grp < 4; ++grp) {
+                float gv[4], uv[4], hv[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    gv[k] = acc[i][0][4 * grp + k];
+                    uv[k] = acc[i][1][4 * grp + k];
+                    const float den = 1.0f + __builtin_amdgcn_exp2f(gv[k] * -1.44269504088896341f);
+                    hv[k] = gv[k] * __builtin_amdgcn_rcpf(den) * uv[k];
                 }
-        }
+                q_quad_transpose(hv, lane & 3);
+                q_quad_transpose(gv, lane & 3);
+                q_quad_transpose(uv, lane & 3);
+                const int row = row0 + i * 32 + 8 * grp + 4 * (lane >> 5) + (lane & 3);
+                if (row < row_end) {
+                    const size_t o = (size_t)row * N + c4;
+                    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+                    __builtin_nontemporal_store(
+                        __builtin_bit_cast(u32x2_t, __builtin_convertvector(
+                                                        f32x4_t{hv[0], hv[1], hv[2], hv[3]},
+                                                        bf16x4_t)),
+                        reinterpret_cast<u32x2_t *>(H + o));
+                    *reinterpret_cast<f32x4_t *>(g.g_out + o) = f32x4_t{gv[0], gv[1], gv[2], gv[3]};
+                    *reinterpret_cast<f32x4_t *>(g.u_out + o) = f32x4_t{uv[0], uv[1], uv[2], uv[3]};
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
     } else if constexpr (EPI == QE_DSWIGLU) {
         // dg = da u s (1 + g (1 - s)), du = da g s with s = sigmoid(g).  Each
         // 4 x 4 block of da is quad-transposed so that a lane holds 4
