@@ -253,6 +253,126 @@ struct QTile {
     int c, e, row0, row_end, n0, kt0, nk, part;
 };
 
+// ---- global -> LDS copies of one tile (1 KiB instructions: 64 lanes x 16 B).
+// K-contiguous operand (A always, B with BKC): a stage is 256 lines x 64
+// K values, 32 instructions of 8 lines; instruction g = lines 8 g ..
+// 8 g + 7, lane l line 8 g + l / 8, LDS chunk l % 8 = K chunk c ^
+// aswz(line).  A's 32 MBE lines are MBE instructions per wavefront.
+// Weights, 32 instructions per stage, 8 per wavefront.
+//   N-contiguous, NMAT = 1: instruction g holds K rows 2 g, 2 g + 1 (512 B
+//   each), lane l row 2 g + l / 32, LDS chunk l % 32 = column chunk
+//   c ^ bswz1(row).  NMAT = 2: instructions 0..15 the first sub-tile,
+//   16..31 the second (waves 0, 1 and 2, 3), each 4 K rows of 256 B,
+//   lane l row 4 (g % 16) + l / 16, LDS chunk l % 16 = c ^ bswz2(row).
+//   K-contiguous: like A, lines n0 .. n0 + 255 (NMAT = 2: lines 0..127
+//   of the stage from B0, 128..255 from B1, waves 0, 1 and 2, 3).
+// Copies of stage s are clamped to the last stage (harmless re-reads).
+// K offsets: K-contiguous operands advance 64 elements per stage, the
+// N-contiguous weights 64 rows.
+template <typename Mode, int MBE>
+struct QLoad {
+    static constexpr int NMAT = Mode::NMAT;
+    static constexpr bool BKC = Mode::BKC, DUAL = Mode::DUAL, GROUPK = Mode::GROUPK;
+    __amdgpu_buffer_rsrc_t ra, ra2, rb, rb2;
+    uint32_t a_vo[MBE], b_vo[8];
+    int wave, kt0, nk, K1, N;
+
+    __device__ __forceinline__ QLoad(const QArgs &g, const QTile &t) {
+        const int lane = threadIdx.x & 63;
+        wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        kt0 = t.kt0;
+        nk = t.nk;
+        K1 = g.K1;
+        N = g.N;
+        ra = q_rsrc(g.A, (uint32_t)((size_t)g.a_lines * g.lda * 2));
+        ra2 = ra;
+        if constexpr (DUAL) ra2 = q_rsrc(g.A2, (uint32_t)((size_t)g.a_lines * g.lda * 2));
+#pragma unroll
+        for (int j = 0; j < MBE; ++j) {
+            const int r = 8 * (wave * MBE + j) + (lane >> 3);
+            const int c = (lane & 7) ^ q_aswz(r);
+            a_vo[j] = (uint32_t)(((size_t)(t.row0 + r) * g.lda + c * 8) * 2);
+        }
+        const uint16_t *Bw = (NMAT == 2 && wave >= 2) ? g.B1 : g.B0;
+        size_t b_mat = 0;
+        uint32_t b_bytes;
+        if constexpr (GROUPK) {
+            b_bytes = (uint32_t)((size_t)N * g.ldb * 2);
+        } else if constexpr (BKC) {
+            b_mat = (size_t)t.e * N * g.ldb;
+            b_bytes = (uint32_t)((size_t)N * g.ldb * 2);
+        } else {
+            b_mat = (size_t)t.e * g.K * N;
+            b_bytes = (uint32_t)((size_t)g.K * N * 2);
+        }
+        rb = q_rsrc(Bw + b_mat, b_bytes);
+        rb2 = rb;
+        if constexpr (DUAL) rb2 = q_rsrc(g.B2 + b_mat, b_bytes);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if constexpr (BKC) {
+                const int gi = wave * 8 + j;
+                const int r = 8 * gi + (lane >> 3);                    // line of the stage
+                const int c = (lane & 7) ^ q_aswz(r);
+                const int line = NMAT == 2 ? t.n0 + (r & 127) : t.n0 + r;
+                b_vo[j] = (uint32_t)(((size_t)line * g.ldb + c * 8) * 2);
+            } else {
+                int r, c;
+                if constexpr (NMAT == 2) {
+                    r = 4 * (((wave & 1) << 3) + j) + (lane >> 4);
+                    c = (lane & 15) ^ q_bswz2(r);
+                } else {
+                    r = 2 * (wave * 8 + j) + (lane >> 5);
+                    c = (lane & 31) ^ q_bswz1(r);
+                }
+                b_vo[j] = (uint32_t)(((size_t)r * N + t.n0 + c * 8) * 2);
+            }
+        }
+    }
+    __device__ __forceinline__ int b_dst(int j) const {
+        if constexpr (NMAT == 2 && !BKC)
+            return (wave >> 1) * (QSLOT / 2) + (((wave & 1) << 3) + j) * 1024;
+        else
+            return (wave * 8 + j) * 1024;
+    }
+    __device__ __forceinline__ void a_copy(uint8_t *slot, int s, int j) const {
+        const int k0 = (kt0 + min(s, nk - 1)) * QBK;
+        if constexpr (DUAL) {
+            if (k0 >= K1) {
+                q_dma(ra2, slot + (wave * MBE + j) * 1024, a_vo[j], (uint32_t)((k0 - K1) * 2));
+                return;
+            }
+        }
+        q_dma(ra, slot + (wave * MBE + j) * 1024, a_vo[j], (uint32_t)(k0 * 2));
+    }
+    __device__ __forceinline__ void b_copy(uint8_t *slot, int s, int j) const {
+        const int k0 = (kt0 + min(s, nk - 1)) * QBK;
+        if constexpr (BKC) {
+            if constexpr (DUAL) {
+                if (k0 >= K1) {
+                    q_dma(rb2, slot + b_dst(j), b_vo[j], (uint32_t)((k0 - K1) * 2));
+                    return;
+                }
+            }
+            q_dma(rb, slot + b_dst(j), b_vo[j], (uint32_t)(k0 * 2));
+        } else {
+            q_dma(rb, slot + b_dst(j), b_vo[j], (uint32_t)((size_t)k0 * N * 2));
+        }
+    }
+    // The copies of stages 0 and 1: activations of stage 0, weights of
+    // stages 0 and 1, activations of stage 1 (MBE + 16 + MBE instructions).
+    __device__ __forceinline__ void prologue(const QSlots &S) const {
+#pragma unroll
+        for (int j = 0; j < MBE; ++j) a_copy(S.a0, 0, j);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) b_copy(S.b0, 0, j);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) b_copy(S.b1, 1, j);
+#pragma unroll
+        for (int j = 0; j < MBE; ++j) a_copy(S.a1, 1, j);
+    }
+};
+
 // 4 x 4 transpose across the lanes of a quad (DPP quad permutations):
 // before, lane p of the quad holds v[k] = element (row k, column p); after,
 // v[k] = element (row p, column k).  Two butterfly stages (partner lanes
@@ -298,99 +418,9 @@ __device__ __forceinline__ void q_tile_run(const QSlots &S, const QArgs &g, cons
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-    // ---- global -> LDS copies (1 KiB instructions: 64 lanes x 16 B).
-    // K-contiguous operand (A always, B with BKC): a stage is 256 lines x 64
-    // K values, 32 instructions of 8 lines; instruction g = lines 8 g ..
-    // 8 g + 7, lane l line 8 g + l / 8, LDS chunk l % 8 = K chunk c ^
-    // aswz(line).  A's 32 MBE lines are MBE instructions per wavefront.
-    const __amdgpu_buffer_rsrc_t ra =
-        q_rsrc(g.A, (uint32_t)((size_t)g.a_lines * g.lda * 2));
-    __amdgpu_buffer_rsrc_t ra2 = ra;
-    if constexpr (DUAL) ra2 = q_rsrc(g.A2, (uint32_t)((size_t)g.a_lines * g.lda * 2));
-    uint32_t a_vo[MBE];
-#pragma unroll
-    for (int j = 0; j < MBE; ++j) {
-        const int r = 8 * (wave * MBE + j) + (lane >> 3);
-        const int c = (lane & 7) ^ q_aswz(r);
-        a_vo[j] = (uint32_t)(((size_t)(row0 + r) * g.lda + c * 8) * 2);
-    }
-    // Weights, 32 instructions per stage, 8 per wavefront.
-    //   N-contiguous, NMAT = 1: instruction g holds K rows 2 g, 2 g + 1 (512 B
-    //   each), lane l row 2 g + l / 32, LDS chunk l % 32 = column chunk
-    //   c ^ bswz1(row).  NMAT = 2: instructions 0..15 the first sub-tile,
-    //   16..31 the second (waves 0, 1 and 2, 3), each 4 K rows of 256 B,
-    //   lane l row 4 (g % 16) + l / 16, LDS chunk l % 16 = c ^ bswz2(row).
-    //   K-contiguous: like A, lines n0 .. n0 + 255 (NMAT = 2: lines 0..127
-    //   of the stage from B0, 128..255 from B1, waves 0, 1 and 2, 3).
-    const uint16_t *Bw = (NMAT == 2 && wave >= 2) ? g.B1 : g.B0;
-    size_t b_mat = 0;
-    uint32_t b_bytes;
-    if constexpr (GROUPK) {
-        b_bytes = (uint32_t)((size_t)N * g.ldb * 2);
-    } else if constexpr (BKC) {
-        b_mat = (size_t)e * N * g.ldb;
-        b_bytes = (uint32_t)((size_t)N * g.ldb * 2);
-    } else {
-        b_mat = (size_t)e * g.K * N;
-        b_bytes = (uint32_t)((size_t)g.K * N * 2);
-    }
-    const __amdgpu_buffer_rsrc_t rb = q_rsrc(Bw + b_mat, b_bytes);
-    __amdgpu_buffer_rsrc_t rb2 = rb;
-    if constexpr (DUAL) rb2 = q_rsrc(g.B2 + b_mat, b_bytes);
-    uint32_t b_vo[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        if constexpr (BKC) {
-            const int gi = wave * 8 + j;
-            const int r = 8 * gi + (lane >> 3);                    // line of the stage
-            const int c = (lane & 7) ^ q_aswz(r);
-            const int line = NMAT == 2 ? n0 + (r & 127) : n0 + r;
-            b_vo[j] = (uint32_t)(((size_t)line * g.ldb + c * 8) * 2);
-        } else {
-            int r, c;
-            if constexpr (NMAT == 2) {
-                r = 4 * (((wave & 1) << 3) + j) + (lane >> 4);
-                c = (lane & 15) ^ q_bswz2(r);
-            } else {
-                r = 2 * (wave * 8 + j) + (lane >> 5);
-                c = (lane & 31) ^ q_bswz1(r);
-            }
-            b_vo[j] = (uint32_t)(((size_t)r * N + n0 + c * 8) * 2);
-        }
-    }
-    auto b_dst = [&](int j) Q_INLINE {
-        if constexpr (NMAT == 2 && !BKC)
-            return (wave >> 1) * (QSLOT / 2) + (((wave & 1) << 3) + j) * 1024;
-        else
-            return (wave * 8 + j) * 1024;
-    };
-    // Copies of stage s (clamped to the last stage: harmless re-reads).
-    // K offsets: K-contiguous operands advance 64 elements per stage, the
-    // N-contiguous weights 64 rows.
-    auto a_copy = [&](uint8_t *slot, int s, int j) Q_INLINE {
-        int k0 = (kt0 + min(s, nk - 1)) * QBK;
-        if constexpr (DUAL) {
-            if (k0 >= g.K1) {
-                q_dma(ra2, slot + (wave * MBE + j) * 1024, a_vo[j], (uint32_t)((k0 - g.K1) * 2));
-                return;
-            }
-        }
-        q_dma(ra, slot + (wave * MBE + j) * 1024, a_vo[j], (uint32_t)(k0 * 2));
-    };
-    auto b_copy = [&](uint8_t *slot, int s, int j) Q_INLINE {
-        const int k0 = (kt0 + min(s, nk - 1)) * QBK;
-        if constexpr (BKC) {
-            if constexpr (DUAL) {
-                if (k0 >= g.K1) {
-                    q_dma(rb2, slot + b_dst(j), b_vo[j], (uint32_t)((k0 - g.K1) * 2));
-                    return;
-                }
-            }
-            q_dma(rb, slot + b_dst(j), b_vo[j], (uint32_t)(k0 * 2));
-        } else {
-            q_dma(rb, slot + b_dst(j), b_vo[j], (uint32_t)((size_t)k0 * N * 2));
-        }
-    };
+    const QLoad<Mode, MBE> L(g, t);
+    auto a_copy = [&](uint8_t *slot, int s, int j) Q_INLINE { L.a_copy(slot, s, j); };
+    auto b_copy = [&](uint8_t *slot, int s, int j) Q_INLINE { L.b_copy(slot, s, j); };
 
     // ---- fragment reads.
     // A block i, step h (16 K values): line 32 i + l % 32, K chunk 2 h + l / 32
@@ -523,14 +553,7 @@ __device__ __forceinline__ void q_tile_run(const QSlots &S, const QArgs &g, cons
     if (nk > 0) {
         // Prologue: what the windows of stages -2 and -1 would have issued,
         // then the fragments of step (0, 0).
-#pragma unroll
-        for (int j = 0; j < MBE; ++j) a_copy(slot_a(std::integral_constant<int, 0>{}), 0, j);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) b_copy(slot_b(std::integral_constant<int, 0>{}), 0, j);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) b_copy(slot_b(std::integral_constant<int, 1>{}), 1, j);
-#pragma unroll
-        for (int j = 0; j < MBE; ++j) a_copy(slot_a(std::integral_constant<int, 1>{}), 1, j);
+        L.prologue(S);
         q_barrier<8 + MBE>();
         q_for<NR>([&](auto r_c) Q_INLINE {
             read_item(std::integral_constant<int, 0>{}, r_c,
@@ -854,7 +877,7 @@ __device__ __forceinline__ void q_body_dw(const QArgs &g, const int32_t *__restr
         return base;
     };
     const int lo = boundary(xcd), hi = xcd == 7 ? E * per_e : boundary(xcd + 1);
-    for (int idx = lo + j; idx < hi; idx += cu_per_xcd) {
+    auto tile_at = [&](int idx) Q_INLINE {
         QTile t{};
         t.e = idx / per_e;
         int mt, nt;
@@ -868,8 +891,9 @@ __device__ __forceinline__ void q_body_dw(const QArgs &g, const int32_t *__restr
         t.kt0 = kstage;
         t.nk = (counts[t.e] + QBK - 1) / QBK;
         t.part = 0;
-        q_tile_run<Mode, 8>(S, g, t);
-    }
+        return t;
+    };
+    for (int idx = lo + j; idx < hi; idx += cu_per_xcd) q_tile_run<Mode, 8>(S, g, tile_at(idx));
 }
 
 inline bool q_fits(int rows, int K, int N, int bnm) {
