@@ -160,6 +160,40 @@ def test_w8_gateup_fills_last_round(wl, kind):
     run_w8_parity(checked_inputs(wl))
 
 
+@pytest.mark.parametrize("wl", [sw(32, 200, 1928, E=56, seed=353),
+                                sw(16, 136, 2048, E=40, top_k=3, seed=354)],
+                         ids=lambda w: w.name)
+def test_gateup_w8_stage_with_workspace(wl):
+    """moe_expert_gateup_w8_ws (the layer's gate/up kernels: whole slabs,
+    column halves and quarters, the quarters' K halves added by a finishing
+    kernel) against the oracle's h, fed the oracle's dispatch; the stage
+    without a workspace (every slab whole) the same way."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    plan = w8_tail_plan(wl.E * ((wl.f + 255) // 256), cus)
+    if plan is None or plan[2] == 0:
+        pytest.skip(f"{cus} CUs give plan {plan}: no quarters to add")
+    announce(f"gate/up stage with workspace {wl.name}: plan {plan}")
+    k = wl.top_k
+    inp = checked_inputs(wl)
+    (q1, s1, q3, s3, _, _), (hq1, hs1, hq3, hs3, _, _) = quantized(inp)
+    idx_o, _ = oracle.route(inp.x, inp.w_gate, top_k=k)
+    c_o, off_o, _, src_o = oracle.dispatch(idx_o, wl.E)
+    xp_o = inp.x[torch.as_tensor(src_o // k)].contiguous()
+    expert_of_row = np.repeat(np.arange(wl.E, dtype=np.int32), c_o)
+    h_ref = oracle.expert_hidden_w8(xp_o, expert_of_row, hq1, hs1, hq3, hs3)
+    c_d = torch.as_tensor(c_o, device=DEV)
+    off_d = torch.as_tensor(off_o, device=DEV)
+    ws = moe.alloc_workspace(wl.T, wl.d, wl.f, wl.E, torch.bfloat16, DEV, top_k=k)
+    ws.fill_(0xFF)   # the stage must not depend on the workspace's contents
+    h_ws = moe.expert_gateup_w8(xp_o.to(DEV), c_d, off_d, q1, s1, q3, s3, top_k=k, workspace=ws)
+    h = moe.expert_gateup_w8(xp_o.to(DEV), c_d, off_d, q1, s1, q3, s3, top_k=k)
+    torch.cuda.synchronize()
+    for name, got in (("with workspace", h_ws), ("without", h)):
+        err = row_max_rel_err(got, h_ref)
+        announce(f"  {name}: row-max-rel err {err:.3e}")
+        assert err <= 1e-2, (name, err)
+
+
 def test_int8_layer_stays_near_the_bf16_layer():
     """Per-column int8 codes change the layer by the quantization error
     only: the int8 layer's output is close to the bf16 layer's."""
