@@ -384,8 +384,12 @@ def measure_backward(wl_name, steps, warmup):
     for _ in range(warmup):
         step()
     ms = time_region(step, steps, stream)
+    # Eight grouped products of 2 kT d f: the recomputed g and u (two),
+    # da (one: dy W2^T, from which the routing-weight gradient follows
+    # without recomputing o), dXp (two) and dW1, dW3, dW2 (three); plus the
+    # router's dx and dW_gate terms.
     R = 2 * wl.T
-    flops = 9 * 2.0 * R * wl.d * wl.f + 4.0 * wl.T * wl.d * wl.E
+    flops = 8 * 2.0 * R * wl.d * wl.f + 4.0 * wl.T * wl.d * wl.E
     ach = flops / (ms * 1e-3) / 1e12
     log(f"{wl_name} backward: {ms:.3f} ms/step ({wl.T / ms * 1e3:.0f} tokens/s); "
         f"{ach:.0f} TFLOP/s = {ach / PEAK_BF16_TFLOPS * 100:.1f}% of bf16 peak")

@@ -349,16 +349,41 @@ __global__ __launch_bounds__(256) void bwd_gemm_kernel(GemmArgs p) {
         }
 }
 
+// The routed rows' dy for the dSwiGLU product (bf16): one wavefront per
+// token t copies dy[t] to dyp[pos[t, s]] for every slot s and stores the
+// slot's routing weight in w_row[pos[t, s]].
+__global__ __launch_bounds__(256) void bwd_gather_dy_kernel(const uint4 *__restrict__ dy,
+                                                            const int32_t *__restrict__ pos,
+                                                            const float *__restrict__ w, int n_tok,
+                                                            int k, int row_vecs,
+                                                            uint4 *__restrict__ dyp,
+                                                            float *__restrict__ w_row) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= n_tok) return;
+    for (int s = 0; s < k; ++s) {
+        const int r = pos[k * t + s];
+        if (lane == 0) w_row[r] = w[k * t + s];
+        for (int j = lane; j < row_vecs; j += 64)
+            dyp[(size_t)r * row_vecs + j] = dy[(size_t)t * row_vecs + j];
+    }
+}
+
 // One workgroup per token t: for each slot s with row r = pos[t, s],
 //   dw_s = sum_i dy[t, i] o[r, i]     (fixed-order block reduction)
 //   dO[r, i] = w[t, s] dy[t, i]       (layer dtype)
 // then dl[t, :] = 0 except dl[t, idx_s] = w_s (dw_s - sum_r w_r dw_r).
+// With dw_part (o not computed): dw_s = sum over the nct column tiles c of
+// dw_part[r, c], the parts of h . (dy W2^T) = dy . o that the dSwiGLU
+// product leaves, added in tile order by the first wavefront's lanes
+// (lane l the tiles l, l + 64, ...) and then across its lanes (xor 32 ..
+// 1): a fixed order.
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_route_grad_kernel(
     const T *__restrict__ dy, const float *__restrict__ o, const int32_t *__restrict__ idx,
     const float *__restrict__ w, const int32_t *__restrict__ pos, int d, int E, int k,
     T *__restrict__ dO, float *__restrict__ dl, const int *__restrict__ o_parts,
-    size_t part_stride) {
+    size_t part_stride, const float *__restrict__ dw_part, int nct) {
     __shared__ float part[4][kMaxTopK];
     const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const bool two = o_parts && *o_parts == 2;   // o = part 0 + part 1
@@ -369,12 +394,19 @@ __global__ __launch_bounds__(256) void bwd_route_grad_kernel(
         const int r = pos[k * t + s];
         const float ws = w[k * t + s];
         float acc = 0.0f;
-        for (int i = tid; i < d; i += 256) {
-            const float g = to_f32(dy[(size_t)t * d + i]);
-            float ov = o[(size_t)r * d + i];
-            if (two) ov += o[part_stride + (size_t)r * d + i];
-            acc += g * ov;
-            dO[(size_t)r * d + i] = from_f32<T>(ws * g);
+        if (dw_part) {
+            if (wave == 0)
+                for (int c = lane; c < nct; c += 64) acc += dw_part[(size_t)r * nct + c];
+            for (int i = tid; i < d; i += 256)
+                dO[(size_t)r * d + i] = from_f32<T>(ws * to_f32(dy[(size_t)t * d + i]));
+        } else {
+            for (int i = tid; i < d; i += 256) {
+                const float g = to_f32(dy[(size_t)t * d + i]);
+                float ov = o[(size_t)r * d + i];
+                if (two) ov += o[part_stride + (size_t)r * d + i];
+                acc += g * ov;
+                dO[(size_t)r * d + i] = from_f32<T>(ws * g);
+            }
         }
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
@@ -629,12 +661,42 @@ hipError_t run_backward_t(const moe_shape_t &s, const T *x, const T *wg, const T
         if (e == hipSuccess)
             e = gemm<T, OP_KC, OP_MNC, GROUP_ROWS, EPI_UP>(a, rt * tiles_of(f), str);
     }
+    // bf16 layers whose sizes fit the pipelined tile body need no o: the
+    // dSwiGLU product takes the routed rows' dy unscaled, z = dy W2[e]^T,
+    // and the routing-weight gradient dy . o = h . z comes from its epilogue
+    // in per-column-tile parts (w_row and the parts live in the o region,
+    // which dXp takes over later).
+    bool zpath = false;
+    if constexpr (sizeof(T) == 2)
+        zpath = q_bt_dswiglu_supported(R, d, f) && (size_t)(1 + f / 256) <= (size_t)kMaxDownSplit * d;
+    const int nct = f / 256;
+    float *w_row = O;
+    float *dw_part = O + ((R + 63) / 64) * 64;
+    bool da_done = false, dxp_done = false;
+    if constexpr (sizeof(T) == 2) {
+        if (zpath && e == hipSuccess && Tn > 0) {
+            hipLaunchKernelGGL(bwd_gather_dy_kernel, dim3((Tn + 3) / 4), dim3(256), 0, str,
+                               reinterpret_cast<const uint4 *>(dy), pos, w, Tn, k, d / 8,
+                               reinterpret_cast<uint4 *>(dO), w_row);
+            e = hipGetLastError();
+            if (e == hipSuccess)
+                e = q_launch_bt_dswiglu(R, E, dO, w2, d, f, counts, offsets, G, U, dG, dU, w_row,
+                                        H, dw_part, str);
+            if (e == hipSuccess) {
+                hipLaunchKernelGGL(bwd_route_grad_kernel<T>, dim3(Tn), dim3(256), 0, str, dy, O,
+                                   idx, w, pos, d, E, k, dO, dl, nullptr, (size_t)0, dw_part,
+                                   nct);
+                e = hipGetLastError();
+            }
+            da_done = true;
+        }
+    }
     // o = h W2[e]: the forward's down kernels for bf16 (at prefill sizes the
     // variant that cuts the reduction in parts; route_grad adds them), the
     // generic GEMM for fp32
     const int *o_parts = nullptr;
     if constexpr (sizeof(T) == 2) {
-        if (e == hipSuccess) {
+        if (e == hipSuccess && !zpath) {
             const hipError_t de = launch_down_split_bf16(R, E, H, counts, offsets, w2, f, d, 0,
                                                          pstride, O, nparts, str);
             if (de == hipSuccess) o_parts = nparts;
@@ -650,18 +712,17 @@ hipError_t run_backward_t(const moe_shape_t &s, const T *x, const T *wg, const T
             e = gemm<T, OP_KC, OP_MNC, GROUP_ROWS, EPI_STORE>(a, rt * tiles_of(d), str);
     }
     // routing-weight gradients, dO and dl
-    if (e == hipSuccess && Tn > 0) {
+    if (e == hipSuccess && Tn > 0 && !zpath) {
         hipLaunchKernelGGL(bwd_route_grad_kernel<T>, dim3(Tn), dim3(256), 0, str, dy, O, idx, w,
-                           pos, d, E, k, dO, dl, o_parts, pstride);
+                           pos, d, E, k, dO, dl, o_parts, pstride, nullptr, 0);
         e = hipGetLastError();
     }
     // da = dO W2[e]^T, with dg, du in the epilogue.  The weight matrices are
     // read K-contiguous here (a row of W2[e] is a column of W2[e]^T); bf16
-    // layers whose sizes fit the forward's direct-to-LDS pipeline take its
-    // variant for such operands, other shapes the generic GEMM.
-    bool da_done = false, dxp_done = false;
+    // layers of other sizes take the direct-to-LDS variant for such
+    // operands where it fits, other shapes the generic GEMM.
     if constexpr (sizeof(T) == 2) {
-        if (e == hipSuccess) {
+        if (e == hipSuccess && !da_done) {
             const hipError_t fe = launch_bt_dswiglu_bf16(R, E, dO, w2, d, f, counts, offsets,
                                                          G, U, dG, dU, str);
             da_done = fe == hipSuccess;

@@ -1216,11 +1216,6 @@ hipError_t launch_bt_dswiglu_bf16(int rows, int E, const uint16_t *A, const uint
                                   const float *g, const float *u, uint16_t *dg, uint16_t *du,
                                   hipStream_t stream) {
     if (!bt_shape_ok(rows, K1, N)) return hipErrorNotSupported;
-    {
-        const hipError_t qe =
-            q_launch_bt_dswiglu(rows, E, A, B, K1, N, counts, offsets, g, u, dg, du, stream);
-        if (qe != hipErrorNotSupported) return qe;
-    }
     const int grid = prefill_grid(rows, E, N / PBN);
     hipLaunchKernelGGL(prefill_dma_bt_dswiglu_kernel, dim3(grid), dim3(PWM * PWN * 64), 0,
                        stream, A, B, counts, offsets, E, K1, N, rows, g, u, dg, du);

@@ -208,8 +208,12 @@ __device__ __forceinline__ float q_makespan(const int (&m)[3], int n_cols, int S
 //          (row tiles of one expert) and the tile's expert selects B.
 //   EPI    QE_SWIGLU: h = bf16(silu(a b0) * (a b1)) (GU: also g, u fp32);
 //          QE_F32:    C = a b fp32 (KSPLIT: part p at C + p * part_stride);
-//          QE_DSWIGLU: da = a b, then dg = da * u * silu'(g) and
-//                     du = da * silu(g), bf16, with g, u fp32 inputs;
+//          QE_DSWIGLU: z = a b with a the routed rows' dy, da = w z (w the
+//                     row's routing weight), then dg = da * u * silu'(g) and
+//                     du = da * silu(g), bf16, with g, u fp32 inputs; also
+//                     the row's h . z over the tile's columns (the
+//                     routing-weight gradient dy . o = h . (dy W2^T), per
+//                     column tile);
 //          QE_DW:     C (and C2 for NMAT = 2) = the fp32 sums, [E, M, N].
 enum { QE_SWIGLU = 0, QE_F32 = 1, QE_DSWIGLU = 2, QE_DW = 3 };
 
@@ -241,6 +245,9 @@ struct QArgs {
     int K, N, M;         // reduction length (stages x 64; DUAL: 2 K1), columns, GROUPK rows
     int a_lines, lda, ldb, K1;
     const float *g_in, *u_in;
+    const float *w_row;      // QE_DSWIGLU: routing weight of each grouped row
+    const uint16_t *h_in;    // QE_DSWIGLU: h [rows, N]
+    float *dw_part;          // QE_DSWIGLU: per-row partial sums of h . z, [rows, N / 256]
     float *g_out, *u_out;
     size_t part_stride;
 };
@@ -654,16 +661,26 @@ __device__ __forceinline__ void q_tile_run(const QSlots &S, const QArgs &g, cons
                 __builtin_amdgcn_sched_barrier(0);
             }
     } else if constexpr (EPI == QE_DSWIGLU) {
-        // dg = da u s (1 + g (1 - s)), du = da g s with s = sigmoid(g).  Each
-        // 4 x 4 block of da is quad-transposed so that a lane holds 4
-        // consecutive columns of one row: g and u are read and dg, du written
-        // as row segments, and the next block's g, u loads are issued before
-        // the current block is computed (rows clamped into the tile).
+        // z = dy W2^T for the routed rows (the accumulators), da = w z,
+        // dg = da u s (1 + g (1 - s)), du = da g s with s = sigmoid(g).
+        // Each 4 x 4 block of z is quad-transposed so that a lane holds 4
+        // consecutive columns of one row: g, u, h and the row's weight are
+        // read and dg, du written as row segments, and the next block's
+        // loads are issued before the current block is computed (rows
+        // clamped into the tile).  The routing-weight gradient's part from
+        // this tile, sum over its 256 columns of h z, is reduced in a fixed
+        // order: a lane's 4 columns of both 32-column blocks, the 8 lanes
+        // of the row (xor 4, 8, 16), then the 4 wavefronts through LDS
+        // ((w0 + w1) + (w2 + w3)).
         uint16_t *dG = static_cast<uint16_t *>(g.C);
         uint16_t *dU = static_cast<uint16_t *>(g.C2);
         typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
         constexpr int NBLK = MBE * 2;
         float4 gb[2][4], ub[2][4];
+        uint2 hb[2][4];
+        float wr[2][4];
+        float hz[4];
+        float *red = reinterpret_cast<float *>(S.b2);   // [4 wavefronts][256 rows]
         auto blk_row = [&](int i, int grp) Q_INLINE {
             return row0 + i * 32 + 8 * grp + 4 * (lane >> 5) + (lane & 3);
         };
@@ -673,9 +690,12 @@ __device__ __forceinline__ void q_tile_run(const QSlots &S, const QArgs &g, cons
             constexpr int i = b / 2, j = b % 2;
 #pragma unroll
             for (int grp = 0; grp < 4; ++grp) {
-                const size_t o = (size_t)min(blk_row(i, grp), row_end - 1) * N + blk_col(j);
+                const int r = min(blk_row(i, grp), row_end - 1);
+                const size_t o = (size_t)r * N + blk_col(j);
                 gb[bf][grp] = *reinterpret_cast<const float4 *>(g.g_in + o);
                 ub[bf][grp] = *reinterpret_cast<const float4 *>(g.u_in + o);
+                hb[bf][grp] = *reinterpret_cast<const uint2 *>(g.h_in + o);
+                wr[bf][grp] = g.w_row[r];
             }
         };
         load_blk(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
@@ -692,13 +712,21 @@ __device__ __forceinline__ void q_tile_run(const QSlots &S, const QArgs &g, cons
                 q_quad_transpose(v, lane & 3);
                 const float gg[4] = {gb[bf][grp].x, gb[bf][grp].y, gb[bf][grp].z, gb[bf][grp].w};
                 const float uu[4] = {ub[bf][grp].x, ub[bf][grp].y, ub[bf][grp].z, ub[bf][grp].w};
+                const float hh[4] = {bf16_to_f32(hb[bf][grp].x & 0xffffu),
+                                     bf16_to_f32(hb[bf][grp].x >> 16),
+                                     bf16_to_f32(hb[bf][grp].y & 0xffffu),
+                                     bf16_to_f32(hb[bf][grp].y >> 16)};
+                const float hs = ((hh[0] * v[0] + hh[1] * v[1]) + hh[2] * v[2]) + hh[3] * v[3];
+                if constexpr (j == 0) hz[grp] = hs;
+                else hz[grp] += hs;
                 f32x4_t dg, du;
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
+                    const float da = wr[bf][grp] * v[k];
                     const float sg = __builtin_amdgcn_rcpf(
                         1.0f + __builtin_amdgcn_exp2f(gg[k] * -1.44269504088896341f));
-                    dg[k] = v[k] * uu[k] * sg * (1.0f + gg[k] * (1.0f - sg));
-                    du[k] = v[k] * gg[k] * sg;
+                    dg[k] = da * uu[k] * sg * (1.0f + gg[k] * (1.0f - sg));
+                    du[k] = da * gg[k] * sg;
                 }
                 const int row = blk_row(i, grp);
                 if (row < row_end) {
@@ -708,9 +736,27 @@ __device__ __forceinline__ void q_tile_run(const QSlots &S, const QArgs &g, cons
                     *reinterpret_cast<uint2 *>(dU + o) =
                         __builtin_bit_cast(uint2, __builtin_convertvector(du, bf16x4_t));
                 }
+                if constexpr (j == 1) {
+                    float t = hz[grp];
+                    t += __shfl_xor(t, 4, 64);
+                    t += __shfl_xor(t, 8, 64);
+                    t += __shfl_xor(t, 16, 64);
+                    if ((lane & 28) == 0)
+                        red[wave * 256 + i * 32 + 8 * grp + 4 * (lane >> 5) + (lane & 3)] = t;
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
         });
+        // The rings are idle after the K loop's last barrier; the next
+        // tile refills slot b2 only after its prologue barrier, and the
+        // barrier below keeps every wavefront's reads of red before it.
+        __syncthreads();
+        const int tid = threadIdx.x;
+        if (tid < 32 * MBE && row0 + tid < row_end) {
+            const float t = (red[tid] + red[256 + tid]) + (red[512 + tid] + red[768 + tid]);
+            g.dw_part[(size_t)(row0 + tid) * (N / QBN) + n0 / QBN] = t;
+        }
+        __syncthreads();
     } else if constexpr (EPI == QE_F32) {
         // fp32 sums as 16-byte row segments: each 4 x 4 block of a lane
         // quad is quad-transposed so that a lane holds 4 consecutive

@@ -6,17 +6,20 @@
 namespace moe {
 namespace {
 
-// Backward: da = dO W2[e]^T with dg, du in the epilogue (B K-contiguous:
-// W2[e] [f, d] read along d).
+// Backward: z = dY W2[e]^T for the routed rows' dy, da = w z with dg, du
+// in the epilogue, and the per-column-tile partial sums of h . z (B
+// K-contiguous: W2[e] [f, d] read along d).
 __global__ __launch_bounds__(QT, 1) void q_bt_dswiglu_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B,
     const int32_t *__restrict__ counts, const int32_t *__restrict__ offsets, int E, int K1, int N,
     int a_rows, const float *__restrict__ gin, const float *__restrict__ uin,
-    uint16_t *__restrict__ dg, uint16_t *__restrict__ du, int cu_per_xcd) {
+    uint16_t *__restrict__ dg, uint16_t *__restrict__ du, const float *__restrict__ w_row,
+    const uint16_t *__restrict__ h, float *__restrict__ dw_part, int cu_per_xcd) {
     QArgs g{};
     g.A = A; g.B0 = B; g.C = dg; g.C2 = du;
     g.K = K1; g.N = N; g.a_lines = a_rows; g.lda = K1; g.ldb = K1;
     g.g_in = gin; g.u_in = uin;
+    g.w_row = w_row; g.h_in = h; g.dw_part = dw_part;
     q_body<QMode<1, QE_DSWIGLU, false, false, true>>(g, counts, offsets, E, 1, cu_per_xcd,
                                                      nullptr);
 }
@@ -39,16 +42,20 @@ __global__ __launch_bounds__(QT, 1) void q_bt_store_split_kernel(
 }  // namespace
 
 // Backward products with K-contiguous weights (see moe_internal.h).
-hipError_t q_launch_bt_dswiglu(int rows, int E, const uint16_t *dO, const uint16_t *w2, int K1,
+bool q_bt_dswiglu_supported(int rows, int K1, int N) {
+    return q_fits(rows, K1, N, QBN) && (uint64_t)N * K1 * 2 < ((uint64_t)1 << 32);
+}
+
+hipError_t q_launch_bt_dswiglu(int rows, int E, const uint16_t *dyp, const uint16_t *w2, int K1,
                                int N, const int32_t *counts, const int32_t *offsets,
                                const float *g, const float *u, uint16_t *dg, uint16_t *du,
+                               const float *w_row, const uint16_t *h, float *dw_part,
                                hipStream_t stream) {
-    if (!q_fits(rows, K1, N, QBN) || (uint64_t)N * K1 * 2 >= ((uint64_t)1 << 32))
-        return hipErrorNotSupported;
+    if (!q_bt_dswiglu_supported(rows, K1, N)) return hipErrorNotSupported;
     const int cpx = q_cus_per_xcd();
     if (cpx < 0) return hipErrorNotSupported;
-    hipLaunchKernelGGL(q_bt_dswiglu_kernel, dim3(8 * cpx), dim3(QT), 0, stream, dO, w2, counts,
-                       offsets, E, K1, N, rows, g, u, dg, du, cpx);
+    hipLaunchKernelGGL(q_bt_dswiglu_kernel, dim3(8 * cpx), dim3(QT), 0, stream, dyp, w2, counts,
+                       offsets, E, K1, N, rows, g, u, dg, du, w_row, h, dw_part, cpx);
     return hipGetLastError();
 }
 

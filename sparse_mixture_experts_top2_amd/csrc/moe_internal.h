@@ -280,16 +280,21 @@ hipError_t q_launch_down(int rows, int E, const uint16_t *h, const int32_t *coun
                          const int32_t *offsets, const uint16_t *w2, int K, int N, float *o,
                          int parts, size_t part_stride, int cu_per_xcd, int *parts_out,
                          hipStream_t stream);
-// The backward's products on the same pipeline.  bt_dswiglu: da = dO
-// w2[e]^T (w2[e] [N, K1] read along K1), turned into dg, du (bf16) with g,
-// u (fp32), all [rows, N].  bt_store_split: C = A B[e]^T + A2 B2[e]^T
-// (B[e], B2[e] [N, K1]), the 2 K1 reduction cut into parts chosen from
-// the counts (count to *parts_out, part p at C + p * part_stride).
-// hipErrorNotSupported unless K1 % 64 == 0, N % 256 == 0 and the operands
-// fit 32-bit offsets.
-hipError_t q_launch_bt_dswiglu(int rows, int E, const uint16_t *dO, const uint16_t *w2, int K1,
+// The backward's products on the same pipeline.  bt_dswiglu: z = dyp
+// w2[e]^T (dyp the routed rows' dy, unscaled; w2[e] [N, K1] read along
+// K1), da = w_row z turned into dg, du (bf16) with g, u (fp32), all
+// [rows, N]; and dw_part [rows, N / 256] = each row's sum of h z over each
+// 256-column tile (h bf16 [rows, N]), the routing-weight gradient's parts.
+// bt_store_split: C = A B[e]^T + A2 B2[e]^T (B[e], B2[e] [N, K1]), the
+// 2 K1 reduction cut into parts chosen from the counts (count to
+// *parts_out, part p at C + p * part_stride).  hipErrorNotSupported
+// unless K1 % 64 == 0, N % 256 == 0 and the operands fit 32-bit offsets
+// (q_bt_dswiglu_supported).
+bool q_bt_dswiglu_supported(int rows, int K1, int N);
+hipError_t q_launch_bt_dswiglu(int rows, int E, const uint16_t *dyp, const uint16_t *w2, int K1,
                                int N, const int32_t *counts, const int32_t *offsets,
                                const float *g, const float *u, uint16_t *dg, uint16_t *du,
+                               const float *w_row, const uint16_t *h, float *dw_part,
                                hipStream_t stream);
 hipError_t q_launch_bt_store_split(int rows, int E, const uint16_t *A, const uint16_t *B,
                                    const uint16_t *A2, const uint16_t *B2, int K1, int N,
