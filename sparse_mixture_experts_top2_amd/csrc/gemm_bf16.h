@@ -579,11 +579,16 @@ __device__ __forceinline__ void q_tile_run(const QSlots &S, const QArgs &g, cons
         q_barrier<0>();
     }
 
+    // The epilogues take the lane index afresh from the hardware (mbcnt):
+    // the one computed at the kernel's start is kept in scratch through
+    // the K loop, and each reload's wait (vmcnt, in order) would also wait
+    // for the epilogue's prefetched loads.
+    const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
     // 32x32 accumulator layout: value q of lane l is row 8 (q / 4) + 4 (l / 32)
     // + q % 4, column l % 32 of the block.
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     typedef float f32x2_t __attribute__((ext_vector_type(2)));
-    const int odd = lane & 1;
+    const int odd = ln & 1;
     // Store two bf16 values of this lane's column, rows q and q + 1 (v0, v1),
     // as 4-byte column pairs: lanes l and l ^ 1 hold neighbouring columns
     // of the same rows and swap one value (a DPP quad permutation), so that
@@ -609,7 +614,7 @@ __device__ __forceinline__ void q_tile_run(const QSlots &S, const QArgs &g, cons
         // slower here: the transposes lengthen the epilogue more than the
         // halved store count saves.)
         uint16_t *H = static_cast<uint16_t *>(g.C);
-        const int col = n0 + wave * 32 + (lane & 31);
+        const int col = n0 + wave * 32 + (ln & 31);
 #pragma unroll
         for (int i = 0; i < MBE; ++i)
 #pragma unroll
@@ -619,7 +624,7 @@ __device__ __forceinline__ void q_tile_run(const QSlots &S, const QArgs &g, cons
                     const float den = 1.0f + __builtin_amdgcn_exp2f(gv * -1.44269504088896341f);
                     return gv * __builtin_amdgcn_rcpf(den) * uv;
                 };
-                const int row_q = row0 + i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                const int row_q = row0 + i * 32 + 8 * (q >> 2) + 4 * (ln >> 5) + (q & 3);
                 store_pair(H, row_q, col, hval(q), hval(q + 1));
             }
     } else if constexpr (EPI == QE_SWIGLU) {
@@ -630,7 +635,7 @@ __device__ __forceinline__ void q_tile_run(const QSlots &S, const QArgs &g, cons
         // quarter of the store instructions of column stores).
         typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
         uint16_t *H = static_cast<uint16_t *>(g.C);
-        const int c4 = n0 + wave * 32 + ((lane & 31) & ~3);
+        const int c4 = n0 + wave * 32 + ((ln & 31) & ~3);
 #pragma unroll
         for (int i = 0; i < MBE; ++i)
 #pragma unroll
@@ -643,10 +648,10 @@ __device__ __forceinline__ void q_tile_run(const QSlots &S, const QArgs &g, cons
                     const float den = 1.0f + __builtin_amdgcn_exp2f(gv[k] * -1.44269504088896341f);
                     hv[k] = gv[k] * __builtin_amdgcn_rcpf(den) * uv[k];
                 }
-                q_quad_transpose(hv, lane & 3);
-                q_quad_transpose(gv, lane & 3);
-                q_quad_transpose(uv, lane & 3);
-                const int row = row0 + i * 32 + 8 * grp + 4 * (lane >> 5) + (lane & 3);
+                q_quad_transpose(hv, ln & 3);
+                q_quad_transpose(gv, ln & 3);
+                q_quad_transpose(uv, ln & 3);
+                const int row = row0 + i * 32 + 8 * grp + 4 * (ln >> 5) + (ln & 3);
                 if (row < row_end) {
                     const size_t o = (size_t)row * N + c4;
                     typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -682,9 +687,9 @@ __device__ __forceinline__ void q_tile_run(const QSlots &S, const QArgs &g, cons
         float hz[4];
         float *red = reinterpret_cast<float *>(S.b2);   // [4 wavefronts][256 rows]
         auto blk_row = [&](int i, int grp) Q_INLINE {
-            return row0 + i * 32 + 8 * grp + 4 * (lane >> 5) + (lane & 3);
+            return row0 + i * 32 + 8 * grp + 4 * (ln >> 5) + (ln & 3);
         };
-        auto blk_col = [&](int j) Q_INLINE { return n0 + wave * 64 + j * 32 + ((lane & 31) & ~3); };
+        auto blk_col = [&](int j) Q_INLINE { return n0 + wave * 64 + j * 32 + ((ln & 31) & ~3); };
         auto load_blk = [&](auto b_c, auto buf_c) Q_INLINE {
             constexpr int b = decltype(b_c)::value, bf = decltype(buf_c)::value;
             constexpr int i = b / 2, j = b % 2;
@@ -709,7 +714,7 @@ __device__ __forceinline__ void q_tile_run(const QSlots &S, const QArgs &g, cons
                 float v[4];
 #pragma unroll
                 for (int k = 0; k < 4; ++k) v[k] = acc[i][j][4 * grp + k];
-                q_quad_transpose(v, lane & 3);
+                q_quad_transpose(v, ln & 3);
                 const float gg[4] = {gb[bf][grp].x, gb[bf][grp].y, gb[bf][grp].z, gb[bf][grp].w};
                 const float uu[4] = {ub[bf][grp].x, ub[bf][grp].y, ub[bf][grp].z, ub[bf][grp].w};
                 const float hh[4] = {bf16_to_f32(hb[bf][grp].x & 0xffffu),
@@ -741,8 +746,8 @@ __device__ __forceinline__ void q_tile_run(const QSlots &S, const QArgs &g, cons
                     t += __shfl_xor(t, 4, 64);
                     t += __shfl_xor(t, 8, 64);
                     t += __shfl_xor(t, 16, 64);
-                    if ((lane & 28) == 0)
-                        red[wave * 256 + i * 32 + 8 * grp + 4 * (lane >> 5) + (lane & 3)] = t;
+                    if ((ln & 28) == 0)
+                        red[wave * 256 + i * 32 + 8 * grp + 4 * (ln >> 5) + (ln & 3)] = t;
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -773,9 +778,9 @@ __device__ __forceinline__ void q_tile_run(const QSlots &S, const QArgs &g, cons
                     float v[4];
 #pragma unroll
                     for (int k = 0; k < 4; ++k) v[k] = acc[i][j][4 * grp + k];
-                    q_quad_transpose(v, lane & 3);
-                    const int row = row0 + i * 32 + 8 * grp + 4 * (lane >> 5) + (lane & 3);
-                    const int c4 = n0 + wave * 64 + j * 32 + ((lane & 31) & ~3);
+                    q_quad_transpose(v, ln & 3);
+                    const int row = row0 + i * 32 + 8 * grp + 4 * (ln >> 5) + (ln & 3);
+                    const int c4 = n0 + wave * 64 + j * 32 + ((ln & 31) & ~3);
                     if (row < row_end)
                         *reinterpret_cast<f32x4_t *>(O + (size_t)row * N + c4) =
                             f32x4_t{v[0], v[1], v[2], v[3]};
@@ -796,10 +801,10 @@ __device__ __forceinline__ void q_tile_run(const QSlots &S, const QArgs &g, cons
                     float v[4];
 #pragma unroll
                     for (int k = 0; k < 4; ++k) v[k] = acc[i][j][4 * grp + k];
-                    q_quad_transpose(v, lane & 3);
-                    const int row = row0 + i * 32 + 8 * grp + 4 * (lane >> 5) + (lane & 3);
+                    q_quad_transpose(v, ln & 3);
+                    const int row = row0 + i * 32 + 8 * grp + 4 * (ln >> 5) + (ln & 3);
                     const int c4 = (NMAT == 2 ? n0 + wave * 32 : n0 + wave * 64 + j * 32) +
-                                   ((lane & 31) & ~3);
+                                   ((ln & 31) & ~3);
                     const f32x4_t out = {v[0], v[1], v[2], v[3]};
                     __builtin_nontemporal_store(
                         out, reinterpret_cast<f32x4_t *>((j == 1 ? O1 : O0) + (size_t)row * N + c4));
