@@ -407,9 +407,15 @@ __device__ __forceinline__ void q_quad_transpose(float (&v)[4], int p) {
 template <typename Mode, int MBE>
 __device__ __forceinline__ void q_tile_run(const QSlots &S, const QArgs &g, const QTile &t) {
     constexpr int NMAT = Mode::NMAT, EPI = Mode::EPI;
-    constexpr bool BKC = Mode::BKC, DUAL = Mode::DUAL, GROUPK = Mode::GROUPK;
+    constexpr bool BKC = Mode::BKC;
     const int N = g.N;
-    const int e = t.e, row0 = t.row0, row_end = t.row_end, n0 = t.n0, kt0 = t.kt0, nk = t.nk;
+    // The tile's fields are uniform across the workgroup: held in scalar
+    // registers, they cannot be spilled to (and reloaded from) scratch.
+    const int e = __builtin_amdgcn_readfirstlane(t.e);
+    const int row0 = __builtin_amdgcn_readfirstlane(t.row0);
+    const int row_end = __builtin_amdgcn_readfirstlane(t.row_end);
+    const int n0 = __builtin_amdgcn_readfirstlane(t.n0);
+    const int nk = __builtin_amdgcn_readfirstlane(t.nk);
     auto slot_a = [&](auto i_c) Q_INLINE {
         constexpr int i = decltype(i_c)::value % QAS;
         if constexpr (i == 0) return S.a0;
