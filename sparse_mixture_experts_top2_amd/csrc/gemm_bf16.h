@@ -59,6 +59,17 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 #define Q_INLINE __attribute__((always_inline))
 
+// The thread index, taken afresh for each tile: the empty asm hides that it
+// is the same on every tile, so the copy and fragment offsets derived from
+// it are recomputed per tile (a few integer ops) instead of being held
+// across the whole persistent loop, where they were spilled to scratch and
+// reloaded in every epilogue.
+__device__ __forceinline__ int q_tid() {
+    int t = (int)threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
+
 template <int I, int N, typename F>
 __device__ __forceinline__ void q_for_from(F &&f) {
     if constexpr (I < N) {
@@ -285,8 +296,8 @@ struct QLoad {
     int wave, kt0, nk, K1, N;
 
     __device__ __forceinline__ QLoad(const QArgs &g, const QTile &t) {
-        const int lane = threadIdx.x & 63;
-        wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const int tid = q_tid(), lane = tid & 63;
+        wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         kt0 = t.kt0;
         nk = t.nk;
         K1 = g.K1;
@@ -428,7 +439,7 @@ __device__ __forceinline__ void q_tile_run(const QSlots &S, const QArgs &g, cons
         else return S.b2;
     };
 
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = q_tid(), lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
     const QLoad<Mode, MBE> L(g, t);
