@@ -70,33 +70,33 @@ __device__ __forceinline__ float load1<float>(const float *p) { return *p; }
 template <>
 __device__ __forceinline__ float load1<uint16_t>(const uint16_t *p) { return bf16_to_f32(*p); }
 
-// Router row j (E values) widened to fp32.  When E is a multiple of the
-// values per 16 bytes, every row is 16-byte aligned (w_gate is 16-byte
-// aligned), so it is read with vector loads, one condition per 16 bytes,
-// and slots e >= E hold 0.  Otherwise element by element, slots e >= E
-// repeating column E-1 (their sums are never read).  The clamp bound sits
-// in a vector register so that the compiler does not hoist EMAX uniform
-// compares or offsets out of the loop into scalar registers.
-template <typename T, int EMAX>
+// Router row j (E values) widened to fp32.  VEC (E a multiple of the values
+// per 16 bytes): every row is 16-byte aligned (w_gate is 16-byte aligned),
+// so it is read with vector loads; a 16-byte group past E re-reads the
+// row's first group (in bounds) and its slots are set to 0.  Every load is
+// unconditional, so a chunk's row loads are all in flight together rather
+// than each waiting behind a branch.  Otherwise element by element, slots
+// e >= E repeating column E-1 (their sums are never read).  The clamp
+// bound sits in a vector register so that the compiler does not hoist EMAX
+// uniform compares or offsets out of the loop into scalar registers.
+template <typename T, int EMAX, bool VEC>
 __device__ __forceinline__ void load_router_row(const T *row, int E, float (&wr)[EMAX]) {
     constexpr int per16 = 16 / (int)sizeof(T);
-    if (E % per16 == 0) {
+    if constexpr (VEC) {
 #pragma unroll
-        for (int v = 0; v < EMAX / per16; ++v) {
+        for (int v = 0; v < (EMAX + per16 - 1) / per16; ++v) {
+            const bool in = v == 0 || v * per16 < E;
+            const int g = in ? v : 0;
             float t[8];
-            if (v * per16 < E) {
-                if constexpr (sizeof(T) == 2) {
-                    load8<T>(row + v * 8, t);
-                } else {
-                    float4 q = reinterpret_cast<const float4 *>(row)[v];
-                    t[0] = q.x; t[1] = q.y; t[2] = q.z; t[3] = q.w;
-                }
+            if constexpr (sizeof(T) == 2) {
+                load8<T>(row + g * 8, t);
             } else {
-#pragma unroll
-                for (int i = 0; i < per16; ++i) t[i] = 0.0f;
+                float4 q = reinterpret_cast<const float4 *>(row)[g];
+                t[0] = q.x; t[1] = q.y; t[2] = q.z; t[3] = q.w;
             }
 #pragma unroll
-            for (int i = 0; i < per16; ++i) wr[v * per16 + i] = t[i];
+            for (int i = 0; i < per16 && v * per16 + i < EMAX; ++i)
+                wr[v * per16 + i] = in ? t[i] : 0.0f;
         }
     } else {
         int last;
@@ -234,40 +234,49 @@ __global__ __launch_bounds__(256) void route_kernel(const T *__restrict__ x,
 #pragma unroll
         for (int e = 0; e < EMAX; ++e) acc[tt][e] = 0.0f;
 
-    for (int c = tid; c < nchunk; c += 256) {
-        float xv[TPB][8];
-#pragma unroll
-        for (int tt = 0; tt < TPB; ++tt) {
-            const int t = min(t0 + tt, n_tok - 1);
-            load8<T>(x + (size_t)t * d + c * 8, xv[tt]);
-        }
-        if constexpr (NORM) {
-            float gv[8];
-            load8<T>(g + c * 8, gv);
+    // The row loader's form is fixed for the whole loop (E is uniform), so
+    // the loop body holds no branch around its loads.
+    auto chunks = [&](auto vec_c) __attribute__((always_inline)) {
+        constexpr bool VEC = decltype(vec_c)::value;
+        for (int c = tid; c < nchunk; c += 256) {
+            float xv[TPB][8];
 #pragma unroll
             for (int tt = 0; tt < TPB; ++tt) {
+                const int t = min(t0 + tt, n_tok - 1);
+                load8<T>(x + (size_t)t * d + c * 8, xv[tt]);
+            }
+            if constexpr (NORM) {
+                float gv[8];
+                load8<T>(g + c * 8, gv);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) xv[tt][i] = xv[tt][i] * rstd[tt] * gv[i];
-                store8<T>(xn_out + (size_t)min(t0 + tt, n_tok - 1) * d + c * 8, xv[tt]);
-                // the router sees the rounded values the experts will see
+                for (int tt = 0; tt < TPB; ++tt) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) xv[tt][i] = round_to<T>(xv[tt][i]);
+                    for (int i = 0; i < 8; ++i) xv[tt][i] = xv[tt][i] * rstd[tt] * gv[i];
+                    store8<T>(xn_out + (size_t)min(t0 + tt, n_tok - 1) * d + c * 8, xv[tt]);
+                    // the router sees the rounded values the experts will see
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) xv[tt][i] = round_to<T>(xv[tt][i]);
+                }
+            }
+            // Router rows are read 8 at a time when few values are accumulated;
+            // wider rows (32+ experts per token) go one or two at a time so that
+            // the accumulators and the row stay in registers.
+            constexpr int RU = EMAX >= 64 ? 1 : EMAX >= 32 ? 2 : 8;
+#pragma unroll RU
+            for (int r = 0; r < 8; ++r) {
+                float wr[EMAX];
+                load_router_row<T, EMAX, VEC>(wg + (size_t)(c * 8 + r) * E, E, wr);
+#pragma unroll
+                for (int tt = 0; tt < TPB; ++tt)
+#pragma unroll
+                    for (int e = 0; e < EMAX; ++e) acc[tt][e] += xv[tt][r] * wr[e];
             }
         }
-        // Router rows are read 8 at a time when few values are accumulated;
-        // wider rows (32+ experts per token) go one or two at a time so that
-        // the accumulators and the row stay in registers.
-        constexpr int RU = EMAX >= 64 ? 1 : EMAX >= 32 ? 2 : 8;
-#pragma unroll RU
-        for (int r = 0; r < 8; ++r) {
-            float wr[EMAX];
-            load_router_row<T, EMAX>(wg + (size_t)(c * 8 + r) * E, E, wr);
-#pragma unroll
-            for (int tt = 0; tt < TPB; ++tt)
-#pragma unroll
-                for (int e = 0; e < EMAX; ++e) acc[tt][e] += xv[tt][r] * wr[e];
-        }
-    }
+    };
+    if (E % (16 / (int)sizeof(T)) == 0)
+        chunks(std::true_type{});
+    else
+        chunks(std::false_type{});
     // Reduce-scatter butterfly over the wavefront: at each step a lane keeps
     // half of its remaining values and adds its partner's copy of that half,
     // so after log2(64) steps lane l holds the wavefront sum of value l
