@@ -420,8 +420,9 @@ __device__ __forceinline__ void q_tile_run(const QSlots &S, const QArgs &g, cons
     constexpr int NMAT = Mode::NMAT, EPI = Mode::EPI;
     constexpr bool BKC = Mode::BKC;
     const int N = g.N;
-    // The tile's fields are uniform across the workgroup: held in scalar
-    // registers, they cannot be spilled to (and reloaded from) scratch.
+    // The tile's fields are uniform across the workgroup, so they go to
+    // scalar registers; held in vector registers they were spilled and
+    // reloaded from scratch in the epilogue.
     const int e = __builtin_amdgcn_readfirstlane(t.e);
     const int row0 = __builtin_amdgcn_readfirstlane(t.row0);
     const int row_end = __builtin_amdgcn_readfirstlane(t.row_end);
